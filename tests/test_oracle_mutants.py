@@ -1,0 +1,49 @@
+"""Planted mistakes in copies of the oracle must each break some pin.
+
+Each mutant is the oracle's source with one textual change (a flipped
+comparison, a dropped term, a wrong operand), loaded as a separate module
+on the CPU; the real oracle is never modified."""
+import os
+import types
+
+import pytest
+
+from oracle_pins import run_all
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                   "oracle", "sffn_oracle.py")
+
+MUTATIONS = [
+    ("pack: >= instead of >", "cols = lo + np.flatnonzero(z[t, lo:hi] > 0)",
+     "cols = lo + np.flatnonzero(z[t, lo:hi] >= 0)"),
+    ("pack: keeps the last C", "keep = cols[:C]", "keep = cols[-C:] if C else cols[:0]"),
+    ("pack: flag at cnt == C", "row_flag = (cnt > C).any(axis=1)",
+     "row_flag = (cnt >= C).any(axis=1)"),
+    ("pack: capped count", "cnt[t, b] = len(cols)", "cnt[t, b] = min(len(cols), C)"),
+    ("dense: ReLU dropped", "h = a * u", "h = z * u"),
+    ("dense: up projection dropped", "h = a * u", "h = a"),
+    ("relu: leaky", "return np.where(z > 0, z, 0.0)",
+     "return np.where(z > 0, z, 0.01 * z)"),
+    ("sparse: up projection dropped", "h = a if wu is None else a * float(x[t] @ wu[:, j])",
+     "h = a"),
+    ("hybrid: >= K", "if nnz[t] > K or row_flag[t]:", "if nnz[t] >= K or row_flag[t]:"),
+    ("hybrid: flag ignored", "if nnz[t] > K or row_flag[t]:", "if nnz[t] > K:"),
+    ("backward: dU W_u^T dropped", "dx = dz @ wg.T + du @ wu.T", "dx = dz @ wg.T"),
+    ("backward: mask dropped", 'dz = dh * it["u"] * m + l1_coeff * m',
+     'dz = dh * it["u"] + l1_coeff * m'),
+    ("backward: dW_d uses A", 'dw_down=it["h"].T @ dy)', 'dw_down=it["a"].T @ dy)'),
+    ("backward: transposed dW_g", "return dict(dx=dx, dw_gate=x.T @ dz, dw_up=x.T @ du,",
+     "return dict(dx=dx, dw_gate=(dz.T @ x).T[:, ::-1].copy(), dw_up=x.T @ du,"),
+    ("bf16: 7 significant bits", "s = m * 256.0", "s = m * 128.0"),
+    ("bf16: ties away", "r = np.round(s)", "r = np.floor(s + 0.5)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutant_is_caught(name, old, new):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation target not found: {old}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(old, new, 1), "oracle_mutant", "exec"), mod.__dict__)
+    failures = run_all(mod)
+    assert failures, f"mutant '{name}' passed every pin"
