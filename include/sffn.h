@@ -1,0 +1,211 @@
+/*
+ * sffn.h - activation-sparse ReLU feedforward layer for AMD Instinct MI355X
+ * (gfx950), C ABI.
+ *
+ * The layer is the feedforward block of "Sparser, Faster, Lighter
+ * Transformer Language Models" (Cetin et al.):
+ *
+ *   gated      y = (ReLU(x W_g) * (x W_u)) W_d
+ *   non-gated  y = ReLU(x W_1) W_2
+ *
+ * (gist.science explainer, "2. Methodology" B, inference kernels; appendix
+ * Table 2 for the gated/non-gated shapes). The sparse forward packs the gate
+ * activations into TwELL inside the gate GEMM's epilogue and then runs the
+ * up and down projections only over each token's active neurons, without a
+ * dense hidden tensor in memory (same section). TwELL is tile-wise ELLPACK:
+ * each row's columns are cut into 1-D tiles of W columns and every
+ * (row, tile) keeps a fixed-capacity list of (value, column) plus a count
+ * ("2. Methodology" A; wispaper blog, "1. TwELL: Tile-wise ELLPACK").
+ *
+ * Conventions shared by every call:
+ *   - Every call returns an sffn_status and never aborts or throws.
+ *   - Argument errors (null or misaligned pointers, bad sizes) are found on
+ *     the host before anything is enqueued and return SFFN_E_ARG.
+ *   - All device work is enqueued on the caller's stream; no call
+ *     synchronises the stream except sffn_check().
+ *   - Pointers are device pointers unless stated; every array is
+ *     caller-owned and must be 16-byte aligned. The library never frees
+ *     caller memory.
+ *   - A handle is not thread-safe; use one handle per concurrently used
+ *     stream.
+ *   - T = 0 is a no-op that returns SFFN_OK.
+ *   - Layouts (row-major, contiguous):
+ *       x, dy        [T, d]            dtype of the descriptor
+ *       w_gate, w_up [F, d]            neuron-major (row j = column j of
+ *                                      the math d x F matrix, i.e. the
+ *                                      nn.Linear weight layout)
+ *       w_down       [F, d]            row j = neuron j's output weights
+ *                                      (the math F x d matrix as is)
+ *       y, dx        [T, d]            float32
+ *       z            [T, F]            float32 gate pre-activations
+ *   - "active" means strictly z > 0; slots inside a tile ascend by column.
+ */
+#ifndef SFFN_H
+#define SFFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sffn_status;
+#define SFFN_OK             0
+#define SFFN_E_ARG         -1  /* null/misaligned pointer, bad size or enum */
+#define SFFN_E_UNSUPPORTED -2  /* shape outside the supported set, wrong GPU */
+#define SFFN_E_HIP         -3  /* HIP runtime or launch error; see sffn_last_error */
+#define SFFN_E_CAPACITY    -4  /* a caller buffer was too small (data dependent) */
+
+/* element type of x, the weights and dy */
+#define SFFN_F32  0
+#define SFFN_BF16 1
+
+/* forward modes */
+#define SFFN_SPARSE 0   /* gate GEMM + TwELL, sparse up/down, dense path for flagged rows */
+#define SFFN_DENSE  1   /* plain dense layer: the same library's baseline */
+
+/* operations, for sffn_workspace_bytes */
+#define SFFN_OP_PACK           0
+#define SFFN_OP_FORWARD_SPARSE 1
+#define SFFN_OP_FORWARD_DENSE  2
+
+typedef struct sffn_handle sffn_handle;
+
+/*
+ * Layer descriptor.
+ *   d          model width; d % 64 == 0, bf16: d % 512 == 0 and d <= 4096,
+ *              f32: d % 256 == 0 and d <= 2048 (SFFN_E_UNSUPPORTED otherwise)
+ *   d_ff       F, the number of neurons; F % 128 == 0, F <= 65408 so a
+ *              neuron id fits uint16
+ *   gated      1 gated, 0 non-gated (w_up unused and must be NULL)
+ *   tile       TwELL tile width W; 128 is the one supported width
+ *   twell_cap  C, TwELL slots per (row, tile); 1 <= C <= 128
+ *   ell_cap    K, Hybrid ELL capacity (0 = inference only)
+ *   dtype      SFFN_BF16 (bf16 inputs, fp32 accumulation) or SFFN_F32
+ *              (fp32 inputs and fp32 arithmetic throughout)
+ */
+typedef struct sffn_desc {
+  int32_t d;
+  int32_t d_ff;
+  int32_t gated;
+  int32_t tile;
+  int32_t twell_cap;
+  int32_t ell_cap;
+  int32_t dtype;
+} sffn_desc;
+
+/*
+ * TwELL buffers (device, caller-owned). n_t = F / W.
+ *   val       [T, n_t, C] float32   slot values, the gate pre-activation
+ *                                   z[t, j] (> 0) as accumulated in fp32;
+ *                                   unused slots hold 0.0
+ *   idx       [T, n_t, C] uint16    slot neuron ids j (global); unused 0
+ *   cnt       [T, n_t]    int32     true number of positives in the tile
+ *                                   (not capped at C)
+ *   row_flag  [T]         uint8     1 iff some tile of the row has cnt > C
+ *   flagged   [T]         int32     the flagged rows in ascending order;
+ *                                   the first *n_flagged entries are valid
+ *   n_flagged [1]         int32     number of flagged rows
+ * Rows whose tiles all fit (row_flag 0) are stored losslessly; a flagged
+ * row keeps its first C slots per tile and the layer computes it densely.
+ */
+typedef struct sffn_twell {
+  float*    val;
+  uint16_t* idx;
+  int32_t*  cnt;
+  uint8_t*  row_flag;
+  int32_t*  flagged;
+  int32_t*  n_flagged;
+} sffn_twell;
+
+/* Create a handle for the current HIP device. Validates the descriptor
+ * (SFFN_E_ARG / SFFN_E_UNSUPPORTED) before touching the device; returns
+ * SFFN_E_UNSUPPORTED when the current device is not gfx950 and SFFN_E_HIP
+ * when no device can be queried. Allocates only host memory. */
+sffn_status sffn_create(const sffn_desc* desc, sffn_handle** out);
+
+/* Destroy a handle (NULL is allowed). */
+void sffn_destroy(sffn_handle* h);
+
+/* Text of the last error recorded on the handle ("" if none). The string
+ * lives until the next call on the handle. */
+const char* sffn_last_error(const sffn_handle* h);
+
+/* Static name of a status code. */
+const char* sffn_status_string(sffn_status s);
+
+/* Bytes of device workspace that operation op needs for T tokens. The
+ * workspace is caller-allocated, at least 256-byte aligned, and its
+ * contents need not be initialised. */
+sffn_status sffn_workspace_bytes(const sffn_handle* h, int64_t T, int32_t op,
+                                 size_t* bytes);
+
+/* ReLU + TwELL pack of a given pre-activation tensor z [T, F] float32
+ * (the format of "2. Methodology" A on the gist.science explainer, here as
+ * a stand-alone kernel that reads z). Fills every field of *tw. The result
+ * is a pure function of z (bit-exact, deterministic). */
+sffn_status sffn_pack_twell(sffn_handle* h, const float* z, int64_t T,
+                            const sffn_twell* tw, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* Gate pre-activations z = x W_g, [T, F] float32, computed by the same
+ * MFMA main loop as the fused gate GEMM of sffn_forward (so packing this z
+ * with sffn_pack_twell reproduces the forward's TwELL bit for bit). */
+sffn_status sffn_gate_preact(sffn_handle* h, const void* x, const void* w_gate,
+                             int64_t T, float* z, hipStream_t stream);
+
+/*
+ * Forward pass y [T, d] float32.
+ *   mode SFFN_SPARSE: gate GEMM with ReLU + TwELL pack in its epilogue
+ *     ("2. Methodology" B: gate projection), then the fused up/down
+ *     projection over each unflagged row's active neurons (same section:
+ *     fused up/down projection); flagged rows (a tile overflowed C) are
+ *     computed by a dense path restricted to those rows, the dense backup
+ *     of the Hybrid format used as a safety valve at inference. If tw is
+ *     non-NULL the TwELL is written there, else into the workspace.
+ *   mode SFFN_DENSE: the plain dense layer with the same kernels' GEMMs;
+ *     for bf16 the hidden activations are rounded once to bf16 between the
+ *     two GEMMs, as in a standard bf16 feedforward. tw must be NULL.
+ * w_up must be NULL iff the layer is non-gated. The workspace must hold
+ * sffn_workspace_bytes(op = SFFN_OP_FORWARD_SPARSE or _DENSE).
+ */
+sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate,
+                         const void* w_up, const void* w_down, int64_t T,
+                         float* y, const sffn_twell* tw, int32_t mode,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Synchronise the stream and report the first asynchronous error since
+ * the last check (SFFN_E_HIP), else SFFN_OK. */
+sffn_status sffn_check(sffn_handle* h, hipStream_t stream);
+
+/*
+ * Per-kernel timing. While enabled, every kernel launch of sffn_forward,
+ * sffn_pack_twell and sffn_gate_preact is bracketed by two HIP events
+ * recorded on the call's stream. sffn_profile_read waits for the recorded
+ * events, writes for each kernel id k < n the summed milliseconds and the
+ * number of launches since the last read (or since enabling), and resets
+ * the sums. Disabling drops pending records. Kernel ids:
+ */
+#define SFFN_K_GATE_TWELL    0  /* gate GEMM with the ReLU + TwELL epilogue */
+#define SFFN_K_FLAGS         1  /* overflow flags and flagged-row list */
+#define SFFN_K_SPARSE_UPDOWN 2  /* fused sparse up/down projection */
+#define SFFN_K_FLAG_GATEUP   3  /* gate/up GEMM of the flagged rows */
+#define SFFN_K_FLAG_DOWN     4  /* down GEMM of the flagged rows (split-K) */
+#define SFFN_K_SPLITK_REDUCE 5  /* split-K reduction into the flagged rows */
+#define SFFN_K_DENSE_GATEUP  6  /* dense mode: gate/up GEMM */
+#define SFFN_K_DENSE_DOWN    7  /* dense mode: down GEMM */
+#define SFFN_K_PACK          8  /* stand-alone TwELL pack */
+#define SFFN_K_GATE_PREACT   9  /* gate GEMM writing z */
+#define SFFN_K_COUNT        10
+sffn_status sffn_profile_enable(sffn_handle* h, int32_t enable);
+sffn_status sffn_profile_read(sffn_handle* h, double* total_ms, int32_t* launches, int32_t n);
+/* Static name of a kernel id ("" if out of range). */
+const char* sffn_kernel_name(int32_t k);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFFN_H */

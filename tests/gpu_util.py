@@ -1,0 +1,61 @@
+"""Helpers shared by the GPU tests: device copies of the seeded inputs,
+the oracle's view of the same inputs, and error measures."""
+import numpy as np
+import torch
+
+from unstructured_sparse_feedforward_amd import SparseFFN
+
+
+def dev(inp, name):
+    """Device tensor of one input, in the workload's storage dtype."""
+    a = getattr(inp, name)
+    if a is None:
+        return None
+    if inp.wl.dtype == "bf16":
+        return torch.from_numpy(inp.bits(name).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def math_weights(inp):
+    """float64 weights in the pages' orientation: W_g, W_u are d x F and
+    W_d is F x d."""
+    wg = inp.w_gate.astype(np.float64).T
+    wu = None if inp.w_up is None else inp.w_up.astype(np.float64).T
+    wd = inp.w_down.astype(np.float64)
+    return wg, wu, wd
+
+
+def layer(inp, **kw):
+    w = inp.wl
+    return SparseFFN(w.d, w.F, gated=w.gated, twell_cap=kw.get("C", w.twell_cap),
+                     tile=w.tile, dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+
+
+def rel_fro(got, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    got = np.asarray(got, dtype=np.float64)
+    n = np.linalg.norm(ref)
+    return np.linalg.norm(got - ref) / (n if n > 0 else 1.0)
+
+
+def assert_close_bf16(got, ref, what=""):
+    """Bound for bf16 inputs with fp32 accumulation: relative Frobenius
+    error <= 1e-3 and max-abs error <= 1e-2 * max|ref|."""
+    r = rel_fro(got, ref)
+    mx = np.abs(np.asarray(got, np.float64) - ref).max() if np.size(ref) else 0.0
+    assert r <= 1e-3, f"{what}: relative Frobenius error {r:.3e} > 1e-3"
+    assert mx <= 1e-2 * max(np.abs(ref).max(), 1e-30), f"{what}: max-abs {mx:.3e}"
+
+
+def assert_close_f32(got, ref, what=""):
+    """Bound for fp32 inputs: relative Frobenius error <= 1e-5."""
+    r = rel_fro(got, ref)
+    assert r <= 1e-5, f"{what}: relative Frobenius error {r:.3e} > 1e-5"
+
+
+def twell_np(tw):
+    torch.cuda.synchronize()
+    out = {k: v.cpu().numpy() for k, v in tw.items()}
+    out["idx"] = out["idx"].view(np.uint16).astype(np.int64)
+    out["n_flagged"] = int(out["n_flagged"][0])
+    return out

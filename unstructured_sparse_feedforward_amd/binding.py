@@ -1,0 +1,231 @@
+"""Thin Python binding of libsffn.so (the C ABI in include/sffn.h).
+
+Argument marshalling only: every step of the layer runs in the library's
+HIP kernels. PyTorch supplies device memory and the current stream. There
+is no fallback: if libsffn.so is missing or fails to load, every entry
+point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsffn.so")
+
+SFFN_OK = 0
+SFFN_E_ARG = -1
+SFFN_E_UNSUPPORTED = -2
+SFFN_E_HIP = -3
+SFFN_E_CAPACITY = -4
+
+SFFN_F32 = 0
+SFFN_BF16 = 1
+SFFN_SPARSE = 0
+SFFN_DENSE = 1
+SFFN_OP_PACK = 0
+SFFN_OP_FORWARD_SPARSE = 1
+SFFN_OP_FORWARD_DENSE = 2
+
+# every symbol include/sffn.h declares
+EXPORTS = ("sffn_create", "sffn_destroy", "sffn_last_error", "sffn_status_string",
+           "sffn_workspace_bytes", "sffn_pack_twell", "sffn_gate_preact",
+           "sffn_forward", "sffn_check", "sffn_profile_enable", "sffn_profile_read",
+           "sffn_kernel_name")
+SFFN_K_COUNT = 10
+
+
+class SffnDesc(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("gated", ctypes.c_int32), ("tile", ctypes.c_int32),
+                ("twell_cap", ctypes.c_int32), ("ell_cap", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class SffnTwell(ctypes.Structure):
+    _fields_ = [("val", ctypes.c_void_p), ("idx", ctypes.c_void_p),
+                ("cnt", ctypes.c_void_p), ("row_flag", ctypes.c_void_p),
+                ("flagged", ctypes.c_void_p), ("n_flagged", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libsffn.so once; raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run unstructured_sparse_feedforward_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.sffn_create.argtypes = [ctypes.POINTER(SffnDesc), ctypes.POINTER(vp)]
+    lib.sffn_create.restype = i32
+    lib.sffn_destroy.argtypes = [vp]
+    lib.sffn_destroy.restype = None
+    lib.sffn_last_error.argtypes = [vp]
+    lib.sffn_last_error.restype = ctypes.c_char_p
+    lib.sffn_status_string.argtypes = [i32]
+    lib.sffn_status_string.restype = ctypes.c_char_p
+    lib.sffn_workspace_bytes.argtypes = [vp, i64, i32, ctypes.POINTER(sz)]
+    lib.sffn_workspace_bytes.restype = i32
+    lib.sffn_pack_twell.argtypes = [vp, vp, i64, ctypes.POINTER(SffnTwell), vp, sz, vp]
+    lib.sffn_pack_twell.restype = i32
+    lib.sffn_gate_preact.argtypes = [vp, vp, vp, i64, vp, vp]
+    lib.sffn_gate_preact.restype = i32
+    lib.sffn_forward.argtypes = [vp, vp, vp, vp, vp, i64, vp, ctypes.POINTER(SffnTwell), i32,
+                                 vp, sz, vp]
+    lib.sffn_forward.restype = i32
+    lib.sffn_check.argtypes = [vp, vp]
+    lib.sffn_check.restype = i32
+    lib.sffn_profile_enable.argtypes = [vp, i32]
+    lib.sffn_profile_enable.restype = i32
+    lib.sffn_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double),
+                                      ctypes.POINTER(i32), i32]
+    lib.sffn_profile_read.restype = i32
+    lib.sffn_kernel_name.argtypes = [i32]
+    lib.sffn_kernel_name.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+class SffnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+class SparseFFN:
+    """One feedforward layer's handle.
+
+    Weights are passed to each call (neuron-major [F, d] for w_gate, w_up
+    and w_down); x is [T, d]; outputs are float32.
+    """
+
+    def __init__(self, d: int, d_ff: int, gated: bool = True, twell_cap: int = 8,
+                 tile: int = 128, ell_cap: int = 0, dtype: torch.dtype = torch.bfloat16):
+        self.lib = load_library()
+        self.d, self.d_ff, self.gated = d, d_ff, gated
+        self.tile, self.twell_cap, self.ell_cap = tile, twell_cap, ell_cap
+        self.dtype = dtype
+        self.n_t = d_ff // tile
+        self.desc = SffnDesc(d, d_ff, int(gated), tile, twell_cap, ell_cap,
+                             SFFN_BF16 if dtype == torch.bfloat16 else SFFN_F32)
+        h = ctypes.c_void_p()
+        st = self.lib.sffn_create(ctypes.byref(self.desc), ctypes.byref(h))
+        if st != SFFN_OK:
+            raise SffnError(st, f"sffn_create: {self.lib.sffn_status_string(st).decode()}")
+        self.h = h
+        self._ws: Dict[str, torch.Tensor] = {}
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.sffn_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _check(self, st: int, what: str):
+        if st != SFFN_OK:
+            err = self.lib.sffn_last_error(self.h).decode()
+            raise SffnError(st, f"{what}: {self.lib.sffn_status_string(st).decode()} {err}")
+
+    def workspace_bytes(self, T: int, op: int) -> int:
+        n = ctypes.c_size_t()
+        self._check(self.lib.sffn_workspace_bytes(self.h, T, op, ctypes.byref(n)),
+                    "sffn_workspace_bytes")
+        return n.value
+
+    def workspace(self, T: int, op: int, device=None):
+        """A 256-byte aligned device buffer of the needed size (cached and
+        grown per operation); returns (pointer, bytes)."""
+        n = self.workspace_bytes(T, op)
+        key = str(op)
+        buf = self._ws.get(key)
+        if buf is None or buf.numel() < n + 256:
+            buf = torch.empty(n + 256, dtype=torch.uint8, device=device or "cuda")
+            self._ws[key] = buf
+        p = buf.data_ptr()
+        return (p + 255) // 256 * 256, n
+
+    def new_twell(self, T: int, device="cuda") -> Dict[str, torch.Tensor]:
+        C, nt = self.twell_cap, self.n_t
+        return dict(
+            val=torch.empty((T, nt, C), dtype=torch.float32, device=device),
+            idx=torch.empty((T, nt, C), dtype=torch.int16, device=device),  # uint16 bits
+            cnt=torch.empty((T, nt), dtype=torch.int32, device=device),
+            row_flag=torch.empty((T,), dtype=torch.uint8, device=device),
+            flagged=torch.empty((max(T, 1),), dtype=torch.int32, device=device),
+            n_flagged=torch.zeros((4,), dtype=torch.int32, device=device),
+        )
+
+    @staticmethod
+    def _tw_struct(tw: Dict[str, torch.Tensor]) -> SffnTwell:
+        return SffnTwell(*(tw[k].data_ptr() for k in
+                           ("val", "idx", "cnt", "row_flag", "flagged", "n_flagged")))
+
+    def pack_twell(self, z: torch.Tensor, tw: Optional[Dict[str, torch.Tensor]] = None):
+        T = z.shape[0]
+        tw = tw if tw is not None else self.new_twell(T, z.device)
+        ws, n = self.workspace(T, SFFN_OP_PACK, z.device)
+        s = self._tw_struct(tw)
+        self._check(self.lib.sffn_pack_twell(self.h, _ptr(z), T, ctypes.byref(s), ws, n,
+                                             _stream()), "sffn_pack_twell")
+        return tw
+
+    def gate_preact(self, x: torch.Tensor, w_gate: torch.Tensor,
+                    z: Optional[torch.Tensor] = None) -> torch.Tensor:
+        T = x.shape[0]
+        if z is None:
+            z = torch.empty((T, self.d_ff), dtype=torch.float32, device=x.device)
+        self._check(self.lib.sffn_gate_preact(self.h, _ptr(x), _ptr(w_gate), T, _ptr(z),
+                                              _stream()), "sffn_gate_preact")
+        return z
+
+    def forward(self, x: torch.Tensor, w_gate: torch.Tensor, w_up: Optional[torch.Tensor],
+                w_down: torch.Tensor, mode: str = "sparse",
+                tw: Optional[Dict[str, torch.Tensor]] = None,
+                y: Optional[torch.Tensor] = None) -> torch.Tensor:
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty((T, self.d), dtype=torch.float32, device=x.device)
+        m = SFFN_SPARSE if mode == "sparse" else SFFN_DENSE
+        op = SFFN_OP_FORWARD_SPARSE if m == SFFN_SPARSE else SFFN_OP_FORWARD_DENSE
+        ws, n = self.workspace(T, op, x.device)
+        s = ctypes.byref(self._tw_struct(tw)) if tw is not None else None
+        self._check(self.lib.sffn_forward(self.h, _ptr(x), _ptr(w_gate), _ptr(w_up),
+                                          _ptr(w_down), T, _ptr(y), s, m, ws, n, _stream()),
+                    "sffn_forward")
+        return y
+
+    def check(self):
+        self._check(self.lib.sffn_check(self.h, _stream()), "sffn_check")
+
+    def profile(self, enable: bool = True):
+        """Bracket every kernel launch with HIP events on the call's stream."""
+        self._check(self.lib.sffn_profile_enable(self.h, int(enable)), "sffn_profile_enable")
+
+    def profile_read(self) -> Dict[str, tuple]:
+        """{kernel name: (total ms, launches)} since the last read."""
+        n = SFFN_K_COUNT
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int32 * n)()
+        self._check(self.lib.sffn_profile_read(self.h, ms, cnt, n), "sffn_profile_read")
+        return {self.lib.sffn_kernel_name(k).decode(): (ms[k], cnt[k])
+                for k in range(n) if cnt[k]}

@@ -1,0 +1,504 @@
+// C ABI of the sparse feedforward library: argument validation, workspace
+// layout and the order of kernel launches for each call. See include/sffn.h
+// for the contract of every entry point.
+#include <string.h>
+
+#include <algorithm>
+
+#include <string>
+#include <vector>
+
+#include "sffn.h"
+#include "sffn_internal.hpp"
+
+struct sffn_prof_rec {
+  int k;
+  hipEvent_t a, b;
+};
+
+struct sffn_handle {
+  sffn_desc desc;
+  int device;
+  int num_cu;
+  int n_t;
+  std::string err;
+  // per-kernel event timing
+  bool prof = false;
+  std::vector<hipEvent_t> pool;
+  std::vector<sffn_prof_rec> recs;
+  double tot_ms[SFFN_K_COUNT] = {};
+  int32_t launches[SFFN_K_COUNT] = {};
+};
+
+namespace {
+
+using namespace sffn;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+
+sffn_status fail(sffn_handle* h, sffn_status st, const std::string& msg) {
+  if (h) h->err = msg;
+  return st;
+}
+
+sffn_status hip_fail(sffn_handle* h, hipError_t e, const char* where) {
+  return fail(h, SFFN_E_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+sffn_status validate_desc(const sffn_desc* d) {
+  if (!d) return SFFN_E_ARG;
+  if (d->dtype != SFFN_F32 && d->dtype != SFFN_BF16) return SFFN_E_ARG;
+  if (d->gated != 0 && d->gated != 1) return SFFN_E_ARG;
+  if (d->d <= 0 || d->d_ff <= 0 || d->tile <= 0 || d->twell_cap <= 0 || d->ell_cap < 0)
+    return SFFN_E_ARG;
+  if (d->tile != kTile) return SFFN_E_UNSUPPORTED;
+  if (d->d_ff % kTile != 0 || d->d_ff > 65408) return SFFN_E_UNSUPPORTED;
+  if (d->twell_cap > kTile) return SFFN_E_UNSUPPORTED;
+  const int ch = d->dtype == SFFN_BF16 ? 512 : 256;
+  if (d->d % ch != 0 || d->d / ch > 8) return SFFN_E_UNSUPPORTED;
+  const int nch = d->d / ch;
+  if (nch != 1 && nch != 2 && nch != 4 && nch != 8) return SFFN_E_UNSUPPORTED;
+  return SFFN_OK;
+}
+
+Dtype dt_of(const sffn_handle* h) { return h->desc.dtype == SFFN_BF16 ? kBF16 : kF32; }
+size_t esize(const sffn_handle* h) { return h->desc.dtype == SFFN_BF16 ? 2 : 4; }
+int ovf_words(int64_t T) { return (int)((T + 31) / 32); }
+constexpr int kSplitMax = 16;
+
+// Workspace layout. Every region starts at a 256-byte boundary.
+struct Layout {
+  size_t ovf = 0, tw_val = 0, tw_idx = 0, tw_cnt = 0, tw_flag = 0, tw_list = 0, tw_nf = 0;
+  size_t hid = 0, part = 0, total = 0;
+};
+
+Layout layout(const sffn_handle* h, int64_t T, int op) {
+  Layout L;
+  const int64_t F = h->desc.d_ff, d = h->desc.d, C = h->desc.twell_cap, nt = h->n_t;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  if (op == SFFN_OP_PACK || op == SFFN_OP_FORWARD_SPARSE) {
+    L.ovf = take((size_t)nt * ovf_words(T) * 4);
+  }
+  if (op == SFFN_OP_FORWARD_SPARSE) {
+    L.tw_val = take((size_t)T * nt * C * 4);
+    L.tw_idx = take((size_t)T * nt * C * 2);
+    L.tw_cnt = take((size_t)T * nt * 4);
+    L.tw_flag = take((size_t)T);
+    L.tw_list = take((size_t)T * 4);
+    L.tw_nf = take(4);
+    // hidden rows of flagged tokens: bf16 hi|lo [T, 2F] or fp32 [T, F]
+    L.hid = take((size_t)T * F * 4);
+    // split-K partials of the flagged down projection: at most
+    // split_target / (d / 128) row tiles of 128 rows
+    const int ntl = (int)(d / 128);
+    const int tiles = std::max(1, h->num_cu / ntl);
+    L.part = take((size_t)tiles * 128 * d * 4);
+  }
+  if (op == SFFN_OP_FORWARD_DENSE) {
+    L.hid = take((size_t)T * F * esize(h));
+  }
+  L.total = o;
+  return L;
+}
+
+template <typename P>
+P* at(void* ws, size_t off) { return (P*)((char*)ws + off); }
+
+hipEvent_t take_event(sffn_handle* h) {
+  if (!h->pool.empty()) {
+    hipEvent_t e = h->pool.back();
+    h->pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one kernel launch with events when profiling is on.
+struct ProfScope {
+  sffn_handle* h;
+  int k;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  ProfScope(sffn_handle* h_, int k_, hipStream_t s_) : h(h_), k(k_), s(s_) {
+    if (h->prof && (a = take_event(h)) != nullptr) hipEventRecord(a, s);
+  }
+  ~ProfScope() {
+    if (!a) return;
+    hipEvent_t b = take_event(h);
+    if (!b) {
+      h->pool.push_back(a);
+      return;
+    }
+    hipEventRecord(b, s);
+    h->recs.push_back({k, a, b});
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* sffn_status_string(sffn_status s) {
+  switch (s) {
+    case SFFN_OK: return "SFFN_OK";
+    case SFFN_E_ARG: return "SFFN_E_ARG";
+    case SFFN_E_UNSUPPORTED: return "SFFN_E_UNSUPPORTED";
+    case SFFN_E_HIP: return "SFFN_E_HIP";
+    case SFFN_E_CAPACITY: return "SFFN_E_CAPACITY";
+    default: return "unknown status";
+  }
+}
+
+sffn_status sffn_create(const sffn_desc* desc, sffn_handle** out) {
+  if (!out) return SFFN_E_ARG;
+  *out = nullptr;
+  const sffn_status st = validate_desc(desc);
+  if (st != SFFN_OK) return st;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SFFN_E_HIP;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SFFN_E_HIP;
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return SFFN_E_UNSUPPORTED;
+  sffn_handle* h = new sffn_handle();
+  h->desc = *desc;
+  h->device = dev;
+  h->num_cu = prop.multiProcessorCount;
+  h->n_t = desc->d_ff / kTile;
+  *out = h;
+  return SFFN_OK;
+}
+
+void sffn_destroy(sffn_handle* h) {
+  if (!h) return;
+  for (auto& r : h->recs) {
+    hipEventDestroy(r.a);
+    hipEventDestroy(r.b);
+  }
+  for (auto e : h->pool) hipEventDestroy(e);
+  delete h;
+}
+
+const char* sffn_last_error(const sffn_handle* h) { return h ? h->err.c_str() : ""; }
+
+sffn_status sffn_workspace_bytes(const sffn_handle* h, int64_t T, int32_t op, size_t* bytes) {
+  if (!h || !bytes || T < 0) return SFFN_E_ARG;
+  if (op != SFFN_OP_PACK && op != SFFN_OP_FORWARD_SPARSE && op != SFFN_OP_FORWARD_DENSE)
+    return SFFN_E_ARG;
+  *bytes = layout(h, T, op).total;
+  return SFFN_OK;
+}
+
+static bool twell_ok(const sffn_twell* tw) {
+  return tw && aligned16(tw->val) && aligned16(tw->idx) && aligned16(tw->cnt) &&
+         aligned16(tw->row_flag) && aligned16(tw->flagged) && aligned16(tw->n_flagged);
+}
+
+sffn_status sffn_pack_twell(sffn_handle* h, const float* z, int64_t T, const sffn_twell* tw,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!h) return SFFN_E_ARG;
+  if (T < 0 || T > (int64_t)1 << 30) return fail(h, SFFN_E_ARG, "T out of range");
+  if (T == 0) return SFFN_OK;
+  if (!aligned16(z)) return fail(h, SFFN_E_ARG, "z must be a non-null 16-byte aligned pointer");
+  if (!twell_ok(tw)) return fail(h, SFFN_E_ARG, "TwELL buffers must be non-null and 16-byte aligned");
+  const Layout L = layout(h, T, SFFN_OP_PACK);
+  if (!ws || ws_bytes < L.total || ((uintptr_t)ws % kAlign) != 0)
+    return fail(h, SFFN_E_ARG, "workspace missing, too small or not 256-byte aligned");
+  const int ow = ovf_words(T);
+  uint32_t* ovf = at<uint32_t>(ws, L.ovf);
+  hipError_t e;
+  {
+    ProfScope ps(h, SFFN_K_PACK, stream);
+    e = launch_pack(z, T, h->desc.d_ff, h->desc.twell_cap, tw->val, tw->idx, tw->cnt, ovf, ow,
+                    stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "pack");
+  {
+    ProfScope ps(h, SFFN_K_FLAGS, stream);
+    e = launch_flags(ovf, h->n_t, ow, T, tw->row_flag, tw->flagged, tw->n_flagged, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "flags");
+  return SFFN_OK;
+}
+
+sffn_status sffn_gate_preact(sffn_handle* h, const void* x, const void* w_gate, int64_t T,
+                             float* z, hipStream_t stream) {
+  if (!h) return SFFN_E_ARG;
+  if (T < 0 || T > (int64_t)1 << 30) return fail(h, SFFN_E_ARG, "T out of range");
+  if (T == 0) return SFFN_OK;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(z))
+    return fail(h, SFFN_E_ARG, "x, w_gate and z must be non-null 16-byte aligned pointers");
+  GemmArgs g = {};
+  g.A = x;
+  g.lda = h->desc.d;
+  g.M = (int)T;
+  g.B0 = w_gate;
+  g.ldb = h->desc.d;
+  g.N = h->desc.d_ff;
+  g.K = h->desc.d;
+  g.out = z;
+  g.ldo = h->desc.d_ff;
+  g.grid = gemm_grid(dt_of(h), 1, h->num_cu);
+  hipError_t e;
+  {
+    ProfScope ps(h, SFFN_K_GATE_PREACT, stream);
+    e = launch_gemm(dt_of(h), 1, false, kEpiStoreF32, g, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "gate GEMM");
+  return SFFN_OK;
+}
+
+static sffn_status forward_dense(sffn_handle* h, const void* x, const void* wg, const void* wu,
+                                 const void* wd, int64_t T, float* y, void* ws,
+                                 const Layout& L, hipStream_t stream) {
+  const sffn_desc& D = h->desc;
+  const Dtype dt = dt_of(h);
+  void* hid = at<char>(ws, L.hid);
+  // H = ReLU(x W_g) * (x W_u)  (or ReLU(x W_1)), bf16-rounded for bf16 layers
+  GemmArgs g = {};
+  g.A = x;
+  g.lda = D.d;
+  g.M = (int)T;
+  g.B0 = wg;
+  g.B1 = wu;
+  g.ldb = D.d;
+  g.N = D.d_ff;
+  g.K = D.d;
+  g.out = hid;
+  g.ldo = D.d_ff;
+  g.act = 1;
+  const int nb = D.gated ? 2 : 1;
+  g.grid = gemm_grid(dt, nb, h->num_cu);
+  hipError_t e;
+  {
+    ProfScope ps(h, SFFN_K_DENSE_GATEUP, stream);
+    e = launch_gemm(dt, nb, false, dt == kBF16 ? kEpiHiddenBF16 : kEpiStoreF32, g, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "dense gate/up GEMM");
+  // y = H W_d
+  GemmArgs g2 = {};
+  g2.A = hid;
+  g2.lda = D.d_ff;
+  g2.M = (int)T;
+  g2.B0 = wd;
+  g2.ldb = D.d;
+  g2.N = D.d;
+  g2.K = D.d_ff;
+  g2.out = y;
+  g2.ldo = D.d;
+  g2.grid = gemm_grid(dt, 1, h->num_cu);
+  {
+    ProfScope ps(h, SFFN_K_DENSE_DOWN, stream);
+    e = launch_gemm(dt, 1, true, kEpiStoreF32, g2, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "dense down GEMM");
+  return SFFN_OK;
+}
+
+sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, const void* w_up,
+                         const void* w_down, int64_t T, float* y, const sffn_twell* tw,
+                         int32_t mode, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!h) return SFFN_E_ARG;
+  const sffn_desc& D = h->desc;
+  if (mode != SFFN_SPARSE && mode != SFFN_DENSE) return fail(h, SFFN_E_ARG, "unknown mode");
+  if (T < 0 || T > (int64_t)1 << 30) return fail(h, SFFN_E_ARG, "T out of range");
+  if (T == 0) return SFFN_OK;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_down) || !aligned16(y))
+    return fail(h, SFFN_E_ARG, "x, w_gate, w_down and y must be non-null 16-byte aligned pointers");
+  if (D.gated ? !aligned16(w_up) : w_up != nullptr)
+    return fail(h, SFFN_E_ARG, "w_up must be a 16-byte aligned pointer iff the layer is gated");
+  if (mode == SFFN_DENSE && tw) return fail(h, SFFN_E_ARG, "dense mode takes no TwELL");
+  if (tw && !twell_ok(tw))
+    return fail(h, SFFN_E_ARG, "TwELL buffers must be non-null and 16-byte aligned");
+  const Layout L = layout(h, T, mode == SFFN_SPARSE ? SFFN_OP_FORWARD_SPARSE : SFFN_OP_FORWARD_DENSE);
+  if (!ws || ws_bytes < L.total || ((uintptr_t)ws % kAlign) != 0)
+    return fail(h, SFFN_E_ARG, "workspace missing, too small or not 256-byte aligned");
+  if (mode == SFFN_DENSE) return forward_dense(h, x, w_gate, w_up, w_down, T, y, ws, L, stream);
+
+  const Dtype dt = dt_of(h);
+  sffn_twell t;
+  if (tw) {
+    t = *tw;
+  } else {
+    t.val = at<float>(ws, L.tw_val);
+    t.idx = at<uint16_t>(ws, L.tw_idx);
+    t.cnt = at<int32_t>(ws, L.tw_cnt);
+    t.row_flag = at<uint8_t>(ws, L.tw_flag);
+    t.flagged = at<int32_t>(ws, L.tw_list);
+    t.n_flagged = at<int32_t>(ws, L.tw_nf);
+  }
+  const int ow = ovf_words(T);
+  uint32_t* ovf = at<uint32_t>(ws, L.ovf);
+
+  // 1. gate GEMM, ReLU + TwELL pack + overflow bits in the epilogue
+  GemmArgs g = {};
+  g.A = x;
+  g.lda = D.d;
+  g.M = (int)T;
+  g.B0 = w_gate;
+  g.ldb = D.d;
+  g.N = D.d_ff;
+  g.K = D.d;
+  g.tw_val = t.val;
+  g.tw_idx = t.idx;
+  g.tw_cnt = t.cnt;
+  g.ovf = ovf;
+  g.C = D.twell_cap;
+  g.n_t = h->n_t;
+  g.ovf_words = ow;
+  g.grid = gemm_grid(dt, 1, h->num_cu);
+  hipError_t e;
+  {
+    ProfScope ps(h, SFFN_K_GATE_TWELL, stream);
+    e = launch_gemm(dt, 1, false, kEpiTwell, g, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "gate GEMM + TwELL");
+  // 2. flagged rows
+  {
+    ProfScope ps(h, SFFN_K_FLAGS, stream);
+    e = launch_flags(ovf, h->n_t, ow, T, t.row_flag, t.flagged, t.n_flagged, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "flags");
+  // 3. sparse up/down over the unflagged rows
+  {
+    ProfScope ps(h, SFFN_K_SPARSE_UPDOWN, stream);
+    e = launch_sparse_updown(dt, D.gated != 0, x, w_up, w_down, t.val, t.idx, t.cnt, t.row_flag,
+                             T, D.d, h->n_t, D.twell_cap, y, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "sparse up/down");
+  // 4. dense path for the flagged rows: hidden rows, then down projection
+  void* hid = at<char>(ws, L.hid);
+  GemmArgs f = {};
+  f.A = x;
+  f.lda = D.d;
+  f.a_rows = t.flagged;
+  f.m_dev = t.n_flagged;
+  f.B0 = w_gate;
+  f.B1 = w_up;
+  f.ldb = D.d;
+  f.N = D.d_ff;
+  f.K = D.d;
+  f.out = hid;
+  f.act = 1;
+  const int nb = D.gated ? 2 : 1;
+  f.grid = gemm_grid(dt, nb, h->num_cu);
+  {
+    ProfScope ps(h, SFFN_K_FLAG_GATEUP, stream);
+    if (dt == kBF16) {
+      f.ldo = 2 * (int64_t)D.d_ff;
+      f.lo_off = D.d_ff;
+      e = launch_gemm(dt, nb, false, kEpiHiddenSplit, f, stream);
+    } else {
+      f.ldo = D.d_ff;
+      e = launch_gemm(dt, nb, false, kEpiStoreF32, f, stream);
+    }
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "flagged gate/up GEMM");
+  GemmArgs f2 = {};
+  f2.A = hid;
+  f2.m_dev = t.n_flagged;
+  f2.B0 = w_down;
+  f2.ldb = D.d;
+  f2.N = D.d;
+  if (dt == kBF16) {
+    // [H_hi | H_lo] x [W_d ; W_d]: K = 2F with the B index wrapped at F
+    f2.lda = 2 * (int64_t)D.d_ff;
+    f2.K = 2 * D.d_ff;
+    f2.kwrap = D.d_ff;
+  } else {
+    f2.lda = D.d_ff;
+    f2.K = D.d_ff;
+  }
+  f2.out = y;
+  f2.ldo = D.d;
+  f2.out_rows = t.flagged;
+  f2.part = at<float>(ws, L.part);
+  f2.split_target = h->num_cu;
+  const int nkt = f2.K / (dt == kBF16 ? 64 : 32);
+  f2.split_max = std::min(kSplitMax, nkt);
+  f2.grid = gemm_grid(dt, 1, h->num_cu);
+  {
+    ProfScope ps(h, SFFN_K_FLAG_DOWN, stream);
+    e = launch_gemm(dt, 1, true, kEpiStoreF32, f2, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "flagged down GEMM");
+  {
+    ProfScope ps(h, SFFN_K_SPLITK_REDUCE, stream);
+    e = launch_splitk_reduce(f2, y, D.d, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "split-K reduce");
+  return SFFN_OK;
+}
+
+static void drop_records(sffn_handle* h) {
+  for (auto& r : h->recs) {
+    h->pool.push_back(r.a);
+    h->pool.push_back(r.b);
+  }
+  h->recs.clear();
+}
+
+sffn_status sffn_profile_enable(sffn_handle* h, int32_t enable) {
+  if (!h) return SFFN_E_ARG;
+  h->prof = enable != 0;
+  if (!h->prof) drop_records(h);
+  for (int k = 0; k < SFFN_K_COUNT; ++k) {
+    h->tot_ms[k] = 0;
+    h->launches[k] = 0;
+  }
+  return SFFN_OK;
+}
+
+sffn_status sffn_profile_read(sffn_handle* h, double* total_ms, int32_t* launches, int32_t n) {
+  if (!h || n < 0 || (n > 0 && (!total_ms || !launches))) return SFFN_E_ARG;
+  sffn_status st = SFFN_OK;
+  for (auto& r : h->recs) {
+    float ms = 0.0f;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) {
+      st = hip_fail(h, e, "profile events");
+      continue;
+    }
+    h->tot_ms[r.k] += ms;
+    h->launches[r.k] += 1;
+  }
+  drop_records(h);
+  for (int k = 0; k < n; ++k) {
+    total_ms[k] = k < SFFN_K_COUNT ? h->tot_ms[k] : 0.0;
+    launches[k] = k < SFFN_K_COUNT ? h->launches[k] : 0;
+  }
+  for (int k = 0; k < SFFN_K_COUNT; ++k) {
+    h->tot_ms[k] = 0;
+    h->launches[k] = 0;
+  }
+  return st;
+}
+
+const char* sffn_kernel_name(int32_t k) {
+  static const char* names[SFFN_K_COUNT] = {
+      "gate_gemm_twell", "flags",        "sparse_updown", "flagged_gateup", "flagged_down",
+      "splitk_reduce",   "dense_gateup", "dense_down",    "pack_twell",     "gate_preact"};
+  return (k >= 0 && k < SFFN_K_COUNT) ? names[k] : "";
+}
+
+sffn_status sffn_check(sffn_handle* h, hipStream_t stream) {
+  if (!h) return SFFN_E_ARG;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(h, e, "stream");
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(h, e, "async");
+  return SFFN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,393 @@
+// MFMA GEMM for gfx950 with the epilogues the feedforward layer needs.
+//
+// C[M, N] = A[M, K] * B^T, A row-major with k contiguous, B either [N, K]
+// (k contiguous: W_gate and W_up stored neuron-major) or [K, N] (n
+// contiguous: W_down stored neuron-major, used by the down projection).
+// bf16 operands use v_mfma_f32_32x32x16_bf16; fp32 operands use the full
+// precision v_mfma_f32_32x32x2_f32, so an fp32 layer never rounds to a
+// narrower type.
+//
+// Block tile 128 x 128, 256 threads as 2 x 2 waves of 64 x 64 (2 x 2 MFMA
+// 32 x 32 tiles each). Each stage holds 128 bytes of K per row (64 bf16 or
+// 32 fp32) for A and every B operand; stages are double-buffered in LDS
+// with the next stage prefetched into registers while the current one is
+// multiplied. LDS rows are 8 chunks of 16 bytes with the chunk index XORed
+// by (row & 7), so the 16-byte fragment reads of 8 consecutive rows hit
+// distinct banks. A [K, N] operand is transposed in registers on its way
+// into LDS, so every fragment read is the same 16-byte k-contiguous load.
+//
+// The grid is persistent: each workgroup walks a strided list of tiles.
+// Consecutive workgroup ids are placed on different XCDs by the hardware,
+// so tiles are first split into one contiguous range per XCD and, inside
+// it, ordered in groups of 8 M-tiles so that the workgroups running at the
+// same time on one XCD share A rows and B columns in its L2.
+#include "sffn_internal.hpp"
+
+namespace sffn {
+namespace {
+
+constexpr int BM = 128;
+constexpr int BN = 128;
+constexpr int NT = 256;
+constexpr int ROWB = 128;                 // bytes of K per LDS row per stage
+constexpr int TILEB = BM * ROWB;          // 16 KB per operand per stage
+constexpr int LDC = BN + 4;               // fp32 epilogue tile pitch
+constexpr int NXCD = 8;
+constexpr int GROUP_M = 8;
+
+template <typename E> struct ET;
+template <> struct ET<uint16_t> { static constexpr int EPC = 8; static constexpr int BK = 64; };
+template <> struct ET<float> { static constexpr int EPC = 4; static constexpr int BK = 32; };
+
+template <int NB>
+constexpr int smem_bytes() {
+  constexpr int main_b = 2 * (1 + NB) * TILEB;
+  constexpr int epi_b = BM * LDC * 4;
+  return main_b > epi_b ? main_b : epi_b;
+}
+
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * ROWB + ((chunk ^ (row & 7)) << 4);
+}
+
+__device__ __forceinline__ u32x4_t ld16(const char* p) { return *(const u32x4_t*)p; }
+__device__ __forceinline__ u32x2_t ld8(const char* p) { return *(const u32x2_t*)p; }
+
+// Number of K splits for a (possibly device-sized) problem.
+// The host keeps split_max <= the number of K stages, so every split owns
+// at least one stage.
+__device__ __forceinline__ int num_splits(const GemmArgs& g, int mt, int ntl) {
+  if (g.part == nullptr) return 1;
+  int s = g.split_target / (mt * ntl);
+  if (s > g.split_max) s = g.split_max;
+  return s < 1 ? 1 : s;
+}
+
+template <typename E>
+__device__ __forceinline__ void mfma_step(const u32x4_t& a, const u32x4_t& b, f32x16_t& c);
+
+template <>
+__device__ __forceinline__ void mfma_step<uint16_t>(const u32x4_t& a, const u32x4_t& b, f32x16_t& c) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                              __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ void mfma_step<float>(const u32x4_t& a, const u32x4_t& b, f32x16_t& c) {
+  // lane half h holds k = 4*(2s+h) .. +3; the four MFMAs each take one of
+  // them, A and B agreeing on which k every lane half contributes.
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[e]), __uint_as_float(b[e]), c, 0, 0, 0);
+}
+
+template <typename E, int NB, bool BT, int EPI>
+__global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
+  constexpr int BK = ET<E>::BK;
+  constexpr int STAGE = (1 + NB) * TILEB;
+  __shared__ __align__(16) char smem[smem_bytes<NB>()];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wr = wave >> 1;
+  const int wc = wave & 1;
+
+  const int M = g.m_dev ? *g.m_dev : g.M;
+  if (M <= 0) return;
+  const int mt = (M + BM - 1) / BM;
+  const int ntl = g.N / BN;
+  const int nkt = g.K / BK;
+  const int S = (EPI == kEpiStoreF32) ? num_splits(g, mt, ntl) : 1;
+  const int ntiles = mt * ntl * S;
+  const int Mpad = mt * BM;
+
+  // XCD-contiguous tile ranges
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % NXCD;
+  const int G8 = G / NXCD;
+  const int local = blockIdx.x / NXCD;
+  const int per = (ntiles + NXCD - 1) / NXCD;
+  const int t_begin = xcd * per;
+  const int t_end = min(ntiles, t_begin + per);
+
+  const char* Ab = (const char*)g.A;
+  const char* Bb[2] = {(const char*)g.B0, (const char*)g.B1};
+  const int64_t lda_b = g.lda * (int64_t)sizeof(E);
+  const int64_t ldb_b = g.ldb * (int64_t)sizeof(E);
+
+  for (int L = t_begin + local; L < t_end; L += G8) {
+    // decode (split, m-tile, n-tile) with grouped M ordering
+    const int ks = L / (mt * ntl);
+    const int r = L - ks * mt * ntl;
+    const int grp = r / (GROUP_M * ntl);
+    const int first_m = grp * GROUP_M;
+    const int gsz = min(mt - first_m, GROUP_M);
+    const int rr = r - grp * GROUP_M * ntl;
+    const int tm = first_m + rr % gsz;
+    const int tn = rr / gsz;
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int kt0 = (int)((int64_t)ks * nkt / S);
+    const int kt1 = (int)((int64_t)(ks + 1) * nkt / S);
+
+    // ---- per-thread global addresses
+    const int lrow = tid >> 3;   // + 32*i
+    const int lch = tid & 7;
+    const char* a_src[4];
+    bool a_ok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = m0 + lrow + 32 * i;
+      a_ok[i] = m < M;
+      int64_t pr = a_ok[i] ? (g.a_rows ? g.a_rows[m] : m) : 0;
+      a_src[i] = Ab + pr * lda_b + lch * 16;
+    }
+    // B, k-contiguous: rows n0 + lrow + 32 i; B, n-contiguous: see below
+    const int bg = tid & 31;     // n group of 4
+    const int bkg = tid >> 5;    // k group
+    constexpr int RK = ET<E>::EPC;  // k rows per thread when transposing
+
+    u32x4_t ra[4];
+    u32x4_t rb[NB][4];
+    u32x2_t rbt[NB][8];
+
+    auto load_stage = [&](int kt) {
+      const int64_t ka = (int64_t)kt * BK * sizeof(E);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ra[i] = a_ok[i] ? ld16(a_src[i] + ka) : u32x4_t{0, 0, 0, 0};
+      int64_t kb = (int64_t)kt * BK;
+      if (g.kwrap > 0) kb %= g.kwrap;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (!BT) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int n = n0 + lrow + 32 * i;
+            rb[nb][i] = ld16(Bb[nb] + n * ldb_b + kb * sizeof(E) + lch * 16);
+          }
+        } else {
+          // rows k = kb + bkg*RK + q, columns n0 + 4*bg .. +3
+          const char* p = Bb[nb] + (kb + bkg * RK) * ldb_b + (int64_t)(n0 + 4 * bg) * sizeof(E);
+          if constexpr (sizeof(E) == 2) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) rbt[nb][q] = ld8(p + q * ldb_b);
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) rb[nb][q] = ld16(p + q * ldb_b);
+          }
+        }
+      }
+    };
+
+    auto store_stage = [&](int st) {
+      char* base = smem + st * STAGE;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(u32x4_t*)(base + lds_off(lrow + 32 * i, lch)) = ra[i];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        char* bbase = base + (1 + nb) * TILEB;
+        if constexpr (!BT) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) *(u32x4_t*)(bbase + lds_off(lrow + 32 * i, lch)) = rb[nb][i];
+        } else if constexpr (sizeof(E) == 2) {
+          // 8 k rows x 4 bf16 columns -> 4 n rows x 8 k
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            u32x4_t o;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const uint32_t r0 = rbt[nb][2 * p][c >> 1];
+              const uint32_t r1 = rbt[nb][2 * p + 1][c >> 1];
+              o[p] = (c & 1) ? ((r0 >> 16) | (r1 & 0xFFFF0000u)) : ((r0 & 0xFFFFu) | (r1 << 16));
+            }
+            *(u32x4_t*)(bbase + lds_off(4 * bg + c, bkg)) = o;
+          }
+        } else {
+          // 4 k rows x 4 fp32 columns -> 4 n rows x 4 k
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            u32x4_t o = {rb[nb][0][c], rb[nb][1][c], rb[nb][2][c], rb[nb][3][c]};
+            *(u32x4_t*)(bbase + lds_off(4 * bg + c, bkg)) = o;
+          }
+        }
+      }
+    };
+
+    f32x16_t acc[NB][2][2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) acc[nb][i][j][q] = 0.0f;
+
+    __syncthreads();  // LDS free (previous tile's epilogue done)
+    if (kt0 < kt1) {
+      load_stage(kt0);
+      store_stage(0);
+    }
+    __syncthreads();
+
+    for (int kt = kt0; kt < kt1; ++kt) {
+      const int st = (kt - kt0) & 1;
+      const bool more = kt + 1 < kt1;
+      if (more) load_stage(kt + 1);
+      const char* sa = smem + st * STAGE;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int ch = 2 * s + (lane >> 5);
+        u32x4_t af[2];
+        u32x4_t bfr[NB][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int row = wr * 64 + i * 32 + (lane & 31);
+          af[i] = *(const u32x4_t*)(sa + lds_off(row, ch));
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int row = wc * 64 + j * 32 + (lane & 31);
+            bfr[nb][j] = *(const u32x4_t*)(sa + (1 + nb) * TILEB + lds_off(row, ch));
+          }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) mfma_step<E>(af[i], bfr[nb][j], acc[nb][i][j]);
+      }
+      if (more) store_stage(st ^ 1);
+      __syncthreads();
+    }
+
+    // ---- epilogue: accumulators -> fp32 tile in LDS
+    float* sC = (float*)smem;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int row = wr * 64 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+          const int col = wc * 64 + j * 32 + (lane & 31);
+          float v;
+          if constexpr (NB == 2) {
+            const float zv = acc[0][i][j][q];
+            v = (zv > 0.0f ? zv : 0.0f) * acc[1][i][j][q];
+          } else {
+            v = acc[0][i][j][q];
+            if (EPI != kEpiTwell && g.act) v = v > 0.0f ? v : 0.0f;
+          }
+          sC[row * LDC + col] = v;
+        }
+    __syncthreads();
+
+    uint32_t bits = 0;
+    for (int q = 0; q < 32; ++q) {
+      const int row = wave * 32 + q;
+      const int m = m0 + row;
+      if (m >= M) break;
+      const f32x2_t v = *(const f32x2_t*)(sC + row * LDC + 2 * lane);
+      const int col = n0 + 2 * lane;
+      if constexpr (EPI == kEpiTwell) {
+        const int64_t slot = ((int64_t)m * g.n_t + tn);
+        const int n = twell_pack_row(v[0], v[1], lane, n0, g.C, g.tw_val + slot * g.C,
+                                     g.tw_idx + slot * g.C, g.tw_cnt + slot);
+        bits |= (n > g.C ? 1u : 0u) << q;
+      } else if constexpr (EPI == kEpiStoreF32) {
+        float* dst;
+        if (S > 1) {
+          dst = g.part + ((int64_t)ks * Mpad + m) * g.N;
+        } else {
+          const int64_t orow = g.out_rows ? g.out_rows[m] : m;
+          dst = (float*)g.out + orow * g.ldo;
+        }
+        *(f32x2_t*)(dst + col) = v;
+      } else if constexpr (EPI == kEpiHiddenBF16) {
+        uint16_t* dst = (uint16_t*)g.out + (int64_t)m * g.ldo;
+        *(uint32_t*)(dst + col) = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+      } else {  // kEpiHiddenSplit
+        uint16_t* dst = (uint16_t*)g.out + (int64_t)m * g.ldo;
+        const uint32_t h0 = f32_to_bf16(v[0]);
+        const uint32_t h1 = f32_to_bf16(v[1]);
+        const uint32_t l0 = f32_to_bf16(v[0] - __uint_as_float(h0 << 16));
+        const uint32_t l1 = f32_to_bf16(v[1] - __uint_as_float(h1 << 16));
+        *(uint32_t*)(dst + col) = h0 | (h1 << 16);
+        *(uint32_t*)(dst + g.lo_off + col) = l0 | (l1 << 16);
+      }
+    }
+    if constexpr (EPI == kEpiTwell) {
+      const int word = (m0 + wave * 32) >> 5;
+      if (lane == 0 && m0 + wave * 32 < M) g.ovf[(int64_t)tn * g.ovf_words + word] = bits;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, float* y, int64_t ldy) {
+  const int M = *g.m_dev;
+  if (M <= 0) return;
+  const int mt = (M + BM - 1) / BM;
+  const int ntl = g.N / BN;
+  const int S = num_splits(g, mt, ntl);
+  if (S <= 1) return;
+  const int Mpad = mt * BM;
+  const int n4 = g.N / 4;
+  const int64_t total = (int64_t)M * n4;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int m = (int)(e / n4);
+    const int c = (int)(e - (int64_t)m * n4) * 4;
+    f32x4_t s = *(const f32x4_t*)(g.part + (int64_t)m * g.N + c);
+    for (int k = 1; k < S; ++k) s += *(const f32x4_t*)(g.part + ((int64_t)k * Mpad + m) * g.N + c);
+    *(f32x4_t*)(y + (int64_t)g.out_rows[m] * ldy + c) = s;
+  }
+}
+
+template <typename E, int NB, bool BT, int EPI>
+hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_kernel<E, NB, BT, EPI>), dim3(g.grid), dim3(NT), 0, s, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int gemm_grid(Dtype, int nb, int num_cu) {
+  // workgroups resident per CU given the LDS footprint (160 KB per CU)
+  const int lds = nb == 2 ? smem_bytes<2>() : smem_bytes<1>();
+  int per_cu = (160 * 1024) / lds;
+  if (per_cu < 1) per_cu = 1;
+  int g = num_cu * per_cu;
+  return (g / NXCD) * NXCD;
+}
+
+hipError_t launch_gemm(Dtype dt, int nb, bool bt, Epi epi, const GemmArgs& g, hipStream_t s) {
+#define SFFN_GEMM_CASE(E, NB_, BT_, EPI_) \
+  if (nb == NB_ && bt == BT_ && epi == EPI_) return launch_t<E, NB_, BT_, EPI_>(g, s);
+  if (dt == kBF16) {
+    SFFN_GEMM_CASE(uint16_t, 1, false, kEpiTwell)
+    SFFN_GEMM_CASE(uint16_t, 1, false, kEpiStoreF32)
+    SFFN_GEMM_CASE(uint16_t, 1, false, kEpiHiddenBF16)
+    SFFN_GEMM_CASE(uint16_t, 1, false, kEpiHiddenSplit)
+    SFFN_GEMM_CASE(uint16_t, 2, false, kEpiHiddenBF16)
+    SFFN_GEMM_CASE(uint16_t, 2, false, kEpiHiddenSplit)
+    SFFN_GEMM_CASE(uint16_t, 1, true, kEpiStoreF32)
+  } else {
+    SFFN_GEMM_CASE(float, 1, false, kEpiTwell)
+    SFFN_GEMM_CASE(float, 1, false, kEpiStoreF32)
+    SFFN_GEMM_CASE(float, 2, false, kEpiStoreF32)
+    SFFN_GEMM_CASE(float, 1, true, kEpiStoreF32)
+  }
+#undef SFFN_GEMM_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_splitk_reduce(const GemmArgs& g, float* y, int64_t ldy, hipStream_t s) {
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(g.grid), dim3(256), 0, s, g, y, ldy);
+  return hipGetLastError();
+}
+
+}  // namespace sffn

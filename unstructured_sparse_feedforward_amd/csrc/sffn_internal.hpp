@@ -1,0 +1,149 @@
+// Internal declarations shared by the library's translation units:
+// vector types, wave-level helpers, the TwELL row packer and the launcher
+// entry points that the C ABI (api.hip) calls.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace sffn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kTile = 128;  // TwELL tile width W
+
+// ---------------------------------------------------------------- bf16 bits
+
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// float32 -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------- wave ops
+
+// Sum over the 64 lanes, result in every lane. Rows of 16 lanes are reduced
+// with DPP (quad swaps, half-row and row mirrors), then the four row sums
+// are read out of lanes 0/16/32/48 and added in a fixed order.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xF, 0xF, true);  // row_half_mirror
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xF, 0xF, true);  // row_mirror
+  int iv = __float_as_int(v);
+  float s0 = __int_as_float(__builtin_amdgcn_readlane(iv, 0));
+  float s1 = __int_as_float(__builtin_amdgcn_readlane(iv, 16));
+  float s2 = __int_as_float(__builtin_amdgcn_readlane(iv, 32));
+  float s3 = __int_as_float(__builtin_amdgcn_readlane(iv, 48));
+  return (s0 + s1) + (s2 + s3);
+}
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
+
+// ---------------------------------------------------------------- TwELL row
+
+// Pack one (row, tile) of 128 pre-activations held as two per lane
+// (columns 2*lane and 2*lane+1 of the tile) into TwELL: the positive
+// entries in ascending column order go to slots 0..C-1, the remaining
+// slots get (0, 0), and the uncapped count is returned to every lane.
+// Wave-uniform control flow; one wave per call.
+__device__ __forceinline__ int twell_pack_row(float z0, float z1, int lane, int col0, int C,
+                                              float* __restrict__ val, uint16_t* __restrict__ idx,
+                                              int32_t* __restrict__ cnt_out) {
+  const bool p0 = z0 > 0.0f;
+  const bool p1 = z1 > 0.0f;
+  const uint64_t b0 = __ballot(p0);
+  const uint64_t b1 = __ballot(p1);
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int r0 = __popcll(b0 & below) + __popcll(b1 & below);
+  const int r1 = r0 + (p0 ? 1 : 0);
+  const int n = __popcll(b0) + __popcll(b1);
+  if (p0 && r0 < C) { val[r0] = z0; idx[r0] = (uint16_t)(col0 + 2 * lane); }
+  if (p1 && r1 < C) { val[r1] = z1; idx[r1] = (uint16_t)(col0 + 2 * lane + 1); }
+  // padding: slots n..C-1 (C <= 128, two slots per lane)
+  for (int s = lane; s < C; s += kWave) {
+    if (s >= n) { val[s] = 0.0f; idx[s] = 0; }
+  }
+  if (lane == 0) *cnt_out = n;
+  return n;
+}
+
+// ---------------------------------------------------------------- launchers
+
+enum Dtype { kF32 = 0, kBF16 = 1 };
+
+// Epilogues of the MFMA GEMM.
+enum Epi {
+  kEpiTwell = 0,   // ReLU + TwELL pack + overflow bits (gate GEMM)
+  kEpiStoreF32,    // C (or split-K partial) stored as float32, optional row scatter
+  kEpiHiddenBF16,  // H = act(C) rounded to bf16 (dense baseline hidden)
+  kEpiHiddenSplit, // H = act(C) stored as bf16 hi and lo parts (flagged rows)
+};
+
+struct GemmArgs {
+  // A: [M, K] row-major (k contiguous); logical row m reads physical row
+  // a_rows[m] when a_rows is set. M comes from *m_dev when set.
+  const void* A;
+  int64_t lda;
+  const int32_t* a_rows;
+  int M;
+  const int32_t* m_dev;
+  // B: [N, K] (k contiguous) or, when b_trans, [K, N] (n contiguous).
+  // With two B operands (gate and up) both share A. The k index into B is
+  // taken modulo kwrap when kwrap > 0.
+  const void* B0;
+  const void* B1;
+  int64_t ldb;
+  int N;
+  int K;
+  int kwrap;
+  // output
+  void* out;
+  int64_t ldo;
+  const int32_t* out_rows;   // scatter of stored rows (kEpiStoreF32)
+  int act;                   // 1: ReLU on the single-B result; dual B is always ReLU(z)*u
+  int lo_off;                // column offset of the lo part (kEpiHiddenSplit)
+  // split-K (kEpiStoreF32 with a device M): the number of splits S is
+  // chosen on the device so that tiles * S stays near split_target; when
+  // S > 1 the partials go to part[S][Mpad][N] and a reduce kernel adds them.
+  int split_target;
+  int split_max;
+  float* part;
+  // TwELL (kEpiTwell)
+  float* tw_val;
+  uint16_t* tw_idx;
+  int32_t* tw_cnt;
+  uint32_t* ovf;             // [n_t][ovf_words] overflow bits, bit r of word w = row 32w+r
+  int C;
+  int n_t;
+  int ovf_words;
+  int grid;                  // persistent grid size
+};
+
+hipError_t launch_gemm(Dtype dt, int nb, bool b_trans, Epi epi, const GemmArgs& g,
+                       hipStream_t s);
+int gemm_grid(Dtype dt, int nb, int num_cu);
+
+// split-K reduce: y[rows[m]][n] = sum_s part[s][m][n] for m < *m_dev.
+hipError_t launch_splitk_reduce(const GemmArgs& g, float* y, int64_t ldy, hipStream_t s);
+
+hipError_t launch_pack(const float* z, int64_t T, int F, int C, float* val, uint16_t* idx,
+                       int32_t* cnt, uint32_t* ovf, int ovf_words, hipStream_t s);
+hipError_t launch_flags(const uint32_t* ovf, int n_t, int ovf_words, int64_t T, uint8_t* row_flag,
+                        int32_t* flagged, int32_t* n_flagged, hipStream_t s);
+hipError_t launch_sparse_updown(Dtype dt, bool gated, const void* x, const void* wu,
+                                const void* wd, const float* val, const uint16_t* idx,
+                                const int32_t* cnt, const uint8_t* row_flag, int64_t T, int d,
+                                int n_t, int C, float* y, hipStream_t s);
+
+}  // namespace sffn

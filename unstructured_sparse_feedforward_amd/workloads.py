@@ -123,9 +123,10 @@ def round_f32(a: np.ndarray) -> np.ndarray:
 def round_bf16(a32: np.ndarray) -> np.ndarray:
     """float32 -> bfloat16 round-to-nearest-even, returned as float32."""
     u = np.ascontiguousarray(a32, dtype=np.float32).view(np.uint32)
-    u = u.astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return (r.astype(np.uint32) << 16).view(np.float32)
+    # finite inputs: u + 0x8000 stays below 2**32
+    r = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    r &= np.uint32(0xFFFF0000)
+    return r.view(np.float32)
 
 
 def _to_dtype(a64: np.ndarray, dtype: str) -> np.ndarray:
