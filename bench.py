@@ -153,13 +153,15 @@ def main():
         return t / n if n else float("nan")
 
     t_gate = avg(prof, "gate_gemm_twell")
-    t_gath = avg(prof, "sparse_updown")
+    # the sparse up/down projection is two kernels (per-slice partial dot
+    # products, then the down projection); its time is their sum
+    t_gath = (avg(prof, "sparse_up") if W.gated else 0.0) + avg(prof, "sparse_down")
     peak_mm = PEAK_BF16_TFLOPS if W.dtype == "bf16" else PEAK_F32_TFLOPS
     roof_gate = {"bound": "mfma", "kernel": "gate_gemm_twell",
                  "achieved": gate_flops / (t_gate * 1e-3) / 1e12, "peak": peak_mm,
                  "unit": "TFLOP/s", "traffic": None, "avg_ms": t_gate}
     roof_gate["frac"] = roof_gate["achieved"] / peak_mm
-    roof_gath = {"bound": "hbm", "kernel": "sparse_updown",
+    roof_gath = {"bound": "hbm", "kernel": "sparse_up + sparse_down",
                  "achieved": gather_bytes / (t_gath * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
                  "unit": "GB/s", "traffic": None, "avg_ms": t_gath,
                  "algorithmic_bytes": gather_bytes, "active_pairs": pairs}

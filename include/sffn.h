@@ -123,7 +123,8 @@ typedef struct sffn_twell {
 /* Create a handle for the current HIP device. Validates the descriptor
  * (SFFN_E_ARG / SFFN_E_UNSUPPORTED) before touching the device; returns
  * SFFN_E_UNSUPPORTED when the current device is not gfx950 and SFFN_E_HIP
- * when no device can be queried. Allocates only host memory. */
+ * when no device can be queried. Allocates only host memory. Calls on the
+ * handle must be made with the same device current. */
 sffn_status sffn_create(const sffn_desc* desc, sffn_handle** out);
 
 /* Destroy a handle (NULL is allowed). */
@@ -190,15 +191,17 @@ sffn_status sffn_check(sffn_handle* h, hipStream_t stream);
  */
 #define SFFN_K_GATE_TWELL    0  /* gate GEMM with the ReLU + TwELL epilogue */
 #define SFFN_K_FLAGS         1  /* overflow flags and flagged-row list */
-#define SFFN_K_SPARSE_UPDOWN 2  /* fused sparse up/down projection */
-#define SFFN_K_FLAG_GATEUP   3  /* gate/up GEMM of the flagged rows */
+#define SFFN_K_SPARSE_UP     2  /* sparse up projection: per-slice partial dots */
+#define SFFN_K_FLAG_GATEUP   3  /* gate/up GEMM of the flagged rows (+ split-K combine) */
 #define SFFN_K_FLAG_DOWN     4  /* down GEMM of the flagged rows (split-K) */
 #define SFFN_K_SPLITK_REDUCE 5  /* split-K reduction into the flagged rows */
 #define SFFN_K_DENSE_GATEUP  6  /* dense mode: gate/up GEMM */
 #define SFFN_K_DENSE_DOWN    7  /* dense mode: down GEMM */
 #define SFFN_K_PACK          8  /* stand-alone TwELL pack */
 #define SFFN_K_GATE_PREACT   9  /* gate GEMM writing z */
-#define SFFN_K_COUNT        10
+#define SFFN_K_ROWS         10  /* per-row route + ELL compaction of the TwELL */
+#define SFFN_K_SPARSE_DOWN  11  /* sparse down projection into y */
+#define SFFN_K_COUNT        12
 sffn_status sffn_profile_enable(sffn_handle* h, int32_t enable);
 sffn_status sffn_profile_read(sffn_handle* h, double* total_ms, int32_t* launches, int32_t n);
 /* Static name of a kernel id ("" if out of range). */

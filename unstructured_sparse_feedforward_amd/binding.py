@@ -34,7 +34,7 @@ EXPORTS = ("sffn_create", "sffn_destroy", "sffn_last_error", "sffn_status_string
            "sffn_workspace_bytes", "sffn_pack_twell", "sffn_gate_preact",
            "sffn_forward", "sffn_check", "sffn_profile_enable", "sffn_profile_read",
            "sffn_kernel_name")
-SFFN_K_COUNT = 10
+SFFN_K_COUNT = 12
 
 
 class SffnDesc(ctypes.Structure):

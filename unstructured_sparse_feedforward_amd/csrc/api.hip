@@ -73,6 +73,7 @@ constexpr int kSplitMax = 16;
 // Workspace layout. Every region starts at a 256-byte boundary.
 struct Layout {
   size_t ovf = 0, tw_val = 0, tw_idx = 0, tw_cnt = 0, tw_flag = 0, tw_list = 0, tw_nf = 0;
+  size_t ell_a = 0, ell_idx = 0, ell_cnt = 0, bk = 0, upart = 0;
   size_t hid = 0, part = 0, total = 0;
 };
 
@@ -85,10 +86,19 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
     o = align_up(o + bytes);
     return at;
   };
-  if (op == SFFN_OP_PACK || op == SFFN_OP_FORWARD_SPARSE) {
+  if (op == SFFN_OP_PACK) {
     L.ovf = take((size_t)nt * ovf_words(T) * 4);
   }
   if (op == SFFN_OP_FORWARD_SPARSE) {
+    // ELL rows of capacity n_t * C: lossless for every unflagged row
+    const int64_t K = nt * C, Kp = (K + 7) / 8 * 8;
+    int ns, epl;
+    slice_shape(dt_of(h), (int)d, &ns, &epl);
+    L.ell_a = take((size_t)T * K * 4);
+    L.ell_idx = take((size_t)T * K * 2);
+    L.ell_cnt = take((size_t)T * 4);
+    L.bk = take((size_t)T);
+    L.upart = take((size_t)ns * T * Kp * 4);
     L.tw_val = take((size_t)T * nt * C * 4);
     L.tw_idx = take((size_t)T * nt * C * 2);
     L.tw_cnt = take((size_t)T * nt * 4);
@@ -97,11 +107,14 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
     L.tw_nf = take(4);
     // hidden rows of flagged tokens: bf16 hi|lo [T, 2F] or fp32 [T, F]
     L.hid = take((size_t)T * F * 4);
-    // split-K partials of the flagged down projection: at most
-    // split_target / (d / 128) row tiles of 128 rows
-    const int ntl = (int)(d / 128);
-    const int tiles = std::max(1, h->num_cu / ntl);
-    L.part = take((size_t)tiles * 128 * d * 4);
+    // split-K partials of the flagged rows' GEMMs (used one after the
+    // other): a split problem has at most split_target / n_tiles row tiles
+    // of 128 rows; the hidden GEMM keeps one partial set per B operand
+    const int tiles_d = std::max(1, h->num_cu / (int)(d / 128));
+    const int tiles_h = std::max(1, h->num_cu / (int)(F / 128));
+    const size_t part_d = (size_t)tiles_d * 128 * d;
+    const size_t part_h = (size_t)2 * tiles_h * 128 * F;
+    L.part = take(std::max(part_d, part_h) * 4);
   }
   if (op == SFFN_OP_FORWARD_DENSE) {
     L.hid = take((size_t)T * F * esize(h));
@@ -131,7 +144,7 @@ struct ProfScope {
   hipStream_t s;
   hipEvent_t a = nullptr;
   ProfScope(sffn_handle* h_, int k_, hipStream_t s_) : h(h_), k(k_), s(s_) {
-    if (h->prof && (a = take_event(h)) != nullptr) hipEventRecord(a, s);
+    if (h->prof && (a = take_event(h)) != nullptr) (void)hipEventRecord(a, s);
   }
   ~ProfScope() {
     if (!a) return;
@@ -140,7 +153,7 @@ struct ProfScope {
       h->pool.push_back(a);
       return;
     }
-    hipEventRecord(b, s);
+    (void)hipEventRecord(b, s);
     h->recs.push_back({k, a, b});
   }
 };
@@ -182,10 +195,10 @@ sffn_status sffn_create(const sffn_desc* desc, sffn_handle** out) {
 void sffn_destroy(sffn_handle* h) {
   if (!h) return;
   for (auto& r : h->recs) {
-    hipEventDestroy(r.a);
-    hipEventDestroy(r.b);
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
   }
-  for (auto e : h->pool) hipEventDestroy(e);
+  for (auto e : h->pool) (void)hipEventDestroy(e);
   delete h;
 }
 
@@ -337,10 +350,10 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, cons
     t.flagged = at<int32_t>(ws, L.tw_list);
     t.n_flagged = at<int32_t>(ws, L.tw_nf);
   }
-  const int ow = ovf_words(T);
-  uint32_t* ovf = at<uint32_t>(ws, L.ovf);
+  const int K = h->n_t * D.twell_cap;
+  const int Kp = (K + 7) / 8 * 8;
 
-  // 1. gate GEMM, ReLU + TwELL pack + overflow bits in the epilogue
+  // 1. gate GEMM, ReLU + TwELL pack in the epilogue
   GemmArgs g = {};
   g.A = x;
   g.lda = D.d;
@@ -352,10 +365,8 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, cons
   g.tw_val = t.val;
   g.tw_idx = t.idx;
   g.tw_cnt = t.cnt;
-  g.ovf = ovf;
   g.C = D.twell_cap;
   g.n_t = h->n_t;
-  g.ovf_words = ow;
   g.grid = gemm_grid(dt, 1, h->num_cu);
   hipError_t e;
   {
@@ -363,21 +374,39 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, cons
     e = launch_gemm(dt, 1, false, kEpiTwell, g, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "gate GEMM + TwELL");
-  // 2. flagged rows
+
+  // 2. per-row route and ELL compaction (capacity n_t * C: only rows
+  //    whose TwELL overflowed go to the dense path)
+  EllArgs ea = {};
+  ea.val = t.val;
+  ea.idx = t.idx;
+  ea.cnt = t.cnt;
+  ea.T = T;
+  ea.n_t = h->n_t;
+  ea.C = D.twell_cap;
+  ea.K = K;
+  ea.ell_a = at<float>(ws, L.ell_a);
+  ea.ell_idx = at<uint16_t>(ws, L.ell_idx);
+  ea.ell_cnt = at<int32_t>(ws, L.ell_cnt);
+  ea.row_flag = t.row_flag;
+  ea.bk = at<uint8_t>(ws, L.bk);
+  {
+    ProfScope ps(h, SFFN_K_ROWS, stream);
+    e = launch_rows(ea, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "row compaction");
+
+  // 3. dense path for the flagged rows: their ascending list, the hidden
+  //    rows H = ReLU(x W_g) * (x W_u) (split-K over the few rows, then a
+  //    combine that stores H as bf16 hi + lo, or fp32), and y = H W_d
+  //    scattered into the rows (split-K + reduce)
   {
     ProfScope ps(h, SFFN_K_FLAGS, stream);
-    e = launch_flags(ovf, h->n_t, ow, T, t.row_flag, t.flagged, t.n_flagged, stream);
+    e = launch_backup_list(ea.bk, T, t.flagged, t.n_flagged, nullptr, stream);
   }
-  if (e != hipSuccess) return hip_fail(h, e, "flags");
-  // 3. sparse up/down over the unflagged rows
-  {
-    ProfScope ps(h, SFFN_K_SPARSE_UPDOWN, stream);
-    e = launch_sparse_updown(dt, D.gated != 0, x, w_up, w_down, t.val, t.idx, t.cnt, t.row_flag,
-                             T, D.d, h->n_t, D.twell_cap, y, stream);
-  }
-  if (e != hipSuccess) return hip_fail(h, e, "sparse up/down");
-  // 4. dense path for the flagged rows: hidden rows, then down projection
+  if (e != hipSuccess) return hip_fail(h, e, "flagged list");
   void* hid = at<char>(ws, L.hid);
+  float* part = at<float>(ws, L.part);
   GemmArgs f = {};
   f.A = x;
   f.lda = D.d;
@@ -390,18 +419,17 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, cons
   f.K = D.d;
   f.out = hid;
   f.act = 1;
+  f.ldo = dt == kBF16 ? 2 * (int64_t)D.d_ff : (int64_t)D.d_ff;
+  f.lo_off = D.d_ff;
+  f.part = part;
+  f.split_target = h->num_cu;
+  f.split_max = std::min(kSplitMax, D.d / (dt == kBF16 ? 64 : 32));
   const int nb = D.gated ? 2 : 1;
   f.grid = gemm_grid(dt, nb, h->num_cu);
   {
     ProfScope ps(h, SFFN_K_FLAG_GATEUP, stream);
-    if (dt == kBF16) {
-      f.ldo = 2 * (int64_t)D.d_ff;
-      f.lo_off = D.d_ff;
-      e = launch_gemm(dt, nb, false, kEpiHiddenSplit, f, stream);
-    } else {
-      f.ldo = D.d_ff;
-      e = launch_gemm(dt, nb, false, kEpiStoreF32, f, stream);
-    }
+    e = launch_gemm(dt, nb, false, kEpiHiddenSplitK, f, stream);
+    if (e == hipSuccess) e = launch_hidden_combine(dt, nb, f, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "flagged gate/up GEMM");
   GemmArgs f2 = {};
@@ -422,7 +450,7 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, cons
   f2.out = y;
   f2.ldo = D.d;
   f2.out_rows = t.flagged;
-  f2.part = at<float>(ws, L.part);
+  f2.part = part;
   f2.split_target = h->num_cu;
   const int nkt = f2.K / (dt == kBF16 ? 64 : 32);
   f2.split_max = std::min(kSplitMax, nkt);
@@ -437,6 +465,31 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, cons
     e = launch_splitk_reduce(f2, y, D.d, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "split-K reduce");
+
+  // 4. sparse up/down over the ELL rows, d sliced across the XCDs
+  SliceArgs sa = {};
+  sa.x = x;
+  sa.wu = w_up;
+  sa.wd = w_down;
+  sa.ell_idx = ea.ell_idx;
+  sa.ell_a = ea.ell_a;
+  sa.ell_cnt = ea.ell_cnt;
+  sa.bk = ea.bk;
+  sa.T = T;
+  sa.d = D.d;
+  sa.K = K;
+  sa.Kp = Kp;
+  sa.upart = at<float>(ws, L.upart);
+  sa.y = y;
+  if (D.gated) {
+    ProfScope ps(h, SFFN_K_SPARSE_UP, stream);
+    e = launch_updown(dt, true, 0, sa, stream);
+  }
+  if (e == hipSuccess) {
+    ProfScope ps(h, SFFN_K_SPARSE_DOWN, stream);
+    e = launch_updown(dt, D.gated != 0, 1, sa, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "sparse up/down");
   return SFFN_OK;
 }
 
@@ -487,8 +540,9 @@ sffn_status sffn_profile_read(sffn_handle* h, double* total_ms, int32_t* launche
 
 const char* sffn_kernel_name(int32_t k) {
   static const char* names[SFFN_K_COUNT] = {
-      "gate_gemm_twell", "flags",        "sparse_updown", "flagged_gateup", "flagged_down",
-      "splitk_reduce",   "dense_gateup", "dense_down",    "pack_twell",     "gate_preact"};
+      "gate_gemm_twell", "flags",        "sparse_up",  "flagged_gateup", "flagged_down",
+      "splitk_reduce",   "dense_gateup", "dense_down", "pack_twell",     "gate_preact",
+      "rows",            "sparse_down"};
   return (k >= 0 && k < SFFN_K_COUNT) ? names[k] : "";
 }
 

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
   const int mt = (M + BM - 1) / BM;
   const int ntl = g.N / BN;
   const int nkt = g.K / BK;
-  const int S = (EPI == kEpiStoreF32) ? num_splits(g, mt, ntl) : 1;
+  const int S = (EPI == kEpiStoreF32 || EPI == kEpiHiddenSplitK) ? num_splits(g, mt, ntl) : 1;
   const int ntiles = mt * ntl * S;
   const int Mpad = mt * BM;
 
@@ -264,6 +264,27 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
       __syncthreads();
     }
 
+    // ---- split-K partials of the hidden GEMM: raw accumulators of every
+    //      B operand straight from registers, 32 consecutive floats per
+    //      half-wave row
+    if constexpr (EPI == kEpiHiddenSplitK) {
+      if (S > 1) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int q = 0; q < 16; ++q) {
+                const int m = m0 + wr * 64 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+                const int n = n0 + wc * 64 + j * 32 + (lane & 31);
+                if (m < M) g.part[((int64_t)(nb * S + ks) * Mpad + m) * g.N + n] = acc[nb][i][j][q];
+              }
+        continue;
+      }
+    }
+
     // ---- epilogue: accumulators -> fp32 tile in LDS
     float* sC = (float*)smem;
 #pragma unroll
@@ -310,7 +331,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
       } else if constexpr (EPI == kEpiHiddenBF16) {
         uint16_t* dst = (uint16_t*)g.out + (int64_t)m * g.ldo;
         *(uint32_t*)(dst + col) = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-      } else {  // kEpiHiddenSplit
+      } else if (EPI == kEpiHiddenSplitK && sizeof(E) == 4) {
+        // fp32 layer: H kept in fp32
+        *(f32x2_t*)((float*)g.out + (int64_t)m * g.ldo + col) = v;
+      } else {  // bf16 hidden as hi + lo
         uint16_t* dst = (uint16_t*)g.out + (int64_t)m * g.ldo;
         const uint32_t h0 = f32_to_bf16(v[0]);
         const uint32_t h1 = f32_to_bf16(v[1]);
@@ -322,7 +346,50 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
     }
     if constexpr (EPI == kEpiTwell) {
       const int word = (m0 + wave * 32) >> 5;
-      if (lane == 0 && m0 + wave * 32 < M) g.ovf[(int64_t)tn * g.ovf_words + word] = bits;
+      if (g.ovf && lane == 0 && m0 + wave * 32 < M) g.ovf[(int64_t)tn * g.ovf_words + word] = bits;
+    }
+  }
+}
+
+// Sum the split-K partials of the hidden GEMM and apply its epilogue:
+// H = ReLU(z) * u (two B operands) or ReLU(z), stored as bf16 hi and lo
+// parts (bf16 layers) or float32. A no-op when the GEMM did not split.
+template <typename E, int NB>
+__global__ __launch_bounds__(256) void hidden_combine_kernel(GemmArgs g) {
+  const int M = *g.m_dev;
+  if (M <= 0) return;
+  const int mt = (M + BM - 1) / BM;
+  const int ntl = g.N / BN;
+  const int S = num_splits(g, mt, ntl);
+  if (S <= 1) return;
+  const int Mpad = mt * BM;
+  const int n2 = g.N / 2;
+  const int64_t total = (int64_t)M * n2;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int m = (int)(e / n2);
+    const int c = (int)(e - (int64_t)m * n2) * 2;
+    f32x2_t z = {0.0f, 0.0f}, u = {0.0f, 0.0f};
+    for (int k = 0; k < S; ++k) {
+      z += *(const f32x2_t*)(g.part + ((int64_t)k * Mpad + m) * g.N + c);
+      if (NB == 2) u += *(const f32x2_t*)(g.part + ((int64_t)(S + k) * Mpad + m) * g.N + c);
+    }
+    f32x2_t h;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float r = z[q] > 0.0f ? z[q] : 0.0f;
+      h[q] = NB == 2 ? r * u[q] : r;
+    }
+    if constexpr (sizeof(E) == 4) {
+      *(f32x2_t*)((float*)g.out + (int64_t)m * g.ldo + c) = h;
+    } else {
+      uint16_t* dst = (uint16_t*)g.out + (int64_t)m * g.ldo;
+      const uint32_t h0 = f32_to_bf16(h[0]);
+      const uint32_t h1 = f32_to_bf16(h[1]);
+      const uint32_t l0 = f32_to_bf16(h[0] - __uint_as_float(h0 << 16));
+      const uint32_t l1 = f32_to_bf16(h[1] - __uint_as_float(h1 << 16));
+      *(uint32_t*)(dst + c) = h0 | (h1 << 16);
+      *(uint32_t*)(dst + g.lo_off + c) = l0 | (l1 << 16);
     }
   }
 }
@@ -375,14 +442,30 @@ hipError_t launch_gemm(Dtype dt, int nb, bool bt, Epi epi, const GemmArgs& g, hi
     SFFN_GEMM_CASE(uint16_t, 2, false, kEpiHiddenBF16)
     SFFN_GEMM_CASE(uint16_t, 2, false, kEpiHiddenSplit)
     SFFN_GEMM_CASE(uint16_t, 1, true, kEpiStoreF32)
+    SFFN_GEMM_CASE(uint16_t, 1, false, kEpiHiddenSplitK)
+    SFFN_GEMM_CASE(uint16_t, 2, false, kEpiHiddenSplitK)
   } else {
     SFFN_GEMM_CASE(float, 1, false, kEpiTwell)
     SFFN_GEMM_CASE(float, 1, false, kEpiStoreF32)
     SFFN_GEMM_CASE(float, 2, false, kEpiStoreF32)
     SFFN_GEMM_CASE(float, 1, true, kEpiStoreF32)
+    SFFN_GEMM_CASE(float, 1, false, kEpiHiddenSplitK)
+    SFFN_GEMM_CASE(float, 2, false, kEpiHiddenSplitK)
   }
 #undef SFFN_GEMM_CASE
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_hidden_combine(Dtype dt, int nb, const GemmArgs& g, hipStream_t s) {
+  const dim3 grid(g.grid), block(256);
+  if (dt == kBF16) {
+    if (nb == 2) hipLaunchKernelGGL((hidden_combine_kernel<uint16_t, 2>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((hidden_combine_kernel<uint16_t, 1>), grid, block, 0, s, g);
+  } else {
+    if (nb == 2) hipLaunchKernelGGL((hidden_combine_kernel<float, 2>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((hidden_combine_kernel<float, 1>), grid, block, 0, s, g);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_splitk_reduce(const GemmArgs& g, float* y, int64_t ldy, hipStream_t s) {

@@ -88,6 +88,9 @@ enum Epi {
   kEpiStoreF32,    // C (or split-K partial) stored as float32, optional row scatter
   kEpiHiddenBF16,  // H = act(C) rounded to bf16 (dense baseline hidden)
   kEpiHiddenSplit, // H = act(C) stored as bf16 hi and lo parts (flagged rows)
+  kEpiHiddenSplitK,// as kEpiHiddenSplit (fp32 H for fp32 layers), or split-K
+                   // partials of every B operand when the device-sized
+                   // problem splits K (then a combine kernel finishes it)
 };
 
 struct GemmArgs {
@@ -136,14 +139,55 @@ int gemm_grid(Dtype dt, int nb, int num_cu);
 
 // split-K reduce: y[rows[m]][n] = sum_s part[s][m][n] for m < *m_dev.
 hipError_t launch_splitk_reduce(const GemmArgs& g, float* y, int64_t ldy, hipStream_t s);
+// split-K combine of the hidden GEMM (kEpiHiddenSplitK): sums the partials
+// and writes H; a no-op when the GEMM did not split.
+hipError_t launch_hidden_combine(Dtype dt, int nb, const GemmArgs& g, hipStream_t s);
 
 hipError_t launch_pack(const float* z, int64_t T, int F, int C, float* val, uint16_t* idx,
                        int32_t* cnt, uint32_t* ovf, int ovf_words, hipStream_t s);
 hipError_t launch_flags(const uint32_t* ovf, int n_t, int ovf_words, int64_t T, uint8_t* row_flag,
                         int32_t* flagged, int32_t* n_flagged, hipStream_t s);
-hipError_t launch_sparse_updown(Dtype dt, bool gated, const void* x, const void* wu,
-                                const void* wd, const float* val, const uint16_t* idx,
-                                const int32_t* cnt, const uint8_t* row_flag, int64_t T, int d,
-                                int n_t, int C, float* y, hipStream_t s);
+// TwELL -> ELL rows + dense-backup routing (one wave per token row).
+struct EllArgs {
+  const float* val;       // TwELL [T, n_t, C]
+  const uint16_t* idx;
+  const int32_t* cnt;     // [T, n_t]
+  int64_t T;
+  int n_t;
+  int C;
+  int K;                  // ELL capacity
+  float* ell_a;           // [T, K] out
+  uint16_t* ell_idx;      // [T, K] out
+  int32_t* ell_cnt;       // [T] out (0 for backup rows)
+  uint8_t* row_flag;      // [T] out, TwELL overflow (nullable)
+  uint8_t* bk;            // [T] out, 1 = dense backup row
+};
+hipError_t launch_rows(const EllArgs& a, hipStream_t s);
+// Ascending list of the rows with bk[t] != 0, their count and (nullable)
+// every row's backup slot (-1 for ELL rows). One workgroup.
+hipError_t launch_backup_list(const uint8_t* bk, int64_t T, int32_t* brow, int32_t* n_backup,
+                              int32_t* slot, hipStream_t s);
+
+// Sparse up/down over ELL rows, d cut into NS slices (one per XCD group).
+struct SliceArgs {
+  const void* x;          // [T, d]
+  const void* wu;         // [F, d] (gated)
+  const void* wd;         // [F, d]
+  const uint16_t* ell_idx;
+  const float* ell_a;
+  const int32_t* ell_cnt;
+  const uint8_t* bk;      // rows written by the dense path are skipped
+  int64_t T;
+  int d;
+  int K;                  // ELL row stride
+  int Kp;                 // partial-dot row stride (K rounded up to 8)
+  float* upart;           // [NS, T, Kp] per-slice partial dot products
+  float* ell_u;           // [T, K] u per slot (nullable)
+  float* y;               // [T, d]
+};
+void slice_shape(Dtype dt, int d, int* ns, int* epl);
+// phase 0: per-slice partial dot products (gated layers only);
+// phase 1: down projection into y.
+hipError_t launch_updown(Dtype dt, bool gated, int phase, const SliceArgs& a, hipStream_t s);
 
 }  // namespace sffn

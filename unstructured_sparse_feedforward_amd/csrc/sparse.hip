@@ -1,0 +1,332 @@
+// Row compaction (TwELL -> ELL + dense-backup routing) and the sparse
+// up/down projection over the compacted rows.
+//
+// The Hybrid format of "Sparser, Faster, Lighter Transformer Language
+// Models" routes each token row either to a compact ELL matrix (few
+// non-zeros) or to a dense backup (many non-zeros) (gist.science explainer,
+// 2. Methodology A, Hybrid Format for Training; wispaper blog, 2. The Hybrid
+// Training Algorithm). The same conversion with an ELL capacity of n_t * C
+// serves inference: then only rows whose TwELL overflowed go to the backup.
+//
+// Up/down projection (same explainer, 2. Methodology B: fused up/down
+// projection): for every active (neuron j, value a) of a row, u = x . W_u[j],
+// h = a * u, y += h * W_d[j]. MI355X has 8 XCDs with a private 4 MB L2
+// each and a workgroup with id b runs on XCD b % 8. The model dimension is
+// cut into NS slices (8 at d = 2048) and slice s is processed only by
+// workgroups with b % NS == s, so each XCD's L2 holds one slice of W_up and
+// W_down (5632 x 256 bf16 = 2.9 MB each at the 1.5B shape) instead of
+// streaming whole 8 KB neuron rows from HBM/MALL. Phase 1 writes per-slice
+// partial dot products (one float per active pair and slice); phase 2 sums
+// them in slice order (deterministic), scales by the activation and adds
+// the neuron's down weights into the row's y slice. No dense hidden tensor
+// is formed.
+#include "sffn_internal.hpp"
+
+namespace sffn {
+namespace {
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// One wave per token row: count its positives, decide the route, and if
+// the row stays sparse, concatenate its TwELL tile lists (ascending neuron)
+// into ELL slots 0..nnz-1.
+__global__ __launch_bounds__(256) void rows_kernel(EllArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int32_t* cnt = a.cnt + t * a.n_t;
+  int nnz = 0;
+  bool over = false;
+  for (int b = lane; b < a.n_t; b += 64) {
+    const int c = cnt[b];
+    nnz += c;
+    over |= c > a.C;
+  }
+  nnz = wave_sum_int(nnz);
+  const bool flag = __ballot(over) != 0;
+  const bool backup = flag || nnz > a.K;
+  if (lane == 0) {
+    if (a.row_flag) a.row_flag[t] = flag ? 1 : 0;
+    a.bk[t] = backup ? 1 : 0;
+    a.ell_cnt[t] = backup ? 0 : nnz;
+  }
+  if (backup || nnz == 0) return;
+  const int total = a.n_t * a.C;
+  const int64_t src = t * total;
+  const int64_t dst = t * (int64_t)a.K;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int run = 0;
+  for (int q0 = 0; q0 < total && run < nnz; q0 += 64) {
+    const int q = q0 + lane;
+    bool act = false;
+    if (q < total) {
+      const int b = q / a.C;
+      act = (q - b * a.C) < cnt[b];
+    }
+    const uint64_t m = __ballot(act);
+    if (act) {
+      const int k = run + __popcll(m & below);
+      a.ell_idx[dst + k] = a.idx[src + q];
+      a.ell_a[dst + k] = a.val[src + q];
+    }
+    run += __popcll(m);
+  }
+}
+
+// One workgroup: list the backup rows in ascending order, their count and,
+// when requested, every row's backup slot (-1 for ELL rows).
+__global__ __launch_bounds__(1024) void backup_list_kernel(const uint8_t* __restrict__ bk,
+                                                           int64_t T, int32_t* __restrict__ brow,
+                                                           int32_t* __restrict__ n_backup,
+                                                           int32_t* __restrict__ slot) {
+  constexpr int RPT = 16;
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int carry = 0;
+  for (int64_t base = 0; base < T; base += 1024 * RPT) {
+    const int64_t r0 = base + (int64_t)tid * RPT;
+    uint32_t bits = 0;
+    if (r0 + RPT <= T) {
+      const u32x4_t v = *(const u32x4_t*)(bk + r0);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) bits |= ((v[i >> 2] >> (8 * (i & 3))) & 0xFFu) ? (1u << i) : 0u;
+    } else {
+      for (int i = 0; r0 + i < T; ++i) bits |= bk[r0 + i] ? (1u << i) : 0u;
+    }
+    const int c = __popc(bits);
+    int inc = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += v;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int wbase = 0, total = 0;
+    for (int k = 0; k < 16; ++k) {
+      if (k < wave) wbase += wsum[k];
+      total += wsum[k];
+    }
+    int off = carry + wbase + inc - c;
+    for (int i = 0; i < RPT && r0 + i < T; ++i) {
+      if (bits & (1u << i)) {
+        brow[off] = (int32_t)(r0 + i);
+        if (slot) slot[r0 + i] = off;
+        ++off;
+      } else if (slot) {
+        slot[r0 + i] = -1;
+      }
+    }
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) *n_backup = carry;
+}
+
+template <typename E, int EPL> struct Vec;
+template <> struct Vec<uint16_t, 4> {
+  typedef u32x2_t raw;
+  __device__ static void cvt(const raw& v, float* o) {
+    o[0] = bf16lo(v[0]); o[1] = bf16hi(v[0]); o[2] = bf16lo(v[1]); o[3] = bf16hi(v[1]);
+  }
+};
+template <> struct Vec<uint16_t, 8> {
+  typedef u32x4_t raw;
+  __device__ static void cvt(const raw& v, float* o) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { o[2 * k] = bf16lo(v[k]); o[2 * k + 1] = bf16hi(v[k]); }
+  }
+};
+template <> struct Vec<float, 4> {
+  typedef u32x4_t raw;
+  __device__ static void cvt(const raw& v, float* o) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = __uint_as_float(v[k]);
+  }
+};
+
+constexpr int GRP = 32;  // active pairs in flight per wave
+
+// One butterfly exchange at lane distance W over the first 2*HALF values:
+// the lane keeps one half (the upper one if bit W of its lane id is set),
+// sends the other half to its partner and adds what it receives. Template
+// recursion keeps every register index a compile-time constant.
+template <int W, int HALF>
+__device__ __forceinline__ void butterfly(float* v, int lane) {
+  const bool up = (lane & W) != 0;
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) {
+    const float send = up ? v[i] : v[i + HALF];
+    const float keep = up ? v[i + HALF] : v[i];
+    v[i] = keep + __shfl_xor(send, W, 64);
+  }
+  if constexpr (HALF > 1) butterfly<W / 2, HALF / 2>(v, lane);
+}
+
+// Wave totals of 32 per-lane values at once: five butterfly exchanges
+// (distances 32, 16, 8, 4, 2) and a last one between lane pairs. On return
+// lane l holds the total of value (l >> 1) & 31. The order of additions is
+// fixed.
+__device__ __forceinline__ float wave_sum32(float* v, int lane) {
+  butterfly<32, 16>(v, lane);
+  return v[0] + __shfl_xor(v[0], 1, 64);
+}
+
+// Phase 1: upart[s][t][k] = x_t[slice s] . W_u[j_k][slice s].
+template <typename E, int NS, int EPL>
+__global__ __launch_bounds__(256) void up_partial_kernel(SliceArgs a) {
+  using V = Vec<E, EPL>;
+  const int lane = threadIdx.x & 63;
+  const int s = blockIdx.x % NS;
+  const int64_t t = (int64_t)(blockIdx.x / NS) * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int n = a.ell_cnt[t];
+  if (n == 0) return;
+  const int d = NS * 64 * EPL;
+  const int64_t col = (int64_t)s * 64 * EPL + lane * EPL;
+  float xr[EPL];
+  V::cvt(*(const typename V::raw*)((const E*)a.x + t * d + col), xr);
+  const E* wu = (const E*)a.wu + col;
+  const uint16_t* li = a.ell_idx + t * (int64_t)a.K;
+  float* up = a.upart + ((int64_t)s * a.T + t) * a.Kp;
+  for (int k0 = 0; k0 < n; k0 += GRP) {
+    const int m = min(GRP, n - k0);
+    const int jl = li[k0 + min(lane, m - 1)];
+    typename V::raw w[GRP];
+#pragma unroll
+    for (int q = 0; q < GRP; ++q) {
+      const int j = __builtin_amdgcn_readlane(jl, q);
+      w[q] = *(const typename V::raw*)(wu + (int64_t)j * d);
+    }
+    // keep every load of the group in flight before the first use
+    __builtin_amdgcn_sched_barrier(0);
+    float p[GRP];
+#pragma unroll
+    for (int q = 0; q < GRP; ++q) {
+      float f[EPL];
+      V::cvt(w[q], f);
+      float acc = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc = fmaf(xr[e], f[e], acc);
+      p[q] = acc;
+    }
+    const float u = wave_sum32(p, lane);
+    const int q = lane >> 1;
+    if ((lane & 1) == 0 && q < m) up[k0 + q] = u;
+  }
+}
+
+// Phase 2: y_t[slice s] = sum_k a_k * (sum_s' upart[s'][t][k]) * W_d[j_k][slice s]
+// (non-gated: h_k = a_k). Rows routed to the dense backup are skipped.
+template <typename E, int NS, int EPL, bool GATED>
+__global__ __launch_bounds__(256) void down_kernel(SliceArgs a) {
+  using V = Vec<E, EPL>;
+  const int lane = threadIdx.x & 63;
+  const int s = blockIdx.x % NS;
+  const int64_t t = (int64_t)(blockIdx.x / NS) * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  if (a.bk[t]) return;
+  const int n = a.ell_cnt[t];
+  const int d = NS * 64 * EPL;
+  const int64_t col = (int64_t)s * 64 * EPL + lane * EPL;
+  const E* wd = (const E*)a.wd + col;
+  const int64_t rb = t * (int64_t)a.K;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+  for (int k0 = 0; k0 < n; k0 += GRP) {
+    const int m = min(GRP, n - k0);
+    const int kk = k0 + min(lane, m - 1);
+    const int jl = a.ell_idx[rb + kk];
+    float hl = a.ell_a[rb + kk];
+    if constexpr (GATED) {
+      float u = 0.0f;
+#pragma unroll
+      for (int q = 0; q < NS; ++q) u += a.upart[((int64_t)q * a.T + t) * a.Kp + kk];
+      if (a.ell_u && s == 0 && lane < m) a.ell_u[rb + kk] = u;
+      hl *= u;
+    }
+    if (lane >= m) hl = 0.0f;
+    typename V::raw w[GRP];
+#pragma unroll
+    for (int q = 0; q < GRP; ++q) {
+      const int j = __builtin_amdgcn_readlane(jl, q);
+      w[q] = *(const typename V::raw*)(wd + (int64_t)j * d);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < GRP; ++q) {
+      const float h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hl), q));
+      float f[EPL];
+      V::cvt(w[q], f);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(h, f[e], acc[e]);
+    }
+  }
+  float* yo = a.y + t * d + col;
+#pragma unroll
+  for (int e = 0; e < EPL; e += 4) *(f32x4_t*)(yo + e) = f32x4_t{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+}
+
+template <typename E, int NS, int EPL>
+hipError_t launch_slices(const SliceArgs& a, bool gated, int phase, hipStream_t st) {
+  const dim3 grid((unsigned)(NS * ((a.T + 3) / 4)));
+  if (phase == 0) {
+    hipLaunchKernelGGL((up_partial_kernel<E, NS, EPL>), grid, dim3(256), 0, st, a);
+  } else if (gated) {
+    hipLaunchKernelGGL((down_kernel<E, NS, EPL, true>), grid, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((down_kernel<E, NS, EPL, false>), grid, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+void slice_shape(Dtype, int d, int* ns, int* epl) {
+  int n = d / 256;
+  if (n > 8) n = 8;
+  if (n < 1) n = 1;
+  *ns = n;
+  *epl = d / (64 * n);
+}
+
+hipError_t launch_rows(const EllArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(rows_kernel, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_backup_list(const uint8_t* bk, int64_t T, int32_t* brow, int32_t* n_backup,
+                              int32_t* slot, hipStream_t s) {
+  hipLaunchKernelGGL(backup_list_kernel, dim3(1), dim3(1024), 0, s, bk, T, brow, n_backup, slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_updown(Dtype dt, bool gated, int phase, const SliceArgs& a, hipStream_t s) {
+  int ns, epl;
+  slice_shape(dt, a.d, &ns, &epl);
+#define SFFN_SL(E, NS_, EPL_) \
+  if (ns == NS_ && epl == EPL_) return launch_slices<E, NS_, EPL_>(a, gated, phase, s);
+  if (dt == kBF16) {
+    SFFN_SL(uint16_t, 1, 4)
+    SFFN_SL(uint16_t, 2, 4)
+    SFFN_SL(uint16_t, 4, 4)
+    SFFN_SL(uint16_t, 8, 4)
+    SFFN_SL(uint16_t, 8, 8)
+  } else {
+    SFFN_SL(float, 1, 4)
+    SFFN_SL(float, 2, 4)
+    SFFN_SL(float, 4, 4)
+    SFFN_SL(float, 8, 4)
+  }
+#undef SFFN_SL
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sffn

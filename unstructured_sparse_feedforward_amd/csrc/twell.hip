@@ -1,14 +1,10 @@
-// TwELL kernels: the stand-alone pack, the overflow-flag list and the
-// fused sparse up/down projection.
+// TwELL kernels: the stand-alone pack of a given pre-activation tensor and
+// the overflow-flag list.
 //
 // TwELL (tile-wise ELLPACK) keeps, for every (token row, 128-column tile)
 // of the gate activations, a fixed-capacity list of (value, neuron) plus a
 // count ("Sparser, Faster, Lighter Transformer Language Models", gist.science
-// explainer, 2. Methodology A). The fused up/down projection walks each
-// token's list, takes the dot product of the token with the neuron's up
-// weights and adds the scalar times the neuron's down weights to the
-// token's output, so the dense hidden tensor never exists in memory (same
-// page, 2. Methodology B).
+// explainer, 2. Methodology A).
 #include "sffn_internal.hpp"
 
 namespace sffn {
@@ -99,160 +95,6 @@ __global__ __launch_bounds__(1024) void flags_kernel(const uint32_t* __restrict_
   if (tid == 0) *n_flagged = carry;
 }
 
-template <typename E> struct SE;
-template <> struct SE<uint16_t> {
-  static constexpr int EPC = 8;
-  __device__ static void unpack(const u32x4_t& v, float* o) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) { o[2 * k] = bf16lo(v[k]); o[2 * k + 1] = bf16hi(v[k]); }
-  }
-};
-template <> struct SE<float> {
-  static constexpr int EPC = 4;
-  __device__ static void unpack(const u32x4_t& v, float* o) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = __uint_as_float(v[k]);
-  }
-};
-
-// One wave per token. The lane owns elements c*CH + lane*EPC + e of the
-// d-vector (c < NCH chunks, e < EPC), so each 16-byte load of a weight row
-// is coalesced across the wave. The token's TwELL slots are scanned 64 at
-// a time; the active ones are visited in ascending neuron order, two per
-// step so that four weight rows are in flight at once.
-template <typename E, int NCH, bool GATED>
-__global__ __launch_bounds__(256) void sparse_updown_kernel(
-    const E* __restrict__ x, const E* __restrict__ wu, const E* __restrict__ wd,
-    const float* __restrict__ val, const uint16_t* __restrict__ idx,
-    const int32_t* __restrict__ cnt, const uint8_t* __restrict__ row_flag, int64_t T, int d,
-    int n_t, int C, float* __restrict__ y) {
-  constexpr int EPC = SE<E>::EPC;
-  constexpr int CH = 64 * EPC;
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  if (row_flag[t]) return;  // the dense path writes flagged rows
-
-  float xr[NCH][EPC];
-  float yr[NCH][EPC];
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const u32x4_t v = *(const u32x4_t*)(x + t * d + c * CH + lane * EPC);
-    SE<E>::unpack(v, xr[c]);
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) yr[c][e] = 0.0f;
-  }
-
-  const int total = n_t * C;
-  const int64_t tb = t * n_t;
-  for (int base = 0; base < total; base += 64) {
-    const int q = base + lane;
-    bool act = false;
-    float a = 0.0f;
-    int j = 0;
-    if (q < total) {
-      const int b = q / C;
-      const int s = q - b * C;
-      if (s < cnt[tb + b]) {
-        a = val[tb * C + q];
-        j = idx[tb * C + q];
-        act = true;
-      }
-    }
-    uint64_t mask = __ballot(act);
-    while (mask) {
-      const int s0 = __ffsll((unsigned long long)mask) - 1;
-      mask &= mask - 1;
-      const bool two = mask != 0;
-      const int s1 = two ? __ffsll((unsigned long long)mask) - 1 : s0;
-      if (two) mask &= mask - 1;
-      const int j0 = __builtin_amdgcn_readlane(j, s0);
-      const int j1 = __builtin_amdgcn_readlane(j, s1);
-      const float a0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), s0));
-      const float a1 = two ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), s1)) : 0.0f;
-
-      u32x4_t d0[NCH], d1[NCH];
-      const E* wd0 = wd + (int64_t)j0 * d + lane * EPC;
-      const E* wd1 = wd + (int64_t)j1 * d + lane * EPC;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        d0[c] = *(const u32x4_t*)(wd0 + c * CH);
-        d1[c] = *(const u32x4_t*)(wd1 + c * CH);
-      }
-      float h0 = a0, h1 = a1;
-      if constexpr (GATED) {
-        u32x4_t u0[NCH], u1[NCH];
-        const E* wu0 = wu + (int64_t)j0 * d + lane * EPC;
-        const E* wu1 = wu + (int64_t)j1 * d + lane * EPC;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          u0[c] = *(const u32x4_t*)(wu0 + c * CH);
-          u1[c] = *(const u32x4_t*)(wu1 + c * CH);
-        }
-        float p0 = 0.0f, p1 = 0.0f;
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-          float w0[EPC], w1[EPC];
-          SE<E>::unpack(u0[c], w0);
-          SE<E>::unpack(u1[c], w1);
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) {
-            p0 = fmaf(xr[c][e], w0[e], p0);
-            p1 = fmaf(xr[c][e], w1[e], p1);
-          }
-        }
-        h0 = a0 * wave_sum(p0);
-        h1 = a1 * wave_sum(p1);
-      }
-#pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        float w0[EPC], w1[EPC];
-        SE<E>::unpack(d0[c], w0);
-        SE<E>::unpack(d1[c], w1);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          yr[c][e] = fmaf(h0, w0[e], yr[c][e]);
-          yr[c][e] = fmaf(h1, w1[e], yr[c][e]);
-        }
-      }
-    }
-  }
-
-  float* yo = y + t * d + lane * EPC;
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-#pragma unroll
-    for (int e = 0; e < EPC; e += 4)
-      *(f32x4_t*)(yo + c * CH + e) = f32x4_t{yr[c][e], yr[c][e + 1], yr[c][e + 2], yr[c][e + 3]};
-  }
-}
-
-template <typename E, bool G>
-hipError_t launch_sparse_t(int nch, const void* x, const void* wu, const void* wd,
-                           const float* val, const uint16_t* idx, const int32_t* cnt,
-                           const uint8_t* row_flag, int64_t T, int d, int n_t, int C, float* y,
-                           hipStream_t s) {
-  const dim3 grid((unsigned)((T + 3) / 4));
-  const E* xe = (const E*)x;
-  const E* ue = (const E*)wu;
-  const E* de = (const E*)wd;
-  switch (nch) {
-#define SFFN_SP_CASE(N)                                                                          \
-  case N:                                                                                        \
-    hipLaunchKernelGGL((sparse_updown_kernel<E, N, G>), grid, dim3(256), 0, s, xe, ue, de, val, \
-                       idx, cnt, row_flag, T, d, n_t, C, y);                                     \
-    break;
-    SFFN_SP_CASE(1)
-    SFFN_SP_CASE(2)
-    SFFN_SP_CASE(4)
-    SFFN_SP_CASE(8)
-#undef SFFN_SP_CASE
-    default:
-      return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_pack(const float* z, int64_t T, int F, int C, float* val, uint16_t* idx,
@@ -268,23 +110,6 @@ hipError_t launch_flags(const uint32_t* ovf, int n_t, int ovf_words, int64_t T, 
   hipLaunchKernelGGL(flags_kernel, dim3(1), dim3(1024), 0, s, ovf, n_t, ovf_words, T, row_flag,
                      flagged, n_flagged);
   return hipGetLastError();
-}
-
-hipError_t launch_sparse_updown(Dtype dt, bool gated, const void* x, const void* wu,
-                                const void* wd, const float* val, const uint16_t* idx,
-                                const int32_t* cnt, const uint8_t* row_flag, int64_t T, int d,
-                                int n_t, int C, float* y, hipStream_t s) {
-  const int ch = dt == kBF16 ? 512 : 256;
-  const int nch = d / ch;
-  if (dt == kBF16)
-    return gated ? launch_sparse_t<uint16_t, true>(nch, x, wu, wd, val, idx, cnt, row_flag, T, d,
-                                                   n_t, C, y, s)
-                 : launch_sparse_t<uint16_t, false>(nch, x, wu, wd, val, idx, cnt, row_flag, T,
-                                                    d, n_t, C, y, s);
-  return gated ? launch_sparse_t<float, true>(nch, x, wu, wd, val, idx, cnt, row_flag, T, d, n_t,
-                                              C, y, s)
-               : launch_sparse_t<float, false>(nch, x, wu, wd, val, idx, cnt, row_flag, T, d, n_t,
-                                               C, y, s);
 }
 
 }  // namespace sffn
