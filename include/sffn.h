@@ -99,9 +99,11 @@ typedef struct sffn_desc {
 /*
  * TwELL buffers (device, caller-owned). n_t = F / W.
  *   val       [T, n_t, C] float32   slot values, the gate pre-activation
- *                                   z[t, j] (> 0) as accumulated in fp32;
- *                                   unused slots hold 0.0
- *   idx       [T, n_t, C] uint16    slot neuron ids j (global); unused 0
+ *                                   z[t, j] (> 0) as accumulated in fp32
+ *   idx       [T, n_t, C] uint16    slot neuron ids j (global)
+ *                                   Slots s >= min(cnt, C) of a (row, tile)
+ *                                   are not written and hold unspecified
+ *                                   values.
  *   cnt       [T, n_t]    int32     true number of positives in the tile
  *                                   (not capped at C)
  *   row_flag  [T]         uint8     1 iff some tile of the row has cnt > C

@@ -59,3 +59,22 @@ def twell_np(tw):
     out["idx"] = out["idx"].view(np.uint16).astype(np.int64)
     out["n_flagged"] = int(out["n_flagged"][0])
     return out
+
+
+def valid_slots(tw):
+    """Mask [T, n_t, C] of the slots a TwELL defines (s < min(cnt, C));
+    the others are unspecified."""
+    C = tw["val"].shape[2]
+    n = np.minimum(tw["cnt"], C)
+    return np.arange(C)[None, None, :] < n[:, :, None]
+
+
+def assert_twell_equal(a, b, flags=True):
+    """Counts equal, and values and indices equal on every defined slot."""
+    assert np.array_equal(a["cnt"], b["cnt"]), "cnt"
+    m = valid_slots(a)
+    assert np.array_equal(a["idx"][m], b["idx"][m]), "idx"
+    assert np.array_equal(np.asarray(a["val"], np.float64)[m], np.asarray(b["val"], np.float64)[m]), "val"
+    if flags:
+        assert np.array_equal(np.asarray(a["row_flag"]).astype(bool),
+                              np.asarray(b["row_flag"]).astype(bool)), "row_flag"

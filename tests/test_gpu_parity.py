@@ -13,8 +13,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (assert_close_bf16, assert_close_f32, dev, layer, math_weights,
-                      rel_fro, twell_np)
+from gpu_util import (assert_close_bf16, assert_close_f32, assert_twell_equal, dev, layer,
+                      math_weights, rel_fro, twell_np)
 from unstructured_sparse_feedforward_amd import SparseFFN
 from unstructured_sparse_feedforward_amd import workloads as wl
 
@@ -43,10 +43,9 @@ def test_pack_bitexact(T, F, C, seed):
     ffn = SparseFFN(512, F, gated=True, twell_cap=C, dtype=torch.bfloat16)
     tw = twell_np(ffn.pack_twell(torch.from_numpy(z).cuda()))
     ref = oracle.pack_twell(z.astype(np.float64), 128, C)
-    assert np.array_equal(tw["cnt"], ref["cnt"])
-    assert np.array_equal(tw["idx"], ref["idx"])
-    assert np.array_equal(tw["val"].astype(np.float64), ref["val"])
-    assert np.array_equal(tw["row_flag"].astype(bool), ref["row_flag"])
+    # counts, flags and every defined slot bit-exact (slots past the count
+    # are unspecified)
+    assert_twell_equal(tw, ref)
     flagged = np.flatnonzero(ref["row_flag"])
     assert tw["n_flagged"] == len(flagged)
     assert np.array_equal(tw["flagged"][:len(flagged)], flagged)
@@ -83,8 +82,7 @@ def test_fused_twell_matches_pack_of_own_z(w, T):
     z = ffn.gate_preact(x, wg)
     tw_p = ffn.pack_twell(z)
     a, b = twell_np(tw_f), twell_np(tw_p)
-    for k in ("val", "idx", "cnt", "row_flag"):
-        assert np.array_equal(a[k], b[k]), k
+    assert_twell_equal(a, b)
     assert a["n_flagged"] == b["n_flagged"]
     assert np.array_equal(a["flagged"][:a["n_flagged"]], b["flagged"][:b["n_flagged"]])
 
@@ -220,8 +218,7 @@ def test_forward_deterministic():
     y2 = ffn.forward(*args, mode="sparse", tw=tw2).clone()
     assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
     a, b = twell_np(tw1), twell_np(tw2)
-    for k in ("val", "idx", "cnt", "row_flag"):
-        assert np.array_equal(a[k], b[k])
+    assert_twell_equal(a, b)
 
 
 def test_empty_batch_is_noop():

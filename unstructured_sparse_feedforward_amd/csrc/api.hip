@@ -261,6 +261,7 @@ sffn_status sffn_gate_preact(sffn_handle* h, const void* x, const void* w_gate, 
   g.K = h->desc.d;
   g.out = z;
   g.ldo = h->desc.d_ff;
+  g.num_cu = h->num_cu;
   g.grid = gemm_grid(dt_of(h), 1, h->num_cu);
   hipError_t e;
   {
@@ -291,6 +292,7 @@ static sffn_status forward_dense(sffn_handle* h, const void* x, const void* wg, 
   g.ldo = D.d_ff;
   g.act = 1;
   const int nb = D.gated ? 2 : 1;
+  g.num_cu = h->num_cu;
   g.grid = gemm_grid(dt, nb, h->num_cu);
   hipError_t e;
   {
@@ -309,6 +311,7 @@ static sffn_status forward_dense(sffn_handle* h, const void* x, const void* wg, 
   g2.K = D.d_ff;
   g2.out = y;
   g2.ldo = D.d;
+  g2.num_cu = h->num_cu;
   g2.grid = gemm_grid(dt, 1, h->num_cu);
   {
     ProfScope ps(h, SFFN_K_DENSE_DOWN, stream);
@@ -367,6 +370,7 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, cons
   g.tw_cnt = t.cnt;
   g.C = D.twell_cap;
   g.n_t = h->n_t;
+  g.num_cu = h->num_cu;
   g.grid = gemm_grid(dt, 1, h->num_cu);
   hipError_t e;
   {
@@ -425,6 +429,7 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, cons
   f.split_target = h->num_cu;
   f.split_max = std::min(kSplitMax, D.d / (dt == kBF16 ? 64 : 32));
   const int nb = D.gated ? 2 : 1;
+  f.num_cu = h->num_cu;
   f.grid = gemm_grid(dt, nb, h->num_cu);
   {
     ProfScope ps(h, SFFN_K_FLAG_GATEUP, stream);
@@ -454,6 +459,7 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, cons
   f2.split_target = h->num_cu;
   const int nkt = f2.K / (dt == kBF16 ? 64 : 32);
   f2.split_max = std::min(kSplitMax, nkt);
+  f2.num_cu = h->num_cu;
   f2.grid = gemm_grid(dt, 1, h->num_cu);
   {
     ProfScope ps(h, SFFN_K_FLAG_DOWN, stream);

@@ -12,8 +12,8 @@
 // 32 fp32) for A and every B operand; stages are double-buffered in LDS
 // with the next stage prefetched into registers while the current one is
 // multiplied. LDS rows are 8 chunks of 16 bytes with the chunk index XORed
-// by (row & 7), so the 16-byte fragment reads of 8 consecutive rows hit
-// distinct banks. A [K, N] operand is transposed in registers on its way
+// by (row >> 1) & 7, so the 16-byte fragment reads of 16 consecutive rows
+// hit distinct banks. A [K, N] operand is transposed in registers on its way
 // into LDS, so every fragment read is the same 16-byte k-contiguous load.
 //
 // The grid is persistent: each workgroup walks a strided list of tiles.
@@ -46,8 +46,13 @@ constexpr int smem_bytes() {
   return main_b > epi_b ? main_b : epi_b;
 }
 
+// 128-byte LDS rows of 8 16-byte chunks. gfx950's LDS serves 16 lanes of a
+// 16-byte read per cycle across 64 banks (256 bytes): two 128-byte rows per
+// bank line, so the chunk is XORed with (row >> 1) & 7 and 16 consecutive
+// rows at the same logical chunk hit 16 distinct bank groups.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * ROWB + ((chunk ^ (row & 7)) << 4);
+  return row * ROWB + ((chunk ^ swz(row)) << 4);
 }
 
 __device__ __forceinline__ u32x4_t ld16(const char* p) { return *(const u32x4_t*)p; }
@@ -432,6 +437,11 @@ int gemm_grid(Dtype, int nb, int num_cu) {
 }
 
 hipError_t launch_gemm(Dtype dt, int nb, bool bt, Epi epi, const GemmArgs& g, hipStream_t s) {
+  if (g.num_cu > 0 && gemm_big_supported(dt, nb, bt, epi, g)) {
+    GemmArgs b = g;
+    b.grid = gemm_big_grid(g, nb);
+    return launch_gemm_big(nb, bt, epi, b, s);
+  }
 #define SFFN_GEMM_CASE(E, NB_, BT_, EPI_) \
   if (nb == NB_ && bt == BT_ && epi == EPI_) return launch_t<E, NB_, BT_, EPI_>(g, s);
   if (dt == kBF16) {

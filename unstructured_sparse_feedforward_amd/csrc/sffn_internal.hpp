@@ -54,9 +54,9 @@ __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u,
 
 // Pack one (row, tile) of 128 pre-activations held as two per lane
 // (columns 2*lane and 2*lane+1 of the tile) into TwELL: the positive
-// entries in ascending column order go to slots 0..C-1, the remaining
-// slots get (0, 0), and the uncapped count is returned to every lane.
-// Wave-uniform control flow; one wave per call.
+// entries in ascending column order go to slots 0..C-1 (slots past the
+// count are left as they are) and the uncapped count is returned to every
+// lane. Wave-uniform control flow; one wave per call.
 __device__ __forceinline__ int twell_pack_row(float z0, float z1, int lane, int col0, int C,
                                               float* __restrict__ val, uint16_t* __restrict__ idx,
                                               int32_t* __restrict__ cnt_out) {
@@ -70,10 +70,6 @@ __device__ __forceinline__ int twell_pack_row(float z0, float z1, int lane, int 
   const int n = __popcll(b0) + __popcll(b1);
   if (p0 && r0 < C) { val[r0] = z0; idx[r0] = (uint16_t)(col0 + 2 * lane); }
   if (p1 && r1 < C) { val[r1] = z1; idx[r1] = (uint16_t)(col0 + 2 * lane + 1); }
-  // padding: slots n..C-1 (C <= 128, two slots per lane)
-  for (int s = lane; s < C; s += kWave) {
-    if (s >= n) { val[s] = 0.0f; idx[s] = 0; }
-  }
   if (lane == 0) *cnt_out = n;
   return n;
 }
@@ -130,11 +126,18 @@ struct GemmArgs {
   int C;
   int n_t;
   int ovf_words;
-  int grid;                  // persistent grid size
+  int grid;                  // persistent grid size (small-tile kernel)
+  int num_cu;                // compute units (large-tile kernel's grid)
 };
 
+// Runs the large-tile bf16 kernel (gemm_big.hip) when it supports the
+// problem (host-sized M, no row gather/scatter, no split-K), else the
+// small-tile kernel.
 hipError_t launch_gemm(Dtype dt, int nb, bool b_trans, Epi epi, const GemmArgs& g,
                        hipStream_t s);
+bool gemm_big_supported(Dtype dt, int nb, bool bt, Epi epi, const GemmArgs& g);
+int gemm_big_grid(const GemmArgs& g, int nb);
+hipError_t launch_gemm_big(int nb, bool bt, Epi epi, const GemmArgs& g, hipStream_t s);
 int gemm_grid(Dtype dt, int nb, int num_cu);
 
 // split-K reduce: y[rows[m]][n] = sum_s part[s][m][n] for m < *m_dev.
