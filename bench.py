@@ -64,6 +64,28 @@ def _timed(fn, steps, warmup, torch, ffn=None):
     return ev / steps, wall / steps, prof
 
 
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary of
+    this workload (profiles/traffic_<workload>.json), for each kernel whose
+    source file still hashes to what was profiled; else None."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        rec = json.load(f)
+    out = {}
+    for kname, k in rec.get("kernels", {}).items():
+        src = os.path.join(ROOT, "unstructured_sparse_feedforward_amd", "csrc", k["source"])
+        try:
+            h = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        except OSError:
+            continue
+        if h == k.get("source_sha256"):
+            out[kname] = k["bytes_per_launch"]
+    return out
+
+
 def cpu_baseline(inp, sample, np):
     """The oracle's sparse forward (gate, TwELL pack, per-token up/down over
     active neurons, dense rows for flagged tokens) on the first `sample`
@@ -99,6 +121,10 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=-1,
                     help="tokens of the oracle CPU baseline sample (-1 = all, 0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="before the timed work, run a plain elementwise copy of MIB MiB "
+                         "(float32 negate into a second buffer) three times, so hardware "
+                         "counters of the run can be scaled against known bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this layer is "
@@ -115,6 +141,14 @@ def main():
     W = {"gated": wl.GATED_1P5B, "small": wl.SMALL_F32, "nongated29": wl.NONGATED[29],
          "nongated108": wl.NONGATED[108], "nongated911": wl.NONGATED[911]}[args.workload]
     torch.cuda.set_device(0)
+    if args.copy_calibration > 0:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     inp = wl.make_inputs(W, seed=args.seed)
     x, wg, wu, wd = (_dev(inp, k, torch, np) for k in ("x", "w_gate", "w_up", "w_down"))
     ffn = SparseFFN(W.d, W.F, gated=W.gated, twell_cap=W.twell_cap, tile=W.tile,
@@ -166,6 +200,11 @@ def main():
                  "unit": "GB/s", "traffic": None, "avg_ms": t_gath,
                  "algorithmic_bytes": gather_bytes, "active_pairs": pairs}
     roof_gath["frac"] = roof_gath["achieved"] / PEAK_HBM_GBS
+    traffic = measured_traffic(W.name)
+    if "gate_gemm_twell" in traffic:
+        roof_gate["traffic"] = traffic["gate_gemm_twell"]
+    if "sparse_up" in traffic and "sparse_down" in traffic:
+        roof_gath["traffic"] = traffic["sparse_up"] + traffic["sparse_down"]
     dominant, other = (roof_gate, roof_gath) if t_gate >= t_gath else (roof_gath, roof_gate)
 
     out = {

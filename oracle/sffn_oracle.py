@@ -23,8 +23,8 @@ Lighter Transformer Language Models" (Cetin et al.):
   * the backward pass restricted to active entries (explainer
     "2. Methodology" B, training kernels: backpropagation).
 
-Weights use the pages' math orientation: w_gate and w_up are d x F,
-w_down is F x d. Readings where the pages leave a step open:
+Weights use the paper's math orientation: w_gate and w_up are d x F,
+w_down is F x d. Readings where the descriptions leave a step open:
 
   * active means strictly Z > 0 (ReLU); zero, -0.0 and NaN are inactive;
   * slots inside a tile are in ascending column order, padded with

@@ -17,7 +17,7 @@ def dev(inp, name):
 
 
 def math_weights(inp):
-    """float64 weights in the pages' orientation: W_g, W_u are d x F and
+    """float64 weights in the paper's math orientation: W_g, W_u are d x F and
     W_d is F x d."""
     wg = inp.w_gate.astype(np.float64).T
     wu = None if inp.w_up is None else inp.w_up.astype(np.float64).T
