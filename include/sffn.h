@@ -70,6 +70,9 @@ typedef int32_t sffn_status;
 #define SFFN_OP_PACK           0
 #define SFFN_OP_FORWARD_SPARSE 1
 #define SFFN_OP_FORWARD_DENSE  2
+#define SFFN_OP_HYBRID         3
+#define SFFN_OP_FORWARD_TRAIN  4
+#define SFFN_OP_BACKWARD       5
 
 typedef struct sffn_handle sffn_handle;
 
@@ -121,6 +124,42 @@ typedef struct sffn_twell {
   int32_t*  flagged;
   int32_t*  n_flagged;
 } sffn_twell;
+
+/*
+ * Hybrid buffers (device, caller-owned): the training-side format of
+ * "2. Methodology" A ("Hybrid Format for Training") on the gist.science
+ * explainer and "2. The Hybrid Training Algorithm" on the wispaper blog.
+ * A row goes to the dense backup iff its total count of positives exceeds
+ * K (desc.ell_cap) or one of its TwELL tiles overflowed C; every other row
+ * keeps its positives as ELL slots 0..ell_cnt-1 in ascending neuron order.
+ *   ell_a      [T, K]   float32  a = z > 0 of each ELL slot
+ *   ell_u      [T, K]   float32  u = x . W_u[j] of each ELL slot (gated
+ *                                layers; written by sffn_forward_train)
+ *   ell_idx    [T, K]   uint16   neuron ids
+ *   ell_cnt    [T]      int32    slots used (0 for backup rows)
+ *                                (slots >= ell_cnt are unspecified)
+ *   slot       [T]      int32    backup slot of the row, -1 for ELL rows
+ *   brow       [max_backup] int32  backup rows in ascending order
+ *   n_backup   [1]      int32    true number of backup rows (may exceed
+ *                                max_backup: then the rows from slot
+ *                                max_backup on were not computed and the
+ *                                result is invalid; see sffn_hybrid_check)
+ *   bk_a       [max_backup, F] float32  ReLU(z) rows of the backup rows
+ *   bk_u       [max_backup, F] float32  u rows of the backup rows (gated)
+ *   max_backup capacity of brow, bk_a and bk_u in rows
+ */
+typedef struct sffn_hybrid {
+  float*    ell_a;
+  float*    ell_u;
+  uint16_t* ell_idx;
+  int32_t*  ell_cnt;
+  int32_t*  slot;
+  int32_t*  brow;
+  int32_t*  n_backup;
+  float*    bk_a;
+  float*    bk_u;
+  int64_t   max_backup;
+} sffn_hybrid;
 
 /* Create a handle for the current HIP device. Validates the descriptor
  * (SFFN_E_ARG / SFFN_E_UNSUPPORTED) before touching the device; returns
@@ -178,6 +217,31 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate,
                          const void* w_up, const void* w_down, int64_t T,
                          float* y, const sffn_twell* tw, int32_t mode,
                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* TwELL -> Hybrid ("Hybrid Conversion", "2. Methodology" B on the
+ * gist.science explainer): routes every row, fills ell_a, ell_idx, ell_cnt,
+ * slot, brow and n_backup of *hy from *tw. When z [T, F] float32 is given,
+ * the backup rows' bk_a rows are set to ReLU(z) (ell_u and bk_u are not
+ * touched). The result is a pure function of the TwELL (and z). */
+sffn_status sffn_hybrid_compact(sffn_handle* h, const sffn_twell* tw, const float* z,
+                                int64_t T, const sffn_hybrid* hy, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* Training forward: y [T, d] float32 as sffn_forward(SFFN_SPARSE), and the
+ * Hybrid of the step saved for sffn_backward: the TwELL of the gate GEMM
+ * (into tw, or the workspace when tw is NULL) is converted with ELL
+ * capacity K = desc.ell_cap (>= 1); ELL rows' up/down projections run over
+ * their slots and save u per slot; backup rows run densely and save their
+ * ReLU(z) and u rows in fp32 ("Sparse MatMul ... dense backup rows on the
+ * matrix cores, sparse rows on the vector units", "2. Methodology" B). */
+sffn_status sffn_forward_train(sffn_handle* h, const void* x, const void* w_gate,
+                               const void* w_up, const void* w_down, int64_t T, float* y,
+                               const sffn_twell* tw, const sffn_hybrid* hy, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
+
+/* Synchronise the stream and return SFFN_E_CAPACITY when *hy->n_backup
+ * exceeds hy->max_backup, else SFFN_OK (or SFFN_E_HIP). */
+sffn_status sffn_hybrid_check(sffn_handle* h, const sffn_hybrid* hy, hipStream_t stream);
 
 /* Synchronise the stream and report the first asynchronous error since
  * the last check (SFFN_E_HIP), else SFFN_OK. */

@@ -1,0 +1,131 @@
+"""Hybrid format and training forward on the GPU against the CPU oracle.
+
+The compaction is checked bit for bit on a TwELL the GPU packs from a host
+pre-activation tensor (the same tensor the oracle packs); the training
+forward is checked against the oracle's dense layer, Hybrid routing and
+saved activations.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import assert_close_bf16, dev, math_weights, rel_fro, twell_np
+from unstructured_sparse_feedforward_amd import SparseFFN
+from unstructured_sparse_feedforward_amd import binding as B
+from unstructured_sparse_feedforward_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def hybrid_np(hy):
+    torch.cuda.synchronize()
+    out = {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in hy.items()}
+    out["ell_idx"] = out["ell_idx"].view(np.uint16).astype(np.int64)
+    out["n_backup"] = int(out["n_backup"][0])
+    return out
+
+
+def _z(T, F, seed, heavy_frac=0.05, shift=-2.6):
+    r = np.random.default_rng(seed)
+    z = (r.standard_normal((T, F)) + shift).astype(np.float32)
+    heavy = r.random(T) < heavy_frac
+    z[heavy] = r.standard_normal((heavy.sum(), F)).astype(np.float32)
+    z[r.random((T, F)) < 0.002] = 0.0
+    return z
+
+
+@pytest.mark.parametrize("T,F,C,K,seed", [(300, 1024, 16, 8, 0), (129, 5632, 16, 64, 1),
+                                          (64, 512, 4, 64, 2), (1000, 2048, 8, 12, 3)])
+def test_hybrid_compact_bitexact(T, F, C, K, seed):
+    _print(f"hybrid T={T} F={F} C={C} K={K}")
+    z = _z(T, F, seed)
+    ffn = SparseFFN(512, F, gated=True, twell_cap=C, ell_cap=K, dtype=torch.bfloat16)
+    zd = torch.from_numpy(z).cuda()
+    tw = ffn.pack_twell(zd)
+    hy = hybrid_np(ffn.hybrid_compact(tw, T, z=zd))
+    ref_tw = oracle.pack_twell(z.astype(np.float64), 128, C)
+    a = np.where(z > 0, z, 0).astype(np.float64)
+    ref = oracle.hybrid_compact(ref_tw, K, a_dense=a)
+    assert hy["n_backup"] == ref["n_backup"]
+    assert np.array_equal(hy["slot"][:T], ref["slot"])
+    assert np.array_equal(hy["brow"][:ref["n_backup"]], ref["brow"])
+    assert np.array_equal(hy["ell_cnt"], ref["ell_cnt"])
+    m = np.arange(K)[None, :] < ref["ell_cnt"][:, None]
+    assert np.array_equal(hy["ell_idx"][m], ref["ell_idx"][m])
+    assert np.array_equal(hy["ell_a"][m].astype(np.float64), ref["ell_a"][m])
+    assert np.array_equal(hy["bk_a"][:ref["n_backup"]].astype(np.float64), ref["bk_a"])
+    assert ffn.hybrid_check(ffn.hybrid_compact(tw, T, z=zd)) == B.SFFN_OK
+
+
+def test_hybrid_capacity_overflow_is_reported():
+    T, F, C, K = 256, 1024, 16, 8
+    z = _z(T, F, 4, heavy_frac=0.2)
+    ffn = SparseFFN(512, F, gated=True, twell_cap=C, ell_cap=K, dtype=torch.bfloat16)
+    zd = torch.from_numpy(z).cuda()
+    tw = ffn.pack_twell(zd)
+    ref = oracle.hybrid_compact(oracle.pack_twell(z.astype(np.float64), 128, C), K)
+    cap = ref["n_backup"] // 2
+    hyd = ffn.hybrid_compact(tw, T, z=zd, max_backup=cap)
+    hy = hybrid_np(hyd)
+    # the true count is reported, the first cap backup rows are listed
+    assert hy["n_backup"] == ref["n_backup"] > cap
+    assert np.array_equal(hy["brow"][:cap], ref["brow"][:cap])
+    assert ffn.hybrid_check(hyd) == B.SFFN_E_CAPACITY
+
+
+@pytest.mark.parametrize("w,T,seed", [(wl.TRAIN_HYBRID, 300, 5), (wl.TRAIN_HYBRID, 1024, 6),
+                                      (wl.TRAIN_HYBRID.replace(gated=False, F=8192, nnz=40,
+                                                               name="train_nongated"), 200, 7)])
+def test_forward_train(w, T, seed):
+    _print(f"forward_train {w.name} T={T}")
+    inp = wl.make_inputs(w, seed=seed, T=T)
+    ffn = SparseFFN(w.d, w.F, gated=w.gated, twell_cap=w.twell_cap, ell_cap=w.ell_cap,
+                    dtype=torch.bfloat16)
+    y, hyd = ffn.forward_train(*(dev(inp, k) for k in ("x", "w_gate", "w_up", "w_down")))
+    assert ffn.hybrid_check(hyd) == B.SFFN_OK
+    hy = hybrid_np(hyd)
+    wg, wu, wd = math_weights(inp)
+    x64 = inp.x.astype(np.float64)
+    yr, it = oracle.dense_ffn(x64, wg, wu, wd)
+    assert_close_bf16(y.cpu().numpy(), yr, "y")
+    # routing against the oracle's Hybrid of the oracle's own pre-activations;
+    # a row may differ only if one of its pre-activations is within 1e-4 of 0
+    ref = oracle.hybrid_compact(oracle.pack_twell(it["z"], 128, w.twell_cap), w.ell_cap)
+    near = (np.abs(it["z"]) < 1e-4).any(axis=1)
+    same = ~near
+    assert np.array_equal((hy["slot"][:T] >= 0)[same], (ref["slot"] >= 0)[same])
+    assert np.array_equal(hy["ell_cnt"][same], ref["ell_cnt"][same])
+    _print("  backup rows:", hy["n_backup"], " ELL slots:", int(hy["ell_cnt"].sum()))
+    # saved activations: a and u of every ELL slot, ReLU(z) and u rows of backup rows
+    rows, ks = np.nonzero(np.arange(w.ell_cap)[None, :] < hy["ell_cnt"][:, None])
+    js = hy["ell_idx"][rows, ks]
+    assert rel_fro(hy["ell_a"][rows, ks], it["a"][rows, js]) < 1e-5
+    assert np.all(it["z"][rows, js] > -1e-4)
+    if w.gated:
+        assert rel_fro(hy["ell_u"][rows, ks], it["u"][rows, js]) < 1e-5
+    nb = hy["n_backup"]
+    br = hy["brow"][:nb]
+    assert np.array_equal(np.flatnonzero(hy["slot"][:T] >= 0), br)
+    assert rel_fro(hy["bk_a"][:nb], it["a"][br]) < 1e-5
+    if w.gated:
+        assert rel_fro(hy["bk_u"][:nb], it["u"][br]) < 1e-5
+
+
+def test_forward_train_equals_inference_y():
+    """With K >= n_t * C the training forward routes exactly the rows the
+    inference forward sends down its dense path, and both give the same y
+    bit for bit (the same kernels in the same order)."""
+    w = wl.GATED_1P5B
+    inp = wl.make_inputs(w, seed=8, T=512)
+    K = (w.F // 128) * w.twell_cap
+    ffn = SparseFFN(w.d, w.F, gated=True, twell_cap=w.twell_cap, ell_cap=K, dtype=torch.bfloat16)
+    args = [dev(inp, k) for k in ("x", "w_gate", "w_up", "w_down")]
+    y_inf = ffn.forward(*args, mode="sparse").clone()
+    y_tr, hyd = ffn.forward_train(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(y_inf.view(torch.int32), y_tr.view(torch.int32))

@@ -28,12 +28,16 @@ SFFN_DENSE = 1
 SFFN_OP_PACK = 0
 SFFN_OP_FORWARD_SPARSE = 1
 SFFN_OP_FORWARD_DENSE = 2
+SFFN_OP_HYBRID = 3
+SFFN_OP_FORWARD_TRAIN = 4
+SFFN_OP_BACKWARD = 5
 
 # every symbol include/sffn.h declares
 EXPORTS = ("sffn_create", "sffn_destroy", "sffn_last_error", "sffn_status_string",
            "sffn_workspace_bytes", "sffn_pack_twell", "sffn_gate_preact",
            "sffn_forward", "sffn_check", "sffn_profile_enable", "sffn_profile_read",
-           "sffn_kernel_name")
+           "sffn_kernel_name", "sffn_hybrid_compact", "sffn_forward_train",
+           "sffn_hybrid_check")
 SFFN_K_COUNT = 12
 
 
@@ -48,6 +52,14 @@ class SffnTwell(ctypes.Structure):
     _fields_ = [("val", ctypes.c_void_p), ("idx", ctypes.c_void_p),
                 ("cnt", ctypes.c_void_p), ("row_flag", ctypes.c_void_p),
                 ("flagged", ctypes.c_void_p), ("n_flagged", ctypes.c_void_p)]
+
+
+class SffnHybrid(ctypes.Structure):
+    _fields_ = [("ell_a", ctypes.c_void_p), ("ell_u", ctypes.c_void_p),
+                ("ell_idx", ctypes.c_void_p), ("ell_cnt", ctypes.c_void_p),
+                ("slot", ctypes.c_void_p), ("brow", ctypes.c_void_p),
+                ("n_backup", ctypes.c_void_p), ("bk_a", ctypes.c_void_p),
+                ("bk_u", ctypes.c_void_p), ("max_backup", ctypes.c_int64)]
 
 
 _lib = None
@@ -89,6 +101,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sffn_profile_read.restype = i32
     lib.sffn_kernel_name.argtypes = [i32]
     lib.sffn_kernel_name.restype = ctypes.c_char_p
+    lib.sffn_hybrid_compact.argtypes = [vp, ctypes.POINTER(SffnTwell), vp, i64,
+                                        ctypes.POINTER(SffnHybrid), vp, sz, vp]
+    lib.sffn_hybrid_compact.restype = i32
+    lib.sffn_forward_train.argtypes = [vp, vp, vp, vp, vp, i64, vp, ctypes.POINTER(SffnTwell),
+                                       ctypes.POINTER(SffnHybrid), vp, sz, vp]
+    lib.sffn_forward_train.restype = i32
+    lib.sffn_hybrid_check.argtypes = [vp, ctypes.POINTER(SffnHybrid), vp]
+    lib.sffn_hybrid_check.restype = i32
     _lib = lib
     return lib
 
@@ -216,6 +236,62 @@ class SparseFFN:
 
     def check(self):
         self._check(self.lib.sffn_check(self.h, _stream()), "sffn_check")
+
+    # ------------------------------------------------------------ Hybrid
+
+    def new_hybrid(self, T: int, max_backup: Optional[int] = None,
+                   device="cuda") -> Dict[str, torch.Tensor]:
+        K, F = self.ell_cap, self.d_ff
+        R = T if max_backup is None else max_backup
+        f32 = dict(dtype=torch.float32, device=device)
+        return dict(
+            ell_a=torch.empty((T, K), **f32),
+            ell_u=torch.empty((T, K), **f32) if self.gated else None,
+            ell_idx=torch.empty((T, K), dtype=torch.int16, device=device),  # uint16 bits
+            ell_cnt=torch.empty((T,), dtype=torch.int32, device=device),
+            slot=torch.empty((max(T, 1),), dtype=torch.int32, device=device),
+            brow=torch.empty((max(R, 1),), dtype=torch.int32, device=device),
+            n_backup=torch.zeros((4,), dtype=torch.int32, device=device),
+            bk_a=torch.empty((max(R, 1), F), **f32),
+            bk_u=torch.empty((max(R, 1), F), **f32) if self.gated else None,
+            max_backup=R,
+        )
+
+    @staticmethod
+    def _hy_struct(hy) -> SffnHybrid:
+        p = lambda k: None if hy[k] is None else hy[k].data_ptr()
+        return SffnHybrid(p("ell_a"), p("ell_u"), p("ell_idx"), p("ell_cnt"), p("slot"),
+                          p("brow"), p("n_backup"), p("bk_a"), p("bk_u"), hy["max_backup"])
+
+    def hybrid_compact(self, tw: Dict[str, torch.Tensor], T: int,
+                       hy: Optional[Dict[str, torch.Tensor]] = None,
+                       z: Optional[torch.Tensor] = None, max_backup: Optional[int] = None):
+        hy = hy if hy is not None else self.new_hybrid(T, max_backup)
+        ws, n = self.workspace(T, SFFN_OP_HYBRID)
+        ts, hs = self._tw_struct(tw), self._hy_struct(hy)
+        self._check(self.lib.sffn_hybrid_compact(self.h, ctypes.byref(ts), _ptr(z), T,
+                                                 ctypes.byref(hs), ws, n, _stream()),
+                    "sffn_hybrid_compact")
+        return hy
+
+    def forward_train(self, x, w_gate, w_up, w_down, hy=None, tw=None, y=None,
+                      max_backup: Optional[int] = None):
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty((T, self.d), dtype=torch.float32, device=x.device)
+        hy = hy if hy is not None else self.new_hybrid(T, max_backup, x.device)
+        ws, n = self.workspace(T, SFFN_OP_FORWARD_TRAIN, x.device)
+        ts = ctypes.byref(self._tw_struct(tw)) if tw is not None else None
+        hs = self._hy_struct(hy)
+        self._check(self.lib.sffn_forward_train(self.h, _ptr(x), _ptr(w_gate), _ptr(w_up),
+                                                _ptr(w_down), T, _ptr(y), ts, ctypes.byref(hs),
+                                                ws, n, _stream()), "sffn_forward_train")
+        return y, hy
+
+    def hybrid_check(self, hy) -> int:
+        """SFFN_OK, or SFFN_E_CAPACITY when the backup rows exceed capacity."""
+        hs = self._hy_struct(hy)
+        return self.lib.sffn_hybrid_check(self.h, ctypes.byref(hs), _stream())
 
     def profile(self, enable: bool = True):
         """Bracket every kernel launch with HIP events on the call's stream."""

@@ -89,9 +89,14 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
   if (op == SFFN_OP_PACK) {
     L.ovf = take((size_t)nt * ovf_words(T) * 4);
   }
-  if (op == SFFN_OP_FORWARD_SPARSE) {
-    // ELL rows of capacity n_t * C: lossless for every unflagged row
-    const int64_t K = nt * C, Kp = (K + 7) / 8 * 8;
+  if (op == SFFN_OP_HYBRID) {
+    L.bk = take((size_t)T);
+  }
+  if (op == SFFN_OP_FORWARD_SPARSE || op == SFFN_OP_FORWARD_TRAIN) {
+    // inference: ELL rows of capacity n_t * C, lossless for every row whose
+    // TwELL did not overflow; training: capacity K = ell_cap
+    const int64_t K = op == SFFN_OP_FORWARD_TRAIN ? (int64_t)h->desc.ell_cap : nt * C;
+    const int64_t Kp = (K + 7) / 8 * 8;
     int ns, epl;
     slice_shape(dt_of(h), (int)d, &ns, &epl);
     L.ell_a = take((size_t)T * K * 4);
@@ -206,7 +211,8 @@ const char* sffn_last_error(const sffn_handle* h) { return h ? h->err.c_str() : 
 
 sffn_status sffn_workspace_bytes(const sffn_handle* h, int64_t T, int32_t op, size_t* bytes) {
   if (!h || !bytes || T < 0) return SFFN_E_ARG;
-  if (op != SFFN_OP_PACK && op != SFFN_OP_FORWARD_SPARSE && op != SFFN_OP_FORWARD_DENSE)
+  if (op != SFFN_OP_PACK && op != SFFN_OP_FORWARD_SPARSE && op != SFFN_OP_FORWARD_DENSE &&
+      op != SFFN_OP_HYBRID && op != SFFN_OP_FORWARD_TRAIN)
     return SFFN_E_ARG;
   *bytes = layout(h, T, op).total;
   return SFFN_OK;
@@ -321,27 +327,29 @@ static sffn_status forward_dense(sffn_handle* h, const void* x, const void* wg, 
   return SFFN_OK;
 }
 
-sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, const void* w_up,
-                         const void* w_down, int64_t T, float* y, const sffn_twell* tw,
-                         int32_t mode, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!h) return SFFN_E_ARG;
-  const sffn_desc& D = h->desc;
-  if (mode != SFFN_SPARSE && mode != SFFN_DENSE) return fail(h, SFFN_E_ARG, "unknown mode");
-  if (T < 0 || T > (int64_t)1 << 30) return fail(h, SFFN_E_ARG, "T out of range");
-  if (T == 0) return SFFN_OK;
-  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_down) || !aligned16(y))
-    return fail(h, SFFN_E_ARG, "x, w_gate, w_down and y must be non-null 16-byte aligned pointers");
-  if (D.gated ? !aligned16(w_up) : w_up != nullptr)
-    return fail(h, SFFN_E_ARG, "w_up must be a 16-byte aligned pointer iff the layer is gated");
-  if (mode == SFFN_DENSE && tw) return fail(h, SFFN_E_ARG, "dense mode takes no TwELL");
-  if (tw && !twell_ok(tw))
-    return fail(h, SFFN_E_ARG, "TwELL buffers must be non-null and 16-byte aligned");
-  const Layout L = layout(h, T, mode == SFFN_SPARSE ? SFFN_OP_FORWARD_SPARSE : SFFN_OP_FORWARD_DENSE);
-  if (!ws || ws_bytes < L.total || ((uintptr_t)ws % kAlign) != 0)
-    return fail(h, SFFN_E_ARG, "workspace missing, too small or not 256-byte aligned");
-  if (mode == SFFN_DENSE) return forward_dense(h, x, w_gate, w_up, w_down, T, y, ws, L, stream);
+static bool hybrid_ok(const sffn_handle* h, const sffn_hybrid* hy, bool need_u) {
+  if (!hy || hy->max_backup < 0) return false;
+  if (!aligned16(hy->ell_a) || !aligned16(hy->ell_idx) || !aligned16(hy->ell_cnt) ||
+      !aligned16(hy->slot) || !aligned16(hy->n_backup))
+    return false;
+  if (hy->max_backup > 0 && (!aligned16(hy->brow) || !aligned16(hy->bk_a))) return false;
+  if (need_u && h->desc.gated) {
+    if (!aligned16(hy->ell_u)) return false;
+    if (hy->max_backup > 0 && !aligned16(hy->bk_u)) return false;
+  }
+  return true;
+}
 
+// The sparse forward shared by inference (hy == NULL: ELL capacity n_t*C,
+// only TwELL-overflow rows take the dense path) and training (hy != NULL:
+// capacity K = ell_cap, the Hybrid of the step is saved).
+static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_gate,
+                                  const void* w_up, const void* w_down, int64_t T, float* y,
+                                  const sffn_twell* tw, const sffn_hybrid* hy, void* ws,
+                                  const Layout& L, hipStream_t stream) {
+  const sffn_desc& D = h->desc;
   const Dtype dt = dt_of(h);
+  const bool train = hy != nullptr;
   sffn_twell t;
   if (tw) {
     t = *tw;
@@ -353,7 +361,7 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, cons
     t.flagged = at<int32_t>(ws, L.tw_list);
     t.n_flagged = at<int32_t>(ws, L.tw_nf);
   }
-  const int K = h->n_t * D.twell_cap;
+  const int K = train ? D.ell_cap : h->n_t * D.twell_cap;
   const int Kp = (K + 7) / 8 * 8;
 
   // 1. gate GEMM, ReLU + TwELL pack in the epilogue
@@ -379,8 +387,7 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, cons
   }
   if (e != hipSuccess) return hip_fail(h, e, "gate GEMM + TwELL");
 
-  // 2. per-row route and ELL compaction (capacity n_t * C: only rows
-  //    whose TwELL overflowed go to the dense path)
+  // 2. per-row route and ELL compaction
   EllArgs ea = {};
   ea.val = t.val;
   ea.idx = t.idx;
@@ -389,9 +396,9 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, cons
   ea.n_t = h->n_t;
   ea.C = D.twell_cap;
   ea.K = K;
-  ea.ell_a = at<float>(ws, L.ell_a);
-  ea.ell_idx = at<uint16_t>(ws, L.ell_idx);
-  ea.ell_cnt = at<int32_t>(ws, L.ell_cnt);
+  ea.ell_a = train ? hy->ell_a : at<float>(ws, L.ell_a);
+  ea.ell_idx = train ? hy->ell_idx : at<uint16_t>(ws, L.ell_idx);
+  ea.ell_cnt = train ? hy->ell_cnt : at<int32_t>(ws, L.ell_cnt);
   ea.row_flag = t.row_flag;
   ea.bk = at<uint8_t>(ws, L.bk);
   {
@@ -400,79 +407,97 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, cons
   }
   if (e != hipSuccess) return hip_fail(h, e, "row compaction");
 
-  // 3. dense path for the flagged rows: their ascending list, the hidden
-  //    rows H = ReLU(x W_g) * (x W_u) (split-K over the few rows, then a
-  //    combine that stores H as bf16 hi + lo, or fp32), and y = H W_d
-  //    scattered into the rows (split-K + reduce)
+  // 3. the dense path's rows: their ascending list; in training also the
+  //    TwELL's own list of overflowing rows
+  int32_t* brow = train ? hy->brow : t.flagged;
+  int32_t* n_bk = train ? hy->n_backup : t.n_flagged;
+  const int64_t cap = train ? hy->max_backup : T;
   {
     ProfScope ps(h, SFFN_K_FLAGS, stream);
-    e = launch_backup_list(ea.bk, T, t.flagged, t.n_flagged, nullptr, stream);
+    e = launch_backup_list(ea.bk, T, brow, cap, n_bk, train ? hy->slot : nullptr, stream);
+    if (e == hipSuccess && train)
+      e = launch_backup_list(t.row_flag, T, t.flagged, T, t.n_flagged, nullptr, stream);
   }
-  if (e != hipSuccess) return hip_fail(h, e, "flagged list");
+  if (e != hipSuccess) return hip_fail(h, e, "backup list");
+
+  // 4. dense path: hidden rows H = ReLU(x W_g) * (x W_u) (split-K over the
+  //    few rows, then a combine that stores H as bf16 hi + lo, or fp32, and
+  //    in training the ReLU(z) and u rows), then y = H W_d scattered into
+  //    the rows (split-K + reduce)
   void* hid = at<char>(ws, L.hid);
   float* part = at<float>(ws, L.part);
-  GemmArgs f = {};
-  f.A = x;
-  f.lda = D.d;
-  f.a_rows = t.flagged;
-  f.m_dev = t.n_flagged;
-  f.B0 = w_gate;
-  f.B1 = w_up;
-  f.ldb = D.d;
-  f.N = D.d_ff;
-  f.K = D.d;
-  f.out = hid;
-  f.act = 1;
-  f.ldo = dt == kBF16 ? 2 * (int64_t)D.d_ff : (int64_t)D.d_ff;
-  f.lo_off = D.d_ff;
-  f.part = part;
-  f.split_target = h->num_cu;
-  f.split_max = std::min(kSplitMax, D.d / (dt == kBF16 ? 64 : 32));
-  const int nb = D.gated ? 2 : 1;
-  f.num_cu = h->num_cu;
-  f.grid = gemm_grid(dt, nb, h->num_cu);
-  {
-    ProfScope ps(h, SFFN_K_FLAG_GATEUP, stream);
-    e = launch_gemm(dt, nb, false, kEpiHiddenSplitK, f, stream);
-    if (e == hipSuccess) e = launch_hidden_combine(dt, nb, f, stream);
+  const int mcap = train ? (int)std::min<int64_t>(hy->max_backup, T) : 0;
+  if (!train || mcap > 0) {
+    GemmArgs f = {};
+    f.A = x;
+    f.lda = D.d;
+    f.a_rows = brow;
+    f.m_dev = n_bk;
+    f.m_cap = mcap;
+    f.B0 = w_gate;
+    f.B1 = w_up;
+    f.ldb = D.d;
+    f.N = D.d_ff;
+    f.K = D.d;
+    f.out = hid;
+    f.act = 1;
+    f.ldo = dt == kBF16 ? 2 * (int64_t)D.d_ff : (int64_t)D.d_ff;
+    f.lo_off = D.d_ff;
+    if (train) {
+      f.out_a = hy->bk_a;
+      f.out_u = D.gated ? hy->bk_u : nullptr;
+      f.ldo_au = D.d_ff;
+    }
+    f.part = part;
+    f.split_target = h->num_cu;
+    f.split_max = std::min(kSplitMax, D.d / (dt == kBF16 ? 64 : 32));
+    const int nb = D.gated ? 2 : 1;
+    f.num_cu = h->num_cu;
+    f.grid = gemm_grid(dt, nb, h->num_cu);
+    {
+      ProfScope ps(h, SFFN_K_FLAG_GATEUP, stream);
+      e = launch_gemm(dt, nb, false, kEpiHiddenSplitK, f, stream);
+      if (e == hipSuccess) e = launch_hidden_combine(dt, nb, f, stream);
+    }
+    if (e != hipSuccess) return hip_fail(h, e, "dense-path gate/up GEMM");
+    GemmArgs f2 = {};
+    f2.A = hid;
+    f2.m_dev = n_bk;
+    f2.m_cap = mcap;
+    f2.B0 = w_down;
+    f2.ldb = D.d;
+    f2.N = D.d;
+    if (dt == kBF16) {
+      // [H_hi | H_lo] x [W_d ; W_d]: K = 2F with the B index wrapped at F
+      f2.lda = 2 * (int64_t)D.d_ff;
+      f2.K = 2 * D.d_ff;
+      f2.kwrap = D.d_ff;
+    } else {
+      f2.lda = D.d_ff;
+      f2.K = D.d_ff;
+    }
+    f2.out = y;
+    f2.ldo = D.d;
+    f2.out_rows = brow;
+    f2.part = part;
+    f2.split_target = h->num_cu;
+    const int nkt = f2.K / (dt == kBF16 ? 64 : 32);
+    f2.split_max = std::min(kSplitMax, nkt);
+    f2.num_cu = h->num_cu;
+    f2.grid = gemm_grid(dt, 1, h->num_cu);
+    {
+      ProfScope ps(h, SFFN_K_FLAG_DOWN, stream);
+      e = launch_gemm(dt, 1, true, kEpiStoreF32, f2, stream);
+    }
+    if (e != hipSuccess) return hip_fail(h, e, "dense-path down GEMM");
+    {
+      ProfScope ps(h, SFFN_K_SPLITK_REDUCE, stream);
+      e = launch_splitk_reduce(f2, y, D.d, stream);
+    }
+    if (e != hipSuccess) return hip_fail(h, e, "split-K reduce");
   }
-  if (e != hipSuccess) return hip_fail(h, e, "flagged gate/up GEMM");
-  GemmArgs f2 = {};
-  f2.A = hid;
-  f2.m_dev = t.n_flagged;
-  f2.B0 = w_down;
-  f2.ldb = D.d;
-  f2.N = D.d;
-  if (dt == kBF16) {
-    // [H_hi | H_lo] x [W_d ; W_d]: K = 2F with the B index wrapped at F
-    f2.lda = 2 * (int64_t)D.d_ff;
-    f2.K = 2 * D.d_ff;
-    f2.kwrap = D.d_ff;
-  } else {
-    f2.lda = D.d_ff;
-    f2.K = D.d_ff;
-  }
-  f2.out = y;
-  f2.ldo = D.d;
-  f2.out_rows = t.flagged;
-  f2.part = part;
-  f2.split_target = h->num_cu;
-  const int nkt = f2.K / (dt == kBF16 ? 64 : 32);
-  f2.split_max = std::min(kSplitMax, nkt);
-  f2.num_cu = h->num_cu;
-  f2.grid = gemm_grid(dt, 1, h->num_cu);
-  {
-    ProfScope ps(h, SFFN_K_FLAG_DOWN, stream);
-    e = launch_gemm(dt, 1, true, kEpiStoreF32, f2, stream);
-  }
-  if (e != hipSuccess) return hip_fail(h, e, "flagged down GEMM");
-  {
-    ProfScope ps(h, SFFN_K_SPLITK_REDUCE, stream);
-    e = launch_splitk_reduce(f2, y, D.d, stream);
-  }
-  if (e != hipSuccess) return hip_fail(h, e, "split-K reduce");
 
-  // 4. sparse up/down over the ELL rows, d sliced across the XCDs
+  // 5. sparse up/down over the ELL rows, d sliced across the XCDs
   SliceArgs sa = {};
   sa.x = x;
   sa.wu = w_up;
@@ -486,6 +511,7 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, cons
   sa.K = K;
   sa.Kp = Kp;
   sa.upart = at<float>(ws, L.upart);
+  sa.ell_u = (train && D.gated) ? hy->ell_u : nullptr;
   sa.y = y;
   if (D.gated) {
     ProfScope ps(h, SFFN_K_SPARSE_UP, stream);
@@ -496,6 +522,115 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, cons
     e = launch_updown(dt, D.gated != 0, 1, sa, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "sparse up/down");
+  return SFFN_OK;
+}
+
+static sffn_status forward_args(sffn_handle* h, const void* x, const void* w_gate,
+                                const void* w_up, const void* w_down, int64_t T, const float* y,
+                                const sffn_twell* tw) {
+  const sffn_desc& D = h->desc;
+  if (T < 0 || T > (int64_t)1 << 30) return fail(h, SFFN_E_ARG, "T out of range");
+  if (T == 0) return SFFN_OK;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_down) || !aligned16(y))
+    return fail(h, SFFN_E_ARG, "x, w_gate, w_down and y must be non-null 16-byte aligned pointers");
+  if (D.gated ? !aligned16(w_up) : w_up != nullptr)
+    return fail(h, SFFN_E_ARG, "w_up must be a 16-byte aligned pointer iff the layer is gated");
+  if (tw && !twell_ok(tw))
+    return fail(h, SFFN_E_ARG, "TwELL buffers must be non-null and 16-byte aligned");
+  return SFFN_OK;
+}
+
+static bool ws_ok(void* ws, size_t ws_bytes, const Layout& L) {
+  return ws && ws_bytes >= L.total && ((uintptr_t)ws % kAlign) == 0;
+}
+
+sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, const void* w_up,
+                         const void* w_down, int64_t T, float* y, const sffn_twell* tw,
+                         int32_t mode, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!h) return SFFN_E_ARG;
+  if (mode != SFFN_SPARSE && mode != SFFN_DENSE) return fail(h, SFFN_E_ARG, "unknown mode");
+  sffn_status st = forward_args(h, x, w_gate, w_up, w_down, T, y, tw);
+  if (st != SFFN_OK || T == 0) return st;
+  if (mode == SFFN_DENSE && tw) return fail(h, SFFN_E_ARG, "dense mode takes no TwELL");
+  const Layout L = layout(h, T, mode == SFFN_SPARSE ? SFFN_OP_FORWARD_SPARSE : SFFN_OP_FORWARD_DENSE);
+  if (!ws_ok(ws, ws_bytes, L))
+    return fail(h, SFFN_E_ARG, "workspace missing, too small or not 256-byte aligned");
+  if (mode == SFFN_DENSE) return forward_dense(h, x, w_gate, w_up, w_down, T, y, ws, L, stream);
+  return sparse_forward(h, x, w_gate, w_up, w_down, T, y, tw, nullptr, ws, L, stream);
+}
+
+sffn_status sffn_forward_train(sffn_handle* h, const void* x, const void* w_gate,
+                               const void* w_up, const void* w_down, int64_t T, float* y,
+                               const sffn_twell* tw, const sffn_hybrid* hy, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+  if (!h) return SFFN_E_ARG;
+  if (h->desc.ell_cap < 1) return fail(h, SFFN_E_ARG, "training needs desc.ell_cap >= 1");
+  sffn_status st = forward_args(h, x, w_gate, w_up, w_down, T, y, tw);
+  if (st != SFFN_OK || T == 0) return st;
+  if (!hybrid_ok(h, hy, true))
+    return fail(h, SFFN_E_ARG, "Hybrid buffers must be non-null and 16-byte aligned");
+  const Layout L = layout(h, T, SFFN_OP_FORWARD_TRAIN);
+  if (!ws_ok(ws, ws_bytes, L))
+    return fail(h, SFFN_E_ARG, "workspace missing, too small or not 256-byte aligned");
+  return sparse_forward(h, x, w_gate, w_up, w_down, T, y, tw, hy, ws, L, stream);
+}
+
+sffn_status sffn_hybrid_compact(sffn_handle* h, const sffn_twell* tw, const float* z, int64_t T,
+                                const sffn_hybrid* hy, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  if (!h) return SFFN_E_ARG;
+  if (h->desc.ell_cap < 1) return fail(h, SFFN_E_ARG, "the Hybrid needs desc.ell_cap >= 1");
+  if (T < 0 || T > (int64_t)1 << 30) return fail(h, SFFN_E_ARG, "T out of range");
+  if (T == 0) return SFFN_OK;
+  if (!twell_ok(tw)) return fail(h, SFFN_E_ARG, "TwELL buffers must be non-null and 16-byte aligned");
+  if (!hybrid_ok(h, hy, false))
+    return fail(h, SFFN_E_ARG, "Hybrid buffers must be non-null and 16-byte aligned");
+  if (z && !aligned16(z)) return fail(h, SFFN_E_ARG, "z must be 16-byte aligned");
+  const Layout L = layout(h, T, SFFN_OP_HYBRID);
+  if (!ws_ok(ws, ws_bytes, L))
+    return fail(h, SFFN_E_ARG, "workspace missing, too small or not 256-byte aligned");
+  EllArgs ea = {};
+  ea.val = tw->val;
+  ea.idx = tw->idx;
+  ea.cnt = tw->cnt;
+  ea.T = T;
+  ea.n_t = h->n_t;
+  ea.C = h->desc.twell_cap;
+  ea.K = h->desc.ell_cap;
+  ea.ell_a = hy->ell_a;
+  ea.ell_idx = hy->ell_idx;
+  ea.ell_cnt = hy->ell_cnt;
+  ea.row_flag = nullptr;
+  ea.bk = at<uint8_t>(ws, L.bk);
+  hipError_t e;
+  {
+    ProfScope ps(h, SFFN_K_ROWS, stream);
+    e = launch_rows(ea, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "row compaction");
+  {
+    ProfScope ps(h, SFFN_K_FLAGS, stream);
+    e = launch_backup_list(ea.bk, T, hy->brow, hy->max_backup, hy->n_backup, hy->slot, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "backup list");
+  if (z && hy->max_backup > 0) {
+    e = launch_gather_relu_rows(z, h->desc.d_ff, hy->brow, hy->n_backup,
+                                (int)std::min<int64_t>(hy->max_backup, T), hy->bk_a, stream);
+    if (e != hipSuccess) return hip_fail(h, e, "backup rows");
+  }
+  return SFFN_OK;
+}
+
+sffn_status sffn_hybrid_check(sffn_handle* h, const sffn_hybrid* hy, hipStream_t stream) {
+  if (!h || !hy || !aligned16(hy->n_backup)) return SFFN_E_ARG;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(h, e, "stream");
+  int32_t n = 0;
+  e = hipMemcpy(&n, hy->n_backup, sizeof(n), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(h, e, "n_backup");
+  if (n > hy->max_backup)
+    return fail(h, SFFN_E_CAPACITY, "backup rows " + std::to_string(n) + " exceed max_backup " +
+                                        std::to_string(hy->max_backup));
   return SFFN_OK;
 }
 

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
   const int wr = wave >> 1;
   const int wc = wave & 1;
 
-  const int M = g.m_dev ? *g.m_dev : g.M;
+  const int M = g.m_dev ? device_rows(g.m_dev, g.m_cap) : g.M;
   if (M <= 0) return;
   const int mt = (M + BM - 1) / BM;
   const int ntl = g.N / BN;
@@ -290,6 +290,27 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
       }
     }
 
+    // ---- saved ReLU(z) and u rows (training backup rows), straight from
+    //      the accumulators
+    if constexpr (EPI == kEpiHiddenSplitK) {
+      if (g.out_a) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const int m = m0 + wr * 64 + i * 32 + (q >> 2) * 8 + (lane >> 5) * 4 + (q & 3);
+              const int n = n0 + wc * 64 + j * 32 + (lane & 31);
+              if (m < M) {
+                const float zv = acc[0][i][j][q];
+                g.out_a[(int64_t)m * g.ldo_au + n] = zv > 0.0f ? zv : 0.0f;
+                if (NB == 2 && g.out_u) g.out_u[(int64_t)m * g.ldo_au + n] = acc[NB - 1][i][j][q];
+              }
+            }
+      }
+    }
+
     // ---- epilogue: accumulators -> fp32 tile in LDS
     float* sC = (float*)smem;
 #pragma unroll
@@ -361,7 +382,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
 // parts (bf16 layers) or float32. A no-op when the GEMM did not split.
 template <typename E, int NB>
 __global__ __launch_bounds__(256) void hidden_combine_kernel(GemmArgs g) {
-  const int M = *g.m_dev;
+  const int M = device_rows(g.m_dev, g.m_cap);
   if (M <= 0) return;
   const int mt = (M + BM - 1) / BM;
   const int ntl = g.N / BN;
@@ -379,11 +400,15 @@ __global__ __launch_bounds__(256) void hidden_combine_kernel(GemmArgs g) {
       z += *(const f32x2_t*)(g.part + ((int64_t)k * Mpad + m) * g.N + c);
       if (NB == 2) u += *(const f32x2_t*)(g.part + ((int64_t)(S + k) * Mpad + m) * g.N + c);
     }
-    f32x2_t h;
+    f32x2_t h, a;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const float r = z[q] > 0.0f ? z[q] : 0.0f;
-      h[q] = NB == 2 ? r * u[q] : r;
+      a[q] = z[q] > 0.0f ? z[q] : 0.0f;
+      h[q] = NB == 2 ? a[q] * u[q] : a[q];
+    }
+    if (g.out_a) {
+      *(f32x2_t*)(g.out_a + (int64_t)m * g.ldo_au + c) = a;
+      if (NB == 2 && g.out_u) *(f32x2_t*)(g.out_u + (int64_t)m * g.ldo_au + c) = u;
     }
     if constexpr (sizeof(E) == 4) {
       *(f32x2_t*)((float*)g.out + (int64_t)m * g.ldo + c) = h;
@@ -400,7 +425,7 @@ __global__ __launch_bounds__(256) void hidden_combine_kernel(GemmArgs g) {
 }
 
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, float* y, int64_t ldy) {
-  const int M = *g.m_dev;
+  const int M = device_rows(g.m_dev, g.m_cap);
   if (M <= 0) return;
   const int mt = (M + BM - 1) / BM;
   const int ntl = g.N / BN;

@@ -97,6 +97,7 @@ struct GemmArgs {
   const int32_t* a_rows;
   int M;
   const int32_t* m_dev;
+  int m_cap;                 // > 0: a device M is capped at m_cap
   // B: [N, K] (k contiguous) or, when b_trans, [K, N] (n contiguous).
   // With two B operands (gate and up) both share A. The k index into B is
   // taken modulo kwrap when kwrap > 0.
@@ -112,6 +113,9 @@ struct GemmArgs {
   const int32_t* out_rows;   // scatter of stored rows (kEpiStoreF32)
   int act;                   // 1: ReLU on the single-B result; dual B is always ReLU(z)*u
   int lo_off;                // column offset of the lo part (kEpiHiddenSplit)
+  float* out_a;              // kEpiHiddenSplitK: ReLU(z) rows, fp32 [M, ldo_au] (nullable)
+  float* out_u;              // kEpiHiddenSplitK: u rows, fp32 [M, ldo_au] (nullable)
+  int64_t ldo_au;
   // split-K (kEpiStoreF32 with a device M): the number of splits S is
   // chosen on the device so that tiles * S stays near split_target; when
   // S > 1 the partials go to part[S][Mpad][N] and a reduce kernel adds them.
@@ -166,10 +170,21 @@ struct EllArgs {
   uint8_t* bk;            // [T] out, 1 = dense backup row
 };
 hipError_t launch_rows(const EllArgs& a, hipStream_t s);
-// Ascending list of the rows with bk[t] != 0, their count and (nullable)
-// every row's backup slot (-1 for ELL rows). One workgroup.
-hipError_t launch_backup_list(const uint8_t* bk, int64_t T, int32_t* brow, int32_t* n_backup,
-                              int32_t* slot, hipStream_t s);
+// Ascending list of the rows with bk[t] != 0 (the first cap of them), their
+// true count and (nullable) every row's backup slot (-1 for ELL rows).
+// One workgroup; bk must be 16-byte aligned.
+hipError_t launch_backup_list(const uint8_t* bk, int64_t T, int32_t* brow, int64_t cap,
+                              int32_t* n_backup, int32_t* slot, hipStream_t s);
+
+// The number of rows of a GEMM whose M lives on the device.
+__device__ __forceinline__ int device_rows(const int32_t* m_dev, int m_cap) {
+  const int m = *m_dev;
+  return (m_cap > 0 && m > m_cap) ? m_cap : m;
+}
+
+// rows[m] for m < min(*n, cap): out[m, :] = ReLU(z[rows[m], :]) (fp32, F wide)
+hipError_t launch_gather_relu_rows(const float* z, int F, const int32_t* rows, const int32_t* n,
+                                   int cap, float* out, hipStream_t s);
 
 // Sparse up/down over ELL rows, d cut into NS slices (one per XCD group).
 struct SliceArgs {

@@ -77,10 +77,12 @@ __global__ __launch_bounds__(256) void rows_kernel(EllArgs a) {
   }
 }
 
-// One workgroup: list the backup rows in ascending order, their count and,
-// when requested, every row's backup slot (-1 for ELL rows).
+// One workgroup: list the backup rows in ascending order (the first cap of
+// them), their true count and, when requested, every row's backup slot
+// (-1 for ELL rows).
 __global__ __launch_bounds__(1024) void backup_list_kernel(const uint8_t* __restrict__ bk,
                                                            int64_t T, int32_t* __restrict__ brow,
+                                                           int64_t cap,
                                                            int32_t* __restrict__ n_backup,
                                                            int32_t* __restrict__ slot) {
   constexpr int RPT = 16;
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(1024) void backup_list_kernel(const uint8_t* __rest
     int off = carry + wbase + inc - c;
     for (int i = 0; i < RPT && r0 + i < T; ++i) {
       if (bits & (1u << i)) {
-        brow[off] = (int32_t)(r0 + i);
+        if (off < cap) brow[off] = (int32_t)(r0 + i);
         if (slot) slot[r0 + i] = off;
         ++off;
       } else if (slot) {
@@ -287,7 +289,31 @@ hipError_t launch_slices(const SliceArgs& a, bool gated, int phase, hipStream_t 
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void gather_relu_rows_kernel(const float* __restrict__ z, int F,
+                                                               const int32_t* __restrict__ rows,
+                                                               const int32_t* __restrict__ n,
+                                                               int cap, float* __restrict__ out) {
+  const int R = device_rows(n, cap);
+  const int f4 = F / 4;
+  const int64_t total = (int64_t)R * f4;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int m = (int)(e / f4);
+    const int c = (int)(e - (int64_t)m * f4) * 4;
+    f32x4_t v = *(const f32x4_t*)(z + (int64_t)rows[m] * F + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = v[q] > 0.0f ? v[q] : 0.0f;
+    *(f32x4_t*)(out + (int64_t)m * F + c) = v;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gather_relu_rows(const float* z, int F, const int32_t* rows, const int32_t* n,
+                                   int cap, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(gather_relu_rows_kernel, dim3(512), dim3(256), 0, s, z, F, rows, n, cap, out);
+  return hipGetLastError();
+}
 
 void slice_shape(Dtype, int d, int* ns, int* epl) {
   int n = d / 256;
@@ -302,9 +328,10 @@ hipError_t launch_rows(const EllArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_backup_list(const uint8_t* bk, int64_t T, int32_t* brow, int32_t* n_backup,
-                              int32_t* slot, hipStream_t s) {
-  hipLaunchKernelGGL(backup_list_kernel, dim3(1), dim3(1024), 0, s, bk, T, brow, n_backup, slot);
+hipError_t launch_backup_list(const uint8_t* bk, int64_t T, int32_t* brow, int64_t cap,
+                              int32_t* n_backup, int32_t* slot, hipStream_t s) {
+  hipLaunchKernelGGL(backup_list_kernel, dim3(1), dim3(1024), 0, s, bk, T, brow, cap, n_backup,
+                     slot);
   return hipGetLastError();
 }
 
