@@ -239,6 +239,25 @@ sffn_status sffn_forward_train(sffn_handle* h, const void* x, const void* w_gate
                                const sffn_twell* tw, const sffn_hybrid* hy, void* ws,
                                size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Sparse backward over the Hybrid saved by sffn_forward_train ("2.
+ * Methodology" B, training kernels: backpropagation, on the gist.science
+ * explainer). With M = 1[z > 0]: dH = dy W_d^T (only where M = 1),
+ * dU = dH * a, dZ = dH * u * M + l1_coeff * M (non-gated: dZ = dH * M +
+ * l1_coeff * M); dx = dZ W_g^T + dU W_u^T; dW_g = x^T dZ, dW_u = x^T dU,
+ * dW_d = (a * u)^T dy (non-gated: a^T dy). ELL rows run over their slots
+ * (the slots are regrouped by neuron, in ascending row order, for dW);
+ * backup rows run as dense GEMMs. Outputs are overwritten: dx [T, d],
+ * dw_gate, dw_up (NULL iff non-gated), dw_down [F, d] neuron-major, all
+ * float32; rows of never-active neurons are zero. dy has the descriptor's
+ * dtype. The workspace is sized for up to T backup rows; rows from slot
+ * max_backup on are not processed (see sffn_hybrid_check).
+ */
+sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, const void* w_up,
+                          const void* w_down, const sffn_hybrid* hy, const void* dy, int64_t T,
+                          float* dx, float* dw_gate, float* dw_up, float* dw_down, float l1_coeff,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Synchronise the stream and return SFFN_E_CAPACITY when *hy->n_backup
  * exceeds hy->max_backup, else SFFN_OK (or SFFN_E_HIP). */
 sffn_status sffn_hybrid_check(sffn_handle* h, const sffn_hybrid* hy, hipStream_t stream);
@@ -267,7 +286,12 @@ sffn_status sffn_check(sffn_handle* h, hipStream_t stream);
 #define SFFN_K_GATE_PREACT   9  /* gate GEMM writing z */
 #define SFFN_K_ROWS         10  /* per-row route + ELL compaction of the TwELL */
 #define SFFN_K_SPARSE_DOWN  11  /* sparse down projection into y */
-#define SFFN_K_COUNT        12
+#define SFFN_K_BWD_SDDMM    12  /* backward: dy . W_d[j] per ELL slot (partial dots) */
+#define SFFN_K_BWD_DX       13  /* backward: dZ, dU per slot and dx of ELL rows */
+#define SFFN_K_BWD_TRANSPOSE 14 /* backward: ELL slots grouped by neuron */
+#define SFFN_K_BWD_DW       15  /* backward: dW rows from the ELL slots */
+#define SFFN_K_BWD_DENSE    16  /* backward: the backup rows' dense GEMMs */
+#define SFFN_K_COUNT        17
 sffn_status sffn_profile_enable(sffn_handle* h, int32_t enable);
 sffn_status sffn_profile_read(sffn_handle* h, double* total_ms, int32_t* launches, int32_t n);
 /* Static name of a kernel id ("" if out of range). */

@@ -129,3 +129,77 @@ def test_forward_train_equals_inference_y():
     y_tr, hyd = ffn.forward_train(*args)
     torch.cuda.synchronize()
     assert torch.equal(y_inf.view(torch.int32), y_tr.view(torch.int32))
+
+
+# --------------------------------------------------------------- backward
+
+def _grads_ref(inp, l1):
+    wg, wu, wd = math_weights(inp)
+    return oracle.backward(inp.x.astype(np.float64), wg, wu, wd, inp.dy.astype(np.float64),
+                           l1_coeff=l1)
+
+
+# seeds whose pre-activations all keep |z| > 2e-5, so the ReLU mask of the
+# GPU's fp32 pre-activations is the oracle's
+@pytest.mark.parametrize("w,T,seed,l1", [
+    (wl.TRAIN_HYBRID, 256, 47, 0.0),
+    (wl.TRAIN_HYBRID, 512, 57, 0.0),
+    (wl.TRAIN_HYBRID, 256, 47, 0.05),
+    (wl.TRAIN_HYBRID.replace(gated=False, F=8192, nnz=40, name="train_nongated"), 256, 55, 0.0),
+])
+def test_backward(w, T, seed, l1):
+    _print(f"backward {w.name} T={T} l1={l1}")
+    inp = wl.make_inputs(w, seed=seed, T=T)
+    wg, _, _ = math_weights(inp)
+    assert np.abs(inp.x.astype(np.float64) @ wg).min() > 2e-5
+    ffn = SparseFFN(w.d, w.F, gated=w.gated, twell_cap=w.twell_cap, ell_cap=w.ell_cap,
+                    dtype=torch.bfloat16)
+    args = [dev(inp, k) for k in ("x", "w_gate", "w_up", "w_down")]
+    _, hy = ffn.forward_train(*args)
+    assert ffn.hybrid_check(hy) == B.SFFN_OK
+    _print("  backup rows:", int(hy["n_backup"][0].item()))
+    dx, dwg, dwu, dwd = ffn.backward(*args, hy, dev(inp, "dy"), l1_coeff=l1)
+    ref = _grads_ref(inp, l1)
+    assert_close_bf16(dx.cpu().numpy(), ref["dx"], "dx")
+    # dW is neuron-major [F, d]: the transpose of the math d x F matrices
+    assert_close_bf16(dwg.cpu().numpy(), ref["dw_gate"].T, "dw_gate")
+    assert_close_bf16(dwd.cpu().numpy(), ref["dw_down"], "dw_down")
+    if w.gated:
+        assert_close_bf16(dwu.cpu().numpy(), ref["dw_up"].T, "dw_up")
+    # neurons never active in the batch have exactly zero weight gradients
+    dead = ~((inp.x.astype(np.float64) @ wg) > 0).any(axis=0)
+    if dead.any():
+        assert np.all(dwg.cpu().numpy()[dead] == 0) and np.all(dwd.cpu().numpy()[dead] == 0)
+
+
+def test_backward_deterministic():
+    w = wl.TRAIN_HYBRID
+    inp = wl.make_inputs(w, seed=47, T=256)
+    ffn = SparseFFN(w.d, w.F, gated=True, twell_cap=w.twell_cap, ell_cap=w.ell_cap,
+                    dtype=torch.bfloat16)
+    args = [dev(inp, k) for k in ("x", "w_gate", "w_up", "w_down")]
+    _, hy = ffn.forward_train(*args)
+    dy = dev(inp, "dy")
+    g1 = [t.clone() for t in ffn.backward(*args, hy, dy)]
+    g2 = ffn.backward(*args, hy, dy)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_backward_all_rows_backup():
+    """K = 1 sends every row with more than one positive to the dense
+    backup: the gradients come from the dense GEMM path alone."""
+    w = wl.TRAIN_HYBRID.replace(ell_cap=1)
+    inp = wl.make_inputs(w, seed=47, T=256)
+    ffn = SparseFFN(w.d, w.F, gated=True, twell_cap=w.twell_cap, ell_cap=1, dtype=torch.bfloat16)
+    args = [dev(inp, k) for k in ("x", "w_gate", "w_up", "w_down")]
+    _, hy = ffn.forward_train(*args)
+    nb = int(hy["n_backup"][0].item())
+    assert nb > 200
+    dx, dwg, dwu, dwd = ffn.backward(*args, hy, dev(inp, "dy"))
+    ref = _grads_ref(inp, 0.0)
+    assert_close_bf16(dx.cpu().numpy(), ref["dx"], "dx")
+    assert_close_bf16(dwg.cpu().numpy(), ref["dw_gate"].T, "dw_gate")
+    assert_close_bf16(dwu.cpu().numpy(), ref["dw_up"].T, "dw_up")
+    assert_close_bf16(dwd.cpu().numpy(), ref["dw_down"], "dw_down")

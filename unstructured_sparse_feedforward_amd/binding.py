@@ -37,8 +37,8 @@ EXPORTS = ("sffn_create", "sffn_destroy", "sffn_last_error", "sffn_status_string
            "sffn_workspace_bytes", "sffn_pack_twell", "sffn_gate_preact",
            "sffn_forward", "sffn_check", "sffn_profile_enable", "sffn_profile_read",
            "sffn_kernel_name", "sffn_hybrid_compact", "sffn_forward_train",
-           "sffn_hybrid_check")
-SFFN_K_COUNT = 12
+           "sffn_hybrid_check", "sffn_backward")
+SFFN_K_COUNT = 17
 
 
 class SffnDesc(ctypes.Structure):
@@ -109,6 +109,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sffn_forward_train.restype = i32
     lib.sffn_hybrid_check.argtypes = [vp, ctypes.POINTER(SffnHybrid), vp]
     lib.sffn_hybrid_check.restype = i32
+    lib.sffn_backward.argtypes = [vp, vp, vp, vp, vp, ctypes.POINTER(SffnHybrid), vp, i64,
+                                  vp, vp, vp, vp, ctypes.c_float, vp, sz, vp]
+    lib.sffn_backward.restype = i32
     _lib = lib
     return lib
 
@@ -287,6 +290,23 @@ class SparseFFN:
                                                 _ptr(w_down), T, _ptr(y), ts, ctypes.byref(hs),
                                                 ws, n, _stream()), "sffn_forward_train")
         return y, hy
+
+    def backward(self, x, w_gate, w_up, w_down, hy, dy, l1_coeff: float = 0.0):
+        """Gradients (dx [T, d], dw_gate, dw_up, dw_down [F, d]; float32) of
+        the step whose Hybrid ``hy`` sffn_forward_train saved."""
+        T = x.shape[0]
+        f32 = dict(dtype=torch.float32, device=x.device)
+        dx = torch.empty((T, self.d), **f32)
+        dwg = torch.empty((self.d_ff, self.d), **f32)
+        dwu = torch.empty((self.d_ff, self.d), **f32) if self.gated else None
+        dwd = torch.empty((self.d_ff, self.d), **f32)
+        ws, n = self.workspace(T, SFFN_OP_BACKWARD, x.device)
+        hs = self._hy_struct(hy)
+        self._check(self.lib.sffn_backward(self.h, _ptr(x), _ptr(w_gate), _ptr(w_up),
+                                           _ptr(w_down), ctypes.byref(hs), _ptr(dy), T,
+                                           _ptr(dx), _ptr(dwg), _ptr(dwu), _ptr(dwd),
+                                           float(l1_coeff), ws, n, _stream()), "sffn_backward")
+        return dx, dwg, dwu, dwd
 
     def hybrid_check(self, hy) -> int:
         """SFFN_OK, or SFFN_E_CAPACITY when the backup rows exceed capacity."""

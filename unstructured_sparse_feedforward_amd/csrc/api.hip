@@ -75,6 +75,10 @@ struct Layout {
   size_t ovf = 0, tw_val = 0, tw_idx = 0, tw_cnt = 0, tw_flag = 0, tw_list = 0, tw_nf = 0;
   size_t ell_a = 0, ell_idx = 0, ell_cnt = 0, bk = 0, upart = 0;
   size_t hid = 0, part = 0, total = 0;
+  // backward
+  size_t gz = 0, gu = 0, ncnt = 0, noff = 0, ent0 = 0, ent = 0, dH = 0, gz_rm = 0, gu_rm = 0;
+  size_t gz_t = 0, gu_t = 0, gh_t = 0, xb = 0, dyb = 0;
+  int64_t ldt = 0;
 };
 
 Layout layout(const sffn_handle* h, int64_t T, int op) {
@@ -123,6 +127,33 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
   }
   if (op == SFFN_OP_FORWARD_DENSE) {
     L.hid = take((size_t)T * F * esize(h));
+  }
+  if (op == SFFN_OP_BACKWARD) {
+    // sized for up to T backup rows
+    const int64_t K = h->desc.ell_cap, Kp = (K + 7) / 8 * 8;
+    int ns, epl;
+    slice_shape(dt_of(h), (int)d, &ns, &epl);
+    const bool split = h->desc.dtype == SFFN_BF16;
+    const int64_t Tp = (T + 63) / 64 * 64;
+    L.ldt = split ? 2 * Tp : Tp;
+    L.upart = take((size_t)ns * T * Kp * 4);
+    L.gz = take((size_t)T * K * 4);
+    L.gu = take((size_t)T * K * 4);
+    L.ncnt = take((size_t)2 * F * 4);
+    L.noff = take((size_t)(F + 1) * 4);
+    L.ent0 = take((size_t)T * K * 4);
+    L.ent = take((size_t)T * K * 4);
+    L.dH = take((size_t)T * F * 4);
+    L.gz_rm = take((size_t)T * F * 4);
+    L.gu_rm = take((size_t)T * F * 4);
+    L.gz_t = take((size_t)F * L.ldt * esize(h));
+    L.gu_t = take((size_t)F * L.ldt * esize(h));
+    L.gh_t = take((size_t)F * L.ldt * esize(h));
+    L.xb = take((size_t)L.ldt * d * esize(h));
+    L.dyb = take((size_t)L.ldt * d * esize(h));
+    const int tiles_d = std::max(1, h->num_cu / (int)(d / 128));
+    const int tiles_h = std::max(1, h->num_cu / (int)(F / 128));
+    L.part = take(std::max((size_t)tiles_d * 128 * d, (size_t)tiles_h * 128 * F) * 4);
   }
   L.total = o;
   return L;
@@ -212,7 +243,7 @@ const char* sffn_last_error(const sffn_handle* h) { return h ? h->err.c_str() : 
 sffn_status sffn_workspace_bytes(const sffn_handle* h, int64_t T, int32_t op, size_t* bytes) {
   if (!h || !bytes || T < 0) return SFFN_E_ARG;
   if (op != SFFN_OP_PACK && op != SFFN_OP_FORWARD_SPARSE && op != SFFN_OP_FORWARD_DENSE &&
-      op != SFFN_OP_HYBRID && op != SFFN_OP_FORWARD_TRAIN)
+      op != SFFN_OP_HYBRID && op != SFFN_OP_FORWARD_TRAIN && op != SFFN_OP_BACKWARD)
     return SFFN_E_ARG;
   *bytes = layout(h, T, op).total;
   return SFFN_OK;
@@ -621,6 +652,201 @@ sffn_status sffn_hybrid_compact(sffn_handle* h, const sffn_twell* tw, const floa
   return SFFN_OK;
 }
 
+sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, const void* w_up,
+                          const void* w_down, const sffn_hybrid* hy, const void* dy, int64_t T,
+                          float* dx, float* dw_gate, float* dw_up, float* dw_down, float l1_coeff,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!h) return SFFN_E_ARG;
+  const sffn_desc& D = h->desc;
+  if (D.ell_cap < 1) return fail(h, SFFN_E_ARG, "the backward needs desc.ell_cap >= 1");
+  if (T < 0 || T > (int64_t)1 << 30 || T * (int64_t)D.ell_cap >= ((int64_t)1 << 31))
+    return fail(h, SFFN_E_ARG, "T out of range");
+  if (!aligned16(dw_gate) || !aligned16(dw_down) || (D.gated ? !aligned16(dw_up) : dw_up != nullptr))
+    return fail(h, SFFN_E_ARG, "dW pointers must be 16-byte aligned (dw_up iff the layer is gated)");
+  if (T == 0) {
+    // no rows: the weight gradients are zero
+    hipError_t e = hipMemsetAsync(dw_gate, 0, (size_t)D.d_ff * D.d * 4, stream);
+    if (e == hipSuccess && dw_up) e = hipMemsetAsync(dw_up, 0, (size_t)D.d_ff * D.d * 4, stream);
+    if (e == hipSuccess) e = hipMemsetAsync(dw_down, 0, (size_t)D.d_ff * D.d * 4, stream);
+    return e == hipSuccess ? SFFN_OK : hip_fail(h, e, "zero dW");
+  }
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_down) || !aligned16(dy) || !aligned16(dx))
+    return fail(h, SFFN_E_ARG, "x, weights, dy and dx must be non-null 16-byte aligned pointers");
+  if (D.gated ? !aligned16(w_up) : w_up != nullptr)
+    return fail(h, SFFN_E_ARG, "w_up must be a 16-byte aligned pointer iff the layer is gated");
+  if (!hybrid_ok(h, hy, true))
+    return fail(h, SFFN_E_ARG, "Hybrid buffers must be non-null and 16-byte aligned");
+  const Layout L = layout(h, T, SFFN_OP_BACKWARD);
+  if (!ws_ok(ws, ws_bytes, L))
+    return fail(h, SFFN_E_ARG, "workspace missing, too small or not 256-byte aligned");
+  const Dtype dt = dt_of(h);
+  const bool gated = D.gated != 0;
+  const int K = D.ell_cap;
+  const int Kp = (K + 7) / 8 * 8;
+  const int cap = (int)std::min<int64_t>(hy->max_backup, T);
+  hipError_t e;
+
+  // 1. dh = dy . W_d[j] per ELL slot, as per-slice partial dot products
+  SliceArgs sa = {};
+  sa.x = dy;
+  sa.wu = w_down;
+  sa.ell_idx = hy->ell_idx;
+  sa.ell_cnt = hy->ell_cnt;
+  sa.T = T;
+  sa.d = D.d;
+  sa.K = K;
+  sa.Kp = Kp;
+  sa.upart = at<float>(ws, L.upart);
+  {
+    ProfScope ps(h, SFFN_K_BWD_SDDMM, stream);
+    e = launch_updown(dt, true, 0, sa, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "backward dh");
+
+  BwdArgs ba = {};
+  ba.x = x;
+  ba.dy = dy;
+  ba.wg = w_gate;
+  ba.wu = w_up;
+  ba.ell_a = hy->ell_a;
+  ba.ell_u = hy->ell_u;
+  ba.ell_idx = hy->ell_idx;
+  ba.ell_cnt = hy->ell_cnt;
+  ba.slot = hy->slot;
+  ba.T = T;
+  ba.d = D.d;
+  ba.F = D.d_ff;
+  ba.K = K;
+  ba.Kp = Kp;
+  ba.l1 = l1_coeff;
+  ba.dpart = at<float>(ws, L.upart);
+  ba.gz = at<float>(ws, L.gz);
+  ba.gu = at<float>(ws, L.gu);
+  ba.dx = dx;
+  ba.dwg = dw_gate;
+  ba.dwu = dw_up;
+  ba.dwd = dw_down;
+  ba.ncnt = at<int32_t>(ws, L.ncnt);
+  ba.noff = at<int32_t>(ws, L.noff);
+  ba.ent_unsorted = at<int32_t>(ws, L.ent0);
+  ba.ent = at<int32_t>(ws, L.ent);
+  ba.brow = hy->brow;
+  ba.n_backup = hy->n_backup;
+  ba.cap = cap;
+  ba.bk_a = hy->bk_a;
+  ba.bk_u = hy->bk_u;
+  ba.dH = at<float>(ws, L.dH);
+  ba.xb = at<char>(ws, L.xb);
+  ba.dyb = at<char>(ws, L.dyb);
+  ba.gz_rm = at<char>(ws, L.gz_rm);
+  ba.gu_rm = at<char>(ws, L.gu_rm);
+  ba.gz_t = at<char>(ws, L.gz_t);
+  ba.gu_t = at<char>(ws, L.gu_t);
+  ba.gh_t = at<char>(ws, L.gh_t);
+  ba.ldt = L.ldt;
+
+  // 2. dZ, dU per slot and dx of the ELL rows
+  {
+    ProfScope ps(h, SFFN_K_BWD_DX, stream);
+    e = launch_bwd_sparse(dt, gated, 0, ba, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "backward dx");
+  // 3. slots grouped by neuron in ascending row order
+  {
+    ProfScope ps(h, SFFN_K_BWD_TRANSPOSE, stream);
+    e = launch_transpose(ba, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "backward transpose");
+  // 4. dW rows of every neuron from the ELL slots
+  {
+    ProfScope ps(h, SFFN_K_BWD_DW, stream);
+    e = launch_bwd_sparse(dt, gated, 1, ba, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "backward dW");
+
+  // 5. backup rows, densely: dH = dy W_d^T, then dZ/dU, dx rows, and dW +=
+  if (cap > 0) {
+    ProfScope ps(h, SFFN_K_BWD_DENSE, stream);
+    const bool split = dt == kBF16;
+    float* part = at<float>(ws, L.part);
+    e = launch_backup_prep(dt, gated, ba, stream);
+    if (e != hipSuccess) return hip_fail(h, e, "backup rows gather");
+    GemmArgs g = {};
+    g.A = dy;
+    g.lda = D.d;
+    g.a_rows = hy->brow;
+    g.m_dev = hy->n_backup;
+    g.m_cap = cap;
+    g.B0 = w_down;
+    g.ldb = D.d;
+    g.N = D.d_ff;
+    g.K = D.d;
+    g.out = const_cast<float*>(ba.dH);
+    g.ldo = D.d_ff;
+    g.part = part;
+    g.split_target = h->num_cu;
+    g.split_max = std::min(kSplitMax, D.d / (split ? 64 : 32));
+    g.num_cu = h->num_cu;
+    g.grid = gemm_grid(dt, 1, h->num_cu);
+    e = launch_gemm(dt, 1, false, kEpiStoreF32, g, stream);
+    if (e == hipSuccess) e = launch_splitk_reduce(g, (float*)ba.dH, D.d_ff, stream);
+    if (e == hipSuccess) e = launch_backup_grad(dt, gated, ba, stream);
+    if (e != hipSuccess) return hip_fail(h, e, "backup dH");
+    // dx rows = dZ W_g (+ dU W_u), scattered into the backup rows
+    for (int pass = 0; pass < (gated ? 2 : 1); ++pass) {
+      GemmArgs f = {};
+      f.A = pass == 0 ? ba.gz_rm : ba.gu_rm;
+      f.m_dev = hy->n_backup;
+      f.m_cap = cap;
+      f.B0 = pass == 0 ? w_gate : w_up;
+      f.ldb = D.d;
+      f.N = D.d;
+      if (split) {
+        f.lda = 2 * (int64_t)D.d_ff;
+        f.K = 2 * D.d_ff;
+        f.kwrap = D.d_ff;
+      } else {
+        f.lda = D.d_ff;
+        f.K = D.d_ff;
+      }
+      f.out = dx;
+      f.ldo = D.d;
+      f.out_rows = hy->brow;
+      f.accumulate = pass;
+      f.part = part;
+      f.split_target = h->num_cu;
+      f.split_max = std::min(kSplitMax, f.K / (split ? 64 : 32));
+      f.num_cu = h->num_cu;
+      f.grid = gemm_grid(dt, 1, h->num_cu);
+      e = launch_gemm(dt, 1, true, kEpiStoreF32, f, stream);
+      if (e == hipSuccess) e = launch_splitk_reduce(f, dx, D.d, stream);
+      if (e != hipSuccess) return hip_fail(h, e, "backup dx");
+    }
+    // dW += (dZ, dU, H)^T (x, x, dy) over the backup rows
+    for (int pass = 0; pass < 3; ++pass) {
+      if (pass == 1 && !gated) continue;
+      GemmArgs w = {};
+      w.A = pass == 0 ? ba.gz_t : (pass == 1 ? ba.gu_t : ba.gh_t);
+      w.lda = L.ldt;
+      w.M = D.d_ff;
+      w.B0 = pass == 2 ? ba.dyb : ba.xb;
+      w.ldb = D.d;
+      w.N = D.d;
+      w.k_dev = hy->n_backup;
+      w.k_cap = cap;
+      w.k_mult = split ? 2 : 1;
+      w.out = pass == 0 ? dw_gate : (pass == 1 ? dw_up : dw_down);
+      w.ldo = D.d;
+      w.accumulate = 1;
+      w.grid = gemm_grid(dt, 1, h->num_cu);
+      w.num_cu = h->num_cu;
+      e = launch_gemm(dt, 1, true, kEpiStoreF32, w, stream);
+      if (e != hipSuccess) return hip_fail(h, e, "backup dW");
+    }
+  }
+  return SFFN_OK;
+}
+
 sffn_status sffn_hybrid_check(sffn_handle* h, const sffn_hybrid* hy, hipStream_t stream) {
   if (!h || !hy || !aligned16(hy->n_backup)) return SFFN_E_ARG;
   hipError_t e = hipStreamSynchronize(stream);
@@ -683,7 +909,8 @@ const char* sffn_kernel_name(int32_t k) {
   static const char* names[SFFN_K_COUNT] = {
       "gate_gemm_twell", "flags",        "sparse_up",  "flagged_gateup", "flagged_down",
       "splitk_reduce",   "dense_gateup", "dense_down", "pack_twell",     "gate_preact",
-      "rows",            "sparse_down"};
+      "rows",            "sparse_down",  "bwd_sddmm",  "bwd_dx",         "bwd_transpose",
+      "bwd_dw",          "bwd_dense"};
   return (k >= 0 && k < SFFN_K_COUNT) ? names[k] : "";
 }
 

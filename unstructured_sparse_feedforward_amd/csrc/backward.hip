@@ -1,0 +1,444 @@
+// Sparse backward of the feedforward layer over the Hybrid format
+// ("Backpropagation ... transposes the hybrid format for gradient
+// computation without expensive dense reconstructions", gist.science
+// explainer of "Sparser, Faster, Lighter Transformer Language Models",
+// 2. Methodology B, training kernels).
+//
+// For an active slot (neuron j, activation a, up value u) of ELL row t and
+// upstream gradient dy_t: dh = dy_t . W_d[j]; dU = dh * a; dZ = dh * u + l1
+// (gated; non-gated dZ = dh + l1), the ReLU mask being the slot itself.
+// dx_t = sum dZ W_g[j] + dU W_u[j]; dW_g[j] = sum_t dZ x_t,
+// dW_u[j] = sum_t dU x_t, dW_d[j] = sum_t (a u) dy_t.
+//
+// The partial dot products dy_t . W_d[j] reuse the sliced phase-1 kernel
+// (sparse.hip). dx is accumulated per (row, d slice) like the forward's
+// down projection. dW needs the slots grouped by neuron: integer-atomic
+// counts, an exclusive scan, an atomic fill and a per-neuron sort by slot
+// index give every neuron its slots in ascending row order, so the float
+// sums of dW are accumulated in a fixed order (no float atomics).
+#include "sffn_internal.hpp"
+
+namespace sffn {
+namespace {
+
+template <typename E, int EPL> struct BV;
+template <> struct BV<uint16_t, 4> {
+  typedef u32x2_t raw;
+  __device__ static void cvt(const raw& v, float* o) {
+    o[0] = bf16lo(v[0]); o[1] = bf16hi(v[0]); o[2] = bf16lo(v[1]); o[3] = bf16hi(v[1]);
+  }
+};
+template <> struct BV<uint16_t, 8> {
+  typedef u32x4_t raw;
+  __device__ static void cvt(const raw& v, float* o) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) { o[2 * k] = bf16lo(v[k]); o[2 * k + 1] = bf16hi(v[k]); }
+  }
+};
+template <> struct BV<float, 4> {
+  typedef u32x4_t raw;
+  __device__ static void cvt(const raw& v, float* o) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = __uint_as_float(v[k]);
+  }
+};
+
+constexpr int GRP = 32;
+
+// dZ, dU per ELL slot (written by the slice-0 waves) and the row's dx slice.
+template <typename E, int NS, int EPL, bool GATED>
+__global__ __launch_bounds__(256) void dx_sparse_kernel(BwdArgs a) {
+  using V = BV<E, EPL>;
+  const int lane = threadIdx.x & 63;
+  const int s = blockIdx.x % NS;
+  const int64_t t = (int64_t)(blockIdx.x / NS) * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  if (a.slot[t] >= 0) return;  // the dense path writes backup rows
+  const int n = a.ell_cnt[t];
+  const int d = NS * 64 * EPL;
+  const int64_t col = (int64_t)s * 64 * EPL + lane * EPL;
+  const E* wg = (const E*)a.wg + col;
+  const E* wu = (const E*)a.wu + col;
+  const int64_t rb = t * (int64_t)a.K;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+  for (int k0 = 0; k0 < n; k0 += GRP) {
+    const int m = min(GRP, n - k0);
+    const int kk = k0 + min(lane, m - 1);
+    const int jl = a.ell_idx[rb + kk];
+    float dh = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NS; ++q) dh += a.dpart[((int64_t)q * a.T + t) * a.Kp + kk];
+    float dz, du = 0.0f;
+    if constexpr (GATED) {
+      du = dh * a.ell_a[rb + kk];
+      dz = dh * a.ell_u[rb + kk] + a.l1;
+    } else {
+      dz = dh + a.l1;
+    }
+    if (lane >= m) {
+      dz = 0.0f;
+      du = 0.0f;
+    }
+    if (s == 0 && lane < m) {
+      a.gz[rb + kk] = dz;
+      if (GATED) a.gu[rb + kk] = du;
+    }
+    typename V::raw w[GRP];
+    typename V::raw w2[GATED ? GRP : 1];
+#pragma unroll
+    for (int q = 0; q < GRP; ++q) {
+      const int j = __builtin_amdgcn_readlane(jl, q);
+      w[q] = *(const typename V::raw*)(wg + (int64_t)j * d);
+      if constexpr (GATED) w2[q] = *(const typename V::raw*)(wu + (int64_t)j * d);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < GRP; ++q) {
+      const float cz = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dz), q));
+      float f[EPL];
+      V::cvt(w[q], f);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(cz, f[e], acc[e]);
+      if constexpr (GATED) {
+        const float cu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(du), q));
+        V::cvt(w2[q], f);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(cu, f[e], acc[e]);
+      }
+    }
+  }
+  float* o = a.dx + t * d + col;
+#pragma unroll
+  for (int e = 0; e < EPL; e += 4) *(f32x4_t*)(o + e) = f32x4_t{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+}
+
+// ---------------------------------------------------------------- transpose
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+// One wave per row: count every ELL slot's neuron.
+__global__ __launch_bounds__(256) void count_kernel(const uint16_t* __restrict__ ell_idx,
+                                                    const int32_t* __restrict__ ell_cnt, int64_t T,
+                                                    int K, int32_t* __restrict__ ncnt) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int n = ell_cnt[t];
+  for (int k = lane; k < n; k += 64) atomicAdd(&ncnt[ell_idx[t * K + k]], 1);
+}
+
+// Exclusive scan of the F counts into F + 1 offsets; one workgroup.
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ ncnt, int F,
+                                                    int32_t* __restrict__ noff) {
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  int carry = 0;
+  for (int base = 0; base < F; base += 1024) {
+    const int j = base + tid;
+    const int c = j < F ? ncnt[j] : 0;
+    int inc = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += v;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int wbase = 0, total = 0;
+    for (int k = 0; k < 16; ++k) {
+      if (k < wave) wbase += wsum[k];
+      total += wsum[k];
+    }
+    if (j < F) noff[j] = carry + wbase + inc - c;
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) noff[F] = carry;
+}
+
+// One wave per row: place every slot (q = t*K + k) into its neuron's
+// segment at an atomically taken position (order fixed by the sort below).
+__global__ __launch_bounds__(256) void fill_kernel(const uint16_t* __restrict__ ell_idx,
+                                                   const int32_t* __restrict__ ell_cnt, int64_t T,
+                                                   int K, const int32_t* __restrict__ noff,
+                                                   int32_t* __restrict__ cursor,
+                                                   int32_t* __restrict__ ent) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int n = ell_cnt[t];
+  for (int k = lane; k < n; k += 64) {
+    const int j = ell_idx[t * K + k];
+    const int pos = noff[j] + atomicAdd(&cursor[j], 1);
+    ent[pos] = (int32_t)(t * K + k);
+  }
+}
+
+// One wave per neuron: sort its segment ascending by rank counting (slot
+// indices are distinct, so every value's rank is the number of smaller ones).
+__global__ __launch_bounds__(256) void seg_sort_kernel(const int32_t* __restrict__ noff, int F,
+                                                       const int32_t* __restrict__ ent,
+                                                       int32_t* __restrict__ sorted) {
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (j >= F) return;
+  const int b = noff[j];
+  const int n = noff[j + 1] - b;
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int v = i0 + lane < n ? ent[b + i0 + lane] : 0;
+    int rank = 0;
+    for (int c0 = 0; c0 < n; c0 += 64) {
+      const int w = c0 + lane < n ? ent[b + c0 + lane] : 0x7FFFFFFF;
+      const int m = min(64, n - c0);
+      for (int q = 0; q < m; ++q) rank += __builtin_amdgcn_readlane(w, q) < v ? 1 : 0;
+    }
+    if (i0 + lane < n) sorted[b + rank] = v;
+  }
+}
+
+// dW rows of every neuron, one wave per (neuron, d slice): the sums over
+// the neuron's ELL slots in ascending row order. Neurons without slots get
+// zero rows.
+template <typename E, int NS, int EPL, bool GATED>
+__global__ __launch_bounds__(256) void dw_sparse_kernel(BwdArgs a) {
+  using V = BV<E, EPL>;
+  const int lane = threadIdx.x & 63;
+  const int s = blockIdx.x % NS;
+  const int j = (blockIdx.x / NS) * 4 + (threadIdx.x >> 6);
+  if (j >= a.F) return;
+  const int d = NS * 64 * EPL;
+  const int64_t col = (int64_t)s * 64 * EPL + lane * EPL;
+  const E* xs = (const E*)a.x + col;
+  const E* dys = (const E*)a.dy + col;
+  float ag[EPL], au[EPL], ad[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) ag[e] = au[e] = ad[e] = 0.0f;
+  const int b = a.noff[j];
+  const int n = a.noff[j + 1] - b;
+  for (int i0 = 0; i0 < n; i0 += GRP) {
+    const int m = min(GRP, n - i0);
+    const int q = a.ent[b + i0 + min(lane, m - 1)];
+    const int tl = q / a.K;
+    float cz = a.gz[q];
+    float cu = GATED ? a.gu[q] : 0.0f;
+    float ch = GATED ? a.ell_a[q] * a.ell_u[q] : a.ell_a[q];
+    if (lane >= m) cz = cu = ch = 0.0f;
+    typename V::raw xv[GRP], dv[GRP];
+#pragma unroll
+    for (int r = 0; r < GRP; ++r) {
+      const int64_t t = __builtin_amdgcn_readlane(tl, r);
+      xv[r] = *(const typename V::raw*)(xs + t * d);
+      dv[r] = *(const typename V::raw*)(dys + t * d);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < GRP; ++r) {
+      const float z = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cz), r));
+      const float u = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cu), r));
+      const float h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ch), r));
+      float fx[EPL], fd[EPL];
+      V::cvt(xv[r], fx);
+      V::cvt(dv[r], fd);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        ag[e] = fmaf(z, fx[e], ag[e]);
+        if (GATED) au[e] = fmaf(u, fx[e], au[e]);
+        ad[e] = fmaf(h, fd[e], ad[e]);
+      }
+    }
+  }
+  const int64_t ro = (int64_t)j * d + col;
+#pragma unroll
+  for (int e = 0; e < EPL; e += 4) {
+    *(f32x4_t*)(a.dwg + ro + e) = f32x4_t{ag[e], ag[e + 1], ag[e + 2], ag[e + 3]};
+    if (GATED) *(f32x4_t*)(a.dwu + ro + e) = f32x4_t{au[e], au[e + 1], au[e + 2], au[e + 3]};
+    *(f32x4_t*)(a.dwd + ro + e) = f32x4_t{ad[e], ad[e + 1], ad[e + 2], ad[e + 3]};
+  }
+}
+
+// ---------------------------------------------------------------- backup rows
+
+// Rows r < R of x (and dy) gathered through brow into the k-stacked
+// operands of the dW GEMMs: bf16 [2Rp, d] (rows r and Rp + r both hold
+// row brow[r], others zero; the hi and lo parts of the gradient rows meet
+// the same data) or fp32 [Rp, d].
+template <typename E>
+__global__ __launch_bounds__(256) void gather_stack_kernel(const E* __restrict__ src, int d,
+                                                           const int32_t* __restrict__ brow,
+                                                           const int32_t* __restrict__ n, int cap,
+                                                           E* __restrict__ dst) {
+  constexpr int REP = sizeof(E) == 2 ? 2 : 1;
+  const int R = device_rows(n, cap);
+  const int Rp = (R + 63) / 64 * 64;
+  constexpr int EPV = 16 / sizeof(E);
+  const int dv = d / EPV;
+  const int64_t total = (int64_t)REP * Rp * dv;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int row = (int)(e / dv);
+    const int c = (int)(e - (int64_t)row * dv) * EPV;
+    const int r = row % Rp;
+    u32x4_t v = {0, 0, 0, 0};
+    if (r < R) v = *(const u32x4_t*)(src + (int64_t)brow[r] * d + c);
+    *(u32x4_t*)(dst + (int64_t)row * d + c) = v;
+  }
+}
+
+// From dH of the backup rows: dZ, dU (and H = a u for dW_d) in the layouts
+// of the GEMMs that consume them. Row-major [R, 2F] (bf16 hi | lo) or
+// [R, F] (fp32) for dx; neuron-major rows of stride ldt holding hi in
+// columns [0, Rp) and lo in [Rp, 2Rp), zero past R (bf16), or [0, Rp)
+// (fp32), for dW.
+template <typename E, bool GATED>
+__global__ __launch_bounds__(256) void backup_grad_kernel(BwdArgs a) {
+  const int R = device_rows(a.n_backup, a.cap);
+  const int Rp = (R + 63) / 64 * 64;
+  const int F = a.F;
+  const int64_t total = (int64_t)Rp * F;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(e / F);
+    const int j = (int)(e - (int64_t)r * F);
+    float dz = 0.0f, du = 0.0f, h = 0.0f;
+    if (r < R) {
+      const float dh = a.dH[(int64_t)r * F + j];
+      const float av = a.bk_a[(int64_t)r * F + j];
+      const bool on = av > 0.0f;
+      if constexpr (GATED) {
+        const float uv = a.bk_u[(int64_t)r * F + j];
+        du = dh * av;
+        dz = on ? dh * uv + a.l1 : 0.0f;
+        h = av * uv;
+      } else {
+        dz = on ? dh + a.l1 : 0.0f;
+        h = av;
+      }
+    }
+    if constexpr (sizeof(E) == 2) {
+      const uint32_t zh = f32_to_bf16(dz), uh = f32_to_bf16(du), hh = f32_to_bf16(h);
+      const uint32_t zl = f32_to_bf16(dz - __uint_as_float(zh << 16));
+      const uint32_t ul = f32_to_bf16(du - __uint_as_float(uh << 16));
+      const uint32_t hl = f32_to_bf16(h - __uint_as_float(hh << 16));
+      uint16_t* gzr = (uint16_t*)a.gz_rm;
+      uint16_t* gur = (uint16_t*)a.gu_rm;
+      uint16_t* gzt = (uint16_t*)a.gz_t;
+      uint16_t* gut = (uint16_t*)a.gu_t;
+      uint16_t* ght = (uint16_t*)a.gh_t;
+      if (r < R) {
+        gzr[(int64_t)r * 2 * F + j] = (uint16_t)zh;
+        gzr[(int64_t)r * 2 * F + F + j] = (uint16_t)zl;
+        if (GATED) {
+          gur[(int64_t)r * 2 * F + j] = (uint16_t)uh;
+          gur[(int64_t)r * 2 * F + F + j] = (uint16_t)ul;
+        }
+      }
+      const int64_t tr = (int64_t)j * a.ldt;
+      gzt[tr + r] = (uint16_t)zh;
+      gzt[tr + Rp + r] = (uint16_t)zl;
+      if (GATED) {
+        gut[tr + r] = (uint16_t)uh;
+        gut[tr + Rp + r] = (uint16_t)ul;
+      }
+      ght[tr + r] = (uint16_t)hh;
+      ght[tr + Rp + r] = (uint16_t)hl;
+    } else {
+      float* gzr = (float*)a.gz_rm;
+      float* gur = (float*)a.gu_rm;
+      if (r < R) {
+        gzr[(int64_t)r * F + j] = dz;
+        if (GATED) gur[(int64_t)r * F + j] = du;
+      }
+      const int64_t tr = (int64_t)j * a.ldt;
+      ((float*)a.gz_t)[tr + r] = dz;
+      if (GATED) ((float*)a.gu_t)[tr + r] = du;
+      ((float*)a.gh_t)[tr + r] = h;
+    }
+  }
+}
+
+template <typename E, int NS, int EPL>
+hipError_t launch_bwd_t(const BwdArgs& a, bool gated, int which, hipStream_t st) {
+  if (which == 0) {
+    const dim3 grid((unsigned)(NS * ((a.T + 3) / 4)));
+    if (gated) hipLaunchKernelGGL((dx_sparse_kernel<E, NS, EPL, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dx_sparse_kernel<E, NS, EPL, false>), grid, dim3(256), 0, st, a);
+  } else {
+    const dim3 grid((unsigned)(NS * ((a.F + 3) / 4)));
+    if (gated) hipLaunchKernelGGL((dw_sparse_kernel<E, NS, EPL, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dw_sparse_kernel<E, NS, EPL, false>), grid, dim3(256), 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_sparse(Dtype dt, bool gated, int which, const BwdArgs& a, hipStream_t s) {
+  int ns, epl;
+  slice_shape(dt, a.d, &ns, &epl);
+#define SFFN_BW(E, NS_, EPL_) \
+  if (ns == NS_ && epl == EPL_) return launch_bwd_t<E, NS_, EPL_>(a, gated, which, s);
+  if (dt == kBF16) {
+    SFFN_BW(uint16_t, 1, 4)
+    SFFN_BW(uint16_t, 2, 4)
+    SFFN_BW(uint16_t, 4, 4)
+    SFFN_BW(uint16_t, 8, 4)
+    SFFN_BW(uint16_t, 8, 8)
+  } else {
+    SFFN_BW(float, 1, 4)
+    SFFN_BW(float, 2, 4)
+    SFFN_BW(float, 4, 4)
+    SFFN_BW(float, 8, 4)
+  }
+#undef SFFN_BW
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_transpose(const BwdArgs& a, hipStream_t s) {
+  const dim3 rows((unsigned)((a.T + 3) / 4)), blk(256);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(64), blk, 0, s, a.ncnt, (int64_t)2 * a.F);
+  hipLaunchKernelGGL(count_kernel, rows, blk, 0, s, a.ell_idx, a.ell_cnt, a.T, a.K, a.ncnt);
+  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, a.ncnt, a.F, a.noff);
+  hipLaunchKernelGGL(fill_kernel, rows, blk, 0, s, a.ell_idx, a.ell_cnt, a.T, a.K, a.noff,
+                     a.ncnt + a.F, a.ent_unsorted);
+  hipLaunchKernelGGL(seg_sort_kernel, dim3((unsigned)((a.F + 3) / 4)), blk, 0, s, a.noff, a.F,
+                     a.ent_unsorted, a.ent);
+  return hipGetLastError();
+}
+
+hipError_t launch_backup_prep(Dtype dt, bool gated, const BwdArgs& a, hipStream_t s) {
+  const dim3 g(1024), b(256);
+  if (dt == kBF16) {
+    hipLaunchKernelGGL(gather_stack_kernel<uint16_t>, g, b, 0, s, (const uint16_t*)a.x, a.d,
+                       a.brow, a.n_backup, a.cap, (uint16_t*)a.xb);
+    hipLaunchKernelGGL(gather_stack_kernel<uint16_t>, g, b, 0, s, (const uint16_t*)a.dy, a.d,
+                       a.brow, a.n_backup, a.cap, (uint16_t*)a.dyb);
+  } else {
+    hipLaunchKernelGGL(gather_stack_kernel<float>, g, b, 0, s, (const float*)a.x, a.d, a.brow,
+                       a.n_backup, a.cap, (float*)a.xb);
+    hipLaunchKernelGGL(gather_stack_kernel<float>, g, b, 0, s, (const float*)a.dy, a.d, a.brow,
+                       a.n_backup, a.cap, (float*)a.dyb);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_backup_grad(Dtype dt, bool gated, const BwdArgs& a, hipStream_t s) {
+  const dim3 g(2048), b(256);
+  if (dt == kBF16) {
+    if (gated) hipLaunchKernelGGL((backup_grad_kernel<uint16_t, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((backup_grad_kernel<uint16_t, false>), g, b, 0, s, a);
+  } else {
+    if (gated) hipLaunchKernelGGL((backup_grad_kernel<float, true>), g, b, 0, s, a);
+    else hipLaunchKernelGGL((backup_grad_kernel<float, false>), g, b, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sffn

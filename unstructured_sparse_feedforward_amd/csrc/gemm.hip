@@ -102,7 +102,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
   if (M <= 0) return;
   const int mt = (M + BM - 1) / BM;
   const int ntl = g.N / BN;
-  const int nkt = g.K / BK;
+  const int Kd = g.k_dev ? g.k_mult * ((device_rows(g.k_dev, g.k_cap) + 63) / 64 * 64) : g.K;
+  const int nkt = Kd / BK;
   const int S = (EPI == kEpiStoreF32 || EPI == kEpiHiddenSplitK) ? num_splits(g, mt, ntl) : 1;
   const int ntiles = mt * ntl * S;
   const int Mpad = mt * BM;
@@ -353,7 +354,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
           const int64_t orow = g.out_rows ? g.out_rows[m] : m;
           dst = (float*)g.out + orow * g.ldo;
         }
-        *(f32x2_t*)(dst + col) = v;
+        if (g.accumulate && S == 1) {
+          *(f32x2_t*)(dst + col) += v;
+        } else {
+          *(f32x2_t*)(dst + col) = v;
+        }
       } else if constexpr (EPI == kEpiHiddenBF16) {
         uint16_t* dst = (uint16_t*)g.out + (int64_t)m * g.ldo;
         *(uint32_t*)(dst + col) = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
@@ -440,7 +445,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, float* y
     const int c = (int)(e - (int64_t)m * n4) * 4;
     f32x4_t s = *(const f32x4_t*)(g.part + (int64_t)m * g.N + c);
     for (int k = 1; k < S; ++k) s += *(const f32x4_t*)(g.part + ((int64_t)k * Mpad + m) * g.N + c);
-    *(f32x4_t*)(y + (int64_t)g.out_rows[m] * ldy + c) = s;
+    float* dst = y + (int64_t)(g.out_rows ? g.out_rows[m] : m) * ldy + c;
+    if (g.accumulate) s += *(const f32x4_t*)dst;
+    *(f32x4_t*)dst = s;
   }
 }
 

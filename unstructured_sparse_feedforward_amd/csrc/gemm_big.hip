@@ -357,7 +357,9 @@ hipError_t launch_big_t(const GemmArgs& g, hipStream_t s) {
 }  // namespace
 
 bool gemm_big_supported(Dtype dt, int nb, bool bt, Epi epi, const GemmArgs& g) {
-  if (dt != kBF16 || g.m_dev || g.a_rows || g.out_rows || g.part || g.kwrap) return false;
+  if (dt != kBF16 || g.m_dev || g.a_rows || g.out_rows || g.part || g.kwrap || g.k_dev ||
+      g.accumulate)
+    return false;
   if (g.K % BK != 0) return false;
   if (bt && nb != 1) return false;
   if (epi == kEpiTwell) return nb == 1 && !bt && g.ovf == nullptr;

@@ -107,10 +107,16 @@ struct GemmArgs {
   int N;
   int K;
   int kwrap;
+  // K from the device (when k_dev is set): K = k_mult * round_up(min(*k_dev,
+  // k_cap), 64); operands must hold zeros in their padding
+  const int32_t* k_dev;
+  int k_cap;
+  int k_mult;
   // output
   void* out;
   int64_t ldo;
   const int32_t* out_rows;   // scatter of stored rows (kEpiStoreF32)
+  int accumulate;            // kEpiStoreF32 / split-K reduce: out += result
   int act;                   // 1: ReLU on the single-B result; dual B is always ReLU(z)*u
   int lo_off;                // column offset of the lo part (kEpiHiddenSplit)
   float* out_a;              // kEpiHiddenSplitK: ReLU(z) rows, fp32 [M, ldo_au] (nullable)
@@ -207,5 +213,55 @@ void slice_shape(Dtype dt, int d, int* ns, int* epl);
 // phase 0: per-slice partial dot products (gated layers only);
 // phase 1: down projection into y.
 hipError_t launch_updown(Dtype dt, bool gated, int phase, const SliceArgs& a, hipStream_t s);
+
+// Sparse backward over a Hybrid (backward.hip).
+struct BwdArgs {
+  const void* x;          // [T, d]
+  const void* dy;         // [T, d]
+  const void* wg;         // [F, d]
+  const void* wu;         // [F, d] (gated)
+  const float* ell_a;     // [T, K]
+  const float* ell_u;     // [T, K] (gated)
+  const uint16_t* ell_idx;
+  const int32_t* ell_cnt;
+  const int32_t* slot;    // [T] backup slot or -1
+  int64_t T;
+  int d;
+  int F;
+  int K;
+  int Kp;
+  float l1;
+  const float* dpart;     // [NS, T, Kp] partial dy . W_d[j]
+  float* gz;              // [T, K] dZ per ELL slot
+  float* gu;              // [T, K] dU per ELL slot (gated)
+  float* dx;              // [T, d]
+  float* dwg;             // [F, d]
+  float* dwu;             // [F, d] (gated)
+  float* dwd;             // [F, d]
+  int32_t* ncnt;          // [2F] per-neuron counts, then fill cursors
+  int32_t* noff;          // [F + 1]
+  int32_t* ent_unsorted;  // [T*K]
+  int32_t* ent;           // [T*K] slots grouped by neuron, ascending
+  // backup rows
+  const int32_t* brow;
+  const int32_t* n_backup;
+  int cap;                // rows of the backup buffers
+  const float* bk_a;      // [cap, F]
+  const float* bk_u;      // [cap, F]
+  const float* dH;        // [cap, F]
+  void* xb;               // stacked gathered x rows
+  void* dyb;              // stacked gathered dy rows
+  void* gz_rm;            // dZ rows for dx (bf16 hi|lo [cap, 2F] or fp32 [cap, F])
+  void* gu_rm;
+  void* gz_t;             // neuron-major dZ for dW ([F, ldt])
+  void* gu_t;
+  void* gh_t;
+  int64_t ldt;
+};
+// which = 0: dZ/dU per slot and dx of the ELL rows; 1: dW of every neuron
+hipError_t launch_bwd_sparse(Dtype dt, bool gated, int which, const BwdArgs& a, hipStream_t s);
+hipError_t launch_transpose(const BwdArgs& a, hipStream_t s);
+hipError_t launch_backup_prep(Dtype dt, bool gated, const BwdArgs& a, hipStream_t s);
+hipError_t launch_backup_grad(Dtype dt, bool gated, const BwdArgs& a, hipStream_t s);
 
 }  // namespace sffn
