@@ -1,18 +1,25 @@
 #!/usr/bin/env python3
-"""Benchmark of the activation-sparse gated ReLU feedforward forward pass.
+"""Benchmark of the activation-sparse ReLU feedforward layer on one MI355X.
 
 Default workload: one gated layer at the 1.5B-model shape (T = 8192 tokens,
 d = 2048, F = 5632), bf16 inputs with fp32 accumulation, ~29 active
 neurons per token, 1% outlier tokens with ~50% active neurons, TwELL tile
 128 and capacity 8. Inputs are synthetic and seeded, resident in HBM
 before the timed region. A step is one sparse forward: gate GEMM with the
-ReLU + TwELL epilogue, overflow flags, fused sparse up/down projection and
-the dense path for flagged rows.
+ReLU + TwELL epilogue, row routing and ELL compaction, the dense path for
+rows whose TwELL overflowed, and the sparse up/down projection.
+
+Other workloads (--workload): the non-gated layer at 29/108/911 active
+neurons per token (F = 8192, T = 16384); the 18-layer gated stack
+(T = 16384 per layer, active counts ramping 15 -> 120 -> 20, each layer on
+its own seeded input); the training step (forward that saves the Hybrid
+format, then the sparse backward: T = 8192, K = 64, 5% outliers); the small
+fp32 layer.
 
 Prints one JSON line: input tokens/ms, the same library's dense layer on
-the same inputs, the roofline of the dominant kernel (timed with HIP
-events on its own stream inside the timed region) and the CPU oracle timed
-on a bounded sample on the host.
+the same inputs (forward workloads), the roofline of the dominant kernel
+(its launches bracketed by HIP events on their stream inside a timed pass)
+and the CPU oracle timed on a bounded sample on the host.
 """
 import argparse
 import json
@@ -25,9 +32,13 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "input tokens/ms, sparse gated FFN fwd d=2048 ff=5632; % MFMA/HBM roofline"
+METRIC_TRAIN = ("input tokens/ms, sparse gated FFN training step (fwd + bwd, Hybrid K=64) "
+                "d=2048 ff=5632; % MFMA/HBM roofline")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 matrix/vector
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+WORKLOADS = ("gated", "nongated29", "nongated108", "nongated911", "stack18", "train", "small")
 
 
 def _dev(inp, name, torch, np):
@@ -39,13 +50,15 @@ def _dev(inp, name, torch, np):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def _timed(fn, steps, warmup, torch, ffn=None):
-    """Run warmup + timed steps; returns (ms per step, kernel profile)."""
+def _timed(fn, steps, warmup, torch, ffns=()):
+    """Warmup, then `steps` timed steps. Returns (event ms per step, wall ms
+    per step, {kernel: (total ms, launches)} summed over `ffns` when they
+    are given, whose launches are then bracketed by HIP events)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    if ffn is not None:
-        ffn.profile(True)
+    for f in ffns:
+        f.profile(True)
     stream = torch.cuda.current_stream()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -58,16 +71,18 @@ def _timed(fn, steps, warmup, torch, ffn=None):
     wall = (time.perf_counter() - t0) * 1e3
     ev = e0.elapsed_time(e1)
     prof = {}
-    if ffn is not None:
-        prof = ffn.profile_read()
-        ffn.profile(False)
+    for f in ffns:
+        for k, (ms, n) in f.profile_read().items():
+            a, b = prof.get(k, (0.0, 0))
+            prof[k] = (a + ms, b + n)
+        f.profile(False)
     return ev / steps, wall / steps, prof
 
 
 def measured_traffic(workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary of
     this workload (profiles/traffic_<workload>.json), for each kernel whose
-    source file still hashes to what was profiled; else None."""
+    source file still hashes to what was profiled."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
@@ -86,29 +101,69 @@ def measured_traffic(workload):
     return out
 
 
-def cpu_baseline(inp, sample, np):
-    """The oracle's sparse forward (gate, TwELL pack, per-token up/down over
-    active neurons, dense rows for flagged tokens) on the first `sample`
-    tokens."""
-    import oracle
+def _threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count()
+        return os.cpu_count()
+
+
+def oracle_forward_ms(inp, n, np):
+    """Host ms of the oracle's sparse forward (gate GEMM, TwELL pack,
+    per-token up/down over the active neurons, dense rows for flagged
+    tokens) on the first n tokens of one layer."""
+    import oracle
     w = inp.wl
-    x = inp.x[:sample].astype(np.float64)
+    x = inp.x[:n].astype(np.float64)
     wg = inp.w_gate.astype(np.float64).T
     wu = None if inp.w_up is None else inp.w_up.astype(np.float64).T
     wd = inp.w_down.astype(np.float64)
     t0 = time.perf_counter()
     oracle.sparse_ffn(x, wg, wu, wd, w.tile, w.twell_cap)
-    ms = (time.perf_counter() - t0) * 1e3
-    return {"value": sample / ms, "unit": "input tokens/ms", "cores": threads,
+    return (time.perf_counter() - t0) * 1e3
+
+
+def cpu_record(tokens, ms, sample):
+    return {"value": tokens / ms, "unit": "input tokens/ms", "cores": _threads(),
             "kind": "oracle",
-            "sample": f"{sample} of {w.T} tokens, numpy float64 sparse forward "
-                      f"(gate GEMM, TwELL pack, per-token up/down, dense flagged rows); "
-                      f"{ms / 1e3:.1f} s; host os.cpu_count()={os.cpu_count()}"}
+            "sample": f"{sample}; {ms / 1e3:.1f} s; host os.cpu_count()={os.cpu_count()}"}
+
+
+def gather_work(W, cnt, flag, np):
+    """Algorithmic bytes of the sparse up/down projection of one layer:
+    per active pair of an unflagged row the weight rows it reads and its
+    (value, index); per unflagged row its x row, y row, tile counts, flag."""
+    n_flag = int(flag.sum())
+    pairs = int(cnt[~flag].sum())
+    esz = 2 if W.dtype == "bf16" else 4
+    n_t = W.F // W.tile
+    per_pair = (2 if W.gated else 1) * W.d * esz + 6
+    per_tok = W.d * esz + W.d * 4 + 4 * n_t + 1
+    return pairs * per_pair + (W.T - n_flag) * per_tok, pairs, n_flag
+
+
+def roof(kind, name, work, prof, keys, peak, traffic=None):
+    """Roofline record of one kernel (or of consecutive kernels that
+    together make one step of the path) from its per-launch average:
+    `work` is the algorithmic FLOP ("mfma") or bytes ("hbm") over all the
+    launches the profile counted."""
+    ms = sum(prof.get(k, (0.0, 0))[0] for k in keys)
+    n = max([prof.get(k, (0.0, 0))[1] for k in keys] + [0])
+    if n == 0 or ms <= 0:
+        return None
+    per_launch_ms = ms / n
+    w = work / n
+    ach = w / (per_launch_ms * 1e-3) / (1e12 if kind == "mfma" else 1e9)
+    r = {"bound": kind, "kernel": name, "achieved": ach, "peak": peak,
+         "unit": "TFLOP/s" if kind == "mfma" else "GB/s", "frac": ach / peak,
+         "traffic": traffic, "avg_ms": per_launch_ms, "launches": n}
+    r["algorithmic_flop" if kind == "mfma" else "algorithmic_bytes"] = w
+    return r
+
+
+def per_step(prof, steps):
+    return {k: ms / steps for k, (ms, n) in prof.items()}
 
 
 def main():
@@ -116,10 +171,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="gated",
-                    choices=["gated", "nongated29", "nongated108", "nongated911", "small"])
+    ap.add_argument("--workload", default="gated", choices=WORKLOADS)
     ap.add_argument("--cpu-sample", type=int, default=-1,
-                    help="tokens of the oracle CPU baseline sample (-1 = all, 0 = skip)")
+                    help="tokens of the oracle CPU baseline sample (-1 = the workload's "
+                         "default, 0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the timed work, run a plain elementwise copy of MIB MiB "
@@ -138,8 +193,6 @@ def main():
     from unstructured_sparse_feedforward_amd import SparseFFN
     from unstructured_sparse_feedforward_amd import workloads as wl
 
-    W = {"gated": wl.GATED_1P5B, "small": wl.SMALL_F32, "nongated29": wl.NONGATED[29],
-         "nongated108": wl.NONGATED[108], "nongated911": wl.NONGATED[911]}[args.workload]
     torch.cuda.set_device(0)
     if args.copy_calibration > 0:
         n = args.copy_calibration * (1 << 20) // 4
@@ -149,67 +202,97 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
-    inp = wl.make_inputs(W, seed=args.seed)
-    x, wg, wu, wd = (_dev(inp, k, torch, np) for k in ("x", "w_gate", "w_up", "w_down"))
-    ffn = SparseFFN(W.d, W.F, gated=W.gated, twell_cap=W.twell_cap, tile=W.tile,
-                    dtype=torch.bfloat16 if W.dtype == "bf16" else torch.float32)
-    y = torch.empty((W.T, W.d), dtype=torch.float32, device="cuda")
-    tw = ffn.new_twell(W.T)
-    y_dense = torch.empty_like(y)
 
-    sparse = lambda: ffn.forward(x, wg, wu, wd, mode="sparse", tw=tw, y=y)
-    dense = lambda: ffn.forward(x, wg, wu, wd, mode="dense", y=y_dense)
+    if args.workload == "train":
+        out = bench_train(args, np, torch, SparseFFN, wl)
+    else:
+        out = bench_forward(args, np, torch, SparseFFN, wl)
+    print(json.dumps(out), flush=True)
+    return 0
 
+
+def bench_forward(args, np, torch, SparseFFN, wl):
+    stack = args.workload == "stack18"
+    if stack:
+        Ws = [wl.stack_layer(i) for i in range(len(wl.STACK_RAMP))]
+    else:
+        Ws = [{"gated": wl.GATED_1P5B, "small": wl.SMALL_F32, "nongated29": wl.NONGATED[29],
+               "nongated108": wl.NONGATED[108],
+               "nongated911": wl.NONGATED[911]}[args.workload]]
+    W0 = Ws[0]
+    if args.cpu_sample < 0:
+        n_cpu = (256 if stack else 2048 if W0.F == 8192 else W0.T)
+    else:
+        n_cpu = min(args.cpu_sample, W0.T)
+    layers, cpu_ms = [], 0.0
+    for i, W in enumerate(Ws):
+        inp = wl.make_inputs(W, seed=args.seed, layer=i)
+        # the oracle's host time on this layer's first n_cpu tokens
+        if n_cpu > 0:
+            cpu_ms += oracle_forward_ms(inp, n_cpu, np)
+        ffn = SparseFFN(W.d, W.F, gated=W.gated, twell_cap=W.twell_cap, tile=W.tile,
+                        dtype=torch.bfloat16 if W.dtype == "bf16" else torch.float32)
+        y = torch.empty((W.T, W.d), dtype=torch.float32, device="cuda")
+        layers.append(dict(W=W, ffn=ffn, tw=ffn.new_twell(W.T), y=y, yd=torch.empty_like(y),
+                           args=[_dev(inp, k, torch, np)
+                                 for k in ("x", "w_gate", "w_up", "w_down")]))
+        del inp
+        if stack:
+            print(f"layer {i} on the device", file=sys.stderr, flush=True)
+
+    def sparse():
+        for L in layers:
+            L["ffn"].forward(*L["args"], mode="sparse", tw=L["tw"], y=L["y"])
+
+    def dense():
+        for L in layers:
+            L["ffn"].forward(*L["args"], mode="dense", y=L["yd"])
+
+    ffns = [L["ffn"] for L in layers]
     # timed region: K sparse steps, then K dense steps on the same inputs
-    ms, wall_ms, _ = _timed(sparse, args.steps, args.warmup, torch, None)
-    ms_d, wall_d, _ = _timed(dense, args.steps, args.warmup, torch, None)
+    ms, wall_ms, _ = _timed(sparse, args.steps, args.warmup, torch)
+    ms_d, _, _ = _timed(dense, args.steps, args.warmup, torch)
     # the same steps again with every kernel bracketed by HIP events on the
     # launch stream, for the per-kernel durations
-    ms_p, _, prof = _timed(sparse, args.steps, 0, torch, ffn)
-    _, _, prof_d = _timed(dense, args.steps, 0, torch, ffn)
-
-    # algorithmic work of the two main kernels
+    ms_p, _, prof = _timed(sparse, args.steps, 0, torch, ffns)
+    _, _, prof_d = _timed(dense, args.steps, 0, torch, ffns)
     torch.cuda.synchronize()
-    cnt = tw["cnt"].cpu().numpy()
-    flag = tw["row_flag"].cpu().numpy().astype(bool)
-    n_flag = int(flag.sum())
-    pairs = int(cnt[~flag].sum())
-    esz = 2 if W.dtype == "bf16" else 4
-    n_un = W.T - n_flag
-    n_t = W.F // W.tile
-    per_pair = (2 if W.gated else 1) * W.d * esz + 6          # weight rows + (val, idx)
-    per_tok = W.d * esz + W.d * 4 + 4 * n_t + 1               # x, y, counts, flag
-    gather_bytes = pairs * per_pair + n_un * per_tok
-    gate_flops = 2.0 * W.T * W.d * W.F
 
-    def avg(p, k):
-        t, n = p.get(k, (0.0, 0))
-        return t / n if n else float("nan")
-
-    t_gate = avg(prof, "gate_gemm_twell")
+    gbytes, pairs, n_flag = 0.0, 0, 0
+    for L in layers:
+        b, p, nf = gather_work(L["W"], L["tw"]["cnt"].cpu().numpy(),
+                               L["tw"]["row_flag"].cpu().numpy().astype(bool), np)
+        gbytes += b
+        pairs += p
+        n_flag += nf
+    flops = sum(2.0 * W.T * W.d * W.F for W in Ws)
+    peak_mm = PEAK_BF16_TFLOPS if W0.dtype == "bf16" else PEAK_F32_TFLOPS
+    traffic = measured_traffic(W0.name) if not stack else {}
+    r_gate = roof("mfma", "gate_gemm_twell", flops * args.steps, prof, ["gate_gemm_twell"],
+                  peak_mm, traffic.get("gate_gemm_twell"))
     # the sparse up/down projection is two kernels (per-slice partial dot
-    # products, then the down projection); its time is their sum
-    t_gath = (avg(prof, "sparse_up") if W.gated else 0.0) + avg(prof, "sparse_down")
-    peak_mm = PEAK_BF16_TFLOPS if W.dtype == "bf16" else PEAK_F32_TFLOPS
-    roof_gate = {"bound": "mfma", "kernel": "gate_gemm_twell",
-                 "achieved": gate_flops / (t_gate * 1e-3) / 1e12, "peak": peak_mm,
-                 "unit": "TFLOP/s", "traffic": None, "avg_ms": t_gate}
-    roof_gate["frac"] = roof_gate["achieved"] / peak_mm
-    roof_gath = {"bound": "hbm", "kernel": "sparse_up + sparse_down",
-                 "achieved": gather_bytes / (t_gath * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                 "unit": "GB/s", "traffic": None, "avg_ms": t_gath,
-                 "algorithmic_bytes": gather_bytes, "active_pairs": pairs}
-    roof_gath["frac"] = roof_gath["achieved"] / PEAK_HBM_GBS
-    traffic = measured_traffic(W.name)
-    if "gate_gemm_twell" in traffic:
-        roof_gate["traffic"] = traffic["gate_gemm_twell"]
-    if "sparse_up" in traffic and "sparse_down" in traffic:
-        roof_gath["traffic"] = traffic["sparse_up"] + traffic["sparse_down"]
-    dominant, other = (roof_gate, roof_gath) if t_gate >= t_gath else (roof_gath, roof_gate)
-
+    # products, then the down projection); a launch of it is one of each
+    keys = ["sparse_up", "sparse_down"] if W0.gated else ["sparse_down"]
+    tr = (traffic["sparse_up"] + traffic["sparse_down"]
+          if "sparse_up" in traffic and "sparse_down" in traffic else None)
+    r_gath = roof("hbm", " + ".join(keys), gbytes * args.steps, prof, keys, PEAK_HBM_GBS, tr)
+    r_gath["active_pairs_per_step"] = pairs
+    dominant, other = ((r_gate, r_gath) if r_gate["avg_ms"] >= r_gath["avg_ms"]
+                       else (r_gath, r_gate))
+    T = W0.T
+    cfg = {"workload": W0.name, "T": T, "d": W0.d, "d_ff": W0.F, "gated": W0.gated,
+           "nnz_per_token": W0.nnz, "twell_tile": W0.tile, "twell_cap": W0.twell_cap,
+           "outlier_frac": W0.outlier_frac, "seed": args.seed}
+    if stack:
+        cfg.update(workload=wl.STACK_LAYER.name, layers=len(Ws),
+                   nnz_per_token=list(wl.STACK_RAMP),
+                   front_positions=W0.front_positions, front_prob=W0.front_prob,
+                   seq_len=W0.seq_len)
     out = {
-        "metric": METRIC,
-        "value": W.T / ms,
+        "metric": METRIC if not stack else
+        "input tokens/ms through 18 sparse gated FFN layers (fwd) d=2048 ff=5632; "
+        "% MFMA/HBM roofline",
+        "value": T / ms,
         "unit": "input tokens/ms",
         "n_gpus": 1,
         "steps": args.steps,
@@ -218,26 +301,127 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": W.dtype,
+        "dtype": W0.dtype,
         "data": "synthetic",
-        "config": {"workload": W.name, "T": W.T, "d": W.d, "d_ff": W.F, "gated": W.gated,
-                   "nnz_per_token": W.nnz, "twell_tile": W.tile, "twell_cap": W.twell_cap,
-                   "outlier_frac": W.outlier_frac, "seed": args.seed},
+        "config": cfg,
         "roofline": dominant,
         "roofline_other": other,
-        "dense_baseline": {"value": W.T / ms_d, "ms_per_step": ms_d,
+        "dense_baseline": {"value": T / ms_d, "ms_per_step": ms_d,
                            "speedup_sparse_over_dense": ms_d / ms,
-                           "kernels_avg_ms": {k: avg(prof_d, k) for k in prof_d}},
-        "kernels_avg_ms": {k: avg(prof, k) for k in prof},
+                           "kernels_ms_per_step": per_step(prof_d, args.steps)},
+        "kernels_ms_per_step": per_step(prof, args.steps),
         "ms_per_step_wall": wall_ms,
         "ms_per_step_with_kernel_events": ms_p,
-        "flagged_rows": n_flag,
+        "flagged_rows_per_step": n_flag,
     }
-    if args.cpu_sample != 0:
-        n = W.T if args.cpu_sample < 0 else min(args.cpu_sample, W.T)
-        out["cpu_baseline"] = cpu_baseline(inp, n, np)
-    print(json.dumps(out), flush=True)
-    return 0
+    if n_cpu > 0:
+        what = (f"first {n_cpu} tokens of each of the {len(Ws)} layers" if stack
+                else f"first {n_cpu} of {T} tokens")
+        out["cpu_baseline"] = cpu_record(
+            n_cpu, cpu_ms,
+            f"{what}: numpy float64 sparse forward (gate GEMM, TwELL pack, per-token "
+            f"up/down over active neurons, dense flagged rows)")
+    return out
+
+
+def bench_train(args, np, torch, SparseFFN, wl):
+    import oracle
+    W = wl.TRAIN_HYBRID
+    inp = wl.make_inputs(W, seed=args.seed)
+    n_cpu = (1024 if args.cpu_sample < 0 else min(args.cpu_sample, W.T))
+    cpu_ms = 0.0
+    if n_cpu > 0:
+        # the oracle's training step: its float64 forward and backward
+        x = inp.x[:n_cpu].astype(np.float64)
+        wg = inp.w_gate.astype(np.float64).T
+        wu = inp.w_up.astype(np.float64).T
+        wd = inp.w_down.astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.backward(x, wg, wu, wd, inp.dy[:n_cpu].astype(np.float64))
+        cpu_ms = (time.perf_counter() - t0) * 1e3
+        del x, wg, wu, wd
+    a = [_dev(inp, k, torch, np) for k in ("x", "w_gate", "w_up", "w_down")]
+    dy = _dev(inp, "dy", torch, np)
+    del inp
+    d, F, T = W.d, W.F, W.T
+    ffn = SparseFFN(d, F, gated=True, twell_cap=W.twell_cap, ell_cap=W.ell_cap,
+                    dtype=torch.bfloat16)
+    hy = ffn.new_hybrid(T)
+    tw = ffn.new_twell(T)
+    y = torch.empty((T, d), dtype=torch.float32, device="cuda")
+    f32 = dict(dtype=torch.float32, device="cuda")
+    grads = (torch.empty((T, d), **f32), torch.empty((F, d), **f32),
+             torch.empty((F, d), **f32), torch.empty((F, d), **f32))
+
+    def step():
+        ffn.forward_train(*a, hy=hy, tw=tw, y=y)
+        ffn.backward(*a, hy, dy, out=grads)
+
+    ms, wall_ms, _ = _timed(step, args.steps, args.warmup, torch)
+    ms_p, _, prof = _timed(step, args.steps, 0, torch, [ffn])
+    torch.cuda.synchronize()
+    if ffn.hybrid_check(hy) != 0:
+        raise RuntimeError("backup rows exceed the Hybrid's capacity")
+    cnt = hy["ell_cnt"].cpu().numpy().astype(np.int64)
+    slot = hy["slot"].cpu().numpy()[:T]
+    nb = int(hy["n_backup"][0].item())
+    P = int(cnt.sum())               # ELL slots (active pairs of ELL rows)
+    R = int((slot < 0).sum())        # ELL rows
+    S = args.steps
+    # algorithmic bytes per step of the gather-bound kernels (bf16 operands):
+    # forward up/down: per slot W_u, W_d rows + (a, u, idx) saved; per row x, y
+    fwd = P * (2 * d * 2 + 10) + R * (d * 2 + d * 4)
+    # dH = dy . W_d[j] per slot: the W_d row and the index; per row the dy row
+    sddmm = P * (d * 2 + 2) + R * d * 2
+    # dx: per slot W_g, W_u rows, (idx, a, u, dh partial) in, (dZ, dU) out;
+    # per row the dx row
+    bdx = P * (2 * d * 2 + 2 + 12 + 8) + R * d * 4
+    # dW: per slot the x and dy rows and (dZ, dU, a, u, slot id); per neuron
+    # its three dW rows
+    bdw = P * (2 * d * 2 + 20) + F * 3 * d * 4
+    rs = [roof("mfma", "gate_gemm_twell", 2.0 * T * d * F * S, prof, ["gate_gemm_twell"],
+               PEAK_BF16_TFLOPS),
+          roof("hbm", "sparse_up + sparse_down", fwd * S, prof, ["sparse_up", "sparse_down"],
+               PEAK_HBM_GBS),
+          roof("hbm", "bwd_sddmm", sddmm * S, prof, ["bwd_sddmm"], PEAK_HBM_GBS),
+          roof("hbm", "bwd_dx", bdx * S, prof, ["bwd_dx"], PEAK_HBM_GBS),
+          roof("hbm", "bwd_dw", bdw * S, prof, ["bwd_dw"], PEAK_HBM_GBS)]
+    rs = [r for r in rs if r is not None]
+    ks = per_step(prof, S)
+    rs.sort(key=lambda r: -r["avg_ms"] * r["launches"])
+    out = {
+        "metric": METRIC_TRAIN,
+        "value": T / ms,
+        "unit": "input tokens/ms",
+        "n_gpus": 1,
+        "steps": S,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": W.dtype,
+        "data": "synthetic",
+        "config": {"workload": W.name, "T": T, "d": d, "d_ff": F, "gated": True,
+                   "nnz_per_token": W.nnz, "twell_cap": W.twell_cap, "ell_cap": W.ell_cap,
+                   "outlier_frac": W.outlier_frac, "seed": args.seed},
+        "roofline": rs[0],
+        "roofline_other": rs[1:],
+        "dense_baseline": None,
+        "kernels_ms_per_step": ks,
+        "ms_per_step_wall": wall_ms,
+        "ms_per_step_with_kernel_events": ms_p,
+        "backup_rows": nb,
+        "ell_slots": P,
+        "saved_activation_bytes": {
+            "hybrid": int(T * W.ell_cap * 10 + T * 8 + nb * (F * 8 + 4)),
+            "dense_a_u_fp32": int(T * F * 8)},
+    }
+    if n_cpu > 0:
+        out["cpu_baseline"] = cpu_record(
+            n_cpu, cpu_ms, f"first {n_cpu} of {T} tokens: numpy float64 forward and backward "
+                           f"(the gradients of x and of all three weights)")
+    return out
 
 
 if __name__ == "__main__":

@@ -203,3 +203,48 @@ def test_backward_all_rows_backup():
     assert_close_bf16(dwg.cpu().numpy(), ref["dw_gate"].T, "dw_gate")
     assert_close_bf16(dwu.cpu().numpy(), ref["dw_up"].T, "dw_up")
     assert_close_bf16(dwd.cpu().numpy(), ref["dw_down"], "dw_down")
+
+
+def test_training_full_size_sampled():
+    """The training step at its full size (T = 8192, d = 2048, F = 5632,
+    K = 64, 5% outlier tokens) in the launch configuration the benchmark
+    times. dx rows depend only on their own token, so the oracle's
+    backward on the sampled rows gives them exactly; dW columns of a
+    neuron set J depend only on J's weights, so the oracle's backward of
+    the layer restricted to J gives them exactly. Rows and neurons with a
+    pre-activation within 2e-5 of 0 are left out of the sample."""
+    w = wl.TRAIN_HYBRID
+    _print(f"training full size {w.name}")
+    inp = wl.make_inputs(w, seed=11)
+    ffn = SparseFFN(w.d, w.F, gated=True, twell_cap=w.twell_cap, ell_cap=w.ell_cap,
+                    dtype=torch.bfloat16)
+    args = [dev(inp, k) for k in ("x", "w_gate", "w_up", "w_down")]
+    y, hyd = ffn.forward_train(*args)
+    assert ffn.hybrid_check(hyd) == B.SFFN_OK
+    dx, dwg, dwu, dwd = ffn.backward(*args, hyd, dev(inp, "dy"))
+    torch.cuda.synchronize()
+    slot = hyd["slot"].cpu().numpy()[:w.T]
+    nb = int(hyd["n_backup"][0].item())
+    _print("  backup rows:", nb)
+    assert 0 < nb < w.T // 4
+    wg, wu, wd = math_weights(inp)
+    x64, dy64 = inp.x.astype(np.float64), inp.dy.astype(np.float64)
+    rng = np.random.default_rng(0)
+    # rows: ELL rows and backup rows, with all their |z| > 2e-5
+    ell_rows = rng.choice(np.flatnonzero(slot < 0), 96, replace=False)
+    bk_rows = rng.choice(np.flatnonzero(slot >= 0), min(nb, 32), replace=False)
+    rows = np.sort(np.concatenate([ell_rows, bk_rows]))
+    rows = rows[np.abs(x64[rows] @ wg).min(axis=1) > 2e-5]
+    assert rows.size > 100
+    ref = oracle.backward(x64[rows], wg, wu, wd, dy64[rows])
+    yr, _ = oracle.dense_ffn(x64[rows], wg, wu, wd)
+    assert_close_bf16(y.cpu().numpy()[rows], yr, "y rows")
+    assert_close_bf16(dx.cpu().numpy()[rows], ref["dx"], "dx rows")
+    # neurons: a random set whose pre-activations over all T tokens keep |z| > 2e-5
+    J = np.sort(rng.choice(w.F, 96, replace=False))
+    J = J[np.abs(x64 @ wg[:, J]).min(axis=0) > 2e-5]
+    assert J.size > 64
+    refJ = oracle.backward(x64, wg[:, J], wu[:, J], wd[J], dy64)
+    assert_close_bf16(dwg.cpu().numpy()[J], refJ["dw_gate"].T, "dw_gate neurons")
+    assert_close_bf16(dwu.cpu().numpy()[J], refJ["dw_up"].T, "dw_up neurons")
+    assert_close_bf16(dwd.cpu().numpy()[J], refJ["dw_down"], "dw_down neurons")

@@ -291,15 +291,19 @@ class SparseFFN:
                                                 ws, n, _stream()), "sffn_forward_train")
         return y, hy
 
-    def backward(self, x, w_gate, w_up, w_down, hy, dy, l1_coeff: float = 0.0):
+    def backward(self, x, w_gate, w_up, w_down, hy, dy, l1_coeff: float = 0.0, out=None):
         """Gradients (dx [T, d], dw_gate, dw_up, dw_down [F, d]; float32) of
-        the step whose Hybrid ``hy`` sffn_forward_train saved."""
+        the step whose Hybrid ``hy`` sffn_forward_train saved. ``out`` may
+        pass the four output tensors (dw_up None when non-gated) to reuse."""
         T = x.shape[0]
         f32 = dict(dtype=torch.float32, device=x.device)
-        dx = torch.empty((T, self.d), **f32)
-        dwg = torch.empty((self.d_ff, self.d), **f32)
-        dwu = torch.empty((self.d_ff, self.d), **f32) if self.gated else None
-        dwd = torch.empty((self.d_ff, self.d), **f32)
+        if out is not None:
+            dx, dwg, dwu, dwd = out
+        else:
+            dx = torch.empty((T, self.d), **f32)
+            dwg = torch.empty((self.d_ff, self.d), **f32)
+            dwu = torch.empty((self.d_ff, self.d), **f32) if self.gated else None
+            dwd = torch.empty((self.d_ff, self.d), **f32)
         ws, n = self.workspace(T, SFFN_OP_BACKWARD, x.device)
         hs = self._hy_struct(hy)
         self._check(self.lib.sffn_backward(self.h, _ptr(x), _ptr(w_gate), _ptr(w_up),
