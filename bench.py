@@ -270,9 +270,10 @@ def bench_forward(args, np, torch, SparseFFN, wl):
     traffic = measured_traffic(W0.name) if not stack else {}
     r_gate = roof("mfma", "gate_gemm_twell", flops * args.steps, prof, ["gate_gemm_twell"],
                   peak_mm, traffic.get("gate_gemm_twell"))
-    # the sparse up/down projection is two kernels (per-slice partial dot
-    # products, then the down projection); a launch of it is one of each
-    keys = ["sparse_up", "sparse_down"] if W0.gated else ["sparse_down"]
+    # the sparse up/down projection is three kernels (per-slice partial dot
+    # products, their sums h = a * u, the down projection); a launch of it
+    # is one of each
+    keys = ["sparse_up", "sparse_hsum", "sparse_down"] if W0.gated else ["sparse_down"]
     tr = (traffic["sparse_up"] + traffic["sparse_down"]
           if "sparse_up" in traffic and "sparse_down" in traffic else None)
     r_gath = roof("hbm", " + ".join(keys), gbytes * args.steps, prof, keys, PEAK_HBM_GBS, tr)
@@ -381,8 +382,8 @@ def bench_train(args, np, torch, SparseFFN, wl):
     bdw = P * (2 * d * 2 + 20) + F * 3 * d * 4
     rs = [roof("mfma", "gate_gemm_twell", 2.0 * T * d * F * S, prof, ["gate_gemm_twell"],
                PEAK_BF16_TFLOPS),
-          roof("hbm", "sparse_up + sparse_down", fwd * S, prof, ["sparse_up", "sparse_down"],
-               PEAK_HBM_GBS),
+          roof("hbm", "sparse_up + sparse_hsum + sparse_down", fwd * S, prof,
+               ["sparse_up", "sparse_hsum", "sparse_down"], PEAK_HBM_GBS),
           roof("hbm", "bwd_sddmm", sddmm * S, prof, ["bwd_sddmm"], PEAK_HBM_GBS),
           roof("hbm", "bwd_dx", bdx * S, prof, ["bwd_dx"], PEAK_HBM_GBS),
           roof("hbm", "bwd_dw", bdw * S, prof, ["bwd_dw"], PEAK_HBM_GBS)]

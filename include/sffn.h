@@ -291,7 +291,8 @@ sffn_status sffn_check(sffn_handle* h, hipStream_t stream);
 #define SFFN_K_BWD_TRANSPOSE 14 /* backward: ELL slots grouped by neuron */
 #define SFFN_K_BWD_DW       15  /* backward: dW rows from the ELL slots */
 #define SFFN_K_BWD_DENSE    16  /* backward: the backup rows' dense GEMMs */
-#define SFFN_K_COUNT        17
+#define SFFN_K_SPARSE_HSUM  17  /* sparse up projection: slice partials summed, h = a * u */
+#define SFFN_K_COUNT        18
 sffn_status sffn_profile_enable(sffn_handle* h, int32_t enable);
 sffn_status sffn_profile_read(sffn_handle* h, double* total_ms, int32_t* launches, int32_t n);
 /* Static name of a kernel id ("" if out of range). */

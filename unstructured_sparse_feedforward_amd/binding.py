@@ -38,7 +38,7 @@ EXPORTS = ("sffn_create", "sffn_destroy", "sffn_last_error", "sffn_status_string
            "sffn_forward", "sffn_check", "sffn_profile_enable", "sffn_profile_read",
            "sffn_kernel_name", "sffn_hybrid_compact", "sffn_forward_train",
            "sffn_hybrid_check", "sffn_backward")
-SFFN_K_COUNT = 17
+SFFN_K_COUNT = 18
 
 
 class SffnDesc(ctypes.Structure):

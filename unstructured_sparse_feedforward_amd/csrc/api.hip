@@ -548,6 +548,10 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     ProfScope ps(h, SFFN_K_SPARSE_UP, stream);
     e = launch_updown(dt, true, 0, sa, stream);
   }
+  if (D.gated && e == hipSuccess) {
+    ProfScope ps(h, SFFN_K_SPARSE_HSUM, stream);
+    e = launch_updown(dt, true, 2, sa, stream);
+  }
   if (e == hipSuccess) {
     ProfScope ps(h, SFFN_K_SPARSE_DOWN, stream);
     e = launch_updown(dt, D.gated != 0, 1, sa, stream);
@@ -910,7 +914,7 @@ const char* sffn_kernel_name(int32_t k) {
       "gate_gemm_twell", "flags",        "sparse_up",  "flagged_gateup", "flagged_down",
       "splitk_reduce",   "dense_gateup", "dense_down", "pack_twell",     "gate_preact",
       "rows",            "sparse_down",  "bwd_sddmm",  "bwd_dx",         "bwd_transpose",
-      "bwd_dw",          "bwd_dense"};
+      "bwd_dw",          "bwd_dense",    "sparse_hsum"};
   return (k >= 0 && k < SFFN_K_COUNT) ? names[k] : "";
 }
 

@@ -211,6 +211,7 @@ struct SliceArgs {
 };
 void slice_shape(Dtype dt, int d, int* ns, int* epl);
 // phase 0: per-slice partial dot products (gated layers only);
+// phase 2: their sums u and h = a * u (gated; h over slice 0's partials);
 // phase 1: down projection into y.
 hipError_t launch_updown(Dtype dt, bool gated, int phase, const SliceArgs& a, hipStream_t s);
 

@@ -180,31 +180,95 @@ __device__ __forceinline__ float wave_sum32(float* v, int lane) {
   return v[0] + __shfl_xor(v[0], 1, 64);
 }
 
-// Phase 1: upart[s][t][k] = x_t[slice s] . W_u[j_k][slice s].
-template <typename E, int NS, int EPL>
-__global__ __launch_bounds__(256) void up_partial_kernel(SliceArgs a) {
+// Each lane loads 16 bytes of a weight row slice per pair: a slice of
+// SW elements takes LPR = SW * sizeof(E) / 16 lanes, so a wave covers
+// RPW = 64 / LPR rows at once (two rows of a 256-wide bf16 slice, one row
+// otherwise). Wide loads halve the load instructions per byte, which is
+// what bounds these gathers. Pairs go 32 per row per group: lane i of a
+// row's lane group holds the metadata of slot k0 + i (lanes 32-63 repeat
+// lanes 0-31 when a row spans the whole wave). The metadata loads do not
+// wait for the row's count (the slot index is clamped to the row's K
+// slots), so a group costs one round trip for the metadata and one for the
+// weight rows. Slots past the count read neuron 0 and are discarded (ELL
+// padding is unspecified).
+template <typename E, int SW>
+struct SliceGeom {
+  static constexpr int EPL = 16 / (int)sizeof(E);
+  static constexpr int LPR = SW / EPL;
+  static constexpr int RPW = 64 / LPR;
+  static_assert(RPW == 1 || RPW == 2, "slice of 32 or 64 lanes");
   using V = Vec<E, EPL>;
+  using R = typename V::raw;
+};
+
+// The neuron id of slot q of this lane's row, from the 32 ids held by the
+// row's lanes (wave-uniform index).
+template <int RPW>
+__device__ __forceinline__ int slot_id(int jl, int q, int hf) {
+  if constexpr (RPW == 2) {
+    const int j0 = __builtin_amdgcn_readlane(jl, q);
+    const int j1 = __builtin_amdgcn_readlane(jl, 32 + q);
+    return hf ? j1 : j0;
+  } else {
+    return __builtin_amdgcn_readlane(jl, q);
+  }
+}
+template <int RPW>
+__device__ __forceinline__ float slot_val(float v, int q, int hf) {
+  return __int_as_float(slot_id<RPW>(__float_as_int(v), q, hf));
+}
+
+// Phase 1: upart[s][t][k] = x_t[slice s] . W_u[j_k][slice s].
+template <typename E, int NS, int SW>
+__global__ __launch_bounds__(256) void up_partial_kernel(SliceArgs a) {
+  using G = SliceGeom<E, SW>;
+  constexpr int EPL = G::EPL, RPW = G::RPW;
+  using R = typename G::R;
   const int lane = threadIdx.x & 63;
+  const int hf = RPW == 2 ? lane >> 5 : 0;
+  const int l = lane & (G::LPR - 1);
+  const int i = lane & 31;
   const int s = blockIdx.x % NS;
-  const int64_t t = (int64_t)(blockIdx.x / NS) * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
-  const int n = a.ell_cnt[t];
-  if (n == 0) return;
-  const int d = NS * 64 * EPL;
-  const int64_t col = (int64_t)s * 64 * EPL + lane * EPL;
+  const int64_t t = ((int64_t)(blockIdx.x / NS) * 4 + (threadIdx.x >> 6)) * RPW + hf;
+  if (t - hf >= a.T) return;
+  const bool ok = t < a.T;
+  const int64_t tr = ok ? t : a.T - 1;
+  const int d = NS * SW;
+  const int64_t col = (int64_t)s * SW + l * EPL;
+  // weight rows are addressed as a uniform base plus a 32-bit byte offset
+  // (F * d * sizeof(E) < 4 GiB), so a load needs one offset register
+  const char* wu = (const char*)a.wu;
+  const uint32_t colb = (uint32_t)(col * sizeof(E));
+  const uint32_t rowb = (uint32_t)(d * sizeof(E));
+  const int64_t rb = tr * a.K;
+  // count, x slice and the first group's ids, all at once
+  const int n = ok ? a.ell_cnt[tr] : 0;
+  const R xv = *(const R*)((const E*)a.x + tr * d + col);
+  int jraw = a.ell_idx[rb + min(i, a.K - 1)];
+  int nmax = __builtin_amdgcn_readlane(n, 0);
+  if constexpr (RPW == 2) nmax = max(nmax, __builtin_amdgcn_readlane(n, 32));
+  if (nmax == 0) return;
   float xr[EPL];
-  V::cvt(*(const typename V::raw*)((const E*)a.x + t * d + col), xr);
-  const E* wu = (const E*)a.wu + col;
-  const uint16_t* li = a.ell_idx + t * (int64_t)a.K;
-  float* up = a.upart + ((int64_t)s * a.T + t) * a.Kp;
-  for (int k0 = 0; k0 < n; k0 += GRP) {
-    const int m = min(GRP, n - k0);
-    const int jl = li[k0 + min(lane, m - 1)];
-    typename V::raw w[GRP];
+  G::V::cvt(xv, xr);
+  float* up = a.upart + ((int64_t)s * a.T + tr) * a.Kp;
+  for (int k0 = 0; k0 < nmax; k0 += GRP) {
+    if (k0 > 0) jraw = a.ell_idx[rb + min(k0 + i, a.K - 1)];
+    const bool live = k0 + i < n;
+    const int jl = live ? jraw : 0;
+    // blocks of 8 slots that some row of the wave has (wave-uniform);
+    // totals of the other slots are never stored
+    const int nb = (min(GRP, nmax - k0) + 7) >> 3;
+    R w[GRP];
 #pragma unroll
-    for (int q = 0; q < GRP; ++q) {
-      const int j = __builtin_amdgcn_readlane(jl, q);
-      w[q] = *(const typename V::raw*)(wu + (int64_t)j * d);
+    for (int b = 0; b < GRP / 8; ++b) {
+      if (b < nb) {
+#pragma unroll
+        for (int q = 8 * b; q < 8 * b + 8; ++q)
+          w[q] = *(const R*)(wu + ((uint32_t)slot_id<RPW>(jl, q, hf) * rowb + colb));
+      } else {
+#pragma unroll
+        for (int q = 8 * b; q < 8 * b + 8; ++q) w[q] = R{};
+      }
     }
     // keep every load of the group in flight before the first use
     __builtin_amdgcn_sched_barrier(0);
@@ -212,79 +276,122 @@ __global__ __launch_bounds__(256) void up_partial_kernel(SliceArgs a) {
 #pragma unroll
     for (int q = 0; q < GRP; ++q) {
       float f[EPL];
-      V::cvt(w[q], f);
+      G::V::cvt(w[q], f);
       float acc = 0.0f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc = fmaf(xr[e], f[e], acc);
       p[q] = acc;
     }
-    const float u = wave_sum32(p, lane);
-    const int q = lane >> 1;
-    if ((lane & 1) == 0 && q < m) up[k0 + q] = u;
+    if constexpr (RPW == 2) {
+      // totals over the 32 lanes of each row: lane i ends with slot k0 + i
+      butterfly<16, 16>(p, lane);
+      if (live) up[k0 + i] = p[0];
+    } else {
+      const float u = wave_sum32(p, lane);
+      const int q = lane >> 1;
+      if ((lane & 1) == 0 && k0 + q < n) up[k0 + q] = u;
+    }
   }
 }
 
-// Phase 2: y_t[slice s] = sum_k a_k * (sum_s' upart[s'][t][k]) * W_d[j_k][slice s]
-// (non-gated: h_k = a_k). Rows routed to the dense backup are skipped.
-template <typename E, int NS, int EPL, bool GATED>
-__global__ __launch_bounds__(256) void down_kernel(SliceArgs a) {
-  using V = Vec<E, EPL>;
+// Between the phases (gated): u_k = sum of the slice partials in slice
+// order and h_k = a_k * u_k, written over slice 0's partial (the lane that
+// reads a slot's partials is the one that writes it); u_k is saved for
+// training. One wave per row.
+template <int NS>
+__global__ __launch_bounds__(256) void hsum_kernel(SliceArgs a) {
   const int lane = threadIdx.x & 63;
-  const int s = blockIdx.x % NS;
-  const int64_t t = (int64_t)(blockIdx.x / NS) * 4 + (threadIdx.x >> 6);
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
-  if (a.bk[t]) return;
   const int n = a.ell_cnt[t];
-  const int d = NS * 64 * EPL;
-  const int64_t col = (int64_t)s * 64 * EPL + lane * EPL;
-  const E* wd = (const E*)a.wd + col;
-  const int64_t rb = t * (int64_t)a.K;
+  for (int k = lane; k < n; k += 64) {
+    float u = 0.0f;
+#pragma unroll
+    for (int r = 0; r < NS; ++r) u += a.upart[((int64_t)r * a.T + t) * a.Kp + k];
+    const int64_t q = t * a.K + k;
+    if (a.ell_u) a.ell_u[q] = u;
+    a.upart[t * a.Kp + k] = a.ell_a[q] * u;
+  }
+}
+
+// Phase 2: y_t[slice s] = sum_k h_k * W_d[j_k][slice s], h_k from the sum
+// above (non-gated: h_k = a_k). Rows routed to the dense backup are skipped.
+template <typename E, int NS, int SW, bool GATED>
+__global__ __launch_bounds__(256) void down_kernel(SliceArgs a) {
+  using G = SliceGeom<E, SW>;
+  constexpr int EPL = G::EPL, RPW = G::RPW;
+  using R = typename G::R;
+  const int lane = threadIdx.x & 63;
+  const int hf = RPW == 2 ? lane >> 5 : 0;
+  const int l = lane & (G::LPR - 1);
+  const int i = lane & 31;
+  const int s = blockIdx.x % NS;
+  const int64_t t = ((int64_t)(blockIdx.x / NS) * 4 + (threadIdx.x >> 6)) * RPW + hf;
+  if (t - hf >= a.T) return;
+  const bool ok = t < a.T;
+  const int64_t tr = ok ? t : a.T - 1;
+  const int d = NS * SW;
+  const int64_t col = (int64_t)s * SW + l * EPL;
+  const char* wd = (const char*)a.wd;
+  const uint32_t colb = (uint32_t)(col * sizeof(E));
+  const uint32_t rowb = (uint32_t)(d * sizeof(E));
+  const int64_t rb = tr * a.K;
+  const bool store = ok && a.bk[tr] == 0;
+  const int n = ok ? a.ell_cnt[tr] : 0;
+  int nmax = __builtin_amdgcn_readlane(n, 0);
+  if constexpr (RPW == 2) nmax = max(nmax, __builtin_amdgcn_readlane(n, 32));
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-  for (int k0 = 0; k0 < n; k0 += GRP) {
-    const int m = min(GRP, n - k0);
-    const int kk = k0 + min(lane, m - 1);
-    const int jl = a.ell_idx[rb + kk];
-    float hl = a.ell_a[rb + kk];
-    if constexpr (GATED) {
-      float u = 0.0f;
+  for (int k0 = 0; k0 < nmax; k0 += GRP) {
+    const int k = min(k0 + i, a.K - 1);
+    const bool live = k0 + i < n;
+    int jl = a.ell_idx[rb + k];
+    float hl = GATED ? a.upart[tr * a.Kp + k] : a.ell_a[rb + k];
+    jl = live ? jl : 0;
+    hl = live ? hl : 0.0f;
+    // blocks of 8 slots that some row of the wave has (wave-uniform); the
+    // other slots of a block read neuron 0 with h = 0
+    const int nb = (min(GRP, nmax - k0) + 7) >> 3;
+    R w[GRP];
 #pragma unroll
-      for (int q = 0; q < NS; ++q) u += a.upart[((int64_t)q * a.T + t) * a.Kp + kk];
-      if (a.ell_u && s == 0 && lane < m) a.ell_u[rb + kk] = u;
-      hl *= u;
-    }
-    if (lane >= m) hl = 0.0f;
-    typename V::raw w[GRP];
+    for (int b = 0; b < GRP / 8; ++b)
+      if (b < nb)
 #pragma unroll
-    for (int q = 0; q < GRP; ++q) {
-      const int j = __builtin_amdgcn_readlane(jl, q);
-      w[q] = *(const typename V::raw*)(wd + (int64_t)j * d);
-    }
+        for (int q = 8 * b; q < 8 * b + 8; ++q)
+          w[q] = *(const R*)(wd + ((uint32_t)slot_id<RPW>(jl, q, hf) * rowb + colb));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int q = 0; q < GRP; ++q) {
-      const float h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hl), q));
-      float f[EPL];
-      V::cvt(w[q], f);
+    for (int b = 0; b < GRP / 8; ++b)
+      if (b < nb)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(h, f[e], acc[e]);
-    }
+        for (int q = 8 * b; q < 8 * b + 8; ++q) {
+          const float h = slot_val<RPW>(hl, q, hf);
+          float f[EPL];
+          G::V::cvt(w[q], f);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[e] = fmaf(h, f[e], acc[e]);
+        }
   }
-  float* yo = a.y + t * d + col;
+  if (store) {
+    float* yo = a.y + t * d + col;
 #pragma unroll
-  for (int e = 0; e < EPL; e += 4) *(f32x4_t*)(yo + e) = f32x4_t{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+    for (int e = 0; e < EPL; e += 4) *(f32x4_t*)(yo + e) = f32x4_t{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+  }
 }
 
-template <typename E, int NS, int EPL>
+template <typename E, int NS, int SW>
 hipError_t launch_slices(const SliceArgs& a, bool gated, int phase, hipStream_t st) {
-  const dim3 grid((unsigned)(NS * ((a.T + 3) / 4)));
+  constexpr int RPW = SliceGeom<E, SW>::RPW;
+  const dim3 grid((unsigned)(NS * ((a.T + 4 * RPW - 1) / (4 * RPW))));
   if (phase == 0) {
-    hipLaunchKernelGGL((up_partial_kernel<E, NS, EPL>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((up_partial_kernel<E, NS, SW>), grid, dim3(256), 0, st, a);
+  } else if (phase == 2) {
+    hipLaunchKernelGGL((hsum_kernel<NS>), dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, st, a);
   } else if (gated) {
-    hipLaunchKernelGGL((down_kernel<E, NS, EPL, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((down_kernel<E, NS, SW, true>), grid, dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL((down_kernel<E, NS, EPL, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((down_kernel<E, NS, SW, false>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
@@ -338,19 +445,19 @@ hipError_t launch_backup_list(const uint8_t* bk, int64_t T, int32_t* brow, int64
 hipError_t launch_updown(Dtype dt, bool gated, int phase, const SliceArgs& a, hipStream_t s) {
   int ns, epl;
   slice_shape(dt, a.d, &ns, &epl);
-#define SFFN_SL(E, NS_, EPL_) \
-  if (ns == NS_ && epl == EPL_) return launch_slices<E, NS_, EPL_>(a, gated, phase, s);
+  const int sw = a.d / ns;
+#define SFFN_SL(E, NS_, SW_) \
+  if (ns == NS_ && sw == SW_) return launch_slices<E, NS_, SW_>(a, gated, phase, s);
   if (dt == kBF16) {
-    SFFN_SL(uint16_t, 1, 4)
-    SFFN_SL(uint16_t, 2, 4)
-    SFFN_SL(uint16_t, 4, 4)
-    SFFN_SL(uint16_t, 8, 4)
-    SFFN_SL(uint16_t, 8, 8)
+    SFFN_SL(uint16_t, 2, 256)
+    SFFN_SL(uint16_t, 4, 256)
+    SFFN_SL(uint16_t, 8, 256)
+    SFFN_SL(uint16_t, 8, 512)
   } else {
-    SFFN_SL(float, 1, 4)
-    SFFN_SL(float, 2, 4)
-    SFFN_SL(float, 4, 4)
-    SFFN_SL(float, 8, 4)
+    SFFN_SL(float, 1, 256)
+    SFFN_SL(float, 2, 256)
+    SFFN_SL(float, 4, 256)
+    SFFN_SL(float, 8, 256)
   }
 #undef SFFN_SL
   return hipErrorInvalidValue;
