@@ -296,71 +296,99 @@ __global__ __launch_bounds__(256) void gather_stack_kernel(const E* __restrict__
 // of the GEMMs that consume them. Row-major [R, 2F] (bf16 hi | lo) or
 // [R, F] (fp32) for dx; neuron-major rows of stride ldt holding hi in
 // columns [0, Rp) and lo in [Rp, 2Rp), zero past R (bf16), or [0, Rp)
-// (fp32), for dW.
+// (fp32), for dW. A workgroup takes 64 rows x 64 neurons at a time: it
+// reads and writes the row-major side along neurons, and goes through LDS
+// to write the neuron-major side along rows, so every access is coalesced.
 template <typename E, bool GATED>
 __global__ __launch_bounds__(256) void backup_grad_kernel(BwdArgs a) {
+  constexpr bool BF = sizeof(E) == 2;
+  // per element: hi | lo << 16 (bf16) or the fp32 bits
+  __shared__ uint32_t tz[64][65], tu[64][65], th[64][65];
   const int R = device_rows(a.n_backup, a.cap);
   const int Rp = (R + 63) / 64 * 64;
   const int F = a.F;
-  const int64_t total = (int64_t)Rp * F;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int r = (int)(e / F);
-    const int j = (int)(e - (int64_t)r * F);
-    float dz = 0.0f, du = 0.0f, h = 0.0f;
-    if (r < R) {
-      const float dh = a.dH[(int64_t)r * F + j];
-      const float av = a.bk_a[(int64_t)r * F + j];
-      const bool on = av > 0.0f;
-      if constexpr (GATED) {
-        const float uv = a.bk_u[(int64_t)r * F + j];
-        du = dh * av;
-        dz = on ? dh * uv + a.l1 : 0.0f;
-        h = av * uv;
-      } else {
-        dz = on ? dh + a.l1 : 0.0f;
-        h = av;
-      }
-    }
-    if constexpr (sizeof(E) == 2) {
-      const uint32_t zh = f32_to_bf16(dz), uh = f32_to_bf16(du), hh = f32_to_bf16(h);
-      const uint32_t zl = f32_to_bf16(dz - __uint_as_float(zh << 16));
-      const uint32_t ul = f32_to_bf16(du - __uint_as_float(uh << 16));
-      const uint32_t hl = f32_to_bf16(h - __uint_as_float(hh << 16));
-      uint16_t* gzr = (uint16_t*)a.gz_rm;
-      uint16_t* gur = (uint16_t*)a.gu_rm;
-      uint16_t* gzt = (uint16_t*)a.gz_t;
-      uint16_t* gut = (uint16_t*)a.gu_t;
-      uint16_t* ght = (uint16_t*)a.gh_t;
+  const int tid = threadIdx.x;
+  const int c = tid & 63;   // neuron (load phase) or row (store phase) in the tile
+  const int g = tid >> 6;
+  const int ntj = F / 64;
+  const int ntiles = (Rp / 64) * ntj;
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int r0 = (tile / ntj) * 64;
+    const int j0 = (tile - (tile / ntj) * ntj) * 64;
+#pragma unroll 4
+    for (int p = 0; p < 16; ++p) {
+      const int rl = p * 4 + g;
+      const int r = r0 + rl;
+      const int j = j0 + c;
+      float dz = 0.0f, du = 0.0f, h = 0.0f;
       if (r < R) {
-        gzr[(int64_t)r * 2 * F + j] = (uint16_t)zh;
-        gzr[(int64_t)r * 2 * F + F + j] = (uint16_t)zl;
-        if (GATED) {
-          gur[(int64_t)r * 2 * F + j] = (uint16_t)uh;
-          gur[(int64_t)r * 2 * F + F + j] = (uint16_t)ul;
+        const int64_t q = (int64_t)r * F + j;
+        const float dh = a.dH[q];
+        const float av = a.bk_a[q];
+        const bool on = av > 0.0f;
+        if constexpr (GATED) {
+          const float uv = a.bk_u[q];
+          du = dh * av;
+          dz = on ? dh * uv + a.l1 : 0.0f;
+          h = av * uv;
+        } else {
+          dz = on ? dh + a.l1 : 0.0f;
+          h = av;
         }
       }
-      const int64_t tr = (int64_t)j * a.ldt;
-      gzt[tr + r] = (uint16_t)zh;
-      gzt[tr + Rp + r] = (uint16_t)zl;
-      if (GATED) {
-        gut[tr + r] = (uint16_t)uh;
-        gut[tr + Rp + r] = (uint16_t)ul;
+      if constexpr (BF) {
+        const uint32_t zh = f32_to_bf16(dz), uh = f32_to_bf16(du), hh = f32_to_bf16(h);
+        const uint32_t zl = f32_to_bf16(dz - __uint_as_float(zh << 16));
+        const uint32_t ul = f32_to_bf16(du - __uint_as_float(uh << 16));
+        const uint32_t hl = f32_to_bf16(h - __uint_as_float(hh << 16));
+        if (r < R) {
+          uint16_t* gzr = (uint16_t*)a.gz_rm + (int64_t)r * 2 * F + j;
+          gzr[0] = (uint16_t)zh;
+          gzr[F] = (uint16_t)zl;
+          if (GATED) {
+            uint16_t* gur = (uint16_t*)a.gu_rm + (int64_t)r * 2 * F + j;
+            gur[0] = (uint16_t)uh;
+            gur[F] = (uint16_t)ul;
+          }
+        }
+        tz[rl][c] = zh | (zl << 16);
+        tu[rl][c] = uh | (ul << 16);
+        th[rl][c] = hh | (hl << 16);
+      } else {
+        if (r < R) {
+          ((float*)a.gz_rm)[(int64_t)r * F + j] = dz;
+          if (GATED) ((float*)a.gu_rm)[(int64_t)r * F + j] = du;
+        }
+        tz[rl][c] = __float_as_uint(dz);
+        tu[rl][c] = __float_as_uint(du);
+        th[rl][c] = __float_as_uint(h);
       }
-      ght[tr + r] = (uint16_t)hh;
-      ght[tr + Rp + r] = (uint16_t)hl;
-    } else {
-      float* gzr = (float*)a.gz_rm;
-      float* gur = (float*)a.gu_rm;
-      if (r < R) {
-        gzr[(int64_t)r * F + j] = dz;
-        if (GATED) gur[(int64_t)r * F + j] = du;
-      }
-      const int64_t tr = (int64_t)j * a.ldt;
-      ((float*)a.gz_t)[tr + r] = dz;
-      if (GATED) ((float*)a.gu_t)[tr + r] = du;
-      ((float*)a.gh_t)[tr + r] = h;
     }
+    __syncthreads();
+#pragma unroll 4
+    for (int p = 0; p < 16; ++p) {
+      const int jl = p * 4 + g;
+      const int64_t tr = (int64_t)(j0 + jl) * a.ldt + r0 + c;
+      const uint32_t z = tz[c][jl], u = tu[c][jl], hv = th[c][jl];
+      if constexpr (BF) {
+        uint16_t* gzt = (uint16_t*)a.gz_t + tr;
+        gzt[0] = (uint16_t)z;
+        gzt[Rp] = (uint16_t)(z >> 16);
+        if (GATED) {
+          uint16_t* gut = (uint16_t*)a.gu_t + tr;
+          gut[0] = (uint16_t)u;
+          gut[Rp] = (uint16_t)(u >> 16);
+        }
+        uint16_t* ght = (uint16_t*)a.gh_t + tr;
+        ght[0] = (uint16_t)hv;
+        ght[Rp] = (uint16_t)(hv >> 16);
+      } else {
+        ((float*)a.gz_t)[tr] = __uint_as_float(z);
+        if (GATED) ((float*)a.gu_t)[tr] = __uint_as_float(u);
+        ((float*)a.gh_t)[tr] = __uint_as_float(hv);
+      }
+    }
+    __syncthreads();
   }
 }
 
@@ -430,7 +458,7 @@ hipError_t launch_backup_prep(Dtype dt, bool gated, const BwdArgs& a, hipStream_
 }
 
 hipError_t launch_backup_grad(Dtype dt, bool gated, const BwdArgs& a, hipStream_t s) {
-  const dim3 g(2048), b(256);
+  const dim3 g(1024), b(256);
   if (dt == kBF16) {
     if (gated) hipLaunchKernelGGL((backup_grad_kernel<uint16_t, true>), g, b, 0, s, a);
     else hipLaunchKernelGGL((backup_grad_kernel<uint16_t, false>), g, b, 0, s, a);
