@@ -274,8 +274,7 @@ def bench_forward(args, np, torch, SparseFFN, wl):
     # products, their sums h = a * u, the down projection); a launch of it
     # is one of each
     keys = ["sparse_up", "sparse_hsum", "sparse_down"] if W0.gated else ["sparse_down"]
-    tr = (traffic["sparse_up"] + traffic["sparse_down"]
-          if "sparse_up" in traffic and "sparse_down" in traffic else None)
+    tr = sum(traffic[k] for k in keys) if all(k in traffic for k in keys) else None
     r_gath = roof("hbm", " + ".join(keys), gbytes * args.steps, prof, keys, PEAK_HBM_GBS, tr)
     r_gath["active_pairs_per_step"] = pairs
     dominant, other = ((r_gate, r_gath) if r_gate["avg_ms"] >= r_gath["avg_ms"]

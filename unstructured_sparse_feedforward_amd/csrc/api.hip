@@ -68,7 +68,7 @@ sffn_status validate_desc(const sffn_desc* d) {
 Dtype dt_of(const sffn_handle* h) { return h->desc.dtype == SFFN_BF16 ? kBF16 : kF32; }
 size_t esize(const sffn_handle* h) { return h->desc.dtype == SFFN_BF16 ? 2 : 4; }
 int ovf_words(int64_t T) { return (int)((T + 31) / 32); }
-constexpr int kSplitMax = 16;
+constexpr int kSplitMax = kSplitCap;
 
 // Workspace layout. Every region starts at a 256-byte boundary.
 struct Layout {

@@ -65,6 +65,7 @@ __device__ __forceinline__ int num_splits(const GemmArgs& g, int mt, int ntl) {
   if (g.part == nullptr) return 1;
   int s = g.split_target / (mt * ntl);
   if (s > g.split_max) s = g.split_max;
+  if (s > kSplitCap) s = kSplitCap;
   return s < 1 ? 1 : s;
 }
 
@@ -394,37 +395,55 @@ __global__ __launch_bounds__(256) void hidden_combine_kernel(GemmArgs g) {
   const int S = num_splits(g, mt, ntl);
   if (S <= 1) return;
   const int Mpad = mt * BM;
-  const int n2 = g.N / 2;
-  const int64_t total = (int64_t)M * n2;
+  const int n4 = g.N / 4;
+  const int64_t total = (int64_t)M * n4;
+  const int64_t pstride = (int64_t)Mpad * g.N;  // one split's partials
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
-    const int m = (int)(e / n2);
-    const int c = (int)(e - (int64_t)m * n2) * 2;
-    f32x2_t z = {0.0f, 0.0f}, u = {0.0f, 0.0f};
-    for (int k = 0; k < S; ++k) {
-      z += *(const f32x2_t*)(g.part + ((int64_t)k * Mpad + m) * g.N + c);
-      if (NB == 2) u += *(const f32x2_t*)(g.part + ((int64_t)(S + k) * Mpad + m) * g.N + c);
-    }
-    f32x2_t h, a;
+    const int m = (int)(e / n4);
+    const int c = (int)(e - (int64_t)m * n4) * 4;
+    const float* pz = g.part + (int64_t)m * g.N + c;
+    const float* pu = pz + (int64_t)S * pstride;
+    // every split's partials are loaded before the first add (in split
+    // order, so the sums are deterministic)
+    f32x4_t vz[kSplitCap], vu[kSplitCap];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int k = 0; k < kSplitCap; ++k) {
+      if (k < S) {
+        vz[k] = *(const f32x4_t*)(pz + k * pstride);
+        if (NB == 2) vu[k] = *(const f32x4_t*)(pu + k * pstride);
+      }
+    }
+    f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f}, u = z;
+#pragma unroll
+    for (int k = 0; k < kSplitCap; ++k) {
+      if (k < S) {
+        z += vz[k];
+        if (NB == 2) u += vu[k];
+      }
+    }
+    f32x4_t h, a;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
       a[q] = z[q] > 0.0f ? z[q] : 0.0f;
       h[q] = NB == 2 ? a[q] * u[q] : a[q];
     }
     if (g.out_a) {
-      *(f32x2_t*)(g.out_a + (int64_t)m * g.ldo_au + c) = a;
-      if (NB == 2 && g.out_u) *(f32x2_t*)(g.out_u + (int64_t)m * g.ldo_au + c) = u;
+      *(f32x4_t*)(g.out_a + (int64_t)m * g.ldo_au + c) = a;
+      if (NB == 2 && g.out_u) *(f32x4_t*)(g.out_u + (int64_t)m * g.ldo_au + c) = u;
     }
     if constexpr (sizeof(E) == 4) {
-      *(f32x2_t*)((float*)g.out + (int64_t)m * g.ldo + c) = h;
+      *(f32x4_t*)((float*)g.out + (int64_t)m * g.ldo + c) = h;
     } else {
       uint16_t* dst = (uint16_t*)g.out + (int64_t)m * g.ldo;
-      const uint32_t h0 = f32_to_bf16(h[0]);
-      const uint32_t h1 = f32_to_bf16(h[1]);
-      const uint32_t l0 = f32_to_bf16(h[0] - __uint_as_float(h0 << 16));
-      const uint32_t l1 = f32_to_bf16(h[1] - __uint_as_float(h1 << 16));
-      *(uint32_t*)(dst + c) = h0 | (h1 << 16);
-      *(uint32_t*)(dst + g.lo_off + c) = l0 | (l1 << 16);
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        hi[q] = f32_to_bf16(h[q]);
+        lo[q] = f32_to_bf16(h[q] - __uint_as_float(hi[q] << 16));
+      }
+      *(u32x2_t*)(dst + c) = u32x2_t{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+      *(u32x2_t*)(dst + g.lo_off + c) = u32x2_t{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
     }
   }
 }
@@ -439,15 +458,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, float* y
   const int Mpad = mt * BM;
   const int n4 = g.N / 4;
   const int64_t total = (int64_t)M * n4;
+  const int64_t pstride = (int64_t)Mpad * g.N;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * blockDim.x) {
     const int m = (int)(e / n4);
     const int c = (int)(e - (int64_t)m * n4) * 4;
-    f32x4_t s = *(const f32x4_t*)(g.part + (int64_t)m * g.N + c);
-    for (int k = 1; k < S; ++k) s += *(const f32x4_t*)(g.part + ((int64_t)k * Mpad + m) * g.N + c);
+    const float* p = g.part + (int64_t)m * g.N + c;
     float* dst = y + (int64_t)(g.out_rows ? g.out_rows[m] : m) * ldy + c;
-    if (g.accumulate) s += *(const f32x4_t*)dst;
-    *(f32x4_t*)dst = s;
+    f32x4_t v[kSplitCap];
+#pragma unroll
+    for (int k = 0; k < kSplitCap; ++k)
+      if (k < S) v[k] = *(const f32x4_t*)(p + k * pstride);
+    f32x4_t acc = v[0];
+#pragma unroll
+    for (int k = 1; k < kSplitCap; ++k)
+      if (k < S) acc += v[k];
+    if (g.accumulate) acc += *(const f32x4_t*)dst;
+    *(f32x4_t*)dst = acc;
   }
 }
 

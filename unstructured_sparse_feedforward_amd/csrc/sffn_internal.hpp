@@ -18,6 +18,7 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kTile = 128;  // TwELL tile width W
+constexpr int kSplitCap = 16;  // most K splits of a split-K GEMM
 
 // ---------------------------------------------------------------- bf16 bits
 
