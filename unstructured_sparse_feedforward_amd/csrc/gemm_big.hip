@@ -201,6 +201,30 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16_t (&acc)[NB][
       }
       if (lane < 32 && rbase + lane < M) g.tw_cnt[(int64_t)(rbase + lane) * g.n_t + tb] = cnt_lane;
     }
+  } else if (EPI == kEpiStoreF32 && NB == 1 && g.accumulate) {
+    // out += acc: a block row's 16 x JB old values are loaded together,
+    // then added and stored
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float prev[16][JB];
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+#pragma unroll
+        for (int j = 0; j < JB; ++j) {
+          const int row = m0 + wr * 128 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
+          const int col = n0 + wc * Cfg<NB>::WN + j * 32 + c32;
+          prev[q][j] = (row < M && col < g.N) ? ((const float*)g.out)[(int64_t)row * g.ldo + col] : 0.0f;
+        }
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+#pragma unroll
+        for (int j = 0; j < JB; ++j) {
+          const int row = m0 + wr * 128 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
+          const int col = n0 + wc * Cfg<NB>::WN + j * 32 + c32;
+          if (row < M && col < g.N)
+            ((float*)g.out)[(int64_t)row * g.ldo + col] = prev[q][j] + agpr(acc[0][i][j][q]);
+        }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -419,7 +443,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_bt_kernel(GemmArgs g) {
   const int wr = wave >> 1;
   const int wc = wave & 1;
   const int M = g.M;
-  const int nkt = g.K / BK;
+  // K may live on the device (rows of a backup list, in blocks of 64,
+  // times k_mult for stacked hi/lo parts); then the products accumulate
+  // into the output and a K of 0 leaves it as it is
+  const int Kd = g.k_dev ? g.k_mult * ((device_rows(g.k_dev, g.k_cap) + 63) / 64 * 64) : g.K;
+  const int nkt = Kd / BK;
+  if (nkt == 0) return;
   const TileSched ts(M, g.N, BN);
 
   const char* Ab = (const char*)g.A;
@@ -515,6 +544,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_bt_kernel(GemmArgs g) {
 
     for (int kt = 0; kt < nkt; ++kt) {
       const int st = kt & 1;
+      // B of stage kt+2 into registers now (its LDS buffer is still being
+      // read); into LDS after the barrier, so the loads have three
+      // substeps to arrive
+      const bool pre = kt + 2 < nkt;
+      if (pre) load_b(kt + 2);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < 3; ++s) {
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // fragments of substep s
@@ -528,8 +563,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bt_kernel(GemmArgs g) {
       __builtin_amdgcn_s_waitcnt(kWaitAll);
       wg_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      if (kt + 2 < nkt) {
-        load_b(kt + 2);
+      if (pre) {
         copy_a(kt + 2, st);
         store_b(st);
       }
@@ -556,9 +590,10 @@ hipError_t launch_ring(const GemmArgs& g, hipStream_t s) {
 }  // namespace
 
 bool gemm_big_supported(Dtype dt, int nb, bool bt, Epi epi, const GemmArgs& g) {
-  if (dt != kBF16 || g.m_dev || g.a_rows || g.out_rows || g.part || g.kwrap || g.k_dev ||
-      g.accumulate)
-    return false;
+  if (dt != kBF16 || g.m_dev || g.a_rows || g.out_rows || g.part || g.kwrap) return false;
+  if (g.accumulate && epi != kEpiStoreF32) return false;
+  // a device-sized K (n-contiguous B only) accumulates into the output
+  if (g.k_dev) return bt && nb == 1 && epi == kEpiStoreF32 && g.accumulate && g.k_mult >= 1;
   if (g.K % (bt ? BK : RBK) != 0) return false;
   if (bt) return nb == 1 && epi == kEpiStoreF32;
   if (epi == kEpiTwell) return nb == 1 && g.ovf == nullptr;
