@@ -28,6 +28,10 @@ struct sffn_handle {
   std::vector<sffn_prof_rec> recs;
   double tot_ms[SFFN_K_COUNT] = {};
   int32_t launches[SFFN_K_COUNT] = {};
+  // second stream (default priority) for the dense path of flagged or
+  // backup rows, forked from and joined back into the caller's stream
+  hipStream_t side = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 };
 
 namespace {
@@ -224,12 +228,21 @@ sffn_status sffn_create(const sffn_desc* desc, sffn_handle** out) {
   h->device = dev;
   h->num_cu = prop.multiProcessorCount;
   h->n_t = desc->d_ff / kTile;
+  if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess) {
+    sffn_destroy(h);
+    return SFFN_E_HIP;
+  }
   *out = h;
   return SFFN_OK;
 }
 
 void sffn_destroy(sffn_handle* h) {
   if (!h) return;
+  if (h->side) (void)hipStreamDestroy(h->side);
+  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
+  if (h->ev_join) (void)hipEventDestroy(h->ev_join);
   for (auto& r : h->recs) {
     (void)hipEventDestroy(r.a);
     (void)hipEventDestroy(r.b);
@@ -458,6 +471,19 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   void* hid = at<char>(ws, L.hid);
   float* part = at<float>(ws, L.part);
   const int mcap = train ? (int)std::min<int64_t>(hy->max_backup, T) : 0;
+  // The dense path touches only its rows of y (and its own workspace), the
+  // sparse phases only the others: the dense path runs on the side stream
+  // while the sparse kernels run on the caller's, launched first so that
+  // its few workgroups are not queued behind the sparse grids.
+  hipStream_t main_stream = stream;
+  bool forked = false;
+  if (!train || mcap > 0) {
+    if ((e = hipEventRecord(h->ev_fork, main_stream)) != hipSuccess ||
+        (e = hipStreamWaitEvent(h->side, h->ev_fork, 0)) != hipSuccess)
+      return hip_fail(h, e, "fork");
+    stream = h->side;
+    forked = true;
+  }
   if (!train || mcap > 0) {
     GemmArgs f = {};
     f.A = x;
@@ -527,6 +553,10 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     }
     if (e != hipSuccess) return hip_fail(h, e, "split-K reduce");
   }
+  if (forked) {
+    if ((e = hipEventRecord(h->ev_join, stream)) != hipSuccess) return hip_fail(h, e, "join");
+    stream = main_stream;
+  }
 
   // 5. sparse up/down over the ELL rows, d sliced across the XCDs
   SliceArgs sa = {};
@@ -557,6 +587,8 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     e = launch_updown(dt, D.gated != 0, 1, sa, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "sparse up/down");
+  if (forked && (e = hipStreamWaitEvent(stream, h->ev_join, 0)) != hipSuccess)
+    return hip_fail(h, e, "join");
   return SFFN_OK;
 }
 
