@@ -125,9 +125,16 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
     // of 128 rows; the hidden GEMM keeps one partial set per B operand
     const int tiles_d = std::max(1, h->num_cu / (int)(d / 128));
     const int tiles_h = std::max(1, h->num_cu / (int)(F / 128));
+    // bf16: the small-row GEMM keeps split partials of at most
+    // 2 * num_cu tiles, and always the gate | up partials of every row
+    const size_t part_small =
+        h->desc.dtype == SFFN_BF16
+            ? std::max((size_t)2 * h->num_cu * 128 * 128,
+                       (size_t)((T + 127) / 128 * 128) * (h->desc.gated ? 2 : 1) * F)
+            : 0;
     const size_t part_d = (size_t)tiles_d * 128 * d;
     const size_t part_h = (size_t)2 * tiles_h * 128 * F;
-    L.part = take(std::max(part_d, part_h) * 4);
+    L.part = take(std::max({part_d, part_h, part_small}) * 4);
   }
   if (op == SFFN_OP_FORWARD_DENSE) {
     L.hid = take((size_t)T * F * esize(h));
@@ -322,6 +329,9 @@ sffn_status sffn_gate_preact(sffn_handle* h, const void* x, const void* w_gate, 
   return SFFN_OK;
 }
 
+// split-K target of the small-row GEMMs: two workgroups per CU
+static int small_split_target(const sffn_handle* h) { return 2 * h->num_cu; }
+
 static sffn_status forward_dense(sffn_handle* h, const void* x, const void* wg, const void* wu,
                                  const void* wd, int64_t T, float* y, void* ws,
                                  const Layout& L, hipStream_t stream) {
@@ -484,7 +494,72 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     stream = h->side;
     forked = true;
   }
-  if (!train || mcap > 0) {
+  if ((!train || mcap > 0) && dt == kBF16) {
+    // gate | up of the rows side by side (N = 2F), partials always, then
+    // the combine: H as bf16 hi | lo (and ReLU(z), u rows in training)
+    const int nb = D.gated ? 2 : 1;
+    GemmArgs f = {};
+    f.A = x;
+    f.lda = D.d;
+    f.a_rows = brow;
+    f.m_dev = n_bk;
+    f.m_cap = mcap;
+    f.B0 = w_gate;
+    f.B1 = w_up;
+    f.ldb = D.d;
+    f.N = nb * D.d_ff;
+    f.nsplit = D.gated ? D.d_ff : 0;
+    f.K = D.d;
+    f.out = hid;
+    f.act = 1;
+    f.ldo = 2 * (int64_t)D.d_ff;
+    f.lo_off = D.d_ff;
+    if (train) {
+      f.out_a = hy->bk_a;
+      f.out_u = D.gated ? hy->bk_u : nullptr;
+      f.ldo_au = D.d_ff;
+    }
+    f.part = part;
+    f.split_target = small_split_target(h);
+    f.split_max = std::min(kSplitMax, D.d / 32);
+    f.num_cu = h->num_cu;
+    f.grid = gemm_small_grid(h->num_cu);
+    {
+      ProfScope ps(h, SFFN_K_FLAG_GATEUP, stream);
+      e = launch_gemm_small(false, kEpiHiddenSplitK, f, stream);
+      if (e == hipSuccess) e = launch_hidden_combine_side(nb, f, stream);
+    }
+    if (e != hipSuccess) return hip_fail(h, e, "dense-path gate/up GEMM");
+    // [H_hi | H_lo] x [W_d ; W_d]: K = 2F with the B index wrapped at F
+    GemmArgs f2 = {};
+    f2.A = hid;
+    f2.lda = 2 * (int64_t)D.d_ff;
+    f2.m_dev = n_bk;
+    f2.m_cap = mcap;
+    f2.B0 = w_down;
+    f2.ldb = D.d;
+    f2.N = D.d;
+    f2.K = 2 * D.d_ff;
+    f2.kwrap = D.d_ff;
+    f2.out = y;
+    f2.ldo = D.d;
+    f2.out_rows = brow;
+    f2.part = part;
+    f2.split_target = small_split_target(h);
+    f2.split_max = std::min(kSplitMax, f2.K / 32);
+    f2.num_cu = h->num_cu;
+    f2.grid = gemm_small_grid(h->num_cu);
+    {
+      ProfScope ps(h, SFFN_K_FLAG_DOWN, stream);
+      e = launch_gemm_small(true, kEpiStoreF32, f2, stream);
+    }
+    if (e != hipSuccess) return hip_fail(h, e, "dense-path down GEMM");
+    {
+      ProfScope ps(h, SFFN_K_SPLITK_REDUCE, stream);
+      e = launch_splitk_reduce(f2, y, D.d, stream);
+    }
+    if (e != hipSuccess) return hip_fail(h, e, "split-K reduce");
+  } else if (!train || mcap > 0) {
     GemmArgs f = {};
     f.A = x;
     f.lda = D.d;

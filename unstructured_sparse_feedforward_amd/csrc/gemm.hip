@@ -386,16 +386,22 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
 // Sum the split-K partials of the hidden GEMM and apply its epilogue:
 // H = ReLU(z) * u (two B operands) or ReLU(z), stored as bf16 hi and lo
 // parts (bf16 layers) or float32. A no-op when the GEMM did not split.
-template <typename E, int NB>
+// SIDE: the partials come from gemm_small_kernel, which always leaves them
+// (even unsplit) with the z and u columns side by side in one [Mpad, N] row
+// per split (N = 2F with nsplit = F; N = F for one operand). Otherwise they
+// come from gemm_kernel: z splits then u splits, [Mpad, F] each, and an
+// unsplit GEMM has already written H itself.
+template <typename E, int NB, bool SIDE>
 __global__ __launch_bounds__(256) void hidden_combine_kernel(GemmArgs g) {
   const int M = device_rows(g.m_dev, g.m_cap);
   if (M <= 0) return;
   const int mt = (M + BM - 1) / BM;
   const int ntl = g.N / BN;
   const int S = num_splits(g, mt, ntl);
-  if (S <= 1) return;
+  if (!SIDE && S <= 1) return;
   const int Mpad = mt * BM;
-  const int n4 = g.N / 4;
+  const int Fh = (SIDE && g.nsplit > 0) ? g.nsplit : g.N;   // hidden width
+  const int n4 = Fh / 4;
   const int64_t total = (int64_t)M * n4;
   const int64_t pstride = (int64_t)Mpad * g.N;  // one split's partials
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
@@ -403,7 +409,7 @@ __global__ __launch_bounds__(256) void hidden_combine_kernel(GemmArgs g) {
     const int m = (int)(e / n4);
     const int c = (int)(e - (int64_t)m * n4) * 4;
     const float* pz = g.part + (int64_t)m * g.N + c;
-    const float* pu = pz + (int64_t)S * pstride;
+    const float* pu = SIDE ? pz + Fh : pz + (int64_t)S * pstride;
     // every split's partials are loaded before the first add (in split
     // order, so the sums are deterministic)
     f32x4_t vz[kSplitCap], vu[kSplitCap];
@@ -528,12 +534,19 @@ hipError_t launch_gemm(Dtype dt, int nb, bool bt, Epi epi, const GemmArgs& g, hi
 hipError_t launch_hidden_combine(Dtype dt, int nb, const GemmArgs& g, hipStream_t s) {
   const dim3 grid(g.grid), block(256);
   if (dt == kBF16) {
-    if (nb == 2) hipLaunchKernelGGL((hidden_combine_kernel<uint16_t, 2>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((hidden_combine_kernel<uint16_t, 1>), grid, block, 0, s, g);
+    if (nb == 2) hipLaunchKernelGGL((hidden_combine_kernel<uint16_t, 2, false>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((hidden_combine_kernel<uint16_t, 1, false>), grid, block, 0, s, g);
   } else {
-    if (nb == 2) hipLaunchKernelGGL((hidden_combine_kernel<float, 2>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((hidden_combine_kernel<float, 1>), grid, block, 0, s, g);
+    if (nb == 2) hipLaunchKernelGGL((hidden_combine_kernel<float, 2, false>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((hidden_combine_kernel<float, 1, false>), grid, block, 0, s, g);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_hidden_combine_side(int nb, const GemmArgs& g, hipStream_t s) {
+  const dim3 grid(g.grid), block(256);
+  if (nb == 2) hipLaunchKernelGGL((hidden_combine_kernel<uint16_t, 2, true>), grid, block, 0, s, g);
+  else hipLaunchKernelGGL((hidden_combine_kernel<uint16_t, 1, true>), grid, block, 0, s, g);
   return hipGetLastError();
 }
 

@@ -1,0 +1,328 @@
+// bf16 MFMA GEMM for the few rows of the dense path (flagged rows at
+// inference, backup rows in training), whose row count lives on the device.
+//
+// C[M, N] = A[M, K] * B^T. A is row-major (k contiguous); logical row m
+// reads row a_rows[m] when a list is given. B is [N, K] (k contiguous,
+// copied straight into LDS) or [K, N] (n contiguous, loaded into registers
+// and written into LDS transposed). With nsplit > 0 the N columns are two
+// operands side by side: columns [0, nsplit) from B0, the rest from B1 (the
+// gate and up projections of the same rows). The k index into B wraps at
+// kwrap (the bf16 hi and lo parts of an fp32 operand meet the same B).
+//
+// 128 x 128 tiles, 4 waves of 64 x 64 (2 x 2 v_mfma_f32_32x32x16_bf16).
+// K streams through a ring of NSLOT LDS slots of 32 k each, NSLOT - 1
+// stages in flight: with only a few hundred rows the work is a stream of
+// weight columns, and the loads' latency, not the MFMAs, sets the pace.
+// The registers of an n-contiguous B stage are held for NSLOT - 1 stages
+// (one register set per slot, selected at compile time by unrolling the
+// k loop NSLOT times) before they are written into LDS. K is split over
+// workgroups (the device chooses the split so that there are about
+// split_target tiles); partials go to part[S][Mpad][N] for the reduce or
+// combine kernels of gemm.hip, which use the same tiling.
+#include "sffn_internal.hpp"
+
+namespace sffn {
+namespace {
+
+constexpr int BM = 128;
+constexpr int BN = 128;
+constexpr int NT = 256;
+constexpr int NXCD = 8;
+constexpr int BK = 32;       // k per slot (64 bytes per LDS row)
+constexpr int ROWB = 64;
+constexpr int SLOT = (BM + BN) * ROWB;   // 16 KB
+constexpr int NSLOT = 4;
+constexpr int LPS = 4;       // copies (or B register loads) per wave and stage
+
+constexpr int wait_imm(int vm, int lgkm) {
+  return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
+constexpr int kWaitLgkm0 = wait_imm(63, 0);
+constexpr int kWaitAll = wait_imm(0, 0);
+
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// 64-byte rows of 4 chunks, 4 rows per 256-byte bank line: chunk ^= (row >> 2) & 3
+__device__ __forceinline__ int rlds_off(int row, int chunk) {
+  return row * ROWB + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+// number of K splits, as the reduce and combine kernels compute it
+__device__ __forceinline__ int small_splits(const GemmArgs& g, int mt, int ntl) {
+  if (g.part == nullptr) return 1;
+  int s = g.split_target / (mt * ntl);
+  if (s > g.split_max) s = g.split_max;
+  if (s > kSplitCap) s = kSplitCap;
+  return s < 1 ? 1 : s;
+}
+
+template <bool BT, int EPI>
+__global__ __launch_bounds__(NT) void gemm_small_kernel(GemmArgs g) {
+  __shared__ __align__(16) char smem[NSLOT * SLOT];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wr = wave >> 1;
+  const int wc = wave & 1;
+
+  const int M = g.m_dev ? device_rows(g.m_dev, g.m_cap) : g.M;
+  if (M <= 0) return;
+  const int mt = (M + BM - 1) / BM;
+  const int ntl = g.N / BN;
+  const int nkt_all = g.K / BK;
+  // partials whenever K is split; the hidden GEMM always leaves them to
+  // the combine kernel (ReLU(z) * u needs both operands' tiles)
+  const int S = small_splits(g, mt, ntl);
+  const bool to_part = EPI == kEpiHiddenSplitK || S > 1;
+  const int Mpad = mt * BM;
+  const int ntiles = mt * ntl * S;
+  const int xcd = blockIdx.x % NXCD;
+  const int G8 = gridDim.x / NXCD;
+  const int per = (ntiles + NXCD - 1) / NXCD;
+  const int t_end = min(ntiles, (xcd + 1) * per);
+
+  const int64_t lda_b = g.lda * 2;
+  const int64_t ldb_b = g.ldb * 2;
+  // direct-to-LDS copy lane layout: 16 rows x 64 bytes per instruction
+  const int lr = lane >> 2;
+  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  // n-contiguous B: thread (bg, bkg) loads k rows 2 bkg, 2 bkg + 1 of
+  // columns 8 bg .. 8 bg + 7
+  const int bg = tid & 15;
+  const int bkg = tid >> 4;
+
+  for (int L = xcd * per + blockIdx.x / NXCD; L < t_end; L += G8) {
+    // tiles of one column block are consecutive (they share B in L2)
+    const int ks = L % S;
+    const int rem = L / S;
+    const int tm = rem % mt;
+    const int tn = rem / mt;
+    const int m0 = tm * BM;
+    const int n0 = tn * BN;
+    const int kt0 = (int)((int64_t)ks * nkt_all / S);
+    const int nkt = (int)((int64_t)(ks + 1) * nkt_all / S) - kt0;
+    const char* Bb = (const char*)g.B0;
+    int nb0 = n0;
+    if (g.nsplit > 0 && n0 >= g.nsplit) {
+      Bb = (const char*)g.B1;
+      nb0 = n0 - g.nsplit;
+    }
+
+    const char* a_src[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int m = min(m0 + wave * 32 + i * 16 + lr, M - 1);
+      const int64_t pr = g.a_rows ? g.a_rows[m] : m;
+      a_src[i] = (const char*)g.A + pr * lda_b + lchunk * 16;
+    }
+    const char* b_src[2];
+    if constexpr (!BT) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        b_src[i] = Bb + (int64_t)(nb0 + wave * 32 + i * 16 + lr) * ldb_b + lchunk * 16;
+    }
+    u32x4_t rbs[NSLOT][2];   // n-contiguous B stages in flight
+
+    auto kb_of = [&](int kt) {
+      int64_t kb = (int64_t)(kt0 + kt) * BK;
+      if (g.kwrap > 0) kb %= g.kwrap;
+      return kb;
+    };
+    // stage kt (relative to the split) into slot `slot` (B registers into set `set`)
+    auto issue = [&](int kt, int slot, u32x4_t (&rb)[2]) {
+      char* base = smem + slot * SLOT;
+      const int64_t ka = (int64_t)(kt0 + kt) * BK * 2;
+      const int64_t kb = kb_of(kt);
+      if constexpr (BT) {
+        const char* p = Bb + (kb + 2 * bkg) * ldb_b + (int64_t)(nb0 + 8 * bg) * 2;
+        rb[0] = *(const u32x4_t*)p;
+        rb[1] = *(const u32x4_t*)(p + ldb_b);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + ka),
+                                         (void*)(base + (wave * 32 + i * 16) * ROWB), 16, 0, 0);
+      if constexpr (!BT) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + kb * 2),
+                                           (void*)(base + (BM + wave * 32 + i * 16) * ROWB), 16,
+                                           0, 0);
+      }
+    };
+    // k rows (2 bkg, 2 bkg + 1) x 8 columns -> 8 LDS rows of B, 4 bytes each
+    auto store_b = [&](int slot, const u32x4_t (&rb)[2]) {
+      if constexpr (BT) {
+        char* bbase = smem + slot * SLOT + BM * ROWB;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint32_t r0 = rb[0][c >> 1];
+          const uint32_t r1 = rb[1][c >> 1];
+          const uint32_t v = (c & 1) ? ((r0 >> 16) | (r1 & 0xFFFF0000u)) : ((r0 & 0xFFFFu) | (r1 << 16));
+          *(uint32_t*)(bbase + rlds_off(8 * bg + c, bkg >> 2) + (bkg & 3) * 4) = v;
+        }
+      }
+    };
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    u32x4_t af[2][2], bf[2][2];
+    auto read_frags = [&](int slot, int s, int buf) {
+      const char* sa = smem + slot * SLOT;
+      const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[buf][i] = *(const u32x4_t*)(sa + rlds_off(wr * 64 + i * 32 + (lane & 31), ch));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        bf[buf][j] = *(const u32x4_t*)(sa + BM * ROWB + rlds_off(wc * 64 + j * 32 + (lane & 31), ch));
+    };
+    auto mfmas = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, af[buf][i]), __builtin_bit_cast(bf16x8_t, bf[buf][j]),
+              acc[i][j], 0, 0, 0);
+    };
+    auto spread = [&]() {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      }
+    };
+
+    // Pipeline: stage kt lives in slot kt % NSLOT; every slot is filled up
+    // front (stages past the last one repeat it into slots that are never
+    // read), after the barrier of iteration kt stage kt + NSLOT is issued
+    // into the slot stage kt leaves, and "stage kt+1 has landed" is "at
+    // most NSLOT - 2 stages of copies in flight". n-contiguous B: stage
+    // kt + 1's registers are written into its slot just before the barrier
+    // of iteration kt.
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    wg_barrier();   // the previous tile's readers are done with LDS
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 0; p < NSLOT; ++p) issue(min(p, nkt - 1), p, rbs[p]);
+    __builtin_amdgcn_s_waitcnt(wait_imm((NSLOT - 1) * LPS, 15));   // stage 0 landed
+    store_b(0, rbs[0]);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    wg_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(0, 0, 0);
+
+    for (int kb0 = 0; kb0 < nkt; kb0 += NSLOT) {
+#pragma unroll
+      for (int u = 0; u < NSLOT; ++u) {
+        const int kt = kb0 + u;
+        if (kt >= nkt) break;
+        const int nu = (u + 1) % NSLOT;   // slot (and register set) of stage kt + 1
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(u, 1, 1);
+        mfmas(0);
+        spread();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(wait_imm((NSLOT - 2) * LPS, 0));  // stage kt+1 landed
+        store_b(nu, rbs[nu]);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        wg_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(nu, 0, 0);
+        issue(min(kt + NSLOT, nkt - 1), u, rbs[u]);
+        mfmas(1);
+        spread();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    // ---- epilogue
+    const int h = lane >> 5;
+    const int c32 = lane & 31;
+    if (to_part) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int m = m0 + wr * 64 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
+          if (m < M) {
+            float* dst = g.part + ((int64_t)ks * Mpad + m) * g.N + n0 + wc * 64 + c32;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) dst[j * 32] = acc[i][j][q];
+          }
+        }
+    } else if (g.accumulate) {
+      // out += C: the tile row block's old values are loaded together first
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        float prev[16][2];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int m = m0 + wr * 64 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
+          const int64_t orow = m < M ? (g.out_rows ? g.out_rows[m] : m) : 0;
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            prev[q][j] = m < M ? ((const float*)g.out)[orow * g.ldo + n0 + wc * 64 + j * 32 + c32] : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int m = m0 + wr * 64 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
+          if (m < M) {
+            const int64_t orow = g.out_rows ? g.out_rows[m] : m;
+            float* dst = (float*)g.out + orow * g.ldo + n0 + wc * 64 + c32;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) dst[j * 32] = prev[q][j] + acc[i][j][q];
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int m = m0 + wr * 64 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
+          if (m < M) {
+            const int64_t orow = g.out_rows ? g.out_rows[m] : m;
+            float* dst = (float*)g.out + orow * g.ldo + n0 + wc * 64 + c32;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) dst[j * 32] = acc[i][j][q];
+          }
+        }
+    }
+  }
+}
+
+}  // namespace
+
+bool gemm_small_supported(const GemmArgs& g, bool bt, Epi epi) {
+  if (epi != kEpiStoreF32 && epi != kEpiHiddenSplitK) return false;
+  if (g.k_dev || g.N % BN != 0 || g.K % BK != 0 || g.K < BK) return false;
+  if (g.kwrap > 0 && g.kwrap % BK != 0) return false;
+  if (g.nsplit > 0 && (g.nsplit % BN != 0 || bt)) return false;
+  if (epi == kEpiHiddenSplitK && (g.part == nullptr || g.act != 1)) return false;
+  return true;
+}
+
+// two workgroups per CU (64 KB of LDS each)
+int gemm_small_grid(int num_cu) { return (2 * num_cu / NXCD) * NXCD; }
+
+hipError_t launch_gemm_small(bool bt, Epi epi, const GemmArgs& g, hipStream_t s) {
+  const dim3 grid(g.grid), block(NT);
+  if (epi == kEpiHiddenSplitK) {
+    hipLaunchKernelGGL((gemm_small_kernel<false, kEpiHiddenSplitK>), grid, block, 0, s, g);
+  } else if (bt) {
+    hipLaunchKernelGGL((gemm_small_kernel<true, kEpiStoreF32>), grid, block, 0, s, g);
+  } else {
+    hipLaunchKernelGGL((gemm_small_kernel<false, kEpiStoreF32>), grid, block, 0, s, g);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sffn

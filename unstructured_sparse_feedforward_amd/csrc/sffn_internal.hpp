@@ -10,6 +10,7 @@
 namespace sffn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -137,6 +138,8 @@ struct GemmArgs {
   int C;
   int n_t;
   int ovf_words;
+  int nsplit;                // > 0: columns [0, nsplit) from B0, the rest from B1
+                             // (gemm_small.hip, k-contiguous B)
   int grid;                  // persistent grid size (small-tile kernel)
   int num_cu;                // compute units (large-tile kernel's grid)
 };
@@ -147,6 +150,14 @@ struct GemmArgs {
 hipError_t launch_gemm(Dtype dt, int nb, bool b_trans, Epi epi, const GemmArgs& g,
                        hipStream_t s);
 bool gemm_big_supported(Dtype dt, int nb, bool bt, Epi epi, const GemmArgs& g);
+// bf16 GEMM of the dense path's few, device-counted rows (gemm_small.hip):
+// kEpiStoreF32 (split-K partials for launch_splitk_reduce when split, else
+// stored with out_rows / accumulate) or kEpiHiddenSplitK (always partials,
+// finished by launch_hidden_combine_side).
+bool gemm_small_supported(const GemmArgs& g, bool bt, Epi epi);
+int gemm_small_grid(int num_cu);
+hipError_t launch_gemm_small(bool bt, Epi epi, const GemmArgs& g, hipStream_t s);
+hipError_t launch_hidden_combine_side(int nb, const GemmArgs& g, hipStream_t s);
 int gemm_big_grid(const GemmArgs& g, int nb);
 hipError_t launch_gemm_big(int nb, bool bt, Epi epi, const GemmArgs& g, hipStream_t s);
 int gemm_grid(Dtype dt, int nb, int num_cu);

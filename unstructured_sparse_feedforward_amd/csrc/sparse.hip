@@ -255,32 +255,36 @@ __global__ __launch_bounds__(256) void up_partial_kernel(SliceArgs a) {
     if (k0 > 0) jraw = a.ell_idx[rb + min(k0 + i, a.K - 1)];
     const bool live = k0 + i < n;
     const int jl = live ? jraw : 0;
-    // blocks of 8 slots that some row of the wave has (wave-uniform);
-    // totals of the other slots are never stored
-    const int nb = (min(GRP, nmax - k0) + 7) >> 3;
+    // all 32 slots are loaded (slots past the count read neuron 0; their
+    // totals are never stored)
     R w[GRP];
 #pragma unroll
-    for (int b = 0; b < GRP / 8; ++b) {
-      if (b < nb) {
-#pragma unroll
-        for (int q = 8 * b; q < 8 * b + 8; ++q)
-          w[q] = *(const R*)(wu + ((uint32_t)slot_id<RPW>(jl, q, hf) * rowb + colb));
-      } else {
-#pragma unroll
-        for (int q = 8 * b; q < 8 * b + 8; ++q) w[q] = R{};
-      }
-    }
+    for (int q = 0; q < GRP; ++q)
+      w[q] = *(const R*)(wu + ((uint32_t)slot_id<RPW>(jl, q, hf) * rowb + colb));
     // keep every load of the group in flight before the first use
     __builtin_amdgcn_sched_barrier(0);
     float p[GRP];
 #pragma unroll
     for (int q = 0; q < GRP; ++q) {
-      float f[EPL];
-      G::V::cvt(w[q], f);
-      float acc = 0.0f;
+      if constexpr (sizeof(E) == 2) {
+        // bf16 pairs straight into v_dot2c_f32_bf16 (the products of two
+        // bf16 values are exact in fp32), fp32 accumulation
+        float acc = 0.0f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc = fmaf(xr[e], f[e], acc);
-      p[q] = acc;
+        for (int e = 0; e < EPL / 2; ++e) {
+          const uint32_t xe = xv[e], we = w[q][e];
+          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xe),
+                                                __builtin_bit_cast(bf16x2_t, we), acc, false);
+        }
+        p[q] = acc;
+      } else {
+        float f[EPL];
+        G::V::cvt(w[q], f);
+        float acc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc = fmaf(xr[e], f[e], acc);
+        p[q] = acc;
+      }
     }
     if constexpr (RPW == 2) {
       // totals over the 32 lanes of each row: lane i ends with slot k0 + i
