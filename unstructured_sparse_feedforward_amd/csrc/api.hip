@@ -164,7 +164,8 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
     L.dyb = take((size_t)L.ldt * d * esize(h));
     const int tiles_d = std::max(1, h->num_cu / (int)(d / 128));
     const int tiles_h = std::max(1, h->num_cu / (int)(F / 128));
-    L.part = take(std::max((size_t)tiles_d * 128 * d, (size_t)tiles_h * 128 * F) * 4);
+    L.part = take(std::max({(size_t)tiles_d * 128 * d, (size_t)tiles_h * 128 * F,
+                            (size_t)2 * h->num_cu * 128 * 128}) * 4);
   }
   L.total = o;
   return L;
@@ -895,11 +896,18 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
     g.out = const_cast<float*>(ba.dH);
     g.ldo = D.d_ff;
     g.part = part;
-    g.split_target = h->num_cu;
-    g.split_max = std::min(kSplitMax, D.d / (split ? 64 : 32));
     g.num_cu = h->num_cu;
-    g.grid = gemm_grid(dt, 1, h->num_cu);
-    e = launch_gemm(dt, 1, false, kEpiStoreF32, g, stream);
+    if (split) {
+      g.split_target = small_split_target(h);
+      g.split_max = std::min(kSplitMax, D.d / 32);
+      g.grid = gemm_small_grid(h->num_cu);
+      e = launch_gemm_small(false, kEpiStoreF32, g, stream);
+    } else {
+      g.split_target = h->num_cu;
+      g.split_max = std::min(kSplitMax, D.d / 32);
+      g.grid = gemm_grid(dt, 1, h->num_cu);
+      e = launch_gemm(dt, 1, false, kEpiStoreF32, g, stream);
+    }
     if (e == hipSuccess) e = launch_splitk_reduce(g, (float*)ba.dH, D.d_ff, stream);
     if (e == hipSuccess) e = launch_backup_grad(dt, gated, ba, stream);
     if (e != hipSuccess) return hip_fail(h, e, "backup dH");
@@ -925,11 +933,18 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
       f.out_rows = hy->brow;
       f.accumulate = pass;
       f.part = part;
-      f.split_target = h->num_cu;
-      f.split_max = std::min(kSplitMax, f.K / (split ? 64 : 32));
       f.num_cu = h->num_cu;
-      f.grid = gemm_grid(dt, 1, h->num_cu);
-      e = launch_gemm(dt, 1, true, kEpiStoreF32, f, stream);
+      if (split) {
+        f.split_target = small_split_target(h);
+        f.split_max = std::min(kSplitMax, f.K / 32);
+        f.grid = gemm_small_grid(h->num_cu);
+        e = launch_gemm_small(true, kEpiStoreF32, f, stream);
+      } else {
+        f.split_target = h->num_cu;
+        f.split_max = std::min(kSplitMax, f.K / 32);
+        f.grid = gemm_grid(dt, 1, h->num_cu);
+        e = launch_gemm(dt, 1, true, kEpiStoreF32, f, stream);
+      }
       if (e == hipSuccess) e = launch_splitk_reduce(f, dx, D.d, stream);
       if (e != hipSuccess) return hip_fail(h, e, "backup dx");
     }
