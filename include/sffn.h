@@ -232,8 +232,8 @@ sffn_status sffn_hybrid_compact(sffn_handle* h, const sffn_twell* tw, const floa
  * (into tw, or the workspace when tw is NULL) is converted with ELL
  * capacity K = desc.ell_cap (>= 1); ELL rows' up/down projections run over
  * their slots and save u per slot; backup rows run densely and save their
- * ReLU(z) and u rows in fp32 ("Sparse MatMul ... dense backup rows on the
- * matrix cores, sparse rows on the vector units", "2. Methodology" B). */
+ * ReLU(z) and u rows in fp32 (backup rows on the matrix cores, sparse rows
+ * on the vector units: "2. Methodology" B, training kernels). */
 sffn_status sffn_forward_train(sffn_handle* h, const void* x, const void* w_gate,
                                const void* w_up, const void* w_down, int64_t T, float* y,
                                const sffn_twell* tw, const sffn_hybrid* hy, void* ws,

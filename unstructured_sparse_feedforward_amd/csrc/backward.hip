@@ -1,8 +1,8 @@
-// Sparse backward of the feedforward layer over the Hybrid format
-// ("Backpropagation ... transposes the hybrid format for gradient
-// computation without expensive dense reconstructions", gist.science
-// explainer of "Sparser, Faster, Lighter Transformer Language Models",
-// 2. Methodology B, training kernels).
+// Sparse backward of the feedforward layer over the Hybrid format: the
+// gradients are taken over the stored active entries, with the Hybrid
+// regrouped by neuron for the weight gradients and no dense hidden tensor
+// rebuilt (gist.science explainer of "Sparser, Faster, Lighter Transformer
+// Language Models", 2. Methodology B, training kernels).
 //
 // For an active slot (neuron j, activation a, up value u) of ELL row t and
 // upstream gradient dy_t: dh = dy_t . W_d[j]; dU = dh * a; dZ = dh * u + l1
@@ -11,8 +11,8 @@
 // dW_u[j] = sum_t dU x_t, dW_d[j] = sum_t (a u) dy_t.
 //
 // The partial dot products dy_t . W_d[j] reuse the sliced phase-1 kernel
-// (sparse.hip). dx is accumulated per (row, d slice) like the forward's
-// down projection. dW needs the slots grouped by neuron: integer-atomic
+// (sparse.hip); a row pass sums them into dZ, dU per slot. dx is
+// accumulated per (row, d slice) like the forward's down projection. dW needs the slots grouped by neuron: integer-atomic
 // counts, an exclusive scan, an atomic fill and a per-neuron sort by slot
 // index give every neuron its slots in ascending row order, so the float
 // sums of dW are accumulated in a fixed order (no float atomics).
@@ -21,97 +21,105 @@
 namespace sffn {
 namespace {
 
-template <typename E, int EPL> struct BV;
-template <> struct BV<uint16_t, 4> {
-  typedef u32x2_t raw;
-  __device__ static void cvt(const raw& v, float* o) {
-    o[0] = bf16lo(v[0]); o[1] = bf16hi(v[0]); o[2] = bf16lo(v[1]); o[3] = bf16hi(v[1]);
-  }
-};
-template <> struct BV<uint16_t, 8> {
-  typedef u32x4_t raw;
-  __device__ static void cvt(const raw& v, float* o) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) { o[2 * k] = bf16lo(v[k]); o[2 * k + 1] = bf16hi(v[k]); }
-  }
-};
-template <> struct BV<float, 4> {
-  typedef u32x4_t raw;
-  __device__ static void cvt(const raw& v, float* o) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = __uint_as_float(v[k]);
-  }
-};
-
-constexpr int GRP = 32;
-
-// dZ, dU per ELL slot (written by the slice-0 waves) and the row's dx slice.
-template <typename E, int NS, int EPL, bool GATED>
-__global__ __launch_bounds__(256) void dx_sparse_kernel(BwdArgs a) {
-  using V = BV<E, EPL>;
+// dZ and dU per ELL slot from the slice partials of dh = dy . W_d[j]
+// (summed in slice order): dU = dh * a, dZ = dh * u + l1 (non-gated
+// dZ = dh + l1). One wave per row.
+template <int NS, bool GATED>
+__global__ __launch_bounds__(256) void dzu_kernel(BwdArgs a) {
   const int lane = threadIdx.x & 63;
-  const int s = blockIdx.x % NS;
-  const int64_t t = (int64_t)(blockIdx.x / NS) * 4 + (threadIdx.x >> 6);
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
-  if (a.slot[t] >= 0) return;  // the dense path writes backup rows
   const int n = a.ell_cnt[t];
-  const int d = NS * 64 * EPL;
-  const int64_t col = (int64_t)s * 64 * EPL + lane * EPL;
-  const E* wg = (const E*)a.wg + col;
-  const E* wu = (const E*)a.wu + col;
-  const int64_t rb = t * (int64_t)a.K;
+  for (int k = lane; k < n; k += 64) {
+    float dh = 0.0f;
+#pragma unroll
+    for (int r = 0; r < NS; ++r) dh += a.dpart[((int64_t)r * a.T + t) * a.Kp + k];
+    const int64_t q = t * a.K + k;
+    if constexpr (GATED) {
+      a.gu[q] = dh * a.ell_a[q];
+      a.gz[q] = dh * a.ell_u[q] + a.l1;
+    } else {
+      a.gz[q] = dh + a.l1;
+    }
+  }
+}
+
+constexpr int GRP = 16;   // slots per group: two 16-byte loads each in flight
+
+// dx of the ELL rows: dx_t[slice] = sum_k dZ_k W_g[j_k][slice] + dU_k W_u[j_k][slice],
+// RPW rows per wave with 16-byte lanes (the slice geometry of the forward
+// gathers). Backup rows are left to the dense path.
+template <typename E, int NS, int SW, bool GATED>
+__global__ __launch_bounds__(256) void dx_sparse_kernel(BwdArgs a) {
+  using G = SliceGeom<E, SW>;
+  constexpr int EPL = G::EPL, RPW = G::RPW;
+  using R = typename G::R;
+  const int lane = threadIdx.x & 63;
+  const int hf = RPW == 2 ? lane >> 5 : 0;
+  const int l = lane & (G::LPR - 1);
+  const int i = lane & 31;
+  const int s = blockIdx.x % NS;
+  const int64_t t = ((int64_t)(blockIdx.x / NS) * 4 + (threadIdx.x >> 6)) * RPW + hf;
+  if (t - hf >= a.T) return;
+  const bool ok = t < a.T;
+  const int64_t tr = ok ? t : a.T - 1;
+  const int d = NS * SW;
+  const int64_t col = (int64_t)s * SW + l * EPL;
+  const char* wg = (const char*)a.wg;
+  const char* wu = (const char*)a.wu;
+  const uint32_t colb = (uint32_t)(col * sizeof(E));
+  const uint32_t rowb = (uint32_t)(d * sizeof(E));
+  const int64_t rb = tr * a.K;
+  const bool store = ok && a.slot[tr] < 0;
+  const int n = ok ? a.ell_cnt[tr] : 0;
+  int nmax = __builtin_amdgcn_readlane(n, 0);
+  if constexpr (RPW == 2) nmax = max(nmax, __builtin_amdgcn_readlane(n, 32));
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-  for (int k0 = 0; k0 < n; k0 += GRP) {
-    const int m = min(GRP, n - k0);
-    const int kk = k0 + min(lane, m - 1);
-    const int jl = a.ell_idx[rb + kk];
-    float dh = 0.0f;
+  for (int k0 = 0; k0 < nmax; k0 += 32) {
+    // slot k0 + i of the lane's row: neuron, dZ, dU (0 past the count)
+    const int k = min(k0 + i, a.K - 1);
+    const bool live = k0 + i < n;
+    int jl = a.ell_idx[rb + k];
+    float zl = a.gz[rb + k];
+    float ul = GATED ? a.gu[rb + k] : 0.0f;
+    jl = live ? jl : 0;
+    zl = live ? zl : 0.0f;
+    ul = live ? ul : 0.0f;
+    const int m = min(32, nmax - k0);
 #pragma unroll
-    for (int q = 0; q < NS; ++q) dh += a.dpart[((int64_t)q * a.T + t) * a.Kp + kk];
-    float dz, du = 0.0f;
-    if constexpr (GATED) {
-      du = dh * a.ell_a[rb + kk];
-      dz = dh * a.ell_u[rb + kk] + a.l1;
-    } else {
-      dz = dh + a.l1;
-    }
-    if (lane >= m) {
-      dz = 0.0f;
-      du = 0.0f;
-    }
-    if (s == 0 && lane < m) {
-      a.gz[rb + kk] = dz;
-      if (GATED) a.gu[rb + kk] = du;
-    }
-    typename V::raw w[GRP];
-    typename V::raw w2[GATED ? GRP : 1];
+    for (int g = 0; g < 32 / GRP; ++g) {
+      if (g * GRP >= m) break;
+      R w[GRP], w2[GATED ? GRP : 1];
 #pragma unroll
-    for (int q = 0; q < GRP; ++q) {
-      const int j = __builtin_amdgcn_readlane(jl, q);
-      w[q] = *(const typename V::raw*)(wg + (int64_t)j * d);
-      if constexpr (GATED) w2[q] = *(const typename V::raw*)(wu + (int64_t)j * d);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+      for (int q = 0; q < GRP; ++q) {
+        const uint32_t off = (uint32_t)slot_id<RPW>(jl, g * GRP + q, hf) * rowb + colb;
+        w[q] = *(const R*)(wg + off);
+        if constexpr (GATED) w2[q] = *(const R*)(wu + off);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int q = 0; q < GRP; ++q) {
-      const float cz = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dz), q));
-      float f[EPL];
-      V::cvt(w[q], f);
+      for (int q = 0; q < GRP; ++q) {
+        const float cz = slot_val<RPW>(zl, g * GRP + q, hf);
+        float f[EPL];
+        G::V::cvt(w[q], f);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(cz, f[e], acc[e]);
-      if constexpr (GATED) {
-        const float cu = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(du), q));
-        V::cvt(w2[q], f);
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(cz, f[e], acc[e]);
+        if constexpr (GATED) {
+          const float cu = slot_val<RPW>(ul, g * GRP + q, hf);
+          G::V::cvt(w2[q], f);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(cu, f[e], acc[e]);
+          for (int e = 0; e < EPL; ++e) acc[e] = fmaf(cu, f[e], acc[e]);
+        }
       }
     }
   }
-  float* o = a.dx + t * d + col;
+  if (store) {
+    float* o = a.dx + t * d + col;
 #pragma unroll
-  for (int e = 0; e < EPL; e += 4) *(f32x4_t*)(o + e) = f32x4_t{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+    for (int e = 0; e < EPL; e += 4) *(f32x4_t*)(o + e) = f32x4_t{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+  }
 }
 
 // ---------------------------------------------------------------- transpose
@@ -204,63 +212,82 @@ __global__ __launch_bounds__(256) void seg_sort_kernel(const int32_t* __restrict
   }
 }
 
-// dW rows of every neuron, one wave per (neuron, d slice): the sums over
-// the neuron's ELL slots in ascending row order. Neurons without slots get
-// zero rows.
-template <typename E, int NS, int EPL, bool GATED>
+// dW rows of every neuron: the sums over the neuron's ELL slots in
+// ascending row order, RPW neurons per wave and d slice with 16-byte lanes
+// over the x and dy rows of the slots. Neurons without slots get zero rows.
+template <typename E, int NS, int SW, bool GATED>
 __global__ __launch_bounds__(256) void dw_sparse_kernel(BwdArgs a) {
-  using V = BV<E, EPL>;
+  using G = SliceGeom<E, SW>;
+  constexpr int EPL = G::EPL, RPW = G::RPW;
+  using R = typename G::R;
   const int lane = threadIdx.x & 63;
+  const int hf = RPW == 2 ? lane >> 5 : 0;
+  const int l = lane & (G::LPR - 1);
+  const int i = lane & 31;
   const int s = blockIdx.x % NS;
-  const int j = (blockIdx.x / NS) * 4 + (threadIdx.x >> 6);
-  if (j >= a.F) return;
-  const int d = NS * 64 * EPL;
-  const int64_t col = (int64_t)s * 64 * EPL + lane * EPL;
+  const int j = ((blockIdx.x / NS) * 4 + (threadIdx.x >> 6)) * RPW + hf;
+  if (j - hf >= a.F) return;
+  const bool ok = j < a.F;
+  const int jr = ok ? j : a.F - 1;
+  const int d = NS * SW;
+  const int64_t col = (int64_t)s * SW + l * EPL;
   const E* xs = (const E*)a.x + col;
   const E* dys = (const E*)a.dy + col;
+  const int b0 = a.noff[jr];
+  const int n = ok ? a.noff[jr + 1] - b0 : 0;
+  int nmax = __builtin_amdgcn_readlane(n, 0);
+  if constexpr (RPW == 2) nmax = max(nmax, __builtin_amdgcn_readlane(n, 32));
   float ag[EPL], au[EPL], ad[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) ag[e] = au[e] = ad[e] = 0.0f;
-  const int b = a.noff[j];
-  const int n = a.noff[j + 1] - b;
-  for (int i0 = 0; i0 < n; i0 += GRP) {
-    const int m = min(GRP, n - i0);
-    const int q = a.ent[b + i0 + min(lane, m - 1)];
-    const int tl = q / a.K;
-    float cz = a.gz[q];
-    float cu = GATED ? a.gu[q] : 0.0f;
-    float ch = GATED ? a.ell_a[q] * a.ell_u[q] : a.ell_a[q];
-    if (lane >= m) cz = cu = ch = 0.0f;
-    typename V::raw xv[GRP], dv[GRP];
-#pragma unroll
-    for (int r = 0; r < GRP; ++r) {
-      const int64_t t = __builtin_amdgcn_readlane(tl, r);
-      xv[r] = *(const typename V::raw*)(xs + t * d);
-      dv[r] = *(const typename V::raw*)(dys + t * d);
+  for (int i0 = 0; i0 < nmax; i0 += 32) {
+    // slot i0 + i of the lane's neuron: its row and dZ, dU, h (0 past the count)
+    const bool live = i0 + i < n;
+    const int q = live ? a.ent[b0 + i0 + i] : 0;
+    const int tl = live ? q / a.K : 0;
+    float cz = 0.0f, cu = 0.0f, ch = 0.0f;
+    if (live) {
+      cz = a.gz[q];
+      if (GATED) cu = a.gu[q];
+      ch = GATED ? a.ell_a[q] * a.ell_u[q] : a.ell_a[q];
     }
-    __builtin_amdgcn_sched_barrier(0);
+    const int m = min(32, nmax - i0);
 #pragma unroll
-    for (int r = 0; r < GRP; ++r) {
-      const float z = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cz), r));
-      const float u = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cu), r));
-      const float h = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ch), r));
-      float fx[EPL], fd[EPL];
-      V::cvt(xv[r], fx);
-      V::cvt(dv[r], fd);
+    for (int g = 0; g < 32 / GRP; ++g) {
+      if (g * GRP >= m) break;
+      R xv[GRP], dv[GRP];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        ag[e] = fmaf(z, fx[e], ag[e]);
-        if (GATED) au[e] = fmaf(u, fx[e], au[e]);
-        ad[e] = fmaf(h, fd[e], ad[e]);
+      for (int r = 0; r < GRP; ++r) {
+        const int64_t t = slot_id<RPW>(tl, g * GRP + r, hf);
+        xv[r] = *(const R*)(xs + t * d);
+        dv[r] = *(const R*)(dys + t * d);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < GRP; ++r) {
+        const float z = slot_val<RPW>(cz, g * GRP + r, hf);
+        const float u = slot_val<RPW>(cu, g * GRP + r, hf);
+        const float hh = slot_val<RPW>(ch, g * GRP + r, hf);
+        float fx[EPL], fd[EPL];
+        G::V::cvt(xv[r], fx);
+        G::V::cvt(dv[r], fd);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          ag[e] = fmaf(z, fx[e], ag[e]);
+          if (GATED) au[e] = fmaf(u, fx[e], au[e]);
+          ad[e] = fmaf(hh, fd[e], ad[e]);
+        }
       }
     }
   }
-  const int64_t ro = (int64_t)j * d + col;
+  if (ok) {
+    const int64_t ro = (int64_t)j * d + col;
 #pragma unroll
-  for (int e = 0; e < EPL; e += 4) {
-    *(f32x4_t*)(a.dwg + ro + e) = f32x4_t{ag[e], ag[e + 1], ag[e + 2], ag[e + 3]};
-    if (GATED) *(f32x4_t*)(a.dwu + ro + e) = f32x4_t{au[e], au[e + 1], au[e + 2], au[e + 3]};
-    *(f32x4_t*)(a.dwd + ro + e) = f32x4_t{ad[e], ad[e + 1], ad[e + 2], ad[e + 3]};
+    for (int e = 0; e < EPL; e += 4) {
+      *(f32x4_t*)(a.dwg + ro + e) = f32x4_t{ag[e], ag[e + 1], ag[e + 2], ag[e + 3]};
+      if (GATED) *(f32x4_t*)(a.dwu + ro + e) = f32x4_t{au[e], au[e + 1], au[e + 2], au[e + 3]};
+      *(f32x4_t*)(a.dwd + ro + e) = f32x4_t{ad[e], ad[e + 1], ad[e + 2], ad[e + 3]};
+    }
   }
 }
 
@@ -392,16 +419,20 @@ __global__ __launch_bounds__(256) void backup_grad_kernel(BwdArgs a) {
   }
 }
 
-template <typename E, int NS, int EPL>
+template <typename E, int NS, int SW>
 hipError_t launch_bwd_t(const BwdArgs& a, bool gated, int which, hipStream_t st) {
+  constexpr int RPW = SliceGeom<E, SW>::RPW;
   if (which == 0) {
-    const dim3 grid((unsigned)(NS * ((a.T + 3) / 4)));
-    if (gated) hipLaunchKernelGGL((dx_sparse_kernel<E, NS, EPL, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((dx_sparse_kernel<E, NS, EPL, false>), grid, dim3(256), 0, st, a);
+    const dim3 rows((unsigned)((a.T + 3) / 4));
+    if (gated) hipLaunchKernelGGL((dzu_kernel<NS, true>), rows, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dzu_kernel<NS, false>), rows, dim3(256), 0, st, a);
+    const dim3 grid((unsigned)(NS * ((a.T + 4 * RPW - 1) / (4 * RPW))));
+    if (gated) hipLaunchKernelGGL((dx_sparse_kernel<E, NS, SW, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dx_sparse_kernel<E, NS, SW, false>), grid, dim3(256), 0, st, a);
   } else {
-    const dim3 grid((unsigned)(NS * ((a.F + 3) / 4)));
-    if (gated) hipLaunchKernelGGL((dw_sparse_kernel<E, NS, EPL, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((dw_sparse_kernel<E, NS, EPL, false>), grid, dim3(256), 0, st, a);
+    const dim3 grid((unsigned)(NS * ((a.F + 4 * RPW - 1) / (4 * RPW))));
+    if (gated) hipLaunchKernelGGL((dw_sparse_kernel<E, NS, SW, true>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dw_sparse_kernel<E, NS, SW, false>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
@@ -411,19 +442,19 @@ hipError_t launch_bwd_t(const BwdArgs& a, bool gated, int which, hipStream_t st)
 hipError_t launch_bwd_sparse(Dtype dt, bool gated, int which, const BwdArgs& a, hipStream_t s) {
   int ns, epl;
   slice_shape(dt, a.d, &ns, &epl);
-#define SFFN_BW(E, NS_, EPL_) \
-  if (ns == NS_ && epl == EPL_) return launch_bwd_t<E, NS_, EPL_>(a, gated, which, s);
+  const int sw = a.d / ns;
+#define SFFN_BW(E, NS_, SW_) \
+  if (ns == NS_ && sw == SW_) return launch_bwd_t<E, NS_, SW_>(a, gated, which, s);
   if (dt == kBF16) {
-    SFFN_BW(uint16_t, 1, 4)
-    SFFN_BW(uint16_t, 2, 4)
-    SFFN_BW(uint16_t, 4, 4)
-    SFFN_BW(uint16_t, 8, 4)
-    SFFN_BW(uint16_t, 8, 8)
+    SFFN_BW(uint16_t, 2, 256)
+    SFFN_BW(uint16_t, 4, 256)
+    SFFN_BW(uint16_t, 8, 256)
+    SFFN_BW(uint16_t, 8, 512)
   } else {
-    SFFN_BW(float, 1, 4)
-    SFFN_BW(float, 2, 4)
-    SFFN_BW(float, 4, 4)
-    SFFN_BW(float, 8, 4)
+    SFFN_BW(float, 1, 256)
+    SFFN_BW(float, 2, 256)
+    SFFN_BW(float, 4, 256)
+    SFFN_BW(float, 8, 256)
   }
 #undef SFFN_BW
   return hipErrorInvalidValue;

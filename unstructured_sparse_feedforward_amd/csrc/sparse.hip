@@ -131,28 +131,6 @@ __global__ __launch_bounds__(1024) void backup_list_kernel(const uint8_t* __rest
   if (tid == 0) *n_backup = carry;
 }
 
-template <typename E, int EPL> struct Vec;
-template <> struct Vec<uint16_t, 4> {
-  typedef u32x2_t raw;
-  __device__ static void cvt(const raw& v, float* o) {
-    o[0] = bf16lo(v[0]); o[1] = bf16hi(v[0]); o[2] = bf16lo(v[1]); o[3] = bf16hi(v[1]);
-  }
-};
-template <> struct Vec<uint16_t, 8> {
-  typedef u32x4_t raw;
-  __device__ static void cvt(const raw& v, float* o) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) { o[2 * k] = bf16lo(v[k]); o[2 * k + 1] = bf16hi(v[k]); }
-  }
-};
-template <> struct Vec<float, 4> {
-  typedef u32x4_t raw;
-  __device__ static void cvt(const raw& v, float* o) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = __uint_as_float(v[k]);
-  }
-};
-
 constexpr int GRP = 32;  // active pairs in flight per wave
 
 // One butterfly exchange at lane distance W over the first 2*HALF values:
@@ -178,44 +156,6 @@ __device__ __forceinline__ void butterfly(float* v, int lane) {
 __device__ __forceinline__ float wave_sum32(float* v, int lane) {
   butterfly<32, 16>(v, lane);
   return v[0] + __shfl_xor(v[0], 1, 64);
-}
-
-// Each lane loads 16 bytes of a weight row slice per pair: a slice of
-// SW elements takes LPR = SW * sizeof(E) / 16 lanes, so a wave covers
-// RPW = 64 / LPR rows at once (two rows of a 256-wide bf16 slice, one row
-// otherwise). Wide loads halve the load instructions per byte, which is
-// what bounds these gathers. Pairs go 32 per row per group: lane i of a
-// row's lane group holds the metadata of slot k0 + i (lanes 32-63 repeat
-// lanes 0-31 when a row spans the whole wave). The metadata loads do not
-// wait for the row's count (the slot index is clamped to the row's K
-// slots), so a group costs one round trip for the metadata and one for the
-// weight rows. Slots past the count read neuron 0 and are discarded (ELL
-// padding is unspecified).
-template <typename E, int SW>
-struct SliceGeom {
-  static constexpr int EPL = 16 / (int)sizeof(E);
-  static constexpr int LPR = SW / EPL;
-  static constexpr int RPW = 64 / LPR;
-  static_assert(RPW == 1 || RPW == 2, "slice of 32 or 64 lanes");
-  using V = Vec<E, EPL>;
-  using R = typename V::raw;
-};
-
-// The neuron id of slot q of this lane's row, from the 32 ids held by the
-// row's lanes (wave-uniform index).
-template <int RPW>
-__device__ __forceinline__ int slot_id(int jl, int q, int hf) {
-  if constexpr (RPW == 2) {
-    const int j0 = __builtin_amdgcn_readlane(jl, q);
-    const int j1 = __builtin_amdgcn_readlane(jl, 32 + q);
-    return hf ? j1 : j0;
-  } else {
-    return __builtin_amdgcn_readlane(jl, q);
-  }
-}
-template <int RPW>
-__device__ __forceinline__ float slot_val(float v, int q, int hf) {
-  return __int_as_float(slot_id<RPW>(__float_as_int(v), q, hf));
 }
 
 // Phase 1: upart[s][t][k] = x_t[slice s] . W_u[j_k][slice s].
