@@ -486,9 +486,11 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   // sparse phases only the others: the dense path runs on the side stream
   // while the sparse kernels run on the caller's, launched first so that
   // its few workgroups are not queued behind the sparse grids.
+  // With per-kernel timing on, everything stays on the caller's stream so
+  // that each kernel's events bracket that kernel alone.
   hipStream_t main_stream = stream;
   bool forked = false;
-  if (!train || mcap > 0) {
+  if ((!train || mcap > 0) && !h->prof) {
     if ((e = hipEventRecord(h->ev_fork, main_stream)) != hipSuccess ||
         (e = hipStreamWaitEvent(h->side, h->ev_fork, 0)) != hipSuccess)
       return hip_fail(h, e, "fork");
