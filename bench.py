@@ -314,6 +314,8 @@ def bench_forward(args, np, torch, SparseFFN, wl):
         "ms_per_step_with_kernel_events": ms_p,
         "flagged_rows_per_step": n_flag,
     }
+    if stack:
+        out["dispatch"] = per_layer_dispatch(layers, args.steps, torch)
     if n_cpu > 0:
         what = (f"first {n_cpu} tokens of each of the {len(Ws)} layers" if stack
                 else f"first {n_cpu} of {T} tokens")
@@ -322,6 +324,44 @@ def bench_forward(args, np, torch, SparseFFN, wl):
             f"{what}: numpy float64 sparse forward (gate GEMM, TwELL pack, per-token "
             f"up/down over active neurons, dense flagged rows)")
     return out
+
+
+def per_layer_dispatch(layers, steps, torch):
+    """Per-layer sparse/dense choice for a stack: each layer's sparse and
+    dense forward are timed alone, every layer then runs in its faster mode,
+    and the whole stack is timed again with those choices."""
+    def time_one(fn, reps=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    t_sp, t_de, modes = [], [], []
+    for L in layers:
+        sp = time_one(lambda: L["ffn"].forward(*L["args"], mode="sparse", tw=L["tw"], y=L["y"]))
+        de = time_one(lambda: L["ffn"].forward(*L["args"], mode="dense", y=L["yd"]))
+        t_sp.append(sp)
+        t_de.append(de)
+        modes.append("sparse" if sp <= de else "dense")
+
+    def chosen():
+        for L, m in zip(layers, modes):
+            if m == "sparse":
+                L["ffn"].forward(*L["args"], mode="sparse", tw=L["tw"], y=L["y"])
+            else:
+                L["ffn"].forward(*L["args"], mode="dense", y=L["yd"])
+
+    ms, _, _ = _timed(chosen, steps, 3, torch)
+    T = layers[0]["W"].T
+    return {"value": T / ms, "ms_per_step": ms, "modes": modes,
+            "layer_ms_sparse": t_sp, "layer_ms_dense": t_de}
 
 
 def bench_train(args, np, torch, SparseFFN, wl):
