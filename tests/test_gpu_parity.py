@@ -221,6 +221,23 @@ def test_forward_deterministic():
     assert_twell_equal(a, b)
 
 
+def test_forward_same_with_kernel_timing():
+    """Per-kernel timing runs the flagged rows' dense path on the caller's
+    stream instead of the handle's second stream; y is the same bit for bit."""
+    inp = wl.make_inputs(wl.GATED_1P5B, seed=23, T=1500)
+    ffn = layer(inp)
+    args = [dev(inp, k) for k in ("x", "w_gate", "w_up", "w_down")]
+    tw = ffn.new_twell(1500)
+    y1 = ffn.forward(*args, mode="sparse", tw=tw).clone()
+    assert twell_np(tw)["n_flagged"] > 0
+    ffn.profile(True)
+    y2 = ffn.forward(*args, mode="sparse").clone()
+    prof = ffn.profile_read()
+    ffn.profile(False)
+    assert prof["flagged_gateup"][1] == 1 and prof["sparse_down"][1] == 1
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
 def test_empty_batch_is_noop():
     inp = wl.make_inputs(wl.SMALL_F32, seed=19, T=4)
     ffn = layer(inp)

@@ -33,7 +33,9 @@ __device__ __forceinline__ int wave_sum_int(int v) {
 
 // One wave per token row: count its positives, decide the route, and if
 // the row stays sparse, concatenate its TwELL tile lists (ascending neuron)
-// into ELL slots 0..nnz-1.
+// into ELL slots 0..nnz-1. Lane b takes tile b (64 tiles per pass): an
+// exclusive prefix of the stored counts gives each tile's first ELL slot,
+// and the lane copies its tile's entries, so only live slots are read.
 __global__ __launch_bounds__(256) void rows_kernel(EllArgs a) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -41,8 +43,10 @@ __global__ __launch_bounds__(256) void rows_kernel(EllArgs a) {
   const int32_t* cnt = a.cnt + t * a.n_t;
   int nnz = 0;
   bool over = false;
+  int c0 = 0;  // the count of tile `lane` (first pass of 64 tiles)
   for (int b = lane; b < a.n_t; b += 64) {
     const int c = cnt[b];
+    if (b < 64) c0 = c;
     nnz += c;
     over |= c > a.C;
   }
@@ -55,25 +59,25 @@ __global__ __launch_bounds__(256) void rows_kernel(EllArgs a) {
     a.ell_cnt[t] = backup ? 0 : nnz;
   }
   if (backup || nnz == 0) return;
-  const int total = a.n_t * a.C;
-  const int64_t src = t * total;
+  // not flagged: every tile count is <= C, so all entries are stored
   const int64_t dst = t * (int64_t)a.K;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int run = 0;
-  for (int q0 = 0; q0 < total && run < nnz; q0 += 64) {
-    const int q = q0 + lane;
-    bool act = false;
-    if (q < total) {
-      const int b = q / a.C;
-      act = (q - b * a.C) < cnt[b];
+  int base = 0;
+  for (int b0 = 0; b0 < a.n_t; b0 += 64) {
+    const int b = b0 + lane;
+    const int c = b < a.n_t ? (b0 == 0 ? c0 : cnt[b]) : 0;
+    int inc = c;  // inclusive prefix over the lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += v;
     }
-    const uint64_t m = __ballot(act);
-    if (act) {
-      const int k = run + __popcll(m & below);
-      a.ell_idx[dst + k] = a.idx[src + q];
-      a.ell_a[dst + k] = a.val[src + q];
+    const int64_t src = (t * a.n_t + b) * (int64_t)a.C;
+    const int64_t pos = dst + base + inc - c;
+    for (int s = 0; s < c; ++s) {
+      a.ell_idx[pos + s] = a.idx[src + s];
+      a.ell_a[pos + s] = a.val[src + s];
     }
-    run += __popcll(m);
+    base += __shfl(inc, 63, 64);
   }
 }
 
