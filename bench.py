@@ -162,6 +162,53 @@ def roof(kind, name, work, prof, keys, peak, traffic=None):
     return r
 
 
+def _socket_power_w():
+    """One reading of the GPU's socket power (amd-smi), or None."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["amd-smi", "metric", "--power", "-g", "0"], capture_output=True,
+                             text=True, timeout=10).stdout
+    except Exception:
+        return None
+    m = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", out)
+    return float(m.group(1)) if m else None
+
+
+def measure_energy(fn, tokens, torch, seconds=3.0):
+    """Average socket power while fn runs back to back for about `seconds`
+    (amd-smi sampled from a host thread) and the energy per input token."""
+    import threading
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            p = _socket_power_w()
+            if p is not None:
+                samples.append(p)
+            stop.wait(0.1)
+
+    for _ in range(5):
+        fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler)
+    th.start()
+    steps, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        steps += 10
+        torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    p = sum(samples) / len(samples)
+    return {"power_W": p, "samples": len(samples), "steps": steps,
+            "uJ_per_token": p * elapsed / (steps * tokens) * 1e6}
+
+
 def per_step(prof, steps):
     return {k: ms / steps for k, (ms, n) in prof.items()}
 
@@ -176,6 +223,9 @@ def main():
                     help="tokens of the oracle CPU baseline sample (-1 = the workload's "
                          "default, 0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--energy", action="store_true",
+                    help="also run the sparse and dense forwards for ~3 s each while sampling "
+                         "the socket power with amd-smi, and report energy per token")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the timed work, run a plain elementwise copy of MIB MiB "
                          "(float32 negate into a second buffer) three times, so hardware "
@@ -316,6 +366,13 @@ def bench_forward(args, np, torch, SparseFFN, wl):
     }
     if stack:
         out["dispatch"] = per_layer_dispatch(layers, args.steps, torch)
+    if args.energy:
+        idle = _socket_power_w()
+        e_sp = measure_energy(sparse, T, torch)
+        e_de = measure_energy(dense, T, torch)
+        out["energy"] = {"idle_W": idle, "sparse": e_sp, "dense": e_de,
+                         "method": "amd-smi socket power sampled every ~0.1-0.3 s from a host "
+                                   "thread while the forward runs back to back for ~3 s"}
     if n_cpu > 0:
         what = (f"first {n_cpu} tokens of each of the {len(Ws)} layers" if stack
                 else f"first {n_cpu} of {T} tokens")
