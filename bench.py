@@ -9,7 +9,8 @@ before the timed region. A step is one sparse forward: gate GEMM with the
 ReLU + TwELL epilogue, row routing and ELL compaction, the dense path for
 rows whose TwELL overflowed, and the sparse up/down projection.
 
-Other workloads (--workload): the non-gated layer at 29/108/911 active
+Other workloads (--workload): the gated layer at 15 active neurons per
+token (a stronger L1 stand-in, same shape); the non-gated layer at 29/108/911 active
 neurons per token (F = 8192, T = 16384); the 18-layer gated stack
 (T = 16384 per layer, active counts ramping 15 -> 120 -> 20, each layer on
 its own seeded input); the training step (forward that saves the Hybrid
@@ -38,7 +39,8 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 matrix/vector
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
-WORKLOADS = ("gated", "nongated29", "nongated108", "nongated911", "stack18", "train", "small")
+WORKLOADS = ("gated", "gated15", "nongated29", "nongated108", "nongated911", "stack18", "train",
+             "small")
 
 
 def _dev(inp, name, torch, np):
@@ -266,7 +268,8 @@ def bench_forward(args, np, torch, SparseFFN, wl):
     if stack:
         Ws = [wl.stack_layer(i) for i in range(len(wl.STACK_RAMP))]
     else:
-        Ws = [{"gated": wl.GATED_1P5B, "small": wl.SMALL_F32, "nongated29": wl.NONGATED[29],
+        Ws = [{"gated": wl.GATED_1P5B, "gated15": wl.GATED_1P5B_NNZ15,
+               "small": wl.SMALL_F32, "nongated29": wl.NONGATED[29],
                "nongated108": wl.NONGATED[108],
                "nongated911": wl.NONGATED[911]}[args.workload]]
     W0 = Ws[0]
