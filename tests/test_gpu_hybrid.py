@@ -205,6 +205,32 @@ def test_backward_all_rows_backup():
     assert_close_bf16(dwd.cpu().numpy(), ref["dw_down"], "dw_down")
 
 
+@pytest.mark.parametrize("max_backup", [None, 0])
+def test_backward_no_backup_rows(max_backup):
+    """No outlier tokens and K = 64 keep every row on the ELL path. With
+    backup buffers (None: T rows) their dW products are zero and the ELL
+    sums add to them; without (0 rows) the ELL sums are stored alone."""
+    w = wl.TRAIN_HYBRID.replace(outlier_frac=0.0)
+    _print(f"backward no backup rows max_backup={max_backup}")
+    inp = wl.make_inputs(w, seed=47, T=256)
+    wg, _, _ = math_weights(inp)
+    assert np.abs(inp.x.astype(np.float64) @ wg).min() > 2e-5
+    ffn = SparseFFN(w.d, w.F, gated=True, twell_cap=w.twell_cap, ell_cap=w.ell_cap,
+                    dtype=torch.bfloat16)
+    args = [dev(inp, k) for k in ("x", "w_gate", "w_up", "w_down")]
+    _, hy = ffn.forward_train(*args, max_backup=max_backup)
+    assert ffn.hybrid_check(hy) == B.SFFN_OK
+    assert int(hy["n_backup"][0].item()) == 0
+    # stale values in the outputs must not leak into the result
+    outs = tuple(torch.full((n, w.d), 7.0, device="cuda") for n in (256, w.F, w.F, w.F))
+    dx, dwg, dwu, dwd = ffn.backward(*args, hy, dev(inp, "dy"), out=outs)
+    ref = _grads_ref(inp, 0.0)
+    assert_close_bf16(dx.cpu().numpy(), ref["dx"], "dx")
+    assert_close_bf16(dwg.cpu().numpy(), ref["dw_gate"].T, "dw_gate")
+    assert_close_bf16(dwu.cpu().numpy(), ref["dw_up"].T, "dw_up")
+    assert_close_bf16(dwd.cpu().numpy(), ref["dw_down"], "dw_down")
+
+
 def test_training_full_size_sampled():
     """The training step at its full size (T = 8192, d = 2048, F = 5632,
     K = 64, 5% outlier tokens) in the launch configuration the benchmark

@@ -865,20 +865,8 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
     e = launch_bwd_sparse(dt, gated, 0, ba, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "backward dx");
-  // 3. slots grouped by neuron in ascending row order
-  {
-    ProfScope ps(h, SFFN_K_BWD_TRANSPOSE, stream);
-    e = launch_transpose(ba, stream);
-  }
-  if (e != hipSuccess) return hip_fail(h, e, "backward transpose");
-  // 4. dW rows of every neuron from the ELL slots
-  {
-    ProfScope ps(h, SFFN_K_BWD_DW, stream);
-    e = launch_bwd_sparse(dt, gated, 1, ba, stream);
-  }
-  if (e != hipSuccess) return hip_fail(h, e, "backward dW");
-
-  // 5. backup rows, densely: dH = dy W_d^T, then dZ/dU, dx rows, and dW +=
+  // 3. backup rows, densely: dH = dy W_d^T, then dZ/dU, dx rows and their
+  // dW products (zeros when no row took the backup path)
   if (cap > 0) {
     ProfScope ps(h, SFFN_K_BWD_DENSE, stream);
     const bool split = dt == kBF16;
@@ -950,7 +938,7 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
       if (e == hipSuccess) e = launch_splitk_reduce(f, dx, D.d, stream);
       if (e != hipSuccess) return hip_fail(h, e, "backup dx");
     }
-    // dW += (dZ, dU, H)^T (x, x, dy) over the backup rows
+    // dW = (dZ, dU, H)^T (x, x, dy) over the backup rows
     for (int pass = 0; pass < 3; ++pass) {
       if (pass == 1 && !gated) continue;
       GemmArgs w = {};
@@ -965,13 +953,28 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
       w.k_mult = split ? 2 : 1;
       w.out = pass == 0 ? dw_gate : (pass == 1 ? dw_up : dw_down);
       w.ldo = D.d;
-      w.accumulate = 1;
+      w.accumulate = 0;
       w.grid = gemm_grid(dt, 1, h->num_cu);
       w.num_cu = h->num_cu;
       e = launch_gemm(dt, 1, true, kEpiStoreF32, w, stream);
       if (e != hipSuccess) return hip_fail(h, e, "backup dW");
     }
   }
+  // 4. slots grouped by neuron in ascending row order
+  {
+    ProfScope ps(h, SFFN_K_BWD_TRANSPOSE, stream);
+    e = launch_transpose(ba, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "backward transpose");
+  // 5. dW rows of every neuron from the ELL slots, added to the backup
+  // rows' products when there are backup buffers
+  {
+    ProfScope ps(h, SFFN_K_BWD_DW, stream);
+    ba.accumulate = cap > 0;
+    e = launch_bwd_sparse(dt, gated, 1, ba, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "backward dW");
+
   return SFFN_OK;
 }
 

@@ -214,7 +214,8 @@ __global__ __launch_bounds__(256) void seg_sort_kernel(const int32_t* __restrict
 
 // dW rows of every neuron: the sums over the neuron's ELL slots in
 // ascending row order, RPW neurons per wave and d slice with 16-byte lanes
-// over the x and dy rows of the slots. Neurons without slots get zero rows.
+// over the x and dy rows of the slots, added to dW's rows when accumulating
+// (the backup rows' products); else neurons without slots get zero rows.
 template <typename E, int NS, int SW, bool GATED>
 __global__ __launch_bounds__(256) void dw_sparse_kernel(BwdArgs a) {
   using G = SliceGeom<E, SW>;
@@ -237,9 +238,26 @@ __global__ __launch_bounds__(256) void dw_sparse_kernel(BwdArgs a) {
   const int n = ok ? a.noff[jr + 1] - b0 : 0;
   int nmax = __builtin_amdgcn_readlane(n, 0);
   if constexpr (RPW == 2) nmax = max(nmax, __builtin_amdgcn_readlane(n, 32));
+  const int64_t ro = (int64_t)j * d + col;
   float ag[EPL], au[EPL], ad[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) ag[e] = au[e] = ad[e] = 0.0f;
+  if (a.accumulate && ok) {
+    // the backup rows' products are already stored: the sums continue them
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) {
+      const f32x4_t vg = *(const f32x4_t*)(a.dwg + ro + e);
+      f32x4_t vu = {};
+      if (GATED) vu = *(const f32x4_t*)(a.dwu + ro + e);
+      const f32x4_t vd = *(const f32x4_t*)(a.dwd + ro + e);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        ag[e + c] = vg[c];
+        au[e + c] = vu[c];
+        ad[e + c] = vd[c];
+      }
+    }
+  }
   for (int i0 = 0; i0 < nmax; i0 += 32) {
     // slot i0 + i of the lane's neuron: its row and dZ, dU, h (0 past the count)
     const bool live = i0 + i < n;
@@ -281,7 +299,6 @@ __global__ __launch_bounds__(256) void dw_sparse_kernel(BwdArgs a) {
     }
   }
   if (ok) {
-    const int64_t ro = (int64_t)j * d + col;
 #pragma unroll
     for (int e = 0; e < EPL; e += 4) {
       *(f32x4_t*)(a.dwg + ro + e) = f32x4_t{ag[e], ag[e + 1], ag[e + 2], ag[e + 3]};

@@ -444,11 +444,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_bt_kernel(GemmArgs g) {
   const int wc = wave & 1;
   const int M = g.M;
   // K may live on the device (rows of a backup list, in blocks of 64,
-  // times k_mult for stacked hi/lo parts); then the products accumulate
-  // into the output and a K of 0 leaves it as it is
+  // times k_mult for stacked hi/lo parts); a K of 0 leaves an accumulated
+  // output as it is and stores zeros otherwise
   const int Kd = g.k_dev ? g.k_mult * ((device_rows(g.k_dev, g.k_cap) + 63) / 64 * 64) : g.K;
   const int nkt = Kd / BK;
-  if (nkt == 0) return;
+  if (nkt == 0 && g.accumulate) return;
   const TileSched ts(M, g.N, BN);
 
   const char* Ab = (const char*)g.A;
@@ -526,52 +526,54 @@ __global__ __launch_bounds__(NT, 1) void gemm_bt_kernel(GemmArgs g) {
         bfr[buf][0][j] = *(const u32x4_t*)(sa + BM * ROWB + lds_off(wc * 128 + j * 32 + (lane & 31), ch));
     };
 
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
-    wg_barrier();   // the previous tile's readers are done with LDS
-    __builtin_amdgcn_sched_barrier(0);
-    load_b(0);
-    copy_a(0, 0);
-    store_b(0);
-    if (nkt > 1) {
-      load_b(1);
-      copy_a(1, 1);
-      store_b(1);
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
-    wg_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(0, 0, 0);
-
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int st = kt & 1;
-      // B of stage kt+2 into registers now (its LDS buffer is still being
-      // read); into LDS after the barrier, so the loads have three
-      // substeps to arrive
-      const bool pre = kt + 2 < nkt;
-      if (pre) load_b(kt + 2);
+    if (nkt > 0) {
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+      wg_barrier();   // the previous tile's readers are done with LDS
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // fragments of substep s
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(st, s + 1, (s + 1) & 1);
-        mfma_substep<NB>(acc, af[s & 1], bfr[s & 1]);
-        interleave_reads();
-        __builtin_amdgcn_sched_barrier(0);
+      load_b(0);
+      copy_a(0, 0);
+      store_b(0);
+      if (nkt > 1) {
+        load_b(1);
+        copy_a(1, 1);
+        store_b(1);
       }
-      // stage kt+1 is in LDS
       __builtin_amdgcn_s_waitcnt(kWaitAll);
       wg_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      if (pre) {
-        copy_a(kt + 2, st);
-        store_b(st);
+      read_frags(0, 0, 0);
+
+      for (int kt = 0; kt < nkt; ++kt) {
+        const int st = kt & 1;
+        // B of stage kt+2 into registers now (its LDS buffer is still being
+        // read); into LDS after the barrier, so the loads have three
+        // substeps to arrive
+        const bool pre = kt + 2 < nkt;
+        if (pre) load_b(kt + 2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+          __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // fragments of substep s
+          __builtin_amdgcn_sched_barrier(0);
+          read_frags(st, s + 1, (s + 1) & 1);
+          mfma_substep<NB>(acc, af[s & 1], bfr[s & 1]);
+          interleave_reads();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // stage kt+1 is in LDS
+        __builtin_amdgcn_s_waitcnt(kWaitAll);
+        wg_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (pre) {
+          copy_a(kt + 2, st);
+          store_b(st);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(st ^ 1, 0, 0);
+        mfma_substep<NB>(acc, af[1], bfr[1]);
+        interleave_reads();
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(st ^ 1, 0, 0);
-      mfma_substep<NB>(acc, af[1], bfr[1]);
-      interleave_reads();
-      __builtin_amdgcn_sched_barrier(0);
     }
     epilogue<NB, EPI>(g, acc, m0, n0, wr, wc, lane);
   }
@@ -592,8 +594,8 @@ hipError_t launch_ring(const GemmArgs& g, hipStream_t s) {
 bool gemm_big_supported(Dtype dt, int nb, bool bt, Epi epi, const GemmArgs& g) {
   if (dt != kBF16 || g.m_dev || g.a_rows || g.out_rows || g.part || g.kwrap) return false;
   if (g.accumulate && epi != kEpiStoreF32) return false;
-  // a device-sized K (n-contiguous B only) accumulates into the output
-  if (g.k_dev) return bt && nb == 1 && epi == kEpiStoreF32 && g.accumulate && g.k_mult >= 1;
+  // a device-sized K: n-contiguous B only
+  if (g.k_dev) return bt && nb == 1 && epi == kEpiStoreF32 && g.k_mult >= 1;
   if (g.K % (bt ? BK : RBK) != 0) return false;
   if (bt) return nb == 1 && epi == kEpiStoreF32;
   if (epi == kEpiTwell) return nb == 1 && g.ovf == nullptr;

@@ -314,6 +314,7 @@ struct BwdArgs {
   float* dwg;             // [F, d]
   float* dwu;             // [F, d] (gated)
   float* dwd;             // [F, d]
+  int accumulate;         // dW of the ELL slots adds to what dW holds
   int32_t* ncnt;          // [2F] per-neuron counts, then fill cursors
   int32_t* noff;          // [F + 1]
   int32_t* ent_unsorted;  // [T*K]
