@@ -80,7 +80,7 @@ struct Layout {
   size_t ell_a = 0, ell_idx = 0, ell_cnt = 0, bk = 0, upart = 0;
   size_t hid = 0, part = 0, total = 0;
   // backward
-  size_t gz = 0, gu = 0, ncnt = 0, noff = 0, ent0 = 0, ent = 0, dH = 0, gz_rm = 0, gu_rm = 0;
+  size_t gz = 0, gu = 0, ncnt = 0, noff = 0, ent0 = 0, meta = 0, dH = 0, gz_rm = 0, gu_rm = 0;
   size_t gz_t = 0, gu_t = 0, gh_t = 0, xb = 0, dyb = 0;
   int64_t ldt = 0;
 };
@@ -153,7 +153,7 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
     L.ncnt = take((size_t)2 * F * 4);
     L.noff = take((size_t)(F + 1) * 4);
     L.ent0 = take((size_t)T * K * 4);
-    L.ent = take((size_t)T * K * 4);
+    L.meta = take((size_t)T * K * 16);
     L.dH = take((size_t)T * F * 4);
     L.gz_rm = take((size_t)T * F * 4);
     L.gu_rm = take((size_t)T * F * 4);
@@ -843,7 +843,7 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
   ba.ncnt = at<int32_t>(ws, L.ncnt);
   ba.noff = at<int32_t>(ws, L.noff);
   ba.ent_unsorted = at<int32_t>(ws, L.ent0);
-  ba.ent = at<int32_t>(ws, L.ent);
+  ba.meta = at<f32x4_t>(ws, L.meta);
   ba.brow = hy->brow;
   ba.n_backup = hy->n_backup;
   ba.cap = cap;

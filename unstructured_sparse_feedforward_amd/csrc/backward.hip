@@ -191,59 +191,86 @@ __global__ __launch_bounds__(256) void fill_kernel(const uint16_t* __restrict__ 
 }
 
 // One wave per neuron: sort its segment ascending by rank counting (slot
-// indices are distinct, so every value's rank is the number of smaller ones).
-__global__ __launch_bounds__(256) void seg_sort_kernel(const int32_t* __restrict__ noff, int F,
-                                                       const int32_t* __restrict__ ent,
-                                                       int32_t* __restrict__ sorted) {
+// indices are distinct, so every value's rank is the number of smaller
+// ones) and store each slot as the record the dW sums read: {row, dZ, dU,
+// h} with h = a*u (gated) or a.
+template <bool GATED>
+__global__ __launch_bounds__(256) void seg_sort_kernel(BwdArgs a) {
   const int lane = threadIdx.x & 63;
   const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (j >= F) return;
-  const int b = noff[j];
-  const int n = noff[j + 1] - b;
+  if (j >= a.F) return;
+  const int b = a.noff[j];
+  const int n = a.noff[j + 1] - b;
+  const int32_t* ent = a.ent_unsorted;
   for (int i0 = 0; i0 < n; i0 += 64) {
-    const int v = i0 + lane < n ? ent[b + i0 + lane] : 0;
+    const bool live = i0 + lane < n;
+    const int v = live ? ent[b + i0 + lane] : 0;
     int rank = 0;
     for (int c0 = 0; c0 < n; c0 += 64) {
       const int w = c0 + lane < n ? ent[b + c0 + lane] : 0x7FFFFFFF;
       const int m = min(64, n - c0);
       for (int q = 0; q < m; ++q) rank += __builtin_amdgcn_readlane(w, q) < v ? 1 : 0;
     }
-    if (i0 + lane < n) sorted[b + rank] = v;
+    if (live) {
+      const float h = GATED ? a.ell_a[v] * a.ell_u[v] : a.ell_a[v];
+      a.meta[b + rank] = f32x4_t{__int_as_float(v / a.K), a.gz[v], GATED ? a.gu[v] : 0.0f, h};
+    }
   }
 }
 
 // dW rows of every neuron: the sums over the neuron's ELL slots in
-// ascending row order, RPW neurons per wave and d slice with 16-byte lanes
-// over the x and dy rows of the slots, added to dW's rows when accumulating
-// (the backup rows' products); else neurons without slots get zero rows.
-template <typename E, int NS, int SW, bool GATED>
+// ascending row order of (dZ*x, dU*x, h*dy), added to dW's rows when
+// accumulating (the backup rows' products are stored there); otherwise
+// neurons without slots get zero rows. A lane loads 16 bytes of a row, a
+// neuron's SW-column slice takes LPR lanes, so a wave sums RPW neurons. The
+// x and dy rows a slice gathers are random over all T rows, so an XCD keeps
+// to one slice at a time: workgroup b runs on XCD b mod 8 and the blocks
+// are ordered slice phase first, so the x and dy columns in use on an XCD
+// (T * SW * 4 bytes) stay within its L2. The wave stages the slot records
+// of its neurons in LDS, 64 per neuron at a time, and reads them back as
+// broadcasts; records past a neuron's count are zero (row 0, no weight).
+template <typename E, int SW, bool GATED, int GRP>
 __global__ __launch_bounds__(256) void dw_sparse_kernel(BwdArgs a) {
-  using G = SliceGeom<E, SW>;
-  constexpr int EPL = G::EPL, RPW = G::RPW;
-  using R = typename G::R;
+  constexpr int EPL = 16 / (int)sizeof(E);
+  constexpr int LPR = SW / EPL;
+  constexpr int RPW = 64 / LPR;
+  constexpr int CH = 64;
+  static_assert(RPW >= 1 && RPW <= 8 && CH % GRP == 0, "slice geometry");
+  using V = Vec<E, EPL>;
+  using R = typename V::raw;
+  __shared__ f32x4_t rec[4][RPW][CH];
   const int lane = threadIdx.x & 63;
-  const int hf = RPW == 2 ? lane >> 5 : 0;
-  const int l = lane & (G::LPR - 1);
-  const int i = lane & 31;
-  const int s = blockIdx.x % NS;
-  const int j = ((blockIdx.x / NS) * 4 + (threadIdx.x >> 6)) * RPW + hf;
-  if (j - hf >= a.F) return;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane / LPR;
+  const int l = lane % LPR;
+  const int nsl = a.d / SW;
+  const int nbk = (a.F + 4 * RPW - 1) / (4 * RPW);
+  int slice, grp;
+  if (nsl % 8 == 0) {
+    const int q = blockIdx.x / 8;
+    slice = (q / nbk) * 8 + blockIdx.x % 8;
+    grp = q % nbk;
+  } else {
+    slice = blockIdx.x % nsl;
+    grp = blockIdx.x / nsl;
+  }
+  const int jw = (grp * 4 + wave) * RPW;
+  if (jw >= a.F) return;
+  const int j = jw + r;
   const bool ok = j < a.F;
-  const int jr = ok ? j : a.F - 1;
-  const int d = NS * SW;
-  const int64_t col = (int64_t)s * SW + l * EPL;
+  const int b0 = ok ? a.noff[j] : 0;
+  const int n = ok ? a.noff[j + 1] - b0 : 0;
+  int nmax = 0;
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) nmax = max(nmax, __builtin_amdgcn_readlane(n, q * LPR));
+  const int col = slice * SW + l * EPL;
+  const int64_t ro = (int64_t)j * a.d + col;
   const E* xs = (const E*)a.x + col;
   const E* dys = (const E*)a.dy + col;
-  const int b0 = a.noff[jr];
-  const int n = ok ? a.noff[jr + 1] - b0 : 0;
-  int nmax = __builtin_amdgcn_readlane(n, 0);
-  if constexpr (RPW == 2) nmax = max(nmax, __builtin_amdgcn_readlane(n, 32));
-  const int64_t ro = (int64_t)j * d + col;
   float ag[EPL], au[EPL], ad[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) ag[e] = au[e] = ad[e] = 0.0f;
   if (a.accumulate && ok) {
-    // the backup rows' products are already stored: the sums continue them
 #pragma unroll
     for (int e = 0; e < EPL; e += 4) {
       const f32x4_t vg = *(const f32x4_t*)(a.dwg + ro + e);
@@ -258,42 +285,40 @@ __global__ __launch_bounds__(256) void dw_sparse_kernel(BwdArgs a) {
       }
     }
   }
-  for (int i0 = 0; i0 < nmax; i0 += 32) {
-    // slot i0 + i of the lane's neuron: its row and dZ, dU, h (0 past the count)
-    const bool live = i0 + i < n;
-    const int q = live ? a.ent[b0 + i0 + i] : 0;
-    const int tl = live ? q / a.K : 0;
-    float cz = 0.0f, cu = 0.0f, ch = 0.0f;
-    if (live) {
-      cz = a.gz[q];
-      if (GATED) cu = a.gu[q];
-      ch = GATED ? a.ell_a[q] * a.ell_u[q] : a.ell_a[q];
-    }
-    const int m = min(32, nmax - i0);
+  for (int i0 = 0; i0 < nmax; i0 += CH) {
+    // stage the records of slots i0 .. i0+63 of the wave's neurons
 #pragma unroll
-    for (int g = 0; g < 32 / GRP; ++g) {
-      if (g * GRP >= m) break;
+    for (int q = 0; q < RPW; ++q) {
+      const int bq = __builtin_amdgcn_readlane(b0, q * LPR);
+      const int nq = __builtin_amdgcn_readlane(n, q * LPR);
+      f32x4_t v = {};
+      if (i0 + lane < nq) v = a.meta[bq + i0 + lane];
+      rec[wave][q][lane] = v;
+    }
+    // a wave's LDS accesses complete in issue order: no barrier is needed
+    // between its own writes and reads
+    const int m = min(CH, nmax - i0);
+    for (int g0 = 0; g0 < m; g0 += GRP) {
+      f32x4_t md[GRP];
       R xv[GRP], dv[GRP];
 #pragma unroll
-      for (int r = 0; r < GRP; ++r) {
-        const int64_t t = slot_id<RPW>(tl, g * GRP + r, hf);
-        xv[r] = *(const R*)(xs + t * d);
-        dv[r] = *(const R*)(dys + t * d);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      for (int k = 0; k < GRP; ++k) md[k] = rec[wave][r][g0 + k];
 #pragma unroll
-      for (int r = 0; r < GRP; ++r) {
-        const float z = slot_val<RPW>(cz, g * GRP + r, hf);
-        const float u = slot_val<RPW>(cu, g * GRP + r, hf);
-        const float hh = slot_val<RPW>(ch, g * GRP + r, hf);
+      for (int k = 0; k < GRP; ++k) {
+        const int64_t t = __float_as_int(md[k][0]);
+        xv[k] = *(const R*)(xs + t * a.d);
+        dv[k] = *(const R*)(dys + t * a.d);
+      }
+#pragma unroll
+      for (int k = 0; k < GRP; ++k) {
         float fx[EPL], fd[EPL];
-        G::V::cvt(xv[r], fx);
-        G::V::cvt(dv[r], fd);
+        V::cvt(xv[k], fx);
+        V::cvt(dv[k], fd);
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-          ag[e] = fmaf(z, fx[e], ag[e]);
-          if (GATED) au[e] = fmaf(u, fx[e], au[e]);
-          ad[e] = fmaf(hh, fd[e], ad[e]);
+          ag[e] = fmaf(md[k][1], fx[e], ag[e]);
+          if (GATED) au[e] = fmaf(md[k][2], fx[e], au[e]);
+          ad[e] = fmaf(md[k][3], fd[e], ad[e]);
         }
       }
     }
@@ -447,9 +472,12 @@ hipError_t launch_bwd_t(const BwdArgs& a, bool gated, int which, hipStream_t st)
     if (gated) hipLaunchKernelGGL((dx_sparse_kernel<E, NS, SW, true>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((dx_sparse_kernel<E, NS, SW, false>), grid, dim3(256), 0, st, a);
   } else {
-    const dim3 grid((unsigned)(NS * ((a.F + 4 * RPW - 1) / (4 * RPW))));
-    if (gated) hipLaunchKernelGGL((dw_sparse_kernel<E, NS, SW, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((dw_sparse_kernel<E, NS, SW, false>), grid, dim3(256), 0, st, a);
+    // 128-column slices (bf16: four neurons per wave)
+    constexpr int DSW = 128;
+    constexpr int DRPW = 64 / (DSW * (int)sizeof(E) / 16);
+    const dim3 grid((unsigned)((a.d / DSW) * ((a.F + 4 * DRPW - 1) / (4 * DRPW))));
+    if (gated) hipLaunchKernelGGL((dw_sparse_kernel<E, DSW, true, 4>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dw_sparse_kernel<E, DSW, false, 4>), grid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
@@ -484,8 +512,8 @@ hipError_t launch_transpose(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, a.ncnt, a.F, a.noff);
   hipLaunchKernelGGL(fill_kernel, rows, blk, 0, s, a.ell_idx, a.ell_cnt, a.T, a.K, a.noff,
                      a.ncnt + a.F, a.ent_unsorted);
-  hipLaunchKernelGGL(seg_sort_kernel, dim3((unsigned)((a.F + 3) / 4)), blk, 0, s, a.noff, a.F,
-                     a.ent_unsorted, a.ent);
+  if (a.wu) hipLaunchKernelGGL(seg_sort_kernel<true>, dim3((unsigned)((a.F + 3) / 4)), blk, 0, s, a);
+  else hipLaunchKernelGGL(seg_sort_kernel<false>, dim3((unsigned)((a.F + 3) / 4)), blk, 0, s, a);
   return hipGetLastError();
 }
 

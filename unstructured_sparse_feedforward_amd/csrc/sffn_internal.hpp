@@ -317,8 +317,8 @@ struct BwdArgs {
   int accumulate;         // dW of the ELL slots adds to what dW holds
   int32_t* ncnt;          // [2F] per-neuron counts, then fill cursors
   int32_t* noff;          // [F + 1]
-  int32_t* ent_unsorted;  // [T*K]
-  int32_t* ent;           // [T*K] slots grouped by neuron, ascending
+  int32_t* ent_unsorted;  // [T*K] slot ids grouped by neuron
+  f32x4_t* meta;          // [T*K] {row, dZ, dU, h} grouped by neuron, ascending rows
   // backup rows
   const int32_t* brow;
   const int32_t* n_backup;
