@@ -80,7 +80,7 @@ struct Layout {
   size_t ell_a = 0, ell_idx = 0, ell_cnt = 0, bk = 0, upart = 0;
   size_t hid = 0, part = 0, total = 0;
   // backward
-  size_t gz = 0, gu = 0, ncnt = 0, noff = 0, ent0 = 0, meta = 0, dH = 0, gz_rm = 0, gu_rm = 0;
+  size_t gz = 0, gu = 0, drec = 0, ncnt = 0, noff = 0, ent0 = 0, meta = 0, dH = 0, gz_rm = 0, gu_rm = 0;
   size_t gz_t = 0, gu_t = 0, gh_t = 0, xb = 0, dyb = 0;
   int64_t ldt = 0;
 };
@@ -150,6 +150,7 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
     L.upart = take((size_t)ns * T * Kp * 4);
     L.gz = take((size_t)T * K * 4);
     L.gu = take((size_t)T * K * 4);
+    L.drec = take((size_t)T * K * 16);
     L.ncnt = take((size_t)2 * F * 4);
     L.noff = take((size_t)(F + 1) * 4);
     L.ent0 = take((size_t)T * K * 4);
@@ -836,6 +837,7 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
   ba.dpart = at<float>(ws, L.upart);
   ba.gz = at<float>(ws, L.gz);
   ba.gu = at<float>(ws, L.gu);
+  ba.drec = at<f32x4_t>(ws, L.drec);
   ba.dx = dx;
   ba.dwg = dw_gate;
   ba.dwu = dw_up;

@@ -35,88 +35,107 @@ __global__ __launch_bounds__(256) void dzu_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < NS; ++r) dh += a.dpart[((int64_t)r * a.T + t) * a.Kp + k];
     const int64_t q = t * a.K + k;
+    float gz, gu = 0.0f;
     if constexpr (GATED) {
-      a.gu[q] = dh * a.ell_a[q];
-      a.gz[q] = dh * a.ell_u[q] + a.l1;
+      gu = dh * a.ell_a[q];
+      gz = dh * a.ell_u[q] + a.l1;
+      a.gu[q] = gu;
     } else {
-      a.gz[q] = dh + a.l1;
+      gz = dh + a.l1;
     }
+    a.gz[q] = gz;
+    a.drec[q] = f32x4_t{__int_as_float((int)a.ell_idx[q]), gz, gu, 0.0f};
   }
 }
 
-constexpr int GRP = 16;   // slots per group: two 16-byte loads each in flight
-
-// dx of the ELL rows: dx_t[slice] = sum_k dZ_k W_g[j_k][slice] + dU_k W_u[j_k][slice],
-// RPW rows per wave with 16-byte lanes (the slice geometry of the forward
-// gathers). Backup rows are left to the dense path.
-template <typename E, int NS, int SW, bool GATED>
+// dx of the ELL rows: dx_t = sum over the row's slots of dZ W_g[j] + dU W_u[j]
+// (backup rows are left to the dense path). A lane loads 16 bytes of a
+// weight row, a row's SW-column slice takes LPR lanes, so a wave sums RPW
+// rows. Workgroup b runs on XCD b mod 8 and the blocks are ordered slice
+// phase first, so an XCD gathers from one slice of W_g and W_u at a time
+// (F * SW * 4 bytes, within its L2). The wave stages its rows' slot records
+// {neuron, dZ, dU} in LDS, 64 per row at a time, and reads them back as
+// broadcasts; records past a row's count are zero (neuron 0, no weight).
+template <typename E, int SW, bool GATED, int GRP>
 __global__ __launch_bounds__(256) void dx_sparse_kernel(BwdArgs a) {
-  using G = SliceGeom<E, SW>;
-  constexpr int EPL = G::EPL, RPW = G::RPW;
-  using R = typename G::R;
+  constexpr int EPL = 16 / (int)sizeof(E);
+  constexpr int LPR = SW / EPL;
+  constexpr int RPW = 64 / LPR;
+  constexpr int CH = 64;
+  static_assert(RPW >= 1 && RPW <= 8 && CH % GRP == 0, "slice geometry");
+  using V = Vec<E, EPL>;
+  using R = typename V::raw;
+  __shared__ f32x4_t rec[4][RPW][CH];
   const int lane = threadIdx.x & 63;
-  const int hf = RPW == 2 ? lane >> 5 : 0;
-  const int l = lane & (G::LPR - 1);
-  const int i = lane & 31;
-  const int s = blockIdx.x % NS;
-  const int64_t t = ((int64_t)(blockIdx.x / NS) * 4 + (threadIdx.x >> 6)) * RPW + hf;
-  if (t - hf >= a.T) return;
-  const bool ok = t < a.T;
-  const int64_t tr = ok ? t : a.T - 1;
-  const int d = NS * SW;
-  const int64_t col = (int64_t)s * SW + l * EPL;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane / LPR;
+  const int l = lane % LPR;
+  const int nsl = a.d / SW;
+  const int64_t nbk = (a.T + 4 * RPW - 1) / (4 * RPW);
+  int slice;
+  int64_t grp;
+  if (nsl % 8 == 0) {
+    const int64_t q = blockIdx.x / 8;
+    slice = (int)(q / nbk) * 8 + blockIdx.x % 8;
+    grp = q % nbk;
+  } else {
+    slice = blockIdx.x % nsl;
+    grp = blockIdx.x / nsl;
+  }
+  const int64_t tw = (grp * 4 + wave) * RPW;
+  if (tw >= a.T) return;
+  const int64_t t = tw + r;
+  const bool store = t < a.T && a.slot[t] < 0;
+  const int n = store ? a.ell_cnt[t] : 0;
+  int nmax = 0;
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) nmax = max(nmax, __builtin_amdgcn_readlane(n, q * LPR));
+  const int col = slice * SW + l * EPL;
   const char* wg = (const char*)a.wg;
   const char* wu = (const char*)a.wu;
-  const uint32_t colb = (uint32_t)(col * sizeof(E));
-  const uint32_t rowb = (uint32_t)(d * sizeof(E));
-  const int64_t rb = tr * a.K;
-  const bool store = ok && a.slot[tr] < 0;
-  const int n = ok ? a.ell_cnt[tr] : 0;
-  int nmax = __builtin_amdgcn_readlane(n, 0);
-  if constexpr (RPW == 2) nmax = max(nmax, __builtin_amdgcn_readlane(n, 32));
+  const uint32_t colb = (uint32_t)col * sizeof(E);
+  const uint32_t rowb = (uint32_t)a.d * sizeof(E);
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-  for (int k0 = 0; k0 < nmax; k0 += 32) {
-    // slot k0 + i of the lane's row: neuron, dZ, dU (0 past the count)
-    const int k = min(k0 + i, a.K - 1);
-    const bool live = k0 + i < n;
-    int jl = a.ell_idx[rb + k];
-    float zl = a.gz[rb + k];
-    float ul = GATED ? a.gu[rb + k] : 0.0f;
-    jl = live ? jl : 0;
-    zl = live ? zl : 0.0f;
-    ul = live ? ul : 0.0f;
-    const int m = min(32, nmax - k0);
+  for (int k0 = 0; k0 < nmax; k0 += CH) {
 #pragma unroll
-    for (int g = 0; g < 32 / GRP; ++g) {
-      if (g * GRP >= m) break;
+    for (int q = 0; q < RPW; ++q) {
+      const int nq = __builtin_amdgcn_readlane(n, q * LPR);
+      f32x4_t v = {};
+      if (k0 + lane < nq) v = a.drec[(tw + q) * a.K + k0 + lane];
+      rec[wave][q][lane] = v;
+    }
+    // a wave's LDS accesses complete in issue order: no barrier is needed
+    // between its own writes and reads
+    const int m = min(CH, nmax - k0);
+    for (int g0 = 0; g0 < m; g0 += GRP) {
+      f32x4_t md[GRP];
       R w[GRP], w2[GATED ? GRP : 1];
 #pragma unroll
-      for (int q = 0; q < GRP; ++q) {
-        const uint32_t off = (uint32_t)slot_id<RPW>(jl, g * GRP + q, hf) * rowb + colb;
-        w[q] = *(const R*)(wg + off);
-        if constexpr (GATED) w2[q] = *(const R*)(wu + off);
+      for (int k = 0; k < GRP; ++k) md[k] = rec[wave][r][g0 + k];
+#pragma unroll
+      for (int k = 0; k < GRP; ++k) {
+        const uint32_t off = (uint32_t)__float_as_int(md[k][0]) * rowb + colb;
+        w[k] = *(const R*)(wg + off);
+        if constexpr (GATED) w2[k] = *(const R*)(wu + off);
       }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int q = 0; q < GRP; ++q) {
-        const float cz = slot_val<RPW>(zl, g * GRP + q, hf);
+      for (int k = 0; k < GRP; ++k) {
         float f[EPL];
-        G::V::cvt(w[q], f);
+        V::cvt(w[k], f);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(cz, f[e], acc[e]);
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(md[k][1], f[e], acc[e]);
         if constexpr (GATED) {
-          const float cu = slot_val<RPW>(ul, g * GRP + q, hf);
-          G::V::cvt(w2[q], f);
+          V::cvt(w2[k], f);
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[e] = fmaf(cu, f[e], acc[e]);
+          for (int e = 0; e < EPL; ++e) acc[e] = fmaf(md[k][2], f[e], acc[e]);
         }
       }
     }
   }
   if (store) {
-    float* o = a.dx + t * d + col;
+    float* o = a.dx + t * a.d + col;
 #pragma unroll
     for (int e = 0; e < EPL; e += 4) *(f32x4_t*)(o + e) = f32x4_t{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
   }
@@ -463,14 +482,16 @@ __global__ __launch_bounds__(256) void backup_grad_kernel(BwdArgs a) {
 
 template <typename E, int NS, int SW>
 hipError_t launch_bwd_t(const BwdArgs& a, bool gated, int which, hipStream_t st) {
-  constexpr int RPW = SliceGeom<E, SW>::RPW;
   if (which == 0) {
     const dim3 rows((unsigned)((a.T + 3) / 4));
     if (gated) hipLaunchKernelGGL((dzu_kernel<NS, true>), rows, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((dzu_kernel<NS, false>), rows, dim3(256), 0, st, a);
-    const dim3 grid((unsigned)(NS * ((a.T + 4 * RPW - 1) / (4 * RPW))));
-    if (gated) hipLaunchKernelGGL((dx_sparse_kernel<E, NS, SW, true>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((dx_sparse_kernel<E, NS, SW, false>), grid, dim3(256), 0, st, a);
+    // 128-column slices (bf16: four rows per wave)
+    constexpr int XSW = 128;
+    constexpr int XRPW = 64 / (XSW * (int)sizeof(E) / 16);
+    const dim3 grid((unsigned)((a.d / XSW) * ((a.T + 4 * XRPW - 1) / (4 * XRPW))));
+    if (gated) hipLaunchKernelGGL((dx_sparse_kernel<E, XSW, true, 4>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((dx_sparse_kernel<E, XSW, false, 4>), grid, dim3(256), 0, st, a);
   } else {
     // 128-column slices (bf16: four neurons per wave)
     constexpr int DSW = 128;

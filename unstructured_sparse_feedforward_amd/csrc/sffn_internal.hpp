@@ -310,6 +310,7 @@ struct BwdArgs {
   const float* dpart;     // [NS, T, Kp] partial dy . W_d[j]
   float* gz;              // [T, K] dZ per ELL slot
   float* gu;              // [T, K] dU per ELL slot (gated)
+  f32x4_t* drec;          // [T, K] {neuron, dZ, dU} per ELL slot
   float* dx;              // [T, d]
   float* dwg;             // [F, d]
   float* dwu;             // [F, d] (gated)
