@@ -162,82 +162,85 @@ __device__ __forceinline__ float wave_sum32(float* v, int lane) {
   return v[0] + __shfl_xor(v[0], 1, 64);
 }
 
-// Phase 1: upart[s][t][k] = x_t[slice s] . W_u[j_k][slice s].
+// Sum over the 8 lanes of each lane octet, result in all 8 (quad swaps,
+// then the half-row mirror pairs lane i with 7 - i); a fixed order.
+__device__ __forceinline__ float octet_sum(float v) {
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xF, 0xF, true);  // row_half_mirror
+  return v;
+}
+
+// Phase 1: upart[s][t][k] = x_t[slice s] . W_u[j_k][slice s]. One row per
+// wave; the wave's 8 lane octets take 8 slots at once, an octet's lanes
+// split the SW-column slice (16-byte loads, 8 lanes cover 128 contiguous
+// bytes) and an octet sum gives the slot's partial. The row's neuron ids
+// are staged in LDS, 64 at a time, and read back as broadcasts; ids past
+// the count are 0 (the partial is not stored). Workgroup b runs on XCD
+// b mod 8, so with 8 slices an XCD gathers from one slice of W_u.
 template <typename E, int NS, int SW>
 __global__ __launch_bounds__(256) void up_partial_kernel(SliceArgs a) {
-  using G = SliceGeom<E, SW>;
-  constexpr int EPL = G::EPL, RPW = G::RPW;
-  using R = typename G::R;
+  constexpr int EPL = 16 / (int)sizeof(E);
+  constexpr int NLD = SW / 8 / EPL;      // 16-byte loads per lane per slot
+  constexpr int CH = 64;
+  constexpr int U = 1;                   // steps of 8 slots in flight
+  using R = u32x4_t;
+  __shared__ int rec[4][CH];
   const int lane = threadIdx.x & 63;
-  const int hf = RPW == 2 ? lane >> 5 : 0;
-  const int l = lane & (G::LPR - 1);
-  const int i = lane & 31;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 3;
+  const int l = lane & 7;
   const int s = blockIdx.x % NS;
-  const int64_t t = ((int64_t)(blockIdx.x / NS) * 4 + (threadIdx.x >> 6)) * RPW + hf;
-  if (t - hf >= a.T) return;
-  const bool ok = t < a.T;
-  const int64_t tr = ok ? t : a.T - 1;
-  const int d = NS * SW;
-  const int64_t col = (int64_t)s * SW + l * EPL;
-  // weight rows are addressed as a uniform base plus a 32-bit byte offset
-  // (F * d * sizeof(E) < 4 GiB), so a load needs one offset register
+  const int64_t t = (int64_t)(blockIdx.x / NS) * 4 + wave;
+  if (t >= a.T) return;
+  const int n = a.ell_cnt[t];
+  if (n == 0) return;
+  // this lane's columns of load i: s * SW + i * 8 * EPL + l * EPL
+  const int col0 = s * SW + l * EPL;
   const char* wu = (const char*)a.wu;
-  const uint32_t colb = (uint32_t)(col * sizeof(E));
-  const uint32_t rowb = (uint32_t)(d * sizeof(E));
-  const int64_t rb = tr * a.K;
-  // count, x slice and the first group's ids, all at once
-  const int n = ok ? a.ell_cnt[tr] : 0;
-  const R xv = *(const R*)((const E*)a.x + tr * d + col);
-  int jraw = a.ell_idx[rb + min(i, a.K - 1)];
-  int nmax = __builtin_amdgcn_readlane(n, 0);
-  if constexpr (RPW == 2) nmax = max(nmax, __builtin_amdgcn_readlane(n, 32));
-  if (nmax == 0) return;
-  float xr[EPL];
-  G::V::cvt(xv, xr);
-  float* up = a.upart + ((int64_t)s * a.T + tr) * a.Kp;
-  for (int k0 = 0; k0 < nmax; k0 += GRP) {
-    if (k0 > 0) jraw = a.ell_idx[rb + min(k0 + i, a.K - 1)];
-    const bool live = k0 + i < n;
-    const int jl = live ? jraw : 0;
-    // all 32 slots are loaded (slots past the count read neuron 0; their
-    // totals are never stored)
-    R w[GRP];
+  const uint32_t colb = (uint32_t)col0 * sizeof(E);
+  const uint32_t rowb = (uint32_t)a.d * sizeof(E);
+  R xv[NLD];
 #pragma unroll
-    for (int q = 0; q < GRP; ++q)
-      w[q] = *(const R*)(wu + ((uint32_t)slot_id<RPW>(jl, q, hf) * rowb + colb));
-    // keep every load of the group in flight before the first use
-    __builtin_amdgcn_sched_barrier(0);
-    float p[GRP];
+  for (int i = 0; i < NLD; ++i) xv[i] = *(const R*)((const E*)a.x + t * a.d + col0 + i * 8 * EPL);
+  float* up = a.upart + ((int64_t)s * a.T + t) * a.Kp;
+  for (int c0 = 0; c0 < n; c0 += CH) {
+    rec[wave][lane] = c0 + lane < n ? (int)a.ell_idx[t * a.K + c0 + lane] : 0;
+    // a wave's LDS accesses complete in issue order: no barrier is needed
+    // between its own writes and reads
+    const int m = min(CH, n - c0);
+    for (int k0 = 0; k0 < m; k0 += 8 * U) {
+      R w[U][NLD];
 #pragma unroll
-    for (int q = 0; q < GRP; ++q) {
-      if constexpr (sizeof(E) == 2) {
-        // bf16 pairs straight into v_dot2c_f32_bf16 (the products of two
-        // bf16 values are exact in fp32), fp32 accumulation
-        float acc = 0.0f;
+      for (int u = 0; u < U; ++u) {
+        const uint32_t off = (uint32_t)rec[wave][k0 + 8 * u + g] * rowb + colb;
 #pragma unroll
-        for (int e = 0; e < EPL / 2; ++e) {
-          const uint32_t xe = xv[e], we = w[q][e];
-          acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xe),
-                                                __builtin_bit_cast(bf16x2_t, we), acc, false);
-        }
-        p[q] = acc;
-      } else {
-        float f[EPL];
-        G::V::cvt(w[q], f);
-        float acc = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc = fmaf(xr[e], f[e], acc);
-        p[q] = acc;
+        for (int i = 0; i < NLD; ++i) w[u][i] = *(const R*)(wu + off + i * 8 * 16);
       }
-    }
-    if constexpr (RPW == 2) {
-      // totals over the 32 lanes of each row: lane i ends with slot k0 + i
-      butterfly<16, 16>(p, lane);
-      if (live) up[k0 + i] = p[0];
-    } else {
-      const float u = wave_sum32(p, lane);
-      const int q = lane >> 1;
-      if ((lane & 1) == 0 && k0 + q < n) up[k0 + q] = u;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          if constexpr (sizeof(E) == 2) {
+            // bf16 pairs straight into v_dot2c_f32_bf16 (the products of two
+            // bf16 values are exact in fp32), fp32 accumulation
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t xe = xv[i][e], we = w[u][i][e];
+              acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xe),
+                                                    __builtin_bit_cast(bf16x2_t, we), acc, false);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc = fmaf(__uint_as_float(xv[i][e]), __uint_as_float(w[u][i][e]), acc);
+          }
+        }
+        acc = octet_sum(acc);
+        const int k = c0 + k0 + 8 * u + g;
+        if (l == 0 && k0 + 8 * u + g < m) up[k] = acc;
+      }
     }
   }
 }
@@ -262,67 +265,89 @@ __global__ __launch_bounds__(256) void hsum_kernel(SliceArgs a) {
   }
 }
 
-// Phase 2: y_t[slice s] = sum_k h_k * W_d[j_k][slice s], h_k from the sum
-// above (non-gated: h_k = a_k). Rows routed to the dense backup are skipped.
-template <typename E, int NS, int SW, bool GATED>
+// Phase 2: y_t = sum_k h_k * W_d[j_k], h_k from the sum above (non-gated:
+// h_k = a_k); rows routed to the dense path are skipped. A lane loads 16
+// bytes of a W_d row, a row's SW-column slice takes LPR lanes, so a wave
+// sums RPW rows. Workgroup b runs on XCD b mod 8 and the blocks are ordered
+// slice phase first, so an XCD gathers from one slice of W_d at a time. The
+// wave stages its rows' slot records {neuron, h} in LDS, 64 per row at a
+// time, and reads them back as broadcasts; records past a row's count are
+// zero (neuron 0, no weight).
+template <typename E, int SW, bool GATED, int G>
 __global__ __launch_bounds__(256) void down_kernel(SliceArgs a) {
-  using G = SliceGeom<E, SW>;
-  constexpr int EPL = G::EPL, RPW = G::RPW;
-  using R = typename G::R;
+  constexpr int EPL = 16 / (int)sizeof(E);
+  constexpr int LPR = SW / EPL;
+  constexpr int RPW = 64 / LPR;
+  constexpr int CH = 64;
+  static_assert(RPW >= 1 && RPW <= 8 && CH % G == 0, "slice geometry");
+  using V = Vec<E, EPL>;
+  using R = typename V::raw;
+  __shared__ f32x2_t rec[4][RPW][CH];
   const int lane = threadIdx.x & 63;
-  const int hf = RPW == 2 ? lane >> 5 : 0;
-  const int l = lane & (G::LPR - 1);
-  const int i = lane & 31;
-  const int s = blockIdx.x % NS;
-  const int64_t t = ((int64_t)(blockIdx.x / NS) * 4 + (threadIdx.x >> 6)) * RPW + hf;
-  if (t - hf >= a.T) return;
-  const bool ok = t < a.T;
-  const int64_t tr = ok ? t : a.T - 1;
-  const int d = NS * SW;
-  const int64_t col = (int64_t)s * SW + l * EPL;
+  const int wave = threadIdx.x >> 6;
+  const int r = lane / LPR;
+  const int l = lane % LPR;
+  const int nsl = a.d / SW;
+  const int64_t nbk = (a.T + 4 * RPW - 1) / (4 * RPW);
+  int slice;
+  int64_t grp;
+  if (nsl % 8 == 0) {
+    const int64_t q = blockIdx.x / 8;
+    slice = (int)(q / nbk) * 8 + blockIdx.x % 8;
+    grp = q % nbk;
+  } else {
+    slice = blockIdx.x % nsl;
+    grp = blockIdx.x / nsl;
+  }
+  const int64_t tw = (grp * 4 + wave) * RPW;
+  if (tw >= a.T) return;
+  const int64_t t = tw + r;
+  const bool store = t < a.T && a.bk[t] == 0;
+  const int n = store ? a.ell_cnt[t] : 0;
+  int nmax = 0;
+#pragma unroll
+  for (int q = 0; q < RPW; ++q) nmax = max(nmax, __builtin_amdgcn_readlane(n, q * LPR));
+  const int col = slice * SW + l * EPL;
   const char* wd = (const char*)a.wd;
-  const uint32_t colb = (uint32_t)(col * sizeof(E));
-  const uint32_t rowb = (uint32_t)(d * sizeof(E));
-  const int64_t rb = tr * a.K;
-  const bool store = ok && a.bk[tr] == 0;
-  const int n = ok ? a.ell_cnt[tr] : 0;
-  int nmax = __builtin_amdgcn_readlane(n, 0);
-  if constexpr (RPW == 2) nmax = max(nmax, __builtin_amdgcn_readlane(n, 32));
+  const uint32_t colb = (uint32_t)col * sizeof(E);
+  const uint32_t rowb = (uint32_t)a.d * sizeof(E);
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-  for (int k0 = 0; k0 < nmax; k0 += GRP) {
-    const int k = min(k0 + i, a.K - 1);
-    const bool live = k0 + i < n;
-    int jl = a.ell_idx[rb + k];
-    float hl = GATED ? a.upart[tr * a.Kp + k] : a.ell_a[rb + k];
-    jl = live ? jl : 0;
-    hl = live ? hl : 0.0f;
-    // blocks of 8 slots that some row of the wave has (wave-uniform); the
-    // other slots of a block read neuron 0 with h = 0
-    const int nb = (min(GRP, nmax - k0) + 7) >> 3;
-    R w[GRP];
+  for (int k0 = 0; k0 < nmax; k0 += CH) {
 #pragma unroll
-    for (int b = 0; b < GRP / 8; ++b)
-      if (b < nb)
+    for (int q = 0; q < RPW; ++q) {
+      const int nq = __builtin_amdgcn_readlane(n, q * LPR);
+      f32x2_t v = {};
+      if (k0 + lane < nq) {
+        const int64_t tq = tw + q;
+        v[0] = __int_as_float((int)a.ell_idx[tq * a.K + k0 + lane]);
+        v[1] = GATED ? a.upart[tq * a.Kp + k0 + lane] : a.ell_a[tq * a.K + k0 + lane];
+      }
+      rec[wave][q][lane] = v;
+    }
+    // a wave's LDS accesses complete in issue order: no barrier is needed
+    // between its own writes and reads
+    const int m = min(CH, nmax - k0);
+    for (int g0 = 0; g0 < m; g0 += G) {
+      f32x2_t md[G];
+      R w[G];
 #pragma unroll
-        for (int q = 8 * b; q < 8 * b + 8; ++q)
-          w[q] = *(const R*)(wd + ((uint32_t)slot_id<RPW>(jl, q, hf) * rowb + colb));
-    __builtin_amdgcn_sched_barrier(0);
+      for (int k = 0; k < G; ++k) md[k] = rec[wave][r][g0 + k];
 #pragma unroll
-    for (int b = 0; b < GRP / 8; ++b)
-      if (b < nb)
+      for (int k = 0; k < G; ++k)
+        w[k] = *(const R*)(wd + ((uint32_t)__float_as_int(md[k][0]) * rowb + colb));
 #pragma unroll
-        for (int q = 8 * b; q < 8 * b + 8; ++q) {
-          const float h = slot_val<RPW>(hl, q, hf);
-          float f[EPL];
-          G::V::cvt(w[q], f);
+      for (int k = 0; k < G; ++k) {
+        float f[EPL];
+        V::cvt(w[k], f);
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) acc[e] = fmaf(h, f[e], acc[e]);
-        }
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(md[k][1], f[e], acc[e]);
+      }
+    }
   }
   if (store) {
-    float* yo = a.y + t * d + col;
+    float* yo = a.y + t * a.d + col;
 #pragma unroll
     for (int e = 0; e < EPL; e += 4) *(f32x4_t*)(yo + e) = f32x4_t{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
   }
@@ -333,13 +358,17 @@ hipError_t launch_slices(const SliceArgs& a, bool gated, int phase, hipStream_t 
   constexpr int RPW = SliceGeom<E, SW>::RPW;
   const dim3 grid((unsigned)(NS * ((a.T + 4 * RPW - 1) / (4 * RPW))));
   if (phase == 0) {
-    hipLaunchKernelGGL((up_partial_kernel<E, NS, SW>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((up_partial_kernel<E, NS, SW>), dim3((unsigned)(NS * ((a.T + 3) / 4))),
+                       dim3(256), 0, st, a);
   } else if (phase == 2) {
     hipLaunchKernelGGL((hsum_kernel<NS>), dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, st, a);
-  } else if (gated) {
-    hipLaunchKernelGGL((down_kernel<E, NS, SW, true>), grid, dim3(256), 0, st, a);
   } else {
-    hipLaunchKernelGGL((down_kernel<E, NS, SW, false>), grid, dim3(256), 0, st, a);
+    // 256-column slices (bf16: two rows per wave)
+    constexpr int DSW = 256;
+    constexpr int DRPW = 64 / (DSW * (int)sizeof(E) / 16);
+    const dim3 dgrid((unsigned)((a.d / DSW) * ((a.T + 4 * DRPW - 1) / (4 * DRPW))));
+    if (gated) hipLaunchKernelGGL((down_kernel<E, DSW, true, 4>), dgrid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((down_kernel<E, DSW, false, 4>), dgrid, dim3(256), 0, st, a);
   }
   return hipGetLastError();
 }
