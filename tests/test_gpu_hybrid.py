@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_close_bf16, dev, math_weights, rel_fro, twell_np
+from gpu_util import assert_close_bf16, assert_close_f32, dev, math_weights, rel_fro, twell_np
 from unstructured_sparse_feedforward_amd import SparseFFN
 from unstructured_sparse_feedforward_amd import binding as B
 from unstructured_sparse_feedforward_amd import workloads as wl
@@ -229,6 +229,34 @@ def test_backward_no_backup_rows(max_backup):
     assert_close_bf16(dwg.cpu().numpy(), ref["dw_gate"].T, "dw_gate")
     assert_close_bf16(dwu.cpu().numpy(), ref["dw_up"].T, "dw_up")
     assert_close_bf16(dwd.cpu().numpy(), ref["dw_down"], "dw_down")
+
+
+def test_training_f32():
+    """The fp32 training step (true fp32 GEMMs, no split operands) against
+    the oracle at the fp32 bound, on a layer where about half the rows take
+    the dense backup path (K = 20 of about 20 active, 5% outliers)."""
+    w = wl.SMALL_F32.replace(ell_cap=20, outlier_frac=0.05, train=True)
+    _print("training f32")
+    inp = wl.make_inputs(w, seed=6)
+    wg, wu, wd = math_weights(inp)
+    x64 = inp.x.astype(np.float64)
+    assert np.abs(x64 @ wg).min() > 1e-4
+    ffn = SparseFFN(w.d, w.F, gated=True, twell_cap=w.twell_cap, ell_cap=w.ell_cap,
+                    dtype=torch.float32)
+    args = [dev(inp, k) for k in ("x", "w_gate", "w_up", "w_down")]
+    y, hy = ffn.forward_train(*args)
+    assert ffn.hybrid_check(hy) == B.SFFN_OK
+    nb = int(hy["n_backup"][0].item())
+    _print("  backup rows:", nb)
+    assert 20 < nb < w.T - 20
+    dx, dwg, dwu, dwd = ffn.backward(*args, hy, dev(inp, "dy"), l1_coeff=0.01)
+    yr, _ = oracle.dense_ffn(x64, wg, wu, wd)
+    ref = _grads_ref(inp, 0.01)
+    assert_close_f32(y.cpu().numpy(), yr, "y")
+    assert_close_f32(dx.cpu().numpy(), ref["dx"], "dx")
+    assert_close_f32(dwg.cpu().numpy(), ref["dw_gate"].T, "dw_gate")
+    assert_close_f32(dwu.cpu().numpy(), ref["dw_up"].T, "dw_up")
+    assert_close_f32(dwd.cpu().numpy(), ref["dw_down"], "dw_down")
 
 
 def test_training_full_size_sampled():

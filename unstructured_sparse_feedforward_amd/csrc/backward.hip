@@ -384,96 +384,113 @@ __global__ __launch_bounds__(256) void gather_stack_kernel(const E* __restrict__
 // of the GEMMs that consume them. Row-major [R, 2F] (bf16 hi | lo) or
 // [R, F] (fp32) for dx; neuron-major rows of stride ldt holding hi in
 // columns [0, Rp) and lo in [Rp, 2Rp), zero past R (bf16), or [0, Rp)
-// (fp32), for dW. A workgroup takes 64 rows x 64 neurons at a time: it
-// reads and writes the row-major side along neurons, and goes through LDS
-// to write the neuron-major side along rows, so every access is coalesced.
+// (fp32), for dW. A workgroup takes 64 rows x 64 neurons at a time; a
+// thread takes two neighbouring neurons of a row on the row-major side and
+// two neighbouring rows of a neuron on the neuron-major side (through LDS),
+// so every access is coalesced and at least 4 bytes wide.
 template <typename E, bool GATED>
 __global__ __launch_bounds__(256) void backup_grad_kernel(BwdArgs a) {
   constexpr bool BF = sizeof(E) == 2;
-  // per element: hi | lo << 16 (bf16) or the fp32 bits
-  __shared__ uint32_t tz[64][65], tu[64][65], th[64][65];
+  // per element: hi | lo << 16 (bf16) or the fp32 bits; [neuron][row]
+  __shared__ uint32_t tz[64][66], tu[64][66], th[64][66];
   const int R = device_rows(a.n_backup, a.cap);
   const int Rp = (R + 63) / 64 * 64;
   const int F = a.F;
   const int tid = threadIdx.x;
-  const int c = tid & 63;   // neuron (load phase) or row (store phase) in the tile
-  const int g = tid >> 6;
+  const int c2 = (tid & 31) * 2;   // neuron pair (load side) or row pair (store side)
+  const int g = tid >> 5;
   const int ntj = F / 64;
   const int ntiles = (Rp / 64) * ntj;
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int r0 = (tile / ntj) * 64;
     const int j0 = (tile - (tile / ntj) * ntj) * 64;
-#pragma unroll 4
-    for (int p = 0; p < 16; ++p) {
-      const int rl = p * 4 + g;
+#pragma unroll 2
+    for (int p = 0; p < 8; ++p) {
+      const int rl = p * 8 + g;
       const int r = r0 + rl;
-      const int j = j0 + c;
-      float dz = 0.0f, du = 0.0f, h = 0.0f;
+      const int j = j0 + c2;
+      float dz[2] = {0.0f, 0.0f}, du[2] = {0.0f, 0.0f}, h[2] = {0.0f, 0.0f};
       if (r < R) {
         const int64_t q = (int64_t)r * F + j;
-        const float dh = a.dH[q];
-        const float av = a.bk_a[q];
-        const bool on = av > 0.0f;
-        if constexpr (GATED) {
-          const float uv = a.bk_u[q];
-          du = dh * av;
-          dz = on ? dh * uv + a.l1 : 0.0f;
-          h = av * uv;
-        } else {
-          dz = on ? dh + a.l1 : 0.0f;
-          h = av;
+        const f32x2_t dh = *(const f32x2_t*)(a.dH + q);
+        const f32x2_t av = *(const f32x2_t*)(a.bk_a + q);
+        f32x2_t uv = {0.0f, 0.0f};
+        if (GATED) uv = *(const f32x2_t*)(a.bk_u + q);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const bool on = av[e] > 0.0f;
+          if constexpr (GATED) {
+            du[e] = dh[e] * av[e];
+            dz[e] = on ? dh[e] * uv[e] + a.l1 : 0.0f;
+            h[e] = av[e] * uv[e];
+          } else {
+            dz[e] = on ? dh[e] + a.l1 : 0.0f;
+            h[e] = av[e];
+          }
         }
       }
       if constexpr (BF) {
-        const uint32_t zh = f32_to_bf16(dz), uh = f32_to_bf16(du), hh = f32_to_bf16(h);
-        const uint32_t zl = f32_to_bf16(dz - __uint_as_float(zh << 16));
-        const uint32_t ul = f32_to_bf16(du - __uint_as_float(uh << 16));
-        const uint32_t hl = f32_to_bf16(h - __uint_as_float(hh << 16));
+        uint32_t zh[2], zl[2], uh[2], ul[2], hh[2], hl[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          zh[e] = f32_to_bf16(dz[e]);
+          uh[e] = f32_to_bf16(du[e]);
+          hh[e] = f32_to_bf16(h[e]);
+          zl[e] = f32_to_bf16(dz[e] - __uint_as_float(zh[e] << 16));
+          ul[e] = f32_to_bf16(du[e] - __uint_as_float(uh[e] << 16));
+          hl[e] = f32_to_bf16(h[e] - __uint_as_float(hh[e] << 16));
+          tz[c2 + e][rl] = zh[e] | (zl[e] << 16);
+          tu[c2 + e][rl] = uh[e] | (ul[e] << 16);
+          th[c2 + e][rl] = hh[e] | (hl[e] << 16);
+        }
         if (r < R) {
-          uint16_t* gzr = (uint16_t*)a.gz_rm + (int64_t)r * 2 * F + j;
-          gzr[0] = (uint16_t)zh;
-          gzr[F] = (uint16_t)zl;
+          uint32_t* gzr = (uint32_t*)((uint16_t*)a.gz_rm + (int64_t)r * 2 * F + j);
+          gzr[0] = zh[0] | (zh[1] << 16);
+          gzr[F / 2] = zl[0] | (zl[1] << 16);
           if (GATED) {
-            uint16_t* gur = (uint16_t*)a.gu_rm + (int64_t)r * 2 * F + j;
-            gur[0] = (uint16_t)uh;
-            gur[F] = (uint16_t)ul;
+            uint32_t* gur = (uint32_t*)((uint16_t*)a.gu_rm + (int64_t)r * 2 * F + j);
+            gur[0] = uh[0] | (uh[1] << 16);
+            gur[F / 2] = ul[0] | (ul[1] << 16);
           }
         }
-        tz[rl][c] = zh | (zl << 16);
-        tu[rl][c] = uh | (ul << 16);
-        th[rl][c] = hh | (hl << 16);
       } else {
         if (r < R) {
-          ((float*)a.gz_rm)[(int64_t)r * F + j] = dz;
-          if (GATED) ((float*)a.gu_rm)[(int64_t)r * F + j] = du;
+          *(f32x2_t*)((float*)a.gz_rm + (int64_t)r * F + j) = f32x2_t{dz[0], dz[1]};
+          if (GATED) *(f32x2_t*)((float*)a.gu_rm + (int64_t)r * F + j) = f32x2_t{du[0], du[1]};
         }
-        tz[rl][c] = __float_as_uint(dz);
-        tu[rl][c] = __float_as_uint(du);
-        th[rl][c] = __float_as_uint(h);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          tz[c2 + e][rl] = __float_as_uint(dz[e]);
+          tu[c2 + e][rl] = __float_as_uint(du[e]);
+          th[c2 + e][rl] = __float_as_uint(h[e]);
+        }
       }
     }
     __syncthreads();
-#pragma unroll 4
-    for (int p = 0; p < 16; ++p) {
-      const int jl = p * 4 + g;
-      const int64_t tr = (int64_t)(j0 + jl) * a.ldt + r0 + c;
-      const uint32_t z = tz[c][jl], u = tu[c][jl], hv = th[c][jl];
+#pragma unroll 2
+    for (int p = 0; p < 8; ++p) {
+      const int jl = p * 8 + g;
+      const int64_t tr = (int64_t)(j0 + jl) * a.ldt + r0 + c2;
+      const uint32_t z0 = tz[jl][c2], z1 = tz[jl][c2 + 1];
+      const uint32_t u0 = tu[jl][c2], u1 = tu[jl][c2 + 1];
+      const uint32_t h0 = th[jl][c2], h1 = th[jl][c2 + 1];
       if constexpr (BF) {
-        uint16_t* gzt = (uint16_t*)a.gz_t + tr;
-        gzt[0] = (uint16_t)z;
-        gzt[Rp] = (uint16_t)(z >> 16);
+        uint32_t* gzt = (uint32_t*)((uint16_t*)a.gz_t + tr);
+        gzt[0] = (z0 & 0xFFFFu) | (z1 << 16);
+        gzt[Rp / 2] = (z0 >> 16) | (z1 & 0xFFFF0000u);
         if (GATED) {
-          uint16_t* gut = (uint16_t*)a.gu_t + tr;
-          gut[0] = (uint16_t)u;
-          gut[Rp] = (uint16_t)(u >> 16);
+          uint32_t* gut = (uint32_t*)((uint16_t*)a.gu_t + tr);
+          gut[0] = (u0 & 0xFFFFu) | (u1 << 16);
+          gut[Rp / 2] = (u0 >> 16) | (u1 & 0xFFFF0000u);
         }
-        uint16_t* ght = (uint16_t*)a.gh_t + tr;
-        ght[0] = (uint16_t)hv;
-        ght[Rp] = (uint16_t)(hv >> 16);
+        uint32_t* ght = (uint32_t*)((uint16_t*)a.gh_t + tr);
+        ght[0] = (h0 & 0xFFFFu) | (h1 << 16);
+        ght[Rp / 2] = (h0 >> 16) | (h1 & 0xFFFF0000u);
       } else {
-        ((float*)a.gz_t)[tr] = __uint_as_float(z);
-        if (GATED) ((float*)a.gu_t)[tr] = __uint_as_float(u);
-        ((float*)a.gh_t)[tr] = __uint_as_float(hv);
+        *(f32x2_t*)((float*)a.gz_t + tr) = f32x2_t{__uint_as_float(z0), __uint_as_float(z1)};
+        if (GATED)
+          *(f32x2_t*)((float*)a.gu_t + tr) = f32x2_t{__uint_as_float(u0), __uint_as_float(u1)};
+        *(f32x2_t*)((float*)a.gh_t + tr) = f32x2_t{__uint_as_float(h0), __uint_as_float(h1)};
       }
     }
     __syncthreads();
