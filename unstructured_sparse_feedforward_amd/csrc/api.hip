@@ -80,7 +80,7 @@ struct Layout {
   size_t ell_a = 0, ell_idx = 0, ell_cnt = 0, bk = 0, upart = 0;
   size_t hid = 0, part = 0, total = 0;
   // backward
-  size_t gz = 0, gu = 0, drec = 0, ncnt = 0, noff = 0, ent0 = 0, meta = 0, dH = 0, gz_rm = 0, gu_rm = 0;
+  size_t gz = 0, gu = 0, drec = 0, ncnt = 0, noff = 0, ent0 = 0, meta = 0, dH = 0, gz_rm = 0;
   size_t gz_t = 0, gu_t = 0, gh_t = 0, xb = 0, dyb = 0;
   int64_t ldt = 0;
 };
@@ -156,8 +156,8 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
     L.ent0 = take((size_t)T * K * 4);
     L.meta = take((size_t)T * K * 16);
     L.dH = take((size_t)T * F * 4);
-    L.gz_rm = take((size_t)T * F * 4);
-    L.gu_rm = take((size_t)T * F * 4);
+    // dZ and dU rows: bf16 [T, 4F] (dZ hi | lo, dU hi | lo), fp32 two [T, F]
+    L.gz_rm = take((size_t)T * F * 8);
     L.gz_t = take((size_t)F * L.ldt * esize(h));
     L.gu_t = take((size_t)F * L.ldt * esize(h));
     L.gh_t = take((size_t)F * L.ldt * esize(h));
@@ -855,7 +855,13 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
   ba.xb = at<char>(ws, L.xb);
   ba.dyb = at<char>(ws, L.dyb);
   ba.gz_rm = at<char>(ws, L.gz_rm);
-  ba.gu_rm = at<char>(ws, L.gu_rm);
+  if (dt == kBF16) {
+    ba.gu_rm = at<char>(ws, L.gz_rm) + (size_t)2 * D.d_ff * 2;
+    ba.ld_rm = (int64_t)4 * D.d_ff;
+  } else {
+    ba.gu_rm = at<char>(ws, L.gz_rm) + (size_t)T * D.d_ff * 4;
+    ba.ld_rm = D.d_ff;
+  }
   ba.gz_t = at<char>(ws, L.gz_t);
   ba.gu_t = at<char>(ws, L.gu_t);
   ba.gh_t = at<char>(ws, L.gh_t);
@@ -903,21 +909,26 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
     if (e == hipSuccess) e = launch_splitk_reduce(g, (float*)ba.dH, D.d_ff, stream);
     if (e == hipSuccess) e = launch_backup_grad(dt, gated, ba, stream);
     if (e != hipSuccess) return hip_fail(h, e, "backup dH");
-    // dx rows = dZ W_g (+ dU W_u), scattered into the backup rows
-    for (int pass = 0; pass < (gated ? 2 : 1); ++pass) {
+    // dx rows = dZ W_g (+ dU W_u), scattered into the backup rows: bf16 as
+    // one product over K = 4F (dZ hi | lo against W_g, then dU hi | lo
+    // against W_u), fp32 as two
+    for (int pass = 0; pass < (gated && !split ? 2 : 1); ++pass) {
       GemmArgs f = {};
       f.A = pass == 0 ? ba.gz_rm : ba.gu_rm;
+      f.lda = ba.ld_rm;
       f.m_dev = hy->n_backup;
       f.m_cap = cap;
       f.B0 = pass == 0 ? w_gate : w_up;
       f.ldb = D.d;
       f.N = D.d;
       if (split) {
-        f.lda = 2 * (int64_t)D.d_ff;
-        f.K = 2 * D.d_ff;
+        f.K = (gated ? 4 : 2) * D.d_ff;
         f.kwrap = D.d_ff;
+        if (gated) {
+          f.B1 = w_up;
+          f.kcat = 2 * D.d_ff;
+        }
       } else {
-        f.lda = D.d_ff;
         f.K = D.d_ff;
       }
       f.out = dx;

@@ -381,8 +381,8 @@ __global__ __launch_bounds__(256) void gather_stack_kernel(const E* __restrict__
 }
 
 // From dH of the backup rows: dZ, dU (and H = a u for dW_d) in the layouts
-// of the GEMMs that consume them. Row-major [R, 2F] (bf16 hi | lo) or
-// [R, F] (fp32) for dx; neuron-major rows of stride ldt holding hi in
+// of the GEMMs that consume them. Row-major rows of stride ld_rm, hi | lo
+// (bf16, 2F wide) or fp32 (F wide), for dx; neuron-major rows of stride ldt holding hi in
 // columns [0, Rp) and lo in [Rp, 2Rp), zero past R (bf16), or [0, Rp)
 // (fp32), for dW. A workgroup takes 64 rows x 64 neurons at a time; a
 // thread takes two neighbouring neurons of a row on the row-major side and
@@ -444,19 +444,19 @@ __global__ __launch_bounds__(256) void backup_grad_kernel(BwdArgs a) {
           th[c2 + e][rl] = hh[e] | (hl[e] << 16);
         }
         if (r < R) {
-          uint32_t* gzr = (uint32_t*)((uint16_t*)a.gz_rm + (int64_t)r * 2 * F + j);
+          uint32_t* gzr = (uint32_t*)((uint16_t*)a.gz_rm + r * a.ld_rm + j);
           gzr[0] = zh[0] | (zh[1] << 16);
           gzr[F / 2] = zl[0] | (zl[1] << 16);
           if (GATED) {
-            uint32_t* gur = (uint32_t*)((uint16_t*)a.gu_rm + (int64_t)r * 2 * F + j);
+            uint32_t* gur = (uint32_t*)((uint16_t*)a.gu_rm + r * a.ld_rm + j);
             gur[0] = uh[0] | (uh[1] << 16);
             gur[F / 2] = ul[0] | (ul[1] << 16);
           }
         }
       } else {
         if (r < R) {
-          *(f32x2_t*)((float*)a.gz_rm + (int64_t)r * F + j) = f32x2_t{dz[0], dz[1]};
-          if (GATED) *(f32x2_t*)((float*)a.gu_rm + (int64_t)r * F + j) = f32x2_t{du[0], du[1]};
+          *(f32x2_t*)((float*)a.gz_rm + r * a.ld_rm + j) = f32x2_t{dz[0], dz[1]};
+          if (GATED) *(f32x2_t*)((float*)a.gu_rm + r * a.ld_rm + j) = f32x2_t{du[0], du[1]};
         }
 #pragma unroll
         for (int e = 0; e < 2; ++e) {

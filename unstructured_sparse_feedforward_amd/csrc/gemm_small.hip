@@ -6,8 +6,10 @@
 // copied straight into LDS) or [K, N] (n contiguous, loaded into registers
 // and written into LDS transposed). With nsplit > 0 the N columns are two
 // operands side by side: columns [0, nsplit) from B0, the rest from B1 (the
-// gate and up projections of the same rows). The k index into B wraps at
-// kwrap (the bf16 hi and lo parts of an fp32 operand meet the same B).
+// gate and up projections of the same rows); with kcat > 0 they follow
+// each other along K (dZ W_g + dU W_u as one product). The k index into B
+// wraps at kwrap (the bf16 hi and lo parts of an fp32 operand meet the
+// same B).
 //
 // 128 x 128 tiles, 4 waves of 64 x 64 (2 x 2 v_mfma_f32_32x32x16_bf16).
 // K streams through a ring of NSLOT LDS slots of 32 k each, NSLOT - 1
@@ -125,6 +127,7 @@ __global__ __launch_bounds__(NT) void gemm_small_kernel(GemmArgs g) {
 
     auto kb_of = [&](int kt) {
       int64_t kb = (int64_t)(kt0 + kt) * BK;
+      if (g.kcat > 0 && kb >= g.kcat) kb -= g.kcat;
       if (g.kwrap > 0) kb %= g.kwrap;
       return kb;
     };
@@ -134,7 +137,9 @@ __global__ __launch_bounds__(NT) void gemm_small_kernel(GemmArgs g) {
       const int64_t ka = (int64_t)(kt0 + kt) * BK * 2;
       const int64_t kb = kb_of(kt);
       if constexpr (BT) {
-        const char* p = Bb + (kb + 2 * bkg) * ldb_b + (int64_t)(nb0 + 8 * bg) * 2;
+        const char* bs =
+            g.kcat > 0 && (int64_t)(kt0 + kt) * BK >= g.kcat ? (const char*)g.B1 : Bb;
+        const char* p = bs + (kb + 2 * bkg) * ldb_b + (int64_t)(nb0 + 8 * bg) * 2;
         rb[0] = *(const u32x4_t*)p;
         rb[1] = *(const u32x4_t*)(p + ldb_b);
       }
@@ -305,6 +310,7 @@ bool gemm_small_supported(const GemmArgs& g, bool bt, Epi epi) {
   if (epi != kEpiStoreF32 && epi != kEpiHiddenSplitK) return false;
   if (g.k_dev || g.N % BN != 0 || g.K % BK != 0 || g.K < BK) return false;
   if (g.kwrap > 0 && g.kwrap % BK != 0) return false;
+  if (g.kcat > 0 && (!bt || g.nsplit > 0 || g.kcat % BK != 0 || g.B1 == nullptr)) return false;
   if (g.nsplit > 0 && (g.nsplit % BN != 0 || bt)) return false;
   if (epi == kEpiHiddenSplitK && (g.part == nullptr || g.act != 1)) return false;
   return true;
@@ -314,6 +320,8 @@ bool gemm_small_supported(const GemmArgs& g, bool bt, Epi epi) {
 int gemm_small_grid(int num_cu) { return (2 * num_cu / NXCD) * NXCD; }
 
 hipError_t launch_gemm_small(bool bt, Epi epi, const GemmArgs& g, hipStream_t s) {
+  if (!gemm_small_supported(g, bt, epi) || g.grid < NXCD || g.grid % NXCD != 0)
+    return hipErrorInvalidValue;
   const dim3 grid(g.grid), block(NT);
   if (epi == kEpiHiddenSplitK) {
     hipLaunchKernelGGL((gemm_small_kernel<false, kEpiHiddenSplitK>), grid, block, 0, s, g);

@@ -164,14 +164,17 @@ struct GemmArgs {
   const int32_t* m_dev;
   int m_cap;                 // > 0: a device M is capped at m_cap
   // B: [N, K] (k contiguous) or, when b_trans, [K, N] (n contiguous).
-  // With two B operands (gate and up) both share A. The k index into B is
-  // taken modulo kwrap when kwrap > 0.
+  // With two B operands (gate and up) both share A. With kcat > 0 (small
+  // GEMM, n-contiguous B) the two operands follow each other along K
+  // instead: k < kcat reads B0, k >= kcat reads B1 at k - kcat. The k index
+  // into B is then taken modulo kwrap when kwrap > 0.
   const void* B0;
   const void* B1;
   int64_t ldb;
   int N;
   int K;
   int kwrap;
+  int kcat;
   // K from the device (when k_dev is set): K = k_mult * round_up(min(*k_dev,
   // k_cap), 64); operands must hold zeros in their padding
   const int32_t* k_dev;
@@ -329,8 +332,9 @@ struct BwdArgs {
   const float* dH;        // [cap, F]
   void* xb;               // stacked gathered x rows
   void* dyb;              // stacked gathered dy rows
-  void* gz_rm;            // dZ rows for dx (bf16 hi|lo [cap, 2F] or fp32 [cap, F])
-  void* gu_rm;
+  void* gz_rm;            // dZ rows for dx (bf16 hi|lo or fp32), row stride ld_rm
+  void* gu_rm;            // dU rows, the same layout
+  int64_t ld_rm;
   void* gz_t;             // neuron-major dZ for dW ([F, ldt])
   void* gu_t;
   void* gh_t;
