@@ -266,6 +266,21 @@ def test_no_active_neurons():
     assert torch.count_nonzero(y).item() == 0
 
 
+@pytest.mark.parametrize("d,F,T", [(512, 1024, 200), (1024, 2048, 150), (4096, 1024, 70)])
+def test_forward_bf16_model_dims(d, F, T):
+    """Every supported bf16 model width (the d slices: 2 x 256, 4 x 256,
+    8 x 512 for up; 256-column slices for down), with outlier rows."""
+    w = wl.GATED_1P5B.replace(d=d, F=F, nnz=F * 0.01, outlier_frac=0.05,
+                              name=f"gated_d{d}_F{F}")
+    _print(f"forward bf16 d={d} F={F} T={T}")
+    inp = wl.make_inputs(w, seed=24, T=T)
+    ffn = layer(inp)
+    tw = ffn.new_twell(T)
+    y = ffn.forward(*(dev(inp, k) for k in ("x", "w_gate", "w_up", "w_down")), tw=tw)
+    assert twell_np(tw)["n_flagged"] > 0
+    assert_close_bf16(y.cpu().numpy(), _oracle_y(inp), "y")
+
+
 # --------------------------------------------------------------- full size
 
 def test_full_size_sampled_rows():
@@ -290,3 +305,17 @@ def test_full_size_sampled_rows():
     # with probability ~3e-8 per tile
     assert set(np.flatnonzero(inp.outlier)) <= set(flagged.tolist())
     assert len(flagged) - inp.outlier.sum() <= 2
+
+
+def test_full_size_nongated_sampled_rows():
+    """The non-gated workload at its full size (T = 16384, d = 2048,
+    F = 8192, bf16, ~29 active per token, no outliers) in the launch
+    configuration the benchmark times; 256 sampled rows against the oracle."""
+    w = wl.NONGATED[29]
+    inp = wl.make_inputs(w, seed=0)
+    ffn = layer(inp)
+    y = ffn.forward(*(dev(inp, k) for k in ("x", "w_gate", "w_up", "w_down"))).cpu().numpy()
+    rows = np.sort(np.random.default_rng(1).choice(w.T, 256, replace=False))
+    wg, _, wd = math_weights(inp)
+    y_ref, _ = oracle.dense_ffn(inp.x[rows].astype(np.float64), wg, None, wd)
+    assert_close_bf16(y[rows], y_ref, "sampled rows")

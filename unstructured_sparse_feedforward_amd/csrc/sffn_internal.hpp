@@ -77,44 +77,6 @@ template <> struct Vec<float, 4> {
   }
 };
 
-// Each lane loads 16 bytes of a weight row slice per pair: a slice of
-// SW elements takes LPR = SW * sizeof(E) / 16 lanes, so a wave covers
-// RPW = 64 / LPR rows at once (two rows of a 256-wide bf16 slice, one row
-// otherwise). Wide loads halve the load instructions per byte, which is
-// what bounds these gathers. Pairs go 32 per row per group: lane i of a
-// row's lane group holds the metadata of slot k0 + i (lanes 32-63 repeat
-// lanes 0-31 when a row spans the whole wave). The metadata loads do not
-// wait for the row's count (the slot index is clamped to the row's K
-// slots), so a group costs one round trip for the metadata and one for the
-// weight rows. Slots past the count read neuron 0 and are discarded (ELL
-// padding is unspecified).
-template <typename E, int SW>
-struct SliceGeom {
-  static constexpr int EPL = 16 / (int)sizeof(E);
-  static constexpr int LPR = SW / EPL;
-  static constexpr int RPW = 64 / LPR;
-  static_assert(RPW == 1 || RPW == 2, "slice of 32 or 64 lanes");
-  using V = Vec<E, EPL>;
-  using R = typename V::raw;
-};
-
-// The neuron id of slot q of this lane's row, from the 32 ids held by the
-// row's lanes (wave-uniform index).
-template <int RPW>
-__device__ __forceinline__ int slot_id(int jl, int q, int hf) {
-  if constexpr (RPW == 2) {
-    const int j0 = __builtin_amdgcn_readlane(jl, q);
-    const int j1 = __builtin_amdgcn_readlane(jl, 32 + q);
-    return hf ? j1 : j0;
-  } else {
-    return __builtin_amdgcn_readlane(jl, q);
-  }
-}
-template <int RPW>
-__device__ __forceinline__ float slot_val(float v, int q, int hf) {
-  return __int_as_float(slot_id<RPW>(__float_as_int(v), q, hf));
-}
-
 // ---------------------------------------------------------------- TwELL row
 
 // Pack one (row, tile) of 128 pre-activations held as two per lane

@@ -135,33 +135,6 @@ __global__ __launch_bounds__(1024) void backup_list_kernel(const uint8_t* __rest
   if (tid == 0) *n_backup = carry;
 }
 
-constexpr int GRP = 32;  // active pairs in flight per wave
-
-// One butterfly exchange at lane distance W over the first 2*HALF values:
-// the lane keeps one half (the upper one if bit W of its lane id is set),
-// sends the other half to its partner and adds what it receives. Template
-// recursion keeps every register index a compile-time constant.
-template <int W, int HALF>
-__device__ __forceinline__ void butterfly(float* v, int lane) {
-  const bool up = (lane & W) != 0;
-#pragma unroll
-  for (int i = 0; i < HALF; ++i) {
-    const float send = up ? v[i] : v[i + HALF];
-    const float keep = up ? v[i + HALF] : v[i];
-    v[i] = keep + __shfl_xor(send, W, 64);
-  }
-  if constexpr (HALF > 1) butterfly<W / 2, HALF / 2>(v, lane);
-}
-
-// Wave totals of 32 per-lane values at once: five butterfly exchanges
-// (distances 32, 16, 8, 4, 2) and a last one between lane pairs. On return
-// lane l holds the total of value (l >> 1) & 31. The order of additions is
-// fixed.
-__device__ __forceinline__ float wave_sum32(float* v, int lane) {
-  butterfly<32, 16>(v, lane);
-  return v[0] + __shfl_xor(v[0], 1, 64);
-}
-
 // Sum over the 8 lanes of each lane octet, result in all 8 (quad swaps,
 // then the half-row mirror pairs lane i with 7 - i); a fixed order.
 __device__ __forceinline__ float octet_sum(float v) {
@@ -355,8 +328,6 @@ __global__ __launch_bounds__(256) void down_kernel(SliceArgs a) {
 
 template <typename E, int NS, int SW>
 hipError_t launch_slices(const SliceArgs& a, bool gated, int phase, hipStream_t st) {
-  constexpr int RPW = SliceGeom<E, SW>::RPW;
-  const dim3 grid((unsigned)(NS * ((a.T + 4 * RPW - 1) / (4 * RPW))));
   if (phase == 0) {
     hipLaunchKernelGGL((up_partial_kernel<E, NS, SW>), dim3((unsigned)(NS * ((a.T + 3) / 4))),
                        dim3(256), 0, st, a);
