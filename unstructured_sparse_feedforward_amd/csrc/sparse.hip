@@ -33,12 +33,18 @@ __device__ __forceinline__ int wave_sum_int(int v) {
 
 // One wave per token row: count its positives, decide the route, and if
 // the row stays sparse, concatenate its TwELL tile lists (ascending neuron)
-// into ELL slots 0..nnz-1. Lane b takes tile b (64 tiles per pass): an
-// exclusive prefix of the stored counts gives each tile's first ELL slot,
-// and the lane copies its tile's entries, so only live slots are read.
+// into ELL slots 0..nnz-1. Lane b takes tile b (64 tiles per pass) and an
+// exclusive prefix of the counts gives each tile's first ELL slot (kept in
+// LDS); then the wave copies the row's slots 64 at a time, lane o taking
+// ELL slot o from the tile whose range holds it (binary search of the tile
+// starts), so loads and stores are contiguous runs.
+constexpr int kMaxTiles = 512;   // F <= 65408 with 128-column tiles
+
 __global__ __launch_bounds__(256) void rows_kernel(EllArgs a) {
+  __shared__ int tstart[4][kMaxTiles + 1];
   const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
   if (t >= a.T) return;
   const int32_t* cnt = a.cnt + t * a.n_t;
   int nnz = 0;
@@ -60,7 +66,7 @@ __global__ __launch_bounds__(256) void rows_kernel(EllArgs a) {
   }
   if (backup || nnz == 0) return;
   // not flagged: every tile count is <= C, so all entries are stored
-  const int64_t dst = t * (int64_t)a.K;
+  int* ts = tstart[wave];
   int base = 0;
   for (int b0 = 0; b0 < a.n_t; b0 += 64) {
     const int b = b0 + lane;
@@ -71,13 +77,28 @@ __global__ __launch_bounds__(256) void rows_kernel(EllArgs a) {
       const int v = __shfl_up(inc, o, 64);
       if (lane >= o) inc += v;
     }
-    const int64_t src = (t * a.n_t + b) * (int64_t)a.C;
-    const int64_t pos = dst + base + inc - c;
-    for (int s = 0; s < c; ++s) {
-      a.ell_idx[pos + s] = a.idx[src + s];
-      a.ell_a[pos + s] = a.val[src + s];
-    }
+    if (b < a.n_t) ts[b] = base + inc - c;
     base += __shfl(inc, 63, 64);
+  }
+  // a wave's LDS accesses complete in issue order: no barrier is needed
+  // between its own writes and reads
+  const int64_t dst = t * (int64_t)a.K;
+  const int64_t src0 = t * a.n_t * (int64_t)a.C;
+  for (int o0 = 0; o0 < nnz; o0 += 64) {
+    const int o = o0 + lane;
+    if (o < nnz) {
+      // the last tile whose start is <= o (empty tiles share a start with
+      // the next tile and are skipped by taking the last)
+      int lo = 0, hi = a.n_t - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ts[mid] <= o) lo = mid;
+        else hi = mid - 1;
+      }
+      const int64_t src = src0 + (int64_t)lo * a.C + (o - ts[lo]);
+      a.ell_idx[dst + o] = a.idx[src];
+      a.ell_a[dst + o] = a.val[src];
+    }
   }
 }
 
