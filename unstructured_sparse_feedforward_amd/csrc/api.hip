@@ -534,17 +534,17 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
       if (e == hipSuccess) e = launch_hidden_combine_side(nb, f, stream);
     }
     if (e != hipSuccess) return hip_fail(h, e, "dense-path gate/up GEMM");
-    // [H_hi | H_lo] x [W_d ; W_d]: K = 2F with the B index wrapped at F
+    // H_hi W_d + H_lo W_d: a dual A over the F rows of W_d
     GemmArgs f2 = {};
     f2.A = hid;
     f2.lda = 2 * (int64_t)D.d_ff;
+    f2.alo = D.d_ff;
     f2.m_dev = n_bk;
     f2.m_cap = mcap;
     f2.B0 = w_down;
     f2.ldb = D.d;
     f2.N = D.d;
-    f2.K = 2 * D.d_ff;
-    f2.kwrap = D.d_ff;
+    f2.K = D.d_ff;
     f2.out = y;
     f2.ldo = D.d;
     f2.out_rows = brow;
@@ -910,8 +910,8 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
     if (e == hipSuccess) e = launch_backup_grad(dt, gated, ba, stream);
     if (e != hipSuccess) return hip_fail(h, e, "backup dH");
     // dx rows = dZ W_g (+ dU W_u), scattered into the backup rows: bf16 as
-    // one product over K = 4F (dZ hi | lo against W_g, then dU hi | lo
-    // against W_u), fp32 as two
+    // one product (dZ hi and lo against W_g, then dU hi and lo against W_u),
+    // fp32 as two
     for (int pass = 0; pass < (gated && !split ? 2 : 1); ++pass) {
       GemmArgs f = {};
       f.A = pass == 0 ? ba.gz_rm : ba.gu_rm;
@@ -922,11 +922,12 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
       f.ldb = D.d;
       f.N = D.d;
       if (split) {
-        f.K = (gated ? 4 : 2) * D.d_ff;
-        f.kwrap = D.d_ff;
+        // dual A (hi | lo parts F apart) over the F rows of W_g, then of W_u
+        f.K = (gated ? 2 : 1) * D.d_ff;
+        f.alo = D.d_ff;
         if (gated) {
           f.B1 = w_up;
-          f.kcat = 2 * D.d_ff;
+          f.kcat = D.d_ff;
         }
       } else {
         f.K = D.d_ff;

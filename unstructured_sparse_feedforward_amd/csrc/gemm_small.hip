@@ -9,7 +9,8 @@
 // gate and up projections of the same rows); with kcat > 0 they follow
 // each other along K (dZ W_g + dU W_u as one product). The k index into B
 // wraps at kwrap (the bf16 hi and lo parts of an fp32 operand meet the
-// same B).
+// same B), or, with alo > 0, A holds the lo part alo columns after the hi
+// part and every B stage is read once for both (twice the MFMAs).
 //
 // 128 x 128 tiles, 4 waves of 64 x 64 (2 x 2 v_mfma_f32_32x32x16_bf16).
 // K streams through a ring of NSLOT LDS slots of 32 k each, NSLOT - 1
@@ -32,9 +33,16 @@ constexpr int NT = 256;
 constexpr int NXCD = 8;
 constexpr int BK = 32;       // k per slot (64 bytes per LDS row)
 constexpr int ROWB = 64;
-constexpr int SLOT = (BM + BN) * ROWB;   // 16 KB
-constexpr int NSLOT = 4;
-constexpr int LPS = 4;       // copies (or B register loads) per wave and stage
+
+// Ring geometry: a slot holds an A tile and a B tile (16 KB), or with a
+// dual A (hi and lo parts) two A tiles and a B tile (24 KB); four slots,
+// or three with a dual A, so that two workgroups fit a CU's LDS. LPS is
+// the copies (or B register loads) per wave and stage.
+template <bool DUAL> struct Ring {
+  static constexpr int SLOT = ((DUAL ? 2 : 1) * BM + BN) * ROWB;
+  static constexpr int NSLOT = DUAL ? 3 : 4;
+  static constexpr int LPS = DUAL ? 6 : 4;
+};
 
 constexpr int wait_imm(int vm, int lgkm) {
   return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
@@ -58,8 +66,11 @@ __device__ __forceinline__ int small_splits(const GemmArgs& g, int mt, int ntl) 
   return s < 1 ? 1 : s;
 }
 
-template <bool BT, int EPI>
+template <bool BT, int EPI, bool DUAL>
 __global__ __launch_bounds__(NT) void gemm_small_kernel(GemmArgs g) {
+  constexpr int SLOT = Ring<DUAL>::SLOT;
+  constexpr int NSLOT = Ring<DUAL>::NSLOT;
+  constexpr int LPS = Ring<DUAL>::LPS;
   __shared__ __align__(16) char smem[NSLOT * SLOT];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -134,7 +145,11 @@ __global__ __launch_bounds__(NT) void gemm_small_kernel(GemmArgs g) {
     // stage kt (relative to the split) into slot `slot` (B registers into set `set`)
     auto issue = [&](int kt, int slot, u32x4_t (&rb)[2]) {
       char* base = smem + slot * SLOT;
-      const int64_t ka = (int64_t)(kt0 + kt) * BK * 2;
+      // A column of the stage: with a dual A the hi part of the second
+      // operand (k >= kcat) starts alo after the first's
+      int64_t kac = (int64_t)(kt0 + kt) * BK;
+      if (DUAL && g.kcat > 0 && kac >= g.kcat) kac += g.alo;
+      const int64_t ka = kac * 2;
       const int64_t kb = kb_of(kt);
       if constexpr (BT) {
         const char* bs =
@@ -147,6 +162,13 @@ __global__ __launch_bounds__(NT) void gemm_small_kernel(GemmArgs g) {
       for (int i = 0; i < 2; ++i)
         __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + ka),
                                          (void*)(base + (wave * 32 + i * 16) * ROWB), 16, 0, 0);
+      if constexpr (DUAL) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + ka + g.alo * 2),
+                                           (void*)(base + (BM + BN + wave * 32 + i * 16) * ROWB),
+                                           16, 0, 0);
+      }
       if constexpr (!BT) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -176,7 +198,7 @@ __global__ __launch_bounds__(NT) void gemm_small_kernel(GemmArgs g) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-    u32x4_t af[2][2], bf[2][2];
+    u32x4_t af[2][2], bf[2][2], al[2][DUAL ? 2 : 1];
     auto read_frags = [&](int slot, int s, int buf) {
       const char* sa = smem + slot * SLOT;
       const int ch = 2 * s + (lane >> 5);
@@ -186,6 +208,12 @@ __global__ __launch_bounds__(NT) void gemm_small_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         bf[buf][j] = *(const u32x4_t*)(sa + BM * ROWB + rlds_off(wc * 64 + j * 32 + (lane & 31), ch));
+      if constexpr (DUAL) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          al[buf][i] = *(const u32x4_t*)(sa + (BM + BN) * ROWB +
+                                         rlds_off(wr * 64 + i * 32 + (lane & 31), ch));
+      }
     };
     auto mfmas = [&](int buf) {
 #pragma unroll
@@ -195,13 +223,24 @@ __global__ __launch_bounds__(NT) void gemm_small_kernel(GemmArgs g) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               __builtin_bit_cast(bf16x8_t, af[buf][i]), __builtin_bit_cast(bf16x8_t, bf[buf][j]),
               acc[i][j], 0, 0, 0);
+      if constexpr (DUAL) {
+        // the lo part meets the same B fragments
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, al[buf][i]), __builtin_bit_cast(bf16x8_t, bf[buf][j]),
+                acc[i][j], 0, 0, 0);
+      }
     };
     auto spread = [&]() {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < (DUAL ? 6 : 4); ++k) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
       }
+      if constexpr (DUAL) __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     };
 
     // Pipeline: stage kt lives in slot kt % NSLOT; every slot is filled up
@@ -311,12 +350,13 @@ bool gemm_small_supported(const GemmArgs& g, bool bt, Epi epi) {
   if (g.k_dev || g.N % BN != 0 || g.K % BK != 0 || g.K < BK) return false;
   if (g.kwrap > 0 && g.kwrap % BK != 0) return false;
   if (g.kcat > 0 && (!bt || g.nsplit > 0 || g.kcat % BK != 0 || g.B1 == nullptr)) return false;
+  if (g.alo > 0 && (!bt || epi != kEpiStoreF32 || g.kwrap > 0 || g.nsplit > 0)) return false;
   if (g.nsplit > 0 && (g.nsplit % BN != 0 || bt)) return false;
   if (epi == kEpiHiddenSplitK && (g.part == nullptr || g.act != 1)) return false;
   return true;
 }
 
-// two workgroups per CU (64 KB of LDS each)
+// two workgroups per CU (64 or 72 KB of LDS each)
 int gemm_small_grid(int num_cu) { return (2 * num_cu / NXCD) * NXCD; }
 
 hipError_t launch_gemm_small(bool bt, Epi epi, const GemmArgs& g, hipStream_t s) {
@@ -324,11 +364,13 @@ hipError_t launch_gemm_small(bool bt, Epi epi, const GemmArgs& g, hipStream_t s)
     return hipErrorInvalidValue;
   const dim3 grid(g.grid), block(NT);
   if (epi == kEpiHiddenSplitK) {
-    hipLaunchKernelGGL((gemm_small_kernel<false, kEpiHiddenSplitK>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((gemm_small_kernel<false, kEpiHiddenSplitK, false>), grid, block, 0, s, g);
+  } else if (bt && g.alo > 0) {
+    hipLaunchKernelGGL((gemm_small_kernel<true, kEpiStoreF32, true>), grid, block, 0, s, g);
   } else if (bt) {
-    hipLaunchKernelGGL((gemm_small_kernel<true, kEpiStoreF32>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((gemm_small_kernel<true, kEpiStoreF32, false>), grid, block, 0, s, g);
   } else {
-    hipLaunchKernelGGL((gemm_small_kernel<false, kEpiStoreF32>), grid, block, 0, s, g);
+    hipLaunchKernelGGL((gemm_small_kernel<false, kEpiStoreF32, false>), grid, block, 0, s, g);
   }
   return hipGetLastError();
 }

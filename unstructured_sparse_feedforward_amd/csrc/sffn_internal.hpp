@@ -137,6 +137,10 @@ struct GemmArgs {
   int K;
   int kwrap;
   int kcat;
+  // dual A (small GEMM, n-contiguous B): A's lo part sits alo columns after
+  // its hi part (for k >= kcat the hi part itself starts alo later) and
+  // C = A_hi B + A_lo B over the K columns of B
+  int64_t alo;
   // K from the device (when k_dev is set): K = k_mult * round_up(min(*k_dev,
   // k_cap), 64); operands must hold zeros in their padding
   const int32_t* k_dev;
