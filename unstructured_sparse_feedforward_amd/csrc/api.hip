@@ -524,7 +524,9 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
       f.ldo_au = D.d_ff;
     }
     f.part = part;
-    f.split_target = small_split_target(h);
+    // about one tile per CU: with only a few rows a deeper split costs
+    // more in partials than it gains in parallel loads
+    f.split_target = h->num_cu;
     f.split_max = std::min(kSplitMax, D.d / 32);
     f.num_cu = h->num_cu;
     f.grid = gemm_small_grid(h->num_cu);
