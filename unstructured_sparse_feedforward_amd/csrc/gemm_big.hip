@@ -150,47 +150,67 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16_t (&acc)[NB][
   const int h = lane >> 5;     // which of the register's two rows
   const int c32 = lane & 31;   // column inside the 32-column block
   if constexpr (EPI == kEpiTwell) {
-    // wave columns [n0 + wc*128, +128) are TwELL tile tb
+    // wave columns [n0 + wc*128, +128) are TwELL tile tb. Register q of
+    // block (i, j) holds row r0(q) in lanes 0-31 and row r0(q) + 4 in
+    // lanes 32-63, column j*32 + lane%32: four ballots give a row pair's
+    // 128 columns. A row pair without a positive costs the ballots and one
+    // scalar test. The wave index is uniform (read through readfirstlane),
+    // so the ballots, counts and tests stay in scalar registers.
     const int tb = (n0 >> 7) + wc;
     if (tb * kTile >= g.N) return;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int C = g.C;
+    const uint32_t row_entries = (uint32_t)g.n_t * (uint32_t)C;
+    const uint32_t half_off = (uint32_t)h * 4u * row_entries;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rbase = m0 + wr * 128 + i * 32;
+      if (rbase >= M) break;
+      const bool full = rbase + 32 <= M;
+      // this block's first entry of tile tb; the block spans 32 rows, so
+      // every entry offset from it fits 32 bits
+      const int64_t e0 = ((int64_t)rbase * g.n_t + tb) * C;
+      char* vbase = (char*)(g.tw_val + e0);
+      char* ibase = (char*)(g.tw_idx + e0);
       int cnt_lane = 0;  // lane r < 32 collects the count of row rbase + r
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int r0 = (q >> 2) * 8 + (q & 3);   // block row of the lane half h = 0
-        const int row = rbase + r0 + h * 4;
-        const bool rok = row < M;
+        const int r0 = (q >> 2) * 8 + (q & 3);
+        // lanes whose row exists (all of them but in the last row block)
+        const uint64_t okm = full ? ~0ull : __ballot(rbase + r0 + h * 4 < M);
         float av[4];
         uint64_t bal[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           av[j] = agpr(acc[0][i][j][q]);
-          bal[j] = __ballot(rok && av[j] > 0.0f);
+          bal[j] = __ballot(av[j] > 0.0f) & okm;
         }
-        // positives of the two rows before block j, and in total
-        int pre0[4], pre1[4];
-        int n0c = 0, n1c = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          pre0[j] = n0c;
-          pre1[j] = n1c;
-          n0c += __popc((uint32_t)bal[j]);
-          n1c += __popc((uint32_t)(bal[j] >> 32));
-        }
-        cnt_lane = lane == r0 ? n0c : (lane == r0 + 4 ? n1c : cnt_lane);
-        if (rok) {
-          const int64_t slot = ((int64_t)row * g.n_t + tb) * g.C;
+        if ((bal[0] | bal[1] | bal[2] | bal[3]) != 0) {
+          // per block j: positives of the two rows before it, less (for
+          // the second row) the first row's positives in block j, which the
+          // lane's 64-bit prefix count includes
+          int base0[4], base1[4];
+          int n0c = 0, n1c = 0;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            if (av[j] > 0.0f) {
-              const int rank = (h ? pre1[j] - __popc((uint32_t)bal[j]) : pre0[j]) +
-                               __popcll(bal[j] & below);
-              if (rank < g.C) {
-                g.tw_val[slot + rank] = av[j];
-                g.tw_idx[slot + rank] = (uint16_t)(tb * kTile + j * 32 + c32);
+            const int c0 = __popc((uint32_t)bal[j]);
+            base0[j] = n0c;
+            base1[j] = n1c - c0;
+            n0c += c0;
+            n1c += __popc((uint32_t)(bal[j] >> 32));
+          }
+          cnt_lane = lane == r0 ? n0c : (lane == r0 + 4 ? n1c : cnt_lane);
+          const uint32_t ro = (uint32_t)r0 * row_entries + half_off;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (bal[j] == 0) continue;
+            if ((bal[j] >> lane) & 1) {
+              const int rank = (h ? base1[j] : base0[j]) +
+                               (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[j] >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
+              if (rank < C) {
+                const uint32_t e = ro + (uint32_t)rank;
+                *(float*)(vbase + e * 4u) = av[j];
+                *(uint16_t*)(ibase + e * 2u) = (uint16_t)(tb * kTile + j * 32 + c32);
               }
             }
           }
@@ -283,7 +303,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
   const int wr = wave >> 1;
   const int wc = wave & 1;
   const int M = g.M;
