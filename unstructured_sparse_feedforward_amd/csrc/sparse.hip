@@ -12,13 +12,14 @@
 // projection): for every active (neuron j, value a) of a row, u = x . W_u[j],
 // h = a * u, y += h * W_d[j]. MI355X has 8 XCDs with a private 4 MB L2
 // each and a workgroup with id b runs on XCD b % 8. The model dimension is
-// cut into NS slices (8 at d = 2048) and slice s is processed only by
-// workgroups with b % NS == s, so each XCD's L2 holds one slice of W_up and
-// W_down (5632 x 256 bf16 = 2.9 MB each at the 1.5B shape) instead of
-// streaming whole 8 KB neuron rows from HBM/MALL. Phase 1 writes per-slice
-// partial dot products (one float per active pair and slice); phase 2 sums
-// them in slice order (deterministic), scales by the activation and adds
-// the neuron's down weights into the row's y slice. No dense hidden tensor
+// cut into 256-column slices (up: 512 at d = 4096, where 8 slices cover
+// it) and each grid is ordered so that an XCD works
+// on one slice at a time, so its L2 holds one slice of W_up or W_down
+// (5632 x 256 bf16 = 2.9 MB at the 1.5B shape) instead of streaming whole
+// 4 KB neuron rows from HBM/MALL. Phase 1 writes per-slice partial dot
+// products (one float per active pair and slice); a small kernel sums them
+// in slice order (deterministic) and scales by the activation; phase 2 adds
+// the neurons' down weights into the rows' y slices. No dense hidden tensor
 // is formed.
 #include "sffn_internal.hpp"
 
