@@ -23,13 +23,16 @@
 //
 // Every epilogue works on the accumulator registers directly. In the
 // 32 x 32 MFMA layout register q of a block holds, for lanes 0-31 and
-// 32-63, 32 consecutive columns of two different rows; a wave's 128
-// columns are exactly one 128-column TwELL tile, so the four blocks of a
+// 32-63, 32 consecutive columns of two different rows; when a wave's 128
+// columns are exactly one 128-column TwELL tile, the four blocks of a
 // register index give two complete tile rows: four ballots, scalar
 // popcounts and a lane prefix count place every positive entry in its
 // ascending slot (the TwELL of "Sparser, Faster, Lighter Transformer
 // Language Models", gist.science explainer, 2. Methodology A, written in
-// the gate GEMM's epilogue as in 2. Methodology B).
+// the gate GEMM's epilogue as in 2. Methodology B). That epilogue is
+// scalar and vector work with the matrix cores idle, so the gate GEMM
+// runs as gemm_twell2_kernel: 256 x 128 tiles (one TwELL tile wide), two
+// workgroups per CU, one workgroup's epilogue beside the other's MFMAs.
 #include "sffn_internal.hpp"
 
 namespace sffn {
@@ -142,6 +145,86 @@ __device__ __forceinline__ void mfma_substep(f32x16_t (&acc)[NB][4][Cfg<NB>::JB]
 
 // ---------------------------------------------------------------- epilogues
 
+// ReLU + TwELL of a wave's NI x 32 rows of one 128-column TwELL tile tb
+// (the wave's accumulator blocks acc[i][j], rows rbase0 + 32 i).
+template <int NI>
+__device__ __forceinline__ void twell_epilogue(const GemmArgs& g, f32x16_t (&acc)[NI][4],
+                                               int rbase0, int tb, int lane) {
+  const int M = g.M;
+  const int h = lane >> 5;     // which of the register's two rows
+  const int c32 = lane & 31;   // column inside the 32-column block
+  // Register q of block (i, j) holds row r0(q) in lanes 0-31 and row
+  // r0(q) + 4 in lanes 32-63, column j*32 + lane%32: four ballots give a
+  // row pair's 128 columns. A row pair without a positive costs the
+  // ballots and one scalar test. Callers derive rbase0 and tb from a
+  // uniform (readfirstlane) wave index, so that the ballots, counts and
+  // tests stay in scalar registers.
+  if (tb * kTile >= g.N) return;
+  const int C = g.C;
+  const uint32_t row_entries = (uint32_t)g.n_t * (uint32_t)C;
+  const uint32_t half_off = (uint32_t)h * 4u * row_entries;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int rbase = rbase0 + i * 32;
+    if (rbase >= M) break;
+    const bool full = rbase + 32 <= M;
+    // this block's first entry of tile tb; the block spans 32 rows, so
+    // every entry offset from it fits 32 bits
+    const int64_t e0 = ((int64_t)rbase * g.n_t + tb) * C;
+    char* vbase = (char*)(g.tw_val + e0);
+    char* ibase = (char*)(g.tw_idx + e0);
+    int cnt_lane = 0;  // lane r < 32 collects the count of row rbase + r
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int r0 = (q >> 2) * 8 + (q & 3);
+      // lanes whose row exists (all of them but in the last row block)
+      const uint64_t okm = full ? ~0ull : __ballot(rbase + r0 + h * 4 < M);
+      float av[4];
+      uint64_t bal[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        av[j] = agpr(acc[i][j][q]);
+        bal[j] = __ballot(av[j] > 0.0f) & okm;
+      }
+      if ((bal[0] | bal[1] | bal[2] | bal[3]) != 0) {
+        // per block j: positives of the two rows before it, less (for
+        // the second row) the first row's positives in block j, which the
+        // lane's 64-bit prefix count includes
+        int base0[4], base1[4];
+        int n0c = 0, n1c = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c0 = __popc((uint32_t)bal[j]);
+          base0[j] = n0c;
+          base1[j] = n1c - c0;
+          n0c += c0;
+          n1c += __popc((uint32_t)(bal[j] >> 32));
+        }
+        cnt_lane = lane == r0 ? n0c : (lane == r0 + 4 ? n1c : cnt_lane);
+        const uint32_t ro = (uint32_t)r0 * row_entries + half_off;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (bal[j] == 0) continue;
+          if ((bal[j] >> lane) & 1) {
+            const int rank = (h ? base1[j] : base0[j]) +
+                             (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[j] >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
+            if (rank < C) {
+              const uint32_t e = ro + (uint32_t)rank;
+              *(float*)(vbase + e * 4u) = av[j];
+              *(uint16_t*)(ibase + e * 2u) = (uint16_t)(tb * kTile + j * 32 + c32);
+            }
+          }
+        }
+      }
+      // one register index at a time: keeps the accumulator reads of
+      // later groups from being hoisted
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (lane < 32 && rbase + lane < M) g.tw_cnt[(int64_t)(rbase + lane) * g.n_t + tb] = cnt_lane;
+  }
+}
+
 template <int NB, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16_t (&acc)[NB][4][Cfg<NB>::JB],
                                          int m0, int n0, int wr, int wc, int lane) {
@@ -149,79 +232,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16_t (&acc)[NB][
   const int M = g.M;
   const int h = lane >> 5;     // which of the register's two rows
   const int c32 = lane & 31;   // column inside the 32-column block
-  if constexpr (EPI == kEpiTwell) {
-    // wave columns [n0 + wc*128, +128) are TwELL tile tb. Register q of
-    // block (i, j) holds row r0(q) in lanes 0-31 and row r0(q) + 4 in
-    // lanes 32-63, column j*32 + lane%32: four ballots give a row pair's
-    // 128 columns. A row pair without a positive costs the ballots and one
-    // scalar test. The wave index is uniform (read through readfirstlane),
-    // so the ballots, counts and tests stay in scalar registers.
-    const int tb = (n0 >> 7) + wc;
-    if (tb * kTile >= g.N) return;
-    const int C = g.C;
-    const uint32_t row_entries = (uint32_t)g.n_t * (uint32_t)C;
-    const uint32_t half_off = (uint32_t)h * 4u * row_entries;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rbase = m0 + wr * 128 + i * 32;
-      if (rbase >= M) break;
-      const bool full = rbase + 32 <= M;
-      // this block's first entry of tile tb; the block spans 32 rows, so
-      // every entry offset from it fits 32 bits
-      const int64_t e0 = ((int64_t)rbase * g.n_t + tb) * C;
-      char* vbase = (char*)(g.tw_val + e0);
-      char* ibase = (char*)(g.tw_idx + e0);
-      int cnt_lane = 0;  // lane r < 32 collects the count of row rbase + r
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int r0 = (q >> 2) * 8 + (q & 3);
-        // lanes whose row exists (all of them but in the last row block)
-        const uint64_t okm = full ? ~0ull : __ballot(rbase + r0 + h * 4 < M);
-        float av[4];
-        uint64_t bal[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          av[j] = agpr(acc[0][i][j][q]);
-          bal[j] = __ballot(av[j] > 0.0f) & okm;
-        }
-        if ((bal[0] | bal[1] | bal[2] | bal[3]) != 0) {
-          // per block j: positives of the two rows before it, less (for
-          // the second row) the first row's positives in block j, which the
-          // lane's 64-bit prefix count includes
-          int base0[4], base1[4];
-          int n0c = 0, n1c = 0;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int c0 = __popc((uint32_t)bal[j]);
-            base0[j] = n0c;
-            base1[j] = n1c - c0;
-            n0c += c0;
-            n1c += __popc((uint32_t)(bal[j] >> 32));
-          }
-          cnt_lane = lane == r0 ? n0c : (lane == r0 + 4 ? n1c : cnt_lane);
-          const uint32_t ro = (uint32_t)r0 * row_entries + half_off;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (bal[j] == 0) continue;
-            if ((bal[j] >> lane) & 1) {
-              const int rank = (h ? base1[j] : base0[j]) +
-                               (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[j] >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
-              if (rank < C) {
-                const uint32_t e = ro + (uint32_t)rank;
-                *(float*)(vbase + e * 4u) = av[j];
-                *(uint16_t*)(ibase + e * 2u) = (uint16_t)(tb * kTile + j * 32 + c32);
-              }
-            }
-          }
-        }
-        // one register index at a time: keeps the accumulator reads of
-        // later groups from being hoisted
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (lane < 32 && rbase + lane < M) g.tw_cnt[(int64_t)(rbase + lane) * g.n_t + tb] = cnt_lane;
-    }
-  } else if (EPI == kEpiStoreF32 && NB == 1 && g.accumulate) {
+  static_assert(EPI != kEpiTwell, "the TwELL gate GEMM is gemm_twell2_kernel");
+  if (EPI == kEpiStoreF32 && NB == 1 && g.accumulate) {
     // out += acc: a block row's 16 x JB old values are loaded together,
     // then added and stored
 #pragma unroll
@@ -434,6 +446,149 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------- two per CU
+
+// The gate GEMM + TwELL with two workgroups per CU, so that one
+// workgroup's TwELL epilogue (scalar and vector work that leaves the
+// matrix cores idle) runs beside the other's main loop. A block tile is
+// 256 rows x one 128-column TwELL tile; wave w multiplies rows 64 w .. +64
+// against all 128 columns (2 x 4 MFMA blocks, 128 accumulator registers),
+// so every wave owns whole TwELL tile rows. Three 24 KB ring slots per
+// workgroup (k-contiguous A and B copied straight into LDS), six copies
+// per wave and stage, the same waits and barriers as the ring kernel.
+constexpr int P2_BN = 128;
+constexpr int P2_NSLOT = 3;
+constexpr int P2_SLOT = (BM + P2_BN) * RROWB;   // 24 KB
+constexpr int P2_LPS = 6;                        // 4 A + 2 B copies per wave
+
+__device__ __forceinline__ void p2_reads() {
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+}
+__device__ __forceinline__ void p2_reads_copies() {
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one global-to-LDS copy
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+}
+
+__global__ __launch_bounds__(NT, 2) void gemm_twell2_kernel(GemmArgs g) {
+  static_assert((P2_NSLOT - 1) * P2_LPS <= 63, "vmcnt range");
+  __shared__ __align__(16) char smem[P2_NSLOT * P2_SLOT];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int M = g.M;
+  const int nkt = g.K / RBK;
+  const TileSched ts(M, g.N, P2_BN);
+  const char* Ab = (const char*)g.A;
+  const char* Bb = (const char*)g.B0;
+  const int64_t lda_b = g.lda * 2;
+  const int64_t ldb_b = g.ldb * 2;
+  // direct-to-LDS copy lane layout as in the ring kernel
+  const int lr = lane >> 2;
+  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
+
+  for (int L = ts.t_begin + ts.local; L < ts.t_end; L += ts.G8) {
+    int m0, n0;
+    ts.coords(L, P2_BN, m0, n0);
+    const char* a_src[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = min(m0 + wave * 64 + i * 16 + lr, M - 1);
+      a_src[i] = Ab + (int64_t)m * lda_b + lchunk * 16;
+    }
+    const char* b_src[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int n = min(n0 + wave * 32 + i * 16 + lr, g.N - 1);
+      b_src[i] = Bb + (int64_t)n * ldb_b + lchunk * 16;
+    }
+    auto issue_stage = [&](int kt, int slot) {
+      char* base = smem + slot * P2_SLOT;
+      const int64_t kb = (int64_t)kt * RBK * 2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + kb),
+                                         (void*)(base + (wave * 64 + i * 16) * RROWB), 16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + kb),
+                                         (void*)(base + (BM + wave * 32 + i * 16) * RROWB), 16,
+                                         0, 0);
+    };
+
+    f32x16_t acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+    u32x4_t af[2][2];
+    u32x4_t bfr[2][4];
+    auto read_frags = [&](int slot, int s, int buf) {
+      const char* sa = smem + slot * P2_SLOT;
+      const int ch = 2 * s + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        af[buf][i] = *(const u32x4_t*)(sa + rlds_off(wave * 64 + i * 32 + (lane & 31), ch));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bfr[buf][j] = *(const u32x4_t*)(sa + BM * RROWB + rlds_off(j * 32 + (lane & 31), ch));
+    };
+    auto mfmas = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, af[buf][i]), __builtin_bit_cast(bf16x8_t, bfr[buf][j]),
+              acc[i][j], 0, 0, 0);
+    };
+
+    // the ring kernel's pipeline with three slots (see there)
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    wg_barrier();   // the previous tile's readers are done with LDS
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int p = 0; p < P2_NSLOT; ++p) issue_stage(min(p, nkt - 1), p);
+    __builtin_amdgcn_s_waitcnt(wait_imm((P2_NSLOT - 1) * P2_LPS, 15));  // stage 0 landed
+    wg_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(0, 0, 0);
+
+    int slot = 0;
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int next = slot + 1 == P2_NSLOT ? 0 : slot + 1;
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // fragments of substep 0
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(slot, 1, 1);
+      mfmas(0);
+      p2_reads();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(wait_imm((P2_NSLOT - 2) * P2_LPS, 0));
+      wg_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(next, 0, 0);
+      issue_stage(min(kt + P2_NSLOT, nkt - 1), slot);
+      mfmas(1);
+      p2_reads_copies();
+      __builtin_amdgcn_sched_barrier(0);
+      slot = next;
+    }
+    twell_epilogue<2>(g, acc, m0 + wave * 64, n0 >> 7, lane);
+  }
+}
+
 // ---------------------------------------------------------------- n-contiguous B
 
 constexpr int BK = 64;        // bf16 elements of K per stage (128 bytes per row)
@@ -636,7 +791,11 @@ hipError_t launch_gemm_big(int nb, bool bt, Epi epi, const GemmArgs& g, hipStrea
     hipLaunchKernelGGL((gemm_bt_kernel<kEpiStoreF32>), dim3(g.grid), dim3(NT), 0, s, g);
     return hipGetLastError();
   }
-  if (epi == kEpiTwell) return launch_ring<1, kEpiTwell>(g, s);
+  if (epi == kEpiTwell) {
+    // two workgroups per CU
+    hipLaunchKernelGGL(gemm_twell2_kernel, dim3(2 * (g.num_cu / NXCD) * NXCD), dim3(NT), 0, s, g);
+    return hipGetLastError();
+  }
   if (epi == kEpiStoreF32) return launch_ring<1, kEpiStoreF32>(g, s);
   if (epi == kEpiHiddenBF16) return nb == 2 ? launch_ring<2, kEpiHiddenBF16>(g, s)
                                             : launch_ring<1, kEpiHiddenBF16>(g, s);
