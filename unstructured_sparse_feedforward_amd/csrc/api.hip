@@ -78,7 +78,7 @@ constexpr int kSplitMax = kSplitCap;
 struct Layout {
   size_t ovf = 0, tw_val = 0, tw_idx = 0, tw_cnt = 0, tw_flag = 0, tw_list = 0, tw_nf = 0;
   size_t ell_a = 0, ell_idx = 0, ell_cnt = 0, bk = 0, upart = 0;
-  size_t hid = 0, part = 0, total = 0;
+  size_t hid = 0, zovf = 0, part = 0, total = 0;
   // backward
   size_t gz = 0, gu = 0, drec = 0, ncnt = 0, noff = 0, ent0 = 0, meta = 0, dH = 0, gz_rm = 0;
   size_t gz_t = 0, gu_t = 0, gh_t = 0, xb = 0, dyb = 0;
@@ -120,6 +120,8 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
     L.tw_nf = take(4);
     // hidden rows of flagged tokens: bf16 hi|lo [T, 2F] or fp32 [T, F]
     L.hid = take((size_t)T * F * 4);
+    // bf16: the gate pre-activations of overflowing tile rows [T, F]
+    if (h->desc.dtype == SFFN_BF16) L.zovf = take((size_t)T * F * 4);
     // split-K partials of the flagged rows' GEMMs (used one after the
     // other): a split problem has at most split_target / n_tiles row tiles
     // of 128 rows; the hidden GEMM keeps one partial set per B operand
@@ -434,9 +436,10 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   g.tw_cnt = t.cnt;
   g.C = D.twell_cap;
   g.n_t = h->n_t;
+  g.zovf = dt == kBF16 ? at<float>(ws, L.zovf) : nullptr;
   g.num_cu = h->num_cu;
   g.grid = gemm_grid(dt, 1, h->num_cu);
-  hipError_t e;
+  hipError_t e = hipSuccess;
   {
     ProfScope ps(h, SFFN_K_GATE_TWELL, stream);
     e = launch_gemm(dt, 1, false, kEpiTwell, g, stream);
@@ -499,8 +502,10 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     forked = true;
   }
   if ((!train || mcap > 0) && dt == kBF16) {
-    // gate | up of the rows side by side (N = 2F), partials always, then
-    // the combine: H as bf16 hi | lo (and ReLU(z), u rows in training)
+    // ReLU(z) of the rows comes from the gate GEMM itself (their TwELL
+    // tiles, and the saved pre-activations of the tiles that overflowed);
+    // gated layers add u = x W_u (split-K partials) and the combine forms
+    // H = ReLU(z) u as bf16 hi | lo (and ReLU(z), u rows in training)
     const int nb = D.gated ? 2 : 1;
     GemmArgs f = {};
     f.A = x;
@@ -508,11 +513,9 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     f.a_rows = brow;
     f.m_dev = n_bk;
     f.m_cap = mcap;
-    f.B0 = w_gate;
-    f.B1 = w_up;
+    f.B0 = w_up;
     f.ldb = D.d;
-    f.N = nb * D.d_ff;
-    f.nsplit = D.gated ? D.d_ff : 0;
+    f.N = D.d_ff;
     f.K = D.d;
     f.out = hid;
     f.act = 1;
@@ -523,6 +526,12 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
       f.out_u = D.gated ? hy->bk_u : nullptr;
       f.ldo_au = D.d_ff;
     }
+    f.tw_val = t.val;
+    f.tw_idx = t.idx;
+    f.tw_cnt = t.cnt;
+    f.C = D.twell_cap;
+    f.n_t = h->n_t;
+    f.zovf = at<float>(ws, L.zovf);
     f.part = part;
     // about one tile per CU: with only a few rows a deeper split costs
     // more in partials than it gains in parallel loads
@@ -532,10 +541,10 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     f.grid = gemm_small_grid(h->num_cu);
     {
       ProfScope ps(h, SFFN_K_FLAG_GATEUP, stream);
-      e = launch_gemm_small(false, kEpiHiddenSplitK, f, stream);
-      if (e == hipSuccess) e = launch_hidden_combine_side(nb, f, stream);
+      if (D.gated) e = launch_gemm_small(false, kEpiHiddenSplitK, f, stream);
+      if (e == hipSuccess) e = launch_flag_hidden(nb, f, stream);
     }
-    if (e != hipSuccess) return hip_fail(h, e, "dense-path gate/up GEMM");
+    if (e != hipSuccess) return hip_fail(h, e, "dense-path hidden rows");
     // H_hi W_d + H_lo W_d: a dual A over the F rows of W_d
     GemmArgs f2 = {};
     f2.A = hid;

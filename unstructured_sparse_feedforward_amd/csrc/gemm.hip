@@ -383,24 +383,20 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
   }
 }
 
-// Sum the split-K partials of the hidden GEMM and apply its epilogue:
-// H = ReLU(z) * u (two B operands) or ReLU(z), stored as bf16 hi and lo
-// parts (bf16 layers) or float32. A no-op when the GEMM did not split.
-// SIDE: the partials come from gemm_small_kernel, which always leaves them
-// (even unsplit) with the z and u columns side by side in one [Mpad, N] row
-// per split (N = 2F with nsplit = F; N = F for one operand). Otherwise they
-// come from gemm_kernel: z splits then u splits, [Mpad, F] each, and an
-// unsplit GEMM has already written H itself.
-template <typename E, int NB, bool SIDE>
+// Sum the split-K partials of the hidden GEMM (gemm_kernel: z splits then
+// u splits, [Mpad, F] each) and apply its epilogue: H = ReLU(z) * u (two B
+// operands) or ReLU(z), stored as bf16 hi and lo parts (bf16 layers) or
+// float32. A no-op when the GEMM did not split (it has written H itself).
+template <typename E, int NB>
 __global__ __launch_bounds__(256) void hidden_combine_kernel(GemmArgs g) {
   const int M = device_rows(g.m_dev, g.m_cap);
   if (M <= 0) return;
   const int mt = (M + BM - 1) / BM;
   const int ntl = g.N / BN;
   const int S = num_splits(g, mt, ntl);
-  if (!SIDE && S <= 1) return;
+  if (S <= 1) return;
   const int Mpad = mt * BM;
-  const int Fh = (SIDE && g.nsplit > 0) ? g.nsplit : g.N;   // hidden width
+  const int Fh = g.N;   // hidden width
   const int n4 = Fh / 4;
   const int64_t total = (int64_t)M * n4;
   const int64_t pstride = (int64_t)Mpad * g.N;  // one split's partials
@@ -409,7 +405,7 @@ __global__ __launch_bounds__(256) void hidden_combine_kernel(GemmArgs g) {
     const int m = (int)(e / n4);
     const int c = (int)(e - (int64_t)m * n4) * 4;
     const float* pz = g.part + (int64_t)m * g.N + c;
-    const float* pu = SIDE ? pz + Fh : pz + (int64_t)S * pstride;
+    const float* pu = pz + (int64_t)S * pstride;
     // every split's partials are loaded before the first add (in split
     // order, so the sums are deterministic)
     f32x4_t vz[kSplitCap], vu[kSplitCap];
@@ -531,22 +527,94 @@ hipError_t launch_gemm(Dtype dt, int nb, bool bt, Epi epi, const GemmArgs& g, hi
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_hidden_combine(Dtype dt, int nb, const GemmArgs& g, hipStream_t s) {
-  const dim3 grid(g.grid), block(256);
-  if (dt == kBF16) {
-    if (nb == 2) hipLaunchKernelGGL((hidden_combine_kernel<uint16_t, 2, false>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((hidden_combine_kernel<uint16_t, 1, false>), grid, block, 0, s, g);
-  } else {
-    if (nb == 2) hipLaunchKernelGGL((hidden_combine_kernel<float, 2, false>), grid, block, 0, s, g);
-    else hipLaunchKernelGGL((hidden_combine_kernel<float, 1, false>), grid, block, 0, s, g);
+namespace {
+
+// One workgroup per (dense-path row, two TwELL tiles): each half takes one
+// tile's 128 columns. a = ReLU(z) is the tile's saved pre-activations when
+// its count exceeds C, else zeros with the tile's TwELL entries scattered in
+// (through LDS); u is the sum of the split-K partials in split order.
+template <int NB>
+__global__ __launch_bounds__(256) void flag_hidden_kernel(GemmArgs g) {
+  __shared__ float at[2][kTile];
+  const int M = device_rows(g.m_dev, g.m_cap);
+  if (M <= 0) return;
+  const int F = g.N;
+  const int mt = (M + BM - 1) / BM;
+  const int S = NB == 2 ? num_splits(g, mt, F / BN) : 0;
+  const int64_t pstride = (int64_t)mt * BM * F;
+  const int npairs = (g.n_t + 1) / 2;
+  const int half = threadIdx.x >> 7;
+  const int c = threadIdx.x & 127;
+  const int64_t units = (int64_t)M * npairs;
+  for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const int m = (int)(unit / npairs);
+    const int b = (int)(unit - (int64_t)m * npairs) * 2 + half;
+    const bool tile_ok = b < g.n_t;
+    const int col = b * kTile + c;
+    // the partials depend on the dense-path row only: in flight first
+    float pv[kSplitCap];
+    if (NB == 2 && tile_ok) {
+      const float* pu = g.part + (int64_t)m * F + col;
+#pragma unroll
+      for (int k = 0; k < kSplitCap; ++k)
+        if (k < S) pv[k] = pu[k * pstride];
+    }
+    const int64_t t = g.a_rows[m];
+    const int cnt = tile_ok ? g.tw_cnt[t * g.n_t + b] : 0;
+    float a = 0.0f;
+    if (tile_ok && cnt > g.C) {
+      const float z = g.zovf[t * F + col];
+      a = z > 0.0f ? z : 0.0f;
+    }
+    at[half][c] = a;
+    __syncthreads();
+    if (tile_ok && cnt <= g.C && c < cnt) {
+      const int64_t e = (t * g.n_t + b) * g.C + c;
+      at[half][g.tw_idx[e] - b * kTile] = g.tw_val[e];
+    }
+    __syncthreads();
+    if (tile_ok) {
+      a = at[half][c];
+      float u = 0.0f;
+      if (NB == 2) {
+#pragma unroll
+        for (int k = 0; k < kSplitCap; ++k)
+          if (k < S) u += pv[k];
+      }
+      const float h = NB == 2 ? a * u : a;
+      if (g.out_a) {
+        g.out_a[(int64_t)m * g.ldo_au + col] = a;
+        if (NB == 2 && g.out_u) g.out_u[(int64_t)m * g.ldo_au + col] = u;
+      }
+      const uint32_t hi = f32_to_bf16(h);
+      const uint32_t lo = f32_to_bf16(h - __uint_as_float(hi << 16));
+      uint16_t* dst = (uint16_t*)g.out + (int64_t)m * g.ldo + col;
+      dst[0] = (uint16_t)hi;
+      dst[g.lo_off] = (uint16_t)lo;
+    }
+    __syncthreads();   // at[] is rewritten by the next unit
   }
+}
+
+}  // namespace
+
+hipError_t launch_flag_hidden(int nb, const GemmArgs& g, hipStream_t s) {
+  // several units per CU in flight: each is a short chain of dependent loads
+  const dim3 grid((unsigned)(8 * g.num_cu)), block(256);
+  if (nb == 2) hipLaunchKernelGGL(flag_hidden_kernel<2>, grid, block, 0, s, g);
+  else hipLaunchKernelGGL(flag_hidden_kernel<1>, grid, block, 0, s, g);
   return hipGetLastError();
 }
 
-hipError_t launch_hidden_combine_side(int nb, const GemmArgs& g, hipStream_t s) {
+hipError_t launch_hidden_combine(Dtype dt, int nb, const GemmArgs& g, hipStream_t s) {
   const dim3 grid(g.grid), block(256);
-  if (nb == 2) hipLaunchKernelGGL((hidden_combine_kernel<uint16_t, 2, true>), grid, block, 0, s, g);
-  else hipLaunchKernelGGL((hidden_combine_kernel<uint16_t, 1, true>), grid, block, 0, s, g);
+  if (dt == kBF16) {
+    if (nb == 2) hipLaunchKernelGGL((hidden_combine_kernel<uint16_t, 2>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((hidden_combine_kernel<uint16_t, 1>), grid, block, 0, s, g);
+  } else {
+    if (nb == 2) hipLaunchKernelGGL((hidden_combine_kernel<float, 2>), grid, block, 0, s, g);
+    else hipLaunchKernelGGL((hidden_combine_kernel<float, 1>), grid, block, 0, s, g);
+  }
   return hipGetLastError();
 }
 

@@ -201,6 +201,13 @@ __device__ __forceinline__ void twell_epilogue(const GemmArgs& g, f32x16_t (&acc
           n1c += __popc((uint32_t)(bal[j] >> 32));
         }
         cnt_lane = lane == r0 ? n0c : (lane == r0 + 4 ? n1c : cnt_lane);
+        // a tile row that overflows C keeps all its pre-activations, so that
+        // the dense path of its row needs no gate recomputation
+        if (g.zovf != nullptr && (n0c > C || n1c > C) && (h ? n1c > C : n0c > C)) {
+          float* zr = g.zovf + (int64_t)(rbase + r0 + h * 4) * g.N + tb * kTile + c32;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) zr[j * 32] = av[j];
+        }
         const uint32_t ro = (uint32_t)r0 * row_entries + half_off;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {

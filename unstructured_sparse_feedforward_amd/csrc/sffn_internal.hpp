@@ -167,6 +167,8 @@ struct GemmArgs {
   uint16_t* tw_idx;
   int32_t* tw_cnt;
   uint32_t* ovf;             // [n_t][ovf_words] overflow bits, bit r of word w = row 32w+r
+  float* zovf;               // bf16 gate: [M, N] fp32 pre-activations of the tile rows
+                             // whose count exceeds C (other entries are not written)
   int C;
   int n_t;
   int ovf_words;
@@ -185,11 +187,10 @@ bool gemm_big_supported(Dtype dt, int nb, bool bt, Epi epi, const GemmArgs& g);
 // bf16 GEMM of the dense path's few, device-counted rows (gemm_small.hip):
 // kEpiStoreF32 (split-K partials for launch_splitk_reduce when split, else
 // stored with out_rows / accumulate) or kEpiHiddenSplitK (always partials,
-// finished by launch_hidden_combine_side).
+// finished by launch_flag_hidden).
 bool gemm_small_supported(const GemmArgs& g, bool bt, Epi epi);
 int gemm_small_grid(int num_cu);
 hipError_t launch_gemm_small(bool bt, Epi epi, const GemmArgs& g, hipStream_t s);
-hipError_t launch_hidden_combine_side(int nb, const GemmArgs& g, hipStream_t s);
 int gemm_big_grid(const GemmArgs& g, int nb);
 hipError_t launch_gemm_big(int nb, bool bt, Epi epi, const GemmArgs& g, hipStream_t s);
 int gemm_grid(Dtype dt, int nb, int num_cu);
@@ -199,6 +200,13 @@ hipError_t launch_splitk_reduce(const GemmArgs& g, float* y, int64_t ldy, hipStr
 // split-K combine of the hidden GEMM (kEpiHiddenSplitK): sums the partials
 // and writes H; a no-op when the GEMM did not split.
 hipError_t launch_hidden_combine(Dtype dt, int nb, const GemmArgs& g, hipStream_t s);
+// Hidden rows of the dense path from the gate GEMM's own outputs (bf16):
+// for row m (physical row a_rows[m]) a = ReLU(z) from its TwELL tiles
+// (tw_*, C, n_t; tiles with a count above C from zovf), u from the split-K
+// partials of x W_u (gated, as gemm_small's kEpiHiddenSplitK leaves them),
+// H = a u (or a) stored as bf16 hi | lo into out; a and u rows into
+// out_a / out_u when set.
+hipError_t launch_flag_hidden(int nb, const GemmArgs& g, hipStream_t s);
 
 hipError_t launch_pack(const float* z, int64_t T, int F, int C, float* val, uint16_t* idx,
                        int32_t* cnt, uint32_t* ovf, int ovf_words, hipStream_t s);
