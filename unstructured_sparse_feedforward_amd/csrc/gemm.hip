@@ -529,70 +529,69 @@ hipError_t launch_gemm(Dtype dt, int nb, bool bt, Epi epi, const GemmArgs& g, hi
 
 namespace {
 
-// One workgroup per (dense-path row, two TwELL tiles): each half takes one
-// tile's 128 columns. a = ReLU(z) is the tile's saved pre-activations when
-// its count exceeds C, else zeros with the tile's TwELL entries scattered in
-// (through LDS); u is the sum of the split-K partials in split order.
+// One thread per 4 columns of a dense-path row. a = ReLU(z) is the tile's
+// saved pre-activations when its count exceeds C, else the tile's TwELL
+// entries that fall on the 4 columns (at most C ascending ids, read by all
+// the tile's threads); u is the sum of the split-K partials in split order.
 template <int NB>
 __global__ __launch_bounds__(256) void flag_hidden_kernel(GemmArgs g) {
-  __shared__ float at[2][kTile];
   const int M = device_rows(g.m_dev, g.m_cap);
   if (M <= 0) return;
   const int F = g.N;
   const int mt = (M + BM - 1) / BM;
   const int S = NB == 2 ? num_splits(g, mt, F / BN) : 0;
   const int64_t pstride = (int64_t)mt * BM * F;
-  const int npairs = (g.n_t + 1) / 2;
-  const int half = threadIdx.x >> 7;
-  const int c = threadIdx.x & 127;
-  const int64_t units = (int64_t)M * npairs;
-  for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
-    const int m = (int)(unit / npairs);
-    const int b = (int)(unit - (int64_t)m * npairs) * 2 + half;
-    const bool tile_ok = b < g.n_t;
-    const int col = b * kTile + c;
+  const int f4 = F / 4;
+  const int64_t total = (int64_t)M * f4;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int m = (int)(e / f4);
+    const int c = (int)(e - (int64_t)m * f4) * 4;
     // the partials depend on the dense-path row only: in flight first
-    float pv[kSplitCap];
-    if (NB == 2 && tile_ok) {
-      const float* pu = g.part + (int64_t)m * F + col;
+    f32x4_t pv[kSplitCap];
+    if (NB == 2) {
+      const float* pu = g.part + (int64_t)m * F + c;
 #pragma unroll
       for (int k = 0; k < kSplitCap; ++k)
-        if (k < S) pv[k] = pu[k * pstride];
+        if (k < S) pv[k] = *(const f32x4_t*)(pu + k * pstride);
     }
     const int64_t t = g.a_rows[m];
-    const int cnt = tile_ok ? g.tw_cnt[t * g.n_t + b] : 0;
-    float a = 0.0f;
-    if (tile_ok && cnt > g.C) {
-      const float z = g.zovf[t * F + col];
-      a = z > 0.0f ? z : 0.0f;
-    }
-    at[half][c] = a;
-    __syncthreads();
-    if (tile_ok && cnt <= g.C && c < cnt) {
-      const int64_t e = (t * g.n_t + b) * g.C + c;
-      at[half][g.tw_idx[e] - b * kTile] = g.tw_val[e];
-    }
-    __syncthreads();
-    if (tile_ok) {
-      a = at[half][c];
-      float u = 0.0f;
-      if (NB == 2) {
+    const int b = c / kTile;
+    const int cnt = g.tw_cnt[t * g.n_t + b];
+    f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (cnt > g.C) {
+      a = *(const f32x4_t*)(g.zovf + t * F + c);
 #pragma unroll
-        for (int k = 0; k < kSplitCap; ++k)
-          if (k < S) u += pv[k];
+      for (int q = 0; q < 4; ++q) a[q] = a[q] > 0.0f ? a[q] : 0.0f;
+    } else {
+      const int64_t e0 = (t * g.n_t + b) * g.C;
+      for (int k = 0; k < cnt; ++k) {
+        const int d = (int)g.tw_idx[e0 + k] - c;
+        if (d >= 0 && d < 4) a[d] = g.tw_val[e0 + k];
       }
-      const float h = NB == 2 ? a * u : a;
-      if (g.out_a) {
-        g.out_a[(int64_t)m * g.ldo_au + col] = a;
-        if (NB == 2 && g.out_u) g.out_u[(int64_t)m * g.ldo_au + col] = u;
-      }
-      const uint32_t hi = f32_to_bf16(h);
-      const uint32_t lo = f32_to_bf16(h - __uint_as_float(hi << 16));
-      uint16_t* dst = (uint16_t*)g.out + (int64_t)m * g.ldo + col;
-      dst[0] = (uint16_t)hi;
-      dst[g.lo_off] = (uint16_t)lo;
     }
-    __syncthreads();   // at[] is rewritten by the next unit
+    f32x4_t u = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (NB == 2) {
+#pragma unroll
+      for (int k = 0; k < kSplitCap; ++k)
+        if (k < S) u += pv[k];
+    }
+    f32x4_t h;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) h[q] = NB == 2 ? a[q] * u[q] : a[q];
+    if (g.out_a) {
+      *(f32x4_t*)(g.out_a + (int64_t)m * g.ldo_au + c) = a;
+      if (NB == 2 && g.out_u) *(f32x4_t*)(g.out_u + (int64_t)m * g.ldo_au + c) = u;
+    }
+    uint16_t* dst = (uint16_t*)g.out + (int64_t)m * g.ldo;
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      hi[q] = f32_to_bf16(h[q]);
+      lo[q] = f32_to_bf16(h[q] - __uint_as_float(hi[q] << 16));
+    }
+    *(u32x2_t*)(dst + c) = u32x2_t{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+    *(u32x2_t*)(dst + g.lo_off + c) = u32x2_t{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
   }
 }
 
