@@ -284,7 +284,8 @@ sffn_status sffn_check(sffn_handle* h, hipStream_t stream);
 #define SFFN_K_GATE_TWELL    0  /* gate GEMM with the ReLU + TwELL epilogue */
 #define SFFN_K_FLAGS         1  /* overflow flags and flagged-row list */
 #define SFFN_K_SPARSE_UP     2  /* sparse up projection: per-slice partial dots */
-#define SFFN_K_FLAG_GATEUP   3  /* gate/up GEMM of the flagged rows (+ split-K combine) */
+#define SFFN_K_FLAG_GATEUP   3  /* hidden rows of the dense path: bf16 up GEMM + combine
+                                    from the gate's own outputs, fp32 gate/up GEMM + combine */
 #define SFFN_K_FLAG_DOWN     4  /* down GEMM of the flagged rows (split-K) */
 #define SFFN_K_SPLITK_REDUCE 5  /* split-K reduction into the flagged rows */
 #define SFFN_K_DENSE_GATEUP  6  /* dense mode: gate/up GEMM */

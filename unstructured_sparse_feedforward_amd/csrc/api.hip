@@ -128,11 +128,10 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
     const int tiles_d = std::max(1, h->num_cu / (int)(d / 128));
     const int tiles_h = std::max(1, h->num_cu / (int)(F / 128));
     // bf16: the small-row GEMM keeps split partials of at most
-    // 2 * num_cu tiles, and always the gate | up partials of every row
+    // 2 * num_cu tiles, and always the up partials of every row
     const size_t part_small =
         h->desc.dtype == SFFN_BF16
-            ? std::max((size_t)2 * h->num_cu * 128 * 128,
-                       (size_t)((T + 127) / 128 * 128) * (h->desc.gated ? 2 : 1) * F)
+            ? std::max((size_t)2 * h->num_cu * 128 * 128, (size_t)((T + 127) / 128 * 128) * F)
             : 0;
     const size_t part_d = (size_t)tiles_d * 128 * d;
     const size_t part_h = (size_t)2 * tiles_h * 128 * F;
@@ -606,7 +605,7 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
       e = launch_gemm(dt, nb, false, kEpiHiddenSplitK, f, stream);
       if (e == hipSuccess) e = launch_hidden_combine(dt, nb, f, stream);
     }
-    if (e != hipSuccess) return hip_fail(h, e, "dense-path gate/up GEMM");
+    if (e != hipSuccess) return hip_fail(h, e, "dense-path hidden rows");
     GemmArgs f2 = {};
     f2.A = hid;
     f2.m_dev = n_bk;
