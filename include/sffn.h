@@ -164,9 +164,9 @@ typedef struct sffn_hybrid {
 /* Create a handle for the current HIP device. Validates the descriptor
  * (SFFN_E_ARG / SFFN_E_UNSUPPORTED) before touching the device; returns
  * SFFN_E_UNSUPPORTED when the current device is not gfx950 and SFFN_E_HIP
- * when no device can be queried. Allocates host memory, one HIP stream
- * (default priority) and two events; no device memory. Calls on the
- * handle must be made with the same device current. */
+ * when no device can be queried. Allocates host memory only (per-kernel
+ * timing events are created on demand). Calls on the handle must be made
+ * with the same device current. */
 sffn_status sffn_create(const sffn_desc* desc, sffn_handle** out);
 
 /* Destroy a handle (NULL is allowed). */
@@ -213,10 +213,6 @@ sffn_status sffn_gate_preact(sffn_handle* h, const void* x, const void* w_gate,
  *     two GEMMs, as in a standard bf16 feedforward. tw must be NULL.
  * w_up must be NULL iff the layer is non-gated. The workspace must hold
  * sffn_workspace_bytes(op = SFFN_OP_FORWARD_SPARSE or _DENSE).
- * In sparse mode the flagged rows' dense path runs on the handle's own
- * stream, forked from `stream` after the row routing and joined back into
- * it before the call returns: to the caller all work is ordered on
- * `stream` (this also holds under stream capture).
  */
 sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate,
                          const void* w_up, const void* w_down, int64_t T,
@@ -273,11 +269,10 @@ sffn_status sffn_check(sffn_handle* h, hipStream_t stream);
 
 /*
  * Per-kernel timing. While enabled, every kernel launch of the library is
- * bracketed by two HIP events recorded on the call's stream, and the dense
- * path of flagged or backup rows, which otherwise runs on a second stream
- * alongside the sparse kernels, runs on the call's stream too, so that
- * each interval holds one kernel alone. sffn_profile_read waits for the recorded
- * events, writes for each kernel id k < n the summed milliseconds and the
+ * bracketed by two HIP events recorded on the call's stream, so that each
+ * interval holds one kernel id's launches alone. sffn_profile_read waits
+ * for the recorded events, writes for each kernel id k < n the summed
+ * milliseconds and the
  * number of launches since the last read (or since enabling), and resets
  * the sums. Disabling drops pending records. Kernel ids:
  */

@@ -28,10 +28,6 @@ struct sffn_handle {
   std::vector<sffn_prof_rec> recs;
   double tot_ms[SFFN_K_COUNT] = {};
   int32_t launches[SFFN_K_COUNT] = {};
-  // second stream (default priority) for the dense path of flagged or
-  // backup rows, forked from and joined back into the caller's stream
-  hipStream_t side = nullptr;
-  hipEvent_t ev_fork = nullptr, ev_join = nullptr;
 };
 
 namespace {
@@ -238,21 +234,12 @@ sffn_status sffn_create(const sffn_desc* desc, sffn_handle** out) {
   h->device = dev;
   h->num_cu = prop.multiProcessorCount;
   h->n_t = desc->d_ff / kTile;
-  if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
-      hipEventCreateWithFlags(&h->ev_fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&h->ev_join, hipEventDisableTiming) != hipSuccess) {
-    sffn_destroy(h);
-    return SFFN_E_HIP;
-  }
   *out = h;
   return SFFN_OK;
 }
 
 void sffn_destroy(sffn_handle* h) {
   if (!h) return;
-  if (h->side) (void)hipStreamDestroy(h->side);
-  if (h->ev_fork) (void)hipEventDestroy(h->ev_fork);
-  if (h->ev_join) (void)hipEventDestroy(h->ev_join);
   for (auto& r : h->recs) {
     (void)hipEventDestroy(r.a);
     (void)hipEventDestroy(r.b);
@@ -478,28 +465,18 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   }
   if (e != hipSuccess) return hip_fail(h, e, "backup list");
 
-  // 4. dense path: hidden rows H = ReLU(x W_g) * (x W_u) (split-K over the
+  // 4. dense path: hidden rows H = ReLU(z) * (x W_u) (split-K over the
   //    few rows, then a combine that stores H as bf16 hi + lo, or fp32, and
   //    in training the ReLU(z) and u rows), then y = H W_d scattered into
-  //    the rows (split-K + reduce)
+  //    the rows (split-K + reduce). The dense path touches only its rows of
+  //    y (and its own workspace), the sparse phases only the others. It
+  //    runs in line on the caller's stream: on a second stream its few
+  //    workgroups were starved beside the sparse grids and ended last,
+  //    which measured slower than running it in line.
   void* hid = at<char>(ws, L.hid);
   float* part = at<float>(ws, L.part);
   const int mcap = train ? (int)std::min<int64_t>(hy->max_backup, T) : 0;
-  // The dense path touches only its rows of y (and its own workspace), the
-  // sparse phases only the others: the dense path runs on the side stream
-  // while the sparse kernels run on the caller's, launched first so that
-  // its few workgroups are not queued behind the sparse grids.
-  // With per-kernel timing on, everything stays on the caller's stream so
-  // that each kernel's events bracket that kernel alone.
-  hipStream_t main_stream = stream;
-  bool forked = false;
-  if ((!train || mcap > 0) && !h->prof) {
-    if ((e = hipEventRecord(h->ev_fork, main_stream)) != hipSuccess ||
-        (e = hipStreamWaitEvent(h->side, h->ev_fork, 0)) != hipSuccess)
-      return hip_fail(h, e, "fork");
-    stream = h->side;
-    forked = true;
-  }
+  GemmArgs down_late = {};   // bf16: the dense path's down product, run last
   if ((!train || mcap > 0) && dt == kBF16) {
     // ReLU(z) of the rows comes from the gate GEMM itself (their TwELL
     // tiles, and the saved pre-activations of the tiles that overflowed);
@@ -563,16 +540,8 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     f2.split_max = std::min(kSplitMax, f2.K / 32);
     f2.num_cu = h->num_cu;
     f2.grid = gemm_small_grid(h->num_cu);
-    {
-      ProfScope ps(h, SFFN_K_FLAG_DOWN, stream);
-      e = launch_gemm_small(true, kEpiStoreF32, f2, stream);
-    }
-    if (e != hipSuccess) return hip_fail(h, e, "dense-path down GEMM");
-    {
-      ProfScope ps(h, SFFN_K_SPLITK_REDUCE, stream);
-      e = launch_splitk_reduce(f2, y, D.d, stream);
-    }
-    if (e != hipSuccess) return hip_fail(h, e, "split-K reduce");
+    // launched after the sparse down projection
+    down_late = f2;
   } else if (!train || mcap > 0) {
     GemmArgs f = {};
     f.A = x;
@@ -642,10 +611,6 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     }
     if (e != hipSuccess) return hip_fail(h, e, "split-K reduce");
   }
-  if (forked) {
-    if ((e = hipEventRecord(h->ev_join, stream)) != hipSuccess) return hip_fail(h, e, "join");
-    stream = main_stream;
-  }
 
   // 5. sparse up/down over the ELL rows, d sliced across the XCDs
   SliceArgs sa = {};
@@ -676,8 +641,18 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     e = launch_updown(dt, D.gated != 0, 1, sa, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "sparse up/down");
-  if (forked && (e = hipStreamWaitEvent(stream, h->ev_join, 0)) != hipSuccess)
-    return hip_fail(h, e, "join");
+  if (down_late.out != nullptr) {
+    {
+      ProfScope ps(h, SFFN_K_FLAG_DOWN, stream);
+      e = launch_gemm_small(true, kEpiStoreF32, down_late, stream);
+    }
+    if (e != hipSuccess) return hip_fail(h, e, "dense-path down GEMM");
+    {
+      ProfScope ps(h, SFFN_K_SPLITK_REDUCE, stream);
+      e = launch_splitk_reduce(down_late, y, D.d, stream);
+    }
+    if (e != hipSuccess) return hip_fail(h, e, "split-K reduce");
+  }
   return SFFN_OK;
 }
 
