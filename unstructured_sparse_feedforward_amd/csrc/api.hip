@@ -944,8 +944,10 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
       w.A = pass == 0 ? ba.gz_t : (pass == 1 ? ba.gu_t : ba.gh_t);
       w.lda = L.ldt;
       w.M = D.d_ff;
+      // bf16: x and dy rows transposed ([d, ldt], k-contiguous like A);
+      // fp32: row-major [Rp, d]
       w.B0 = pass == 2 ? ba.dyb : ba.xb;
-      w.ldb = D.d;
+      w.ldb = split ? L.ldt : D.d;
       w.N = D.d;
       w.k_dev = hy->n_backup;
       w.k_cap = cap;
@@ -953,9 +955,9 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
       w.out = pass == 0 ? dw_gate : (pass == 1 ? dw_up : dw_down);
       w.ldo = D.d;
       w.accumulate = 0;
-      w.grid = gemm_grid(dt, 1, h->num_cu);
       w.num_cu = h->num_cu;
-      e = launch_gemm(dt, 1, true, kEpiStoreF32, w, stream);
+      w.grid = gemm_grid(dt, 1, h->num_cu);
+      e = launch_gemm(dt, 1, !split, kEpiStoreF32, w, stream);
       if (e != hipSuccess) return hip_fail(h, e, "backup dW");
     }
   }

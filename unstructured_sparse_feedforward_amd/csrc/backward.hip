@@ -383,6 +383,53 @@ __global__ __launch_bounds__(256) void gather_stack_kernel(const E* __restrict__
   }
 }
 
+// bf16: the same rows transposed, column-major [d, ldt]: column c holds
+// x[brow[r]][c] at k = r and k = Rp + r for r < R, zeros up to 2 Rp, so that
+// both operands of the dW GEMMs are k-contiguous. A workgroup moves 64 rows
+// x 64 columns through LDS: 16-byte loads along the rows, 16-byte stores
+// along the columns.
+__global__ __launch_bounds__(256) void gather_stack_t_kernel(const uint16_t* __restrict__ src,
+                                                             int d, const int32_t* __restrict__ brow,
+                                                             const int32_t* __restrict__ n, int cap,
+                                                             uint16_t* __restrict__ dst,
+                                                             int64_t ldt) {
+  __shared__ __align__(16) uint16_t tile[64][72];   // [column][row]
+  const int R = device_rows(n, cap);
+  const int Rp = (R + 63) / 64 * 64;
+  const int tid = threadIdx.x;
+  const int nct = d / 64;
+  const int ntiles = (Rp / 64) * nct;
+  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int r0 = (t / nct) * 64;
+    const int c0 = (t - (t / nct) * nct) * 64;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int e = p * 256 + tid;     // 64 rows x 8 chunks of 8 columns
+      const int rl = e >> 3;
+      const int ch = e & 7;
+      u32x4_t v = {0, 0, 0, 0};
+      if (r0 + rl < R) v = *(const u32x4_t*)(src + (int64_t)brow[r0 + rl] * d + c0 + ch * 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        tile[ch * 8 + 2 * q][rl] = (uint16_t)(v[q] & 0xFFFFu);
+        tile[ch * 8 + 2 * q + 1][rl] = (uint16_t)(v[q] >> 16);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int e = p * 256 + tid;     // 64 columns x 8 chunks of 8 rows
+      const int cl = e >> 3;
+      const int ch = e & 7;
+      const u32x4_t v = *(const u32x4_t*)&tile[cl][ch * 8];
+      uint16_t* o = dst + (int64_t)(c0 + cl) * ldt + r0 + ch * 8;
+      *(u32x4_t*)o = v;
+      *(u32x4_t*)(o + Rp) = v;
+    }
+    __syncthreads();
+  }
+}
+
 // From dH of the backup rows: dZ, dU (and H = a u for dW_d) in the layouts
 // of the GEMMs that consume them. Row-major rows of stride ld_rm, hi | lo
 // (bf16, 2F wide) or fp32 (F wide), for dx; neuron-major rows of stride ldt holding hi in
@@ -561,10 +608,10 @@ hipError_t launch_transpose(const BwdArgs& a, hipStream_t s) {
 hipError_t launch_backup_prep(Dtype dt, bool gated, const BwdArgs& a, hipStream_t s) {
   const dim3 g(1024), b(256);
   if (dt == kBF16) {
-    hipLaunchKernelGGL(gather_stack_kernel<uint16_t>, g, b, 0, s, (const uint16_t*)a.x, a.d,
-                       a.brow, a.n_backup, a.cap, (uint16_t*)a.xb);
-    hipLaunchKernelGGL(gather_stack_kernel<uint16_t>, g, b, 0, s, (const uint16_t*)a.dy, a.d,
-                       a.brow, a.n_backup, a.cap, (uint16_t*)a.dyb);
+    hipLaunchKernelGGL(gather_stack_t_kernel, g, b, 0, s, (const uint16_t*)a.x, a.d, a.brow,
+                       a.n_backup, a.cap, (uint16_t*)a.xb, a.ldt);
+    hipLaunchKernelGGL(gather_stack_t_kernel, g, b, 0, s, (const uint16_t*)a.dy, a.d, a.brow,
+                       a.n_backup, a.cap, (uint16_t*)a.dyb, a.ldt);
   } else {
     hipLaunchKernelGGL(gather_stack_kernel<float>, g, b, 0, s, (const float*)a.x, a.d, a.brow,
                        a.n_backup, a.cap, (float*)a.xb);

@@ -240,6 +240,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16_t (&acc)[NB][
   const int h = lane >> 5;     // which of the register's two rows
   const int c32 = lane & 31;   // column inside the 32-column block
   static_assert(EPI != kEpiTwell, "the TwELL gate GEMM is gemm_twell2_kernel");
+  // the whole block tile inside the output: stores without bounds tests
+  const bool full = m0 + BM <= M && n0 + 2 * Cfg<NB>::WN <= g.N;
   if (EPI == kEpiStoreF32 && NB == 1 && g.accumulate) {
     // out += acc: a block row's 16 x JB old values are loaded together,
     // then added and stored
@@ -254,43 +256,68 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16_t (&acc)[NB][
           const int col = n0 + wc * Cfg<NB>::WN + j * 32 + c32;
           prev[q][j] = (row < M && col < g.N) ? ((const float*)g.out)[(int64_t)row * g.ldo + col] : 0.0f;
         }
+      // every sum before the first store: a store issued between two of
+      // the loads' uses would make each use wait for all memory operations
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+#pragma unroll
+        for (int j = 0; j < JB; ++j) prev[q][j] += agpr(acc[0][i][j][q]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int q = 0; q < 16; ++q)
 #pragma unroll
         for (int j = 0; j < JB; ++j) {
           const int row = m0 + wr * 128 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
           const int col = n0 + wc * Cfg<NB>::WN + j * 32 + c32;
-          if (row < M && col < g.N)
-            ((float*)g.out)[(int64_t)row * g.ldo + col] = prev[q][j] + agpr(acc[0][i][j][q]);
+          if (row < M && col < g.N) ((float*)g.out)[(int64_t)row * g.ldo + col] = prev[q][j];
         }
     }
   } else {
+    // a block row's 16 x JB values are read out of the accumulators into
+    // registers of their own first, then stored: with one register reused
+    // for every value each store would wait for the previous one to leave
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      float v[16][JB];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int row = m0 + wr * 128 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
-        __builtin_amdgcn_sched_barrier(0);
-        if (row >= M) continue;
+      for (int q = 0; q < 16; ++q)
 #pragma unroll
         for (int j = 0; j < JB; ++j) {
-          const int col = n0 + wc * Cfg<NB>::WN + j * 32 + c32;
-          if (col >= g.N) continue;
-          float v;
           if constexpr (NB == 2) {
             const float z = agpr(acc[0][i][j][q]);
-            v = (z > 0.0f ? z : 0.0f) * agpr(acc[1][i][j][q]);
+            v[q][j] = (z > 0.0f ? z : 0.0f) * agpr(acc[1][i][j][q]);
           } else {
-            v = agpr(acc[0][i][j][q]);
-            if (g.act) v = v > 0.0f ? v : 0.0f;
+            const float t = agpr(acc[0][i][j][q]);
+            v[q][j] = g.act ? (t > 0.0f ? t : 0.0f) : t;
           }
-          if constexpr (EPI == kEpiStoreF32) {
-            ((float*)g.out)[(int64_t)row * g.ldo + col] = v;
-          } else {  // kEpiHiddenBF16
-            ((uint16_t*)g.out)[(int64_t)row * g.ldo + col] = (uint16_t)f32_to_bf16(v);
+        }
+      auto put = [&](int q, int j, int row, int col) {
+        if constexpr (EPI == kEpiStoreF32) {
+          ((float*)g.out)[(int64_t)row * g.ldo + col] = v[q][j];
+        } else {  // kEpiHiddenBF16
+          ((uint16_t*)g.out)[(int64_t)row * g.ldo + col] = (uint16_t)f32_to_bf16(v[q][j]);
+        }
+      };
+      if (full) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+#pragma unroll
+          for (int j = 0; j < JB; ++j)
+            put(q, j, m0 + wr * 128 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3),
+                n0 + wc * Cfg<NB>::WN + j * 32 + c32);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int row = m0 + wr * 128 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
+          if (row >= M) continue;
+#pragma unroll
+          for (int j = 0; j < JB; ++j) {
+            const int col = n0 + wc * Cfg<NB>::WN + j * 32 + c32;
+            if (col < g.N) put(q, j, row, col);
           }
         }
       }
+    }
   }
 }
 
@@ -326,7 +353,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
   const int wr = wave >> 1;
   const int wc = wave & 1;
   const int M = g.M;
-  const int nkt = g.K / RBK;
+  // K may live on the device (as in the n-contiguous kernel below)
+  const int Kd = g.k_dev ? g.k_mult * ((device_rows(g.k_dev, g.k_cap) + 63) / 64 * 64) : g.K;
+  const int nkt = Kd / RBK;
+  if (nkt == 0 && g.accumulate) return;
   const TileSched ts(M, g.N, BN);
 
   const char* Ab = (const char*)g.A;
@@ -415,6 +445,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
     // which lgkmcnt can count), then reads the next ones while it
     // multiplies; the second substep of a stage runs after the barrier and
     // reads the first fragments of the next stage.
+    if (nkt > 0) {
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     wg_barrier();   // the previous tile's readers are done with LDS
     __builtin_amdgcn_sched_barrier(0);
@@ -448,6 +479,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
       interleave_reads_copies();
       __builtin_amdgcn_sched_barrier(0);
       slot = next;
+    }
     }
     epilogue<NB, EPI>(g, acc, m0, n0, wr, wc, lane);
   }
@@ -776,8 +808,8 @@ hipError_t launch_ring(const GemmArgs& g, hipStream_t s) {
 bool gemm_big_supported(Dtype dt, int nb, bool bt, Epi epi, const GemmArgs& g) {
   if (dt != kBF16 || g.m_dev || g.a_rows || g.out_rows || g.part || g.kwrap) return false;
   if (g.accumulate && epi != kEpiStoreF32) return false;
-  // a device-sized K: n-contiguous B only
-  if (g.k_dev) return bt && nb == 1 && epi == kEpiStoreF32 && g.k_mult >= 1;
+  // a device-sized K: one B operand, float32 output
+  if (g.k_dev) return nb == 1 && epi == kEpiStoreF32 && g.k_mult >= 1;
   if (g.K % (bt ? BK : RBK) != 0) return false;
   if (bt) return nb == 1 && epi == kEpiStoreF32;
   if (epi == kEpiTwell) return nb == 1 && g.ovf == nullptr;

@@ -33,6 +33,7 @@ constexpr int NT = 256;
 constexpr int NXCD = 8;
 constexpr int BK = 32;       // k per slot (64 bytes per LDS row)
 constexpr int ROWB = 64;
+constexpr int kGroupRows = 8;   // row tiles per group of the tile order
 
 // Ring geometry: a slot holds an A tile and a B tile (16 KB), or with a
 // dual A (hi and lo parts) two A tiles and a B tile (24 KB); four slots,
@@ -67,7 +68,7 @@ __device__ __forceinline__ int small_splits(const GemmArgs& g, int mt, int ntl) 
 }
 
 template <bool BT, int EPI, bool DUAL>
-__global__ __launch_bounds__(NT) void gemm_small_kernel(GemmArgs g) {
+__global__ __launch_bounds__(NT, 2) void gemm_small_kernel(GemmArgs g) {
   constexpr int SLOT = Ring<DUAL>::SLOT;
   constexpr int NSLOT = Ring<DUAL>::NSLOT;
   constexpr int LPS = Ring<DUAL>::LPS;
@@ -82,7 +83,12 @@ __global__ __launch_bounds__(NT) void gemm_small_kernel(GemmArgs g) {
   if (M <= 0) return;
   const int mt = (M + BM - 1) / BM;
   const int ntl = g.N / BN;
-  const int nkt_all = g.K / BK;
+  // K may live on the device (backup rows, in blocks of 64, times k_mult
+  // for stacked hi and lo parts); a K of 0 leaves an accumulated output as
+  // it is and stores zeros otherwise
+  const int nkt_all =
+      (g.k_dev ? g.k_mult * ((device_rows(g.k_dev, g.k_cap) + 63) / 64 * 64) : g.K) / BK;
+  if (nkt_all == 0 && g.accumulate) return;
   // partials whenever K is split; the hidden GEMM always leaves them to
   // the combine kernel (ReLU(z) * u needs both operands' tiles)
   const int S = small_splits(g, mt, ntl);
@@ -105,11 +111,17 @@ __global__ __launch_bounds__(NT) void gemm_small_kernel(GemmArgs g) {
   const int bkg = tid >> 4;
 
   for (int L = xcd * per + blockIdx.x / NXCD; L < t_end; L += G8) {
-    // tiles of one column block are consecutive (they share B in L2)
+    // the splits of a tile are consecutive, then up to 8 row tiles of one
+    // column block (they share B in L2), then the group's next column
+    // block (the group's A rows stay in L2 while the columns stream past)
     const int ks = L % S;
     const int rem = L / S;
-    const int tm = rem % mt;
-    const int tn = rem / mt;
+    const int grp = rem / (kGroupRows * ntl);
+    const int gm0 = grp * kGroupRows;
+    const int gcount = min(kGroupRows, mt - gm0);
+    const int r2 = rem - grp * kGroupRows * ntl;
+    const int tn = r2 / gcount;
+    const int tm = gm0 + (r2 - tn * gcount);
     const int m0 = tm * BM;
     const int n0 = tn * BN;
     const int kt0 = (int)((int64_t)ks * nkt_all / S);
@@ -155,8 +167,11 @@ __global__ __launch_bounds__(NT) void gemm_small_kernel(GemmArgs g) {
         const char* bs =
             g.kcat > 0 && (int64_t)(kt0 + kt) * BK >= g.kcat ? (const char*)g.B1 : Bb;
         const char* p = bs + (kb + 2 * bkg) * ldb_b + (int64_t)(nb0 + 8 * bg) * 2;
-        rb[0] = *(const u32x4_t*)p;
-        rb[1] = *(const u32x4_t*)(p + ldb_b);
+        // issued as opaque loads: the compiler's own wait insertion loses
+        // count of these across the unrolled loop's back edge and drains
+        // every load in flight; the explicit waits below cover them
+        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(rb[0]) : "v"(p));
+        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(rb[1]) : "v"(p + ldb_b));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -250,57 +265,78 @@ __global__ __launch_bounds__(NT) void gemm_small_kernel(GemmArgs g) {
     // most NSLOT - 2 stages of copies in flight". n-contiguous B: stage
     // kt + 1's registers are written into its slot just before the barrier
     // of iteration kt.
+    if (nkt > 0) {
     __builtin_amdgcn_s_waitcnt(kWaitAll);
     wg_barrier();   // the previous tile's readers are done with LDS
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int p = 0; p < NSLOT; ++p) issue(min(p, nkt - 1), p, rbs[p]);
+    __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(wait_imm((NSLOT - 1) * LPS, 15));   // stage 0 landed
+    __builtin_amdgcn_sched_barrier(0);
     store_b(0, rbs[0]);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     wg_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_frags(0, 0, 0);
 
-    for (int kb0 = 0; kb0 < nkt; kb0 += NSLOT) {
+    // one stage: kt's second half-step and kt+1's first, with stage kt+1
+    // landed, written (n-contiguous B) and made visible in between
+    auto stage = [&](int kt, int u) __attribute__((always_inline)) {
+      const int nu = (u + 1) % NSLOT;   // slot (and register set) of stage kt + 1
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(u, 1, 1);
+      mfmas(0);
+      spread();
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(wait_imm((NSLOT - 2) * LPS, 0));  // stage kt+1 landed
+      __builtin_amdgcn_sched_barrier(0);
+      store_b(nu, rbs[nu]);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      wg_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(nu, 0, 0);
+      issue(min(kt + NSLOT, nkt - 1), u, rbs[u]);
+      mfmas(1);
+      spread();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // whole groups of NSLOT stages (the slot and register set of a stage
+    // are compile-time constants after unrolling), then the last few
+    // stages outside the loop: no exit from inside the unrolled group
+    int kb0 = 0;
+    for (; kb0 + NSLOT <= nkt; kb0 += NSLOT) {
 #pragma unroll
-      for (int u = 0; u < NSLOT; ++u) {
-        const int kt = kb0 + u;
-        if (kt >= nkt) break;
-        const int nu = (u + 1) % NSLOT;   // slot (and register set) of stage kt + 1
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(u, 1, 1);
-        mfmas(0);
-        spread();
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(wait_imm((NSLOT - 2) * LPS, 0));  // stage kt+1 landed
-        store_b(nu, rbs[nu]);
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        wg_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(nu, 0, 0);
-        issue(min(kt + NSLOT, nkt - 1), u, rbs[u]);
-        mfmas(1);
-        spread();
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int u = 0; u < NSLOT; ++u) stage(kb0 + u, u);
+    }
+#pragma unroll
+    for (int u = 0; u < NSLOT - 1; ++u) {
+      if (kb0 + u >= nkt) break;
+      stage(kb0 + u, u);
+    }
+    if constexpr (BT) {
+      // the repeats past the last stage were loaded into registers too:
+      // they land before any of those registers is given to another value
+      __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
+#pragma unroll
+      for (int u = 0; u < NSLOT; ++u) asm volatile("" ::"v"(rbs[u][0]), "v"(rbs[u][1]));
+    }
     }
 
     // ---- epilogue
     const int h = lane >> 5;
     const int c32 = lane & 31;
     if (to_part) {
+      // the partials have Mpad rows: rows past M are written (never read)
+      float* pbase = g.part + ((int64_t)ks * Mpad + m0 + wr * 64 + h * 4) * g.N + n0 + wc * 64 + c32;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-          const int m = m0 + wr * 64 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
-          if (m < M) {
-            float* dst = g.part + ((int64_t)ks * Mpad + m) * g.N + n0 + wc * 64 + c32;
+          float* dst = pbase + (int64_t)(i * 32 + (q >> 2) * 8 + (q & 3)) * g.N;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) dst[j * 32] = acc[i][j][q];
-          }
+          for (int j = 0; j < 2; ++j) dst[j * 32] = acc[i][j][q];
         }
     } else if (g.accumulate) {
       // out += C: the tile row block's old values are loaded together first
@@ -347,7 +383,12 @@ __global__ __launch_bounds__(NT) void gemm_small_kernel(GemmArgs g) {
 
 bool gemm_small_supported(const GemmArgs& g, bool bt, Epi epi) {
   if (epi != kEpiStoreF32 && epi != kEpiHiddenSplitK) return false;
-  if (g.k_dev || g.N % BN != 0 || g.K % BK != 0 || g.K < BK) return false;
+  if (g.N % BN != 0) return false;
+  // a device-sized K: one plain product per tile (no split, no second operand)
+  if (g.k_dev)
+    return bt && epi == kEpiStoreF32 && g.part == nullptr && g.k_mult >= 1 && g.kcat == 0 &&
+           g.alo == 0 && g.kwrap == 0 && g.nsplit == 0;
+  if (g.K % BK != 0 || g.K < BK) return false;
   if (g.kwrap > 0 && g.kwrap % BK != 0) return false;
   if (g.kcat > 0 && (!bt || g.nsplit > 0 || g.kcat % BK != 0 || g.B1 == nullptr)) return false;
   if (g.alo > 0 && (!bt || epi != kEpiStoreF32 || g.kwrap > 0 || g.nsplit > 0)) return false;
