@@ -205,6 +205,28 @@ def test_backward_all_rows_backup():
     assert_close_bf16(dwd.cpu().numpy(), ref["dw_down"], "dw_down")
 
 
+def test_backward_wide_ell_rows():
+    """With TwELL capacity C = 128 (no tile can overflow) and K = 3000 the
+    outlier rows (about half of the 5632 neurons active) stay in the ELL:
+    rows of up to 47 units of 64 slots, so that the neuron-major grouping
+    orders slots across several units of a row and across blocks of units."""
+    w = wl.TRAIN_HYBRID.replace(twell_cap=128, ell_cap=3000)
+    _print("backward wide ELL rows K=3000")
+    inp = wl.make_inputs(w, seed=53, T=256)
+    ffn = SparseFFN(w.d, w.F, gated=True, twell_cap=w.twell_cap, ell_cap=w.ell_cap,
+                    dtype=torch.bfloat16)
+    args = [dev(inp, k) for k in ("x", "w_gate", "w_up", "w_down")]
+    _, hy = ffn.forward_train(*args)
+    assert ffn.hybrid_check(hy) == B.SFFN_OK
+    assert int(hy["ell_cnt"].max().item()) > 64
+    dx, dwg, dwu, dwd = ffn.backward(*args, hy, dev(inp, "dy"))
+    ref = _grads_ref(inp, 0.0)
+    assert_close_bf16(dx.cpu().numpy(), ref["dx"], "dx")
+    assert_close_bf16(dwg.cpu().numpy(), ref["dw_gate"].T, "dw_gate")
+    assert_close_bf16(dwu.cpu().numpy(), ref["dw_up"].T, "dw_up")
+    assert_close_bf16(dwd.cpu().numpy(), ref["dw_down"], "dw_down")
+
+
 @pytest.mark.parametrize("max_backup", [None, 0])
 def test_backward_no_backup_rows(max_backup):
     """No outlier tokens and K = 64 keep every row on the ELL path. With

@@ -76,7 +76,7 @@ struct Layout {
   size_t ell_a = 0, ell_idx = 0, ell_cnt = 0, bk = 0, upart = 0;
   size_t hid = 0, zovf = 0, part = 0, total = 0;
   // backward
-  size_t gz = 0, gu = 0, drec = 0, ncnt = 0, noff = 0, ent0 = 0, meta = 0, dH = 0, gz_rm = 0;
+  size_t drec = 0, ncnt = 0, noff = 0, thist = 0, toff = 0, meta = 0, dH = 0, gz_rm = 0;
   size_t gz_t = 0, gu_t = 0, gh_t = 0, xb = 0, dyb = 0;
   int64_t ldt = 0;
 };
@@ -145,12 +145,12 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
     const int64_t Tp = (T + 63) / 64 * 64;
     L.ldt = split ? 2 * Tp : Tp;
     L.upart = take((size_t)ns * T * Kp * 4);
-    L.gz = take((size_t)T * K * 4);
-    L.gu = take((size_t)T * K * 4);
     L.drec = take((size_t)T * K * 16);
-    L.ncnt = take((size_t)2 * F * 4);
+    const int64_t F4 = (F + 3) / 4, nblk = transpose_blocks(T, (int)K);
+    L.ncnt = take((size_t)F4 * 16);
     L.noff = take((size_t)(F + 1) * 4);
-    L.ent0 = take((size_t)T * K * 4);
+    L.thist = take((size_t)nblk * F4 * 4);
+    L.toff = take((size_t)nblk * F4 * 16);
     L.meta = take((size_t)T * K * 16);
     L.dH = take((size_t)T * F * 4);
     // dZ and dU rows: bf16 [T, 4F] (dZ hi | lo, dU hi | lo), fp32 two [T, F]
@@ -820,8 +820,6 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
   ba.Kp = Kp;
   ba.l1 = l1_coeff;
   ba.dpart = at<float>(ws, L.upart);
-  ba.gz = at<float>(ws, L.gz);
-  ba.gu = at<float>(ws, L.gu);
   ba.drec = at<f32x4_t>(ws, L.drec);
   ba.dx = dx;
   ba.dwg = dw_gate;
@@ -829,7 +827,8 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
   ba.dwd = dw_down;
   ba.ncnt = at<int32_t>(ws, L.ncnt);
   ba.noff = at<int32_t>(ws, L.noff);
-  ba.ent_unsorted = at<int32_t>(ws, L.ent0);
+  ba.thist = at<uint32_t>(ws, L.thist);
+  ba.toff = at<int32_t>(ws, L.toff);
   ba.meta = at<f32x4_t>(ws, L.meta);
   ba.brow = hy->brow;
   ba.n_backup = hy->n_backup;

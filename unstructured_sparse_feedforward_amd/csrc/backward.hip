@@ -38,16 +38,17 @@ __global__ __launch_bounds__(256) void dzu_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < NS; ++r) dh += a.dpart[((int64_t)r * a.T + t) * a.Kp + k];
     const int64_t q = t * a.K + k;
-    float gz, gu = 0.0f;
+    float gz, gu = 0.0f, hv;
     if constexpr (GATED) {
-      gu = dh * a.ell_a[q];
-      gz = dh * a.ell_u[q] + a.l1;
-      a.gu[q] = gu;
+      const float av = a.ell_a[q], uv = a.ell_u[q];
+      gu = dh * av;
+      gz = dh * uv + a.l1;
+      hv = av * uv;
     } else {
       gz = dh + a.l1;
+      hv = a.ell_a[q];
     }
-    a.gz[q] = gz;
-    a.drec[q] = f32x4_t{__int_as_float((int)a.ell_idx[q]), gz, gu, 0.0f};
+    a.drec[q] = f32x4_t{__int_as_float((int)a.ell_idx[q]), gz, gu, hv};
   }
 }
 
@@ -146,21 +147,112 @@ __global__ __launch_bounds__(256) void dx_sparse_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- transpose
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* __restrict__ p, int64_t n) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0;
+// The ELL slots grouped by neuron, ascending rows within a neuron, as a
+// counting sort without global atomics. The slots are taken in units of 64
+// (row t, slots 64c .. 64c + 63, ceil(K / 64) units per row, units in row
+// order) and the units in blocks of kUnitsPerBlock. A neuron occurs at most
+// once in a row, so its place is fixed by (block, order inside the block):
+// per block a count of every neuron, per neuron the prefix of its block
+// counts, then per block the units in order. A neuron's count inside a
+// block is below 256: the counts are bytes, four to a 32-bit word, in LDS.
+constexpr int kUnitsPerBlock = 32;
+
+// The first kUnitsPerBlock units of block b: lane i < nu returns the
+// number of slots of unit i (of its row's slots from 64 c on, at most 64
+// used), with t0 / c0 the row and chunk of the block's first unit. The
+// counts are loaded by all lanes at once, not one dependent load per unit.
+__device__ __forceinline__ int unit_counts(const BwdArgs& a, int cpr, int u0, int nu, int lane,
+                                           int& t0, int& c0) {
+  t0 = u0 / cpr;
+  c0 = u0 - t0 * cpr;
+  int n = 0;
+  if (lane < nu) {
+    const int u = u0 + lane;
+    const int t = u / cpr;
+    n = a.ell_cnt[t] - (u - t * cpr) * 64;
+  }
+  return n;
 }
 
-// One wave per row: count every ELL slot's neuron.
-__global__ __launch_bounds__(256) void count_kernel(const uint16_t* __restrict__ ell_idx,
-                                                    const int32_t* __restrict__ ell_cnt, int64_t T,
-                                                    int K, int32_t* __restrict__ ncnt) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const int n = ell_cnt[t];
-  for (int k = lane; k < n; k += 64) atomicAdd(&ncnt[ell_idx[t * K + k]], 1);
+// Per block of units: every neuron's count, as bytes [nblk][F4 words].
+__global__ __launch_bounds__(256) void block_count_kernel(BwdArgs a, int cpr, int nunits, int F4,
+                                                          uint32_t* __restrict__ hist) {
+  extern __shared__ uint32_t c4[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int i = tid; i < F4; i += 256) c4[i] = 0;
+  const int u0 = blockIdx.x * kUnitsPerBlock;
+  const int nu = min(kUnitsPerBlock, nunits - u0);
+  int t0, c0;
+  const int ucnt = unit_counts(a, cpr, u0, nu, lane, t0, c0);
+  // wave w takes units w, w + 4, ...: ids first, then the counts
+  constexpr int PER = kUnitsPerBlock / 4;
+  int jv[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int i = p * 4 + wave;
+    const int n = __builtin_amdgcn_readlane(ucnt, i);
+    const int c = c0 + i;
+    const int64_t t = t0 + c / cpr;
+    const int k = (c % cpr) * 64 + lane;
+    jv[p] = (i < nu && lane < n) ? (int)a.ell_idx[t * a.K + k] : -1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < PER; ++p)
+    if (jv[p] >= 0) atomicAdd(&c4[jv[p] >> 2], 1u << ((jv[p] & 3) * 8));
+  __syncthreads();
+  for (int i = tid; i < F4; i += 256) hist[(int64_t)blockIdx.x * F4 + i] = c4[i];
+}
+
+// Per neuron: the exclusive prefix of its block counts (off [nblk][4 F4])
+// and its total (ncnt). A workgroup takes 64 neurons (16 count words);
+// thread (s, w) sums word w over the s-th of 16 runs of blocks, the runs'
+// sums are combined in LDS, then each thread writes its run's prefixes.
+// The run is read in batches of 16 loads.
+__global__ __launch_bounds__(256) void block_scan_kernel(const uint32_t* __restrict__ hist,
+                                                         int nblk, int F4,
+                                                         int32_t* __restrict__ off,
+                                                         int32_t* __restrict__ ncnt) {
+  __shared__ i32x4_t part[16][16];
+  const int w = threadIdx.x & 15;
+  const int s = threadIdx.x >> 4;
+  const int W = blockIdx.x * 16 + w;
+  const int L = (nblk + 15) / 16;
+  const int b0 = min(nblk, s * L), b1 = min(nblk, b0 + L);
+  auto bytes = [](uint32_t v) {
+    return i32x4_t{(int)(v & 0xFF), (int)((v >> 8) & 0xFF), (int)((v >> 16) & 0xFF), (int)(v >> 24)};
+  };
+  i32x4_t sum = {0, 0, 0, 0};
+  if (W < F4) {
+    for (int bb = b0; bb < b1; bb += 16) {
+      uint32_t v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = bb + q < b1 ? hist[(int64_t)(bb + q) * F4 + W] : 0u;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) sum += bytes(v[q]);
+    }
+  }
+  part[s][w] = sum;
+  __syncthreads();
+  i32x4_t base = {0, 0, 0, 0}, total = {0, 0, 0, 0};
+  for (int q = 0; q < 16; ++q) {
+    if (q < s) base += part[q][w];
+    total += part[q][w];
+  }
+  if (W >= F4) return;
+  for (int bb = b0; bb < b1; bb += 16) {
+    uint32_t v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) v[q] = bb + q < b1 ? hist[(int64_t)(bb + q) * F4 + W] : 0u;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      if (bb + q < b1) *(i32x4_t*)(off + ((int64_t)(bb + q) * F4 + W) * 4) = base;
+      base += bytes(v[q]);
+    }
+  }
+  if (s == 0) *(i32x4_t*)(ncnt + (int64_t)W * 4) = total;
 }
 
 // Exclusive scan of the F counts into F + 1 offsets; one workgroup.
@@ -194,48 +286,57 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   if (tid == 0) noff[F] = carry;
 }
 
-// One wave per row: place every slot (q = t*K + k) into its neuron's
-// segment at an atomically taken position (order fixed by the sort below).
-__global__ __launch_bounds__(256) void fill_kernel(const uint16_t* __restrict__ ell_idx,
-                                                   const int32_t* __restrict__ ell_cnt, int64_t T,
-                                                   int K, const int32_t* __restrict__ noff,
-                                                   int32_t* __restrict__ cursor,
-                                                   int32_t* __restrict__ ent) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const int n = ell_cnt[t];
-  for (int k = lane; k < n; k += 64) {
-    const int j = ell_idx[t * K + k];
-    const int pos = noff[j] + atomicAdd(&cursor[j], 1);
-    ent[pos] = (int32_t)(t * K + k);
+// Per block of units, one wave: the units in order, each slot taking the
+// next place of its neuron (noff + block prefix + the block's earlier
+// units holding the neuron), stored as the record the dW sums read: {row,
+// dZ, dU, h}. The neuron ids are loaded first, then the places are taken
+// in unit order (a wave's LDS operations complete in issue order), then
+// the records are moved, eight units' loads at a time.
+__global__ __launch_bounds__(64) void block_place_kernel(BwdArgs a, int cpr, int nunits, int F4,
+                                                         const int32_t* __restrict__ off) {
+  extern __shared__ uint32_t c4[];
+  const int lane = threadIdx.x;
+  for (int i = lane; i < F4; i += 64) c4[i] = 0;
+  const int u0 = blockIdx.x * kUnitsPerBlock;
+  const int nu = min(kUnitsPerBlock, nunits - u0);
+  int t0, c0;
+  const int ucnt = unit_counts(a, cpr, u0, nu, lane, t0, c0);
+  int jv[kUnitsPerBlock];
+  int64_t q[kUnitsPerBlock];
+#pragma unroll
+  for (int i = 0; i < kUnitsPerBlock; ++i) {
+    const int n = __builtin_amdgcn_readlane(ucnt, i);
+    const int c = c0 + i;
+    const int64_t t = t0 + c / cpr;
+    q[i] = t * a.K + (c % cpr) * 64 + lane;
+    jv[i] = (i < nu && lane < n) ? (int)a.ell_idx[q[i]] : -1;
   }
-}
-
-// One wave per neuron: sort its segment ascending by rank counting (slot
-// indices are distinct, so every value's rank is the number of smaller
-// ones) and store each slot as the record the dW sums read: {row, dZ, dU,
-// h} with h = a*u (gated) or a.
-template <bool GATED>
-__global__ __launch_bounds__(256) void seg_sort_kernel(BwdArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (j >= a.F) return;
-  const int b = a.noff[j];
-  const int n = a.noff[j + 1] - b;
-  const int32_t* ent = a.ent_unsorted;
-  for (int i0 = 0; i0 < n; i0 += 64) {
-    const bool live = i0 + lane < n;
-    const int v = live ? ent[b + i0 + lane] : 0;
-    int rank = 0;
-    for (int c0 = 0; c0 < n; c0 += 64) {
-      const int w = c0 + lane < n ? ent[b + c0 + lane] : 0x7FFFFFFF;
-      const int m = min(64, n - c0);
-      for (int q = 0; q < m; ++q) rank += __builtin_amdgcn_readlane(w, q) < v ? 1 : 0;
+  int loc[kUnitsPerBlock];
+#pragma unroll
+  for (int i = 0; i < kUnitsPerBlock; ++i) {
+    loc[i] = 0;
+    if (jv[i] >= 0) {
+      const int sh = (jv[i] & 3) * 8;
+      loc[i] = (int)((atomicAdd(&c4[jv[i] >> 2], 1u << sh) >> sh) & 0xFF);
     }
-    if (live) {
-      const float h = GATED ? a.ell_a[v] * a.ell_u[v] : a.ell_a[v];
-      a.meta[b + rank] = f32x4_t{__int_as_float(v / a.K), a.gz[v], GATED ? a.gu[v] : 0.0f, h};
+  }
+  const int32_t* offb = off + (int64_t)blockIdx.x * F4 * 4;
+  constexpr int G = 8;
+#pragma unroll
+  for (int g0 = 0; g0 < kUnitsPerBlock; g0 += G) {
+    int pos[G];
+    f32x4_t r[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int j = max(jv[g0 + i], 0);
+      pos[i] = a.noff[j] + offb[j] + loc[g0 + i];
+      r[i] = jv[g0 + i] >= 0 ? a.drec[q[g0 + i]] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (jv[g0 + i] < 0) continue;
+      const int t = t0 + (c0 + g0 + i) / cpr;
+      a.meta[pos[i]] = f32x4_t{__int_as_float(t), r[i][1], r[i][2], r[i][3]};
     }
   }
 }
@@ -593,15 +694,25 @@ hipError_t launch_bwd_sparse(Dtype dt, bool gated, int which, const BwdArgs& a, 
   return hipErrorInvalidValue;
 }
 
+int64_t transpose_blocks(int64_t T, int K) {
+  const int64_t nunits = T * ((K + 63) / 64);
+  return (nunits + kUnitsPerBlock - 1) / kUnitsPerBlock;
+}
+
 hipError_t launch_transpose(const BwdArgs& a, hipStream_t s) {
-  const dim3 rows((unsigned)((a.T + 3) / 4)), blk(256);
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(64), blk, 0, s, a.ncnt, (int64_t)2 * a.F);
-  hipLaunchKernelGGL(count_kernel, rows, blk, 0, s, a.ell_idx, a.ell_cnt, a.T, a.K, a.ncnt);
+  const int cpr = (a.K + 63) / 64;
+  const int nunits = (int)(a.T * cpr);
+  const int64_t nblk = transpose_blocks(a.T, a.K);
+  const int F4 = (a.F + 3) / 4;
+  if (nblk == 0 || F4 * 4 > 65536) return hipErrorInvalidValue;
+  const size_t lds = (size_t)F4 * 4;
+  hipLaunchKernelGGL(block_count_kernel, dim3((unsigned)nblk), dim3(256), lds, s, a, cpr, nunits,
+                     F4, a.thist);
+  hipLaunchKernelGGL(block_scan_kernel, dim3((unsigned)((F4 + 15) / 16)), dim3(256), 0, s,
+                     a.thist, (int)nblk, F4, a.toff, a.ncnt);
   hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, a.ncnt, a.F, a.noff);
-  hipLaunchKernelGGL(fill_kernel, rows, blk, 0, s, a.ell_idx, a.ell_cnt, a.T, a.K, a.noff,
-                     a.ncnt + a.F, a.ent_unsorted);
-  if (a.wu) hipLaunchKernelGGL(seg_sort_kernel<true>, dim3((unsigned)((a.F + 3) / 4)), blk, 0, s, a);
-  else hipLaunchKernelGGL(seg_sort_kernel<false>, dim3((unsigned)((a.F + 3) / 4)), blk, 0, s, a);
+  hipLaunchKernelGGL(block_place_kernel, dim3((unsigned)nblk), dim3(64), lds, s, a, cpr, nunits,
+                     F4, a.toff);
   return hipGetLastError();
 }
 

@@ -328,16 +328,19 @@ __global__ __launch_bounds__(NT, 2) void gemm_small_kernel(GemmArgs g) {
     const int h = lane >> 5;
     const int c32 = lane & 31;
     if (to_part) {
-      // the partials have Mpad rows: rows past M are written (never read)
       float* pbase = g.part + ((int64_t)ks * Mpad + m0 + wr * 64 + h * 4) * g.N + n0 + wc * 64 + c32;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 2; ++i) {
+        if (m0 + wr * 64 + i * 32 >= M) continue;   // a block of padding rows
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
+          const int m = m0 + wr * 64 + i * 32 + (q >> 2) * 8 + h * 4 + (q & 3);
+          if (m >= M) continue;
           float* dst = pbase + (int64_t)(i * 32 + (q >> 2) * 8 + (q & 3)) * g.N;
 #pragma unroll
           for (int j = 0; j < 2; ++j) dst[j * 32] = acc[i][j][q];
         }
+      }
     } else if (g.accumulate) {
       // out += C: the tile row block's old values are loaded together first
 #pragma unroll

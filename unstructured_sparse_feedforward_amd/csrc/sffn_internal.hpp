@@ -15,6 +15,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
@@ -285,17 +286,16 @@ struct BwdArgs {
   int Kp;
   float l1;
   const float* dpart;     // [NS, T, Kp] partial dy . W_d[j]
-  float* gz;              // [T, K] dZ per ELL slot
-  float* gu;              // [T, K] dU per ELL slot (gated)
-  f32x4_t* drec;          // [T, K] {neuron, dZ, dU} per ELL slot
+  f32x4_t* drec;          // [T, K] {neuron, dZ, dU, h} per ELL slot
   float* dx;              // [T, d]
   float* dwg;             // [F, d]
   float* dwu;             // [F, d] (gated)
   float* dwd;             // [F, d]
   int accumulate;         // dW of the ELL slots adds to what dW holds
-  int32_t* ncnt;          // [2F] per-neuron counts, then fill cursors
+  int32_t* ncnt;          // [4 F4] per-neuron slot counts (F4 = ceil(F / 4))
   int32_t* noff;          // [F + 1]
-  int32_t* ent_unsorted;  // [T*K] slot ids grouped by neuron
+  uint32_t* thist;        // [nblk, F4] per block of slot units: neuron counts, bytes
+  int32_t* toff;          // [nblk, 4 F4] per block: each neuron's slots in earlier blocks
   f32x4_t* meta;          // [T*K] {row, dZ, dU, h} grouped by neuron, ascending rows
   // backup rows
   const int32_t* brow;
@@ -317,6 +317,8 @@ struct BwdArgs {
 // which = 0: dZ/dU per slot and dx of the ELL rows; 1: dW of every neuron
 hipError_t launch_bwd_sparse(Dtype dt, bool gated, int which, const BwdArgs& a, hipStream_t s);
 hipError_t launch_transpose(const BwdArgs& a, hipStream_t s);
+// blocks of slot units of the transpose's counting sort (sizes thist, toff)
+int64_t transpose_blocks(int64_t T, int K);
 hipError_t launch_backup_prep(Dtype dt, bool gated, const BwdArgs& a, hipStream_t s);
 hipError_t launch_backup_grad(Dtype dt, bool gated, const BwdArgs& a, hipStream_t s);
 
