@@ -145,6 +145,8 @@ __global__ __launch_bounds__(256) void dx_sparse_kernel(BwdArgs a) {
   }
 }
 
+constexpr int kDwGrp = 4;   // slots in flight per wave in the dW sums
+
 // ---------------------------------------------------------------- transpose
 
 // The ELL slots grouped by neuron, ascending rows within a neuron, as a
@@ -342,22 +344,24 @@ __global__ __launch_bounds__(64) void block_place_kernel(BwdArgs a, int cpr, int
 }
 
 // dW rows of every neuron: the sums over the neuron's ELL slots in
-// ascending row order of (dZ*x, dU*x, h*dy), added to dW's rows when
-// accumulating (the backup rows' products are stored there); otherwise
-// neurons without slots get zero rows. A lane loads 16 bytes of a row, a
-// neuron's SW-column slice takes LPR lanes, so a wave sums RPW neurons. The
-// x and dy rows a slice gathers are random over all T rows, so an XCD keeps
-// to one slice at a time: workgroup b runs on XCD b mod 8 and the blocks
-// are ordered slice phase first, so the x and dy columns in use on an XCD
-// (T * SW * 4 bytes) stay within its L2. The wave stages the slot records
-// of its neurons in LDS, 64 per neuron at a time, and reads them back as
-// broadcasts; records past a neuron's count are zero (row 0, no weight).
-template <typename E, int SW, bool GATED, int GRP>
+// ascending row order of (dZ*x, dU*x) (SIDE 0: dW_g, dW_u) or h*dy (SIDE 1:
+// dW_d), added to dW's rows when accumulating (the backup rows' products
+// are stored there); otherwise neurons without slots get zero rows. A lane
+// loads 16 bytes of a row, a neuron's SW-column slice takes LPR lanes, so a
+// wave sums RPW neurons. The rows a slice gathers are random over all T
+// rows, so an XCD keeps to one slice at a time: workgroup b runs on XCD b
+// mod 8 and the blocks are ordered slice phase first, so that the columns
+// in use on an XCD (T * SW * 2 bytes of x or of dy: one operand per launch)
+// stay within its L2. The wave stages the slot records of its neurons in
+// LDS, 64 per neuron at a time, and reads them back as broadcasts; records
+// past a neuron's count are zero (row 0, no weight).
+template <typename E, int SW, bool GATED, int GRP, int SIDE>
 __global__ __launch_bounds__(256) void dw_sparse_kernel(BwdArgs a) {
   constexpr int EPL = 16 / (int)sizeof(E);
   constexpr int LPR = SW / EPL;
   constexpr int RPW = 64 / LPR;
   constexpr int CH = 64;
+  constexpr bool TWO = SIDE == 0 && GATED;   // dW_g and dW_u from the same x rows
   static_assert(RPW >= 1 && RPW <= 8 && CH % GRP == 0, "slice geometry");
   using V = Vec<E, EPL>;
   using R = typename V::raw;
@@ -388,23 +392,22 @@ __global__ __launch_bounds__(256) void dw_sparse_kernel(BwdArgs a) {
   for (int q = 0; q < RPW; ++q) nmax = max(nmax, __builtin_amdgcn_readlane(n, q * LPR));
   const int col = slice * SW + l * EPL;
   const int64_t ro = (int64_t)j * a.d + col;
-  const E* xs = (const E*)a.x + col;
-  const E* dys = (const E*)a.dy + col;
-  float ag[EPL], au[EPL], ad[EPL];
+  const E* src = (const E*)(SIDE == 0 ? a.x : a.dy) + col;
+  float* out0 = SIDE == 0 ? a.dwg : a.dwd;
+  float* out1 = a.dwu;
+  float g0[EPL], g1[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) ag[e] = au[e] = ad[e] = 0.0f;
+  for (int e = 0; e < EPL; ++e) g0[e] = g1[e] = 0.0f;
   if (a.accumulate && ok) {
 #pragma unroll
     for (int e = 0; e < EPL; e += 4) {
-      const f32x4_t vg = *(const f32x4_t*)(a.dwg + ro + e);
-      f32x4_t vu = {};
-      if (GATED) vu = *(const f32x4_t*)(a.dwu + ro + e);
-      const f32x4_t vd = *(const f32x4_t*)(a.dwd + ro + e);
+      const f32x4_t v0 = *(const f32x4_t*)(out0 + ro + e);
+      f32x4_t v1 = {};
+      if (TWO) v1 = *(const f32x4_t*)(out1 + ro + e);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        ag[e + c] = vg[c];
-        au[e + c] = vu[c];
-        ad[e + c] = vd[c];
+        g0[e + c] = v0[c];
+        g1[e + c] = v1[c];
       }
     }
   }
@@ -421,27 +424,22 @@ __global__ __launch_bounds__(256) void dw_sparse_kernel(BwdArgs a) {
     // a wave's LDS accesses complete in issue order: no barrier is needed
     // between its own writes and reads
     const int m = min(CH, nmax - i0);
-    for (int g0 = 0; g0 < m; g0 += GRP) {
+    for (int gg = 0; gg < m; gg += GRP) {
       f32x4_t md[GRP];
-      R xv[GRP], dv[GRP];
+      R xv[GRP];
 #pragma unroll
-      for (int k = 0; k < GRP; ++k) md[k] = rec[wave][r][g0 + k];
+      for (int k = 0; k < GRP; ++k) md[k] = rec[wave][r][gg + k];
 #pragma unroll
-      for (int k = 0; k < GRP; ++k) {
-        const int64_t t = __float_as_int(md[k][0]);
-        xv[k] = *(const R*)(xs + t * a.d);
-        dv[k] = *(const R*)(dys + t * a.d);
-      }
+      for (int k = 0; k < GRP; ++k) xv[k] = *(const R*)(src + (int64_t)__float_as_int(md[k][0]) * a.d);
 #pragma unroll
       for (int k = 0; k < GRP; ++k) {
-        float fx[EPL], fd[EPL];
+        float fx[EPL];
         V::cvt(xv[k], fx);
-        V::cvt(dv[k], fd);
+        const float w0 = SIDE == 0 ? md[k][1] : md[k][3];
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-          ag[e] = fmaf(md[k][1], fx[e], ag[e]);
-          if (GATED) au[e] = fmaf(md[k][2], fx[e], au[e]);
-          ad[e] = fmaf(md[k][3], fd[e], ad[e]);
+          g0[e] = fmaf(w0, fx[e], g0[e]);
+          if (TWO) g1[e] = fmaf(md[k][2], fx[e], g1[e]);
         }
       }
     }
@@ -449,9 +447,8 @@ __global__ __launch_bounds__(256) void dw_sparse_kernel(BwdArgs a) {
   if (ok) {
 #pragma unroll
     for (int e = 0; e < EPL; e += 4) {
-      *(f32x4_t*)(a.dwg + ro + e) = f32x4_t{ag[e], ag[e + 1], ag[e + 2], ag[e + 3]};
-      if (GATED) *(f32x4_t*)(a.dwu + ro + e) = f32x4_t{au[e], au[e + 1], au[e + 2], au[e + 3]};
-      *(f32x4_t*)(a.dwd + ro + e) = f32x4_t{ad[e], ad[e + 1], ad[e + 2], ad[e + 3]};
+      *(f32x4_t*)(out0 + ro + e) = f32x4_t{g0[e], g0[e + 1], g0[e + 2], g0[e + 3]};
+      if (TWO) *(f32x4_t*)(out1 + ro + e) = f32x4_t{g1[e], g1[e + 1], g1[e + 2], g1[e + 3]};
     }
   }
 }
@@ -661,12 +658,19 @@ hipError_t launch_bwd_t(const BwdArgs& a, bool gated, int which, hipStream_t st)
     if (gated) hipLaunchKernelGGL((dx_sparse_kernel<E, XSW, true, 4>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((dx_sparse_kernel<E, XSW, false, 4>), grid, dim3(256), 0, st, a);
   } else {
-    // 128-column slices (bf16: four neurons per wave)
-    constexpr int DSW = 128;
+    // 256-column slices (bf16: two neurons per wave): one gathered operand
+    // per launch keeps an XCD's slice of it (T x 512 bytes) near its L2
+    constexpr int DSW = 256;
     constexpr int DRPW = 64 / (DSW * (int)sizeof(E) / 16);
     const dim3 grid((unsigned)((a.d / DSW) * ((a.F + 4 * DRPW - 1) / (4 * DRPW))));
-    if (gated) hipLaunchKernelGGL((dw_sparse_kernel<E, DSW, true, 4>), grid, dim3(256), 0, st, a);
-    else hipLaunchKernelGGL((dw_sparse_kernel<E, DSW, false, 4>), grid, dim3(256), 0, st, a);
+    // x side (dW_g, dW_u), then dy side (dW_d): one gathered operand per launch
+    if (gated) {
+      hipLaunchKernelGGL((dw_sparse_kernel<E, DSW, true, kDwGrp, 0>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((dw_sparse_kernel<E, DSW, true, kDwGrp, 1>), grid, dim3(256), 0, st, a);
+    } else {
+      hipLaunchKernelGGL((dw_sparse_kernel<E, DSW, false, kDwGrp, 0>), grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((dw_sparse_kernel<E, DSW, false, kDwGrp, 1>), grid, dim3(256), 0, st, a);
+    }
   }
   return hipGetLastError();
 }
