@@ -38,11 +38,13 @@ constexpr int kGroupRows = 8;   // row tiles per group of the tile order
 // Ring geometry: a slot holds an A tile and a B tile (16 KB), or with a
 // dual A (hi and lo parts) two A tiles and a B tile (24 KB); four slots,
 // or three with a dual A, so that two workgroups fit a CU's LDS. LPS is
-// the copies (or B register loads) per wave and stage.
-template <bool DUAL> struct Ring {
+// the memory operations per wave and stage: A copies (two, or four with a
+// dual A), then two B copies or, for an n-contiguous B, eight B loads.
+template <bool DUAL, bool BT> struct Ring {
   static constexpr int SLOT = ((DUAL ? 2 : 1) * BM + BN) * ROWB;
   static constexpr int NSLOT = DUAL ? 3 : 4;
-  static constexpr int LPS = DUAL ? 6 : 4;
+  static constexpr int LPS = (DUAL ? 4 : 2) + (BT ? 8 : 2);
+  static_assert((NSLOT - 1) * LPS <= 63, "vmcnt range");
 };
 
 constexpr int wait_imm(int vm, int lgkm) {
@@ -69,9 +71,9 @@ __device__ __forceinline__ int small_splits(const GemmArgs& g, int mt, int ntl) 
 
 template <bool BT, int EPI, bool DUAL>
 __global__ __launch_bounds__(NT, 2) void gemm_small_kernel(GemmArgs g) {
-  constexpr int SLOT = Ring<DUAL>::SLOT;
-  constexpr int NSLOT = Ring<DUAL>::NSLOT;
-  constexpr int LPS = Ring<DUAL>::LPS;
+  constexpr int SLOT = Ring<DUAL, BT>::SLOT;
+  constexpr int NSLOT = Ring<DUAL, BT>::NSLOT;
+  constexpr int LPS = Ring<DUAL, BT>::LPS;
   __shared__ __align__(16) char smem[NSLOT * SLOT];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -105,10 +107,11 @@ __global__ __launch_bounds__(NT, 2) void gemm_small_kernel(GemmArgs g) {
   // direct-to-LDS copy lane layout: 16 rows x 64 bytes per instruction
   const int lr = lane >> 2;
   const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  // n-contiguous B: thread (bg, bkg) loads k rows 2 bkg, 2 bkg + 1 of
-  // columns 8 bg .. 8 bg + 7
-  const int bg = tid & 15;
-  const int bkg = tid >> 4;
+  // n-contiguous B: lane l of wave w loads k rows 8 w .. 8 w + 7 of
+  // columns 2 l and 2 l + 1 (4 bytes each: a wave reads 256 contiguous
+  // bytes of a k row per load) and writes them as 16 bytes of each
+  // column's LDS row (16 lanes of a store touch 8 distinct 16-byte bank
+  // groups: at most two-way conflicts)
 
   for (int L = xcd * per + blockIdx.x / NXCD; L < t_end; L += G8) {
     // the splits of a tile are consecutive, then up to 8 row tiles of one
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_small_kernel(GemmArgs g) {
       for (int i = 0; i < 2; ++i)
         b_src[i] = Bb + (int64_t)(nb0 + wave * 32 + i * 16 + lr) * ldb_b + lchunk * 16;
     }
-    u32x4_t rbs[NSLOT][2];   // n-contiguous B stages in flight
+    uint32_t rbs[NSLOT][8];   // n-contiguous B stages in flight
 
     auto kb_of = [&](int kt) {
       int64_t kb = (int64_t)(kt0 + kt) * BK;
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_small_kernel(GemmArgs g) {
       return kb;
     };
     // stage kt (relative to the split) into slot `slot` (B registers into set `set`)
-    auto issue = [&](int kt, int slot, u32x4_t (&rb)[2]) {
+    auto issue = [&](int kt, int slot, uint32_t (&rb)[8]) {
       char* base = smem + slot * SLOT;
       // A column of the stage: with a dual A the hi part of the second
       // operand (k >= kcat) starts alo after the first's
@@ -166,12 +169,13 @@ __global__ __launch_bounds__(NT, 2) void gemm_small_kernel(GemmArgs g) {
       if constexpr (BT) {
         const char* bs =
             g.kcat > 0 && (int64_t)(kt0 + kt) * BK >= g.kcat ? (const char*)g.B1 : Bb;
-        const char* p = bs + (kb + 2 * bkg) * ldb_b + (int64_t)(nb0 + 8 * bg) * 2;
+        const char* p = bs + (kb + 8 * wave) * ldb_b + (int64_t)(nb0 + 2 * lane) * 2;
         // issued as opaque loads: the compiler's own wait insertion loses
         // count of these across the unrolled loop's back edge and drains
         // every load in flight; the explicit waits below cover them
-        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(rb[0]) : "v"(p));
-        asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(rb[1]) : "v"(p + ldb_b));
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          asm volatile("global_load_dword %0, %1, off" : "=v"(rb[r]) : "v"(p + r * ldb_b));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -192,17 +196,18 @@ __global__ __launch_bounds__(NT, 2) void gemm_small_kernel(GemmArgs g) {
                                            0, 0);
       }
     };
-    // k rows (2 bkg, 2 bkg + 1) x 8 columns -> 8 LDS rows of B, 4 bytes each
-    auto store_b = [&](int slot, const u32x4_t (&rb)[2]) {
+    // 8 k rows x columns (2 l, 2 l + 1) -> chunk w of LDS rows 2 l, 2 l + 1
+    auto store_b = [&](int slot, const uint32_t (&rb)[8]) {
       if constexpr (BT) {
         char* bbase = smem + slot * SLOT + BM * ROWB;
+        u32x4_t lo, hi;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const uint32_t r0 = rb[0][c >> 1];
-          const uint32_t r1 = rb[1][c >> 1];
-          const uint32_t v = (c & 1) ? ((r0 >> 16) | (r1 & 0xFFFF0000u)) : ((r0 & 0xFFFFu) | (r1 << 16));
-          *(uint32_t*)(bbase + rlds_off(8 * bg + c, bkg >> 2) + (bkg & 3) * 4) = v;
+        for (int q = 0; q < 4; ++q) {
+          lo[q] = (rb[2 * q] & 0xFFFFu) | (rb[2 * q + 1] << 16);
+          hi[q] = (rb[2 * q] >> 16) | (rb[2 * q + 1] & 0xFFFF0000u);
         }
+        *(u32x4_t*)(bbase + rlds_off(2 * lane, wave)) = lo;
+        *(u32x4_t*)(bbase + rlds_off(2 * lane + 1, wave)) = hi;
       }
     };
 
@@ -320,7 +325,9 @@ __global__ __launch_bounds__(NT, 2) void gemm_small_kernel(GemmArgs g) {
       // they land before any of those registers is given to another value
       __builtin_amdgcn_s_waitcnt(wait_imm(0, 15));
 #pragma unroll
-      for (int u = 0; u < NSLOT; ++u) asm volatile("" ::"v"(rbs[u][0]), "v"(rbs[u][1]));
+      for (int u = 0; u < NSLOT; ++u)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) asm volatile("" ::"v"(rbs[u][r]));
     }
     }
 
