@@ -459,9 +459,9 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   const int64_t cap = train ? hy->max_backup : T;
   {
     ProfScope ps(h, SFFN_K_FLAGS, stream);
-    e = launch_backup_list(ea.bk, T, brow, cap, n_bk, train ? hy->slot : nullptr, stream);
-    if (e == hipSuccess && train)
-      e = launch_backup_list(t.row_flag, T, t.flagged, T, t.n_flagged, nullptr, stream);
+    const ListArgs lb = {ea.bk, brow, cap, n_bk, train ? hy->slot : nullptr};
+    const ListArgs lf = {t.row_flag, t.flagged, T, t.n_flagged, nullptr};
+    e = launch_backup_list(lb, train ? &lf : nullptr, T, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "backup list");
 
@@ -741,7 +741,8 @@ sffn_status sffn_hybrid_compact(sffn_handle* h, const sffn_twell* tw, const floa
   if (e != hipSuccess) return hip_fail(h, e, "row compaction");
   {
     ProfScope ps(h, SFFN_K_FLAGS, stream);
-    e = launch_backup_list(ea.bk, T, hy->brow, hy->max_backup, hy->n_backup, hy->slot, stream);
+    const ListArgs lb = {ea.bk, hy->brow, hy->max_backup, hy->n_backup, hy->slot};
+    e = launch_backup_list(lb, nullptr, T, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "backup list");
   if (z && hy->max_backup > 0) {

@@ -486,12 +486,17 @@ __global__ __launch_bounds__(256) void gather_stack_kernel(const E* __restrict__
 // both operands of the dW GEMMs are k-contiguous. A workgroup moves 64 rows
 // x 64 columns through LDS: 16-byte loads along the rows, 16-byte stores
 // along the columns.
-__global__ __launch_bounds__(256) void gather_stack_t_kernel(const uint16_t* __restrict__ src,
+__global__ __launch_bounds__(256) void gather_stack_t_kernel(const uint16_t* __restrict__ src0,
+                                                             const uint16_t* __restrict__ src1,
                                                              int d, const int32_t* __restrict__ brow,
                                                              const int32_t* __restrict__ n, int cap,
-                                                             uint16_t* __restrict__ dst,
+                                                             uint16_t* __restrict__ dst0,
+                                                             uint16_t* __restrict__ dst1,
                                                              int64_t ldt) {
   __shared__ __align__(16) uint16_t tile[64][72];   // [column][row]
+  // blockIdx.y: x (0) or dy (1)
+  const uint16_t* src = blockIdx.y ? src1 : src0;
+  uint16_t* dst = blockIdx.y ? dst1 : dst0;
   const int R = device_rows(n, cap);
   const int Rp = (R + 63) / 64 * 64;
   const int tid = threadIdx.x;
@@ -552,7 +557,7 @@ __global__ __launch_bounds__(256) void backup_grad_kernel(BwdArgs a) {
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int r0 = (tile / ntj) * 64;
     const int j0 = (tile - (tile / ntj) * ntj) * 64;
-#pragma unroll 2
+#pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int rl = p * 8 + g;
       const int r = r0 + rl;
@@ -723,10 +728,9 @@ hipError_t launch_transpose(const BwdArgs& a, hipStream_t s) {
 hipError_t launch_backup_prep(Dtype dt, bool gated, const BwdArgs& a, hipStream_t s) {
   const dim3 g(1024), b(256);
   if (dt == kBF16) {
-    hipLaunchKernelGGL(gather_stack_t_kernel, g, b, 0, s, (const uint16_t*)a.x, a.d, a.brow,
-                       a.n_backup, a.cap, (uint16_t*)a.xb, a.ldt);
-    hipLaunchKernelGGL(gather_stack_t_kernel, g, b, 0, s, (const uint16_t*)a.dy, a.d, a.brow,
-                       a.n_backup, a.cap, (uint16_t*)a.dyb, a.ldt);
+    hipLaunchKernelGGL(gather_stack_t_kernel, dim3(512, 2), b, 0, s, (const uint16_t*)a.x,
+                       (const uint16_t*)a.dy, a.d, a.brow, a.n_backup, a.cap, (uint16_t*)a.xb,
+                       (uint16_t*)a.dyb, a.ldt);
   } else {
     hipLaunchKernelGGL(gather_stack_kernel<float>, g, b, 0, s, (const float*)a.x, a.d, a.brow,
                        a.n_backup, a.cap, (float*)a.xb);

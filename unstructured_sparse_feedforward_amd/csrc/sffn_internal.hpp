@@ -231,9 +231,16 @@ struct EllArgs {
 hipError_t launch_rows(const EllArgs& a, hipStream_t s);
 // Ascending list of the rows with bk[t] != 0 (the first cap of them), their
 // true count and (nullable) every row's backup slot (-1 for ELL rows).
-// One workgroup; bk must be 16-byte aligned.
-hipError_t launch_backup_list(const uint8_t* bk, int64_t T, int32_t* brow, int64_t cap,
-                              int32_t* n_backup, int32_t* slot, hipStream_t s);
+// One workgroup per list (two lists, l1 non-null, in one launch); bk must
+// be 16-byte aligned.
+struct ListArgs {
+  const uint8_t* bk;
+  int32_t* brow;
+  int64_t cap;
+  int32_t* n;
+  int32_t* slot;
+};
+hipError_t launch_backup_list(const ListArgs& l0, const ListArgs* l1, int64_t T, hipStream_t s);
 
 // The number of rows of a GEMM whose M lives on the device.
 __device__ __forceinline__ int device_rows(const int32_t* m_dev, int m_cap) {

@@ -106,11 +106,14 @@ __global__ __launch_bounds__(256) void rows_kernel(EllArgs a) {
 // One workgroup: list the backup rows in ascending order (the first cap of
 // them), their true count and, when requested, every row's backup slot
 // (-1 for ELL rows).
-__global__ __launch_bounds__(1024) void backup_list_kernel(const uint8_t* __restrict__ bk,
-                                                           int64_t T, int32_t* __restrict__ brow,
-                                                           int64_t cap,
-                                                           int32_t* __restrict__ n_backup,
-                                                           int32_t* __restrict__ slot) {
+__global__ __launch_bounds__(1024) void backup_list_kernel(ListArgs l0, ListArgs l1, int64_t T) {
+  // workgroup b builds list b (two lists in one launch in training)
+  const ListArgs& L = blockIdx.x ? l1 : l0;
+  const uint8_t* __restrict__ bk = L.bk;
+  int32_t* __restrict__ brow = L.brow;
+  const int64_t cap = L.cap;
+  int32_t* __restrict__ n_backup = L.n;
+  int32_t* __restrict__ slot = L.slot;
   constexpr int RPT = 16;
   __shared__ int wsum[16];
   const int tid = threadIdx.x;
@@ -405,10 +408,10 @@ hipError_t launch_rows(const EllArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_backup_list(const uint8_t* bk, int64_t T, int32_t* brow, int64_t cap,
-                              int32_t* n_backup, int32_t* slot, hipStream_t s) {
-  hipLaunchKernelGGL(backup_list_kernel, dim3(1), dim3(1024), 0, s, bk, T, brow, cap, n_backup,
-                     slot);
+hipError_t launch_backup_list(const ListArgs& l0, const ListArgs* l1, int64_t T, hipStream_t s) {
+  const ListArgs none = {};
+  hipLaunchKernelGGL(backup_list_kernel, dim3(l1 ? 2 : 1), dim3(1024), 0, s, l0, l1 ? *l1 : none,
+                     T);
   return hipGetLastError();
 }
 
