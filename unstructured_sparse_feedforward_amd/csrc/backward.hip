@@ -293,7 +293,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
 // units holding the neuron), stored as the record the dW sums read: {row,
 // dZ, dU, h}. The neuron ids are loaded first, then the places are taken
 // in unit order (a wave's LDS operations complete in issue order), then
-// the records are moved, eight units' loads at a time.
+// the records are moved, the loads of all 32 units issued together.
 __global__ __launch_bounds__(64) void block_place_kernel(BwdArgs a, int cpr, int nunits, int F4,
                                                          const int32_t* __restrict__ off) {
   extern __shared__ uint32_t c4[];
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(64) void block_place_kernel(BwdArgs a, int cpr, int
     }
   }
   const int32_t* offb = off + (int64_t)blockIdx.x * F4 * 4;
-  constexpr int G = 8;
+  constexpr int G = 32;
 #pragma unroll
   for (int g0 = 0; g0 < kUnitsPerBlock; g0 += G) {
     int pos[G];
