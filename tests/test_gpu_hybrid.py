@@ -144,6 +144,8 @@ def _grads_ref(inp, l1):
 @pytest.mark.parametrize("w,T,seed,l1", [
     (wl.TRAIN_HYBRID, 256, 47, 0.0),
     (wl.TRAIN_HYBRID, 512, 57, 0.0),
+    # 264 rows: a last block of 8 slot units in the neuron-major grouping
+    (wl.TRAIN_HYBRID, 264, 102, 0.0),
     (wl.TRAIN_HYBRID, 256, 47, 0.05),
     (wl.TRAIN_HYBRID.replace(gated=False, F=8192, nnz=40, name="train_nongated"), 256, 55, 0.0),
 ])
