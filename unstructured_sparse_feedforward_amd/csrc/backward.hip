@@ -13,10 +13,10 @@
 // The partial dot products dy_t . W_d[j] reuse the sliced phase-1 kernel
 // (sparse.hip); a row pass sums them into dZ, dU per slot. dx is
 // accumulated per (row, d slice) like the forward's down projection. dW
-// needs the slots grouped by neuron: integer-atomic counts, an exclusive
-// scan, an atomic fill and a per-neuron sort by slot index give every
-// neuron its slots in ascending row order, so the float sums of dW are
-// accumulated in a fixed order (no float atomics). Rows on the dense
+// needs the slots grouped by neuron: a counting sort over blocks of slot
+// units (per-block counts, per-neuron prefixes, in-order placement) gives
+// every neuron its slots in ascending row order, so the float sums of dW
+// are accumulated in a fixed order (no float atomics). Rows on the dense
 // backup path are handled by GEMMs (api.hip) before the dW sums, which
 // then add to the backup rows' stored products.
 #include "sffn_internal.hpp"
