@@ -12,16 +12,18 @@
 // same B), or, with alo > 0, A holds the lo part alo columns after the hi
 // part and every B stage is read once for both (twice the MFMAs).
 //
-// 128 x 128 tiles, 4 waves of 64 x 64 (2 x 2 v_mfma_f32_32x32x16_bf16).
-// K streams through a ring of NSLOT LDS slots of 32 k each, NSLOT - 1
-// stages in flight: with only a few hundred rows the work is a stream of
-// weight columns, and the loads' latency, not the MFMAs, sets the pace.
-// The registers of an n-contiguous B stage are held for NSLOT - 1 stages
-// (one register set per slot, selected at compile time by unrolling the
-// k loop NSLOT times) before they are written into LDS. K is split over
-// workgroups (the device chooses the split so that there are about
-// split_target tiles); partials go to part[S][Mpad][N] for the reduce or
-// combine kernels of gemm.hip, which use the same tiling.
+// 128 x 128 tiles, 4 waves of 64 x 64 (2 x 2 v_mfma_f32_32x32x16_bf16),
+// two workgroups per CU. K streams through a ring of NSLOT LDS slots of
+// 32 k each, NSLOT - 1 stages in flight: with only a few hundred rows the
+// work is a stream of operand tiles, and the rate at which a CU's copies
+// arrive from L2 (about the same with one or two workgroups per CU, or
+// with a deeper ring), not the MFMAs, sets the pace. The registers of an
+// n-contiguous B stage are held for NSLOT - 1 stages (one register set per
+// slot, selected at compile time by unrolling the k loop NSLOT times)
+// before they are written into LDS. K may come from the device (backup
+// rows). K is split over workgroups (the device chooses the split so that
+// there are about split_target tiles); partials go to part[S][Mpad][N] for
+// the reduce or combine kernels of gemm.hip, which use the same tiling.
 #include "sffn_internal.hpp"
 
 namespace sffn {
