@@ -21,8 +21,12 @@
  *   - Every call returns an sffn_status and never aborts or throws.
  *   - Argument errors (null or misaligned pointers, bad sizes) are found on
  *     the host before anything is enqueued and return SFFN_E_ARG.
- *   - All device work is enqueued on the caller's stream; no call
- *     synchronises the stream except sffn_check().
+ *   - All device work is ordered on the caller's stream; no call
+ *     synchronises the stream except sffn_check() and sffn_hybrid_check().
+ *     sffn_backward forks part of its work to a second stream of the handle
+ *     (created on first use, default priority) and joins it back through
+ *     events before it returns; work enqueued on the caller's stream after
+ *     the call sees all of its results.
  *   - Pointers are device pointers unless stated; every array is
  *     caller-owned and must be 16-byte aligned. The library never frees
  *     caller memory.
@@ -165,8 +169,9 @@ typedef struct sffn_hybrid {
  * (SFFN_E_ARG / SFFN_E_UNSUPPORTED) before touching the device; returns
  * SFFN_E_UNSUPPORTED when the current device is not gfx950 and SFFN_E_HIP
  * when no device can be queried. Allocates host memory only (per-kernel
- * timing events are created on demand). Calls on the handle must be made
- * with the same device current. */
+ * timing events and the backward's second stream and its two events are
+ * created on demand, on the device current at that call). Calls on the
+ * handle must be made with the same device current. */
 sffn_status sffn_create(const sffn_desc* desc, sffn_handle** out);
 
 /* Destroy a handle (NULL is allowed). */
@@ -252,7 +257,9 @@ sffn_status sffn_forward_train(sffn_handle* h, const void* x, const void* w_gate
  * dw_gate, dw_up (NULL iff non-gated), dw_down [F, d] neuron-major, all
  * float32; rows of never-active neurons are zero. dy has the descriptor's
  * dtype. The workspace is sized for up to T backup rows; rows from slot
- * max_backup on are not processed (see sffn_hybrid_check).
+ * max_backup on are not processed (see sffn_hybrid_check). With backup
+ * rows the neuron-major regrouping runs on the handle's second stream,
+ * beside the backup rows' dW products, joined before the dW sums.
  */
 sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, const void* w_up,
                           const void* w_down, const sffn_hybrid* hy, const void* dy, int64_t T,

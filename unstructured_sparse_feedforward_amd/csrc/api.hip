@@ -28,6 +28,10 @@ struct sffn_handle {
   std::vector<sffn_prof_rec> recs;
   double tot_ms[SFFN_K_COUNT] = {};
   int32_t launches[SFFN_K_COUNT] = {};
+  // the backward's second stream (created on first use): the neuron-major
+  // grouping runs beside the backup rows' dW products, which leave CUs free
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
 };
 
 namespace {
@@ -245,6 +249,9 @@ void sffn_destroy(sffn_handle* h) {
     (void)hipEventDestroy(r.b);
   }
   for (auto e : h->pool) (void)hipEventDestroy(e);
+  if (h->fork) (void)hipEventDestroy(h->fork);
+  if (h->join) (void)hipEventDestroy(h->join);
+  if (h->side) (void)hipStreamDestroy(h->side);
   delete h;
 }
 
@@ -860,6 +867,7 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
   if (e != hipSuccess) return hip_fail(h, e, "backward dx");
   // 3. backup rows, densely: dH = dy W_d^T, then dZ/dU, dx rows and their
   // dW products (zeros when no row took the backup path)
+  bool transposed = false;
   if (cap > 0) {
     ProfScope ps(h, SFFN_K_BWD_DENSE, stream);
     const bool split = dt == kBF16;
@@ -937,6 +945,23 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
       if (e == hipSuccess) e = launch_splitk_reduce(f, dx, D.d, stream);
       if (e != hipSuccess) return hip_fail(h, e, "backup dx");
     }
+    // the neuron-major grouping (needs only the slot records) on the second
+    // stream, beside the dW products
+    if (!h->side) {
+      e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&h->join, hipEventDisableTiming);
+      if (e != hipSuccess) return hip_fail(h, e, "second stream");
+    }
+    e = hipEventRecord(h->fork, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
+    if (e == hipSuccess) {
+      ProfScope ps(h, SFFN_K_BWD_TRANSPOSE, h->side);
+      e = launch_transpose(ba, h->side);
+    }
+    if (e == hipSuccess) e = hipEventRecord(h->join, h->side);
+    if (e != hipSuccess) return hip_fail(h, e, "backward transpose");
+    transposed = true;
     // dW = (dZ, dU, H)^T (x, x, dy) over the backup rows
     for (int pass = 0; pass < 3; ++pass) {
       if (pass == 1 && !gated) continue;
@@ -961,8 +986,11 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
       if (e != hipSuccess) return hip_fail(h, e, "backup dW");
     }
   }
-  // 4. slots grouped by neuron in ascending row order
-  {
+  // 4. slots grouped by neuron in ascending row order (with backup rows it
+  //    ran on the second stream beside their dW products: join it here)
+  if (transposed) {
+    e = hipStreamWaitEvent(stream, h->join, 0);
+  } else {
     ProfScope ps(h, SFFN_K_BWD_TRANSPOSE, stream);
     e = launch_transpose(ba, stream);
   }
