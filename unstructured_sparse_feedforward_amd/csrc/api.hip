@@ -862,7 +862,9 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
   // 2. dZ, dU per slot and dx of the ELL rows
   {
     ProfScope ps(h, SFFN_K_BWD_DX, stream);
-    e = launch_bwd_sparse(dt, gated, 0, ba, stream);
+    // with backup rows the dx sums of the ELL rows run later, on the
+    // second stream beside the dW products
+    e = launch_bwd_sparse(dt, gated, cap > 0 ? 2 : 0, ba, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "backward dx");
   // 3. backup rows, densely: dH = dy W_d^T, then dZ/dU, dx rows and their
@@ -955,6 +957,10 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
     }
     e = hipEventRecord(h->fork, stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
+    if (e == hipSuccess) {
+      ProfScope ps(h, SFFN_K_BWD_DX, h->side);
+      e = launch_bwd_sparse(dt, gated, 3, ba, h->side);
+    }
     if (e == hipSuccess) {
       ProfScope ps(h, SFFN_K_BWD_TRANSPOSE, h->side);
       e = launch_transpose(ba, h->side);

@@ -652,17 +652,20 @@ __global__ __launch_bounds__(256) void backup_grad_kernel(BwdArgs a) {
 
 template <typename E, int NS, int SW>
 hipError_t launch_bwd_t(const BwdArgs& a, bool gated, int which, hipStream_t st) {
-  if (which == 0) {
+  if (which == 0 || which == 2) {
     const dim3 rows((unsigned)((a.T + 3) / 4));
     if (gated) hipLaunchKernelGGL((dzu_kernel<NS, true>), rows, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((dzu_kernel<NS, false>), rows, dim3(256), 0, st, a);
+  }
+  if (which == 0 || which == 3) {
     // 128-column slices (bf16: four rows per wave)
     constexpr int XSW = 128;
     constexpr int XRPW = 64 / (XSW * (int)sizeof(E) / 16);
     const dim3 grid((unsigned)((a.d / XSW) * ((a.T + 4 * XRPW - 1) / (4 * XRPW))));
     if (gated) hipLaunchKernelGGL((dx_sparse_kernel<E, XSW, true, 4>), grid, dim3(256), 0, st, a);
     else hipLaunchKernelGGL((dx_sparse_kernel<E, XSW, false, 4>), grid, dim3(256), 0, st, a);
-  } else {
+  }
+  if (which == 1) {
     // 256-column slices (bf16: two neurons per wave): one gathered operand
     // per launch keeps an XCD's slice of it (T x 512 bytes) near its L2
     constexpr int DSW = 256;

@@ -321,7 +321,8 @@ struct BwdArgs {
   void* gh_t;
   int64_t ldt;
 };
-// which = 0: dZ/dU per slot and dx of the ELL rows; 1: dW of every neuron
+// which = 0: dZ/dU per slot and dx of the ELL rows (2: dZ/dU only, 3: dx
+// only); 1: dW of every neuron
 hipError_t launch_bwd_sparse(Dtype dt, bool gated, int which, const BwdArgs& a, hipStream_t s);
 hipError_t launch_transpose(const BwdArgs& a, hipStream_t s);
 // blocks of slot units of the transpose's counting sort (sizes thist, toff)
