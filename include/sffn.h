@@ -258,8 +258,9 @@ sffn_status sffn_forward_train(sffn_handle* h, const void* x, const void* w_gate
  * float32; rows of never-active neurons are zero. dy has the descriptor's
  * dtype. The workspace is sized for up to T backup rows; rows from slot
  * max_backup on are not processed (see sffn_hybrid_check). With backup
- * rows the neuron-major regrouping runs on the handle's second stream,
- * beside the backup rows' dW products, joined before the dW sums.
+ * rows the ELL rows' dx sums and the neuron-major regrouping run on the
+ * handle's second stream, beside the backup rows' dW products, joined
+ * before the dW sums.
  */
 sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, const void* w_up,
                           const void* w_down, const sffn_hybrid* hy, const void* dy, int64_t T,
