@@ -189,6 +189,34 @@ def test_backward_deterministic():
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
+def test_backward_same_with_kernel_timing_and_side_stream():
+    """With backup rows the backward forks the ELL rows' dx sums and the
+    neuron-major grouping to a second stream and joins it before the dW
+    sums. With per-kernel timing on (events recorded on both streams) and
+    on a non-default caller stream, every gradient is the same bit for bit
+    as a plain run on the default stream."""
+    w = wl.TRAIN_HYBRID
+    inp = wl.make_inputs(w, seed=61, T=512)
+    ffn = SparseFFN(w.d, w.F, gated=True, twell_cap=w.twell_cap, ell_cap=w.ell_cap,
+                    dtype=torch.bfloat16)
+    args = [dev(inp, k) for k in ("x", "w_gate", "w_up", "w_down")]
+    _, hy = ffn.forward_train(*args)
+    assert int(hy["n_backup"][0].item()) > 0
+    dy = dev(inp, "dy")
+    g1 = [t.clone() for t in ffn.backward(*args, hy, dy)]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ffn.profile(True)
+        g2 = [t.clone() for t in ffn.backward(*args, hy, dy)]
+        prof = ffn.profile_read()
+        ffn.profile(False)
+    torch.cuda.synchronize()
+    assert prof["bwd_dx"][1] >= 1 and prof["bwd_transpose"][1] == 1
+    for a, b in zip(g1, g2):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
 def test_backward_all_rows_backup():
     """K = 1 sends every row with more than one positive to the dense
     backup: the gradients come from the dense GEMM path alone."""
