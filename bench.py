@@ -323,6 +323,25 @@ def bench_forward(args, np, torch, SparseFFN, wl):
     traffic = measured_traffic(W0.name) if not stack else {}
     r_gate = roof("mfma", "gate_gemm_twell", flops * args.steps, prof, ["gate_gemm_twell"],
                   peak_mm, traffic.get("gate_gemm_twell"))
+    if not stack and W0.dtype == "bf16":
+        # context, not part of the path: the vendor bf16 GEMM (torch linear,
+        # hipBLASLt) on the gate's shape, plain output, no epilogue
+        x0, wg0 = layers[0]["args"][0], layers[0]["args"][1]
+        for _ in range(3):
+            torch.nn.functional.linear(x0, wg0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            torch.nn.functional.linear(x0, wg0)
+        e1.record()
+        torch.cuda.synchronize()
+        vms = e0.elapsed_time(e1) / args.steps
+        vflop = 2.0 * W0.T * W0.d * W0.F
+        r_gate["vendor_gemm_same_shape"] = {
+            "kernel": "torch.nn.functional.linear bf16 (hipBLASLt), bf16 output, no epilogue",
+            "avg_ms": vms, "achieved": vflop / (vms * 1e-3) / 1e12,
+            "frac": vflop / (vms * 1e-3) / 1e12 / peak_mm}
     # the sparse up/down projection is three kernels (per-slice partial dot
     # products, their sums h = a * u, the down projection); a launch of it
     # is one of each
