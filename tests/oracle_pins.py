@@ -125,6 +125,14 @@ def check_hybrid_golden(orc):
     assert np.array_equal(h2["ell_cnt"], e2["ell_cnt"])
     assert np.array_equal(h2["slot"], e2["slot"])
     assert np.array_equal(h2["brow"], e2["brow"])
+    # backup rows carry the dense A and U rows of their tokens
+    z = np.array(g["z"])
+    a = np.where(z > 0, z, 0.0)
+    u = np.array(g["u"])
+    for K, e in ((3, e3), (2, e2)):
+        hy = orc.hybrid_compact(tw, K, a, u)
+        assert np.array_equal(hy["bk_a"], np.array(e["bk_a"])), K
+        assert np.array_equal(hy["bk_u"], np.array(e["bk_u"])), K
 
 
 def check_hybrid_invariants(orc):
@@ -156,6 +164,14 @@ def check_hybrid_invariants(orc):
     hy = orc.hybrid_compact(tw, F, a)
     assert np.array_equal(hy["slot"] >= 0, tw["row_flag"])
     assert np.array_equal(orc.unpack_hybrid(hy, F), a)
+    # the backup's u rows are the given U rows of the backup tokens, at the
+    # same slots as their A rows (U independent of A here)
+    u = r.standard_normal((T, F))
+    for K in (0, 5):
+        hy = orc.hybrid_compact(orc.pack_twell(z, W, W), K, a, u)
+        for s_, t in enumerate(np.flatnonzero(nnz > K)):
+            assert np.array_equal(hy["bk_u"][s_], u[t])
+            assert np.array_equal(hy["bk_a"][s_], a[t])
 
 
 # --------------------------------------------------------------- dense layer
@@ -212,6 +228,38 @@ def check_bf16_rounding(orc):
     assert orc.round_bf16(np.array([1 + 2.0 ** -8]))[0] == 1.0
     assert orc.round_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == 1 + 2.0 ** -6
     assert orc.round_bf16(np.array([-(1 + 2.0 ** -8)]))[0] == -1.0
+
+
+def check_bf16_hidden_golden(orc):
+    """Hand-worked standard bf16 layer: H rounded once, ties to even."""
+    g = _golden("ffn_bf16_hidden_1x2x3.json")
+    y = orc.dense_ffn_bf16_hidden(np.array(g["x"]), np.array(g["w_gate"]),
+                                  np.array(g["w_up"]), np.array(g["w_down"]))
+    assert np.array_equal(y, np.array(g["y"]))
+
+
+def check_bf16_hidden_vs_torch(orc):
+    """Integer inputs keep every H exact in float32, so torch's own bf16
+    conversion of H (float32 -> bfloat16, round to nearest even) is exact
+    to compare against; H spans values well above 256, where bf16 drops
+    bits. Gated and non-gated."""
+    r = _rng(14)
+    for gated in (True, False):
+        x = r.integers(-4, 5, (9, 6)).astype(np.float64)
+        wg = r.integers(-4, 5, (6, 16)).astype(np.float64)
+        wu = r.integers(-9, 10, (6, 16)).astype(np.float64) if gated else None
+        wd = r.integers(-3, 4, (16, 6)).astype(np.float64)
+        y = orc.dense_ffn_bf16_hidden(x, wg, wu, wd)
+        tx = torch.from_numpy(x)
+        h = torch.relu(tx @ torch.from_numpy(wg))
+        if gated:
+            h = h * (tx @ torch.from_numpy(wu))
+        assert float(h.abs().max()) > 512 or not gated
+        hb = h.float().to(torch.bfloat16).double()
+        ref = (hb @ torch.from_numpy(wd)).numpy()
+        assert np.array_equal(y, ref)
+        # at least one H was changed by the rounding
+        assert gated is False or bool((hb != h).any())
 
 
 # --------------------------------------------------------------- sparse layer

@@ -36,6 +36,19 @@ MUTATIONS = [
      "return dict(dx=dx, dw_gate=(dz.T @ x).T[:, ::-1].copy(), dw_up=x.T @ du,"),
     ("bf16: 7 significant bits", "s = m * 256.0", "s = m * 128.0"),
     ("bf16: ties away", "r = np.round(s)", "r = np.floor(s + 0.5)"),
+    ("bf16 layer: no rounding", 'hb = round_bf16(it["h"])', 'hb = it["h"]'),
+    ("bf16 layer: rounds y", 'hb = round_bf16(it["h"])\n    return hb @ np.asarray(w_down, dtype=np.float64)',
+     'return round_bf16(it["h"] @ np.asarray(w_down, dtype=np.float64))'),
+    ("bf16 layer: rounds A instead of H", 'hb = round_bf16(it["h"])',
+     'hb = round_bf16(it["a"]) * (1.0 if it["u"] is None else it["u"])'),
+    ("bf16 layer: rounds A and U before the product", 'hb = round_bf16(it["h"])',
+     'hb = round_bf16(it["a"]) * (1.0 if it["u"] is None else round_bf16(it["u"]))'),
+    ("bf16 layer: rounds before the ReLU", 'hb = round_bf16(it["h"])',
+     'hb = relu(round_bf16(it["z"])) * (1.0 if it["u"] is None else it["u"])'),
+    ("hybrid: bk_u from A", 'out["bk_u"] = np.asarray(u_dense, dtype=np.float64)[brow]',
+     'out["bk_u"] = np.asarray(a_dense, dtype=np.float64)[brow]'),
+    ("hybrid: bk_u rows of the ELL rows", 'out["bk_u"] = np.asarray(u_dense, dtype=np.float64)[brow]',
+     'out["bk_u"] = np.asarray(u_dense, dtype=np.float64)[np.flatnonzero(slot < 0)[:len(brow)]]'),
 ]
 
 
