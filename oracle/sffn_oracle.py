@@ -239,7 +239,7 @@ def unpack_hybrid(hy, F, a_dense_rows=None):
 # backward
 # ---------------------------------------------------------------------------
 
-def backward(x, w_gate, w_up, w_down, dy, l1_coeff=0.0):
+def backward(x, w_gate, w_up, w_down, dy, l1_coeff=0.0, mask=None):
     """Gradients of the gated layer for upstream dy (matrix calculus).
 
     M = 1[Z > 0];  dH = dy W_d^T;  dU = dH * A;  dZ = dH * U * M + l1 * M
@@ -247,25 +247,36 @@ def backward(x, w_gate, w_up, w_down, dy, l1_coeff=0.0):
     Non-gated (w_up None): dA = dy W_2^T; dZ = dA * M + l1 * M;
     dx = dZ W_1^T; dW_1 = x^T dZ; dW_2 = A^T dy.
     The l1 term is the derivative of l1 * sum(A) through the ReLU mask.
+
+    ``mask`` (boolean [T, F]) fixes the active set M instead of Z > 0; then
+    A = Z * M and H = A * U. It serves a caller whose active set was decided
+    by a lower-precision Z: entries with Z within that precision of zero
+    may be active on one side and not on the other, and the gradients are
+    then compared on the same set.
     """
     x = np.asarray(x, dtype=np.float64)
     dy = np.asarray(dy, dtype=np.float64)
     wg = np.asarray(w_gate, dtype=np.float64)
     wd = np.asarray(w_down, dtype=np.float64)
     _, it = dense_ffn(x, w_gate, w_up, w_down)
-    m = (it["z"] > 0).astype(np.float64)
+    if mask is None:
+        m = (it["z"] > 0).astype(np.float64)
+        a = it["a"]
+    else:
+        m = np.asarray(mask, dtype=bool).astype(np.float64)
+        a = it["z"] * m
     dh = dy @ wd.T
     if w_up is None:
         dz = dh * m + l1_coeff * m
         dx = dz @ wg.T
         return dict(dx=dx, dw_gate=x.T @ dz, dw_up=None,
-                    dw_down=it["a"].T @ dy)
+                    dw_down=a.T @ dy)
     wu = np.asarray(w_up, dtype=np.float64)
-    du = dh * it["a"]
+    du = dh * a
     dz = dh * it["u"] * m + l1_coeff * m
     dx = dz @ wg.T + du @ wu.T
     return dict(dx=dx, dw_gate=x.T @ dz, dw_up=x.T @ du,
-                dw_down=it["h"].T @ dy)
+                dw_down=(a * it["u"]).T @ dy)
 
 
 def backward_sparse(x, w_gate, w_up, w_down, dy, hy, l1_coeff=0.0):

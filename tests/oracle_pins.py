@@ -340,6 +340,37 @@ def check_backward_vs_autograd(orc):
                 assert np.allclose(gr["dw_up"], twu.grad.numpy(), rtol=1e-12, atol=1e-12)
 
 
+def check_backward_given_mask_vs_autograd(orc):
+    """A fixed active set M: the layer with A = Z * M (M constant) under
+    torch autograd; M = 1[Z > 0] reproduces the plain backward exactly."""
+    r = _rng(15)
+    for gated in (True, False):
+        x, wg, wu, wd = _rand_layer(r, 6, 5, 11, gated)
+        dy = r.standard_normal((6, 5))
+        z = x @ wg
+        assert np.array_equal(orc.backward(x, wg, wu, wd, dy, 0.2, mask=z > 0)["dx"],
+                              orc.backward(x, wg, wu, wd, dy, 0.2)["dx"])
+        # a mask that disagrees with Z > 0 on a third of the entries
+        m = (z > 0) ^ (r.random(z.shape) < 0.33)
+        gr = orc.backward(x, wg, wu, wd, dy, l1_coeff=0.2, mask=m)
+        tx = torch.tensor(x, requires_grad=True)
+        twg = torch.tensor(wg, requires_grad=True)
+        twd = torch.tensor(wd, requires_grad=True)
+        a = (tx @ twg) * torch.from_numpy(m.astype(np.float64))
+        if gated:
+            twu = torch.tensor(wu, requires_grad=True)
+            h = a * (tx @ twu)
+        else:
+            h = a
+        loss = ((h @ twd) * torch.from_numpy(dy)).sum() + 0.2 * a.sum()
+        loss.backward()
+        assert np.allclose(gr["dx"], tx.grad.numpy(), rtol=1e-12, atol=1e-12)
+        assert np.allclose(gr["dw_gate"], twg.grad.numpy(), rtol=1e-12, atol=1e-12)
+        assert np.allclose(gr["dw_down"], twd.grad.numpy(), rtol=1e-12, atol=1e-12)
+        if gated:
+            assert np.allclose(gr["dw_up"], twu.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
 def check_backward_finite_differences(orc):
     # first seeded draw whose pre-activations all keep clear of the kink
     for seed in range(11, 200):

@@ -31,7 +31,7 @@ MUTATIONS = [
     ("backward: dU W_u^T dropped", "dx = dz @ wg.T + du @ wu.T", "dx = dz @ wg.T"),
     ("backward: mask dropped", 'dz = dh * it["u"] * m + l1_coeff * m',
      'dz = dh * it["u"] + l1_coeff * m'),
-    ("backward: dW_d uses A", 'dw_down=it["h"].T @ dy)', 'dw_down=it["a"].T @ dy)'),
+    ("backward: dW_d uses A", 'dw_down=(a * it["u"]).T @ dy)', 'dw_down=a.T @ dy)'),
     ("backward: transposed dW_g", "return dict(dx=dx, dw_gate=x.T @ dz, dw_up=x.T @ du,",
      "return dict(dx=dx, dw_gate=(dz.T @ x).T[:, ::-1].copy(), dw_up=x.T @ du,"),
     ("bf16: 7 significant bits", "s = m * 256.0", "s = m * 128.0"),
@@ -45,6 +45,9 @@ MUTATIONS = [
      'hb = round_bf16(it["a"]) * (1.0 if it["u"] is None else round_bf16(it["u"]))'),
     ("bf16 layer: rounds before the ReLU", 'hb = round_bf16(it["h"])',
      'hb = relu(round_bf16(it["z"])) * (1.0 if it["u"] is None else it["u"])'),
+    ("backward: given mask ignored", "m = np.asarray(mask, dtype=bool).astype(np.float64)",
+     'm = (it["z"] > 0).astype(np.float64)'),
+    ("backward: given mask not applied to A", 'a = it["z"] * m', 'a = it["a"]'),
     ("hybrid: bk_u from A", 'out["bk_u"] = np.asarray(u_dense, dtype=np.float64)[brow]',
      'out["bk_u"] = np.asarray(a_dense, dtype=np.float64)[brow]'),
     ("hybrid: bk_u rows of the ELL rows", 'out["bk_u"] = np.asarray(u_dense, dtype=np.float64)[brow]',
