@@ -284,6 +284,7 @@ def bench_forward(args, np, torch, SparseFFN, wl):
         if n_cpu > 0:
             cpu_ms += oracle_forward_ms(inp, n_cpu, np)
         ffn = SparseFFN(W.d, W.F, gated=W.gated, twell_cap=W.twell_cap, tile=W.tile,
+                        ell_cap=W.ell_cap, dense_rows=W.dense_rows,
                         dtype=torch.bfloat16 if W.dtype == "bf16" else torch.float32)
         y = torch.empty((W.T, W.d), dtype=torch.float32, device="cuda")
         layers.append(dict(W=W, ffn=ffn, tw=ffn.new_twell(W.T), y=y, yd=torch.empty_like(y),
@@ -295,11 +296,18 @@ def bench_forward(args, np, torch, SparseFFN, wl):
 
     def sparse():
         for L in layers:
-            L["ffn"].forward(*L["args"], mode="sparse", tw=L["tw"], y=L["y"])
+            L["ffn"].forward(*L["args"], mode="sparse", tw=L["tw"], y=L["y"], check=False)
 
     def dense():
         for L in layers:
-            L["ffn"].forward(*L["args"], mode="dense", y=L["yd"])
+            L["ffn"].forward(*L["args"], mode="dense", y=L["yd"], check=False)
+
+    # one checked pass first: every routed row fits the dense path's capacity
+    for L in layers:
+        L["ffn"].forward(*L["args"], mode="sparse", tw=L["tw"], y=L["y"])
+        if L["ffn"].dense_rows != L["W"].dense_rows:
+            raise RuntimeError(f"{L['W'].name}: more rows took the dense path than "
+                               f"dense_rows = {L['W'].dense_rows}")
 
     ffns = [L["ffn"] for L in layers]
     # timed region: K sparse steps, then K dense steps on the same inputs
@@ -310,6 +318,8 @@ def bench_forward(args, np, torch, SparseFFN, wl):
     ms_p, _, prof = _timed(sparse, args.steps, 0, torch, ffns)
     _, _, prof_d = _timed(dense, args.steps, 0, torch, ffns)
     torch.cuda.synchronize()
+    for f in ffns:
+        f.check()
 
     gbytes, pairs, n_flag = 0.0, 0, 0
     for L in layers:
@@ -424,8 +434,9 @@ def per_layer_dispatch(layers, steps, torch):
 
     t_sp, t_de, modes = [], [], []
     for L in layers:
-        sp = time_one(lambda: L["ffn"].forward(*L["args"], mode="sparse", tw=L["tw"], y=L["y"]))
-        de = time_one(lambda: L["ffn"].forward(*L["args"], mode="dense", y=L["yd"]))
+        sp = time_one(lambda: L["ffn"].forward(*L["args"], mode="sparse", tw=L["tw"], y=L["y"],
+                                               check=False))
+        de = time_one(lambda: L["ffn"].forward(*L["args"], mode="dense", y=L["yd"], check=False))
         t_sp.append(sp)
         t_de.append(de)
         modes.append("sparse" if sp <= de else "dense")
@@ -433,9 +444,9 @@ def per_layer_dispatch(layers, steps, torch):
     def chosen():
         for L, m in zip(layers, modes):
             if m == "sparse":
-                L["ffn"].forward(*L["args"], mode="sparse", tw=L["tw"], y=L["y"])
+                L["ffn"].forward(*L["args"], mode="sparse", tw=L["tw"], y=L["y"], check=False)
             else:
-                L["ffn"].forward(*L["args"], mode="dense", y=L["yd"])
+                L["ffn"].forward(*L["args"], mode="dense", y=L["yd"], check=False)
 
     ms, _, _ = _timed(chosen, steps, 3, torch)
     T = layers[0]["W"].T
@@ -464,7 +475,7 @@ def bench_train(args, np, torch, SparseFFN, wl):
     del inp
     d, F, T = W.d, W.F, W.T
     ffn = SparseFFN(d, F, gated=True, twell_cap=W.twell_cap, ell_cap=W.ell_cap,
-                    dtype=torch.bfloat16)
+                    dense_rows=W.dense_rows, dtype=torch.bfloat16)
     hy = ffn.new_hybrid(T)
     tw = ffn.new_twell(T)
     y = torch.empty((T, d), dtype=torch.float32, device="cuda")
@@ -473,12 +484,16 @@ def bench_train(args, np, torch, SparseFFN, wl):
              torch.empty((F, d), **f32), torch.empty((F, d), **f32))
 
     def step():
-        ffn.forward_train(*a, hy=hy, tw=tw, y=y)
+        ffn.forward_train(*a, hy=hy, tw=tw, y=y, check=False)
         ffn.backward(*a, hy, dy, out=grads)
+
+    # one checked step first: the backup rows fit the Hybrid's capacity
+    ffn.forward_train(*a, hy=hy, tw=tw, y=y)
 
     ms, wall_ms, _ = _timed(step, args.steps, args.warmup, torch)
     ms_p, _, prof = _timed(step, args.steps, 0, torch, [ffn])
     torch.cuda.synchronize()
+    ffn.check()
     if ffn.hybrid_check(hy) != 0:
         raise RuntimeError("backup rows exceed the Hybrid's capacity")
     cnt = hy["ell_cnt"].cpu().numpy().astype(np.int64)

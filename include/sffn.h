@@ -19,6 +19,12 @@
  *
  * Conventions shared by every call:
  *   - Every call returns an sffn_status and never aborts or throws.
+ *   - Device memory the library needs per call is the caller's workspace;
+ *     its size (sffn_workspace_bytes) follows the sparse work: the ELL
+ *     capacity K and the dense path's row capacity R (desc.dense_rows),
+ *     never T x F. Data-dependent overflow of R (more rows on the dense
+ *     path than it holds) is not an argument error: the dense path's rows
+ *     are then not valid, and sffn_check() reports SFFN_E_CAPACITY.
  *   - Argument errors (null or misaligned pointers, bad sizes) are found on
  *     the host before anything is enqueued and return SFFN_E_ARG.
  *   - All device work is ordered on the caller's stream; no call
@@ -89,9 +95,20 @@ typedef struct sffn_handle sffn_handle;
  *   gated      1 gated, 0 non-gated (w_up unused and must be NULL)
  *   tile       TwELL tile width W; 128 is the one supported width
  *   twell_cap  C, TwELL slots per (row, tile); 1 <= C <= 128
- *   ell_cap    K, Hybrid ELL capacity (0 = inference only)
+ *   ell_cap    K, the ELL capacity of the sparse path: a row with more
+ *              than K active neurons, or with a TwELL tile holding more
+ *              than C, takes the dense path (the Hybrid routing rule,
+ *              "2. Methodology" A on the gist.science explainer). Training
+ *              needs K >= 1. At inference K = 0 means n_t * C (only rows
+ *              with an overflowing tile go dense); a K above n_t * C acts
+ *              as n_t * C.
  *   dtype      SFFN_BF16 (bf16 inputs, fp32 accumulation) or SFFN_F32
  *              (fp32 inputs and fp32 arithmetic throughout)
+ *   dense_rows R, the most rows one call computes on the dense path
+ *              (rows routed away from the ELL at inference, backup rows in
+ *              training); the workspace holds R dense rows. 0 means T
+ *              (every row may go dense; the workspace then grows as T x F).
+ *              More routed rows than R: see sffn_check.
  */
 typedef struct sffn_desc {
   int32_t d;
@@ -101,6 +118,7 @@ typedef struct sffn_desc {
   int32_t twell_cap;
   int32_t ell_cap;
   int32_t dtype;
+  int32_t dense_rows;
 } sffn_desc;
 
 /*
@@ -145,8 +163,9 @@ typedef struct sffn_twell {
  *   slot       [T]      int32    backup slot of the row, -1 for ELL rows
  *   brow       [max_backup] int32  backup rows in ascending order
  *   n_backup   [1]      int32    true number of backup rows (may exceed
- *                                max_backup: then the rows from slot
- *                                max_backup on were not computed and the
+ *                                the capacity R' = min(max_backup,
+ *                                desc.dense_rows): then the rows from
+ *                                slot R' on were not computed and the
  *                                result is invalid; see sffn_hybrid_check)
  *   bk_a       [max_backup, F] float32  ReLU(z) rows of the backup rows
  *   bk_u       [max_backup, F] float32  u rows of the backup rows (gated)
@@ -168,10 +187,12 @@ typedef struct sffn_hybrid {
 /* Create a handle for the current HIP device. Validates the descriptor
  * (SFFN_E_ARG / SFFN_E_UNSUPPORTED) before touching the device; returns
  * SFFN_E_UNSUPPORTED when the current device is not gfx950 and SFFN_E_HIP
- * when no device can be queried. Allocates host memory only (per-kernel
- * timing events and the backward's second stream and its two events are
- * created on demand, on the device current at that call). Calls on the
- * handle must be made with the same device current. */
+ * when no device can be queried. Allocates host memory and one 256-byte
+ * block of device memory (the handle's status and counter words, zeroed
+ * here; freed by sffn_destroy). Per-kernel timing events and the
+ * backward's second stream and its two events are created on demand, on
+ * the device current at that call. Calls on the handle must be made with
+ * the same device current. */
 sffn_status sffn_create(const sffn_desc* desc, sffn_handle** out);
 
 /* Destroy a handle (NULL is allowed). */
@@ -218,6 +239,12 @@ sffn_status sffn_gate_preact(sffn_handle* h, const void* x, const void* w_gate,
  *     two GEMMs, as in a standard bf16 feedforward. tw must be NULL.
  * w_up must be NULL iff the layer is non-gated. The workspace must hold
  * sffn_workspace_bytes(op = SFFN_OP_FORWARD_SPARSE or _DENSE).
+ * SPARSE: rows whose TwELL overflowed, or with more than K = desc.ell_cap
+ * active neurons, take the dense path; when more than desc.dense_rows rows
+ * do, the outputs of the dense path's rows are not valid (rows past the
+ * capacity are not computed, and the saved pre-activations of overflowing
+ * tiles may not all fit), the rows on the ELL path are unaffected, and the
+ * next sffn_check returns SFFN_E_CAPACITY.
  */
 sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate,
                          const void* w_up, const void* w_down, int64_t T,
@@ -256,8 +283,11 @@ sffn_status sffn_forward_train(sffn_handle* h, const void* x, const void* w_gate
  * backup rows run as dense GEMMs. Outputs are overwritten: dx [T, d],
  * dw_gate, dw_up (NULL iff non-gated), dw_down [F, d] neuron-major, all
  * float32; rows of never-active neurons are zero. dy has the descriptor's
- * dtype. The workspace is sized for up to T backup rows; rows from slot
- * max_backup on are not processed (see sffn_hybrid_check). With backup
+ * dtype. The workspace holds min(T, desc.dense_rows) backup rows; rows
+ * from slot min(max_backup, desc.dense_rows) on are not processed (the
+ * training forward has then already flagged the overflow: see
+ * sffn_hybrid_check and sffn_check). T = 0 stores zero weight gradients
+ * (no workspace needed). With backup
  * rows the ELL rows' dx sums and the neuron-major regrouping run on the
  * handle's second stream, beside the backup rows' dW products, joined
  * before the dW sums.
@@ -268,11 +298,15 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Synchronise the stream and return SFFN_E_CAPACITY when *hy->n_backup
- * exceeds hy->max_backup, else SFFN_OK (or SFFN_E_HIP). */
+ * exceeds hy->max_backup or desc.dense_rows (when that is set), else
+ * SFFN_OK (or SFFN_E_HIP). */
 sffn_status sffn_hybrid_check(sffn_handle* h, const sffn_hybrid* hy, hipStream_t stream);
 
 /* Synchronise the stream and report the first asynchronous error since
- * the last check (SFFN_E_HIP), else SFFN_OK. */
+ * the last check (SFFN_E_HIP); else SFFN_E_CAPACITY when a call since the
+ * last check routed more rows to the dense path than it could hold
+ * (desc.dense_rows, or max_backup in training), so that some rows were not
+ * computed; else SFFN_OK. The capacity report is cleared by the check. */
 sffn_status sffn_check(sffn_handle* h, hipStream_t stream);
 
 /*

@@ -26,9 +26,13 @@ def math_weights(inp):
 
 
 def layer(inp, **kw):
+    """The workload's layer handle, with its ELL and dense-row capacities
+    (as the benchmark builds it) unless overridden."""
     w = inp.wl
     return SparseFFN(w.d, w.F, gated=w.gated, twell_cap=kw.get("C", w.twell_cap),
-                     tile=w.tile, dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+                     tile=w.tile, ell_cap=kw.get("ell_cap", w.ell_cap),
+                     dense_rows=kw.get("dense_rows", w.dense_rows),
+                     dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32)
 
 
 def rel_fro(got, ref):

@@ -52,6 +52,7 @@ def _create(**kw):
     (dict(dtype=7), B.SFFN_E_ARG),
     (dict(twell_cap=0), B.SFFN_E_ARG),
     (dict(ell_cap=-1), B.SFFN_E_ARG),
+    (dict(dense_rows=-1), B.SFFN_E_ARG),
     (dict(tile=64), B.SFFN_E_UNSUPPORTED),
     (dict(d_ff=5600), B.SFFN_E_UNSUPPORTED),
     (dict(d_ff=65536), B.SFFN_E_UNSUPPORTED),

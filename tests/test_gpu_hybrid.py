@@ -354,3 +354,63 @@ def test_training_full_size_sampled():
     assert_close_bf16(dwg.cpu().numpy()[J], refJ["dw_gate"].T, "dw_gate neurons")
     assert_close_bf16(dwu.cpu().numpy()[J], refJ["dw_up"].T, "dw_up neurons")
     assert_close_bf16(dwd.cpu().numpy()[J], refJ["dw_down"], "dw_down neurons")
+
+
+def _plant_near_zero(inp, pairs):
+    """Make z[t, j] = x_t . W_g[:, j] vanish up to about 1e-10 for the
+    given (t, j) pairs (distinct j): the column's entries at the four
+    largest |x_t[k]| are cleared, then set one by one to the bf16 value
+    nearest to -(x_t . w without entry k) / x_t[k]; each step leaves at
+    most 2^-9 of the residual, so four steps bring it from O(1) to about
+    1e-10. The GPU's float32 sum of the same products errs by about 1e-7,
+    so the sign of such an entry, and with it the ReLU mask, is a coin
+    toss."""
+    x = inp.x.astype(np.float64)
+    for t, j in pairs:
+        w = inp.w_gate[j].astype(np.float64)
+        ks = np.argsort(-np.abs(x[t]))[:4]
+        w[ks] = 0.0
+        for k in ks:
+            rest = x[t] @ w - x[t, k] * w[k]
+            w[k] = float(wl.round_bf16(np.array([-rest / x[t, k]], dtype=np.float32))[0])
+        inp.w_gate[j] = w.astype(np.float32)
+
+
+def test_backward_mask_disagreement():
+    """Pre-activations planted within 1e-10 of zero make the GPU's ReLU mask
+    (decided on its float32 z) differ from the oracle's (float64) on some
+    entries. The masks may differ only where |z| < 1e-3, and the gradients
+    match the oracle's backward evaluated on the GPU's own mask (as saved
+    in the Hybrid: ELL slots and positive entries of the backup rows)."""
+    w = wl.TRAIN_HYBRID
+    T = 256
+    inp = wl.make_inputs(w, seed=71, T=T)
+    r = np.random.default_rng(5)
+    pairs = list(zip(r.choice(T, 96), r.choice(w.F, 96, replace=False)))
+    _plant_near_zero(inp, pairs)
+    wg, wu, wd = math_weights(inp)
+    x64 = inp.x.astype(np.float64)
+    z = x64 @ wg
+    assert max(abs(z[t, j]) for t, j in pairs) < 1e-8
+    ffn = SparseFFN(w.d, w.F, gated=True, twell_cap=w.twell_cap, ell_cap=w.ell_cap,
+                    dtype=torch.bfloat16)
+    args = [dev(inp, k) for k in ("x", "w_gate", "w_up", "w_down")]
+    y, hyd = ffn.forward_train(*args)
+    dx, dwg, dwu, dwd = ffn.backward(*args, hyd, dev(inp, "dy"))
+    hy = hybrid_np(hyd)
+    mask = np.zeros((T, w.F), dtype=bool)
+    for t in range(T):
+        if hy["slot"][t] >= 0:
+            mask[t] = hy["bk_a"][hy["slot"][t]] > 0
+        else:
+            mask[t, hy["ell_idx"][t, :hy["ell_cnt"][t]]] = True
+    diff = mask != (z > 0)
+    _print(f"  mask disagreements: {int(diff.sum())} (of {len(pairs)} planted)")
+    assert np.all(np.abs(z[diff]) < 1e-3)
+    assert diff.sum() >= 4
+    ref = oracle.backward(x64, wg, wu, wd, inp.dy.astype(np.float64), mask=mask)
+    assert_close_bf16(y.cpu().numpy(), oracle.dense_ffn(x64, wg, wu, wd)[0], "y")
+    assert_close_bf16(dx.cpu().numpy(), ref["dx"], "dx")
+    assert_close_bf16(dwg.cpu().numpy(), ref["dw_gate"].T, "dw_gate")
+    assert_close_bf16(dwu.cpu().numpy(), ref["dw_up"].T, "dw_up")
+    assert_close_bf16(dwd.cpu().numpy(), ref["dw_down"], "dw_down")

@@ -45,7 +45,7 @@ class SffnDesc(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("gated", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("twell_cap", ctypes.c_int32), ("ell_cap", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("dense_rows", ctypes.c_int32)]
 
 
 class SffnTwell(ctypes.Structure):
@@ -130,28 +130,61 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+DEFAULT_DENSE_ROWS = 1024
+
+
 class SparseFFN:
     """One feedforward layer's handle.
 
     Weights are passed to each call (neuron-major [F, d] for w_gate, w_up
     and w_down); x is [T, d]; outputs are float32.
+
+    ``ell_cap`` is the ELL capacity K of the sparse path (rows with more
+    active neurons, or with an overflowing TwELL tile, take the dense
+    path; 0 at inference = n_t * C). ``dense_rows`` is the most rows one
+    call computes on the dense path; the workspace holds that many dense
+    rows (0 = every row, a T x F workspace). When a call routes more rows
+    than that, the dense path's rows are not valid (the ELL rows are) and
+    ``sffn_check`` reports SFFN_E_CAPACITY. The calls here check by default
+    (``check=True``, one stream synchronisation per call): on that report
+    the handle is rebuilt with ``dense_rows = 0`` and the call is repeated,
+    so results are always complete. ``check=False`` skips the
+    synchronisation; the caller then runs :meth:`check` itself before
+    trusting the results.
     """
 
     def __init__(self, d: int, d_ff: int, gated: bool = True, twell_cap: int = 8,
-                 tile: int = 128, ell_cap: int = 0, dtype: torch.dtype = torch.bfloat16):
+                 tile: int = 128, ell_cap: int = 0, dtype: torch.dtype = torch.bfloat16,
+                 dense_rows: int = DEFAULT_DENSE_ROWS):
         self.lib = load_library()
         self.d, self.d_ff, self.gated = d, d_ff, gated
         self.tile, self.twell_cap, self.ell_cap = tile, twell_cap, ell_cap
         self.dtype = dtype
         self.n_t = d_ff // tile
-        self.desc = SffnDesc(d, d_ff, int(gated), tile, twell_cap, ell_cap,
-                             SFFN_BF16 if dtype == torch.bfloat16 else SFFN_F32)
+        self.h = None
+        self._ws: Dict[str, torch.Tensor] = {}
+        self._create(dense_rows)
+
+    def _create(self, dense_rows: int):
+        self.close()
+        self.dense_rows = dense_rows
+        self.desc = SffnDesc(self.d, self.d_ff, int(self.gated), self.tile, self.twell_cap,
+                             self.ell_cap,
+                             SFFN_BF16 if self.dtype == torch.bfloat16 else SFFN_F32,
+                             dense_rows)
         h = ctypes.c_void_p()
         st = self.lib.sffn_create(ctypes.byref(self.desc), ctypes.byref(h))
         if st != SFFN_OK:
             raise SffnError(st, f"sffn_create: {self.lib.sffn_status_string(st).decode()}")
         self.h = h
-        self._ws: Dict[str, torch.Tensor] = {}
+
+    def _grow(self) -> bool:
+        """After a capacity report: rebuild with a T-row dense capacity.
+        Returns False when the capacity was already unbounded."""
+        if self.dense_rows == 0:
+            return False
+        self._create(0)
+        return True
 
     def close(self):
         if getattr(self, "h", None):
@@ -168,6 +201,14 @@ class SparseFFN:
         if st != SFFN_OK:
             err = self.lib.sffn_last_error(self.h).decode()
             raise SffnError(st, f"{what}: {self.lib.sffn_status_string(st).decode()} {err}")
+
+    def _capacity_ok(self) -> bool:
+        """sffn_check: False on a capacity report, raise on other errors."""
+        st = self.lib.sffn_check(self.h, _stream())
+        if st == SFFN_E_CAPACITY:
+            return False
+        self._check(st, "sffn_check")
+        return True
 
     def workspace_bytes(self, T: int, op: int) -> int:
         n = ctypes.c_size_t()
@@ -224,28 +265,36 @@ class SparseFFN:
     def forward(self, x: torch.Tensor, w_gate: torch.Tensor, w_up: Optional[torch.Tensor],
                 w_down: torch.Tensor, mode: str = "sparse",
                 tw: Optional[Dict[str, torch.Tensor]] = None,
-                y: Optional[torch.Tensor] = None) -> torch.Tensor:
+                y: Optional[torch.Tensor] = None, check: bool = True) -> torch.Tensor:
         T = x.shape[0]
         if y is None:
             y = torch.empty((T, self.d), dtype=torch.float32, device=x.device)
         m = SFFN_SPARSE if mode == "sparse" else SFFN_DENSE
         op = SFFN_OP_FORWARD_SPARSE if m == SFFN_SPARSE else SFFN_OP_FORWARD_DENSE
-        ws, n = self.workspace(T, op, x.device)
-        s = ctypes.byref(self._tw_struct(tw)) if tw is not None else None
-        self._check(self.lib.sffn_forward(self.h, _ptr(x), _ptr(w_gate), _ptr(w_up),
-                                          _ptr(w_down), T, _ptr(y), s, m, ws, n, _stream()),
-                    "sffn_forward")
-        return y
+        while True:
+            ws, n = self.workspace(T, op, x.device)
+            s = ctypes.byref(self._tw_struct(tw)) if tw is not None else None
+            self._check(self.lib.sffn_forward(self.h, _ptr(x), _ptr(w_gate), _ptr(w_up),
+                                              _ptr(w_down), T, _ptr(y), s, m, ws, n,
+                                              _stream()), "sffn_forward")
+            if not check or self._capacity_ok() or not self._grow():
+                return y
 
     def check(self):
+        """sffn_check: raises SffnError (SFFN_E_CAPACITY when a call since the
+        last check routed more rows to the dense path than it holds)."""
         self._check(self.lib.sffn_check(self.h, _stream()), "sffn_check")
 
     # ------------------------------------------------------------ Hybrid
 
     def new_hybrid(self, T: int, max_backup: Optional[int] = None,
                    device="cuda") -> Dict[str, torch.Tensor]:
+        """Hybrid buffers; ``max_backup`` defaults to the handle's dense-row
+        capacity (T when that is unbounded)."""
         K, F = self.ell_cap, self.d_ff
-        R = T if max_backup is None else max_backup
+        if max_backup is None:
+            max_backup = min(T, self.dense_rows) if self.dense_rows > 0 else T
+        R = max_backup
         f32 = dict(dtype=torch.float32, device=device)
         return dict(
             ell_a=torch.empty((T, K), **f32),
@@ -278,18 +327,33 @@ class SparseFFN:
         return hy
 
     def forward_train(self, x, w_gate, w_up, w_down, hy=None, tw=None, y=None,
-                      max_backup: Optional[int] = None):
+                      max_backup: Optional[int] = None, check: bool = True):
+        """Training forward; returns (y, Hybrid). With ``check`` a capacity
+        report (more backup rows than max_backup or dense_rows) rebuilds the
+        handle with a T-row capacity, gives a caller-less Hybrid T backup
+        rows, and repeats the call; a caller's Hybrid that is too small
+        raises SffnError(SFFN_E_CAPACITY)."""
         T = x.shape[0]
         if y is None:
             y = torch.empty((T, self.d), dtype=torch.float32, device=x.device)
+        own = hy is None
         hy = hy if hy is not None else self.new_hybrid(T, max_backup, x.device)
-        ws, n = self.workspace(T, SFFN_OP_FORWARD_TRAIN, x.device)
-        ts = ctypes.byref(self._tw_struct(tw)) if tw is not None else None
-        hs = self._hy_struct(hy)
-        self._check(self.lib.sffn_forward_train(self.h, _ptr(x), _ptr(w_gate), _ptr(w_up),
-                                                _ptr(w_down), T, _ptr(y), ts, ctypes.byref(hs),
-                                                ws, n, _stream()), "sffn_forward_train")
-        return y, hy
+        while True:
+            ws, n = self.workspace(T, SFFN_OP_FORWARD_TRAIN, x.device)
+            ts = ctypes.byref(self._tw_struct(tw)) if tw is not None else None
+            hs = self._hy_struct(hy)
+            self._check(self.lib.sffn_forward_train(self.h, _ptr(x), _ptr(w_gate), _ptr(w_up),
+                                                    _ptr(w_down), T, _ptr(y), ts,
+                                                    ctypes.byref(hs), ws, n, _stream()),
+                        "sffn_forward_train")
+            if not check or self._capacity_ok():
+                return y, hy
+            if not own and hy["max_backup"] < T:
+                self._check(SFFN_E_CAPACITY, "sffn_forward_train: the Hybrid's max_backup")
+            if not self._grow() and not own:
+                self._check(SFFN_E_CAPACITY, "sffn_forward_train")
+            if own:
+                hy = self.new_hybrid(T, T, x.device)
 
     def backward(self, x, w_gate, w_up, w_down, hy, dy, l1_coeff: float = 0.0, out=None):
         """Gradients (dx [T, d], dw_gate, dw_up, dw_down [F, d]; float32) of

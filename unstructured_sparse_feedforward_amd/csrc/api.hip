@@ -32,6 +32,12 @@ struct sffn_handle {
   // grouping runs beside the backup rows' dW products, which leave CUs free
   hipStream_t side = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  // device words: [0] capacity-overflow status (read and cleared by
+  // sffn_check), [1] the gate epilogue's overflow-record counter (zeroed by
+  // the list kernel that follows the gate GEMM; dirty when a call stopped
+  // in between, then zeroed before the next gate GEMM)
+  int32_t* dstate = nullptr;
+  bool ctr_dirty = false;
 };
 
 namespace {
@@ -57,7 +63,8 @@ sffn_status validate_desc(const sffn_desc* d) {
   if (!d) return SFFN_E_ARG;
   if (d->dtype != SFFN_F32 && d->dtype != SFFN_BF16) return SFFN_E_ARG;
   if (d->gated != 0 && d->gated != 1) return SFFN_E_ARG;
-  if (d->d <= 0 || d->d_ff <= 0 || d->tile <= 0 || d->twell_cap <= 0 || d->ell_cap < 0)
+  if (d->d <= 0 || d->d_ff <= 0 || d->tile <= 0 || d->twell_cap <= 0 || d->ell_cap < 0 ||
+      d->dense_rows < 0)
     return SFFN_E_ARG;
   if (d->tile != kTile) return SFFN_E_UNSUPPORTED;
   if (d->d_ff % kTile != 0 || d->d_ff > 65408) return SFFN_E_UNSUPPORTED;
@@ -74,11 +81,24 @@ size_t esize(const sffn_handle* h) { return h->desc.dtype == SFFN_BF16 ? 2 : 4; 
 int ovf_words(int64_t T) { return (int)((T + 31) / 32); }
 constexpr int kSplitMax = kSplitCap;
 
+// R: the dense path's row capacity of a call over T rows
+int64_t dense_cap(const sffn_handle* h, int64_t T) {
+  return h->desc.dense_rows > 0 ? std::min<int64_t>(h->desc.dense_rows, T) : T;
+}
+
+// K: the ELL capacity of the sparse path (training: the Hybrid's K;
+// inference: ell_cap when set and below n_t * C, else n_t * C)
+int ell_k(const sffn_handle* h, bool train) {
+  const int full = h->n_t * h->desc.twell_cap;
+  if (train) return h->desc.ell_cap;
+  return (h->desc.ell_cap > 0 && h->desc.ell_cap < full) ? h->desc.ell_cap : full;
+}
+
 // Workspace layout. Every region starts at a 256-byte boundary.
 struct Layout {
   size_t ovf = 0, tw_val = 0, tw_idx = 0, tw_cnt = 0, tw_flag = 0, tw_list = 0, tw_nf = 0;
-  size_t ell_a = 0, ell_idx = 0, ell_cnt = 0, bk = 0, upart = 0;
-  size_t hid = 0, zovf = 0, part = 0, total = 0;
+  size_t ell_a = 0, ell_idx = 0, ell_cnt = 0, bk = 0, upart = 0, dlist = 0, ndense = 0;
+  size_t hid = 0, zovf = 0, ovf_map = 0, part = 0, total = 0;
   // backward
   size_t drec = 0, ncnt = 0, noff = 0, thist = 0, toff = 0, meta = 0, dH = 0, gz_rm = 0;
   size_t gz_t = 0, gu_t = 0, gh_t = 0, xb = 0, dyb = 0;
@@ -101,10 +121,12 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
     L.bk = take((size_t)T);
   }
   if (op == SFFN_OP_FORWARD_SPARSE || op == SFFN_OP_FORWARD_TRAIN) {
-    // inference: ELL rows of capacity n_t * C, lossless for every row whose
-    // TwELL did not overflow; training: capacity K = ell_cap
-    const int64_t K = op == SFFN_OP_FORWARD_TRAIN ? (int64_t)h->desc.ell_cap : nt * C;
+    // ELL rows of capacity K (inference: lossless for every row whose TwELL
+    // did not overflow when K = n_t * C); the dense path holds R rows
+    const bool train = op == SFFN_OP_FORWARD_TRAIN;
+    const int64_t K = ell_k(h, train);
     const int64_t Kp = (K + 7) / 8 * 8;
+    const int64_t R = dense_cap(h, T);
     int ns, epl;
     slice_shape(dt_of(h), (int)d, &ns, &epl);
     L.ell_a = take((size_t)T * K * 4);
@@ -118,20 +140,30 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
     L.tw_flag = take((size_t)T);
     L.tw_list = take((size_t)T * 4);
     L.tw_nf = take(4);
-    // hidden rows of flagged tokens: bf16 hi|lo [T, 2F] or fp32 [T, F]
-    L.hid = take((size_t)T * F * 4);
-    // bf16: the gate pre-activations of overflowing tile rows [T, F]
-    if (h->desc.dtype == SFFN_BF16) L.zovf = take((size_t)T * F * 4);
+    // inference: the dense path's rows (training keeps them in the Hybrid)
+    if (!train) {
+      L.dlist = take((size_t)R * 4);
+      L.ndense = take(4);
+    }
+    // hidden rows of the dense path: bf16 hi|lo [R, 2F] or fp32 [R, F]
+    L.hid = take((size_t)R * F * 4);
+    // bf16: the gate pre-activations of overflowing tile rows, one
+    // 128-float record each (a dense-path row overflows at most n_t
+    // tiles), and every (row, tile)'s record number
+    if (h->desc.dtype == SFFN_BF16) {
+      L.zovf = take((size_t)R * nt * kTile * 4);
+      L.ovf_map = take((size_t)T * nt * 4);
+    }
     // split-K partials of the flagged rows' GEMMs (used one after the
     // other): a split problem has at most split_target / n_tiles row tiles
     // of 128 rows; the hidden GEMM keeps one partial set per B operand
     const int tiles_d = std::max(1, h->num_cu / (int)(d / 128));
     const int tiles_h = std::max(1, h->num_cu / (int)(F / 128));
     // bf16: the small-row GEMM keeps split partials of at most
-    // 2 * num_cu tiles, and always the up partials of every row
+    // 2 * num_cu tiles, and always the up partials of every dense row
     const size_t part_small =
         h->desc.dtype == SFFN_BF16
-            ? std::max((size_t)2 * h->num_cu * 128 * 128, (size_t)((T + 127) / 128 * 128) * F)
+            ? std::max((size_t)2 * h->num_cu * 128 * 128, (size_t)((R + 127) / 128 * 128) * F)
             : 0;
     const size_t part_d = (size_t)tiles_d * 128 * d;
     const size_t part_h = (size_t)2 * tiles_h * 128 * F;
@@ -141,13 +173,14 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
     L.hid = take((size_t)T * F * esize(h));
   }
   if (op == SFFN_OP_BACKWARD) {
-    // sized for up to T backup rows
+    // sized for up to R backup rows
     const int64_t K = h->desc.ell_cap, Kp = (K + 7) / 8 * 8;
+    const int64_t R = dense_cap(h, T);
     int ns, epl;
     slice_shape(dt_of(h), (int)d, &ns, &epl);
     const bool split = h->desc.dtype == SFFN_BF16;
-    const int64_t Tp = (T + 63) / 64 * 64;
-    L.ldt = split ? 2 * Tp : Tp;
+    const int64_t Rp = (R + 63) / 64 * 64;
+    L.ldt = split ? 2 * Rp : Rp;
     L.upart = take((size_t)ns * T * Kp * 4);
     L.drec = take((size_t)T * K * 16);
     const int64_t F4 = (F + 3) / 4, nblk = transpose_blocks(T, (int)K);
@@ -156,9 +189,9 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
     L.thist = take((size_t)nblk * F4 * 4);
     L.toff = take((size_t)nblk * F4 * 16);
     L.meta = take((size_t)T * K * 16);
-    L.dH = take((size_t)T * F * 4);
-    // dZ and dU rows: bf16 [T, 4F] (dZ hi | lo, dU hi | lo), fp32 two [T, F]
-    L.gz_rm = take((size_t)T * F * 8);
+    L.dH = take((size_t)R * F * 4);
+    // dZ and dU rows: bf16 [R, 4F] (dZ hi | lo, dU hi | lo), fp32 two [R, F]
+    L.gz_rm = take((size_t)R * F * 8);
     L.gz_t = take((size_t)F * L.ldt * esize(h));
     L.gu_t = take((size_t)F * L.ldt * esize(h));
     L.gh_t = take((size_t)F * L.ldt * esize(h));
@@ -233,11 +266,18 @@ sffn_status sffn_create(const sffn_desc* desc, sffn_handle** out) {
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SFFN_E_HIP;
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return SFFN_E_UNSUPPORTED;
+  int32_t* dstate = nullptr;
+  if (hipMalloc((void**)&dstate, 256) != hipSuccess) return SFFN_E_HIP;
+  if (hipMemset(dstate, 0, 256) != hipSuccess) {
+    (void)hipFree(dstate);
+    return SFFN_E_HIP;
+  }
   sffn_handle* h = new sffn_handle();
   h->desc = *desc;
   h->device = dev;
   h->num_cu = prop.multiProcessorCount;
   h->n_t = desc->d_ff / kTile;
+  h->dstate = dstate;
   *out = h;
   return SFFN_OK;
 }
@@ -252,6 +292,7 @@ void sffn_destroy(sffn_handle* h) {
   if (h->fork) (void)hipEventDestroy(h->fork);
   if (h->join) (void)hipEventDestroy(h->join);
   if (h->side) (void)hipStreamDestroy(h->side);
+  if (h->dstate) (void)hipFree(h->dstate);
   delete h;
 }
 
@@ -412,8 +453,20 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     t.flagged = at<int32_t>(ws, L.tw_list);
     t.n_flagged = at<int32_t>(ws, L.tw_nf);
   }
-  const int K = train ? D.ell_cap : h->n_t * D.twell_cap;
+  const int K = ell_k(h, train);
   const int Kp = (K + 7) / 8 * 8;
+  const int64_t R = dense_cap(h, T);
+  // rows the dense path computes: training min(max_backup, R), inference R
+  const int mcap = (int)(train ? std::min<int64_t>(hy->max_backup, R) : R);
+  int32_t* status = h->dstate;
+  int32_t* ovf_ctr = h->dstate + 1;
+  hipError_t e = hipSuccess;
+  if (dt == kBF16 && h->ctr_dirty) {
+    // a call stopped between its gate GEMM and its list kernel
+    e = hipMemsetAsync(ovf_ctr, 0, 4, stream);
+    if (e != hipSuccess) return hip_fail(h, e, "overflow-record counter");
+    h->ctr_dirty = false;
+  }
 
   // 1. gate GEMM, ReLU + TwELL pack in the epilogue
   GemmArgs g = {};
@@ -429,10 +482,15 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   g.tw_cnt = t.cnt;
   g.C = D.twell_cap;
   g.n_t = h->n_t;
-  g.zovf = dt == kBF16 ? at<float>(ws, L.zovf) : nullptr;
+  if (dt == kBF16) {
+    g.zovf = at<float>(ws, L.zovf);
+    g.ovf_map = at<int32_t>(ws, L.ovf_map);
+    g.ovf_ctr = ovf_ctr;
+    g.ovf_cap = (int)(R * h->n_t);
+    h->ctr_dirty = true;
+  }
   g.num_cu = h->num_cu;
   g.grid = gemm_grid(dt, 1, h->num_cu);
-  hipError_t e = hipSuccess;
   {
     ProfScope ps(h, SFFN_K_GATE_TWELL, stream);
     e = launch_gemm(dt, 1, false, kEpiTwell, g, stream);
@@ -459,18 +517,20 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   }
   if (e != hipSuccess) return hip_fail(h, e, "row compaction");
 
-  // 3. the dense path's rows: their ascending list; in training also the
-  //    TwELL's own list of overflowing rows
-  int32_t* brow = train ? hy->brow : t.flagged;
-  int32_t* n_bk = train ? hy->n_backup : t.n_flagged;
-  const int64_t cap = train ? hy->max_backup : T;
+  // 3. the dense path's rows: their ascending list (the first mcap of them;
+  //    more raise the capacity status), and the TwELL's own list of
+  //    overflowing rows
+  int32_t* brow = train ? hy->brow : at<int32_t>(ws, L.dlist);
+  int32_t* n_bk = train ? hy->n_backup : at<int32_t>(ws, L.ndense);
   {
     ProfScope ps(h, SFFN_K_FLAGS, stream);
-    const ListArgs lb = {ea.bk, brow, cap, n_bk, train ? hy->slot : nullptr};
-    const ListArgs lf = {t.row_flag, t.flagged, T, t.n_flagged, nullptr};
-    e = launch_backup_list(lb, train ? &lf : nullptr, T, stream);
+    const ListArgs lb = {ea.bk, brow, mcap, n_bk, train ? hy->slot : nullptr, status,
+                         dt == kBF16 ? ovf_ctr : nullptr};
+    const ListArgs lf = {t.row_flag, t.flagged, T, t.n_flagged, nullptr, nullptr, nullptr};
+    e = launch_backup_list(lb, &lf, T, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "backup list");
+  h->ctr_dirty = false;
 
   // 4. dense path: hidden rows H = ReLU(z) * (x W_u) (split-K over the
   //    few rows, then a combine that stores H as bf16 hi + lo, or fp32, and
@@ -482,9 +542,8 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   //    which measured slower than running it in line.
   void* hid = at<char>(ws, L.hid);
   float* part = at<float>(ws, L.part);
-  const int mcap = train ? (int)std::min<int64_t>(hy->max_backup, T) : 0;
   GemmArgs down_late = {};   // bf16: the dense path's down product, run last
-  if ((!train || mcap > 0) && dt == kBF16) {
+  if (mcap > 0 && dt == kBF16) {
     // ReLU(z) of the rows comes from the gate GEMM itself (their TwELL
     // tiles, and the saved pre-activations of the tiles that overflowed);
     // gated layers add u = x W_u (split-K partials) and the combine forms
@@ -515,6 +574,8 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     f.C = D.twell_cap;
     f.n_t = h->n_t;
     f.zovf = at<float>(ws, L.zovf);
+    f.ovf_map = at<int32_t>(ws, L.ovf_map);
+    f.ovf_cap = (int)(R * h->n_t);
     f.part = part;
     // about one tile per CU: with only a few rows a deeper split costs
     // more in partials than it gains in parallel loads
@@ -549,7 +610,7 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     f2.grid = gemm_small_grid(h->num_cu);
     // launched after the sparse down projection
     down_late = f2;
-  } else if (!train || mcap > 0) {
+  } else if (mcap > 0) {
     GemmArgs f = {};
     f.A = x;
     f.lda = D.d;
@@ -748,7 +809,8 @@ sffn_status sffn_hybrid_compact(sffn_handle* h, const sffn_twell* tw, const floa
   if (e != hipSuccess) return hip_fail(h, e, "row compaction");
   {
     ProfScope ps(h, SFFN_K_FLAGS, stream);
-    const ListArgs lb = {ea.bk, hy->brow, hy->max_backup, hy->n_backup, hy->slot};
+    const ListArgs lb = {ea.bk, hy->brow, hy->max_backup, hy->n_backup, hy->slot, nullptr,
+                         nullptr};
     e = launch_backup_list(lb, nullptr, T, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "backup list");
@@ -791,7 +853,7 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
   const bool gated = D.gated != 0;
   const int K = D.ell_cap;
   const int Kp = (K + 7) / 8 * 8;
-  const int cap = (int)std::min<int64_t>(hy->max_backup, T);
+  const int cap = (int)std::min<int64_t>(hy->max_backup, dense_cap(h, T));
   hipError_t e;
 
   // 1. dh = dy . W_d[j] per ELL slot, as per-slice partial dot products
@@ -851,7 +913,7 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
     ba.gu_rm = at<char>(ws, L.gz_rm) + (size_t)2 * D.d_ff * 2;
     ba.ld_rm = (int64_t)4 * D.d_ff;
   } else {
-    ba.gu_rm = at<char>(ws, L.gz_rm) + (size_t)T * D.d_ff * 4;
+    ba.gu_rm = at<char>(ws, L.gz_rm) + (size_t)dense_cap(h, T) * D.d_ff * 4;
     ba.ld_rm = D.d_ff;
   }
   ba.gz_t = at<char>(ws, L.gz_t);
@@ -869,6 +931,17 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
   if (e != hipSuccess) return hip_fail(h, e, "backward dx");
   // 3. backup rows, densely: dH = dy W_d^T, then dZ/dU, dx rows and their
   // dW products (zeros when no row took the backup path)
+  // once work is forked to the second stream, every return below first
+  // makes the caller's stream wait for it (event join; a host wait of the
+  // second stream if even the join event could not be recorded)
+  bool forked = false;
+  hipError_t join_rec = hipSuccess;
+  auto join_side = [&]() -> hipError_t {
+    if (!forked) return hipSuccess;
+    forked = false;
+    if (join_rec == hipSuccess) return hipStreamWaitEvent(stream, h->join, 0);
+    return hipStreamSynchronize(h->side);
+  };
   bool transposed = false;
   if (cap > 0) {
     ProfScope ps(h, SFFN_K_BWD_DENSE, stream);
@@ -957,7 +1030,9 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
     }
     e = hipEventRecord(h->fork, stream);
     if (e == hipSuccess) e = hipStreamWaitEvent(h->side, h->fork, 0);
-    if (e == hipSuccess) {
+    if (e != hipSuccess) return hip_fail(h, e, "backward fork");
+    forked = true;
+    {
       ProfScope ps(h, SFFN_K_BWD_DX, h->side);
       e = launch_bwd_sparse(dt, gated, 3, ba, h->side);
     }
@@ -965,8 +1040,12 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
       ProfScope ps(h, SFFN_K_BWD_TRANSPOSE, h->side);
       e = launch_transpose(ba, h->side);
     }
-    if (e == hipSuccess) e = hipEventRecord(h->join, h->side);
-    if (e != hipSuccess) return hip_fail(h, e, "backward transpose");
+    join_rec = hipEventRecord(h->join, h->side);
+    if (e == hipSuccess) e = join_rec;
+    if (e != hipSuccess) {
+      (void)join_side();
+      return hip_fail(h, e, "backward transpose");
+    }
     transposed = true;
     // dW = (dZ, dU, H)^T (x, x, dy) over the backup rows
     for (int pass = 0; pass < 3; ++pass) {
@@ -989,13 +1068,16 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
       w.num_cu = h->num_cu;
       w.grid = gemm_grid(dt, 1, h->num_cu);
       e = launch_gemm(dt, 1, !split, kEpiStoreF32, w, stream);
-      if (e != hipSuccess) return hip_fail(h, e, "backup dW");
+      if (e != hipSuccess) {
+        (void)join_side();
+        return hip_fail(h, e, "backup dW");
+      }
     }
   }
   // 4. slots grouped by neuron in ascending row order (with backup rows it
   //    ran on the second stream beside their dW products: join it here)
   if (transposed) {
-    e = hipStreamWaitEvent(stream, h->join, 0);
+    e = join_side();
   } else {
     ProfScope ps(h, SFFN_K_BWD_TRANSPOSE, stream);
     e = launch_transpose(ba, stream);
@@ -1020,9 +1102,11 @@ sffn_status sffn_hybrid_check(sffn_handle* h, const sffn_hybrid* hy, hipStream_t
   int32_t n = 0;
   e = hipMemcpy(&n, hy->n_backup, sizeof(n), hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(h, e, "n_backup");
-  if (n > hy->max_backup)
-    return fail(h, SFFN_E_CAPACITY, "backup rows " + std::to_string(n) + " exceed max_backup " +
-                                        std::to_string(hy->max_backup));
+  int64_t cap = hy->max_backup;
+  if (h->desc.dense_rows > 0) cap = std::min<int64_t>(cap, h->desc.dense_rows);
+  if (n > cap)
+    return fail(h, SFFN_E_CAPACITY, "backup rows " + std::to_string(n) + " exceed the capacity " +
+                                        std::to_string(cap) + " (max_backup, dense_rows)");
   return SFFN_OK;
 }
 
@@ -1086,6 +1170,14 @@ sffn_status sffn_check(sffn_handle* h, hipStream_t stream) {
   if (e != hipSuccess) return hip_fail(h, e, "stream");
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(h, e, "async");
+  int32_t st = 0;
+  e = hipMemcpy(&st, h->dstate, sizeof(st), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && st != 0) e = hipMemset(h->dstate, 0, sizeof(st));
+  if (e != hipSuccess) return hip_fail(h, e, "status");
+  if (st != 0)
+    return fail(h, SFFN_E_CAPACITY,
+                "more rows took the dense path than its capacity (desc.dense_rows, or "
+                "max_backup in training); those rows were not computed");
   return SFFN_OK;
 }
 

@@ -201,12 +201,25 @@ __device__ __forceinline__ void twell_epilogue(const GemmArgs& g, f32x16_t (&acc
           n1c += __popc((uint32_t)(bal[j] >> 32));
         }
         cnt_lane = lane == r0 ? n0c : (lane == r0 + 4 ? n1c : cnt_lane);
-        // a tile row that overflows C keeps all its pre-activations, so that
-        // the dense path of its row needs no gate recomputation
-        if (g.zovf != nullptr && (n0c > C || n1c > C) && (h ? n1c > C : n0c > C)) {
-          float* zr = g.zovf + (int64_t)(rbase + r0 + h * 4) * g.N + tb * kTile + c32;
+        // a tile row that overflows C keeps all its pre-activations in a
+        // record of its own (taken from a device counter), so that the
+        // dense path of its row needs no gate recomputation; the record's
+        // number goes to the row's entry of the tile map
+        if (g.zovf != nullptr && (n0c > C || n1c > C)) {
+          const bool o0 = n0c > C, o1 = n1c > C;
+          int rec = 0;
+          if ((lane == 0 && o0) || (lane == 32 && o1)) rec = atomicAdd(g.ovf_ctr, 1);
+          const int r_0 = __builtin_amdgcn_readlane(rec, 0);
+          const int r_1 = __builtin_amdgcn_readlane(rec, 32);
+          if (h ? o1 : o0) {
+            const int my = h ? r_1 : r_0;
+            if (my < g.ovf_cap) {
+              float* zr = g.zovf + (int64_t)my * kTile + c32;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) zr[j * 32] = av[j];
+              for (int j = 0; j < 4; ++j) zr[j * 32] = av[j];
+            }
+            if (c32 == 0) g.ovf_map[(int64_t)(rbase + r0 + h * 4) * g.n_t + tb] = my;
+          }
         }
         const uint32_t ro = (uint32_t)r0 * row_entries + half_off;
 #pragma unroll

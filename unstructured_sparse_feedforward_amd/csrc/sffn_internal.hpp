@@ -168,8 +168,15 @@ struct GemmArgs {
   uint16_t* tw_idx;
   int32_t* tw_cnt;
   uint32_t* ovf;             // [n_t][ovf_words] overflow bits, bit r of word w = row 32w+r
-  float* zovf;               // bf16 gate: [M, N] fp32 pre-activations of the tile rows
-                             // whose count exceeds C (other entries are not written)
+  float* zovf;               // bf16 gate: fp32 pre-activations of the tile rows whose
+                             // count exceeds C, one 128-float record per such tile row
+                             // [ovf_cap, 128], taken from the counter *ovf_ctr; the
+                             // record of row t, tile b is ovf_map[t * n_t + b]
+                             // (written only for those tile rows; records past
+                             // ovf_cap are not stored)
+  int32_t* ovf_map;
+  int32_t* ovf_ctr;
+  int ovf_cap;
   int C;
   int n_t;
   int ovf_words;
@@ -232,13 +239,17 @@ hipError_t launch_rows(const EllArgs& a, hipStream_t s);
 // Ascending list of the rows with bk[t] != 0 (the first cap of them), their
 // true count and (nullable) every row's backup slot (-1 for ELL rows).
 // One workgroup per list (two lists, l1 non-null, in one launch); bk must
-// be 16-byte aligned.
+// be 16-byte aligned. When the count exceeds cap and status is set,
+// *status gets bit 0; when reset is set, *reset is zeroed at the end (the
+// gate epilogue's overflow-record counter, consumed by then).
 struct ListArgs {
   const uint8_t* bk;
   int32_t* brow;
   int64_t cap;
   int32_t* n;
   int32_t* slot;
+  int32_t* status;
+  int32_t* reset;
 };
 hipError_t launch_backup_list(const ListArgs& l0, const ListArgs* l1, int64_t T, hipStream_t s);
 

@@ -157,7 +157,11 @@ __global__ __launch_bounds__(1024) void backup_list_kernel(ListArgs l0, ListArgs
     carry += total;
     __syncthreads();
   }
-  if (tid == 0) *n_backup = carry;
+  if (tid == 0) {
+    *n_backup = carry;
+    if (L.status && carry > cap) *L.status = 1;
+    if (L.reset) *L.reset = 0;
+  }
 }
 
 // Sum over the 8 lanes of each lane octet, result in all 8 (quad swaps,

@@ -54,7 +54,10 @@ class Workload:
     front_positions: int = 0      # first positions of each sequence ...
     front_prob: float = 0.0       # ... are outliers with this probability
     seq_len: int = 0              # sequence length for the front bias
-    ell_cap: int = 0              # Hybrid ELL capacity K (0 = inference only)
+    ell_cap: int = 0              # ELL capacity K of the sparse path: rows with more
+                                  # active neurons take the dense path (training: the
+                                  # Hybrid's K; 0 at inference = n_t * C)
+    dense_rows: int = 1024        # rows the dense path holds per call (0 = every row)
     train: bool = False           # draw dy as well
 
     @property
@@ -69,16 +72,20 @@ class Workload:
 # The five workloads. Names say what they are; sizes are in the fields.
 SMALL_F32 = Workload("gated_T128_d256_F1024_f32", T=128, d=256, F=1024,
                      gated=True, dtype="f32", nnz=0.02 * 1024, twell_cap=16)
+# ELL capacities sit several standard deviations above the per-token
+# count (29 +- 5.4 here), so that in practice only the outlier tokens take
+# the dense path; the dense-row capacities hold several times the expected
+# number of such tokens.
 GATED_1P5B = Workload("gated_T8192_d2048_F5632_bf16_nnz29", T=8192, d=2048,
                       F=5632, gated=True, dtype="bf16", nnz=29, twell_cap=8,
-                      outlier_frac=0.01)
+                      outlier_frac=0.01, ell_cap=64, dense_rows=512)
 # A stronger L1 than 2e-5 leaves fewer active neurons (listing Table 4,
 # L1 = 3e-5; the pages print no count for it): half the 2e-5 count.
 GATED_1P5B_NNZ15 = GATED_1P5B.replace(name="gated_T8192_d2048_F5632_bf16_nnz15", nnz=15)
 NONGATED = {n: Workload(f"nongated_T16384_d2048_F8192_bf16_nnz{n}", T=16384,
                         d=2048, F=8192, gated=False, dtype="bf16", nnz=n,
-                        twell_cap=c)
-            for n, c in ((29, 8), (108, 16), (911, 48))}
+                        twell_cap=c, ell_cap=k, dense_rows=256)
+            for n, c, k in ((29, 8, 64), (108, 16, 192), (911, 48, 1280))}
 # 18-layer stack: per-layer target active counts ramp 15 -> 120 (layer 5)
 # -> 20 (layer 17); 2% outliers with a front-of-sequence bias.
 STACK_RAMP = [15, 36, 57, 78, 99, 120, 112, 103, 95, 87, 78, 70, 62, 53,
@@ -86,7 +93,7 @@ STACK_RAMP = [15, 36, 57, 78, 99, 120, 112, 103, 95, 87, 78, 70, 62, 53,
 STACK_LAYER = Workload("stack18_T16384_d2048_F5632_bf16", T=16384, d=2048,
                        F=5632, gated=True, dtype="bf16", nnz=66.4,
                        twell_cap=16, outlier_frac=0.02, front_positions=32,
-                       front_prob=0.3, seq_len=2048)
+                       front_prob=0.3, seq_len=2048, ell_cap=256, dense_rows=1024)
 TRAIN_HYBRID = Workload("train_T8192_d2048_F5632_bf16_nnz29_K64", T=8192,
                         d=2048, F=5632, gated=True, dtype="bf16", nnz=29,
                         twell_cap=16, outlier_frac=0.05, ell_cap=64,
