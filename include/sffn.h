@@ -251,6 +251,25 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate,
                          float* y, const sffn_twell* tw, int32_t mode,
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * sffn_forward without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). Same arguments, kernels and
+ * results as sffn_forward; the workspace is instead a static device array
+ * of the library (128 MiB on each GPU the library runs on, held until the
+ * process ends). A call whose sffn_workspace_bytes exceeds 128 MiB
+ * returns SFFN_E_ARG before anything is enqueued (at d = 2048, F = 5632,
+ * C = 8, K = 64, dense_rows = 512 that is above T = 15815). The
+ * call allocates nothing: no hipMalloc, hipFree or event creation
+ * (per-kernel timing is skipped for it). The scratch array is shared by
+ * every call on a GPU, from every handle: calls that overlap on one GPU
+ * (on different streams) race, so the caller orders them. Its contents
+ * need no initialisation.
+ */
+sffn_status sffn_forward_noalloc(sffn_handle* h, const void* x, const void* w_gate,
+                                 const void* w_up, const void* w_down, int64_t T, float* y,
+                                 const sffn_twell* tw, int32_t mode, hipStream_t stream);
+
 /* TwELL -> Hybrid ("Hybrid Conversion", "2. Methodology" B on the
  * gist.science explainer): routes every row, fills ell_a, ell_idx, ell_cnt,
  * slot, brow and n_backup of *hy from *tw. When z [T, F] float32 is given,

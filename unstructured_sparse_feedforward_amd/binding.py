@@ -37,7 +37,7 @@ EXPORTS = ("sffn_create", "sffn_destroy", "sffn_last_error", "sffn_status_string
            "sffn_workspace_bytes", "sffn_pack_twell", "sffn_gate_preact",
            "sffn_forward", "sffn_check", "sffn_profile_enable", "sffn_profile_read",
            "sffn_kernel_name", "sffn_hybrid_compact", "sffn_forward_train",
-           "sffn_hybrid_check", "sffn_backward")
+           "sffn_hybrid_check", "sffn_backward", "sffn_forward_noalloc")
 SFFN_K_COUNT = 18
 
 
@@ -92,6 +92,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sffn_forward.argtypes = [vp, vp, vp, vp, vp, i64, vp, ctypes.POINTER(SffnTwell), i32,
                                  vp, sz, vp]
     lib.sffn_forward.restype = i32
+    lib.sffn_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, vp,
+                                         ctypes.POINTER(SffnTwell), i32, vp]
+    lib.sffn_forward_noalloc.restype = i32
     lib.sffn_check.argtypes = [vp, vp]
     lib.sffn_check.restype = i32
     lib.sffn_profile_enable.argtypes = [vp, i32]
@@ -279,6 +282,20 @@ class SparseFFN:
                                               _stream()), "sffn_forward")
             if not check or self._capacity_ok() or not self._grow():
                 return y
+
+    def forward_noalloc(self, x: torch.Tensor, w_gate: torch.Tensor,
+                        w_up: Optional[torch.Tensor], w_down: torch.Tensor, y: torch.Tensor,
+                        mode: str = "sparse",
+                        tw: Optional[Dict[str, torch.Tensor]] = None) -> torch.Tensor:
+        """sffn_forward_noalloc: as :meth:`forward` with the library's static
+        scratch as workspace; y (and tw) are the caller's. Nothing is
+        allocated and nothing is checked (run :meth:`check` afterwards)."""
+        m = SFFN_SPARSE if mode == "sparse" else SFFN_DENSE
+        s = ctypes.byref(self._tw_struct(tw)) if tw is not None else None
+        self._check(self.lib.sffn_forward_noalloc(self.h, _ptr(x), _ptr(w_gate), _ptr(w_up),
+                                                  _ptr(w_down), x.shape[0], _ptr(y), s, m,
+                                                  _stream()), "sffn_forward_noalloc")
+        return y
 
     def check(self):
         """sffn_check: raises SffnError (SFFN_E_CAPACITY when a call since the

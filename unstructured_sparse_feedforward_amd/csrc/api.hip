@@ -4,7 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
-
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -38,7 +38,40 @@ struct sffn_handle {
   // in between, then zeroed before the next gate GEMM)
   int32_t* dstate = nullptr;
   bool ctr_dirty = false;
+  // this device's copy of the static scratch (sffn_forward_noalloc)
+  void* scratch = nullptr;
+  std::string scratch_err;
 };
+
+// Workspace of sffn_forward_noalloc, for callers that cannot allocate:
+// a file-scope device array, one copy per GPU, held until the process
+// ends. Host code never passes the array's name to a kernel or a copy:
+// its device address comes from hipGetSymbolAddress, looked up once per
+// device (with that device current) when the first handle is created
+// there, and kept below.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's scratch address (device `dev` must be current)
+hipError_t scratch_address(int dev, void** out) {
+  *out = nullptr;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
 
 namespace {
 
@@ -278,6 +311,8 @@ sffn_status sffn_create(const sffn_desc* desc, sffn_handle** out) {
   h->num_cu = prop.multiProcessorCount;
   h->n_t = desc->d_ff / kTile;
   h->dstate = dstate;
+  const hipError_t se = scratch_address(dev, &h->scratch);
+  if (se != hipSuccess) h->scratch_err = hipGetErrorString(se);
   *out = h;
   return SFFN_OK;
 }
@@ -756,6 +791,31 @@ sffn_status sffn_forward(sffn_handle* h, const void* x, const void* w_gate, cons
     return fail(h, SFFN_E_ARG, "workspace missing, too small or not 256-byte aligned");
   if (mode == SFFN_DENSE) return forward_dense(h, x, w_gate, w_up, w_down, T, y, ws, L, stream);
   return sparse_forward(h, x, w_gate, w_up, w_down, T, y, tw, nullptr, ws, L, stream);
+}
+
+sffn_status sffn_forward_noalloc(sffn_handle* h, const void* x, const void* w_gate,
+                                 const void* w_up, const void* w_down, int64_t T, float* y,
+                                 const sffn_twell* tw, int32_t mode, hipStream_t stream) {
+  if (!h) return SFFN_E_ARG;
+  if (mode != SFFN_SPARSE && mode != SFFN_DENSE) return fail(h, SFFN_E_ARG, "unknown mode");
+  sffn_status st = forward_args(h, x, w_gate, w_up, w_down, T, y, tw);
+  if (st != SFFN_OK || T == 0) return st;
+  if (mode == SFFN_DENSE && tw) return fail(h, SFFN_E_ARG, "dense mode takes no TwELL");
+  if (h->scratch == nullptr)
+    return fail(h, SFFN_E_HIP, "static scratch unavailable: " + h->scratch_err);
+  const Layout L = layout(h, T, mode == SFFN_SPARSE ? SFFN_OP_FORWARD_SPARSE : SFFN_OP_FORWARD_DENSE);
+  if (L.total > kScratchBytes)
+    return fail(h, SFFN_E_ARG,
+                "the call needs " + std::to_string(L.total) + " bytes of workspace; the static "
+                "scratch holds " + std::to_string(kScratchBytes) + " (use sffn_forward)");
+  // no timing events here: creating one may allocate
+  const bool prof = h->prof;
+  h->prof = false;
+  st = mode == SFFN_DENSE
+           ? forward_dense(h, x, w_gate, w_up, w_down, T, y, h->scratch, L, stream)
+           : sparse_forward(h, x, w_gate, w_up, w_down, T, y, tw, nullptr, h->scratch, L, stream);
+  h->prof = prof;
+  return st;
 }
 
 sffn_status sffn_forward_train(sffn_handle* h, const void* x, const void* w_gate,
