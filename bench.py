@@ -38,6 +38,11 @@ METRIC_TRAIN = ("input tokens/ms, sparse gated FFN training step (fwd + bwd, Hyb
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3       # MI355X fp32 matrix/vector
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+# aggregate L2 read bandwidth, derived: 8 XCDs x 16 channels x 128 bytes
+# per clock x 2.4 GHz (the L2 of a CDNA XCD: 4 MB in 16 channels of 128 B
+# per clock). The sparse gathers are served from each XCD's L2 slice.
+PEAK_L2_GBS = 8 * 16 * 128 * 2.4
+SCRUB_BYTES = 2 << 30         # cold runs: bytes read between steps (> MALL + L2)
 
 WORKLOADS = ("gated", "gated15", "nongated29", "nongated108", "nongated911", "stack18", "train",
              "small")
@@ -52,26 +57,29 @@ def _dev(inp, name, torch, np):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def _timed(fn, steps, warmup, torch, ffns=()):
+def _timed(fn, steps, warmup, torch, ffns=(), per_step=None):
     """Warmup, then `steps` timed steps. Returns (event ms per step, wall ms
     per step, {kernel: (total ms, launches)} summed over `ffns` when they
-    are given, whose launches are then bracketed by HIP events)."""
+    are given, whose launches are then bracketed by HIP events). With a
+    list `per_step`, each step's own duration (an event before and after
+    it) is appended to it."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     for f in ffns:
         f.profile(True)
     stream = torch.cuda.current_stream()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    ev_ = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
+    ev_[0].record(stream)
+    for i in range(steps):
         fn()
-    e1.record(stream)
+        ev_[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3
-    ev = e0.elapsed_time(e1)
+    ev = ev_[0].elapsed_time(ev_[-1])
+    if per_step is not None:
+        per_step.extend(ev_[i].elapsed_time(ev_[i + 1]) for i in range(steps))
     prof = {}
     for f in ffns:
         for k, (ms, n) in f.profile_read().items():
@@ -79,6 +87,33 @@ def _timed(fn, steps, warmup, torch, ffns=()):
             prof[k] = (a + ms, b + n)
         f.profile(False)
     return ev / steps, wall / steps, prof
+
+
+def _timed_cold(fn, steps, torch, scrub):
+    """`steps` steps, each after a read of the whole scrub buffer (larger
+    than the Infinity Cache and the L2s together), so every step starts
+    with its inputs and weights in HBM only. Returns each step's duration
+    (events right before and after it)."""
+    out = []
+    stream = torch.cuda.current_stream()
+    for _ in range(steps):
+        torch.sum(scrub)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    return out
+
+
+def pct(v):
+    """Median, p10 and p90 of per-step milliseconds."""
+    import numpy as np
+    a = np.asarray(v, dtype=np.float64)
+    return {"p10": float(np.percentile(a, 10)), "median": float(np.median(a)),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
 
 
 def measured_traffic(workload):
@@ -225,9 +260,11 @@ def main():
                     help="tokens of the oracle CPU baseline sample (-1 = the workload's "
                          "default, 0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--energy", action="store_true",
-                    help="also run the sparse and dense forwards for ~3 s each while sampling "
-                         "the socket power with amd-smi, and report energy per token")
+    ap.add_argument("--energy", action=argparse.BooleanOptionalAction, default=True,
+                    help="run the sparse and dense forwards for ~3 s each while sampling the "
+                         "socket power with amd-smi, and report energy per token (default on)")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="cold-cache steps of each mode (a 2 GiB read before each; 0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="before the timed work, run a plain elementwise copy of MIB MiB "
                          "(float32 negate into a second buffer) three times, so hardware "
@@ -311,8 +348,10 @@ def bench_forward(args, np, torch, SparseFFN, wl):
 
     ffns = [L["ffn"] for L in layers]
     # timed region: K sparse steps, then K dense steps on the same inputs
-    ms, wall_ms, _ = _timed(sparse, args.steps, args.warmup, torch)
-    ms_d, _, _ = _timed(dense, args.steps, args.warmup, torch)
+    # (warm: inputs and weights may stay in the caches between steps)
+    sp_steps, de_steps = [], []
+    ms, wall_ms, _ = _timed(sparse, args.steps, args.warmup, torch, per_step=sp_steps)
+    ms_d, _, _ = _timed(dense, args.steps, args.warmup, torch, per_step=de_steps)
     # the same steps again with every kernel bracketed by HIP events on the
     # launch stream, for the per-kernel durations
     ms_p, _, prof = _timed(sparse, args.steps, 0, torch, ffns)
@@ -320,6 +359,20 @@ def bench_forward(args, np, torch, SparseFFN, wl):
     torch.cuda.synchronize()
     for f in ffns:
         f.check()
+    # cold: every step after a 2 GiB read that evicts the caches
+    cold = None
+    if args.cold_steps > 0:
+        scrub = torch.ones(SCRUB_BYTES // 4, dtype=torch.float32, device="cuda")
+        sp_cold = _timed_cold(sparse, args.cold_steps, torch, scrub)
+        de_cold = _timed_cold(dense, args.cold_steps, torch, scrub)
+        del scrub
+        cold = {"method": f"each step after torch.sum over a {SCRUB_BYTES >> 30} GiB buffer "
+                          "(evicts the 256 MB Infinity Cache and the L2s); events around the "
+                          "step alone",
+                "sparse_ms": pct(sp_cold), "dense_ms": pct(de_cold),
+                "value": T_of(layers) / pct(sp_cold)["median"],
+                "dense_value": T_of(layers) / pct(de_cold)["median"],
+                "speedup_sparse_over_dense": pct(de_cold)["median"] / pct(sp_cold)["median"]}
 
     gbytes, pairs, n_flag = 0.0, 0, 0
     for L in layers:
@@ -329,29 +382,40 @@ def bench_forward(args, np, torch, SparseFFN, wl):
         pairs += p
         n_flag += nf
     flops = sum(2.0 * W.T * W.d * W.F for W in Ws)
+    # the dense layer: gate, up and down products (non-gated: two)
+    dense_flops = sum(2.0 * W.T * W.d * W.F * (3 if W.gated else 2) for W in Ws)
     peak_mm = PEAK_BF16_TFLOPS if W0.dtype == "bf16" else PEAK_F32_TFLOPS
     traffic = measured_traffic(W0.name) if not stack else {}
     r_gate = roof("mfma", "gate_gemm_twell", flops * args.steps, prof, ["gate_gemm_twell"],
                   peak_mm, traffic.get("gate_gemm_twell"))
+    torch_ffn = None
     if not stack and W0.dtype == "bf16":
         # context, not part of the path: the vendor bf16 GEMM (torch linear,
-        # hipBLASLt) on the gate's shape, plain output, no epilogue
-        x0, wg0 = layers[0]["args"][0], layers[0]["args"][1]
-        for _ in range(3):
-            torch.nn.functional.linear(x0, wg0)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(args.steps):
-            torch.nn.functional.linear(x0, wg0)
-        e1.record()
-        torch.cuda.synchronize()
-        vms = e0.elapsed_time(e1) / args.steps
+        # hipBLASLt) on the gate's shape, plain output, no epilogue, and
+        # torch's own bf16 dense layer (two or three linear calls with the
+        # ReLU and product between them)
+        x0, wg0, wu0, wd0 = layers[0]["args"]
+        vms = _torch_ms(lambda: torch.nn.functional.linear(x0, wg0), args.steps, torch)
         vflop = 2.0 * W0.T * W0.d * W0.F
         r_gate["vendor_gemm_same_shape"] = {
             "kernel": "torch.nn.functional.linear bf16 (hipBLASLt), bf16 output, no epilogue",
             "avg_ms": vms, "achieved": vflop / (vms * 1e-3) / 1e12,
             "frac": vflop / (vms * 1e-3) / 1e12 / peak_mm}
+        wdT = wd0.t().contiguous()
+        F_ = torch.nn.functional
+
+        def torch_dense():
+            h = F_.relu(F_.linear(x0, wg0))
+            if wu0 is not None:
+                h = h * F_.linear(x0, wu0)
+            return F_.linear(h, wdT)
+
+        tms = _torch_ms(torch_dense, args.steps, torch)
+        del wdT
+        torch_ffn = {"kernel": "torch bf16 dense layer: linear, relu, linear, mul, linear "
+                               "(hipBLASLt GEMMs, bf16 output)",
+                     "ms_per_step": tms, "value": W0.T / tms,
+                     "frac_of_bf16_peak": dense_flops / (tms * 1e-3) / 1e12 / peak_mm}
     # the sparse up/down projection is three kernels (per-slice partial dot
     # products, their sums h = a * u, the down projection); a launch of it
     # is one of each
@@ -359,11 +423,25 @@ def bench_forward(args, np, torch, SparseFFN, wl):
     tr = sum(traffic[k] for k in keys) if all(k in traffic for k in keys) else None
     r_gath = roof("hbm", " + ".join(keys), gbytes * args.steps, prof, keys, PEAK_HBM_GBS, tr)
     r_gath["active_pairs_per_step"] = pairs
+    # the algorithmic bytes are what the path gathers; most of them are
+    # served by the XCDs' L2s (each XCD gathers from one 2.9 MB slice of the
+    # weights at a time), so the frac above is an effective rate. Against
+    # what bounds it: the aggregate L2 bandwidth, and the HBM side measured
+    # by the committed counters
+    r_gath["l2_relative"] = {"peak": PEAK_L2_GBS, "unit": "GB/s",
+                             "frac": r_gath["achieved"] / PEAK_L2_GBS,
+                             "peak_note": "derived: 8 XCDs x 16 L2 channels x 128 B/clk x "
+                                          "2.4 GHz"}
+    r_gath["hbm_side"] = None if tr is None else {
+        "bytes_per_launch": tr, "achieved": tr / (r_gath["avg_ms"] * 1e-3) / 1e9,
+        "frac": tr / (r_gath["avg_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS, "unit": "GB/s",
+        "source": "rocprofv3 FETCH_SIZE + WRITE_SIZE of the three kernels (profiles/)"}
     dominant, other = ((r_gate, r_gath) if r_gate["avg_ms"] >= r_gath["avg_ms"]
                        else (r_gath, r_gate))
     T = W0.T
     cfg = {"workload": W0.name, "T": T, "d": W0.d, "d_ff": W0.F, "gated": W0.gated,
            "nnz_per_token": W0.nnz, "twell_tile": W0.tile, "twell_cap": W0.twell_cap,
+           "ell_cap": W0.ell_cap, "dense_rows": W0.dense_rows,
            "outlier_frac": W0.outlier_frac, "seed": args.seed}
     if stack:
         cfg.update(workload=wl.STACK_LAYER.name, layers=len(Ws),
@@ -388,23 +466,30 @@ def bench_forward(args, np, torch, SparseFFN, wl):
         "config": cfg,
         "roofline": dominant,
         "roofline_other": other,
-        "dense_baseline": {"value": T / ms_d, "ms_per_step": ms_d,
+        "step_ms": pct(sp_steps),
+        "dense_baseline": {"value": T / ms_d, "ms_per_step": ms_d, "step_ms": pct(de_steps),
                            "speedup_sparse_over_dense": ms_d / ms,
+                           "frac_of_mfma_peak": dense_flops / (ms_d * 1e-3) / 1e12 / peak_mm,
                            "kernels_ms_per_step": per_step(prof_d, args.steps)},
+        "cold": cold,
+        "torch_dense_layer": torch_ffn,
         "kernels_ms_per_step": per_step(prof, args.steps),
         "ms_per_step_wall": wall_ms,
         "ms_per_step_with_kernel_events": ms_p,
         "flagged_rows_per_step": n_flag,
+        "device_bytes": forward_bytes(layers),
     }
     if stack:
         out["dispatch"] = per_layer_dispatch(layers, args.steps, torch)
-    if args.energy:
+    if args.energy and not stack:
         idle = _socket_power_w()
         e_sp = measure_energy(sparse, T, torch)
         e_de = measure_energy(dense, T, torch)
-        out["energy"] = {"idle_W": idle, "sparse": e_sp, "dense": e_de,
-                         "method": "amd-smi socket power sampled every ~0.1-0.3 s from a host "
-                                   "thread while the forward runs back to back for ~3 s"}
+        out["energy"] = None if e_sp is None or e_de is None else {
+            "idle_W": idle, "sparse": e_sp, "dense": e_de,
+            "sparse_over_dense": e_sp["uJ_per_token"] / e_de["uJ_per_token"],
+            "method": "amd-smi socket power sampled every ~0.1-0.3 s from a host thread "
+                      "while the forward runs back to back for ~3 s"}
     if n_cpu > 0:
         what = (f"first {n_cpu} tokens of each of the {len(Ws)} layers" if stack
                 else f"first {n_cpu} of {T} tokens")
@@ -413,6 +498,36 @@ def bench_forward(args, np, torch, SparseFFN, wl):
             f"{what}: numpy float64 sparse forward (gate GEMM, TwELL pack, per-token "
             f"up/down over active neurons, dense flagged rows)")
     return out
+
+
+def T_of(layers):
+    return layers[0]["W"].T
+
+
+def _torch_ms(fn, steps, torch):
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def forward_bytes(layers):
+    """Device bytes one layer's forward holds beyond its inputs and y: the
+    library's workspace (and the TwELL the bench passes in) for the sparse
+    forward, the workspace (the bf16 hidden tensor) for the dense one."""
+    from unstructured_sparse_feedforward_amd import binding as B
+    L = layers[0]
+    f, W = L["ffn"], L["W"]
+    tw = sum(t.numel() * t.element_size() for t in L["tw"].values())
+    return {"sparse_workspace": f.workspace_bytes(W.T, B.SFFN_OP_FORWARD_SPARSE),
+            "sparse_twell": tw,
+            "dense_workspace": f.workspace_bytes(W.T, B.SFFN_OP_FORWARD_DENSE)}
 
 
 def per_layer_dispatch(layers, steps, torch):
@@ -454,6 +569,41 @@ def per_layer_dispatch(layers, steps, torch):
             "layer_ms_sparse": t_sp, "layer_ms_dense": t_de}
 
 
+def torch_dense_train(a, dy, steps, torch):
+    """Context, not this library: torch's bf16 dense training step of the
+    same layer (autograd through linear, relu, mul, linear; hipBLASLt
+    GEMMs; bf16 gradients), its time per step and the device memory one
+    step adds to the inputs and weights."""
+    F_ = torch.nn.functional
+    x = a[0].clone().requires_grad_()
+    wg = a[1].clone().requires_grad_()
+    wu = a[2].clone().requires_grad_()
+    wdT = a[3].t().contiguous().requires_grad_()     # [d, F], the linear weight
+    dyb = dy.clone()
+
+    def step():
+        h = F_.relu(F_.linear(x, wg)) * F_.linear(x, wu)
+        yy = F_.linear(h, wdT)
+        return torch.autograd.grad(yy, (x, wg, wu, wdT), dyb)
+
+    step()
+    torch.cuda.synchronize()
+    m0 = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    h = F_.relu(F_.linear(x, wg)) * F_.linear(x, wu)
+    yy = F_.linear(h, wdT)
+    torch.cuda.synchronize()
+    held = torch.cuda.memory_allocated() - m0
+    g = torch.autograd.grad(yy, (x, wg, wu, wdT), dyb)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - m0
+    del g, h, yy
+    ms = _torch_ms(step, steps, torch)
+    return {"kind": "torch autograd bf16 dense layer (not this library)", "ms_per_step": ms,
+            "value": a[0].shape[0] / ms, "peak_bytes": int(peak),
+            "after_forward_bytes": int(held)}
+
+
 def bench_train(args, np, torch, SparseFFN, wl):
     import oracle
     W = wl.TRAIN_HYBRID
@@ -474,26 +624,43 @@ def bench_train(args, np, torch, SparseFFN, wl):
     dy = _dev(inp, "dy", torch, np)
     del inp
     d, F, T = W.d, W.F, W.T
+    # device memory the sparse step adds to its inputs and weights: the
+    # Hybrid, the TwELL, y, the four gradients and the library's workspaces
+    torch.cuda.synchronize()
+    mem0 = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
     ffn = SparseFFN(d, F, gated=True, twell_cap=W.twell_cap, ell_cap=W.ell_cap,
                     dense_rows=W.dense_rows, dtype=torch.bfloat16)
     hy = ffn.new_hybrid(T)
-    tw = ffn.new_twell(T)
     y = torch.empty((T, d), dtype=torch.float32, device="cuda")
     f32 = dict(dtype=torch.float32, device="cuda")
     grads = (torch.empty((T, d), **f32), torch.empty((F, d), **f32),
              torch.empty((F, d), **f32), torch.empty((F, d), **f32))
 
+    # the TwELL of the step lives in the library's workspace (tw = None):
+    # the backward needs only the Hybrid
     def step():
-        ffn.forward_train(*a, hy=hy, tw=tw, y=y, check=False)
+        ffn.forward_train(*a, hy=hy, y=y, check=False)
         ffn.backward(*a, hy, dy, out=grads)
 
     # one checked step first: the backup rows fit the Hybrid's capacity
-    ffn.forward_train(*a, hy=hy, tw=tw, y=y)
+    ffn.forward_train(*a, hy=hy, y=y)
+    torch.cuda.synchronize()
+    mem_fwd = torch.cuda.memory_allocated() - mem0
+    ffn.backward(*a, hy, dy, out=grads)
+    torch.cuda.synchronize()
+    mem_sparse = torch.cuda.max_memory_allocated() - mem0
+    mem_hybrid = sum(v.numel() * v.element_size() for v in hy.values()
+                     if isinstance(v, torch.Tensor))
+    mem_ws = ffn._ws["ws"].numel()
+    mem_grads = sum(t.numel() * t.element_size() for t in grads)
 
-    ms, wall_ms, _ = _timed(step, args.steps, args.warmup, torch)
+    steps_ms = []
+    ms, wall_ms, _ = _timed(step, args.steps, args.warmup, torch, per_step=steps_ms)
     ms_p, _, prof = _timed(step, args.steps, 0, torch, [ffn])
     torch.cuda.synchronize()
     ffn.check()
+    torch_step = torch_dense_train(a, dy, args.steps, torch)
     if ffn.hybrid_check(hy) != 0:
         raise RuntimeError("backup rows exceed the Hybrid's capacity")
     cnt = hy["ell_cnt"].cpu().numpy().astype(np.int64)
@@ -542,6 +709,21 @@ def bench_train(args, np, torch, SparseFFN, wl):
         "roofline": rs[0],
         "roofline_other": rs[1:],
         "dense_baseline": None,
+        "step_ms": pct(steps_ms),
+        "torch_dense_train_step": dict(torch_step, speedup_sparse_over_torch_dense=
+                                       torch_step["ms_per_step"] / ms),
+        "peak_memory_bytes": {
+            "sparse_step": int(mem_sparse),
+            "sparse_saved_for_backward": int(mem_hybrid),
+            "sparse_held_after_forward": int(mem_fwd),
+            "sparse_workspace": int(mem_ws), "sparse_fp32_grads": int(mem_grads),
+            "torch_dense_step": torch_step["peak_bytes"],
+            "torch_dense_held_after_forward": torch_step["after_forward_bytes"],
+            "method": "torch.cuda.max_memory_allocated over one step (and memory_allocated "
+                      "after the forward), less what the inputs and weights already held. "
+                      "Sparse: the Hybrid (what the backward reads), y fp32, the four fp32 "
+                      "gradients and the library's one workspace (TwELL inside it). Torch: "
+                      "the autograd graph's saved tensors, y and its bf16 gradients"},
         "kernels_ms_per_step": ks,
         "ms_per_step_wall": wall_ms,
         "ms_per_step_with_kernel_events": ms_p,

@@ -187,9 +187,9 @@ typedef struct sffn_hybrid {
 /* Create a handle for the current HIP device. Validates the descriptor
  * (SFFN_E_ARG / SFFN_E_UNSUPPORTED) before touching the device; returns
  * SFFN_E_UNSUPPORTED when the current device is not gfx950 and SFFN_E_HIP
- * when no device can be queried. Allocates host memory and one 256-byte
- * block of device memory (the handle's status and counter words, zeroed
- * here; freed by sffn_destroy). Per-kernel timing events and the
+ * when no device can be queried. Allocates host memory and one block of
+ * device memory of about 64 KiB (the handle's status word and counters,
+ * zeroed here; freed by sffn_destroy). Per-kernel timing events and the
  * backward's second stream and its two events are created on demand, on
  * the device current at that call. Calls on the handle must be made with
  * the same device current. */

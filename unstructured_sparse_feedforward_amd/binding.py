@@ -220,14 +220,16 @@ class SparseFFN:
         return n.value
 
     def workspace(self, T: int, op: int, device=None):
-        """A 256-byte aligned device buffer of the needed size (cached and
-        grown per operation); returns (pointer, bytes)."""
+        """A 256-byte aligned device buffer of the needed size; returns
+        (pointer, bytes). One buffer serves every operation of the handle
+        (grown to the largest need): the calls run one after the other on
+        the stream, and no call's workspace outlives it."""
         n = self.workspace_bytes(T, op)
-        key = str(op)
-        buf = self._ws.get(key)
+        buf = self._ws.get("ws")
         if buf is None or buf.numel() < n + 256:
+            self._ws.pop("ws", None)
             buf = torch.empty(n + 256, dtype=torch.uint8, device=device or "cuda")
-            self._ws[key] = buf
+            self._ws["ws"] = buf
         p = buf.data_ptr()
         return (p + 255) // 256 * 256, n
 

@@ -32,8 +32,9 @@ struct sffn_handle {
   // grouping runs beside the backup rows' dW products, which leave CUs free
   hipStream_t side = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
-  // device words: [0] capacity-overflow status (read and cleared by
-  // sffn_check), [1] the gate epilogue's overflow-record counter (zeroed by
+  // device state: word 0 the capacity-overflow status (read and cleared by
+  // sffn_check); from byte kCtrOffset the gate epilogue's overflow-record
+  // counters, one per TwELL tile column, kCtrStride words apart (zeroed by
   // the list kernel that follows the gate GEMM; dirty when a call stopped
   // in between, then zeroed before the next gate GEMM)
   int32_t* dstate = nullptr;
@@ -53,6 +54,8 @@ constexpr size_t kScratchBytes = (size_t)128 << 20;
 static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace {
+constexpr size_t kCtrOffset = 256;
+constexpr size_t kStateBytes = kCtrOffset + (size_t)512 * sffn::kCtrStride * 4;
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
@@ -181,8 +184,8 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
     // hidden rows of the dense path: bf16 hi|lo [R, 2F] or fp32 [R, F]
     L.hid = take((size_t)R * F * 4);
     // bf16: the gate pre-activations of overflowing tile rows, one
-    // 128-float record each (a dense-path row overflows at most n_t
-    // tiles), and every (row, tile)'s record number
+    // 128-float record each, R per tile column (a dense-path row
+    // overflows a column at most once), and every (row, tile)'s record
     if (h->desc.dtype == SFFN_BF16) {
       L.zovf = take((size_t)R * nt * kTile * 4);
       L.ovf_map = take((size_t)T * nt * 4);
@@ -300,8 +303,8 @@ sffn_status sffn_create(const sffn_desc* desc, sffn_handle** out) {
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SFFN_E_HIP;
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return SFFN_E_UNSUPPORTED;
   int32_t* dstate = nullptr;
-  if (hipMalloc((void**)&dstate, 256) != hipSuccess) return SFFN_E_HIP;
-  if (hipMemset(dstate, 0, 256) != hipSuccess) {
+  if (hipMalloc((void**)&dstate, kStateBytes) != hipSuccess) return SFFN_E_HIP;
+  if (hipMemset(dstate, 0, kStateBytes) != hipSuccess) {
     (void)hipFree(dstate);
     return SFFN_E_HIP;
   }
@@ -494,11 +497,11 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   // rows the dense path computes: training min(max_backup, R), inference R
   const int mcap = (int)(train ? std::min<int64_t>(hy->max_backup, R) : R);
   int32_t* status = h->dstate;
-  int32_t* ovf_ctr = h->dstate + 1;
+  int32_t* ovf_ctr = h->dstate + kCtrOffset / 4;
   hipError_t e = hipSuccess;
   if (dt == kBF16 && h->ctr_dirty) {
     // a call stopped between its gate GEMM and its list kernel
-    e = hipMemsetAsync(ovf_ctr, 0, 4, stream);
+    e = hipMemsetAsync(ovf_ctr, 0, (size_t)h->n_t * kCtrStride * 4, stream);
     if (e != hipSuccess) return hip_fail(h, e, "overflow-record counter");
     h->ctr_dirty = false;
   }
@@ -521,7 +524,7 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     g.zovf = at<float>(ws, L.zovf);
     g.ovf_map = at<int32_t>(ws, L.ovf_map);
     g.ovf_ctr = ovf_ctr;
-    g.ovf_cap = (int)(R * h->n_t);
+    g.ovf_cap = (int)R;
     h->ctr_dirty = true;
   }
   g.num_cu = h->num_cu;
@@ -560,8 +563,8 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   {
     ProfScope ps(h, SFFN_K_FLAGS, stream);
     const ListArgs lb = {ea.bk, brow, mcap, n_bk, train ? hy->slot : nullptr, status,
-                         dt == kBF16 ? ovf_ctr : nullptr};
-    const ListArgs lf = {t.row_flag, t.flagged, T, t.n_flagged, nullptr, nullptr, nullptr};
+                         dt == kBF16 ? ovf_ctr : nullptr, h->n_t};
+    const ListArgs lf = {t.row_flag, t.flagged, T, t.n_flagged, nullptr, nullptr, nullptr, 0};
     e = launch_backup_list(lb, &lf, T, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "backup list");
@@ -610,7 +613,7 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     f.n_t = h->n_t;
     f.zovf = at<float>(ws, L.zovf);
     f.ovf_map = at<int32_t>(ws, L.ovf_map);
-    f.ovf_cap = (int)(R * h->n_t);
+    f.ovf_cap = (int)R;
     f.part = part;
     // about one tile per CU: with only a few rows a deeper split costs
     // more in partials than it gains in parallel loads
@@ -870,7 +873,7 @@ sffn_status sffn_hybrid_compact(sffn_handle* h, const sffn_twell* tw, const floa
   {
     ProfScope ps(h, SFFN_K_FLAGS, stream);
     const ListArgs lb = {ea.bk, hy->brow, hy->max_backup, hy->n_backup, hy->slot, nullptr,
-                         nullptr};
+                         nullptr, 0};
     e = launch_backup_list(lb, nullptr, T, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "backup list");

@@ -563,7 +563,7 @@ __global__ __launch_bounds__(256) void flag_hidden_kernel(GemmArgs g) {
       // the tile row's saved pre-activations; a record past the capacity
       // was not stored (the call then reports the overflow) and reads as 0
       const int rec = g.ovf_map[t * g.n_t + b];
-      if (rec >= 0 && rec < g.ovf_cap) {
+      if (rec >= 0) {
         a = *(const f32x4_t*)(g.zovf + (int64_t)rec * kTile + (c - b * kTile));
 #pragma unroll
         for (int q = 0; q < 4; ++q) a[q] = a[q] > 0.0f ? a[q] : 0.0f;

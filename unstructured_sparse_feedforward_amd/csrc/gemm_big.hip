@@ -202,23 +202,27 @@ __device__ __forceinline__ void twell_epilogue(const GemmArgs& g, f32x16_t (&acc
         }
         cnt_lane = lane == r0 ? n0c : (lane == r0 + 4 ? n1c : cnt_lane);
         // a tile row that overflows C keeps all its pre-activations in a
-        // record of its own (taken from a device counter), so that the
-        // dense path of its row needs no gate recomputation; the record's
-        // number goes to the row's entry of the tile map
+        // record of its own, so that the dense path of its row needs no
+        // gate recomputation: the tile column's counter (one per column,
+        // so that the few heavy rows' requests spread over n_t addresses)
+        // hands out the column's next record; its number goes to the row's
+        // entry of the tile map
         if (g.zovf != nullptr && (n0c > C || n1c > C)) {
           const bool o0 = n0c > C, o1 = n1c > C;
           int rec = 0;
-          if ((lane == 0 && o0) || (lane == 32 && o1)) rec = atomicAdd(g.ovf_ctr, 1);
+          if ((lane == 0 && o0) || (lane == 32 && o1))
+            rec = atomicAdd(g.ovf_ctr + tb * kCtrStride, 1);
           const int r_0 = __builtin_amdgcn_readlane(rec, 0);
           const int r_1 = __builtin_amdgcn_readlane(rec, 32);
           if (h ? o1 : o0) {
             const int my = h ? r_1 : r_0;
-            if (my < g.ovf_cap) {
-              float* zr = g.zovf + (int64_t)my * kTile + c32;
+            const int id = my < g.ovf_cap ? tb * g.ovf_cap + my : -1;
+            if (id >= 0) {
+              float* zr = g.zovf + (int64_t)id * kTile + c32;
 #pragma unroll
               for (int j = 0; j < 4; ++j) zr[j * 32] = av[j];
             }
-            if (c32 == 0) g.ovf_map[(int64_t)(rbase + r0 + h * 4) * g.n_t + tb] = my;
+            if (c32 == 0) g.ovf_map[(int64_t)(rbase + r0 + h * 4) * g.n_t + tb] = id;
           }
         }
         const uint32_t ro = (uint32_t)r0 * row_entries + half_off;

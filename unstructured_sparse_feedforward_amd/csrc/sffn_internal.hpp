@@ -21,6 +21,7 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kWave = 64;
 constexpr int kTile = 128;  // TwELL tile width W
 constexpr int kSplitCap = 16;  // most K splits of a split-K GEMM
+constexpr int kCtrStride = 32; // int32 words between two device counters (one per 128-byte line)
 
 // ---------------------------------------------------------------- bf16 bits
 
@@ -169,11 +170,12 @@ struct GemmArgs {
   int32_t* tw_cnt;
   uint32_t* ovf;             // [n_t][ovf_words] overflow bits, bit r of word w = row 32w+r
   float* zovf;               // bf16 gate: fp32 pre-activations of the tile rows whose
-                             // count exceeds C, one 128-float record per such tile row
-                             // [ovf_cap, 128], taken from the counter *ovf_ctr; the
-                             // record of row t, tile b is ovf_map[t * n_t + b]
-                             // (written only for those tile rows; records past
-                             // ovf_cap are not stored)
+                             // count exceeds C, one 128-float record per such tile row:
+                             // tile column b owns records [b * ovf_cap, (b + 1) * ovf_cap)
+                             // [n_t * ovf_cap, 128], taken in order from its counter
+                             // ovf_ctr[b * kCtrStride]; the record of row t, tile b is
+                             // ovf_map[t * n_t + b] (-1: past the capacity, not stored;
+                             // written only for the overflowing tile rows)
   int32_t* ovf_map;
   int32_t* ovf_ctr;
   int ovf_cap;
@@ -240,8 +242,9 @@ hipError_t launch_rows(const EllArgs& a, hipStream_t s);
 // true count and (nullable) every row's backup slot (-1 for ELL rows).
 // One workgroup per list (two lists, l1 non-null, in one launch); bk must
 // be 16-byte aligned. When the count exceeds cap and status is set,
-// *status gets bit 0; when reset is set, *reset is zeroed at the end (the
-// gate epilogue's overflow-record counter, consumed by then).
+// *status gets bit 0; when reset is set, reset[i * kCtrStride] is zeroed
+// for i < n_reset at the end (the gate epilogue's overflow-record
+// counters, consumed by then).
 struct ListArgs {
   const uint8_t* bk;
   int32_t* brow;
@@ -250,6 +253,7 @@ struct ListArgs {
   int32_t* slot;
   int32_t* status;
   int32_t* reset;
+  int n_reset;
 };
 hipError_t launch_backup_list(const ListArgs& l0, const ListArgs* l1, int64_t T, hipStream_t s);
 

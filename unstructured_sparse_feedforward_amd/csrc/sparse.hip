@@ -160,8 +160,9 @@ __global__ __launch_bounds__(1024) void backup_list_kernel(ListArgs l0, ListArgs
   if (tid == 0) {
     *n_backup = carry;
     if (L.status && carry > cap) *L.status = 1;
-    if (L.reset) *L.reset = 0;
   }
+  if (L.reset)
+    for (int i = tid; i < L.n_reset; i += 1024) L.reset[i * kCtrStride] = 0;
 }
 
 // Sum over the 8 lanes of each lane octet, result in all 8 (quad swaps,

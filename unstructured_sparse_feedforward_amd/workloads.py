@@ -97,7 +97,7 @@ STACK_LAYER = Workload("stack18_T16384_d2048_F5632_bf16", T=16384, d=2048,
 TRAIN_HYBRID = Workload("train_T8192_d2048_F5632_bf16_nnz29_K64", T=8192,
                         d=2048, F=5632, gated=True, dtype="bf16", nnz=29,
                         twell_cap=16, outlier_frac=0.05, ell_cap=64,
-                        train=True)
+                        dense_rows=512, train=True)
 
 
 def stack_layer(i: int) -> Workload:
