@@ -95,6 +95,49 @@ def dense_ffn_bf16_hidden(x, w_gate, w_up, w_down):
     return hb @ np.asarray(w_down, dtype=np.float64)
 
 
+def dense_ffn_bf16_store(x, w_gate, w_up, w_down):
+    """The layer whose stored activations are bfloat16: the gate activations
+    A = ReLU(x W_g) and the up values U = x W_u are each rounded once to
+    bf16 (the values the TwELL/Hybrid formats hold when they store 16-bit
+    activations, halving their bytes) and the layer computes with the
+    stored values: H = bf16(A) * bf16(U), y = H W_d (non-gated:
+    y = bf16(A) W_2). Z, the products and y stay exact."""
+    _, it = dense_ffn(x, w_gate, w_up, w_down)
+    a_s = round_bf16(it["a"])
+    h = a_s if it["u"] is None else a_s * round_bf16(it["u"])
+    return h @ np.asarray(w_down, dtype=np.float64)
+
+
+def backward_bf16_store(x, w_gate, w_up, w_down, dy, l1_coeff=0.0, mask=None):
+    """Gradients of :func:`dense_ffn_bf16_store`, with the roundings passed
+    through unchanged (their derivative taken as 1): the backward reads the
+    stored values. With A_s = bf16(Z * M), U_s = bf16(U) and M = 1[Z > 0]
+    (or the given mask): dH = dy W_d^T; dU = dH * A_s;
+    dZ = dH * U_s * M + l1 * M; dx = dZ W_g^T + dU W_u^T; dW_g = x^T dZ;
+    dW_u = x^T dU; dW_d = (A_s * U_s)^T dy. Non-gated: dZ = dH * M + l1 * M,
+    dx = dZ W_1^T, dW_1 = x^T dZ, dW_2 = A_s^T dy."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    wg = np.asarray(w_gate, dtype=np.float64)
+    wd = np.asarray(w_down, dtype=np.float64)
+    _, it = dense_ffn(x, w_gate, w_up, w_down)
+    if mask is None:
+        m = (it["z"] > 0).astype(np.float64)
+    else:
+        m = np.asarray(mask, dtype=bool).astype(np.float64)
+    a_s = round_bf16(it["z"] * m)
+    dh = dy @ wd.T
+    if w_up is None:
+        dz = dh * m + l1_coeff * m
+        return dict(dx=dz @ wg.T, dw_gate=x.T @ dz, dw_up=None, dw_down=a_s.T @ dy)
+    wu = np.asarray(w_up, dtype=np.float64)
+    u_s = round_bf16(it["u"])
+    du = dh * a_s
+    dz = dh * u_s * m + l1_coeff * m
+    return dict(dx=dz @ wg.T + du @ wu.T, dw_gate=x.T @ dz, dw_up=x.T @ du,
+                dw_down=(a_s * u_s).T @ dy)
+
+
 # ---------------------------------------------------------------------------
 # TwELL
 # ---------------------------------------------------------------------------

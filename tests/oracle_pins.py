@@ -262,6 +262,86 @@ def check_bf16_hidden_vs_torch(orc):
         assert gated is False or bool((hb != h).any())
 
 
+def check_bf16_store_golden(orc):
+    """Hand-worked layer with bf16 stored activations, forward and backward."""
+    g = _golden("ffn_bf16_store_1x2x2.json")
+    args = [np.array(g[k]) for k in ("x", "w_gate", "w_up", "w_down")]
+    assert np.array_equal(orc.dense_ffn_bf16_store(*args), np.array(g["y"]))
+    gr = orc.backward_bf16_store(*args, np.array(g["dy"]))
+    for k in ("dx", "dw_gate", "dw_up", "dw_down"):
+        assert np.array_equal(gr[k], np.array(g[k])), k
+
+
+def _ste_bf16(t):
+    """torch: the value rounded to bf16 in the forward, the identity in the
+    backward (exact for values that float32 holds exactly)."""
+    return t + (t.float().to(torch.bfloat16).double() - t).detach()
+
+
+def check_bf16_store_vs_autograd(orc):
+    """Integer inputs keep every A, U and product exact in float32, so
+    torch's own bf16 conversion rounds them as the storage does; torch
+    autograd through the rounding-as-identity gives the gradients. A and U
+    span values above 256, where bf16 drops bits."""
+    r = _rng(16)
+    for gated in (True, False):
+        for l1 in (0.0, 0.5):
+            x = r.integers(-4, 5, (7, 6)).astype(np.float64)
+            wg = r.integers(-60, 61, (6, 16)).astype(np.float64)
+            wu = r.integers(-60, 61, (6, 16)).astype(np.float64) if gated else None
+            wd = r.integers(-3, 4, (16, 6)).astype(np.float64)
+            dy = r.integers(-2, 3, (7, 6)).astype(np.float64)
+            tx = torch.tensor(x, requires_grad=True)
+            twg = torch.tensor(wg, requires_grad=True)
+            twd = torch.tensor(wd, requires_grad=True)
+            z = tx @ twg
+            assert float(z.abs().max()) > 256
+            a = _ste_bf16(torch.relu(z))
+            if gated:
+                twu = torch.tensor(wu, requires_grad=True)
+                h = a * _ste_bf16(tx @ twu)
+            else:
+                h = a
+            y = h @ twd
+            assert np.array_equal(orc.dense_ffn_bf16_store(x, wg, wu, wd), y.detach().numpy())
+            # the L1 term acts on the activation as the layer computes it
+            loss = (y * torch.from_numpy(dy)).sum() + l1 * torch.relu(z).sum()
+            loss.backward()
+            gr = orc.backward_bf16_store(x, wg, wu, wd, dy, l1_coeff=l1)
+            assert np.allclose(gr["dx"], tx.grad.numpy(), rtol=1e-12, atol=1e-9)
+            assert np.allclose(gr["dw_gate"], twg.grad.numpy(), rtol=1e-12, atol=1e-9)
+            assert np.allclose(gr["dw_down"], twd.grad.numpy(), rtol=1e-12, atol=1e-9)
+            if gated:
+                assert np.allclose(gr["dw_up"], twu.grad.numpy(), rtol=1e-12, atol=1e-9)
+            # a given active set (a third of the entries flipped): A = Z * M
+            m = (x @ wg > 0) ^ (r.random((7, 16)) < 0.33)
+            tx.grad = twg.grad = twd.grad = None
+            zm = (tx @ twg) * torch.from_numpy(m.astype(np.float64))
+            a = _ste_bf16(zm)
+            h = a * _ste_bf16(tx @ twu) if gated else a
+            ((h @ twd) * torch.from_numpy(dy)).sum().add(l1 * zm.sum()).backward()
+            gm = orc.backward_bf16_store(x, wg, wu, wd, dy, l1_coeff=l1, mask=m)
+            assert np.allclose(gm["dx"], tx.grad.numpy(), rtol=1e-12, atol=1e-9)
+            assert np.allclose(gm["dw_gate"], twg.grad.numpy(), rtol=1e-12, atol=1e-9)
+            assert np.allclose(gm["dw_down"], twd.grad.numpy(), rtol=1e-12, atol=1e-9)
+
+
+def check_bf16_store_exact_values(orc):
+    """When every A and U is a bf16 value already, the storage changes
+    nothing: the plain layer and its backward come back exactly."""
+    r = _rng(17)
+    x = r.integers(-3, 4, (6, 5)).astype(np.float64)
+    wg = r.integers(-2, 3, (5, 9)).astype(np.float64)
+    wu = r.integers(-2, 3, (5, 9)).astype(np.float64)
+    wd = r.integers(-2, 3, (9, 5)).astype(np.float64)
+    dy = r.integers(-2, 3, (6, 5)).astype(np.float64)
+    y, _ = orc.dense_ffn(x, wg, wu, wd)
+    assert np.array_equal(orc.dense_ffn_bf16_store(x, wg, wu, wd), y)
+    a, b = orc.backward_bf16_store(x, wg, wu, wd, dy, 0.25), orc.backward(x, wg, wu, wd, dy, 0.25)
+    for k in ("dx", "dw_gate", "dw_up", "dw_down"):
+        assert np.array_equal(a[k], b[k]), k
+
+
 # --------------------------------------------------------------- sparse layer
 
 def check_sparse_equals_dense(orc):

@@ -20,8 +20,8 @@ MUTATIONS = [
     ("pack: flag at cnt == C", "row_flag = (cnt > C).any(axis=1)",
      "row_flag = (cnt >= C).any(axis=1)"),
     ("pack: capped count", "cnt[t, b] = len(cols)", "cnt[t, b] = min(len(cols), C)"),
-    ("dense: ReLU dropped", "h = a * u", "h = z * u"),
-    ("dense: up projection dropped", "h = a * u", "h = a"),
+    ("dense: ReLU dropped", "h = a * u\n    y = h @", "h = z * u\n    y = h @"),
+    ("dense: up projection dropped", "h = a * u\n    y = h @", "h = a\n    y = h @"),
     ("relu: leaky", "return np.where(z > 0, z, 0.0)",
      "return np.where(z > 0, z, 0.01 * z)"),
     ("sparse: up projection dropped", "h = a if wu is None else a * float(x[t] @ wu[:, j])",
@@ -45,9 +45,21 @@ MUTATIONS = [
      'hb = round_bf16(it["a"]) * (1.0 if it["u"] is None else round_bf16(it["u"]))'),
     ("bf16 layer: rounds before the ReLU", 'hb = round_bf16(it["h"])',
      'hb = relu(round_bf16(it["z"])) * (1.0 if it["u"] is None else it["u"])'),
-    ("backward: given mask ignored", "m = np.asarray(mask, dtype=bool).astype(np.float64)",
-     'm = (it["z"] > 0).astype(np.float64)'),
+    ("backward: given mask ignored",
+     'm = np.asarray(mask, dtype=bool).astype(np.float64)\n        a = it["z"] * m',
+     'm = (it["z"] > 0).astype(np.float64)\n        a = it["z"] * m'),
+    ("bf16 store: given mask ignored",
+     'm = np.asarray(mask, dtype=bool).astype(np.float64)\n    a_s = round_bf16',
+     'm = (it["z"] > 0).astype(np.float64)\n    a_s = round_bf16'),
     ("backward: given mask not applied to A", 'a = it["z"] * m', 'a = it["a"]'),
+    ("bf16 store: U not rounded in the forward", 'h = a_s if it["u"] is None else a_s * round_bf16(it["u"])',
+     'h = a_s if it["u"] is None else a_s * it["u"]'),
+    ("bf16 store: A not rounded in the forward", 'a_s = round_bf16(it["a"])\n    h = a_s', 'a_s = it["a"]\n    h = a_s'),
+    ("bf16 store: y rounded instead", 'return h @ np.asarray(w_down, dtype=np.float64)\n\n\ndef backward_bf16_store',
+     'return round_bf16(h @ np.asarray(w_down, dtype=np.float64))\n\n\ndef backward_bf16_store'),
+    ("bf16 store: backward reads the unrounded U", "u_s = round_bf16(it[\"u\"])", 'u_s = it["u"]'),
+    ("bf16 store: backward reads the unrounded A", "a_s = round_bf16(it[\"z\"] * m)", 'a_s = it["z"] * m'),
+    ("bf16 store: dW_d from the unrounded H", "dw_down=(a_s * u_s).T @ dy)", 'dw_down=it["h"].T @ dy)'),
     ("hybrid: bk_u from A", 'out["bk_u"] = np.asarray(u_dense, dtype=np.float64)[brow]',
      'out["bk_u"] = np.asarray(a_dense, dtype=np.float64)[brow]'),
     ("hybrid: bk_u rows of the ELL rows", 'out["bk_u"] = np.asarray(u_dense, dtype=np.float64)[brow]',
@@ -58,7 +70,7 @@ MUTATIONS = [
 @pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
 def test_mutant_is_caught(name, old, new):
     src = open(SRC).read()
-    assert src.count(old) >= 1, f"mutation target not found: {old}"
+    assert src.count(old) == 1, f"mutation target not found or not unique: {old}"
     mod = types.ModuleType("oracle_mutant")
     exec(compile(src.replace(old, new, 1), "oracle_mutant", "exec"), mod.__dict__)
     failures = run_all(mod)
