@@ -104,6 +104,14 @@ typedef struct sffn_handle sffn_handle;
  *              as n_t * C.
  *   dtype      SFFN_BF16 (bf16 inputs, fp32 accumulation) or SFFN_F32
  *              (fp32 inputs and fp32 arithmetic throughout)
+ *   store_dtype  SFFN_F32 (0): the stored activations (TwELL values, ELL
+ *              a and u, backup rows' a and u) are float32, the accumulator
+ *              values. SFFN_BF16 (bf16 layers only): they are bf16, rounded
+ *              once (to nearest, ties to even) where they are stored, which
+ *              halves the format's value bytes; the layer then computes
+ *              with the stored values, H = bf16(a) * bf16(u) (the dense
+ *              path's rows too), and the backward reads them, so the
+ *              roundings pass gradients unchanged.
  *   dense_rows R, the most rows one call computes on the dense path
  *              (rows routed away from the ELL at inference, backup rows in
  *              training); the workspace holds R dense rows. 0 means T
@@ -119,12 +127,15 @@ typedef struct sffn_desc {
   int32_t ell_cap;
   int32_t dtype;
   int32_t dense_rows;
+  int32_t store_dtype;
 } sffn_desc;
 
 /*
  * TwELL buffers (device, caller-owned). n_t = F / W.
  *   val       [T, n_t, C] float32   slot values, the gate pre-activation
  *                                   z[t, j] (> 0) as accumulated in fp32
+ *                                   (bf16 bits, uint16, when
+ *                                   desc.store_dtype is SFFN_BF16)
  *   idx       [T, n_t, C] uint16    slot neuron ids j (global)
  *                                   Slots s >= min(cnt, C) of a (row, tile)
  *                                   are not written and hold unspecified
@@ -139,7 +150,7 @@ typedef struct sffn_desc {
  * row keeps its first C slots per tile and the layer computes it densely.
  */
 typedef struct sffn_twell {
-  float*    val;
+  void*     val;
   uint16_t* idx;
   int32_t*  cnt;
   uint8_t*  row_flag;
@@ -157,6 +168,8 @@ typedef struct sffn_twell {
  *   ell_a      [T, K]   float32  a = z > 0 of each ELL slot
  *   ell_u      [T, K]   float32  u = x . W_u[j] of each ELL slot (gated
  *                                layers; written by sffn_forward_train)
+ *              (ell_a, ell_u, bk_a and bk_u hold bf16 bits, uint16,
+ *              when desc.store_dtype is SFFN_BF16)
  *   ell_idx    [T, K]   uint16   neuron ids
  *   ell_cnt    [T]      int32    slots used (0 for backup rows)
  *                                (slots >= ell_cnt are unspecified)
@@ -172,15 +185,15 @@ typedef struct sffn_twell {
  *   max_backup capacity of brow, bk_a and bk_u in rows
  */
 typedef struct sffn_hybrid {
-  float*    ell_a;
-  float*    ell_u;
+  void*     ell_a;
+  void*     ell_u;
   uint16_t* ell_idx;
   int32_t*  ell_cnt;
   int32_t*  slot;
   int32_t*  brow;
   int32_t*  n_backup;
-  float*    bk_a;
-  float*    bk_u;
+  void*     bk_a;
+  void*     bk_u;
   int64_t   max_backup;
 } sffn_hybrid;
 

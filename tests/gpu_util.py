@@ -32,7 +32,8 @@ def layer(inp, **kw):
     return SparseFFN(w.d, w.F, gated=w.gated, twell_cap=kw.get("C", w.twell_cap),
                      tile=w.tile, ell_cap=kw.get("ell_cap", w.ell_cap),
                      dense_rows=kw.get("dense_rows", w.dense_rows),
-                     dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+                     dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32,
+                     store_dtype=kw.get("store_dtype", torch.float32))
 
 
 def rel_fro(got, ref):
@@ -57,9 +58,14 @@ def assert_close_f32(got, ref, what=""):
     assert r <= 1e-5, f"{what}: relative Frobenius error {r:.3e} > 1e-5"
 
 
+def to_np(v):
+    """Host copy; bf16 tensors come back as float32 values."""
+    return v.float().cpu().numpy() if v.dtype == torch.bfloat16 else v.cpu().numpy()
+
+
 def twell_np(tw):
     torch.cuda.synchronize()
-    out = {k: v.cpu().numpy() for k, v in tw.items()}
+    out = {k: to_np(v) for k, v in tw.items()}
     out["idx"] = out["idx"].view(np.uint16).astype(np.int64)
     out["n_flagged"] = int(out["n_flagged"][0])
     return out

@@ -10,7 +10,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_close_bf16, assert_close_f32, dev, math_weights, rel_fro, twell_np
+from gpu_util import (assert_close_bf16, assert_close_f32, dev, math_weights, rel_fro, to_np,
+                      twell_np)
 from unstructured_sparse_feedforward_amd import SparseFFN
 from unstructured_sparse_feedforward_amd import binding as B
 from unstructured_sparse_feedforward_amd import workloads as wl
@@ -24,7 +25,7 @@ def _print(*a):
 
 def hybrid_np(hy):
     torch.cuda.synchronize()
-    out = {k: (v.cpu().numpy() if isinstance(v, torch.Tensor) else v) for k, v in hy.items()}
+    out = {k: (to_np(v) if isinstance(v, torch.Tensor) else v) for k, v in hy.items()}
     out["ell_idx"] = out["ell_idx"].view(np.uint16).astype(np.int64)
     out["n_backup"] = int(out["n_backup"][0])
     return out

@@ -45,7 +45,8 @@ class SffnDesc(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("gated", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("twell_cap", ctypes.c_int32), ("ell_cap", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("dense_rows", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("dense_rows", ctypes.c_int32),
+                ("store_dtype", ctypes.c_int32)]
 
 
 class SffnTwell(ctypes.Structure):
@@ -158,11 +159,14 @@ class SparseFFN:
 
     def __init__(self, d: int, d_ff: int, gated: bool = True, twell_cap: int = 8,
                  tile: int = 128, ell_cap: int = 0, dtype: torch.dtype = torch.bfloat16,
-                 dense_rows: int = DEFAULT_DENSE_ROWS):
+                 dense_rows: int = DEFAULT_DENSE_ROWS,
+                 store_dtype: torch.dtype = torch.float32):
         self.lib = load_library()
         self.d, self.d_ff, self.gated = d, d_ff, gated
         self.tile, self.twell_cap, self.ell_cap = tile, twell_cap, ell_cap
         self.dtype = dtype
+        # dtype of the stored activations (TwELL values, Hybrid a and u)
+        self.store_dtype = store_dtype
         self.n_t = d_ff // tile
         self.h = None
         self._ws: Dict[str, torch.Tensor] = {}
@@ -174,7 +178,8 @@ class SparseFFN:
         self.desc = SffnDesc(self.d, self.d_ff, int(self.gated), self.tile, self.twell_cap,
                              self.ell_cap,
                              SFFN_BF16 if self.dtype == torch.bfloat16 else SFFN_F32,
-                             dense_rows)
+                             dense_rows,
+                             SFFN_BF16 if self.store_dtype == torch.bfloat16 else SFFN_F32)
         h = ctypes.c_void_p()
         st = self.lib.sffn_create(ctypes.byref(self.desc), ctypes.byref(h))
         if st != SFFN_OK:
@@ -236,7 +241,7 @@ class SparseFFN:
     def new_twell(self, T: int, device="cuda") -> Dict[str, torch.Tensor]:
         C, nt = self.twell_cap, self.n_t
         return dict(
-            val=torch.empty((T, nt, C), dtype=torch.float32, device=device),
+            val=torch.empty((T, nt, C), dtype=self.store_dtype, device=device),
             idx=torch.empty((T, nt, C), dtype=torch.int16, device=device),  # uint16 bits
             cnt=torch.empty((T, nt), dtype=torch.int32, device=device),
             row_flag=torch.empty((T,), dtype=torch.uint8, device=device),
@@ -314,7 +319,7 @@ class SparseFFN:
         if max_backup is None:
             max_backup = min(T, self.dense_rows) if self.dense_rows > 0 else T
         R = max_backup
-        f32 = dict(dtype=torch.float32, device=device)
+        f32 = dict(dtype=self.store_dtype, device=device)
         return dict(
             ell_a=torch.empty((T, K), **f32),
             ell_u=torch.empty((T, K), **f32) if self.gated else None,

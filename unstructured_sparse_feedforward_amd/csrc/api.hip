@@ -102,6 +102,9 @@ sffn_status validate_desc(const sffn_desc* d) {
   if (d->d <= 0 || d->d_ff <= 0 || d->tile <= 0 || d->twell_cap <= 0 || d->ell_cap < 0 ||
       d->dense_rows < 0)
     return SFFN_E_ARG;
+  if (d->store_dtype != SFFN_F32 && d->store_dtype != SFFN_BF16) return SFFN_E_ARG;
+  // 16-bit stored activations serve bf16 layers
+  if (d->store_dtype == SFFN_BF16 && d->dtype != SFFN_BF16) return SFFN_E_UNSUPPORTED;
   if (d->tile != kTile) return SFFN_E_UNSUPPORTED;
   if (d->d_ff % kTile != 0 || d->d_ff > 65408) return SFFN_E_UNSUPPORTED;
   if (d->twell_cap > kTile) return SFFN_E_UNSUPPORTED;
@@ -114,6 +117,9 @@ sffn_status validate_desc(const sffn_desc* d) {
 
 Dtype dt_of(const sffn_handle* h) { return h->desc.dtype == SFFN_BF16 ? kBF16 : kF32; }
 size_t esize(const sffn_handle* h) { return h->desc.dtype == SFFN_BF16 ? 2 : 4; }
+// stored activation values: bf16 bits or float32
+int sb_of(const sffn_handle* h) { return h->desc.store_dtype == SFFN_BF16 ? 1 : 0; }
+size_t ssize(const sffn_handle* h) { return h->desc.store_dtype == SFFN_BF16 ? 2 : 4; }
 int ovf_words(int64_t T) { return (int)((T + 31) / 32); }
 constexpr int kSplitMax = kSplitCap;
 
@@ -165,12 +171,12 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
     const int64_t R = dense_cap(h, T);
     int ns, epl;
     slice_shape(dt_of(h), (int)d, &ns, &epl);
-    L.ell_a = take((size_t)T * K * 4);
+    L.ell_a = take((size_t)T * K * ssize(h));
     L.ell_idx = take((size_t)T * K * 2);
     L.ell_cnt = take((size_t)T * 4);
     L.bk = take((size_t)T);
     L.upart = take((size_t)ns * T * Kp * 4);
-    L.tw_val = take((size_t)T * nt * C * 4);
+    L.tw_val = take((size_t)T * nt * C * ssize(h));
     L.tw_idx = take((size_t)T * nt * C * 2);
     L.tw_cnt = take((size_t)T * nt * 4);
     L.tw_flag = take((size_t)T);
@@ -365,7 +371,7 @@ sffn_status sffn_pack_twell(sffn_handle* h, const float* z, int64_t T, const sff
   hipError_t e;
   {
     ProfScope ps(h, SFFN_K_PACK, stream);
-    e = launch_pack(z, T, h->desc.d_ff, h->desc.twell_cap, tw->val, tw->idx, tw->cnt, ovf, ow,
+    e = launch_pack(z, T, h->desc.d_ff, h->desc.twell_cap, sb_of(h), tw->val, tw->idx, tw->cnt, ovf, ow,
                     stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "pack");
@@ -484,7 +490,7 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   if (tw) {
     t = *tw;
   } else {
-    t.val = at<float>(ws, L.tw_val);
+    t.val = at<char>(ws, L.tw_val);
     t.idx = at<uint16_t>(ws, L.tw_idx);
     t.cnt = at<int32_t>(ws, L.tw_cnt);
     t.row_flag = at<uint8_t>(ws, L.tw_flag);
@@ -520,6 +526,7 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   g.tw_cnt = t.cnt;
   g.C = D.twell_cap;
   g.n_t = h->n_t;
+  g.store_bf16 = sb_of(h);
   if (dt == kBF16) {
     g.zovf = at<float>(ws, L.zovf);
     g.ovf_map = at<int32_t>(ws, L.ovf_map);
@@ -544,7 +551,8 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   ea.n_t = h->n_t;
   ea.C = D.twell_cap;
   ea.K = K;
-  ea.ell_a = train ? hy->ell_a : at<float>(ws, L.ell_a);
+  ea.ell_a = train ? hy->ell_a : at<char>(ws, L.ell_a);
+  ea.store_bf16 = sb_of(h);
   ea.ell_idx = train ? hy->ell_idx : at<uint16_t>(ws, L.ell_idx);
   ea.ell_cnt = train ? hy->ell_cnt : at<int32_t>(ws, L.ell_cnt);
   ea.row_flag = t.row_flag;
@@ -611,6 +619,7 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     f.tw_cnt = t.cnt;
     f.C = D.twell_cap;
     f.n_t = h->n_t;
+    f.store_bf16 = sb_of(h);
     f.zovf = at<float>(ws, L.zovf);
     f.ovf_map = at<int32_t>(ws, L.ovf_map);
     f.ovf_cap = (int)R;
@@ -733,6 +742,7 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   sa.Kp = Kp;
   sa.upart = at<float>(ws, L.upart);
   sa.ell_u = (train && D.gated) ? hy->ell_u : nullptr;
+  sa.store_bf16 = sb_of(h);
   sa.y = y;
   if (D.gated) {
     ProfScope ps(h, SFFN_K_SPARSE_UP, stream);
@@ -863,6 +873,7 @@ sffn_status sffn_hybrid_compact(sffn_handle* h, const sffn_twell* tw, const floa
   ea.ell_idx = hy->ell_idx;
   ea.ell_cnt = hy->ell_cnt;
   ea.row_flag = nullptr;
+  ea.store_bf16 = sb_of(h);
   ea.bk = at<uint8_t>(ws, L.bk);
   hipError_t e;
   {
@@ -878,7 +889,7 @@ sffn_status sffn_hybrid_compact(sffn_handle* h, const sffn_twell* tw, const floa
   }
   if (e != hipSuccess) return hip_fail(h, e, "backup list");
   if (z && hy->max_backup > 0) {
-    e = launch_gather_relu_rows(z, h->desc.d_ff, hy->brow, hy->n_backup,
+    e = launch_gather_relu_rows(z, h->desc.d_ff, sb_of(h), hy->brow, hy->n_backup,
                                 (int)std::min<int64_t>(hy->max_backup, T), hy->bk_a, stream);
     if (e != hipSuccess) return hip_fail(h, e, "backup rows");
   }
@@ -943,6 +954,7 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
   ba.wu = w_up;
   ba.ell_a = hy->ell_a;
   ba.ell_u = hy->ell_u;
+  ba.store_bf16 = sb_of(h);
   ba.ell_idx = hy->ell_idx;
   ba.ell_cnt = hy->ell_cnt;
   ba.slot = hy->slot;

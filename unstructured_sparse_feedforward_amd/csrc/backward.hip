@@ -40,13 +40,13 @@ __global__ __launch_bounds__(256) void dzu_kernel(BwdArgs a) {
     const int64_t q = t * a.K + k;
     float gz, gu = 0.0f, hv;
     if constexpr (GATED) {
-      const float av = a.ell_a[q], uv = a.ell_u[q];
+      const float av = sload(a.ell_a, q, a.store_bf16), uv = sload(a.ell_u, q, a.store_bf16);
       gu = dh * av;
       gz = dh * uv + a.l1;
       hv = av * uv;
     } else {
       gz = dh + a.l1;
-      hv = a.ell_a[q];
+      hv = sload(a.ell_a, q, a.store_bf16);
     }
     a.drec[q] = f32x4_t{__int_as_float((int)a.ell_idx[q]), gz, gu, hv};
   }
@@ -566,9 +566,9 @@ __global__ __launch_bounds__(256) void backup_grad_kernel(BwdArgs a) {
       if (r < R) {
         const int64_t q = (int64_t)r * F + j;
         const f32x2_t dh = *(const f32x2_t*)(a.dH + q);
-        const f32x2_t av = *(const f32x2_t*)(a.bk_a + q);
+        const f32x2_t av = sload2(a.bk_a, q, a.store_bf16);
         f32x2_t uv = {0.0f, 0.0f};
-        if (GATED) uv = *(const f32x2_t*)(a.bk_u + q);
+        if (GATED) uv = sload2(a.bk_u, q, a.store_bf16);
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const bool on = av[e] > 0.0f;

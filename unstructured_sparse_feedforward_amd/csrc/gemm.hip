@@ -306,8 +306,9 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
               const int n = n0 + wc * 64 + j * 32 + (lane & 31);
               if (m < M) {
                 const float zv = acc[0][i][j][q];
-                g.out_a[(int64_t)m * g.ldo_au + n] = zv > 0.0f ? zv : 0.0f;
-                if (NB == 2 && g.out_u) g.out_u[(int64_t)m * g.ldo_au + n] = acc[NB - 1][i][j][q];
+                sstore(g.out_a, (int64_t)m * g.ldo_au + n, zv > 0.0f ? zv : 0.0f, g.store_bf16);
+                if (NB == 2 && g.out_u)
+                  sstore(g.out_u, (int64_t)m * g.ldo_au + n, acc[NB - 1][i][j][q], g.store_bf16);
               }
             }
       }
@@ -344,8 +345,9 @@ __global__ __launch_bounds__(NT) void gemm_kernel(GemmArgs g) {
       const int col = n0 + 2 * lane;
       if constexpr (EPI == kEpiTwell) {
         const int64_t slot = ((int64_t)m * g.n_t + tn);
-        const int n = twell_pack_row(v[0], v[1], lane, n0, g.C, g.tw_val + slot * g.C,
-                                     g.tw_idx + slot * g.C, g.tw_cnt + slot);
+        const int n = twell_pack_row(v[0], v[1], lane, n0, g.C,
+                                     (char*)g.tw_val + slot * g.C * (g.store_bf16 ? 2 : 4),
+                                     g.tw_idx + slot * g.C, g.tw_cnt + slot, g.store_bf16);
         bits |= (n > g.C ? 1u : 0u) << q;
       } else if constexpr (EPI == kEpiStoreF32) {
         float* dst;
@@ -431,8 +433,8 @@ __global__ __launch_bounds__(256) void hidden_combine_kernel(GemmArgs g) {
       h[q] = NB == 2 ? a[q] * u[q] : a[q];
     }
     if (g.out_a) {
-      *(f32x4_t*)(g.out_a + (int64_t)m * g.ldo_au + c) = a;
-      if (NB == 2 && g.out_u) *(f32x4_t*)(g.out_u + (int64_t)m * g.ldo_au + c) = u;
+      sstore4(g.out_a, (int64_t)m * g.ldo_au + c, a, g.store_bf16);
+      if (NB == 2 && g.out_u) sstore4(g.out_u, (int64_t)m * g.ldo_au + c, u, g.store_bf16);
     }
     if constexpr (sizeof(E) == 4) {
       *(f32x4_t*)((float*)g.out + (int64_t)m * g.ldo + c) = h;
@@ -558,6 +560,7 @@ __global__ __launch_bounds__(256) void flag_hidden_kernel(GemmArgs g) {
     const int64_t t = g.a_rows[m];
     const int b = c / kTile;
     const int cnt = g.tw_cnt[t * g.n_t + b];
+    const int sb = g.store_bf16;
     f32x4_t a = {0.0f, 0.0f, 0.0f, 0.0f};
     if (cnt > g.C) {
       // the tile row's saved pre-activations; a record past the capacity
@@ -566,27 +569,31 @@ __global__ __launch_bounds__(256) void flag_hidden_kernel(GemmArgs g) {
       if (rec >= 0) {
         a = *(const f32x4_t*)(g.zovf + (int64_t)rec * kTile + (c - b * kTile));
 #pragma unroll
-        for (int q = 0; q < 4; ++q) a[q] = a[q] > 0.0f ? a[q] : 0.0f;
+        for (int q = 0; q < 4; ++q) a[q] = sround(a[q] > 0.0f ? a[q] : 0.0f, sb);
       }
     } else {
       const int64_t e0 = (t * g.n_t + b) * g.C;
       for (int k = 0; k < cnt; ++k) {
         const int d = (int)g.tw_idx[e0 + k] - c;
-        if (d >= 0 && d < 4) a[d] = g.tw_val[e0 + k];
+        if (d >= 0 && d < 4) a[d] = sload(g.tw_val, e0 + k, sb);
       }
     }
+    // with 16-bit storage a and u are the stored (rounded) values, and
+    // H = a u is exact in fp32 (two 8-bit significands)
     f32x4_t u = {0.0f, 0.0f, 0.0f, 0.0f};
     if (NB == 2) {
 #pragma unroll
       for (int k = 0; k < kSplitCap; ++k)
         if (k < S) u += pv[k];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) u[q] = sround(u[q], sb);
     }
     f32x4_t h;
 #pragma unroll
     for (int q = 0; q < 4; ++q) h[q] = NB == 2 ? a[q] * u[q] : a[q];
     if (g.out_a) {
-      *(f32x4_t*)(g.out_a + (int64_t)m * g.ldo_au + c) = a;
-      if (NB == 2 && g.out_u) *(f32x4_t*)(g.out_u + (int64_t)m * g.ldo_au + c) = u;
+      sstore4(g.out_a, (int64_t)m * g.ldo_au + c, a, sb);
+      if (NB == 2 && g.out_u) sstore4(g.out_u, (int64_t)m * g.ldo_au + c, u, sb);
     }
     uint16_t* dst = (uint16_t*)g.out + (int64_t)m * g.ldo;
     uint32_t hi[4], lo[4];

@@ -171,7 +171,8 @@ __device__ __forceinline__ void twell_epilogue(const GemmArgs& g, f32x16_t (&acc
     // this block's first entry of tile tb; the block spans 32 rows, so
     // every entry offset from it fits 32 bits
     const int64_t e0 = ((int64_t)rbase * g.n_t + tb) * C;
-    char* vbase = (char*)(g.tw_val + e0);
+    const int sb = g.store_bf16;
+    char* vbase = (char*)g.tw_val + e0 * (sb ? 2 : 4);
     char* ibase = (char*)(g.tw_idx + e0);
     int cnt_lane = 0;  // lane r < 32 collects the count of row rbase + r
 #pragma unroll
@@ -235,7 +236,8 @@ __device__ __forceinline__ void twell_epilogue(const GemmArgs& g, f32x16_t (&acc
                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
             if (rank < C) {
               const uint32_t e = ro + (uint32_t)rank;
-              *(float*)(vbase + e * 4u) = av[j];
+              if (sb) *(uint16_t*)(vbase + e * 2u) = (uint16_t)f32_to_bf16(av[j]);
+              else *(float*)(vbase + e * 4u) = av[j];
               *(uint16_t*)(ibase + e * 2u) = (uint16_t)(tb * kTile + j * 32 + c32);
             }
           }

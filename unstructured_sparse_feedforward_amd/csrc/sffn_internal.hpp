@@ -34,6 +34,40 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// ---------------------------------------------------------------- stored activations
+
+// Stored activation values (TwELL values, ELL a and u, backup rows' a and
+// u) are float32, or bf16 bits when the layer stores 16-bit activations
+// (sb != 0): then a value is rounded once, to nearest even, where it is
+// stored, and the layer computes with the stored value.
+__device__ __forceinline__ float sround(float v, int sb) {
+  return sb ? __uint_as_float(f32_to_bf16(v) << 16) : v;
+}
+__device__ __forceinline__ float sload(const void* p, int64_t i, int sb) {
+  return sb ? bf16lo(((const uint16_t*)p)[i]) : ((const float*)p)[i];
+}
+__device__ __forceinline__ void sstore(void* p, int64_t i, float v, int sb) {
+  if (sb) ((uint16_t*)p)[i] = (uint16_t)f32_to_bf16(v);
+  else ((float*)p)[i] = v;
+}
+// four consecutive values (16-byte aligned fp32 / 8-byte aligned bf16)
+__device__ __forceinline__ void sstore4(void* p, int64_t i, f32x4_t v, int sb) {
+  if (sb) {
+    *(u32x2_t*)((uint16_t*)p + i) = u32x2_t{f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16),
+                                            f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16)};
+  } else {
+    *(f32x4_t*)((float*)p + i) = v;
+  }
+}
+// two consecutive values (8-byte aligned fp32 / 4-byte aligned bf16)
+__device__ __forceinline__ f32x2_t sload2(const void* p, int64_t i, int sb) {
+  if (sb) {
+    const uint32_t v = *(const uint32_t*)((const uint16_t*)p + i);
+    return f32x2_t{bf16lo(v), bf16hi(v)};
+  }
+  return *(const f32x2_t*)((const float*)p + i);
+}
+
 // ---------------------------------------------------------------- wave ops
 
 // Sum over the 64 lanes, result in every lane. Rows of 16 lanes are reduced
@@ -84,11 +118,12 @@ template <> struct Vec<float, 4> {
 // Pack one (row, tile) of 128 pre-activations held as two per lane
 // (columns 2*lane and 2*lane+1 of the tile) into TwELL: the positive
 // entries in ascending column order go to slots 0..C-1 (slots past the
-// count are left as they are) and the uncapped count is returned to every
-// lane. Wave-uniform control flow; one wave per call.
+// count are left as they are; values stored as sstore with sb) and the
+// uncapped count is returned to every lane. Wave-uniform control flow; one
+// wave per call.
 __device__ __forceinline__ int twell_pack_row(float z0, float z1, int lane, int col0, int C,
-                                              float* __restrict__ val, uint16_t* __restrict__ idx,
-                                              int32_t* __restrict__ cnt_out) {
+                                              void* __restrict__ val, uint16_t* __restrict__ idx,
+                                              int32_t* __restrict__ cnt_out, int sb) {
   const bool p0 = z0 > 0.0f;
   const bool p1 = z1 > 0.0f;
   const uint64_t b0 = __ballot(p0);
@@ -97,8 +132,8 @@ __device__ __forceinline__ int twell_pack_row(float z0, float z1, int lane, int 
   const int r0 = __popcll(b0 & below) + __popcll(b1 & below);
   const int r1 = r0 + (p0 ? 1 : 0);
   const int n = __popcll(b0) + __popcll(b1);
-  if (p0 && r0 < C) { val[r0] = z0; idx[r0] = (uint16_t)(col0 + 2 * lane); }
-  if (p1 && r1 < C) { val[r1] = z1; idx[r1] = (uint16_t)(col0 + 2 * lane + 1); }
+  if (p0 && r0 < C) { sstore(val, r0, z0, sb); idx[r0] = (uint16_t)(col0 + 2 * lane); }
+  if (p1 && r1 < C) { sstore(val, r1, z1, sb); idx[r1] = (uint16_t)(col0 + 2 * lane + 1); }
   if (lane == 0) *cnt_out = n;
   return n;
 }
@@ -155,8 +190,9 @@ struct GemmArgs {
   int accumulate;            // kEpiStoreF32 / split-K reduce: out += result
   int act;                   // 1: ReLU on the single-B result; dual B is always ReLU(z)*u
   int lo_off;                // column offset of the lo part (kEpiHiddenSplit)
-  float* out_a;              // kEpiHiddenSplitK: ReLU(z) rows, fp32 [M, ldo_au] (nullable)
-  float* out_u;              // kEpiHiddenSplitK: u rows, fp32 [M, ldo_au] (nullable)
+  void* out_a;               // kEpiHiddenSplitK: ReLU(z) rows, stored values [M, ldo_au]
+  void* out_u;               // kEpiHiddenSplitK: u rows, stored values [M, ldo_au] (nullable)
+  int store_bf16;            // stored activation values are bf16 (TwELL values, out_a/out_u)
   int64_t ldo_au;
   // split-K (kEpiStoreF32 with a device M): the number of splits S is
   // chosen on the device so that tiles * S stays near split_target; when
@@ -165,7 +201,7 @@ struct GemmArgs {
   int split_max;
   float* part;
   // TwELL (kEpiTwell)
-  float* tw_val;
+  void* tw_val;
   uint16_t* tw_idx;
   int32_t* tw_cnt;
   uint32_t* ovf;             // [n_t][ovf_words] overflow bits, bit r of word w = row 32w+r
@@ -218,20 +254,21 @@ hipError_t launch_hidden_combine(Dtype dt, int nb, const GemmArgs& g, hipStream_
 // out_a / out_u when set.
 hipError_t launch_flag_hidden(int nb, const GemmArgs& g, hipStream_t s);
 
-hipError_t launch_pack(const float* z, int64_t T, int F, int C, float* val, uint16_t* idx,
+hipError_t launch_pack(const float* z, int64_t T, int F, int C, int sb, void* val, uint16_t* idx,
                        int32_t* cnt, uint32_t* ovf, int ovf_words, hipStream_t s);
 hipError_t launch_flags(const uint32_t* ovf, int n_t, int ovf_words, int64_t T, uint8_t* row_flag,
                         int32_t* flagged, int32_t* n_flagged, hipStream_t s);
 // TwELL -> ELL rows + dense-backup routing (one wave per token row).
 struct EllArgs {
-  const float* val;       // TwELL [T, n_t, C]
+  const void* val;        // TwELL [T, n_t, C] stored values
   const uint16_t* idx;
   const int32_t* cnt;     // [T, n_t]
   int64_t T;
   int n_t;
   int C;
   int K;                  // ELL capacity
-  float* ell_a;           // [T, K] out
+  void* ell_a;            // [T, K] out, stored values
+  int store_bf16;
   uint16_t* ell_idx;      // [T, K] out
   int32_t* ell_cnt;       // [T] out (0 for backup rows)
   uint8_t* row_flag;      // [T] out, TwELL overflow (nullable)
@@ -263,9 +300,10 @@ __device__ __forceinline__ int device_rows(const int32_t* m_dev, int m_cap) {
   return (m_cap > 0 && m > m_cap) ? m_cap : m;
 }
 
-// rows[m] for m < min(*n, cap): out[m, :] = ReLU(z[rows[m], :]) (fp32, F wide)
-hipError_t launch_gather_relu_rows(const float* z, int F, const int32_t* rows, const int32_t* n,
-                                   int cap, float* out, hipStream_t s);
+// rows[m] for m < min(*n, cap): out[m, :] = ReLU(z[rows[m], :]) (stored
+// values, F wide)
+hipError_t launch_gather_relu_rows(const float* z, int F, int sb, const int32_t* rows, const int32_t* n,
+                                   int cap, void* out, hipStream_t s);
 
 // Sparse up/down over ELL rows, d cut into NS slices (one per XCD group).
 struct SliceArgs {
@@ -273,7 +311,7 @@ struct SliceArgs {
   const void* wu;         // [F, d] (gated)
   const void* wd;         // [F, d]
   const uint16_t* ell_idx;
-  const float* ell_a;
+  const void* ell_a;      // stored values
   const int32_t* ell_cnt;
   const uint8_t* bk;      // rows written by the dense path are skipped
   int64_t T;
@@ -281,7 +319,8 @@ struct SliceArgs {
   int K;                  // ELL row stride
   int Kp;                 // partial-dot row stride (K rounded up to 8)
   float* upart;           // [NS, T, Kp] per-slice partial dot products
-  float* ell_u;           // [T, K] u per slot (nullable)
+  void* ell_u;            // [T, K] u per slot, stored values (nullable)
+  int store_bf16;
   float* y;               // [T, d]
 };
 void slice_shape(Dtype dt, int d, int* ns, int* epl);
@@ -296,8 +335,9 @@ struct BwdArgs {
   const void* dy;         // [T, d]
   const void* wg;         // [F, d]
   const void* wu;         // [F, d] (gated)
-  const float* ell_a;     // [T, K]
-  const float* ell_u;     // [T, K] (gated)
+  const void* ell_a;      // [T, K] stored values
+  const void* ell_u;      // [T, K] (gated)
+  int store_bf16;
   const uint16_t* ell_idx;
   const int32_t* ell_cnt;
   const int32_t* slot;    // [T] backup slot or -1
@@ -323,8 +363,8 @@ struct BwdArgs {
   const int32_t* brow;
   const int32_t* n_backup;
   int cap;                // rows of the backup buffers
-  const float* bk_a;      // [cap, F]
-  const float* bk_u;      // [cap, F]
+  const void* bk_a;       // [cap, F] stored values
+  const void* bk_u;       // [cap, F]
   const float* dH;        // [cap, F]
   void* xb;               // stacked gathered x rows
   void* dyb;              // stacked gathered dy rows

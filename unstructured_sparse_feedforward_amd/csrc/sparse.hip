@@ -98,7 +98,9 @@ __global__ __launch_bounds__(256) void rows_kernel(EllArgs a) {
       }
       const int64_t src = src0 + (int64_t)lo * a.C + (o - ts[lo]);
       a.ell_idx[dst + o] = a.idx[src];
-      a.ell_a[dst + o] = a.val[src];
+      // the stored value as is (fp32 or bf16 bits)
+      if (a.store_bf16) ((uint16_t*)a.ell_a)[dst + o] = ((const uint16_t*)a.val)[src];
+      else ((float*)a.ell_a)[dst + o] = ((const float*)a.val)[src];
     }
   }
 }
@@ -251,7 +253,9 @@ __global__ __launch_bounds__(256) void up_partial_kernel(SliceArgs a) {
 // Between the phases (gated): u_k = sum of the slice partials in slice
 // order and h_k = a_k * u_k, written over slice 0's partial (the lane that
 // reads a slot's partials is the one that writes it); u_k is saved for
-// training. One wave per row.
+// training. With 16-bit storage a_k is the stored value and u_k is rounded
+// as it would be stored, so that h is what the backward recomputes. One
+// wave per row.
 template <int NS>
 __global__ __launch_bounds__(256) void hsum_kernel(SliceArgs a) {
   const int lane = threadIdx.x & 63;
@@ -263,8 +267,9 @@ __global__ __launch_bounds__(256) void hsum_kernel(SliceArgs a) {
 #pragma unroll
     for (int r = 0; r < NS; ++r) u += a.upart[((int64_t)r * a.T + t) * a.Kp + k];
     const int64_t q = t * a.K + k;
-    if (a.ell_u) a.ell_u[q] = u;
-    a.upart[t * a.Kp + k] = a.ell_a[q] * u;
+    u = sround(u, a.store_bf16);
+    if (a.ell_u) sstore(a.ell_u, q, u, a.store_bf16);
+    a.upart[t * a.Kp + k] = sload(a.ell_a, q, a.store_bf16) * u;
   }
 }
 
@@ -325,7 +330,8 @@ __global__ __launch_bounds__(256) void down_kernel(SliceArgs a) {
       if (k0 + lane < nq) {
         const int64_t tq = tw + q;
         v[0] = __int_as_float((int)a.ell_idx[tq * a.K + k0 + lane]);
-        v[1] = GATED ? a.upart[tq * a.Kp + k0 + lane] : a.ell_a[tq * a.K + k0 + lane];
+        v[1] = GATED ? a.upart[tq * a.Kp + k0 + lane]
+                     : sload(a.ell_a, tq * a.K + k0 + lane, a.store_bf16);
       }
       rec[wave][q][lane] = v;
     }
@@ -375,9 +381,10 @@ hipError_t launch_slices(const SliceArgs& a, bool gated, int phase, hipStream_t 
 }
 
 __global__ __launch_bounds__(256) void gather_relu_rows_kernel(const float* __restrict__ z, int F,
+                                                               int sb,
                                                                const int32_t* __restrict__ rows,
                                                                const int32_t* __restrict__ n,
-                                                               int cap, float* __restrict__ out) {
+                                                               int cap, void* __restrict__ out) {
   const int R = device_rows(n, cap);
   const int f4 = F / 4;
   const int64_t total = (int64_t)R * f4;
@@ -388,15 +395,16 @@ __global__ __launch_bounds__(256) void gather_relu_rows_kernel(const float* __re
     f32x4_t v = *(const f32x4_t*)(z + (int64_t)rows[m] * F + c);
 #pragma unroll
     for (int q = 0; q < 4; ++q) v[q] = v[q] > 0.0f ? v[q] : 0.0f;
-    *(f32x4_t*)(out + (int64_t)m * F + c) = v;
+    sstore4(out, (int64_t)m * F + c, v, sb);
   }
 }
 
 }  // namespace
 
-hipError_t launch_gather_relu_rows(const float* z, int F, const int32_t* rows, const int32_t* n,
-                                   int cap, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(gather_relu_rows_kernel, dim3(512), dim3(256), 0, s, z, F, rows, n, cap, out);
+hipError_t launch_gather_relu_rows(const float* z, int F, int sb, const int32_t* rows,
+                                   const int32_t* n, int cap, void* out, hipStream_t s) {
+  hipLaunchKernelGGL(gather_relu_rows_kernel, dim3(512), dim3(256), 0, s, z, F, sb, rows, n, cap,
+                     out);
   return hipGetLastError();
 }
 

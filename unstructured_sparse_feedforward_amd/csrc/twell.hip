@@ -13,7 +13,7 @@ namespace {
 // One wave per (32-row group, tile): reads z, packs 32 rows and writes the
 // group's overflow word.
 __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ z, int64_t T, int F,
-                                                   int C, float* __restrict__ val,
+                                                   int C, int sb, void* __restrict__ val,
                                                    uint16_t* __restrict__ idx,
                                                    int32_t* __restrict__ cnt,
                                                    uint32_t* __restrict__ ovf, int ovf_words) {
@@ -29,8 +29,9 @@ __global__ __launch_bounds__(256) void pack_kernel(const float* __restrict__ z, 
     if (t >= T) break;
     const f32x2_t v = *(const f32x2_t*)(z + t * F + (int64_t)b * kTile + 2 * lane);
     const int64_t slot = t * n_t + b;
-    const int n = twell_pack_row(v[0], v[1], lane, b * kTile, C, val + slot * C, idx + slot * C,
-                                 cnt + slot);
+    const int n = twell_pack_row(v[0], v[1], lane, b * kTile, C,
+                                 (char*)val + slot * C * (sb ? 2 : 4), idx + slot * C,
+                                 cnt + slot, sb);
     bits |= (n > C ? 1u : 0u) << q;
   }
   if (lane == 0) ovf[(int64_t)b * ovf_words + w] = bits;
@@ -97,11 +98,11 @@ __global__ __launch_bounds__(1024) void flags_kernel(const uint32_t* __restrict_
 
 }  // namespace
 
-hipError_t launch_pack(const float* z, int64_t T, int F, int C, float* val, uint16_t* idx,
+hipError_t launch_pack(const float* z, int64_t T, int F, int C, int sb, void* val, uint16_t* idx,
                        int32_t* cnt, uint32_t* ovf, int ovf_words, hipStream_t s) {
   const int64_t items = (int64_t)ovf_words * (F / kTile);
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, z, T, F, C,
-                     val, idx, cnt, ovf, ovf_words);
+                     sb, val, idx, cnt, ovf, ovf_words);
   return hipGetLastError();
 }
 
