@@ -167,15 +167,16 @@ def cpu_record(tokens, ms, sample):
             "sample": f"{sample}; {ms / 1e3:.1f} s; host os.cpu_count()={os.cpu_count()}"}
 
 
-def gather_work(W, cnt, flag, np):
+def gather_work(W, cnt, flag, np, ssz=4):
     """Algorithmic bytes of the sparse up/down projection of one layer:
     per active pair of an unflagged row the weight rows it reads and its
-    (value, index); per unflagged row its x row, y row, tile counts, flag."""
+    (value, index) (ssz: bytes of a stored value); per unflagged row its x
+    row, y row, tile counts, flag."""
     n_flag = int(flag.sum())
     pairs = int(cnt[~flag].sum())
     esz = 2 if W.dtype == "bf16" else 4
     n_t = W.F // W.tile
-    per_pair = (2 if W.gated else 1) * W.d * esz + 6
+    per_pair = (2 if W.gated else 1) * W.d * esz + ssz + 2
     per_tok = W.d * esz + W.d * 4 + 4 * n_t + 1
     return pairs * per_pair + (W.T - n_flag) * per_tok, pairs, n_flag
 
@@ -263,6 +264,8 @@ def main():
     ap.add_argument("--energy", action=argparse.BooleanOptionalAction, default=True,
                     help="run the sparse and dense forwards for ~3 s each while sampling the "
                          "socket power with amd-smi, and report energy per token (default on)")
+    ap.add_argument("--store", default="f32", choices=("f32", "bf16"),
+                    help="dtype of the stored activations (TwELL values, Hybrid a and u)")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="cold-cache steps of each mode (a 2 GiB read before each; 0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -270,6 +273,9 @@ def main():
                          "(float32 negate into a second buffer) three times, so hardware "
                          "counters of the run can be scaled against known bytes")
     args = ap.parse_args()
+    if args.store == "bf16" and args.workload == "small":
+        print("--store bf16 serves bf16 layers; the small workload is fp32", file=sys.stderr)
+        return 2
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this layer is "
               "benchmarked on one MI355X; sharding is a design note, not a run mode.",
@@ -322,7 +328,8 @@ def bench_forward(args, np, torch, SparseFFN, wl):
             cpu_ms += oracle_forward_ms(inp, n_cpu, np)
         ffn = SparseFFN(W.d, W.F, gated=W.gated, twell_cap=W.twell_cap, tile=W.tile,
                         ell_cap=W.ell_cap, dense_rows=W.dense_rows,
-                        dtype=torch.bfloat16 if W.dtype == "bf16" else torch.float32)
+                        dtype=torch.bfloat16 if W.dtype == "bf16" else torch.float32,
+                        store_dtype=_store(args, torch))
         y = torch.empty((W.T, W.d), dtype=torch.float32, device="cuda")
         layers.append(dict(W=W, ffn=ffn, tw=ffn.new_twell(W.T), y=y, yd=torch.empty_like(y),
                            args=[_dev(inp, k, torch, np)
@@ -377,7 +384,8 @@ def bench_forward(args, np, torch, SparseFFN, wl):
     gbytes, pairs, n_flag = 0.0, 0, 0
     for L in layers:
         b, p, nf = gather_work(L["W"], L["tw"]["cnt"].cpu().numpy(),
-                               L["tw"]["row_flag"].cpu().numpy().astype(bool), np)
+                               L["tw"]["row_flag"].cpu().numpy().astype(bool), np,
+                               ssz=2 if args.store == "bf16" else 4)
         gbytes += b
         pairs += p
         n_flag += nf
@@ -441,7 +449,7 @@ def bench_forward(args, np, torch, SparseFFN, wl):
     T = W0.T
     cfg = {"workload": W0.name, "T": T, "d": W0.d, "d_ff": W0.F, "gated": W0.gated,
            "nnz_per_token": W0.nnz, "twell_tile": W0.tile, "twell_cap": W0.twell_cap,
-           "ell_cap": W0.ell_cap, "dense_rows": W0.dense_rows,
+           "ell_cap": W0.ell_cap, "dense_rows": W0.dense_rows, "store_dtype": args.store,
            "outlier_frac": W0.outlier_frac, "seed": args.seed}
     if stack:
         cfg.update(workload=wl.STACK_LAYER.name, layers=len(Ws),
@@ -498,6 +506,10 @@ def bench_forward(args, np, torch, SparseFFN, wl):
             f"{what}: numpy float64 sparse forward (gate GEMM, TwELL pack, per-token "
             f"up/down over active neurons, dense flagged rows)")
     return out
+
+
+def _store(args, torch):
+    return torch.bfloat16 if args.store == "bf16" else torch.float32
 
 
 def T_of(layers):
@@ -630,7 +642,7 @@ def bench_train(args, np, torch, SparseFFN, wl):
     mem0 = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
     ffn = SparseFFN(d, F, gated=True, twell_cap=W.twell_cap, ell_cap=W.ell_cap,
-                    dense_rows=W.dense_rows, dtype=torch.bfloat16)
+                    dense_rows=W.dense_rows, dtype=torch.bfloat16, store_dtype=_store(args, torch))
     hy = ffn.new_hybrid(T)
     y = torch.empty((T, d), dtype=torch.float32, device="cuda")
     f32 = dict(dtype=torch.float32, device="cuda")
@@ -669,14 +681,16 @@ def bench_train(args, np, torch, SparseFFN, wl):
     P = int(cnt.sum())               # ELL slots (active pairs of ELL rows)
     R = int((slot < 0).sum())        # ELL rows
     S = args.steps
-    # algorithmic bytes per step of the gather-bound kernels (bf16 operands):
+    # algorithmic bytes per step of the gather-bound kernels (bf16 operands,
+    # sv bytes per stored activation value):
     # forward up/down: per slot W_u, W_d rows + (a, u, idx) saved; per row x, y
-    fwd = P * (2 * d * 2 + 10) + R * (d * 2 + d * 4)
+    sv = 2 if args.store == "bf16" else 4
+    fwd = P * (2 * d * 2 + 2 * sv + 2) + R * (d * 2 + d * 4)
     # dH = dy . W_d[j] per slot: the W_d row and the index; per row the dy row
     sddmm = P * (d * 2 + 2) + R * d * 2
     # dx: per slot W_g, W_u rows, (idx, a, u, dh partial) in, (dZ, dU) out;
     # per row the dx row
-    bdx = P * (2 * d * 2 + 2 + 12 + 8) + R * d * 4
+    bdx = P * (2 * d * 2 + 2 + 2 * sv + 4 + 8) + R * d * 4
     # dW: per slot the x and dy rows and (dZ, dU, a, u, slot id); per neuron
     # its three dW rows
     bdw = P * (2 * d * 2 + 20) + F * 3 * d * 4
@@ -705,6 +719,7 @@ def bench_train(args, np, torch, SparseFFN, wl):
         "data": "synthetic",
         "config": {"workload": W.name, "T": T, "d": d, "d_ff": F, "gated": True,
                    "nnz_per_token": W.nnz, "twell_cap": W.twell_cap, "ell_cap": W.ell_cap,
+                   "dense_rows": W.dense_rows, "store_dtype": args.store,
                    "outlier_frac": W.outlier_frac, "seed": args.seed},
         "roofline": rs[0],
         "roofline_other": rs[1:],
@@ -730,7 +745,7 @@ def bench_train(args, np, torch, SparseFFN, wl):
         "backup_rows": nb,
         "ell_slots": P,
         "saved_activation_bytes": {
-            "hybrid": int(T * W.ell_cap * 10 + T * 8 + nb * (F * 8 + 4)),
+            "hybrid": int(T * W.ell_cap * (2 * sv + 2) + T * 8 + nb * (F * 2 * sv + 4)),
             "dense_a_u_fp32": int(T * F * 8)},
     }
     if n_cpu > 0:
