@@ -300,6 +300,8 @@ def main():
 
     if args.workload == "train":
         out = bench_train(args, np, torch, SparseFFN, wl)
+    elif args.workload == "stack18":
+        out = bench_stack(args, np, torch, SparseFFN, wl)
     else:
         out = bench_forward(args, np, torch, SparseFFN, wl)
     print(json.dumps(out), flush=True)
@@ -307,17 +309,13 @@ def main():
 
 
 def bench_forward(args, np, torch, SparseFFN, wl):
-    stack = args.workload == "stack18"
-    if stack:
-        Ws = [wl.stack_layer(i) for i in range(len(wl.STACK_RAMP))]
-    else:
-        Ws = [{"gated": wl.GATED_1P5B, "gated15": wl.GATED_1P5B_NNZ15,
-               "small": wl.SMALL_F32, "nongated29": wl.NONGATED[29],
-               "nongated108": wl.NONGATED[108],
-               "nongated911": wl.NONGATED[911]}[args.workload]]
+    Ws = [{"gated": wl.GATED_1P5B, "gated15": wl.GATED_1P5B_NNZ15,
+           "small": wl.SMALL_F32, "nongated29": wl.NONGATED[29],
+           "nongated108": wl.NONGATED[108],
+           "nongated911": wl.NONGATED[911]}[args.workload]]
     W0 = Ws[0]
     if args.cpu_sample < 0:
-        n_cpu = (256 if stack else 2048 if W0.F == 8192 else W0.T)
+        n_cpu = 2048 if W0.F == 8192 else W0.T
     else:
         n_cpu = min(args.cpu_sample, W0.T)
     layers, cpu_ms = [], 0.0
@@ -335,8 +333,6 @@ def bench_forward(args, np, torch, SparseFFN, wl):
                            args=[_dev(inp, k, torch, np)
                                  for k in ("x", "w_gate", "w_up", "w_down")]))
         del inp
-        if stack:
-            print(f"layer {i} on the device", file=sys.stderr, flush=True)
 
     def sparse():
         for L in layers:
@@ -393,11 +389,11 @@ def bench_forward(args, np, torch, SparseFFN, wl):
     # the dense layer: gate, up and down products (non-gated: two)
     dense_flops = sum(2.0 * W.T * W.d * W.F * (3 if W.gated else 2) for W in Ws)
     peak_mm = PEAK_BF16_TFLOPS if W0.dtype == "bf16" else PEAK_F32_TFLOPS
-    traffic = measured_traffic(W0.name) if not stack else {}
+    traffic = measured_traffic(W0.name)
     r_gate = roof("mfma", "gate_gemm_twell", flops * args.steps, prof, ["gate_gemm_twell"],
                   peak_mm, traffic.get("gate_gemm_twell"))
     torch_ffn = None
-    if not stack and W0.dtype == "bf16":
+    if W0.dtype == "bf16":
         # context, not part of the path: the vendor bf16 GEMM (torch linear,
         # hipBLASLt) on the gate's shape, plain output, no epilogue, and
         # torch's own bf16 dense layer (two or three linear calls with the
@@ -451,15 +447,8 @@ def bench_forward(args, np, torch, SparseFFN, wl):
            "nnz_per_token": W0.nnz, "twell_tile": W0.tile, "twell_cap": W0.twell_cap,
            "ell_cap": W0.ell_cap, "dense_rows": W0.dense_rows, "store_dtype": args.store,
            "outlier_frac": W0.outlier_frac, "seed": args.seed}
-    if stack:
-        cfg.update(workload=wl.STACK_LAYER.name, layers=len(Ws),
-                   nnz_per_token=list(wl.STACK_RAMP),
-                   front_positions=W0.front_positions, front_prob=W0.front_prob,
-                   seq_len=W0.seq_len)
     out = {
-        "metric": METRIC if not stack else
-        "input tokens/ms through 18 sparse gated FFN layers (fwd) d=2048 ff=5632; "
-        "% MFMA/HBM roofline",
+        "metric": METRIC,
         "value": T / ms,
         "unit": "input tokens/ms",
         "n_gpus": 1,
@@ -487,9 +476,7 @@ def bench_forward(args, np, torch, SparseFFN, wl):
         "flagged_rows_per_step": n_flag,
         "device_bytes": forward_bytes(layers),
     }
-    if stack:
-        out["dispatch"] = per_layer_dispatch(layers, args.steps, torch)
-    if args.energy and not stack:
+    if args.energy:
         idle = _socket_power_w()
         e_sp = measure_energy(sparse, T, torch)
         e_de = measure_energy(dense, T, torch)
@@ -499,8 +486,7 @@ def bench_forward(args, np, torch, SparseFFN, wl):
             "method": "amd-smi socket power sampled every ~0.1-0.3 s from a host thread "
                       "while the forward runs back to back for ~3 s"}
     if n_cpu > 0:
-        what = (f"first {n_cpu} tokens of each of the {len(Ws)} layers" if stack
-                else f"first {n_cpu} of {T} tokens")
+        what = f"first {n_cpu} of {T} tokens"
         out["cpu_baseline"] = cpu_record(
             n_cpu, cpu_ms,
             f"{what}: numpy float64 sparse forward (gate GEMM, TwELL pack, per-token "
@@ -542,43 +528,127 @@ def forward_bytes(layers):
             "dense_workspace": f.workspace_bytes(W.T, B.SFFN_OP_FORWARD_DENSE)}
 
 
-def per_layer_dispatch(layers, steps, torch):
-    """Per-layer sparse/dense choice for a stack: each layer's sparse and
-    dense forward are timed alone, every layer then runs in its faster mode,
-    and the whole stack is timed again with those choices."""
-    def time_one(fn, reps=10):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
+def bench_stack(args, np, torch, SparseFFN, wl):
+    """The 18-layer stack chained with residual connections and RMS
+    normalisation: every layer sparse, every layer dense, and each layer in
+    the mode the library picks from its own TwELL (sffn_choose_mode); each
+    layer's two modes are also timed alone on its chained input, to check
+    the library's choices."""
+    from unstructured_sparse_feedforward_amd.stack import FFNStack
+    Ws = [wl.stack_layer(i) for i in range(len(wl.STACK_RAMP))]
+    T = Ws[0].T
+    n_cpu = 256 if args.cpu_sample < 0 else min(args.cpu_sample, T)
+    weights, cpu_ms = [], 0.0
+    for i, W in enumerate(Ws):
+        inp = wl.make_inputs(W, seed=args.seed, layer=i)
+        if i == 0:
+            x0, outlier = inp.x, inp.outlier
+        if n_cpu > 0:
+            cpu_ms += oracle_forward_ms(inp, n_cpu, np)
+        weights.append(tuple(_dev(inp, k, torch, np) for k in ("w_gate", "w_up", "w_down")))
+        del inp
+        print(f"layer {i} on the device", file=sys.stderr, flush=True)
+    stack = FFNStack(weights, Ws, T, store_dtype=_store(args, torch))
+    keep = torch.from_numpy((~outlier).astype(np.float32)).to(torch.bfloat16).cuda()
+    h0 = torch.from_numpy(x0).cuda()
+    info = stack.choose_modes(h0, keep)
+    chosen = list(stack.modes)
+    tw_counts = [(t["cnt"].cpu().numpy(), t["row_flag"].cpu().numpy().astype(bool))
+                 for t in stack.tw]
 
-    t_sp, t_de, modes = [], [], []
-    for L in layers:
-        sp = time_one(lambda: L["ffn"].forward(*L["args"], mode="sparse", tw=L["tw"], y=L["y"],
-                                               check=False))
-        de = time_one(lambda: L["ffn"].forward(*L["args"], mode="dense", y=L["yd"], check=False))
-        t_sp.append(sp)
-        t_de.append(de)
-        modes.append("sparse" if sp <= de else "dense")
+    def run():
+        stack.forward(h0, keep)
 
-    def chosen():
-        for L, m in zip(layers, modes):
-            if m == "sparse":
-                L["ffn"].forward(*L["args"], mode="sparse", tw=L["tw"], y=L["y"], check=False)
-            else:
-                L["ffn"].forward(*L["args"], mode="dense", y=L["yd"], check=False)
-
-    ms, _, _ = _timed(chosen, steps, 3, torch)
-    T = layers[0]["W"].T
-    return {"value": T / ms, "ms_per_step": ms, "modes": modes,
-            "layer_ms_sparse": t_sp, "layer_ms_dense": t_de}
+    res = {}
+    for name, modes in (("sparse", ["sparse"] * len(Ws)), ("dense", ["dense"] * len(Ws)),
+                        ("chosen", chosen)):
+        stack.modes = modes
+        steps_ms = []
+        ms, _, _ = _timed(run, args.steps, args.warmup, torch, per_step=steps_ms)
+        res[name] = {"ms_per_step": ms, "value": T / ms, "step_ms": pct(steps_ms)}
+    stack.modes = ["sparse"] * len(Ws)
+    ms_p, _, prof = _timed(run, args.steps, 0, torch, stack.ffns)
+    stack.check()
+    # each layer alone on its chained input, in both modes
+    rec = []
+    stack.forward(h0, keep, record=rec)
+    alone = []
+    for l, (f, w) in enumerate(zip(stack.ffns, stack.weights)):
+        x = rec[l][0]
+        y = torch.empty((T, Ws[l].d), dtype=torch.float32, device="cuda")
+        t_sp = _torch_ms(lambda: f.forward(x, *w, mode="sparse", tw=stack.tw[l], y=y,
+                                           check=False), 10, torch)
+        t_de = _torch_ms(lambda: f.forward(x, *w, mode="dense", y=y, check=False), 10, torch)
+        alone.append((t_sp, t_de))
+    del rec
+    stack.check()
+    gbytes, pairs, n_flag = 0.0, 0, 0
+    for W, (cnt, flag) in zip(Ws, tw_counts):
+        b, p, nf = gather_work(W, cnt, flag, np, ssz=2 if args.store == "bf16" else 4)
+        gbytes += b
+        pairs += p
+        n_flag += nf
+    flops = sum(2.0 * W.T * W.d * W.F for W in Ws)
+    r_gate = roof("mfma", "gate_gemm_twell", flops * args.steps, prof, ["gate_gemm_twell"],
+                  PEAK_BF16_TFLOPS)
+    keys = ["sparse_up", "sparse_hsum", "sparse_down"]
+    r_gath = roof("hbm", " + ".join(keys), gbytes * args.steps, prof, keys, PEAK_HBM_GBS)
+    r_gath["l2_relative"] = {"peak": PEAK_L2_GBS, "unit": "GB/s",
+                             "frac": r_gath["achieved"] / PEAK_L2_GBS}
+    W0 = Ws[0]
+    ms = res["sparse"]["ms_per_step"]
+    layers = [{"layer": l, "target_active": W.nnz, "mean_active": m, "crossover": c,
+               "chosen": mode, "alone_ms_sparse": a[0], "alone_ms_dense": a[1],
+               "faster_alone": "sparse" if a[0] <= a[1] else "dense"}
+              for l, (W, (mode, m, c), a) in enumerate(zip(Ws, info, alone))]
+    out = {
+        "metric": "input tokens/ms through 18 sparse gated FFN layers (fwd) d=2048 ff=5632; "
+                  "% MFMA/HBM roofline",
+        "value": T / ms,
+        "unit": "input tokens/ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": W0.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.STACK_LAYER.name, "T": T, "d": W0.d, "d_ff": W0.F,
+                   "layers": len(Ws), "nnz_per_token": list(wl.STACK_RAMP),
+                   "twell_cap": W0.twell_cap, "ell_cap": W0.ell_cap,
+                   "dense_rows": W0.dense_rows, "store_dtype": args.store,
+                   "outlier_frac": W0.outlier_frac, "front_positions": W0.front_positions,
+                   "front_prob": W0.front_prob, "seq_len": W0.seq_len,
+                   "chaining": "h += FFN(RMSNorm(h)) per layer (column 0: bias input)",
+                   "seed": args.seed},
+        "roofline": r_gate,
+        "roofline_other": r_gath,
+        "step_ms": res["sparse"]["step_ms"],
+        "dense_baseline": dict(res["dense"], speedup_sparse_over_dense=
+                               res["dense"]["ms_per_step"] / ms),
+        "dispatch": dict(res["chosen"], modes=chosen,
+                         speedup_over_dense=res["dense"]["ms_per_step"] /
+                         res["chosen"]["ms_per_step"],
+                         choices_matching_alone_timing=sum(
+                             L["chosen"] == L["faster_alone"] for L in layers),
+                         rule="sffn_choose_mode: dense iff the layer's mean active neurons "
+                              "per token (non-overflowing rows) exceeds the cost-model "
+                              "crossover"),
+        "layers": layers,
+        "kernels_ms_per_step": per_step(prof, args.steps),
+        "ms_per_step_with_kernel_events": ms_p,
+        "flagged_rows_per_step": n_flag,
+        "active_pairs_per_step": pairs,
+    }
+    if n_cpu > 0:
+        out["cpu_baseline"] = cpu_record(
+            n_cpu, cpu_ms,
+            f"first {n_cpu} tokens of each of the {len(Ws)} layers (each on its own seeded "
+            f"input): numpy float64 sparse forward (gate GEMM, TwELL pack, per-token up/down "
+            f"over active neurons, dense flagged rows)")
+    return out
 
 
 def torch_dense_train(a, dy, steps, torch):

@@ -112,6 +112,9 @@ typedef struct sffn_handle sffn_handle;
  *              with the stored values, H = bf16(a) * bf16(u) (the dense
  *              path's rows too), and the backward reads them, so the
  *              roundings pass gradients unchanged.
+ *   dense_above  mean active neurons per token (over the rows that stay
+ *              sparse) above which sffn_choose_mode picks the dense layer;
+ *              0 = the library's cost model of the two paths on MI355X
  *   dense_rows R, the most rows one call computes on the dense path
  *              (rows routed away from the ELL at inference, backup rows in
  *              training); the workspace holds R dense rows. 0 means T
@@ -128,6 +131,7 @@ typedef struct sffn_desc {
   int32_t dtype;
   int32_t dense_rows;
   int32_t store_dtype;
+  float   dense_above;
 } sffn_desc;
 
 /*
@@ -328,6 +332,21 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
                           const void* w_down, const sffn_hybrid* hy, const void* dy, int64_t T,
                           float* dx, float* dw_gate, float* dw_up, float* dw_down, float l1_coeff,
                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Per-layer choice between the sparse and the dense forward, made from
+ * the layer's own TwELL (the pages attribute the speed-up to each layer's
+ * activation sparsity, which differs from layer to layer: listing page,
+ * Figure 6 and Figures 10-11; at 108 active per token the gain is small,
+ * Table 5). Reads the counts and row flags of *tw (T rows, as a sparse
+ * forward of the layer wrote them), synchronises the stream and sets *mode
+ * to SFFN_DENSE when the mean active neurons per token over the rows whose
+ * TwELL did not overflow exceeds the crossover (desc.dense_above, or when
+ * that is 0 the library's cost model of the two paths on MI355X, which
+ * also counts the overflowing rows' dense-path work), else SFFN_SPARSE.
+ * mean_active and crossover (nullable) receive the two numbers. T = 0
+ * gives SFFN_SPARSE. */
+sffn_status sffn_choose_mode(sffn_handle* h, const sffn_twell* tw, int64_t T, int32_t* mode,
+                             float* mean_active, float* crossover, hipStream_t stream);
 
 /* Synchronise the stream and return SFFN_E_CAPACITY when *hy->n_backup
  * exceeds hy->max_backup or desc.dense_rows (when that is set), else

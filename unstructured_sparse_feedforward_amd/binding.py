@@ -37,7 +37,8 @@ EXPORTS = ("sffn_create", "sffn_destroy", "sffn_last_error", "sffn_status_string
            "sffn_workspace_bytes", "sffn_pack_twell", "sffn_gate_preact",
            "sffn_forward", "sffn_check", "sffn_profile_enable", "sffn_profile_read",
            "sffn_kernel_name", "sffn_hybrid_compact", "sffn_forward_train",
-           "sffn_hybrid_check", "sffn_backward", "sffn_forward_noalloc")
+           "sffn_hybrid_check", "sffn_backward", "sffn_forward_noalloc",
+           "sffn_choose_mode")
 SFFN_K_COUNT = 18
 
 
@@ -46,7 +47,7 @@ class SffnDesc(ctypes.Structure):
                 ("gated", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("twell_cap", ctypes.c_int32), ("ell_cap", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("dense_rows", ctypes.c_int32),
-                ("store_dtype", ctypes.c_int32)]
+                ("store_dtype", ctypes.c_int32), ("dense_above", ctypes.c_float)]
 
 
 class SffnTwell(ctypes.Structure):
@@ -96,6 +97,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.sffn_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, vp,
                                          ctypes.POINTER(SffnTwell), i32, vp]
     lib.sffn_forward_noalloc.restype = i32
+    lib.sffn_choose_mode.argtypes = [vp, ctypes.POINTER(SffnTwell), i64, ctypes.POINTER(i32),
+                                     ctypes.POINTER(ctypes.c_float),
+                                     ctypes.POINTER(ctypes.c_float), vp]
+    lib.sffn_choose_mode.restype = i32
     lib.sffn_check.argtypes = [vp, vp]
     lib.sffn_check.restype = i32
     lib.sffn_profile_enable.argtypes = [vp, i32]
@@ -160,13 +165,14 @@ class SparseFFN:
     def __init__(self, d: int, d_ff: int, gated: bool = True, twell_cap: int = 8,
                  tile: int = 128, ell_cap: int = 0, dtype: torch.dtype = torch.bfloat16,
                  dense_rows: int = DEFAULT_DENSE_ROWS,
-                 store_dtype: torch.dtype = torch.float32):
+                 store_dtype: torch.dtype = torch.float32, dense_above: float = 0.0):
         self.lib = load_library()
         self.d, self.d_ff, self.gated = d, d_ff, gated
         self.tile, self.twell_cap, self.ell_cap = tile, twell_cap, ell_cap
         self.dtype = dtype
         # dtype of the stored activations (TwELL values, Hybrid a and u)
         self.store_dtype = store_dtype
+        self.dense_above = dense_above
         self.n_t = d_ff // tile
         self.h = None
         self._ws: Dict[str, torch.Tensor] = {}
@@ -179,7 +185,8 @@ class SparseFFN:
                              self.ell_cap,
                              SFFN_BF16 if self.dtype == torch.bfloat16 else SFFN_F32,
                              dense_rows,
-                             SFFN_BF16 if self.store_dtype == torch.bfloat16 else SFFN_F32)
+                             SFFN_BF16 if self.store_dtype == torch.bfloat16 else SFFN_F32,
+                             self.dense_above)
         h = ctypes.c_void_p()
         st = self.lib.sffn_create(ctypes.byref(self.desc), ctypes.byref(h))
         if st != SFFN_OK:
@@ -303,6 +310,17 @@ class SparseFFN:
                                                   _ptr(w_down), x.shape[0], _ptr(y), s, m,
                                                   _stream()), "sffn_forward_noalloc")
         return y
+
+    def choose_mode(self, tw: Dict[str, torch.Tensor], T: int):
+        """sffn_choose_mode: ("sparse" or "dense", mean active neurons per
+        token, crossover) from the layer's TwELL of T rows."""
+        m = ctypes.c_int32()
+        mean, cross = ctypes.c_float(), ctypes.c_float()
+        s = self._tw_struct(tw)
+        self._check(self.lib.sffn_choose_mode(self.h, ctypes.byref(s), T, ctypes.byref(m),
+                                              ctypes.byref(mean), ctypes.byref(cross),
+                                              _stream()), "sffn_choose_mode")
+        return ("dense" if m.value == SFFN_DENSE else "sparse"), mean.value, cross.value
 
     def check(self):
         """sffn_check: raises SffnError (SFFN_E_CAPACITY when a call since the

@@ -103,6 +103,7 @@ sffn_status validate_desc(const sffn_desc* d) {
       d->dense_rows < 0)
     return SFFN_E_ARG;
   if (d->store_dtype != SFFN_F32 && d->store_dtype != SFFN_BF16) return SFFN_E_ARG;
+  if (!(d->dense_above >= 0.0f)) return SFFN_E_ARG;
   // 16-bit stored activations serve bf16 layers
   if (d->store_dtype == SFFN_BF16 && d->dtype != SFFN_BF16) return SFFN_E_UNSUPPORTED;
   if (d->tile != kTile) return SFFN_E_UNSUPPORTED;
@@ -1167,6 +1168,56 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
   }
   if (e != hipSuccess) return hip_fail(h, e, "backward dW");
 
+  return SFFN_OK;
+}
+
+// Mean active neurons per token (over the rows that stay sparse) above
+// which the dense layer is faster than the sparse one, from a cost model
+// of the two paths on MI355X (per token; d model width, F neurons; f the
+// fraction of rows whose TwELL overflowed):
+//   dense   t_d = (3 gated, 2 non-gated) * 2 d F flop at 1.05 PFLOP/s
+//   sparse  2 d F flop (gate GEMM) at 0.93 PFLOP/s + 2 ns (routing, lists)
+//           + (1 - f) * per active neuron (2 gated, 1 non-gated) * 2 d bytes
+//             of weight rows gathered at 21 TB/s (the L2-served rate)
+//           + f * 2 t_d (overflowing rows on the dense path, whose hidden
+//             rows enter the down GEMM as two bf16 parts)
+// The rates are the ones measured here for the gate GEMM, the dense layer
+// and a gather micro-benchmark at d = 2048; with f = 0 the model puts the
+// crossover at 100 active per token for the gated layer at F = 5632 and at
+// 132 for the non-gated one at F = 8192, where measured sweeps of the two
+// layers cross at about 100 and 134.
+static float model_crossover(const sffn_desc& D, double f) {
+  const double dF = (double)D.d * D.d_ff;
+  const double t_dense = (D.gated ? 3.0 : 2.0) * 2.0 * dF / 1.05e15;
+  const double t_fixed = 2.0 * dF / 0.93e15 + 2e-9 + f * 2.0 * t_dense;
+  const double t_pair = (1.0 - f) * (D.gated ? 2.0 : 1.0) * 2.0 * D.d / 21e12;
+  const double n = t_pair > 0.0 ? (t_dense - t_fixed) / t_pair : 0.0;
+  return (float)(n > 0.0 ? n : 0.0);
+}
+
+sffn_status sffn_choose_mode(sffn_handle* h, const sffn_twell* tw, int64_t T, int32_t* mode,
+                             float* mean_active, float* crossover, hipStream_t stream) {
+  if (!h || !mode) return SFFN_E_ARG;
+  if (T < 0 || T > (int64_t)1 << 30) return fail(h, SFFN_E_ARG, "T out of range");
+  if (T > 0 && !twell_ok(tw))
+    return fail(h, SFFN_E_ARG, "TwELL buffers must be non-null and 16-byte aligned");
+  double mean = 0.0, f = 0.0;
+  if (T > 0) {
+    unsigned long long* sum = (unsigned long long*)(h->dstate + 2);
+    hipError_t e = hipMemsetAsync(sum, 0, 2 * sizeof(*sum), stream);
+    if (e == hipSuccess) e = launch_count_sum(tw->cnt, tw->row_flag, T, h->n_t, sum, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    unsigned long long v[2] = {0, 0};
+    if (e == hipSuccess) e = hipMemcpy(v, sum, sizeof(v), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(h, e, "active count");
+    mean = v[1] > 0 ? (double)v[0] / (double)v[1] : 0.0;
+    f = 1.0 - (double)v[1] / (double)T;
+  }
+  const float cross =
+      h->desc.dense_above > 0.0f ? h->desc.dense_above : model_crossover(h->desc, f);
+  *mode = mean > cross ? SFFN_DENSE : SFFN_SPARSE;
+  if (mean_active) *mean_active = (float)mean;
+  if (crossover) *crossover = cross;
   return SFFN_OK;
 }
 

@@ -256,6 +256,10 @@ hipError_t launch_flag_hidden(int nb, const GemmArgs& g, hipStream_t s);
 
 hipError_t launch_pack(const float* z, int64_t T, int F, int C, int sb, void* val, uint16_t* idx,
                        int32_t* cnt, uint32_t* ovf, int ovf_words, hipStream_t s);
+// over the rows t < T with row_flag[t] == 0: out[0] += the sum of their
+// n_t tile counts, out[1] += their number (the caller zeroes out first)
+hipError_t launch_count_sum(const int32_t* cnt, const uint8_t* row_flag, int64_t T, int n_t,
+                            unsigned long long* out, hipStream_t s);
 hipError_t launch_flags(const uint32_t* ovf, int n_t, int ovf_words, int64_t T, uint8_t* row_flag,
                         int32_t* flagged, int32_t* n_flagged, hipStream_t s);
 // TwELL -> ELL rows + dense-backup routing (one wave per token row).

@@ -106,6 +106,46 @@ hipError_t launch_pack(const float* z, int64_t T, int F, int C, int sb, void* va
   return hipGetLastError();
 }
 
+namespace {
+// Over the rows whose TwELL did not overflow (row_flag 0): the sum of
+// their tile counts into out[0] and their number into out[1] (64-bit).
+// One thread per row, per-block sums, one atomic add per block and value.
+__global__ __launch_bounds__(256) void count_sum_kernel(const int32_t* __restrict__ cnt,
+                                                        const uint8_t* __restrict__ row_flag,
+                                                        int64_t T, int n_t,
+                                                        unsigned long long* __restrict__ out) {
+  __shared__ unsigned long long part[2][4];
+  unsigned long long s = 0, r = 0;
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < T;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    if (row_flag[t]) continue;
+    const int32_t* c = cnt + t * n_t;
+    for (int b = 0; b < n_t; ++b) s += (unsigned long long)(uint32_t)c[b];
+    r += 1;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    s += __shfl_xor(s, o, 64);
+    r += __shfl_xor(r, o, 64);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    part[0][threadIdx.x >> 6] = s;
+    part[1][threadIdx.x >> 6] = r;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) {
+    const int k = threadIdx.x;
+    atomicAdd(out + k, part[k][0] + part[k][1] + part[k][2] + part[k][3]);
+  }
+}
+}  // namespace
+
+hipError_t launch_count_sum(const int32_t* cnt, const uint8_t* row_flag, int64_t T, int n_t,
+                            unsigned long long* out, hipStream_t s) {
+  hipLaunchKernelGGL(count_sum_kernel, dim3(256), dim3(256), 0, s, cnt, row_flag, T, n_t, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_flags(const uint32_t* ovf, int n_t, int ovf_words, int64_t T, uint8_t* row_flag,
                         int32_t* flagged, int32_t* n_flagged, hipStream_t s) {
   hipLaunchKernelGGL(flags_kernel, dim3(1), dim3(1024), 0, s, ovf, n_t, ovf_words, T, row_flag,
