@@ -138,6 +138,36 @@ def backward_bf16_store(x, w_gate, w_up, w_down, dy, l1_coeff=0.0, mask=None):
                 dw_down=(a_s * u_s).T @ dy)
 
 
+def dense_train_bf16(x, w_gate, w_up, w_down, dy, l1_coeff=0.0):
+    """A standard bf16 dense training step of the layer (the comparator of
+    the sparse step): the two GEMMs' outputs are bf16, Z_s = bf16(x W_g)
+    and U_s = bf16(x W_u); H = bf16(ReLU(Z_s) * U_s); y = H W_d. Backward
+    with M = 1[Z_s > 0]: dH = dy W_d^T; the gradients that enter GEMMs are
+    bf16, dZ = bf16(dH * U_s * M + l1 * M) and dU = bf16(dH * ReLU(Z_s));
+    dx = dZ W_g^T + dU W_u^T; dW_g = x^T dZ; dW_u = x^T dU; dW_d = H^T dy.
+    Non-gated: H = ReLU(Z_s), dZ = bf16(dH * M + l1 * M), dW_2 = H^T dy.
+    Returns dict(y, dx, dw_gate, dw_up, dw_down)."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    wg = np.asarray(w_gate, dtype=np.float64)
+    wd = np.asarray(w_down, dtype=np.float64)
+    z_s = round_bf16(x @ wg)
+    m = (z_s > 0).astype(np.float64)
+    a_s = z_s * m
+    dh = dy @ wd.T
+    if w_up is None:
+        h = a_s
+        dz = round_bf16(dh * m + l1_coeff * m)
+        return dict(y=h @ wd, dx=dz @ wg.T, dw_gate=x.T @ dz, dw_up=None, dw_down=h.T @ dy)
+    wu = np.asarray(w_up, dtype=np.float64)
+    u_s = round_bf16(x @ wu)
+    h = round_bf16(a_s * u_s)
+    dz = round_bf16(dh * u_s * m + l1_coeff * m)
+    du = round_bf16(dh * a_s)
+    return dict(y=h @ wd, dx=dz @ wg.T + du @ wu.T, dw_gate=x.T @ dz, dw_up=x.T @ du,
+                dw_down=h.T @ dy)
+
+
 # ---------------------------------------------------------------------------
 # TwELL
 # ---------------------------------------------------------------------------

@@ -295,7 +295,7 @@ def check_bf16_store_vs_autograd(orc):
             twg = torch.tensor(wg, requires_grad=True)
             twd = torch.tensor(wd, requires_grad=True)
             z = tx @ twg
-            assert float(z.abs().max()) > 256
+            assert float(z.detach().abs().max()) > 256
             a = _ste_bf16(torch.relu(z))
             if gated:
                 twu = torch.tensor(wu, requires_grad=True)
@@ -340,6 +340,79 @@ def check_bf16_store_exact_values(orc):
     a, b = orc.backward_bf16_store(x, wg, wu, wd, dy, 0.25), orc.backward(x, wg, wu, wd, dy, 0.25)
     for k in ("dx", "dw_gate", "dw_up", "dw_down"):
         assert np.array_equal(a[k], b[k]), k
+
+
+def check_dense_train_golden(orc):
+    """Hand-worked standard bf16 dense training step."""
+    g = _golden("ffn_dense_train_bf16_1x2x2.json")
+    r = orc.dense_train_bf16(*(np.array(g[k]) for k in ("x", "w_gate", "w_up", "w_down", "dy")))
+    for k in ("y", "dx", "dw_gate", "dw_up", "dw_down"):
+        assert np.array_equal(r[k], np.array(g[k])), k
+
+
+class _RoundBoth(torch.autograd.Function):
+    """bf16 rounding of the value in the forward and of the gradient in the
+    backward (exact for values float32 holds exactly)."""
+
+    @staticmethod
+    def forward(ctx, t):
+        return t.float().to(torch.bfloat16).double()
+
+    @staticmethod
+    def backward(ctx, g):
+        return g.float().to(torch.bfloat16).double()
+
+
+def check_dense_train_vs_autograd(orc):
+    """The step as torch autograd sees it: the GEMM outputs rounded in
+    value and in gradient (so the gradients entering the weight GEMMs are
+    bf16), H rounded in value only, on integer inputs that float32 holds
+    exactly; values pass 256, where bf16 drops bits."""
+    r = _rng(18)
+    for gated in (True, False):
+        for l1 in (0.0, 0.5):
+            x = r.integers(-4, 5, (7, 6)).astype(np.float64)
+            wg = r.integers(-60, 61, (6, 16)).astype(np.float64)
+            wu = r.integers(-60, 61, (6, 16)).astype(np.float64) if gated else None
+            wd = r.integers(-3, 4, (16, 6)).astype(np.float64)
+            dy = r.integers(-9, 10, (7, 6)).astype(np.float64)
+            tx = torch.tensor(x, requires_grad=True)
+            twg = torch.tensor(wg, requires_grad=True)
+            twd = torch.tensor(wd, requires_grad=True)
+            zs = _RoundBoth.apply(tx @ twg)
+            a = torch.relu(zs)
+            if gated:
+                twu = torch.tensor(wu, requires_grad=True)
+                h = _ste_bf16(a * _RoundBoth.apply(tx @ twu))
+            else:
+                h = a
+            y = h @ twd
+            (y * torch.from_numpy(dy)).sum().add(l1 * a.sum()).backward()
+            got = orc.dense_train_bf16(x, wg, wu, wd, dy, l1_coeff=l1)
+            assert float(zs.detach().abs().max()) > 256
+            assert np.array_equal(got["y"], y.detach().numpy())
+            assert np.allclose(got["dx"], tx.grad.numpy(), rtol=1e-12, atol=1e-9)
+            assert np.allclose(got["dw_gate"], twg.grad.numpy(), rtol=1e-12, atol=1e-9)
+            assert np.allclose(got["dw_down"], twd.grad.numpy(), rtol=1e-12, atol=1e-9)
+            if gated:
+                assert np.allclose(got["dw_up"], twu.grad.numpy(), rtol=1e-12, atol=1e-9)
+
+
+def check_dense_train_exact_values(orc):
+    """With every Z, U, H, dZ and dU a bf16 value already, the step is the
+    plain layer and its backward exactly."""
+    r = _rng(19)
+    x = r.integers(-2, 3, (6, 4)).astype(np.float64)
+    wg = r.integers(-2, 3, (4, 9)).astype(np.float64)
+    wu = r.integers(-2, 3, (4, 9)).astype(np.float64)
+    wd = r.integers(-1, 2, (9, 4)).astype(np.float64)
+    dy = r.integers(-1, 2, (6, 4)).astype(np.float64)
+    got = orc.dense_train_bf16(x, wg, wu, wd, dy, 0.5)
+    y, _ = orc.dense_ffn(x, wg, wu, wd)
+    ref = orc.backward(x, wg, wu, wd, dy, 0.5)
+    assert np.array_equal(got["y"], y)
+    for k in ("dx", "dw_gate", "dw_up", "dw_down"):
+        assert np.array_equal(got[k], ref[k]), k
 
 
 # --------------------------------------------------------------- sparse layer

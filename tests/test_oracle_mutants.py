@@ -60,6 +60,13 @@ MUTATIONS = [
     ("bf16 store: backward reads the unrounded U", "u_s = round_bf16(it[\"u\"])", 'u_s = it["u"]'),
     ("bf16 store: backward reads the unrounded A", "a_s = round_bf16(it[\"z\"] * m)", 'a_s = it["z"] * m'),
     ("bf16 store: dW_d from the unrounded H", "dw_down=(a_s * u_s).T @ dy)", 'dw_down=it["h"].T @ dy)'),
+    ("dense train: dZ not rounded", "dz = round_bf16(dh * u_s * m + l1_coeff * m)",
+     "dz = dh * u_s * m + l1_coeff * m"),
+    ("dense train: dU not rounded", "du = round_bf16(dh * a_s)\n    return dict(y=h @ wd",
+     "du = dh * a_s\n    return dict(y=h @ wd"),
+    ("dense train: H not rounded", "h = round_bf16(a_s * u_s)", "h = a_s * u_s"),
+    ("dense train: U not rounded", "u_s = round_bf16(x @ wu)", "u_s = x @ wu"),
+    ("dense train: Z not rounded", "z_s = round_bf16(x @ wg)", "z_s = x @ wg"),
     ("hybrid: bk_u from A", 'out["bk_u"] = np.asarray(u_dense, dtype=np.float64)[brow]',
      'out["bk_u"] = np.asarray(a_dense, dtype=np.float64)[brow]'),
     ("hybrid: bk_u rows of the ELL rows", 'out["bk_u"] = np.asarray(u_dense, dtype=np.float64)[brow]',
