@@ -651,6 +651,42 @@ def bench_stack(args, np, torch, SparseFFN, wl):
     return out
 
 
+def dense_train(ffn, a, dy, grads, args, torch):
+    """The same library's dense bf16 training step of the layer
+    (sffn_forward_train_dense + sffn_backward_dense): time per step, the
+    bytes of its saved activations and the device memory one step adds to
+    the inputs and weights (its own workspace, act, y; the same fp32
+    gradient buffers as the sparse step, counted again)."""
+    T = a[0].shape[0]
+    y = torch.empty((T, ffn.d), dtype=torch.float32, device="cuda")
+    g = tuple(torch.empty_like(t) for t in grads)
+    ws_before = ffn._ws.pop("ws", None)
+    torch.cuda.synchronize()
+    m0 = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    _, act = ffn.forward_train_dense(*a, y=y)
+    ffn.backward_dense(*a, act, dy, out=g)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - m0 + sum(t.numel() * 4 for t in g) + T * ffn.d * 4
+
+    def step():
+        ffn.forward_train_dense(*a, y=y, act=act)
+        ffn.backward_dense(*a, act, dy, out=g)
+
+    steps_ms = []
+    ms, _, _ = _timed(step, args.steps, args.warmup, torch, per_step=steps_ms)
+    _, _, prof = _timed(step, args.steps, 0, torch, [ffn])
+    ffn.check()
+    flops = 2.0 * T * ffn.d * ffn.d_ff * (9 if ffn.gated else 6)
+    if ws_before is not None:
+        ffn._ws["ws"] = ws_before
+    return {"kind": "this library's dense bf16 training step (sffn_forward_train_dense + "
+                    "sffn_backward_dense)", "ms_per_step": ms, "value": T / ms,
+            "step_ms": pct(steps_ms), "frac_of_mfma_peak": flops / (ms * 1e-3) / 1e12 /
+            PEAK_BF16_TFLOPS, "kernels_ms_per_step": per_step(prof, args.steps),
+            "act_bytes": int(act.numel() * 2), "peak_bytes": int(peak)}
+
+
 def torch_dense_train(a, dy, steps, torch):
     """Context, not this library: torch's bf16 dense training step of the
     same layer (autograd through linear, relu, mul, linear; hipBLASLt
@@ -742,6 +778,7 @@ def bench_train(args, np, torch, SparseFFN, wl):
     ms_p, _, prof = _timed(step, args.steps, 0, torch, [ffn])
     torch.cuda.synchronize()
     ffn.check()
+    dense_step = dense_train(ffn, a, dy, grads, args, torch)
     torch_step = torch_dense_train(a, dy, args.steps, torch)
     if ffn.hybrid_check(hy) != 0:
         raise RuntimeError("backup rows exceed the Hybrid's capacity")
@@ -793,7 +830,8 @@ def bench_train(args, np, torch, SparseFFN, wl):
                    "outlier_frac": W.outlier_frac, "seed": args.seed},
         "roofline": rs[0],
         "roofline_other": rs[1:],
-        "dense_baseline": None,
+        "dense_baseline": dict(dense_step, speedup_sparse_over_dense=
+                               dense_step["ms_per_step"] / ms),
         "step_ms": pct(steps_ms),
         "torch_dense_train_step": dict(torch_step, speedup_sparse_over_torch_dense=
                                        torch_step["ms_per_step"] / ms),
@@ -802,6 +840,8 @@ def bench_train(args, np, torch, SparseFFN, wl):
             "sparse_saved_for_backward": int(mem_hybrid),
             "sparse_held_after_forward": int(mem_fwd),
             "sparse_workspace": int(mem_ws), "sparse_fp32_grads": int(mem_grads),
+            "dense_step": dense_step["peak_bytes"],
+            "dense_saved_for_backward": dense_step["act_bytes"],
             "torch_dense_step": torch_step["peak_bytes"],
             "torch_dense_held_after_forward": torch_step["after_forward_bytes"],
             "method": "torch.cuda.max_memory_allocated over one step (and memory_allocated "

@@ -83,6 +83,8 @@ typedef int32_t sffn_status;
 #define SFFN_OP_HYBRID         3
 #define SFFN_OP_FORWARD_TRAIN  4
 #define SFFN_OP_BACKWARD       5
+#define SFFN_OP_TRAIN_DENSE    6   /* sffn_forward_train_dense */
+#define SFFN_OP_BACKWARD_DENSE 7   /* sffn_backward_dense */
 
 typedef struct sffn_handle sffn_handle;
 
@@ -348,6 +350,38 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
 sffn_status sffn_choose_mode(sffn_handle* h, const sffn_twell* tw, int64_t T, int32_t* mode,
                              float* mean_active, float* crossover, hipStream_t stream);
 
+/*
+ * The same library's dense training step of the layer, the comparator of
+ * the sparse step (sffn_forward_train + sffn_backward): a standard bf16
+ * layer that keeps its hidden activations dense (listing page, Table 1:
+ * training step of the dense models; gist.science explainer, "2.
+ * Methodology" B for the layer and its backpropagation). bf16 layers only,
+ * T a multiple of 64 (SFFN_E_UNSUPPORTED otherwise).
+ * Forward: Z_s = bf16(x W_g), U_s = bf16(x W_u) (gated), H =
+ * bf16(ReLU(Z_s) U_s) (non-gated: ReLU(Z_s)), y = H W_d (float32 [T, d]).
+ * act (caller-owned, sffn_train_dense_act_bytes) receives Z_s [T, F], U_s
+ * [T, F] (gated) and H [T, F], all bf16: the saved activations the
+ * backward reads. The workspace is sffn_workspace_bytes(
+ * SFFN_OP_TRAIN_DENSE) (none).
+ */
+sffn_status sffn_train_dense_act_bytes(const sffn_handle* h, int64_t T, size_t* bytes);
+sffn_status sffn_forward_train_dense(sffn_handle* h, const void* x, const void* w_gate,
+                                     const void* w_up, const void* w_down, int64_t T, float* y,
+                                     void* act, void* ws, size_t ws_bytes, hipStream_t stream);
+/* Backward of sffn_forward_train_dense from its act: with M = 1[Z_s > 0],
+ * dH = dy W_d^T; dZ = bf16(dH U_s M + l1_coeff M) (non-gated: dH M +
+ * l1_coeff M); dU = bf16(dH ReLU(Z_s)); dx = dZ W_g^T + dU W_u^T;
+ * dW_g = x^T dZ, dW_u = x^T dU, dW_d = H^T dy. Outputs float32 and
+ * overwritten, dW neuron-major [F, d] as in sffn_backward. The workspace is
+ * sffn_workspace_bytes(SFFN_OP_BACKWARD_DENSE) (dH [T, F] fp32, dZ | dU
+ * [T, 2F] and dZ, dU, H transposed, bf16). T = 0 stores zero weight
+ * gradients. */
+sffn_status sffn_backward_dense(sffn_handle* h, const void* x, const void* w_gate,
+                                const void* w_up, const void* w_down, const void* act,
+                                const void* dy, int64_t T, float* dx, float* dw_gate,
+                                float* dw_up, float* dw_down, float l1_coeff, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
 /* Synchronise the stream and return SFFN_E_CAPACITY when *hy->n_backup
  * exceeds hy->max_backup or desc.dense_rows (when that is set), else
  * SFFN_OK (or SFFN_E_HIP). */
@@ -388,7 +422,12 @@ sffn_status sffn_check(sffn_handle* h, hipStream_t stream);
 #define SFFN_K_BWD_DW       15  /* backward: dW rows from the ELL slots */
 #define SFFN_K_BWD_DENSE    16  /* backward: the backup rows' dense GEMMs */
 #define SFFN_K_SPARSE_HSUM  17  /* sparse up projection: slice partials summed, h = a * u */
-#define SFFN_K_COUNT        18
+#define SFFN_K_TRAIN_DENSE_GATEUP 18  /* dense training step: gate/up GEMM saving Z, U, H^T */
+#define SFFN_K_TRAIN_DENSE_DOWN   19  /* dense training step: down GEMM */
+#define SFFN_K_BWD_DENSE_DH       20  /* dense backward: dH GEMM forming dZ, dU */
+#define SFFN_K_BWD_DENSE_DX       21  /* dense backward: dx GEMMs */
+#define SFFN_K_BWD_DENSE_DW       22  /* dense backward: dW GEMMs */
+#define SFFN_K_COUNT        23
 sffn_status sffn_profile_enable(sffn_handle* h, int32_t enable);
 sffn_status sffn_profile_read(sffn_handle* h, double* total_ms, int32_t* launches, int32_t n);
 /* Static name of a kernel id ("" if out of range). */

@@ -31,6 +31,8 @@ SFFN_OP_FORWARD_DENSE = 2
 SFFN_OP_HYBRID = 3
 SFFN_OP_FORWARD_TRAIN = 4
 SFFN_OP_BACKWARD = 5
+SFFN_OP_TRAIN_DENSE = 6
+SFFN_OP_BACKWARD_DENSE = 7
 
 # every symbol include/sffn.h declares
 EXPORTS = ("sffn_create", "sffn_destroy", "sffn_last_error", "sffn_status_string",
@@ -38,8 +40,9 @@ EXPORTS = ("sffn_create", "sffn_destroy", "sffn_last_error", "sffn_status_string
            "sffn_forward", "sffn_check", "sffn_profile_enable", "sffn_profile_read",
            "sffn_kernel_name", "sffn_hybrid_compact", "sffn_forward_train",
            "sffn_hybrid_check", "sffn_backward", "sffn_forward_noalloc",
-           "sffn_choose_mode")
-SFFN_K_COUNT = 18
+           "sffn_choose_mode", "sffn_train_dense_act_bytes", "sffn_forward_train_dense",
+           "sffn_backward_dense")
+SFFN_K_COUNT = 23
 
 
 class SffnDesc(ctypes.Structure):
@@ -101,6 +104,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                      ctypes.POINTER(ctypes.c_float),
                                      ctypes.POINTER(ctypes.c_float), vp]
     lib.sffn_choose_mode.restype = i32
+    lib.sffn_train_dense_act_bytes.argtypes = [vp, i64, ctypes.POINTER(sz)]
+    lib.sffn_train_dense_act_bytes.restype = i32
+    lib.sffn_forward_train_dense.argtypes = [vp, vp, vp, vp, vp, i64, vp, vp, vp, sz, vp]
+    lib.sffn_forward_train_dense.restype = i32
+    lib.sffn_backward_dense.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp,
+                                        ctypes.c_float, vp, sz, vp]
+    lib.sffn_backward_dense.restype = i32
     lib.sffn_check.argtypes = [vp, vp]
     lib.sffn_check.restype = i32
     lib.sffn_profile_enable.argtypes = [vp, i32]
@@ -416,6 +426,45 @@ class SparseFFN:
                                            _ptr(w_down), ctypes.byref(hs), _ptr(dy), T,
                                            _ptr(dx), _ptr(dwg), _ptr(dwu), _ptr(dwd),
                                            float(l1_coeff), ws, n, _stream()), "sffn_backward")
+        return dx, dwg, dwu, dwd
+
+    # ------------------------------------------------------------ dense training
+
+    def forward_train_dense(self, x, w_gate, w_up, w_down, y=None, act=None):
+        """The same library's dense bf16 training forward; returns (y, act)
+        with act the saved bf16 activations (Z_s, U_s, H^T)."""
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty((T, self.d), dtype=torch.float32, device=x.device)
+        if act is None:
+            n = ctypes.c_size_t()
+            self._check(self.lib.sffn_train_dense_act_bytes(self.h, T, ctypes.byref(n)),
+                        "sffn_train_dense_act_bytes")
+            act = torch.empty(n.value // 2, dtype=torch.bfloat16, device=x.device)
+        ws, nb = self.workspace(T, SFFN_OP_TRAIN_DENSE, x.device)
+        self._check(self.lib.sffn_forward_train_dense(self.h, _ptr(x), _ptr(w_gate), _ptr(w_up),
+                                                      _ptr(w_down), T, _ptr(y), _ptr(act), ws,
+                                                      nb, _stream()), "sffn_forward_train_dense")
+        return y, act
+
+    def backward_dense(self, x, w_gate, w_up, w_down, act, dy, l1_coeff: float = 0.0,
+                       out=None):
+        """Gradients of the dense training step (dx, dw_gate, dw_up, dw_down)."""
+        T = x.shape[0]
+        f32 = dict(dtype=torch.float32, device=x.device)
+        if out is not None:
+            dx, dwg, dwu, dwd = out
+        else:
+            dx = torch.empty((T, self.d), **f32)
+            dwg = torch.empty((self.d_ff, self.d), **f32)
+            dwu = torch.empty((self.d_ff, self.d), **f32) if self.gated else None
+            dwd = torch.empty((self.d_ff, self.d), **f32)
+        ws, nb = self.workspace(T, SFFN_OP_BACKWARD_DENSE, x.device)
+        self._check(self.lib.sffn_backward_dense(self.h, _ptr(x), _ptr(w_gate), _ptr(w_up),
+                                                 _ptr(w_down), _ptr(act), _ptr(dy), T, _ptr(dx),
+                                                 _ptr(dwg), _ptr(dwu), _ptr(dwd),
+                                                 float(l1_coeff), ws, nb, _stream()),
+                    "sffn_backward_dense")
         return dx, dwg, dwu, dwd
 
     def hybrid_check(self, hy) -> int:

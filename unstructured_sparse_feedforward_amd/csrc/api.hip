@@ -145,6 +145,8 @@ struct Layout {
   // backward
   size_t drec = 0, ncnt = 0, noff = 0, thist = 0, toff = 0, meta = 0, dH = 0, gz_rm = 0;
   size_t gz_t = 0, gu_t = 0, gh_t = 0, xb = 0, dyb = 0;
+  // dense training step
+  size_t dh_f = 0, dh_rm = 0, dz_t = 0, du_t = 0, h_t = 0;
   int64_t ldt = 0;
 };
 
@@ -214,6 +216,15 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
   }
   if (op == SFFN_OP_FORWARD_DENSE) {
     L.hid = take((size_t)T * F * esize(h));
+  }
+  if (op == SFFN_OP_BACKWARD_DENSE) {
+    // dH [T, F] fp32; dZ | dU rows [T, 2F], and dZ, dU and H transposed
+    // [F, T], bf16
+    L.dh_f = take((size_t)T * F * 4);
+    L.dh_rm = take((size_t)T * F * 2 * 2);
+    L.dz_t = take((size_t)T * F * 2);
+    L.du_t = take((size_t)T * F * 2);
+    L.h_t = take((size_t)T * F * 2);
   }
   if (op == SFFN_OP_BACKWARD) {
     // sized for up to R backup rows
@@ -345,9 +356,7 @@ const char* sffn_last_error(const sffn_handle* h) { return h ? h->err.c_str() : 
 
 sffn_status sffn_workspace_bytes(const sffn_handle* h, int64_t T, int32_t op, size_t* bytes) {
   if (!h || !bytes || T < 0) return SFFN_E_ARG;
-  if (op != SFFN_OP_PACK && op != SFFN_OP_FORWARD_SPARSE && op != SFFN_OP_FORWARD_DENSE &&
-      op != SFFN_OP_HYBRID && op != SFFN_OP_FORWARD_TRAIN && op != SFFN_OP_BACKWARD)
-    return SFFN_E_ARG;
+  if (op < SFFN_OP_PACK || op > SFFN_OP_BACKWARD_DENSE) return SFFN_E_ARG;
   *bytes = layout(h, T, op).total;
   return SFFN_OK;
 }
@@ -789,6 +798,7 @@ static sffn_status forward_args(sffn_handle* h, const void* x, const void* w_gat
 }
 
 static bool ws_ok(void* ws, size_t ws_bytes, const Layout& L) {
+  if (L.total == 0) return true;
   return ws && ws_bytes >= L.total && ((uintptr_t)ws % kAlign) == 0;
 }
 
@@ -846,6 +856,189 @@ sffn_status sffn_forward_train(sffn_handle* h, const void* x, const void* w_gate
   if (!ws_ok(ws, ws_bytes, L))
     return fail(h, SFFN_E_ARG, "workspace missing, too small or not 256-byte aligned");
   return sparse_forward(h, x, w_gate, w_up, w_down, T, y, tw, hy, ws, L, stream);
+}
+
+// the dense training step's saved activations: Z_s, U_s (gated) and H,
+// [T, F] bf16 each
+static size_t train_dense_act_elems(const sffn_handle* h, int64_t T) {
+  return (size_t)T * h->desc.d_ff * (h->desc.gated ? 3 : 2);
+}
+
+static sffn_status train_dense_args(sffn_handle* h, int64_t T) {
+  if (h->desc.dtype != SFFN_BF16)
+    return fail(h, SFFN_E_UNSUPPORTED, "the dense training step is the bf16 layer's");
+  if (T < 0 || T > (int64_t)1 << 30) return fail(h, SFFN_E_ARG, "T out of range");
+  if (T % 64 != 0)
+    return fail(h, SFFN_E_UNSUPPORTED, "the dense training step needs T % 64 == 0");
+  return SFFN_OK;
+}
+
+sffn_status sffn_train_dense_act_bytes(const sffn_handle* h, int64_t T, size_t* bytes) {
+  if (!h || !bytes || T < 0) return SFFN_E_ARG;
+  *bytes = train_dense_act_elems(h, T) * 2;
+  return SFFN_OK;
+}
+
+sffn_status sffn_forward_train_dense(sffn_handle* h, const void* x, const void* w_gate,
+                                     const void* w_up, const void* w_down, int64_t T, float* y,
+                                     void* act, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!h) return SFFN_E_ARG;
+  sffn_status st = train_dense_args(h, T);
+  if (st != SFFN_OK) return st;
+  st = forward_args(h, x, w_gate, w_up, w_down, T, y, nullptr);
+  if (st != SFFN_OK || T == 0) return st;
+  if (!aligned16(act)) return fail(h, SFFN_E_ARG, "act must be a non-null 16-byte aligned pointer");
+  const Layout L = layout(h, T, SFFN_OP_TRAIN_DENSE);
+  if (!ws_ok(ws, ws_bytes, L))
+    return fail(h, SFFN_E_ARG, "workspace missing, too small or not 256-byte aligned");
+  const sffn_desc& D = h->desc;
+  const int64_t TF = T * (int64_t)D.d_ff;
+  uint16_t* a16 = (uint16_t*)act;
+  uint16_t* hid = a16 + (D.gated ? 2 : 1) * TF;
+  GemmArgs g = {};
+  g.A = x;
+  g.lda = D.d;
+  g.M = (int)T;
+  g.B0 = w_gate;
+  g.B1 = w_up;
+  g.ldb = D.d;
+  g.N = D.d_ff;
+  g.K = D.d;
+  g.out = hid;
+  g.ldo = D.d_ff;
+  g.save_z = a16;
+  g.save_u = D.gated ? a16 + TF : nullptr;
+  g.ld_save = D.d_ff;
+  g.num_cu = h->num_cu;
+  const int nb = D.gated ? 2 : 1;
+  g.grid = gemm_grid(kBF16, nb, h->num_cu);
+  hipError_t e;
+  {
+    ProfScope ps(h, SFFN_K_TRAIN_DENSE_GATEUP, stream);
+    e = launch_gemm(kBF16, nb, false, kEpiTrainFwd, g, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "dense training gate/up GEMM");
+  GemmArgs g2 = {};
+  g2.A = hid;
+  g2.lda = D.d_ff;
+  g2.M = (int)T;
+  g2.B0 = w_down;
+  g2.ldb = D.d;
+  g2.N = D.d;
+  g2.K = D.d_ff;
+  g2.out = y;
+  g2.ldo = D.d;
+  g2.num_cu = h->num_cu;
+  g2.grid = gemm_grid(kBF16, 1, h->num_cu);
+  {
+    ProfScope ps(h, SFFN_K_TRAIN_DENSE_DOWN, stream);
+    e = launch_gemm(kBF16, 1, true, kEpiStoreF32, g2, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "dense training down GEMM");
+  return SFFN_OK;
+}
+
+sffn_status sffn_backward_dense(sffn_handle* h, const void* x, const void* w_gate,
+                                const void* w_up, const void* w_down, const void* act,
+                                const void* dy, int64_t T, float* dx, float* dw_gate,
+                                float* dw_up, float* dw_down, float l1_coeff, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  if (!h) return SFFN_E_ARG;
+  sffn_status st = train_dense_args(h, T);
+  if (st != SFFN_OK) return st;
+  const sffn_desc& D = h->desc;
+  if (!aligned16(dw_gate) || !aligned16(dw_down) || (D.gated ? !aligned16(dw_up) : dw_up != nullptr))
+    return fail(h, SFFN_E_ARG, "dW pointers must be 16-byte aligned (dw_up iff the layer is gated)");
+  if (T == 0) {
+    hipError_t e = hipMemsetAsync(dw_gate, 0, (size_t)D.d_ff * D.d * 4, stream);
+    if (e == hipSuccess && dw_up) e = hipMemsetAsync(dw_up, 0, (size_t)D.d_ff * D.d * 4, stream);
+    if (e == hipSuccess) e = hipMemsetAsync(dw_down, 0, (size_t)D.d_ff * D.d * 4, stream);
+    return e == hipSuccess ? SFFN_OK : hip_fail(h, e, "zero dW");
+  }
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_down) || !aligned16(dy) ||
+      !aligned16(dx) || !aligned16(act))
+    return fail(h, SFFN_E_ARG, "x, weights, act, dy and dx must be non-null 16-byte aligned pointers");
+  if (D.gated ? !aligned16(w_up) : w_up != nullptr)
+    return fail(h, SFFN_E_ARG, "w_up must be a 16-byte aligned pointer iff the layer is gated");
+  const Layout L = layout(h, T, SFFN_OP_BACKWARD_DENSE);
+  if (!ws_ok(ws, ws_bytes, L))
+    return fail(h, SFFN_E_ARG, "workspace missing, too small or not 256-byte aligned");
+  const int64_t TF = T * (int64_t)D.d_ff;
+  const uint16_t* a16 = (const uint16_t*)act;
+  uint16_t* dzu = at<uint16_t>(ws, L.dh_rm);
+  uint16_t* dzt = at<uint16_t>(ws, L.dz_t);
+  uint16_t* dut = at<uint16_t>(ws, L.du_t);
+  uint16_t* ht = at<uint16_t>(ws, L.h_t);
+  hipError_t e;
+  // dH = dy W_d^T (fp32), then dZ, dU from it and the saved Z_s, U_s
+  // (rows and transposed)
+  float* dhf = at<float>(ws, L.dh_f);
+  GemmArgs g = {};
+  g.A = dy;
+  g.lda = D.d;
+  g.M = (int)T;
+  g.B0 = w_down;
+  g.ldb = D.d;
+  g.N = D.d_ff;
+  g.K = D.d;
+  g.out = dhf;
+  g.ldo = D.d_ff;
+  g.num_cu = h->num_cu;
+  g.grid = gemm_grid(kBF16, 1, h->num_cu);
+  {
+    ProfScope ps(h, SFFN_K_BWD_DENSE_DH, stream);
+    e = launch_gemm(kBF16, 1, false, kEpiStoreF32, g, stream);
+    if (e == hipSuccess)
+      e = launch_dense_grad(dhf, a16, D.gated ? a16 + TF : nullptr, l1_coeff, T, D.d_ff, dzu, dzt,
+                            dut, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "dense backward dH, dZ, dU");
+  // dx = dZ W_g^T (+ dU W_u^T)
+  for (int pass = 0; pass < (D.gated ? 2 : 1); ++pass) {
+    GemmArgs f = {};
+    f.A = dzu + (pass ? D.d_ff : 0);
+    f.lda = 2 * (int64_t)D.d_ff;
+    f.M = (int)T;
+    f.B0 = pass ? w_up : w_gate;
+    f.ldb = D.d;
+    f.N = D.d;
+    f.K = D.d_ff;
+    f.out = dx;
+    f.ldo = D.d;
+    f.accumulate = pass;
+    f.num_cu = h->num_cu;
+    f.grid = gemm_grid(kBF16, 1, h->num_cu);
+    ProfScope ps(h, SFFN_K_BWD_DENSE_DX, stream);
+    e = launch_gemm(kBF16, 1, true, kEpiStoreF32, f, stream);
+    if (e != hipSuccess) return hip_fail(h, e, "dense backward dx GEMM");
+  }
+  // H transposed ([F, T]: the k-contiguous operand of the dW_d GEMM)
+  {
+    ProfScope ps(h, SFFN_K_BWD_DENSE_DW, stream);
+    e = launch_transpose_bf16(a16 + (D.gated ? 2 : 1) * TF, D.d_ff, ht, T, T, D.d_ff, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "dense backward transpose");
+  // dW_g = dZ^T x, dW_u = dU^T x, dW_d = H^T dy (the transposed operands
+  // k-contiguous, x and dy n-contiguous)
+  for (int pass = 0; pass < 3; ++pass) {
+    if (pass == 1 && !D.gated) continue;
+    GemmArgs w = {};
+    w.A = pass == 0 ? (const void*)dzt : pass == 1 ? (const void*)dut : (const void*)ht;
+    w.lda = T;
+    w.M = D.d_ff;
+    w.B0 = pass == 2 ? dy : x;
+    w.ldb = D.d;
+    w.N = D.d;
+    w.K = (int)T;
+    w.out = pass == 0 ? dw_gate : pass == 1 ? dw_up : dw_down;
+    w.ldo = D.d;
+    w.num_cu = h->num_cu;
+    w.grid = gemm_grid(kBF16, 1, h->num_cu);
+    ProfScope ps(h, SFFN_K_BWD_DENSE_DW, stream);
+    e = launch_gemm(kBF16, 1, true, kEpiStoreF32, w, stream);
+    if (e != hipSuccess) return hip_fail(h, e, "dense backward dW GEMM");
+  }
+  return SFFN_OK;
 }
 
 sffn_status sffn_hybrid_compact(sffn_handle* h, const sffn_twell* tw, const float* z, int64_t T,
@@ -1286,7 +1479,8 @@ const char* sffn_kernel_name(int32_t k) {
       "gate_gemm_twell", "flags",        "sparse_up",  "flagged_gateup", "flagged_down",
       "splitk_reduce",   "dense_gateup", "dense_down", "pack_twell",     "gate_preact",
       "rows",            "sparse_down",  "bwd_sddmm",  "bwd_dx",         "bwd_transpose",
-      "bwd_dw",          "bwd_dense",    "sparse_hsum"};
+      "bwd_dw",          "bwd_dense",    "sparse_hsum",  "train_dense_gateup", "train_dense_down",
+      "bwd_dense_dh",    "bwd_dense_dx", "bwd_dense_dw"};
   return (k >= 0 && k < SFFN_K_COUNT) ? names[k] : "";
 }
 

@@ -609,6 +609,140 @@ __global__ __launch_bounds__(256) void flag_hidden_kernel(GemmArgs g) {
 
 }  // namespace
 
+namespace {
+// 64 x 64 tiles through LDS: a thread loads 16 bytes (8 columns) of two
+// rows and, after the barrier, stores 16 bytes (8 rows) of two output rows
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ in,
+                                                             int64_t ldi,
+                                                             uint16_t* __restrict__ out,
+                                                             int64_t ldo, int64_t R, int64_t C) {
+  __shared__ uint16_t tile[64][72];
+  const int tid = threadIdx.x;
+  const int64_t tc = C / 64;
+  const int64_t ntiles = (R / 64) * tc;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t r0 = (t / tc) * 64, c0 = (t % tc) * 64;
+    const int cc = (tid & 7) * 8;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int rr = (tid >> 3) + 32 * p;
+      const u32x4_t v = *(const u32x4_t*)(in + (r0 + rr) * ldi + c0 + cc);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        tile[rr][cc + 2 * k] = (uint16_t)(v[k] & 0xFFFFu);
+        tile[rr][cc + 2 * k + 1] = (uint16_t)(v[k] >> 16);
+      }
+    }
+    __syncthreads();
+    const int rr = (tid & 7) * 8;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int c = (tid >> 3) + 32 * p;
+      u32x4_t v;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        v[k] = (uint32_t)tile[rr + 2 * k][c] | ((uint32_t)tile[rr + 2 * k + 1][c] << 16);
+      *(u32x4_t*)(out + (c0 + c) * ldo + r0 + rr) = v;
+    }
+    __syncthreads();
+  }
+}
+}  // namespace
+
+namespace {
+// 64 x 64 tiles: a thread takes 8 neighbouring neurons of two rows (16-byte
+// loads of dH, Z_s, U_s; 16-byte stores of dZ, dU), and after the barrier
+// 8 neighbouring rows of two neurons from LDS for the transposed stores
+__global__ __launch_bounds__(256) void dense_grad_kernel(const float* __restrict__ dh,
+                                                         const uint16_t* __restrict__ zs,
+                                                         const uint16_t* __restrict__ us,
+                                                         float l1, int64_t T, int64_t F,
+                                                         uint16_t* __restrict__ dzu,
+                                                         uint16_t* __restrict__ dzt,
+                                                         uint16_t* __restrict__ dut) {
+  __shared__ uint16_t tz[64][72], tu[64][72];
+  const int tid = threadIdx.x;
+  const int64_t tc = F / 64;
+  const int64_t ntiles = (T / 64) * tc;
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t r0 = (t / tc) * 64, c0 = (t % tc) * 64;
+    const int cc = (tid & 7) * 8;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int rr = (tid >> 3) + 32 * p;
+      const int64_t e = (r0 + rr) * F + c0 + cc;
+      const f32x4_t h0 = *(const f32x4_t*)(dh + e);
+      const f32x4_t h1 = *(const f32x4_t*)(dh + e + 4);
+      const u32x4_t z = *(const u32x4_t*)(zs + e);
+      u32x4_t u = {0u, 0u, 0u, 0u};
+      if (us) u = *(const u32x4_t*)(us + e);
+      uint32_t oz[4], ou[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t bz[2], bu[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int c = 2 * k + q;
+          const float hv = c < 4 ? h0[c] : h1[c - 4];
+          const float zv = q ? bf16hi(z[k]) : bf16lo(z[k]);
+          const bool on = zv > 0.0f;
+          float dz, du = 0.0f;
+          if (us) {
+            const float uv = q ? bf16hi(u[k]) : bf16lo(u[k]);
+            dz = on ? hv * uv + l1 : 0.0f;
+            du = on ? hv * zv : 0.0f;
+          } else {
+            dz = on ? hv + l1 : 0.0f;
+          }
+          bz[q] = f32_to_bf16(dz);
+          bu[q] = f32_to_bf16(du);
+          tz[rr][cc + c] = (uint16_t)bz[q];
+          tu[rr][cc + c] = (uint16_t)bu[q];
+        }
+        oz[k] = bz[0] | (bz[1] << 16);
+        ou[k] = bu[0] | (bu[1] << 16);
+      }
+      uint16_t* d = dzu + (r0 + rr) * 2 * F + c0 + cc;
+      *(u32x4_t*)d = u32x4_t{oz[0], oz[1], oz[2], oz[3]};
+      if (us) *(u32x4_t*)(d + F) = u32x4_t{ou[0], ou[1], ou[2], ou[3]};
+    }
+    __syncthreads();
+    const int rr = (tid & 7) * 8;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int c = (tid >> 3) + 32 * p;
+      u32x4_t vz, vu;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        vz[k] = (uint32_t)tz[rr + 2 * k][c] | ((uint32_t)tz[rr + 2 * k + 1][c] << 16);
+        vu[k] = (uint32_t)tu[rr + 2 * k][c] | ((uint32_t)tu[rr + 2 * k + 1][c] << 16);
+      }
+      *(u32x4_t*)(dzt + (c0 + c) * T + r0 + rr) = vz;
+      if (us) *(u32x4_t*)(dut + (c0 + c) * T + r0 + rr) = vu;
+    }
+    __syncthreads();
+  }
+}
+}  // namespace
+
+hipError_t launch_dense_grad(const float* dh, const uint16_t* zs, const uint16_t* us, float l1,
+                             int64_t T, int64_t F, uint16_t* dzu, uint16_t* dzt, uint16_t* dut,
+                             hipStream_t s) {
+  const int64_t ntiles = (T / 64) * (F / 64);
+  const unsigned grid = (unsigned)(ntiles < 4096 ? ntiles : 4096);
+  hipLaunchKernelGGL(dense_grad_kernel, dim3(grid), dim3(256), 0, s, dh, zs, us, l1, T, F, dzu,
+                     dzt, dut);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const uint16_t* in, int64_t ldi, uint16_t* out, int64_t ldo,
+                                 int64_t R, int64_t C, hipStream_t s) {
+  const int64_t ntiles = (R / 64) * (C / 64);
+  const unsigned grid = (unsigned)(ntiles < 4096 ? ntiles : 4096);
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(grid), dim3(256), 0, s, in, ldi, out, ldo, R, C);
+  return hipGetLastError();
+}
+
 hipError_t launch_flag_hidden(int nb, const GemmArgs& g, hipStream_t s) {
   // several units per CU in flight: each is a short chain of dependent loads
   const dim3 grid((unsigned)(8 * g.num_cu)), block(256);

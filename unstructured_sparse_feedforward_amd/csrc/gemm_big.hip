@@ -259,6 +259,43 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16_t (&acc)[NB][
   const int h = lane >> 5;     // which of the register's two rows
   const int c32 = lane & 31;   // column inside the 32-column block
   static_assert(EPI != kEpiTwell, "the TwELL gate GEMM is gemm_twell2_kernel");
+  if constexpr (EPI == kEpiTrainFwd) {
+    // register q of block (i, j) holds rows 8 (q / 4) + 4 h + q % 4 of the
+    // block's 32, column j * 32 + lane % 32
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < JB; ++j) {
+        const int col = n0 + wc * Cfg<NB>::WN + j * 32 + c32;
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int row0 = m0 + wr * 128 + i * 32 + g4 * 8 + h * 4;
+          if (row0 >= M || col >= g.N) continue;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int q = g4 * 4 + r;
+            const int64_t row = row0 + r;
+            const int64_t e = row * g.ld_save + col;
+            {
+              const uint32_t zs = f32_to_bf16(agpr(acc[0][i][j][q]));
+              const float zf = __uint_as_float(zs << 16);
+              const float a = zf > 0.0f ? zf : 0.0f;
+              uint32_t hb;
+              if constexpr (NB == 2) {
+                const uint32_t us = f32_to_bf16(agpr(acc[1][i][j][q]));
+                ((uint16_t*)g.save_u)[e] = (uint16_t)us;
+                hb = f32_to_bf16(a * __uint_as_float(us << 16));
+              } else {
+                hb = f32_to_bf16(a);
+              }
+              ((uint16_t*)g.save_z)[e] = (uint16_t)zs;
+              ((uint16_t*)g.out)[row * g.ldo + col] = (uint16_t)hb;
+            }
+          }
+        }
+      }
+    return;
+  }
   // the whole block tile inside the output: stores without bounds tests
   const bool full = m0 + BM <= M && n0 + 2 * Cfg<NB>::WN <= g.N;
   if (EPI == kEpiStoreF32 && NB == 1 && g.accumulate) {
@@ -834,6 +871,7 @@ bool gemm_big_supported(Dtype dt, int nb, bool bt, Epi epi, const GemmArgs& g) {
   if (epi == kEpiTwell) return nb == 1 && g.ovf == nullptr;
   if (epi == kEpiStoreF32) return nb == 1;
   if (epi == kEpiHiddenBF16) return true;
+  if (epi == kEpiTrainFwd) return true;
   return false;
 }
 
@@ -857,6 +895,8 @@ hipError_t launch_gemm_big(int nb, bool bt, Epi epi, const GemmArgs& g, hipStrea
   if (epi == kEpiStoreF32) return launch_ring<1, kEpiStoreF32>(g, s);
   if (epi == kEpiHiddenBF16) return nb == 2 ? launch_ring<2, kEpiHiddenBF16>(g, s)
                                             : launch_ring<1, kEpiHiddenBF16>(g, s);
+  if (epi == kEpiTrainFwd) return nb == 2 ? launch_ring<2, kEpiTrainFwd>(g, s)
+                                          : launch_ring<1, kEpiTrainFwd>(g, s);
   return hipErrorInvalidValue;
 }
 

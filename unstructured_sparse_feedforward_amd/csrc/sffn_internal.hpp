@@ -151,6 +151,9 @@ enum Epi {
   kEpiHiddenSplitK,// as kEpiHiddenSplit (fp32 H for fp32 layers), or split-K
                    // partials of every B operand when the device-sized
                    // problem splits K (then a combine kernel finishes it)
+  kEpiTrainFwd,    // dense bf16 training forward (z | u GEMM): Z_s = bf16(z),
+                   // U_s = bf16(u) to save_z / save_u, H = bf16(ReLU(Z_s) U_s)
+                   // to out
 };
 
 struct GemmArgs {
@@ -218,6 +221,10 @@ struct GemmArgs {
   int C;
   int n_t;
   int ovf_words;
+  // dense bf16 training forward (kEpiTrainFwd)
+  void* save_z;              // bf16 [M, ld_save]
+  void* save_u;              // bf16 [M, ld_save] (gated; nullptr otherwise)
+  int64_t ld_save;
   int nsplit;                // > 0: columns [0, nsplit) from B0, the rest from B1
                              // (gemm_small.hip, k-contiguous B)
   int grid;                  // persistent grid size (small-tile kernel)
@@ -256,6 +263,18 @@ hipError_t launch_flag_hidden(int nb, const GemmArgs& g, hipStream_t s);
 
 hipError_t launch_pack(const float* z, int64_t T, int F, int C, int sb, void* val, uint16_t* idx,
                        int32_t* cnt, uint32_t* ovf, int ovf_words, hipStream_t s);
+// The dense bf16 training backward's elementwise step: from dH [T, F]
+// fp32 and the saved Z_s, U_s [T, F] bf16 (U_s nullptr when non-gated),
+// M = 1[Z_s > 0], dZ = bf16(dH U_s M + l1 M) (non-gated dH M + l1 M) and
+// dU = bf16(dH ReLU(Z_s)): rows into dzu [T, 2F] (dZ | dU) and transposed
+// into dzt, dut [F, T]. T and F multiples of 64.
+hipError_t launch_dense_grad(const float* dh, const uint16_t* zs, const uint16_t* us, float l1,
+                             int64_t T, int64_t F, uint16_t* dzu, uint16_t* dzt, uint16_t* dut,
+                             hipStream_t s);
+// bf16 transpose: out[c * ldo + r] = in[r * ldi + c] for r < R, c < C
+// (R, C multiples of 64; ldi, ldo multiples of 8)
+hipError_t launch_transpose_bf16(const uint16_t* in, int64_t ldi, uint16_t* out, int64_t ldo,
+                                 int64_t R, int64_t C, hipStream_t s);
 // over the rows t < T with row_flag[t] == 0: out[0] += the sum of their
 // n_t tile counts, out[1] += their number (the caller zeroes out first)
 hipError_t launch_count_sum(const int32_t* cnt, const uint8_t* row_flag, int64_t T, int n_t,
