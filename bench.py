@@ -266,6 +266,9 @@ def main():
                          "socket power with amd-smi, and report energy per token (default on)")
     ap.add_argument("--store", default="f32", choices=("f32", "bf16"),
                     help="dtype of the stored activations (TwELL values, Hybrid a and u)")
+    ap.add_argument("--updown", default="sliced", choices=("sliced", "fused"),
+                    help="inference up/down: three XCD-sliced launches (default) or the one "
+                         "fused kernel without slices")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="cold-cache steps of each mode (a 2 GiB read before each; 0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -327,7 +330,7 @@ def bench_forward(args, np, torch, SparseFFN, wl):
         ffn = SparseFFN(W.d, W.F, gated=W.gated, twell_cap=W.twell_cap, tile=W.tile,
                         ell_cap=W.ell_cap, dense_rows=W.dense_rows,
                         dtype=torch.bfloat16 if W.dtype == "bf16" else torch.float32,
-                        store_dtype=_store(args, torch))
+                        store_dtype=_store(args, torch), fused_updown=args.updown == "fused")
         y = torch.empty((W.T, W.d), dtype=torch.float32, device="cuda")
         layers.append(dict(W=W, ffn=ffn, tw=ffn.new_twell(W.T), y=y, yd=torch.empty_like(y),
                            args=[_dev(inp, k, torch, np)
@@ -424,6 +427,8 @@ def bench_forward(args, np, torch, SparseFFN, wl):
     # products, their sums h = a * u, the down projection); a launch of it
     # is one of each
     keys = ["sparse_up", "sparse_hsum", "sparse_down"] if W0.gated else ["sparse_down"]
+    if args.updown == "fused":
+        keys = ["fused_updown"]
     tr = sum(traffic[k] for k in keys) if all(k in traffic for k in keys) else None
     r_gath = roof("hbm", " + ".join(keys), gbytes * args.steps, prof, keys, PEAK_HBM_GBS, tr)
     r_gath["active_pairs_per_step"] = pairs
@@ -446,6 +451,7 @@ def bench_forward(args, np, torch, SparseFFN, wl):
     cfg = {"workload": W0.name, "T": T, "d": W0.d, "d_ff": W0.F, "gated": W0.gated,
            "nnz_per_token": W0.nnz, "twell_tile": W0.tile, "twell_cap": W0.twell_cap,
            "ell_cap": W0.ell_cap, "dense_rows": W0.dense_rows, "store_dtype": args.store,
+           "updown": args.updown,
            "outlier_frac": W0.outlier_frac, "seed": args.seed}
     out = {
         "metric": METRIC,

@@ -117,6 +117,14 @@ typedef struct sffn_handle sffn_handle;
  *   dense_above  mean active neurons per token (over the rows that stay
  *              sparse) above which sffn_choose_mode picks the dense layer;
  *              0 = the library's cost model of the two paths on MI355X
+ *   updown     how the inference forward runs the up/down projection of
+ *              the ELL rows: 0 (default) three launches with the model
+ *              width cut into slices that each XCD's L2 holds (per-slice
+ *              partial dot products, their sums h = a * u, the down
+ *              projection); 1 (bf16 layers) one fused kernel without
+ *              slices, u and y kept in registers (the single fused kernel
+ *              of "2. Methodology" B on the gist.science explainer). The
+ *              training forward always runs the sliced form.
  *   dense_rows R, the most rows one call computes on the dense path
  *              (rows routed away from the ELL at inference, backup rows in
  *              training); the workspace holds R dense rows. 0 means T
@@ -134,6 +142,7 @@ typedef struct sffn_desc {
   int32_t dense_rows;
   int32_t store_dtype;
   float   dense_above;
+  int32_t updown;
 } sffn_desc;
 
 /*
@@ -427,7 +436,8 @@ sffn_status sffn_check(sffn_handle* h, hipStream_t stream);
 #define SFFN_K_BWD_DENSE_DH       20  /* dense backward: dH GEMM forming dZ, dU */
 #define SFFN_K_BWD_DENSE_DX       21  /* dense backward: dx GEMMs */
 #define SFFN_K_BWD_DENSE_DW       22  /* dense backward: dW GEMMs */
-#define SFFN_K_COUNT        23
+#define SFFN_K_FUSED_UPDOWN       23  /* inference up/down in one kernel (desc.updown = 1) */
+#define SFFN_K_COUNT        24
 sffn_status sffn_profile_enable(sffn_handle* h, int32_t enable);
 sffn_status sffn_profile_read(sffn_handle* h, double* total_ms, int32_t* launches, int32_t n);
 /* Static name of a kernel id ("" if out of range). */

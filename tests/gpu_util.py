@@ -33,7 +33,8 @@ def layer(inp, **kw):
                      tile=w.tile, ell_cap=kw.get("ell_cap", w.ell_cap),
                      dense_rows=kw.get("dense_rows", w.dense_rows),
                      dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32,
-                     store_dtype=kw.get("store_dtype", torch.float32))
+                     store_dtype=kw.get("store_dtype", torch.float32),
+                     fused_updown=kw.get("fused_updown", False))
 
 
 def rel_fro(got, ref):

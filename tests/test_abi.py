@@ -54,6 +54,9 @@ def _create(**kw):
     (dict(ell_cap=-1), B.SFFN_E_ARG),
     (dict(dense_rows=-1), B.SFFN_E_ARG),
     (dict(store_dtype=5), B.SFFN_E_ARG),
+    (dict(updown=2), B.SFFN_E_ARG),
+    (dict(updown=1, dtype=B.SFFN_F32, d=256), B.SFFN_E_UNSUPPORTED),
+    (dict(dense_above=-1.0), B.SFFN_E_ARG),
     (dict(store_dtype=B.SFFN_BF16, dtype=B.SFFN_F32, d=256), B.SFFN_E_UNSUPPORTED),
     (dict(tile=64), B.SFFN_E_UNSUPPORTED),
     (dict(d_ff=5600), B.SFFN_E_UNSUPPORTED),

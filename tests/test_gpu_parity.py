@@ -322,3 +322,19 @@ def test_full_size_nongated_sampled_rows():
     wg, _, wd = math_weights(inp)
     y_ref, _ = oracle.dense_ffn(inp.x[rows].astype(np.float64), wg, None, wd)
     assert_close_bf16(y[rows], y_ref, "sampled rows")
+
+
+# --------------------------------------------------------------- one-kernel up/down
+
+@pytest.mark.parametrize("w,T", [(wl.GATED_1P5B, 1024), (wl.NONGATED[108], 512),
+                                 (wl.GATED_1P5B.replace(d=512, F=1024, nnz=10, name="g512"), 300)])
+def test_fused_updown_variant(w, T):
+    """desc.updown = 1 (the up/down projection as one kernel without d
+    slices) against the oracle and against the sliced path."""
+    _print(f"fused up/down {w.name} T={T}")
+    inp = wl.make_inputs(w, seed=25, T=T)
+    args = [dev(inp, k) for k in ("x", "w_gate", "w_up", "w_down")]
+    y = layer(inp, fused_updown=True).forward(*args).cpu().numpy()
+    assert_close_bf16(y, _oracle_y(inp), "y")
+    y_sl = layer(inp).forward(*args).cpu().numpy()
+    assert_close_bf16(y, y_sl.astype(np.float64), "y against the sliced path")

@@ -42,7 +42,7 @@ EXPORTS = ("sffn_create", "sffn_destroy", "sffn_last_error", "sffn_status_string
            "sffn_hybrid_check", "sffn_backward", "sffn_forward_noalloc",
            "sffn_choose_mode", "sffn_train_dense_act_bytes", "sffn_forward_train_dense",
            "sffn_backward_dense")
-SFFN_K_COUNT = 23
+SFFN_K_COUNT = 24
 
 
 class SffnDesc(ctypes.Structure):
@@ -50,7 +50,8 @@ class SffnDesc(ctypes.Structure):
                 ("gated", ctypes.c_int32), ("tile", ctypes.c_int32),
                 ("twell_cap", ctypes.c_int32), ("ell_cap", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("dense_rows", ctypes.c_int32),
-                ("store_dtype", ctypes.c_int32), ("dense_above", ctypes.c_float)]
+                ("store_dtype", ctypes.c_int32), ("dense_above", ctypes.c_float),
+                ("updown", ctypes.c_int32)]
 
 
 class SffnTwell(ctypes.Structure):
@@ -175,7 +176,8 @@ class SparseFFN:
     def __init__(self, d: int, d_ff: int, gated: bool = True, twell_cap: int = 8,
                  tile: int = 128, ell_cap: int = 0, dtype: torch.dtype = torch.bfloat16,
                  dense_rows: int = DEFAULT_DENSE_ROWS,
-                 store_dtype: torch.dtype = torch.float32, dense_above: float = 0.0):
+                 store_dtype: torch.dtype = torch.float32, dense_above: float = 0.0,
+                 fused_updown: bool = False):
         self.lib = load_library()
         self.d, self.d_ff, self.gated = d, d_ff, gated
         self.tile, self.twell_cap, self.ell_cap = tile, twell_cap, ell_cap
@@ -183,6 +185,9 @@ class SparseFFN:
         # dtype of the stored activations (TwELL values, Hybrid a and u)
         self.store_dtype = store_dtype
         self.dense_above = dense_above
+        # the inference up/down as one fused kernel instead of the sliced
+        # three launches
+        self.fused_updown = fused_updown
         self.n_t = d_ff // tile
         self.h = None
         self._ws: Dict[str, torch.Tensor] = {}
@@ -196,7 +201,7 @@ class SparseFFN:
                              SFFN_BF16 if self.dtype == torch.bfloat16 else SFFN_F32,
                              dense_rows,
                              SFFN_BF16 if self.store_dtype == torch.bfloat16 else SFFN_F32,
-                             self.dense_above)
+                             self.dense_above, 1 if self.fused_updown else 0)
         h = ctypes.c_void_p()
         st = self.lib.sffn_create(ctypes.byref(self.desc), ctypes.byref(h))
         if st != SFFN_OK:

@@ -104,6 +104,9 @@ sffn_status validate_desc(const sffn_desc* d) {
     return SFFN_E_ARG;
   if (d->store_dtype != SFFN_F32 && d->store_dtype != SFFN_BF16) return SFFN_E_ARG;
   if (!(d->dense_above >= 0.0f)) return SFFN_E_ARG;
+  if (d->updown != 0 && d->updown != 1) return SFFN_E_ARG;
+  // the one-kernel up/down serves bf16 layers
+  if (d->updown == 1 && d->dtype != SFFN_BF16) return SFFN_E_UNSUPPORTED;
   // 16-bit stored activations serve bf16 layers
   if (d->store_dtype == SFFN_BF16 && d->dtype != SFFN_BF16) return SFFN_E_UNSUPPORTED;
   if (d->tile != kTile) return SFFN_E_UNSUPPORTED;
@@ -754,17 +757,22 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   sa.ell_u = (train && D.gated) ? hy->ell_u : nullptr;
   sa.store_bf16 = sb_of(h);
   sa.y = y;
-  if (D.gated) {
-    ProfScope ps(h, SFFN_K_SPARSE_UP, stream);
-    e = launch_updown(dt, true, 0, sa, stream);
-  }
-  if (D.gated && e == hipSuccess) {
-    ProfScope ps(h, SFFN_K_SPARSE_HSUM, stream);
-    e = launch_updown(dt, true, 2, sa, stream);
-  }
-  if (e == hipSuccess) {
-    ProfScope ps(h, SFFN_K_SPARSE_DOWN, stream);
-    e = launch_updown(dt, D.gated != 0, 1, sa, stream);
+  if (!train && D.updown == 1) {
+    ProfScope ps(h, SFFN_K_FUSED_UPDOWN, stream);
+    e = launch_fused_updown(D.gated != 0, sa, stream);
+  } else {
+    if (D.gated) {
+      ProfScope ps(h, SFFN_K_SPARSE_UP, stream);
+      e = launch_updown(dt, true, 0, sa, stream);
+    }
+    if (D.gated && e == hipSuccess) {
+      ProfScope ps(h, SFFN_K_SPARSE_HSUM, stream);
+      e = launch_updown(dt, true, 2, sa, stream);
+    }
+    if (e == hipSuccess) {
+      ProfScope ps(h, SFFN_K_SPARSE_DOWN, stream);
+      e = launch_updown(dt, D.gated != 0, 1, sa, stream);
+    }
   }
   if (e != hipSuccess) return hip_fail(h, e, "sparse up/down");
   if (down_late.out != nullptr) {
@@ -1480,7 +1488,7 @@ const char* sffn_kernel_name(int32_t k) {
       "splitk_reduce",   "dense_gateup", "dense_down", "pack_twell",     "gate_preact",
       "rows",            "sparse_down",  "bwd_sddmm",  "bwd_dx",         "bwd_transpose",
       "bwd_dw",          "bwd_dense",    "sparse_hsum",  "train_dense_gateup", "train_dense_down",
-      "bwd_dense_dh",    "bwd_dense_dx", "bwd_dense_dw"};
+      "bwd_dense_dh",    "bwd_dense_dx", "bwd_dense_dw", "fused_updown"};
   return (k >= 0 && k < SFFN_K_COUNT) ? names[k] : "";
 }
 

@@ -351,6 +351,9 @@ void slice_shape(Dtype dt, int d, int* ns, int* epl);
 // phase 2: their sums u and h = a * u (gated; h over slice 0's partials);
 // phase 1: down projection into y.
 hipError_t launch_updown(Dtype dt, bool gated, int phase, const SliceArgs& a, hipStream_t s);
+// bf16 layers, d in {512, 1024, 2048, 4096}: the up and down projections of
+// the ELL rows in one kernel without d slices (rows with bk set skipped)
+hipError_t launch_fused_updown(bool gated, const SliceArgs& a, hipStream_t s);
 
 // Sparse backward over a Hybrid (backward.hip).
 struct BwdArgs {

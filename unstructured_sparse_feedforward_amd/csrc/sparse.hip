@@ -362,6 +362,109 @@ __global__ __launch_bounds__(256) void down_kernel(SliceArgs a) {
   }
 }
 
+// The up and down projections in one kernel, without the d slices: one
+// wave per row; a lane holds D / 64 contiguous bf16 of x and accumulates
+// the same columns of y in registers. Per active pair (G at a time): the
+// W_u row's full dot product with x (wave sum), h = a * u (u stays in
+// registers; with 16-bit storage it is rounded as it would be stored),
+// then h * W_d row into y. The rows' {neuron, a} records are staged in LDS
+// as in the sliced kernels. No per-slice partials, one launch; the weight
+// rows come from the whole W_u, W_d on every XCD.
+template <int D, bool GATED, int G>
+__global__ __launch_bounds__(256) void fused_updown_kernel(SliceArgs a) {
+  constexpr int EPL = D / 64;     // bf16 per lane
+  constexpr int NL = EPL / 8;     // 16-byte loads per lane and row
+  static_assert(NL >= 1, "d >= 512");
+  __shared__ f32x2_t rec[4][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= a.T || a.bk[t]) return;
+  const int n = a.ell_cnt[t];
+  const uint32_t colb = (uint32_t)lane * EPL * 2;
+  const uint32_t rowb = (uint32_t)D * 2;
+  const char* wu = (const char*)a.wu;
+  const char* wd = (const char*)a.wd;
+  u32x4_t xv[NL];
+  if (GATED) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+      xv[i] = *(const u32x4_t*)((const char*)a.x + (uint64_t)t * rowb + colb + i * 16);
+  }
+  float y[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) y[e] = 0.0f;
+  for (int c0 = 0; c0 < n; c0 += 64) {
+    f32x2_t v = {0.0f, 0.0f};
+    if (c0 + lane < n) {
+      const int64_t q = t * a.K + c0 + lane;
+      v[0] = __int_as_float((int)a.ell_idx[q]);
+      v[1] = sload(a.ell_a, q, a.store_bf16);
+    }
+    rec[wave][lane] = v;
+    // a wave's LDS accesses complete in issue order: no barrier is needed
+    // between its own writes and reads
+    const int m = min(64, n - c0);
+    for (int k0 = 0; k0 < m; k0 += G) {
+      f32x2_t md[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) md[g] = k0 + g < m ? rec[wave][k0 + g] : f32x2_t{0.0f, 0.0f};
+      float h[G];
+      if (GATED) {
+        u32x4_t w[G][NL];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int i = 0; i < NL; ++i)
+            w[g][i] = *(const u32x4_t*)(wu + (uint32_t)__float_as_int(md[g][0]) * rowb + colb +
+                                        i * 16);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int i = 0; i < NL; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              // the dwords as values first: a bit_cast of a vector element
+              // reads the vector's first element
+              const uint32_t xe = xv[i][e], we = w[g][i][e];
+              acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, xe),
+                                                    __builtin_bit_cast(bf16x2_t, we), acc, false);
+            }
+          // octet sums (DPP), then the 8 octets' sums in a fixed order
+          const int oc = __float_as_int(octet_sum(acc));
+          float u = 0.0f;
+#pragma unroll
+          for (int o = 0; o < 8; ++o) u += __int_as_float(__builtin_amdgcn_readlane(oc, 8 * o));
+          h[g] = md[g][1] * sround(u, a.store_bf16);
+        }
+      } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) h[g] = md[g][1];
+      }
+      u32x4_t w2[G][NL];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+          w2[g][i] = *(const u32x4_t*)(wd + (uint32_t)__float_as_int(md[g][0]) * rowb + colb +
+                                       i * 16);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            y[i * 8 + 2 * e] = fmaf(h[g], bf16lo(w2[g][i][e]), y[i * 8 + 2 * e]);
+            y[i * 8 + 2 * e + 1] = fmaf(h[g], bf16hi(w2[g][i][e]), y[i * 8 + 2 * e + 1]);
+          }
+    }
+  }
+  float* yo = a.y + t * D + lane * EPL;
+#pragma unroll
+  for (int e = 0; e < EPL; e += 4) *(f32x4_t*)(yo + e) = f32x4_t{y[e], y[e + 1], y[e + 2], y[e + 3]};
+}
+
 template <typename E, int NS, int SW>
 hipError_t launch_slices(const SliceArgs& a, bool gated, int phase, hipStream_t st) {
   if (phase == 0) {
@@ -426,6 +529,22 @@ hipError_t launch_backup_list(const ListArgs& l0, const ListArgs* l1, int64_t T,
   hipLaunchKernelGGL(backup_list_kernel, dim3(l1 ? 2 : 1), dim3(1024), 0, s, l0, l1 ? *l1 : none,
                      T);
   return hipGetLastError();
+}
+
+hipError_t launch_fused_updown(bool gated, const SliceArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.T + 3) / 4)), block(256);
+#define SFFN_FU(D_)                                                                      \
+  if (a.d == D_) {                                                                       \
+    if (gated) hipLaunchKernelGGL((fused_updown_kernel<D_, true, 4>), grid, block, 0, s, a); \
+    else hipLaunchKernelGGL((fused_updown_kernel<D_, false, 4>), grid, block, 0, s, a);     \
+    return hipGetLastError();                                                            \
+  }
+  SFFN_FU(512)
+  SFFN_FU(1024)
+  SFFN_FU(2048)
+  SFFN_FU(4096)
+#undef SFFN_FU
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_updown(Dtype dt, bool gated, int phase, const SliceArgs& a, hipStream_t s) {
