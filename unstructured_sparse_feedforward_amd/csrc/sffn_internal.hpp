@@ -70,22 +70,6 @@ __device__ __forceinline__ f32x2_t sload2(const void* p, int64_t i, int sb) {
 
 // ---------------------------------------------------------------- wave ops
 
-// Sum over the 64 lanes, result in every lane. Rows of 16 lanes are reduced
-// with DPP (quad swaps, half-row and row mirrors), then the four row sums
-// are read out of lanes 0/16/32/48 and added in a fixed order.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += __builtin_amdgcn_update_dpp(0.0f, v, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
-  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
-  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x141, 0xF, 0xF, true);  // row_half_mirror
-  v += __builtin_amdgcn_update_dpp(0.0f, v, 0x140, 0xF, 0xF, true);  // row_mirror
-  int iv = __float_as_int(v);
-  float s0 = __int_as_float(__builtin_amdgcn_readlane(iv, 0));
-  float s1 = __int_as_float(__builtin_amdgcn_readlane(iv, 16));
-  float s2 = __int_as_float(__builtin_amdgcn_readlane(iv, 32));
-  float s3 = __int_as_float(__builtin_amdgcn_readlane(iv, 48));
-  return (s0 + s1) + (s2 + s3);
-}
-
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
 
 // ---------------------------------------------------------------- gathers
