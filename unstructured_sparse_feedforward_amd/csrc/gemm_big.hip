@@ -145,11 +145,12 @@ __device__ __forceinline__ void mfma_substep(f32x16_t (&acc)[NB][4][Cfg<NB>::JB]
 
 // ---------------------------------------------------------------- epilogues
 
-// ReLU + TwELL of a wave's NI x 32 rows of one 128-column TwELL tile tb
-// (the wave's accumulator blocks acc[i][j], rows rbase0 + 32 i).
-template <int NI>
-__device__ __forceinline__ void twell_epilogue(const GemmArgs& g, f32x16_t (&acc)[NI][4],
-                                               int rbase0, int tb, int lane) {
+// ReLU + TwELL of 32 rows (rbase ..) of one 128-column TwELL tile tb, held
+// in a wave's accumulator blocks blk[j] (columns 32 j ..); SB: the values
+// are stored as bf16.
+template <bool SB>
+__device__ __forceinline__ void twell_block(const GemmArgs& g, f32x16_t (&blk)[4], int rbase,
+                                            int tb, int lane) {
   const int M = g.M;
   const int h = lane >> 5;     // which of the register's two rows
   const int c32 = lane & 31;   // column inside the 32-column block
@@ -159,48 +160,40 @@ __device__ __forceinline__ void twell_epilogue(const GemmArgs& g, f32x16_t (&acc
   // ballots and one scalar test. Callers derive rbase0 and tb from a
   // uniform (readfirstlane) wave index, so that the ballots, counts and
   // tests stay in scalar registers.
-  if (tb * kTile >= g.N) return;
   const int C = g.C;
   const uint32_t row_entries = (uint32_t)g.n_t * (uint32_t)C;
   const uint32_t half_off = (uint32_t)h * 4u * row_entries;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int rbase = rbase0 + i * 32;
-    if (rbase >= M) break;
+  const uint32_t col0 = (uint32_t)(tb * kTile + c32);
+  {
+    if (rbase >= M) return;
     const bool full = rbase + 32 <= M;
     // this block's first entry of tile tb; the block spans 32 rows, so
     // every entry offset from it fits 32 bits
     const int64_t e0 = ((int64_t)rbase * g.n_t + tb) * C;
-    const int sb = g.store_bf16;
-    char* vbase = (char*)g.tw_val + e0 * (sb ? 2 : 4);
+    char* vbase = (char*)g.tw_val + e0 * (SB ? 2 : 4);
     char* ibase = (char*)(g.tw_idx + e0);
     int cnt_lane = 0;  // lane r < 32 collects the count of row rbase + r
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int r0 = (q >> 2) * 8 + (q & 3);
-      // lanes whose row exists (all of them but in the last row block)
-      const uint64_t okm = full ? ~0ull : __ballot(rbase + r0 + h * 4 < M);
+      // the lane's row exists (all of them but in the last row block)
+      const bool row_ok = full || rbase + r0 + h * 4 < M;
       float av[4];
       uint64_t bal[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        av[j] = agpr(acc[i][j][q]);
-        bal[j] = __ballot(av[j] > 0.0f) & okm;
+        av[j] = agpr(blk[j][q]);
+        bal[j] = __ballot(row_ok && av[j] > 0.0f);
       }
       if ((bal[0] | bal[1] | bal[2] | bal[3]) != 0) {
-        // per block j: positives of the two rows before it, less (for
-        // the second row) the first row's positives in block j, which the
-        // lane's 64-bit prefix count includes
-        int base0[4], base1[4];
-        int n0c = 0, n1c = 0;
+        int c0[4], c1[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int c0 = __popc((uint32_t)bal[j]);
-          base0[j] = n0c;
-          base1[j] = n1c - c0;
-          n0c += c0;
-          n1c += __popc((uint32_t)(bal[j] >> 32));
+          c0[j] = __popc((uint32_t)bal[j]);
+          c1[j] = __popc((uint32_t)(bal[j] >> 32));
         }
+        const int n0c = c0[0] + c0[1] + c0[2] + c0[3];
+        const int n1c = c1[0] + c1[1] + c1[2] + c1[3];
         cnt_lane = lane == r0 ? n0c : (lane == r0 + 4 ? n1c : cnt_lane);
         // a tile row that overflows C keeps all its pre-activations in a
         // record of its own, so that the dense path of its row needs no
@@ -227,20 +220,28 @@ __device__ __forceinline__ void twell_epilogue(const GemmArgs& g, f32x16_t (&acc
           }
         }
         const uint32_t ro = (uint32_t)r0 * row_entries + half_off;
+        int b0 = 0, b1 = 0;  // positives of the two rows in the blocks before j
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          if (bal[j] == 0) continue;
-          if ((bal[j] >> lane) & 1) {
-            const int rank = (h ? base1[j] : base0[j]) +
-                             (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[j] >> 32),
-                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
-            if (rank < C) {
-              const uint32_t e = ro + (uint32_t)rank;
-              if (sb) *(uint16_t*)(vbase + e * 2u) = (uint16_t)f32_to_bf16(av[j]);
-              else *(float*)(vbase + e * 4u) = av[j];
-              *(uint16_t*)(ibase + e * 2u) = (uint16_t)(tb * kTile + j * 32 + c32);
+          if (bal[j] != 0) {
+            // the lane's rank among its row's positives: those of the
+            // earlier blocks, then the ballot bits below it (mbcnt also
+            // counts the first row's bits for the second row, hence - c0)
+            const int base = h ? b1 - c0[j] : b0;
+            if (row_ok && av[j] > 0.0f) {
+              const int rank = base + (int)__builtin_amdgcn_mbcnt_hi(
+                                          (uint32_t)(bal[j] >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
+              if (rank < C) {
+                const uint32_t e = ro + (uint32_t)rank;
+                if constexpr (SB) *(uint16_t*)(vbase + e * 2u) = (uint16_t)f32_to_bf16(av[j]);
+                else *(float*)(vbase + e * 4u) = av[j];
+                *(uint16_t*)(ibase + e * 2u) = (uint16_t)(col0 + (uint32_t)j * 32u);
+              }
             }
           }
+          b0 += c0[j];
+          b1 += c1[j];
         }
       }
       // one register index at a time: keeps the accumulator reads of
@@ -251,6 +252,30 @@ __device__ __forceinline__ void twell_epilogue(const GemmArgs& g, f32x16_t (&acc
   }
 }
 
+// Blocks I.. of a wave's NI: unrolled by recursion, so that every
+// accumulator index is a constant (an accumulator array indexed at run time
+// would live in scratch memory).
+template <int I, int NI, bool SB>
+struct TwellBlocks {
+  static __device__ __forceinline__ void run(const GemmArgs& g, f32x16_t (&acc)[NI][4],
+                                             int rbase0, int tb, int lane) {
+    twell_block<SB>(g, acc[I], rbase0 + I * 32, tb, lane);
+    TwellBlocks<I + 1, NI, SB>::run(g, acc, rbase0, tb, lane);
+  }
+};
+template <int NI, bool SB>
+struct TwellBlocks<NI, NI, SB> {
+  static __device__ __forceinline__ void run(const GemmArgs&, f32x16_t (&)[NI][4], int, int, int) {}
+};
+
+template <int NI>
+__device__ __forceinline__ void twell_epilogue(const GemmArgs& g, f32x16_t (&acc)[NI][4],
+                                               int rbase0, int tb, int lane) {
+  if (tb * kTile >= g.N) return;
+  if (g.store_bf16) TwellBlocks<0, NI, true>::run(g, acc, rbase0, tb, lane);
+  else TwellBlocks<0, NI, false>::run(g, acc, rbase0, tb, lane);
+}
+
 template <int NB, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16_t (&acc)[NB][4][Cfg<NB>::JB],
                                          int m0, int n0, int wr, int wc, int lane) {
@@ -258,7 +283,12 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16_t (&acc)[NB][
   const int M = g.M;
   const int h = lane >> 5;     // which of the register's two rows
   const int c32 = lane & 31;   // column inside the 32-column block
-  static_assert(EPI != kEpiTwell, "the TwELL gate GEMM is gemm_twell2_kernel");
+  if constexpr (EPI == kEpiTwell) {
+    // a wave's 128 columns are one TwELL tile
+    static_assert(NB == 1, "TwELL epilogue: one B operand");
+    twell_epilogue<4>(g, acc[0], m0 + wr * 128, (n0 >> 7) + wc, lane);
+    return;
+  }
   if constexpr (EPI == kEpiTrainFwd) {
     // register q of block (i, j) holds rows 8 (q / 4) + 4 h + q % 4 of the
     // block's 32, column j * 32 + lane % 32
@@ -428,42 +458,46 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
   const int lr = lane >> 2;
   const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
 
-  for (int L = ts.t_begin + ts.local; L < ts.t_end; L += ts.G8) {
+  // Per-lane copy sources of tile L: A rows m0 + 64 wave + 16 i + lane/4,
+  // B rows (columns of C) n0 + BN/4 wave + 16 i + lane/4.
+  struct Src {
+    const char* a[4];
+    const char* b[NB][BPW];
+  };
+  auto tile_src = [&](int L, Src& t) {
     int m0, n0;
     ts.coords(L, BN, m0, n0);
-
-    const char* a_src[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = min(m0 + wave * 64 + i * 16 + lr, M - 1);
-      a_src[i] = Ab + (int64_t)m * lda_b + lchunk * 16;
+      t.a[i] = Ab + (int64_t)m * lda_b + lchunk * 16;
     }
-    const char* b_src[NB][BPW];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int i = 0; i < BPW; ++i) {
         const int n = min(n0 + wave * (BN / 4) + i * 16 + lr, g.N - 1);
-        b_src[nb][i] = Bb[nb] + (int64_t)n * ldb_b + lchunk * 16;
+        t.b[nb][i] = Bb[nb] + (int64_t)n * ldb_b + lchunk * 16;
       }
+  };
+  auto issue_stage = [&](const Src& t, int kt, int slot) {
+    char* base = smem + slot * SLOT;
+    const int64_t kb = (int64_t)kt * RBK * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(t.a[i] + kb),
+                                       (void*)(base + (wave * 64 + i * 16) * RROWB), 16, 0, 0);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < BPW; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (const void*)(t.b[nb][i] + kb),
+            (void*)(base + (BM + nb * BN + wave * (BN / 4) + i * 16) * RROWB), 16, 0, 0);
+  };
 
-    auto issue_stage = [&](int kt, int slot) {
-      char* base = smem + slot * SLOT;
-      const int64_t kb = (int64_t)kt * RBK * 2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + kb),
-                                         (void*)(base + (wave * 64 + i * 16) * RROWB), 16, 0, 0);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < BPW; ++i)
-          __builtin_amdgcn_global_load_lds(
-              (const void*)(b_src[nb][i] + kb),
-              (void*)(base + (BM + nb * BN + wave * (BN / 4) + i * 16) * RROWB), 16, 0, 0);
-    };
-
-    f32x16_t acc[NB][4][JB];
+  f32x16_t acc[NB][4][JB];
+  auto zero_acc = [&]() {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -472,73 +506,135 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
         for (int j = 0; j < JB; ++j)
 #pragma unroll
           for (int q = 0; q < 16; ++q) acc[nb][i][j][q] = 0.0f;
+  };
 
-    u32x4_t af[2][4];
-    u32x4_t bfr[2][NB][JB];
-    auto read_frags = [&](int slot, int s, int buf) {
-      const char* sa = smem + slot * SLOT;
-      const int ch = 2 * s + (lane >> 5);
+  u32x4_t af[2][4];
+  u32x4_t bfr[2][NB][JB];
+  auto read_frags = [&](int slot, int s, int buf) {
+    const char* sa = smem + slot * SLOT;
+    const int ch = 2 * s + (lane >> 5);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[buf][i] = *(const u32x4_t*)(sa + rlds_off(wr * 128 + i * 32 + (lane & 31), ch));
+    for (int i = 0; i < 4; ++i)
+      af[buf][i] = *(const u32x4_t*)(sa + rlds_off(wr * 128 + i * 32 + (lane & 31), ch));
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int j = 0; j < JB; ++j)
-          bfr[buf][nb][j] = *(const u32x4_t*)(sa + (BM + nb * BN) * RROWB +
-                                              rlds_off(wc * C_::WN + j * 32 + (lane & 31), ch));
-    };
+      for (int j = 0; j < JB; ++j)
+        bfr[buf][nb][j] = *(const u32x4_t*)(sa + (BM + nb * BN) * RROWB +
+                                            rlds_off(wc * C_::WN + j * 32 + (lane & 31), ch));
+  };
 
-    // Pipeline. Stage kt lives in slot kt % NSLOT; all NSLOT slots are
-    // filled up front, and after the barrier of iteration kt (which every
-    // wave reaches only once done reading stage kt) stage kt + NSLOT is
-    // copied into the slot stage kt leaves, the copies spread over the
-    // MFMAs. Past the last stage the copies repeat the last stage into
-    // slots that are never read again, so every iteration issues the same
-    // number of copies and "stage kt+1 has landed" is always "at most
-    // NSLOT - 2 stages in flight". A substep first waits for its own
-    // fragments (read one substep earlier, at most 8 reads in flight,
-    // which lgkmcnt can count), then reads the next ones while it
-    // multiplies; the second substep of a stage runs after the barrier and
-    // reads the first fragments of the next stage.
-    if (nkt > 0) {
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
-    wg_barrier();   // the previous tile's readers are done with LDS
+  // One ring stage: substep 0 of stage kt (fragments already in registers),
+  // then, after the barrier, substep 1 while the fragments of the stage in
+  // slot `next` are read and stage `issue` of tile t is copied into the slot
+  // stage kt leaves.
+  //
+  // Pipeline. Stage kt lives in slot (slot0 + kt) % NSLOT; NSLOT stages are
+  // in flight ahead of the one multiplied. After the barrier of iteration kt
+  // (which every wave reaches only once done reading stage kt) the stage
+  // NSLOT further on is copied into the slot stage kt leaves, the copies
+  // spread over the MFMAs. Every iteration issues the same number of
+  // copies, so "stage kt+1 has landed" is always "at most NSLOT - 2 stages
+  // in flight". A substep first waits for its own fragments (read one
+  // substep earlier, at most 8 reads in flight, which lgkmcnt can count),
+  // then reads the next ones while it multiplies; the second substep of a
+  // stage runs after the barrier and reads the first fragments of the
+  // next stage.
+  auto ring_step = [&](int slot, int next, const Src& t, int issue) {
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // fragments of substep 0
     __builtin_amdgcn_sched_barrier(0);
+    read_frags(slot, 1, 1);
+    mfma_substep<NB>(acc, af[0], bfr[0]);
+    interleave_reads();
+    __builtin_amdgcn_sched_barrier(0);
+    // stage kt+1 has landed in this wave's copies, and the fragments of
+    // substep 1 are in registers; the barrier makes every wave's copies
+    // visible and frees stage kt's slot
+    __builtin_amdgcn_s_waitcnt(wait_imm((NSLOT - 2) * LPS, 0));
+    wg_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(next, 0, 0);
+    issue_stage(t, issue, slot);
+    mfma_substep<NB>(acc, af[1], bfr[1]);
+    interleave_reads_copies();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  int L = ts.t_begin + ts.local;
+  if (L >= ts.t_end) return;
+
+  if (nkt >= NSLOT) {
+    // The ring runs on across this workgroup's tiles: the last NSLOT
+    // iterations of a tile copy the first stages of the next one, so the
+    // next tile's first fragments are in registers before the epilogue
+    // and its copies land while the epilogue runs. After the last tile the
+    // copies repeat its last stage into slots never read again.
+    Src cur;
+    tile_src(L, cur);
+    bool has_next = L + ts.G8 < ts.t_end;
 #pragma unroll
-    for (int p = 0; p < NSLOT; ++p) issue_stage(min(p, nkt - 1), p);
+    for (int p = 0; p < NSLOT; ++p) issue_stage(cur, p, p);
     __builtin_amdgcn_s_waitcnt(wait_imm((NSLOT - 1) * LPS, 15));  // stage 0 landed
     wg_barrier();
     __builtin_amdgcn_sched_barrier(0);
     read_frags(0, 0, 0);
-
     int slot = 0;
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int next = slot + 1 == NSLOT ? 0 : slot + 1;
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // fragments of substep 0
+    for (;;) {
+      zero_acc();
+      const int tail = nkt - NSLOT;
+      for (int kt = 0; kt < tail; ++kt) {
+        const int next = slot + 1 == NSLOT ? 0 : slot + 1;
+        ring_step(slot, next, cur, kt + NSLOT);
+        slot = next;
+      }
+      // the tail copies the next tile's first stages (from here on `cur`
+      // describes the next tile)
+      if (has_next) tile_src(L + ts.G8, cur);
+      for (int kt = tail; kt < nkt; ++kt) {
+        const int next = slot + 1 == NSLOT ? 0 : slot + 1;
+        ring_step(slot, next, cur, has_next ? kt - tail : nkt - 1);
+        slot = next;
+      }
+      int m0, n0;
+      ts.coords(L, BN, m0, n0);
+      epilogue<NB, EPI>(g, acc, m0, n0, wr, wc, lane);
+      if (!has_next) break;
+      L += ts.G8;
+      has_next = L + ts.G8 < ts.t_end;
+    }
+    // no direct-to-LDS copy may still be in flight when the wave ends
+    __builtin_amdgcn_s_waitcnt(kWaitAll);
+    return;
+  }
+
+  // K shorter than the ring: each tile fills and drains the ring itself.
+  for (; L < ts.t_end; L += ts.G8) {
+    int m0, n0;
+    ts.coords(L, BN, m0, n0);
+    Src cur;
+    tile_src(L, cur);
+    zero_acc();
+    if (nkt > 0) {
+      __builtin_amdgcn_s_waitcnt(kWaitAll);
+      wg_barrier();   // the previous tile's readers are done with LDS
       __builtin_amdgcn_sched_barrier(0);
-      read_frags(slot, 1, 1);
-      mfma_substep<NB>(acc, af[0], bfr[0]);
-      interleave_reads();
-      __builtin_amdgcn_sched_barrier(0);
-      // stage kt+1 has landed in this wave's copies, and the fragments of
-      // substep 1 are in registers; the barrier makes every wave's copies
-      // visible and frees stage kt's slot
-      __builtin_amdgcn_s_waitcnt(wait_imm((NSLOT - 2) * LPS, 0));
+#pragma unroll
+      for (int p = 0; p < NSLOT; ++p) issue_stage(cur, min(p, nkt - 1), p);
+      __builtin_amdgcn_s_waitcnt(wait_imm((NSLOT - 1) * LPS, 15));  // stage 0 landed
       wg_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      // substep 1 of stage kt; the reads fetch substep 0 of stage kt+1
-      // (stale data after the last stage, never used)
-      read_frags(next, 0, 0);
-      issue_stage(min(kt + NSLOT, nkt - 1), slot);
-      mfma_substep<NB>(acc, af[1], bfr[1]);
-      interleave_reads_copies();
-      __builtin_amdgcn_sched_barrier(0);
-      slot = next;
-    }
+      read_frags(0, 0, 0);
+      int slot = 0;
+      for (int kt = 0; kt < nkt; ++kt) {
+        const int next = slot + 1 == NSLOT ? 0 : slot + 1;
+        // past the last stage the copies repeat it (stale reads, never used)
+        ring_step(slot, next, cur, min(kt + NSLOT, nkt - 1));
+        slot = next;
+      }
     }
     epilogue<NB, EPI>(g, acc, m0, n0, wr, wc, lane);
   }
+  __builtin_amdgcn_s_waitcnt(kWaitAll);
 }
 
 // ---------------------------------------------------------------- two per CU
