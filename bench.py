@@ -247,6 +247,44 @@ def measure_energy(fn, tokens, torch, seconds=3.0):
             "uJ_per_token": p * elapsed / (steps * tokens) * 1e6}
 
 
+def probe_rates(torch):
+    """Device rates from libsffn_probe.so (sffn_probe_rates), in GB/s per CU,
+    or None when the probe library is not built."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                        "unstructured_sparse_feedforward_amd", "libsffn_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.sffn_probe_rates.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+    lib.sffn_probe_rates.restype = ctypes.c_int
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    out = (ctypes.c_double * 5)()
+    st = lib.sffn_probe_rates(n_cu, out, 5)
+    torch.cuda.synchronize()
+    if st != 0:
+        raise RuntimeError(f"sffn_probe_rates failed with HIP error {st}")
+    keys = ("lds_reads", "lds_copies", "lds_reads_and_copies", "loads_row_pieces",
+            "loads_mfma_layout")
+    return {"unit": "GB/s per CU", "num_cu": n_cu,
+            **{k: out[i] / 1e9 for i, k in enumerate(keys)},
+            "note": "lds_*: 16-byte ds_read_b128 fragment reads and 16-byte direct-to-LDS "
+                    "copies (L2-resident source), alone and issued together (both kinds "
+                    "summed); loads_*: 16-byte L2-to-register loads, four lanes per 64-byte "
+                    "row piece vs the 32x32 MFMA operand layout"}
+
+
+def gate_lds_bytes(T, d, F):
+    """LDS bytes one launch of the bf16 gate GEMM + TwELL kernel moves: 256 x
+    128 tiles, each ring stage (32 k) copied into LDS once (256 + 128 rows x
+    64 B), and each of the 4 waves reading 2 A and 4 B 16-byte fragments
+    (1 KB per wave each) per 16 k."""
+    tiles = -(-T // 256) * -(-F // 128)
+    copies = tiles * (256 + 128) * d * 2
+    reads = tiles * 4 * (d // 16) * 6 * 1024
+    return copies + reads
+
+
 def per_step(prof, steps):
     return {k: ms / steps for k, (ms, n) in prof.items()}
 
@@ -395,8 +433,20 @@ def bench_forward(args, np, torch, SparseFFN, wl):
     traffic = measured_traffic(W0.name)
     r_gate = roof("mfma", "gate_gemm_twell", flops * args.steps, prof, ["gate_gemm_twell"],
                   peak_mm, traffic.get("gate_gemm_twell"))
+    rates = probe_rates(torch)
     torch_ffn = None
     if W0.dtype == "bf16":
+        # what bounds the gate GEMM: the LDS traffic of its operand copies and
+        # fragment reads, against the LDS rate probed on this device
+        lb = gate_lds_bytes(W0.T, W0.d, W0.F)
+        per_cu = lb / (r_gate["avg_ms"] * 1e-3) / 1e9 / (rates["num_cu"] if rates else 256)
+        r_gate["lds"] = {
+            "bytes_per_launch": lb, "achieved_per_cu": per_cu, "unit": "GB/s per CU",
+            "ceiling_per_cu": rates["lds_reads_and_copies"] if rates else None,
+            "frac": per_cu / rates["lds_reads_and_copies"] if rates else None,
+            "bytes_per_mfma": lb / (flops / 32768.0),
+            "note": "operand copies into LDS plus fragment reads; the ceiling is the probed "
+                    "rate of the two issued together (device_rates)"}
         # context, not part of the path: the vendor bf16 GEMM (torch linear,
         # hipBLASLt) on the gate's shape, plain output, no epilogue, and
         # torch's own bf16 dense layer (two or three linear calls with the
@@ -475,6 +525,7 @@ def bench_forward(args, np, torch, SparseFFN, wl):
                            "frac_of_mfma_peak": dense_flops / (ms_d * 1e-3) / 1e12 / peak_mm,
                            "kernels_ms_per_step": per_step(prof_d, args.steps)},
         "cold": cold,
+        "device_rates": rates,
         "torch_dense_layer": torch_ffn,
         "kernels_ms_per_step": per_step(prof, args.steps),
         "ms_per_step_wall": wall_ms,

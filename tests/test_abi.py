@@ -26,6 +26,16 @@ def test_library_exports_every_symbol():
         assert hasattr(lib, name), name
 
 
+def test_probe_library_exports_its_header():
+    src = open(os.path.join(ROOT, "include", "sffn_probe.h")).read()
+    names = sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(sffn_\w+)\s*\(", src, re.M)))
+    assert names == ["sffn_probe_rates"]
+    lib = ctypes.CDLL(os.path.join(ROOT, "unstructured_sparse_feedforward_amd",
+                                   "libsffn_probe.so"))
+    for name in names:
+        assert hasattr(lib, name), name
+
+
 def test_status_strings():
     lib = B.load_library()
     assert lib.sffn_status_string(0) == b"SFFN_OK"

@@ -127,3 +127,22 @@ def test_backward_empty_batch_zeroes_weight_gradients(env):
     torch.cuda.synchronize()
     assert all(int(torch.count_nonzero(t).item()) == 0 for t in g)
     assert bool((env["dx"] == 7.0).all())
+
+
+def test_probe_rates_run():
+    """libsffn_probe.so measures finite, positive rates and rejects bad
+    arguments on the host."""
+    import math
+    import os
+    path = os.path.join(os.path.dirname(B.LIB_PATH), "libsffn_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.sffn_probe_rates.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.c_int]
+    lib.sffn_probe_rates.restype = ctypes.c_int
+    out = (ctypes.c_double * 5)()
+    assert lib.sffn_probe_rates(0, out, 5) != 0
+    assert lib.sffn_probe_rates(8, out, 4) != 0
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert lib.sffn_probe_rates(n_cu, out, 5) == 0
+    torch.cuda.synchronize()
+    for v in out:
+        assert math.isfinite(v) and v > 0.0

@@ -2,6 +2,7 @@
 
 Each .hip file under csrc/ is compiled to an object in parallel, then the
 objects are linked into unstructured_sparse_feedforward_amd/libsffn.so.
+The device-rate probes under csrc/probe/ become libsffn_probe.so.
 """
 from __future__ import annotations
 
@@ -17,6 +18,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsffn.so")
+# device-rate probes (LDS and load-path ceilings) that the bench reports
+# beside the GEMM rooflines; not part of the layer library
+PROBE_DIR = os.path.join(CSRC, "probe")
+PROBE_LIB = os.path.join(PKG, "libsffn_probe.so")
 
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -58,7 +63,19 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe(cc)
     return LIB
+
+
+def build_probe(cc: str) -> str:
+    srcs = sorted(os.path.join(PROBE_DIR, f) for f in os.listdir(PROBE_DIR) if f.endswith(".hip"))
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [cc, *FLAGS, "-shared", *srcs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on the probes:\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":
