@@ -520,7 +520,7 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   hipError_t e = hipSuccess;
   if (dt == kBF16 && h->ctr_dirty) {
     // a call stopped between its gate GEMM and its list kernel
-    e = hipMemsetAsync(ovf_ctr, 0, (size_t)h->n_t * kCtrStride * 4, stream);
+    e = launch_zero(ovf_ctr, (size_t)h->n_t * kCtrStride * 4, stream);
     if (e != hipSuccess) return hip_fail(h, e, "overflow-record counter");
     h->ctr_dirty = false;
   }
@@ -958,9 +958,9 @@ sffn_status sffn_backward_dense(sffn_handle* h, const void* x, const void* w_gat
   if (!aligned16(dw_gate) || !aligned16(dw_down) || (D.gated ? !aligned16(dw_up) : dw_up != nullptr))
     return fail(h, SFFN_E_ARG, "dW pointers must be 16-byte aligned (dw_up iff the layer is gated)");
   if (T == 0) {
-    hipError_t e = hipMemsetAsync(dw_gate, 0, (size_t)D.d_ff * D.d * 4, stream);
-    if (e == hipSuccess && dw_up) e = hipMemsetAsync(dw_up, 0, (size_t)D.d_ff * D.d * 4, stream);
-    if (e == hipSuccess) e = hipMemsetAsync(dw_down, 0, (size_t)D.d_ff * D.d * 4, stream);
+    hipError_t e = launch_zero(dw_gate, (size_t)D.d_ff * D.d * 4, stream);
+    if (e == hipSuccess && dw_up) e = launch_zero(dw_up, (size_t)D.d_ff * D.d * 4, stream);
+    if (e == hipSuccess) e = launch_zero(dw_down, (size_t)D.d_ff * D.d * 4, stream);
     return e == hipSuccess ? SFFN_OK : hip_fail(h, e, "zero dW");
   }
   if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_down) || !aligned16(dy) ||
@@ -1111,9 +1111,9 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
     return fail(h, SFFN_E_ARG, "dW pointers must be 16-byte aligned (dw_up iff the layer is gated)");
   if (T == 0) {
     // no rows: the weight gradients are zero
-    hipError_t e = hipMemsetAsync(dw_gate, 0, (size_t)D.d_ff * D.d * 4, stream);
-    if (e == hipSuccess && dw_up) e = hipMemsetAsync(dw_up, 0, (size_t)D.d_ff * D.d * 4, stream);
-    if (e == hipSuccess) e = hipMemsetAsync(dw_down, 0, (size_t)D.d_ff * D.d * 4, stream);
+    hipError_t e = launch_zero(dw_gate, (size_t)D.d_ff * D.d * 4, stream);
+    if (e == hipSuccess && dw_up) e = launch_zero(dw_up, (size_t)D.d_ff * D.d * 4, stream);
+    if (e == hipSuccess) e = launch_zero(dw_down, (size_t)D.d_ff * D.d * 4, stream);
     return e == hipSuccess ? SFFN_OK : hip_fail(h, e, "zero dW");
   }
   if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_down) || !aligned16(dy) || !aligned16(dx))
@@ -1405,7 +1405,7 @@ sffn_status sffn_choose_mode(sffn_handle* h, const sffn_twell* tw, int64_t T, in
   double mean = 0.0, f = 0.0;
   if (T > 0) {
     unsigned long long* sum = (unsigned long long*)(h->dstate + 2);
-    hipError_t e = hipMemsetAsync(sum, 0, 2 * sizeof(*sum), stream);
+    hipError_t e = launch_zero(sum, 2 * sizeof(*sum), stream);
     if (e == hipSuccess) e = launch_count_sum(tw->cnt, tw->row_flag, T, h->n_t, sum, stream);
     if (e == hipSuccess) e = hipStreamSynchronize(stream);
     unsigned long long v[2] = {0, 0};

@@ -259,6 +259,10 @@ hipError_t launch_dense_grad(const float* dh, const uint16_t* zs, const uint16_t
 // (R, C multiples of 64; ldi, ldo multiples of 8)
 hipError_t launch_transpose_bf16(const uint16_t* in, int64_t ldi, uint16_t* out, int64_t ldo,
                                  int64_t R, int64_t C, hipStream_t s);
+// zero `bytes` (a multiple of 4) at p (4-byte aligned) with a kernel on s:
+// a stream that a caller captures into a HIP graph then records a kernel
+// node, not a memset node
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 // over the rows t < T with row_flag[t] == 0: out[0] += the sum of their
 // n_t tile counts, out[1] += their number (the caller zeroes out first)
 hipError_t launch_count_sum(const int32_t* cnt, const uint8_t* row_flag, int64_t T, int n_t,

@@ -5,6 +5,8 @@
 // of the gate activations, a fixed-capacity list of (value, neuron) plus a
 // count ("Sparser, Faster, Lighter Transformer Language Models", gist.science
 // explainer, 2. Methodology A).
+#include <algorithm>
+
 #include "sffn_internal.hpp"
 
 namespace sffn {
@@ -143,6 +145,23 @@ __global__ __launch_bounds__(256) void count_sum_kernel(const int32_t* __restric
 hipError_t launch_count_sum(const int32_t* cnt, const uint8_t* row_flag, int64_t T, int n_t,
                             unsigned long long* out, hipStream_t s) {
   hipLaunchKernelGGL(count_sum_kernel, dim3(256), dim3(256), 0, s, cnt, row_flag, T, n_t, out);
+  return hipGetLastError();
+}
+
+namespace {
+__global__ __launch_bounds__(256) void zero_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+}  // namespace
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  if (p == nullptr || bytes % 4 != 0 || (uintptr_t)p % 4 != 0) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)(bytes / 4);
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t*)p, n);
   return hipGetLastError();
 }
 
