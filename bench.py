@@ -146,19 +146,35 @@ def _threads():
         return os.cpu_count()
 
 
-def oracle_forward_ms(inp, n, np):
+# host time the CPU baseline spends on its sample (the oracle runs over the
+# sample again until this much has passed)
+CPU_MIN_MS = 10000.0
+
+
+def repeat_ms(fn, min_ms):
+    """Run fn once and then again until min_ms of host time has passed (at
+    most 64 runs): (total ms, runs)."""
+    total, runs = 0.0, 0
+    while runs == 0 or (total < min_ms and runs < 64):
+        t0 = time.perf_counter()
+        fn()
+        total += (time.perf_counter() - t0) * 1e3
+        runs += 1
+    return total, runs
+
+
+def oracle_forward_ms(inp, n, np, min_ms=0.0):
     """Host ms of the oracle's sparse forward (gate GEMM, TwELL pack,
     per-token up/down over the active neurons, dense rows for flagged
-    tokens) on the first n tokens of one layer."""
+    tokens) on the first n tokens of one layer, repeated until min_ms:
+    (total ms, runs)."""
     import oracle
     w = inp.wl
     x = inp.x[:n].astype(np.float64)
     wg = inp.w_gate.astype(np.float64).T
     wu = None if inp.w_up is None else inp.w_up.astype(np.float64).T
     wd = inp.w_down.astype(np.float64)
-    t0 = time.perf_counter()
-    oracle.sparse_ffn(x, wg, wu, wd, w.tile, w.twell_cap)
-    return (time.perf_counter() - t0) * 1e3
+    return repeat_ms(lambda: oracle.sparse_ffn(x, wg, wu, wd, w.tile, w.twell_cap), min_ms)
 
 
 def cpu_record(tokens, ms, sample):
@@ -359,12 +375,13 @@ def bench_forward(args, np, torch, SparseFFN, wl):
         n_cpu = 2048 if W0.F == 8192 else W0.T
     else:
         n_cpu = min(args.cpu_sample, W0.T)
-    layers, cpu_ms = [], 0.0
+    layers, cpu_ms, cpu_runs = [], 0.0, 0
     for i, W in enumerate(Ws):
         inp = wl.make_inputs(W, seed=args.seed, layer=i)
         # the oracle's host time on this layer's first n_cpu tokens
         if n_cpu > 0:
-            cpu_ms += oracle_forward_ms(inp, n_cpu, np)
+            ms_, cpu_runs = oracle_forward_ms(inp, n_cpu, np, CPU_MIN_MS / len(Ws))
+            cpu_ms += ms_
         ffn = SparseFFN(W.d, W.F, gated=W.gated, twell_cap=W.twell_cap, tile=W.tile,
                         ell_cap=W.ell_cap, dense_rows=W.dense_rows,
                         dtype=torch.bfloat16 if W.dtype == "bf16" else torch.float32,
@@ -543,9 +560,9 @@ def bench_forward(args, np, torch, SparseFFN, wl):
             "method": "amd-smi socket power sampled every ~0.1-0.3 s from a host thread "
                       "while the forward runs back to back for ~3 s"}
     if n_cpu > 0:
-        what = f"first {n_cpu} of {T} tokens"
+        what = f"first {n_cpu} of {T} tokens, {cpu_runs} run(s)"
         out["cpu_baseline"] = cpu_record(
-            n_cpu, cpu_ms,
+            n_cpu * cpu_runs, cpu_ms,
             f"{what}: numpy float64 sparse forward (gate GEMM, TwELL pack, per-token "
             f"up/down over active neurons, dense flagged rows)")
     return out
@@ -595,13 +612,15 @@ def bench_stack(args, np, torch, SparseFFN, wl):
     Ws = [wl.stack_layer(i) for i in range(len(wl.STACK_RAMP))]
     T = Ws[0].T
     n_cpu = 256 if args.cpu_sample < 0 else min(args.cpu_sample, T)
-    weights, cpu_ms = [], 0.0
+    weights, cpu_ms, cpu_tok = [], 0.0, 0
     for i, W in enumerate(Ws):
         inp = wl.make_inputs(W, seed=args.seed, layer=i)
         if i == 0:
             x0, outlier = inp.x, inp.outlier
         if n_cpu > 0:
-            cpu_ms += oracle_forward_ms(inp, n_cpu, np)
+            ms_, runs_ = oracle_forward_ms(inp, n_cpu, np, CPU_MIN_MS / len(Ws))
+            cpu_ms += ms_
+            cpu_tok += n_cpu * runs_
         weights.append(tuple(_dev(inp, k, torch, np) for k in ("w_gate", "w_up", "w_down")))
         del inp
         print(f"layer {i} on the device", file=sys.stderr, flush=True)
@@ -701,10 +720,12 @@ def bench_stack(args, np, torch, SparseFFN, wl):
     }
     if n_cpu > 0:
         out["cpu_baseline"] = cpu_record(
-            n_cpu, cpu_ms,
-            f"first {n_cpu} tokens of each of the {len(Ws)} layers (each on its own seeded "
-            f"input): numpy float64 sparse forward (gate GEMM, TwELL pack, per-token up/down "
-            f"over active neurons, dense flagged rows)")
+            cpu_tok / len(Ws), cpu_ms,
+            f"first {n_cpu} tokens of each of the {len(Ws)} layers, each layer's oracle run "
+            f"until {CPU_MIN_MS / len(Ws) / 1e3:.2f} s (on the layer's own seeded input, whose "
+            f"values do not change the oracle's cost): numpy float64 sparse forward (gate "
+            f"GEMM, TwELL pack, per-token up/down over active neurons, dense flagged rows); "
+            f"tokens/ms through all {len(Ws)} layers")
     return out
 
 
@@ -783,18 +804,17 @@ def bench_train(args, np, torch, SparseFFN, wl):
     import oracle
     W = wl.TRAIN_HYBRID
     inp = wl.make_inputs(W, seed=args.seed)
-    n_cpu = (1024 if args.cpu_sample < 0 else min(args.cpu_sample, W.T))
-    cpu_ms = 0.0
+    n_cpu = (W.T if args.cpu_sample < 0 else min(args.cpu_sample, W.T))
+    cpu_ms, cpu_runs = 0.0, 0
     if n_cpu > 0:
         # the oracle's training step: its float64 forward and backward
         x = inp.x[:n_cpu].astype(np.float64)
         wg = inp.w_gate.astype(np.float64).T
         wu = inp.w_up.astype(np.float64).T
         wd = inp.w_down.astype(np.float64)
-        t0 = time.perf_counter()
-        oracle.backward(x, wg, wu, wd, inp.dy[:n_cpu].astype(np.float64))
-        cpu_ms = (time.perf_counter() - t0) * 1e3
-        del x, wg, wu, wd
+        dy64 = inp.dy[:n_cpu].astype(np.float64)
+        cpu_ms, cpu_runs = repeat_ms(lambda: oracle.backward(x, wg, wu, wd, dy64), CPU_MIN_MS)
+        del x, wg, wu, wd, dy64
     a = [_dev(inp, k, torch, np) for k in ("x", "w_gate", "w_up", "w_down")]
     dy = _dev(inp, "dy", torch, np)
     del inp
@@ -917,8 +937,9 @@ def bench_train(args, np, torch, SparseFFN, wl):
     }
     if n_cpu > 0:
         out["cpu_baseline"] = cpu_record(
-            n_cpu, cpu_ms, f"first {n_cpu} of {T} tokens: numpy float64 forward and backward "
-                           f"(the gradients of x and of all three weights)")
+            n_cpu * cpu_runs, cpu_ms,
+            f"first {n_cpu} of {T} tokens, {cpu_runs} run(s): numpy float64 forward and "
+            f"backward (the gradients of x and of all three weights)")
     return out
 
 
