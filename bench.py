@@ -294,11 +294,11 @@ def gate_lds_bytes(T, d, F):
     """LDS bytes one launch of the bf16 gate GEMM + TwELL kernel moves: 256 x
     128 tiles, each ring stage (32 k) copied into LDS once (256 + 128 rows x
     64 B), and each of the 4 waves reading 2 A and 4 B 16-byte fragments
-    (1 KB per wave each) per 16 k."""
+    (1 KB per wave each) per 16 k: (copy bytes, read bytes)."""
     tiles = -(-T // 256) * -(-F // 128)
     copies = tiles * (256 + 128) * d * 2
     reads = tiles * 4 * (d // 16) * 6 * 1024
-    return copies + reads
+    return copies, reads
 
 
 def per_step(prof, steps):
@@ -453,17 +453,17 @@ def bench_forward(args, np, torch, SparseFFN, wl):
     rates = probe_rates(torch)
     torch_ffn = None
     if W0.dtype == "bf16":
-        # what bounds the gate GEMM: the LDS traffic of its operand copies and
-        # fragment reads, against the LDS rate probed on this device
-        lb = gate_lds_bytes(W0.T, W0.d, W0.F)
-        per_cu = lb / (r_gate["avg_ms"] * 1e-3) / 1e9 / (rates["num_cu"] if rates else 256)
+        # the gate GEMM's operand copies into LDS and its fragment reads,
+        # each against the rate probed on this device
+        cb, rb = gate_lds_bytes(W0.T, W0.d, W0.F)
+        per_s = (r_gate["avg_ms"] * 1e-3) * 1e9 * (rates["num_cu"] if rates else 256)
         r_gate["lds"] = {
-            "bytes_per_launch": lb, "achieved_per_cu": per_cu, "unit": "GB/s per CU",
-            "ceiling_per_cu": rates["lds_reads_and_copies"] if rates else None,
-            "frac": per_cu / rates["lds_reads_and_copies"] if rates else None,
-            "bytes_per_mfma": lb / (flops / 32768.0),
-            "note": "operand copies into LDS plus fragment reads; the ceiling is the probed "
-                    "rate of the two issued together (device_rates)"}
+            "copy_bytes_per_launch": cb, "read_bytes_per_launch": rb, "unit": "GB/s per CU",
+            "copies_per_cu": cb / per_s, "reads_per_cu": rb / per_s,
+            "copy_frac": cb / per_s / rates["lds_copies"] if rates else None,
+            "read_frac": rb / per_s / rates["lds_reads"] if rates else None,
+            "note": "direct-to-LDS operand copies and 16-byte fragment reads per launch, "
+                    "against the probed rates of each (device_rates)"}
         # context, not part of the path: the vendor bf16 GEMM (torch linear,
         # hipBLASLt) on the gate's shape, plain output, no epilogue, and
         # torch's own bf16 dense layer (two or three linear calls with the

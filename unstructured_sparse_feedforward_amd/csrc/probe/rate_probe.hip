@@ -25,20 +25,28 @@ constexpr int kRows = 8192;    // source rows (32 MiB)
 // 1 KB steps with lane-contiguous 16-byte pieces (no bank conflicts).
 template <int MODE>
 __global__ __launch_bounds__(256) void lds_probe(const char* __restrict__ src, u32x4* out, int reps) {
-  __shared__ __align__(16) char smem[32 * 1024];
+  // reads walk the first 32 KB, copies land in the second (8 KB per wave in
+  // each half)
+  __shared__ __align__(16) u32x4 smem[64 * 1024 / 16];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  char* my = smem + wave * 8192;
   const int rb = (((blockIdx.x / 8) % 4) * 4 + wave) * 16;   // rows < 256: L2-resident
   const char* s = src + (int64_t)(rb + (lane >> 2)) * kRowB + (lane & 3) * 16;
+  for (int i = threadIdx.x; i < 2048; i += 256) smem[i] = u32x4{(unsigned)i, 1u, 2u, 3u};
+  __syncthreads();
   u32x4 acc = {0, 0, 0, 0};
+  // the wave's 8 KB: 8 pieces of 64 lanes x 16 bytes
+  int base = wave * 512 + lane;
   for (int r = 0; r < reps; ++r) {
+    // an offset the compiler cannot see through, so that every repetition
+    // reads LDS again (all 8 reads issued before their results are used)
+    asm volatile("" : "+v"(base));
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       if (MODE != 0)
         __builtin_amdgcn_global_load_lds((const void*)(s + ((r * 8 + c) & 63) * 64),
-                                         (void*)(my + c * 1024), 16, 0, 0);
-      if (MODE != 1) acc ^= *(volatile const u32x4*)(my + c * 1024 + lane * 16);
+                                         (void*)(smem + 2048 + wave * 512 + c * 64), 16, 0, 0);
+      if (MODE != 1) acc ^= smem[base + c * 64];
     }
   }
   __builtin_amdgcn_s_waitcnt(0);   // no copy in flight when the wave ends
