@@ -264,7 +264,9 @@ sffn_status sffn_gate_preact(sffn_handle* h, const void* x, const void* w_gate,
  *     non-NULL the TwELL is written there, else into the workspace.
  *   mode SFFN_DENSE: the plain dense layer with the same kernels' GEMMs;
  *     for bf16 the hidden activations are rounded once to bf16 between the
- *     two GEMMs, as in a standard bf16 feedforward. tw must be NULL.
+ *     two GEMMs, as in a standard bf16 feedforward, and W_d is transposed
+ *     into the workspace first (both operands of the down GEMM then read
+ *     k-contiguous). tw must be NULL.
  * w_up must be NULL iff the layer is non-gated. The workspace must hold
  * sffn_workspace_bytes(op = SFFN_OP_FORWARD_SPARSE or _DENSE).
  * SPARSE: rows whose TwELL overflowed, or with more than K = desc.ell_cap
@@ -371,7 +373,8 @@ sffn_status sffn_choose_mode(sffn_handle* h, const sffn_twell* tw, int64_t T, in
  * act (caller-owned, sffn_train_dense_act_bytes) receives Z_s [T, F], U_s
  * [T, F] (gated) and H [T, F], all bf16: the saved activations the
  * backward reads. The workspace is sffn_workspace_bytes(
- * SFFN_OP_TRAIN_DENSE) (none).
+ * SFFN_OP_TRAIN_DENSE) (W_d transposed, F x d bf16: both operands of the
+ * down GEMM k-contiguous).
  */
 sffn_status sffn_train_dense_act_bytes(const sffn_handle* h, int64_t T, size_t* bytes);
 sffn_status sffn_forward_train_dense(sffn_handle* h, const void* x, const void* w_gate,
@@ -383,8 +386,8 @@ sffn_status sffn_forward_train_dense(sffn_handle* h, const void* x, const void* 
  * dW_g = x^T dZ, dW_u = x^T dU, dW_d = H^T dy. Outputs float32 and
  * overwritten, dW neuron-major [F, d] as in sffn_backward. The workspace is
  * sffn_workspace_bytes(SFFN_OP_BACKWARD_DENSE) (dH [T, F] fp32, dZ | dU
- * [T, 2F] and dZ, dU, H transposed, bf16). T = 0 stores zero weight
- * gradients. */
+ * [T, 2F] and dZ, dU, H transposed, and W_g | W_u, x and dy transposed,
+ * bf16). T = 0 stores zero weight gradients. */
 sffn_status sffn_backward_dense(sffn_handle* h, const void* x, const void* w_gate,
                                 const void* w_up, const void* w_down, const void* act,
                                 const void* dy, int64_t T, float* dx, float* dw_gate,

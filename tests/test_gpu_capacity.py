@@ -119,7 +119,8 @@ def test_caller_hybrid_too_small_raises():
 def test_workspace_follows_the_sparse_work():
     """Workspace bytes at the benchmark shapes: the inference workspace
     (T = 8192, d = 2048, F = 5632, C = 8, K = 64, 512 dense rows) is about
-    the size of the dense layer's bf16 hidden tensor, and no region grows
+    the size of the dense layer's bf16 hidden tensor (the dense layer's
+    workspace is that tensor and its transposed W_d), and no region grows
     as T x F."""
     w = wl.GATED_1P5B
     ffn = SparseFFN(w.d, w.F, gated=True, twell_cap=w.twell_cap, ell_cap=w.ell_cap,
@@ -127,7 +128,7 @@ def test_workspace_follows_the_sparse_work():
     sp = ffn.workspace_bytes(w.T, B.SFFN_OP_FORWARD_SPARSE)
     de = ffn.workspace_bytes(w.T, B.SFFN_OP_FORWARD_DENSE)
     _print(f"inference workspace: sparse {sp / 1e6:.1f} MB, dense {de / 1e6:.1f} MB")
-    assert de == w.T * w.F * 2
+    assert de == w.T * w.F * 2 + w.F * w.d * 2
     assert sp <= 120e6
     # doubling T adds per-token regions only (no T x F region)
     sp2 = ffn.workspace_bytes(2 * w.T, B.SFFN_OP_FORWARD_SPARSE)

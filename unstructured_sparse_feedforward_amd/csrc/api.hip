@@ -145,11 +145,14 @@ struct Layout {
   size_t ovf = 0, tw_val = 0, tw_idx = 0, tw_cnt = 0, tw_flag = 0, tw_list = 0, tw_nf = 0;
   size_t ell_a = 0, ell_idx = 0, ell_cnt = 0, bk = 0, upart = 0, dlist = 0, ndense = 0;
   size_t hid = 0, zovf = 0, ovf_map = 0, part = 0, total = 0;
+  // dense layer: W_d transposed to [d, F] (bf16)
+  size_t wdt = 0;
   // backward
   size_t drec = 0, ncnt = 0, noff = 0, thist = 0, toff = 0, meta = 0, dH = 0, gz_rm = 0;
   size_t gz_t = 0, gu_t = 0, gh_t = 0, xb = 0, dyb = 0;
-  // dense training step
-  size_t dh_f = 0, dh_rm = 0, dz_t = 0, du_t = 0, h_t = 0;
+  // dense training step (transposed weights and inputs, bf16: the
+  // k-contiguous operands of its long-K GEMMs)
+  size_t dh_f = 0, dh_rm = 0, dz_t = 0, du_t = 0, h_t = 0, wgu_t = 0, x_t = 0, dy_t = 0;
   int64_t ldt = 0;
 };
 
@@ -219,15 +222,24 @@ Layout layout(const sffn_handle* h, int64_t T, int op) {
   }
   if (op == SFFN_OP_FORWARD_DENSE) {
     L.hid = take((size_t)T * F * esize(h));
+    if (h->desc.dtype == SFFN_BF16) L.wdt = take((size_t)F * d * 2);
+  }
+  if (op == SFFN_OP_TRAIN_DENSE) {
+    // W_d transposed [d, F]
+    L.wdt = take((size_t)F * d * 2);
   }
   if (op == SFFN_OP_BACKWARD_DENSE) {
     // dH [T, F] fp32; dZ | dU rows [T, 2F], and dZ, dU and H transposed
-    // [F, T], bf16
+    // [F, T], bf16; W_g | W_u transposed [d, 2F] (non-gated: [d, F]); x
+    // and dy transposed [d, T]
     L.dh_f = take((size_t)T * F * 4);
     L.dh_rm = take((size_t)T * F * 2 * 2);
     L.dz_t = take((size_t)T * F * 2);
     L.du_t = take((size_t)T * F * 2);
     L.h_t = take((size_t)T * F * 2);
+    L.wgu_t = take((size_t)d * F * 2 * (h->desc.gated ? 2 : 1));
+    L.x_t = take((size_t)d * T * 2);
+    L.dy_t = take((size_t)d * T * 2);
   }
   if (op == SFFN_OP_BACKWARD) {
     // sized for up to R backup rows
@@ -455,7 +467,8 @@ static sffn_status forward_dense(sffn_handle* h, const void* x, const void* wg, 
     e = launch_gemm(dt, nb, false, dt == kBF16 ? kEpiHiddenBF16 : kEpiStoreF32, g, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "dense gate/up GEMM");
-  // y = H W_d
+  // y = H W_d. bf16: W_d [F, d] is first transposed into the workspace, so
+  // that both operands of the down GEMM are k-contiguous (the long-K ring)
   GemmArgs g2 = {};
   g2.A = hid;
   g2.lda = D.d_ff;
@@ -470,7 +483,15 @@ static sffn_status forward_dense(sffn_handle* h, const void* x, const void* wg, 
   g2.grid = gemm_grid(dt, 1, h->num_cu);
   {
     ProfScope ps(h, SFFN_K_DENSE_DOWN, stream);
-    e = launch_gemm(dt, 1, true, kEpiStoreF32, g2, stream);
+    if (dt == kBF16) {
+      uint16_t* wdt = at<uint16_t>(ws, L.wdt);
+      e = launch_transpose_bf16((const uint16_t*)wd, D.d, wdt, D.d_ff, D.d_ff, D.d, stream);
+      g2.B0 = wdt;
+      g2.ldb = D.d_ff;
+      if (e == hipSuccess) e = launch_gemm(dt, 1, false, kEpiStoreF32, g2, stream);
+    } else {
+      e = launch_gemm(dt, 1, true, kEpiStoreF32, g2, stream);
+    }
   }
   if (e != hipSuccess) return hip_fail(h, e, "dense down GEMM");
   return SFFN_OK;
@@ -930,8 +951,6 @@ sffn_status sffn_forward_train_dense(sffn_handle* h, const void* x, const void* 
   g2.A = hid;
   g2.lda = D.d_ff;
   g2.M = (int)T;
-  g2.B0 = w_down;
-  g2.ldb = D.d;
   g2.N = D.d;
   g2.K = D.d_ff;
   g2.out = y;
@@ -939,8 +958,13 @@ sffn_status sffn_forward_train_dense(sffn_handle* h, const void* x, const void* 
   g2.num_cu = h->num_cu;
   g2.grid = gemm_grid(kBF16, 1, h->num_cu);
   {
+    // W_d transposed first: both operands of the down GEMM k-contiguous
     ProfScope ps(h, SFFN_K_TRAIN_DENSE_DOWN, stream);
-    e = launch_gemm(kBF16, 1, true, kEpiStoreF32, g2, stream);
+    uint16_t* wdt = at<uint16_t>(ws, L.wdt);
+    e = launch_transpose_bf16((const uint16_t*)w_down, D.d, wdt, D.d_ff, D.d_ff, D.d, stream);
+    g2.B0 = wdt;
+    g2.ldb = D.d_ff;
+    if (e == hipSuccess) e = launch_gemm(kBF16, 1, false, kEpiStoreF32, g2, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "dense training down GEMM");
   return SFFN_OK;
@@ -1001,41 +1025,51 @@ sffn_status sffn_backward_dense(sffn_handle* h, const void* x, const void* w_gat
                             dut, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "dense backward dH, dZ, dU");
-  // dx = dZ W_g^T (+ dU W_u^T)
-  for (int pass = 0; pass < (D.gated ? 2 : 1); ++pass) {
+  // dx = [dZ | dU] [W_g | W_u]^T as one GEMM over K = 2F (non-gated: dZ
+  // W_1^T over K = F), with the weights transposed first so that both
+  // operands are k-contiguous
+  {
+    ProfScope ps(h, SFFN_K_BWD_DENSE_DX, stream);
+    uint16_t* wt = at<uint16_t>(ws, L.wgu_t);
+    const int64_t ldw = (D.gated ? 2 : 1) * (int64_t)D.d_ff;
+    e = launch_transpose_bf16((const uint16_t*)w_gate, D.d, wt, ldw, D.d_ff, D.d, stream);
+    if (e == hipSuccess && D.gated)
+      e = launch_transpose_bf16((const uint16_t*)w_up, D.d, wt + D.d_ff, ldw, D.d_ff, D.d, stream);
     GemmArgs f = {};
-    f.A = dzu + (pass ? D.d_ff : 0);
+    f.A = dzu;
     f.lda = 2 * (int64_t)D.d_ff;
     f.M = (int)T;
-    f.B0 = pass ? w_up : w_gate;
-    f.ldb = D.d;
+    f.B0 = wt;
+    f.ldb = ldw;
     f.N = D.d;
-    f.K = D.d_ff;
+    f.K = (int)ldw;
     f.out = dx;
     f.ldo = D.d;
-    f.accumulate = pass;
     f.num_cu = h->num_cu;
     f.grid = gemm_grid(kBF16, 1, h->num_cu);
-    ProfScope ps(h, SFFN_K_BWD_DENSE_DX, stream);
-    e = launch_gemm(kBF16, 1, true, kEpiStoreF32, f, stream);
-    if (e != hipSuccess) return hip_fail(h, e, "dense backward dx GEMM");
+    if (e == hipSuccess) e = launch_gemm(kBF16, 1, false, kEpiStoreF32, f, stream);
   }
-  // H transposed ([F, T]: the k-contiguous operand of the dW_d GEMM)
+  if (e != hipSuccess) return hip_fail(h, e, "dense backward dx GEMM");
+  // H, x and dy transposed ([F, T], [d, T]: the k-contiguous operands of
+  // the dW GEMMs)
+  uint16_t* xt = at<uint16_t>(ws, L.x_t);
+  uint16_t* dyt = at<uint16_t>(ws, L.dy_t);
   {
     ProfScope ps(h, SFFN_K_BWD_DENSE_DW, stream);
     e = launch_transpose_bf16(a16 + (D.gated ? 2 : 1) * TF, D.d_ff, ht, T, T, D.d_ff, stream);
+    if (e == hipSuccess) e = launch_transpose_bf16((const uint16_t*)x, D.d, xt, T, T, D.d, stream);
+    if (e == hipSuccess) e = launch_transpose_bf16((const uint16_t*)dy, D.d, dyt, T, T, D.d, stream);
   }
   if (e != hipSuccess) return hip_fail(h, e, "dense backward transpose");
-  // dW_g = dZ^T x, dW_u = dU^T x, dW_d = H^T dy (the transposed operands
-  // k-contiguous, x and dy n-contiguous)
+  // dW_g = dZ^T x, dW_u = dU^T x, dW_d = H^T dy
   for (int pass = 0; pass < 3; ++pass) {
     if (pass == 1 && !D.gated) continue;
     GemmArgs w = {};
     w.A = pass == 0 ? (const void*)dzt : pass == 1 ? (const void*)dut : (const void*)ht;
     w.lda = T;
     w.M = D.d_ff;
-    w.B0 = pass == 2 ? dy : x;
-    w.ldb = D.d;
+    w.B0 = pass == 2 ? dyt : xt;
+    w.ldb = T;
     w.N = D.d;
     w.K = (int)T;
     w.out = pass == 0 ? dw_gate : pass == 1 ? dw_up : dw_down;
@@ -1043,7 +1077,7 @@ sffn_status sffn_backward_dense(sffn_handle* h, const void* x, const void* w_gat
     w.num_cu = h->num_cu;
     w.grid = gemm_grid(kBF16, 1, h->num_cu);
     ProfScope ps(h, SFFN_K_BWD_DENSE_DW, stream);
-    e = launch_gemm(kBF16, 1, true, kEpiStoreF32, w, stream);
+    e = launch_gemm(kBF16, 1, false, kEpiStoreF32, w, stream);
     if (e != hipSuccess) return hip_fail(h, e, "dense backward dW GEMM");
   }
   return SFFN_OK;
