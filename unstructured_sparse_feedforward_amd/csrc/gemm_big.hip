@@ -10,29 +10,22 @@
 // fragments from LDS for 16 MFMAs, and those reads are spread over the
 // previous substep's MFMAs.
 //
-// k-contiguous operands stream through a ring of NSLOT LDS slots of 32 k
-// each (32 KB per slot), filled by direct-to-LDS copies that are spread
-// over the MFMAs as well; up to NSLOT - 1 stages are in flight while one
-// is multiplied. An n-contiguous B goes through registers instead, with
-// two 64-wide stages.
+// k-contiguous operands stream through a ring of LDS slots filled by
+// direct-to-LDS copies that are spread over the MFMAs as well: 32 k per
+// slot (gemm_ring_kernel), or 64 k per slot for long K
+// (gemm_ring64_kernel). The ring runs on across a workgroup's tiles, so a
+// tile starts with its first fragments in registers. An n-contiguous B
+// goes through registers instead, with two 64-wide stages
+// (gemm_bt_kernel).
 //
-// Measured on the 8192 x 5632 x 2048 gate GEMM, the main loop runs at the
-// MFMA issue rate with the core clock down to about 1.5 GHz: with all 256
-// CUs multiplying, reading LDS and streaming operands the chip is at its
-// power limit, so the clock rather than the schedule sets the pace.
-//
-// Every epilogue works on the accumulator registers directly. In the
-// 32 x 32 MFMA layout register q of a block holds, for lanes 0-31 and
-// 32-63, 32 consecutive columns of two different rows; when a wave's 128
-// columns are exactly one 128-column TwELL tile, the four blocks of a
-// register index give two complete tile rows: four ballots, scalar
-// popcounts and a lane prefix count place every positive entry in its
-// ascending slot (the TwELL of "Sparser, Faster, Lighter Transformer
-// Language Models", gist.science explainer, 2. Methodology A, written in
-// the gate GEMM's epilogue as in 2. Methodology B). That epilogue is
-// scalar and vector work with the matrix cores idle, so the gate GEMM
-// runs as gemm_twell2_kernel: 256 x 128 tiles (one TwELL tile wide), two
-// workgroups per CU, one workgroup's epilogue beside the other's MFMAs.
+// Every epilogue works on the accumulator registers. For the gate GEMM a
+// wave's 128 columns are exactly one 128-column TwELL tile (the TwELL of
+// "Sparser, Faster, Lighter Transformer Language Models", gist.science
+// explainer, 2. Methodology A, written in the gate GEMM's epilogue as in
+// 2. Methodology B): its accumulators go through a 16 KB LDS staging tile
+// per wave, 32 rows at a time, and each lane packs half a row from there
+// (twell_block_lds), so that the epilogue is mostly straight-line vector
+// work with little latency exposed while the matrix cores wait.
 #include "sffn_internal.hpp"
 
 namespace sffn {
@@ -145,140 +138,144 @@ __device__ __forceinline__ void mfma_substep(f32x16_t (&acc)[NB][4][Cfg<NB>::JB]
 
 // ---------------------------------------------------------------- epilogues
 
-// ReLU + TwELL of 32 rows (rbase ..) of one 128-column TwELL tile tb, held
-// in a wave's accumulator blocks blk[j] (columns 32 j ..); SB: the values
-// are stored as bf16.
+// ReLU + TwELL of a wave's 128 x 128 accumulator block (one TwELL tile of
+// 128 rows), staged through LDS 32 rows at a time: the wave writes a
+// block's 64 accumulator registers into its 16 KB staging tile, then lane
+// l takes row l % 32 and its half l / 32 of the 128 columns, builds the
+// mask of its 64 positives, exchanges counts with the other half's lane
+// and stores its share of the row's first C entries in ascending column
+// order. The staging tile holds row r's float c at
+// r * 128 + 4 * (((c / 4) ^ r) % 32) + c % 4 (16-byte chunks XOR-swizzled
+// by row: a lane's 16-byte reads of one chunk index across 16 rows hit 16
+// distinct bank groups).
+__device__ __forceinline__ int stage_off(int r, int c) {
+  return r * 128 + ((((c >> 2) ^ r) & 31) << 2) + (c & 3);
+}
+
 template <bool SB>
-__device__ __forceinline__ void twell_block(const GemmArgs& g, f32x16_t (&blk)[4], int rbase,
-                                            int tb, int lane) {
+__device__ __forceinline__ void twell_block_lds(const GemmArgs& g, f32x16_t (&blk)[4], int rbase,
+                                                int tb, int lane, float* stage) {
   const int M = g.M;
-  const int h = lane >> 5;     // which of the register's two rows
-  const int c32 = lane & 31;   // column inside the 32-column block
-  // Register q of block (i, j) holds row r0(q) in lanes 0-31 and row
-  // r0(q) + 4 in lanes 32-63, column j*32 + lane%32: four ballots give a
-  // row pair's 128 columns. A row pair without a positive costs the
-  // ballots and one scalar test. Callers derive rbase0 and tb from a
-  // uniform (readfirstlane) wave index, so that the ballots, counts and
-  // tests stay in scalar registers.
-  const int C = g.C;
-  const uint32_t row_entries = (uint32_t)g.n_t * (uint32_t)C;
-  const uint32_t half_off = (uint32_t)h * 4u * row_entries;
-  const uint32_t col0 = (uint32_t)(tb * kTile + c32);
+  if (rbase >= M) return;
+  const int h = lane >> 5;
+  const int c32 = lane & 31;
+  // the previous block's reads of the staging tile are done
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  // register q of block j: row r = 8 (q / 4) + q % 4 + 4 h, column
+  // 32 j + c32. Its staging offset splits into a lane part, one of four by
+  // q % 4 (the chunk index's low bits are c32 / 4 ^ 4 h ^ q % 4), and a
+  // constant (the row, and the chunk's high bits j ^ q / 4), so that only
+  // four addresses are live.
+  int lb[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) lb[k] = 512 * h + ((((c32 >> 2) ^ (4 * h) ^ k)) << 2) + (c32 & 3);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      stage[lb[q & 3] + ((q >> 2) * 8 + (q & 3)) * 128 + (((j ^ (q >> 2)) & 3) << 5)] =
+          agpr(blk[j][q]);
+    // a few register indices at a time (bounded register pressure)
+    if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __builtin_amdgcn_sched_barrier(0);
+  const int rr = lane & 31;        // this lane's row of the block
+  const int hh = lane >> 5;        // and its half of the 128 columns
+  const bool row_ok = rbase + rr < M;
+  // the mask of this half's positives, bit k = column 64 hh + k: its 16
+  // chunks of 4 columns from the last down, 4 reads in flight, each
+  // chunk's bits shifted in at the bottom
+  uint32_t mlo = 0, mhi = 0;
   {
-    if (rbase >= M) return;
-    const bool full = rbase + 32 <= M;
-    // this block's first entry of tile tb; the block spans 32 rows, so
-    // every entry offset from it fits 32 bits
-    const int64_t e0 = ((int64_t)rbase * g.n_t + tb) * C;
-    char* vbase = (char*)g.tw_val + e0 * (SB ? 2 : 4);
-    char* ibase = (char*)(g.tw_idx + e0);
-    int cnt_lane = 0;  // lane r < 32 collects the count of row rbase + r
+    const float* rowp = stage + rr * 128;
+    const int hb = ((16 * hh) ^ rr) & 16;
+    const int x = rr & 15;
+#pragma unroll 1
+    for (int c4 = 3; c4 >= 0; --c4) {
+      f32x4_t v[4];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int r0 = (q >> 2) * 8 + (q & 3);
-      // the lane's row exists (all of them but in the last row block)
-      const bool row_ok = full || rbase + r0 + h * 4 < M;
-      float av[4];
-      uint64_t bal[4];
+      for (int k = 3; k >= 0; --k) v[k] = *(const f32x4_t*)(rowp + ((hb | ((4 * c4 + k) ^ x)) << 2));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        av[j] = agpr(blk[j][q]);
-        bal[j] = __ballot(row_ok && av[j] > 0.0f);
+      for (int k = 3; k >= 0; --k) {
+        const uint32_t nib = (uint32_t)(v[k][0] > 0.0f) | ((uint32_t)(v[k][1] > 0.0f) << 1) |
+                             ((uint32_t)(v[k][2] > 0.0f) << 2) | ((uint32_t)(v[k][3] > 0.0f) << 3);
+        mhi = (mhi << 4) | (mlo >> 28);
+        mlo = (mlo << 4) | nib;
       }
-      if ((bal[0] | bal[1] | bal[2] | bal[3]) != 0) {
-        int c0[4], c1[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          c0[j] = __popc((uint32_t)bal[j]);
-          c1[j] = __popc((uint32_t)(bal[j] >> 32));
-        }
-        const int n0c = c0[0] + c0[1] + c0[2] + c0[3];
-        const int n1c = c1[0] + c1[1] + c1[2] + c1[3];
-        cnt_lane = lane == r0 ? n0c : (lane == r0 + 4 ? n1c : cnt_lane);
-        // a tile row that overflows C keeps all its pre-activations in a
-        // record of its own, so that the dense path of its row needs no
-        // gate recomputation: the tile column's counter (one per column,
-        // so that the few heavy rows' requests spread over n_t addresses)
-        // hands out the column's next record; its number goes to the row's
-        // entry of the tile map
-        if (g.zovf != nullptr && (n0c > C || n1c > C)) {
-          const bool o0 = n0c > C, o1 = n1c > C;
-          int rec = 0;
-          if ((lane == 0 && o0) || (lane == 32 && o1))
-            rec = atomicAdd(g.ovf_ctr + tb * kCtrStride, 1);
-          const int r_0 = __builtin_amdgcn_readlane(rec, 0);
-          const int r_1 = __builtin_amdgcn_readlane(rec, 32);
-          if (h ? o1 : o0) {
-            const int my = h ? r_1 : r_0;
-            const int id = my < g.ovf_cap ? tb * g.ovf_cap + my : -1;
-            if (id >= 0) {
-              float* zr = g.zovf + (int64_t)id * kTile + c32;
-#pragma unroll
-              for (int j = 0; j < 4; ++j) zr[j * 32] = av[j];
-            }
-            if (c32 == 0) g.ovf_map[(int64_t)(rbase + r0 + h * 4) * g.n_t + tb] = id;
-          }
-        }
-        const uint32_t ro = (uint32_t)r0 * row_entries + half_off;
-        int b0 = 0, b1 = 0;  // positives of the two rows in the blocks before j
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (bal[j] != 0) {
-            // the lane's rank among its row's positives: those of the
-            // earlier blocks, then the ballot bits below it (mbcnt also
-            // counts the first row's bits for the second row, hence - c0)
-            const int base = h ? b1 - c0[j] : b0;
-            if (row_ok && av[j] > 0.0f) {
-              const int rank = base + (int)__builtin_amdgcn_mbcnt_hi(
-                                          (uint32_t)(bal[j] >> 32),
-                                          __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
-              if (rank < C) {
-                const uint32_t e = ro + (uint32_t)rank;
-                if constexpr (SB) *(uint16_t*)(vbase + e * 2u) = (uint16_t)f32_to_bf16(av[j]);
-                else *(float*)(vbase + e * 4u) = av[j];
-                *(uint16_t*)(ibase + e * 2u) = (uint16_t)(col0 + (uint32_t)j * 32u);
-              }
-            }
-          }
-          b0 += c0[j];
-          b1 += c1[j];
-        }
-      }
-      // one register index at a time: keeps the accumulator reads of
-      // later groups from being hoisted
-      __builtin_amdgcn_sched_barrier(0);
     }
-    if (lane < 32 && rbase + lane < M) g.tw_cnt[(int64_t)(rbase + lane) * g.n_t + tb] = cnt_lane;
+  }
+  uint64_t mask = row_ok ? ((uint64_t)mhi << 32) | mlo : 0;
+  const int n_own = __popcll(mask);
+  const int n_other = __shfl_xor(n_own, 32, 64);
+  const int total = n_own + n_other;
+  const int C = g.C;
+  const int64_t row = (int64_t)rbase + rr;
+  if (hh == 0 && row_ok) g.tw_cnt[row * g.n_t + tb] = total;
+  // a tile row past C keeps all its pre-activations in a record of its
+  // own (the tile column's counter hands out the column's next record; its
+  // number goes to the row's entry of the tile map)
+  if (g.zovf != nullptr) {
+    const bool ovf = row_ok && total > C;
+    int rec = 0;
+    if (ovf && hh == 0) rec = atomicAdd(g.ovf_ctr + tb * kCtrStride, 1);
+    rec = __shfl_xor(rec, 32, 64) + rec;   // one of the two lanes holds it
+    if (ovf) {
+      const int id = rec < g.ovf_cap ? tb * g.ovf_cap + rec : -1;
+      if (id >= 0) {
+        float* zr = g.zovf + (int64_t)id * kTile + 64 * hh;
+#pragma unroll
+        for (int k16 = 0; k16 < 16; ++k16) {
+          const int c = 16 * hh + k16;
+          *(f32x4_t*)(zr + 4 * k16) = *(const f32x4_t*)(stage + rr * 128 + (((c ^ rr) & 31) << 2));
+        }
+      }
+      if (hh == 0) g.ovf_map[row * g.n_t + tb] = id;
+    }
+  }
+  // this half's positives in ascending column order, ranks from the first
+  // half's count for the second half
+  int rank = hh ? n_other : 0;
+  const int64_t e0 = (row * g.n_t + tb) * C;
+  uint64_t m = mask;
+  while (m != 0 && rank < C) {
+    const int k = (int)__builtin_ctzll(m);
+    m &= m - 1;
+    const int col = 64 * hh + k;
+    const float v = stage[stage_off(rr, col)];
+    if constexpr (SB) ((uint16_t*)g.tw_val)[e0 + rank] = (uint16_t)f32_to_bf16(v);
+    else ((float*)g.tw_val)[e0 + rank] = v;
+    g.tw_idx[e0 + rank] = (uint16_t)(tb * kTile + col);
+    ++rank;
   }
 }
 
-// Blocks I.. of a wave's NI: unrolled by recursion, so that every
-// accumulator index is a constant (an accumulator array indexed at run time
-// would live in scratch memory).
 template <int I, int NI, bool SB>
-struct TwellBlocks {
+struct TwellBlocksLds {
   static __device__ __forceinline__ void run(const GemmArgs& g, f32x16_t (&acc)[NI][4],
-                                             int rbase0, int tb, int lane) {
-    twell_block<SB>(g, acc[I], rbase0 + I * 32, tb, lane);
-    TwellBlocks<I + 1, NI, SB>::run(g, acc, rbase0, tb, lane);
+                                             int rbase0, int tb, int lane, float* stage) {
+    twell_block_lds<SB>(g, acc[I], rbase0 + I * 32, tb, lane, stage);
+    TwellBlocksLds<I + 1, NI, SB>::run(g, acc, rbase0, tb, lane, stage);
   }
 };
 template <int NI, bool SB>
-struct TwellBlocks<NI, NI, SB> {
-  static __device__ __forceinline__ void run(const GemmArgs&, f32x16_t (&)[NI][4], int, int, int) {}
+struct TwellBlocksLds<NI, NI, SB> {
+  static __device__ __forceinline__ void run(const GemmArgs&, f32x16_t (&)[NI][4], int, int, int,
+                                             float*) {}
 };
 
 template <int NI>
-__device__ __forceinline__ void twell_epilogue(const GemmArgs& g, f32x16_t (&acc)[NI][4],
-                                               int rbase0, int tb, int lane) {
+__device__ __forceinline__ void twell_epilogue_lds(const GemmArgs& g, f32x16_t (&acc)[NI][4],
+                                                   int rbase0, int tb, int lane, float* stage) {
   if (tb * kTile >= g.N) return;
-  if (g.store_bf16) TwellBlocks<0, NI, true>::run(g, acc, rbase0, tb, lane);
-  else TwellBlocks<0, NI, false>::run(g, acc, rbase0, tb, lane);
+  if (g.store_bf16) TwellBlocksLds<0, NI, true>::run(g, acc, rbase0, tb, lane, stage);
+  else TwellBlocksLds<0, NI, false>::run(g, acc, rbase0, tb, lane, stage);
 }
 
 template <int NB, int EPI>
 __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16_t (&acc)[NB][4][Cfg<NB>::JB],
-                                         int m0, int n0, int wr, int wc, int lane) {
+                                         int m0, int n0, int wr, int wc, int lane,
+                                         float* stage = nullptr) {
   constexpr int JB = Cfg<NB>::JB;
   const int M = g.M;
   const int h = lane >> 5;     // which of the register's two rows
@@ -286,7 +283,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, f32x16_t (&acc)[NB][
   if constexpr (EPI == kEpiTwell) {
     // a wave's 128 columns are one TwELL tile
     static_assert(NB == 1, "TwELL epilogue: one B operand");
-    twell_epilogue<4>(g, acc[0], m0 + wr * 128, (n0 >> 7) + wc, lane);
+    twell_epilogue_lds<4>(g, acc[0], m0 + wr * 128, (n0 >> 7) + wc, lane, stage);
     return;
   }
   if constexpr (EPI == kEpiTrainFwd) {
@@ -431,13 +428,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
   constexpr int LPS = 4 + NB * BPW;      // direct-to-LDS copies per wave and stage
   static_assert(LPS == 8, "stage = 8 copies per wave");
   static_assert((NSLOT - 1) * LPS <= 63, "vmcnt range");
-  __shared__ __align__(16) char smem[NSLOT * SLOT];
+  // the TwELL epilogue's staging tiles (16 KB per wave) follow the ring
+  constexpr int STAGE = EPI == kEpiTwell ? 4 * 32 * 128 * 4 : 0;
+  __shared__ __align__(16) char smem[NSLOT * SLOT + STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
   const int wr = wave >> 1;
   const int wc = wave & 1;
+  float* const stage = STAGE ? (float*)(smem + NSLOT * SLOT) + wave * 4096 : nullptr;
   const int M = g.M;
   // K may live on the device (as in the n-contiguous kernel below)
   const int Kd = g.k_dev ? g.k_mult * ((device_rows(g.k_dev, g.k_cap) + 63) / 64 * 64) : g.K;
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
       }
       int m0, n0;
       ts.coords(L, BN, m0, n0);
-      epilogue<NB, EPI>(g, acc, m0, n0, wr, wc, lane);
+      epilogue<NB, EPI>(g, acc, m0, n0, wr, wc, lane, stage);
       if (!has_next) break;
       L += ts.G8;
       has_next = L + ts.G8 < ts.t_end;
@@ -632,152 +632,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
         slot = next;
       }
     }
-    epilogue<NB, EPI>(g, acc, m0, n0, wr, wc, lane);
+    epilogue<NB, EPI>(g, acc, m0, n0, wr, wc, lane, stage);
   }
   __builtin_amdgcn_s_waitcnt(kWaitAll);
-}
-
-// ---------------------------------------------------------------- two per CU
-
-// The gate GEMM + TwELL with two workgroups per CU, so that one
-// workgroup's TwELL epilogue (scalar and vector work that leaves the
-// matrix cores idle) runs beside the other's main loop. A block tile is
-// 256 rows x one 128-column TwELL tile; wave w multiplies rows 64 w .. +64
-// against all 128 columns (2 x 4 MFMA blocks, 128 accumulator registers),
-// so every wave owns whole TwELL tile rows. Three 24 KB ring slots per
-// workgroup (k-contiguous A and B copied straight into LDS), six copies
-// per wave and stage, the same waits and barriers as the ring kernel.
-constexpr int P2_BN = 128;
-constexpr int P2_NSLOT = 3;
-constexpr int P2_SLOT = (BM + P2_BN) * RROWB;   // 24 KB
-constexpr int P2_LPS = 6;                        // 4 A + 2 B copies per wave
-
-__device__ __forceinline__ void p2_reads() {
-#pragma unroll
-  for (int k = 0; k < 6; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-}
-__device__ __forceinline__ void p2_reads_copies() {
-#pragma unroll
-  for (int k = 0; k < 6; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one global-to-LDS copy
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-}
-
-__global__ __launch_bounds__(NT, 2) void gemm_twell2_kernel(GemmArgs g) {
-  static_assert((P2_NSLOT - 1) * P2_LPS <= 63, "vmcnt range");
-  __shared__ __align__(16) char smem[P2_NSLOT * P2_SLOT];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int M = g.M;
-  const int nkt = g.K / RBK;
-  const TileSched ts(M, g.N, P2_BN);
-  const char* Ab = (const char*)g.A;
-  const char* Bb = (const char*)g.B0;
-  const int64_t lda_b = g.lda * 2;
-  const int64_t ldb_b = g.ldb * 2;
-  // direct-to-LDS copy lane layout as in the ring kernel
-  const int lr = lane >> 2;
-  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
-
-  for (int L = ts.t_begin + ts.local; L < ts.t_end; L += ts.G8) {
-    int m0, n0;
-    ts.coords(L, P2_BN, m0, n0);
-    const char* a_src[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = min(m0 + wave * 64 + i * 16 + lr, M - 1);
-      a_src[i] = Ab + (int64_t)m * lda_b + lchunk * 16;
-    }
-    const char* b_src[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int n = min(n0 + wave * 32 + i * 16 + lr, g.N - 1);
-      b_src[i] = Bb + (int64_t)n * ldb_b + lchunk * 16;
-    }
-    auto issue_stage = [&](int kt, int slot) {
-      char* base = smem + slot * P2_SLOT;
-      const int64_t kb = (int64_t)kt * RBK * 2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(a_src[i] + kb),
-                                         (void*)(base + (wave * 64 + i * 16) * RROWB), 16, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(b_src[i] + kb),
-                                         (void*)(base + (BM + wave * 32 + i * 16) * RROWB), 16,
-                                         0, 0);
-    };
-
-    f32x16_t acc[2][4];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-
-    u32x4_t af[2][2];
-    u32x4_t bfr[2][4];
-    auto read_frags = [&](int slot, int s, int buf) {
-      const char* sa = smem + slot * P2_SLOT;
-      const int ch = 2 * s + (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[buf][i] = *(const u32x4_t*)(sa + rlds_off(wave * 64 + i * 32 + (lane & 31), ch));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[buf][j] = *(const u32x4_t*)(sa + BM * RROWB + rlds_off(j * 32 + (lane & 31), ch));
-    };
-    auto mfmas = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, af[buf][i]), __builtin_bit_cast(bf16x8_t, bfr[buf][j]),
-              acc[i][j], 0, 0, 0);
-    };
-
-    // the ring kernel's pipeline with three slots (see there)
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
-    wg_barrier();   // the previous tile's readers are done with LDS
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int p = 0; p < P2_NSLOT; ++p) issue_stage(min(p, nkt - 1), p);
-    __builtin_amdgcn_s_waitcnt(wait_imm((P2_NSLOT - 1) * P2_LPS, 15));  // stage 0 landed
-    wg_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(0, 0, 0);
-
-    int slot = 0;
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int next = slot + 1 == P2_NSLOT ? 0 : slot + 1;
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // fragments of substep 0
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(slot, 1, 1);
-      mfmas(0);
-      p2_reads();
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(wait_imm((P2_NSLOT - 2) * P2_LPS, 0));
-      wg_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(next, 0, 0);
-      issue_stage(min(kt + P2_NSLOT, nkt - 1), slot);
-      mfmas(1);
-      p2_reads_copies();
-      __builtin_amdgcn_sched_barrier(0);
-      slot = next;
-    }
-    twell_epilogue<2>(g, acc, m0 + wave * 64, n0 >> 7, lane);
-  }
 }
 
 // ---------------------------------------------------------------- n-contiguous B
@@ -976,6 +833,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring64_kernel(GemmArgs g) {
   constexpr int BPW = BN / 4 / 8;                // 8-row copies of B per wave and operand
   constexpr int LPS = APW + NB * BPW;            // copies per wave and stage
   static_assert(LPS == 16, "stage = 16 copies per wave");
+  static_assert(EPI != kEpiTwell, "the TwELL epilogue stages through LDS the ring kernel holds");
   __shared__ __align__(16) char smem[2 * SLOT];
 
   const int tid = threadIdx.x;
@@ -1165,6 +1023,13 @@ hipError_t launch_ring(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
+// the gate GEMM + TwELL on the ring: three 32 KB slots and 64 KB of
+// staging tiles fill the 160 KB of LDS
+hipError_t launch_ring_twell(const GemmArgs& g, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_ring_kernel<1, kEpiTwell, 3>), dim3(g.grid), dim3(NT), 0, s, g);
+  return hipGetLastError();
+}
+
 template <int NB, int EPI>
 hipError_t launch_ring64(const GemmArgs& g, hipStream_t s) {
   hipLaunchKernelGGL((gemm_ring64_kernel<NB, EPI>), dim3(g.grid), dim3(NT), 0, s, g);
@@ -1199,11 +1064,7 @@ hipError_t launch_gemm_big(int nb, bool bt, Epi epi, const GemmArgs& g, hipStrea
     hipLaunchKernelGGL((gemm_bt_kernel<kEpiStoreF32>), dim3(g.grid), dim3(NT), 0, s, g);
     return hipGetLastError();
   }
-  if (epi == kEpiTwell) {
-    // two workgroups per CU
-    hipLaunchKernelGGL(gemm_twell2_kernel, dim3(2 * (g.num_cu / NXCD) * NXCD), dim3(NT), 0, s, g);
-    return hipGetLastError();
-  }
+  if (epi == kEpiTwell) return launch_ring_twell(g, s);
   // long K: 64-k stages (half the barriers and copy waits per MFMA) win;
   // at K = 2048 the 32-k ring is as fast or faster
   if (epi == kEpiStoreF32)
