@@ -292,12 +292,13 @@ def probe_rates(torch):
 
 def gate_lds_bytes(T, d, F):
     """LDS bytes one launch of the bf16 gate GEMM + TwELL kernel moves: 256 x
-    128 tiles, each ring stage (32 k) copied into LDS once (256 + 128 rows x
-    64 B), and each of the 4 waves reading 2 A and 4 B 16-byte fragments
-    (1 KB per wave each) per 16 k: (copy bytes, read bytes)."""
-    tiles = -(-T // 256) * -(-F // 128)
-    copies = tiles * (256 + 128) * d * 2
-    reads = tiles * 4 * (d // 16) * 6 * 1024
+    256 tiles, each ring stage (32 k) copied into LDS once (256 + 256 rows x
+    64 B), and each of the 4 waves reading 4 A and 4 B 16-byte fragments
+    (1 KB per wave each) per 16 k: (copy bytes, read bytes). The epilogue's
+    staging reads (16 KB per wave and 32-row block) are not counted."""
+    tiles = -(-T // 256) * -(-F // 256)
+    copies = tiles * (256 + 256) * d * 2
+    reads = tiles * 4 * (d // 16) * 8 * 1024
     return copies, reads
 
 
