@@ -71,8 +71,15 @@ def test_gate_preact(w, T):
 
 # --------------------------------------------------------------- fused TwELL
 
+G2048 = wl.GATED_1P5B.replace(F=2048, nnz=12, name="g2048")
+
+
 @pytest.mark.parametrize("w,T", [(wl.SMALL_F32, 128), (wl.GATED_1P5B, 1024),
-                                 (wl.NONGATED[108], 333)])
+                                 (wl.NONGATED[108], 333),
+                                 # the full gated shape, and a narrower layer with fewer,
+                                 # more and ragged 256-row tiles than CUs
+                                 (wl.GATED_1P5B, 8192), (G2048, 6144), (G2048, 6100),
+                                 (G2048, 14336)])
 def test_fused_twell_matches_pack_of_own_z(w, T):
     """The gate GEMM's TwELL epilogue equals the stand-alone pack of the
     same kernel's pre-activations, bit for bit (GPU against GPU)."""
