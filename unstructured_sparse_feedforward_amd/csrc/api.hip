@@ -602,14 +602,41 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   //    overflowing rows
   int32_t* brow = train ? hy->brow : at<int32_t>(ws, L.dlist);
   int32_t* n_bk = train ? hy->n_backup : at<int32_t>(ws, L.ndense);
+  // the sparse up/down over the ELL rows, d sliced across the XCDs (step 5)
+  SliceArgs sa = {};
+  sa.x = x;
+  sa.wu = w_up;
+  sa.wd = w_down;
+  sa.ell_idx = ea.ell_idx;
+  sa.ell_a = ea.ell_a;
+  sa.ell_cnt = ea.ell_cnt;
+  sa.bk = ea.bk;
+  sa.T = T;
+  sa.d = D.d;
+  sa.K = K;
+  sa.Kp = Kp;
+  sa.upart = at<float>(ws, L.upart);
+  sa.ell_u = (train && D.gated) ? hy->ell_u : nullptr;
+  sa.store_bf16 = sb_of(h);
+  sa.y = y;
+  // bf16 gated layers with the sliced up/down: the lists are built by eight
+  // extra workgroups of the up projection's launch, and the dense path's
+  // hidden rows are combined in the launch of the slice sums, so that
+  // these short latency-bound steps overlap the sparse ones
+  const bool joint = dt == kBF16 && D.gated && (train || D.updown != 1);
   {
-    ProfScope ps(h, SFFN_K_FLAGS, stream);
     const ListArgs lb = {ea.bk, brow, mcap, n_bk, train ? hy->slot : nullptr, status,
                          dt == kBF16 ? ovf_ctr : nullptr, h->n_t};
     const ListArgs lf = {t.row_flag, t.flagged, T, t.n_flagged, nullptr, nullptr, nullptr, 0};
-    e = launch_backup_list(lb, &lf, T, stream);
+    if (joint) {
+      ProfScope ps(h, SFFN_K_SPARSE_UP, stream);
+      e = launch_up_with_lists(dt, sa, lb, &lf, T, stream);
+    } else {
+      ProfScope ps(h, SFFN_K_FLAGS, stream);
+      e = launch_backup_list(lb, &lf, T, stream);
+    }
   }
-  if (e != hipSuccess) return hip_fail(h, e, "backup list");
+  if (e != hipSuccess) return hip_fail(h, e, joint ? "sparse up + backup list" : "backup list");
   h->ctr_dirty = false;
 
   // 4. dense path: hidden rows H = ReLU(z) * (x W_u) (split-K over the
@@ -623,6 +650,7 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
   void* hid = at<char>(ws, L.hid);
   float* part = at<float>(ws, L.part);
   GemmArgs down_late = {};   // bf16: the dense path's down product, run last
+  GemmArgs hid_late = {};    // joint: the hidden rows' combine, beside the slice sums
   if (mcap > 0 && dt == kBF16) {
     // ReLU(z) of the rows comes from the gate GEMM itself (their TwELL
     // tiles, and the saved pre-activations of the tiles that overflowed);
@@ -667,9 +695,10 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     {
       ProfScope ps(h, SFFN_K_FLAG_GATEUP, stream);
       if (D.gated) e = launch_gemm_small(false, kEpiHiddenSplitK, f, stream);
-      if (e == hipSuccess) e = launch_flag_hidden(nb, f, stream);
+      if (e == hipSuccess && !joint) e = launch_flag_hidden(nb, f, stream);
     }
     if (e != hipSuccess) return hip_fail(h, e, "dense-path hidden rows");
+    if (joint) hid_late = f;
     // H_hi W_d + H_lo W_d: a dual A over the F rows of W_d
     GemmArgs f2 = {};
     f2.A = hid;
@@ -761,34 +790,20 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     if (e != hipSuccess) return hip_fail(h, e, "split-K reduce");
   }
 
-  // 5. sparse up/down over the ELL rows, d sliced across the XCDs
-  SliceArgs sa = {};
-  sa.x = x;
-  sa.wu = w_up;
-  sa.wd = w_down;
-  sa.ell_idx = ea.ell_idx;
-  sa.ell_a = ea.ell_a;
-  sa.ell_cnt = ea.ell_cnt;
-  sa.bk = ea.bk;
-  sa.T = T;
-  sa.d = D.d;
-  sa.K = K;
-  sa.Kp = Kp;
-  sa.upart = at<float>(ws, L.upart);
-  sa.ell_u = (train && D.gated) ? hy->ell_u : nullptr;
-  sa.store_bf16 = sb_of(h);
-  sa.y = y;
+  // 5. sparse up/down over the ELL rows (the up projection already ran when
+  //    joint)
   if (!train && D.updown == 1) {
     ProfScope ps(h, SFFN_K_FUSED_UPDOWN, stream);
     e = launch_fused_updown(D.gated != 0, sa, stream);
   } else {
-    if (D.gated) {
+    if (D.gated && !joint) {
       ProfScope ps(h, SFFN_K_SPARSE_UP, stream);
       e = launch_updown(dt, true, 0, sa, stream);
     }
     if (D.gated && e == hipSuccess) {
       ProfScope ps(h, SFFN_K_SPARSE_HSUM, stream);
-      e = launch_updown(dt, true, 2, sa, stream);
+      e = hid_late.out != nullptr ? launch_flag_hidden_hsum(dt, hid_late, sa, stream)
+                                  : launch_updown(dt, true, 2, sa, stream);
     }
     if (e == hipSuccess) {
       ProfScope ps(h, SFFN_K_SPARSE_DOWN, stream);

@@ -536,7 +536,7 @@ namespace {
 // entries that fall on the 4 columns (at most C ascending ids, read by all
 // the tile's threads); u is the sum of the split-K partials in split order.
 template <int NB>
-__global__ __launch_bounds__(256) void flag_hidden_kernel(GemmArgs g) {
+__device__ __forceinline__ void flag_hidden_rows(const GemmArgs& g, int64_t blk, int64_t nblk) {
   const int M = device_rows(g.m_dev, g.m_cap);
   if (M <= 0) return;
   const int F = g.N;
@@ -545,8 +545,7 @@ __global__ __launch_bounds__(256) void flag_hidden_kernel(GemmArgs g) {
   const int64_t pstride = (int64_t)mt * BM * F;
   const int f4 = F / 4;
   const int64_t total = (int64_t)M * f4;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t e = blk * blockDim.x + threadIdx.x; e < total; e += nblk * blockDim.x) {
     const int m = (int)(e / f4);
     const int c = (int)(e - (int64_t)m * f4) * 4;
     // the partials depend on the dense-path row only: in flight first
@@ -605,6 +604,22 @@ __global__ __launch_bounds__(256) void flag_hidden_kernel(GemmArgs g) {
     *(u32x2_t*)(dst + c) = u32x2_t{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
     *(u32x2_t*)(dst + g.lo_off + c) = u32x2_t{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
   }
+}
+
+template <int NB>
+__global__ __launch_bounds__(256) void flag_hidden_kernel(GemmArgs g) {
+  flag_hidden_rows<NB>(g, blockIdx.x, gridDim.x);
+}
+
+// The same beside the sparse path's slice sums, in one launch: workgroups
+// [0, nflag) combine the dense path's rows, the rest sum the slices. Both
+// are short chains of dependent loads, so they overlap each other's
+// latency.
+template <int NS>
+__global__ __launch_bounds__(256) void flag_hidden_hsum_kernel(GemmArgs g, SliceArgs a,
+                                                               int nflag) {
+  if ((int)blockIdx.x < nflag) flag_hidden_rows<2>(g, blockIdx.x, nflag);
+  else hsum_rows<NS>(a, (int64_t)blockIdx.x - nflag);
 }
 
 }  // namespace
@@ -748,6 +763,19 @@ hipError_t launch_flag_hidden(int nb, const GemmArgs& g, hipStream_t s) {
   const dim3 grid((unsigned)(8 * g.num_cu)), block(256);
   if (nb == 2) hipLaunchKernelGGL(flag_hidden_kernel<2>, grid, block, 0, s, g);
   else hipLaunchKernelGGL(flag_hidden_kernel<1>, grid, block, 0, s, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_flag_hidden_hsum(Dtype dt, const GemmArgs& g, const SliceArgs& a,
+                                   hipStream_t s) {
+  int ns, epl;
+  slice_shape(dt, a.d, &ns, &epl);
+  const int nflag = 8 * g.num_cu;
+  const dim3 grid((unsigned)(nflag + (a.T + 3) / 4)), block(256);
+  if (ns == 2) hipLaunchKernelGGL(flag_hidden_hsum_kernel<2>, grid, block, 0, s, g, a, nflag);
+  else if (ns == 4) hipLaunchKernelGGL(flag_hidden_hsum_kernel<4>, grid, block, 0, s, g, a, nflag);
+  else if (ns == 8) hipLaunchKernelGGL(flag_hidden_hsum_kernel<8>, grid, block, 0, s, g, a, nflag);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -244,6 +244,11 @@ hipError_t launch_hidden_combine(Dtype dt, int nb, const GemmArgs& g, hipStream_
 // H = a u (or a) stored as bf16 hi | lo into out; a and u rows into
 // out_a / out_u when set.
 hipError_t launch_flag_hidden(int nb, const GemmArgs& g, hipStream_t s);
+struct SliceArgs;
+// bf16 gated layers: launch_flag_hidden (two B operands) and the sparse
+// path's slice sums (launch_updown phase 2) in one launch
+hipError_t launch_flag_hidden_hsum(Dtype dt, const GemmArgs& g, const SliceArgs& a,
+                                   hipStream_t s);
 
 hipError_t launch_pack(const float* z, int64_t T, int F, int C, int sb, void* val, uint16_t* idx,
                        int32_t* cnt, uint32_t* ovf, int ovf_words, hipStream_t s);
@@ -335,10 +340,37 @@ struct SliceArgs {
   float* y;               // [T, d]
 };
 void slice_shape(Dtype dt, int d, int* ns, int* epl);
+
+// Between the sparse up and down phases (gated): u_k = sum of the slice
+// partials in slice order and h_k = a_k * u_k, written over slice 0's
+// partial (the lane that reads a slot's partials is the one that writes
+// it); u_k is saved for training. With 16-bit storage a_k is the stored
+// value and u_k is rounded as it would be stored, so that h is what the
+// backward recomputes. One wave per row, four rows per workgroup blk.
+template <int NS>
+__device__ __forceinline__ void hsum_rows(const SliceArgs& a, int64_t blk) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = blk * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const int n = a.ell_cnt[t];
+  for (int k = lane; k < n; k += 64) {
+    float u = 0.0f;
+#pragma unroll
+    for (int r = 0; r < NS; ++r) u += a.upart[((int64_t)r * a.T + t) * a.Kp + k];
+    const int64_t q = t * a.K + k;
+    u = sround(u, a.store_bf16);
+    if (a.ell_u) sstore(a.ell_u, q, u, a.store_bf16);
+    a.upart[t * a.Kp + k] = sload(a.ell_a, q, a.store_bf16) * u;
+  }
+}
 // phase 0: per-slice partial dot products (gated layers only);
 // phase 2: their sums u and h = a * u (gated; h over slice 0's partials);
 // phase 1: down projection into y.
 hipError_t launch_updown(Dtype dt, bool gated, int phase, const SliceArgs& a, hipStream_t s);
+// bf16 gated layers: phase 0 with the row lists of launch_backup_list built
+// beside it in the same launch (l1 nullable)
+hipError_t launch_up_with_lists(Dtype dt, const SliceArgs& a, const ListArgs& l0,
+                                const ListArgs* l1, int64_t T, hipStream_t s);
 // bf16 layers, d in {512, 1024, 2048, 4096}: the up and down projections of
 // the ELL rows in one kernel without d slices (rows with bk set skipped)
 hipError_t launch_fused_updown(bool gated, const SliceArgs& a, hipStream_t s);

@@ -105,24 +105,24 @@ __global__ __launch_bounds__(256) void rows_kernel(EllArgs a) {
   }
 }
 
-// One workgroup: list the backup rows in ascending order (the first cap of
-// them), their true count and, when requested, every row's backup slot
-// (-1 for ELL rows).
-__global__ __launch_bounds__(1024) void backup_list_kernel(ListArgs l0, ListArgs l1, int64_t T) {
-  // workgroup b builds list b (two lists in one launch in training)
-  const ListArgs& L = blockIdx.x ? l1 : l0;
+// One workgroup of NTH threads: list the backup rows in ascending order
+// (the first cap of them), their true count and, when requested, every
+// row's backup slot (-1 for ELL rows).
+template <int NTH>
+__device__ __forceinline__ void list_rows(const ListArgs& L, int64_t T) {
   const uint8_t* __restrict__ bk = L.bk;
   int32_t* __restrict__ brow = L.brow;
   const int64_t cap = L.cap;
   int32_t* __restrict__ n_backup = L.n;
   int32_t* __restrict__ slot = L.slot;
   constexpr int RPT = 16;
-  __shared__ int wsum[16];
+  constexpr int NW = NTH / 64;
+  __shared__ int wsum[NW];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   int carry = 0;
-  for (int64_t base = 0; base < T; base += 1024 * RPT) {
+  for (int64_t base = 0; base < T; base += NTH * RPT) {
     const int64_t r0 = base + (int64_t)tid * RPT;
     uint32_t bits = 0;
     if (r0 + RPT <= T) {
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(1024) void backup_list_kernel(ListArgs l0, ListArgs
     if (lane == 63) wsum[wave] = inc;
     __syncthreads();
     int wbase = 0, total = 0;
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < NW; ++k) {
       if (k < wave) wbase += wsum[k];
       total += wsum[k];
     }
@@ -164,7 +164,12 @@ __global__ __launch_bounds__(1024) void backup_list_kernel(ListArgs l0, ListArgs
     if (L.status && carry > cap) *L.status = 1;
   }
   if (L.reset)
-    for (int i = tid; i < L.n_reset; i += 1024) L.reset[i * kCtrStride] = 0;
+    for (int i = tid; i < L.n_reset; i += NTH) L.reset[i * kCtrStride] = 0;
+}
+
+__global__ __launch_bounds__(1024) void backup_list_kernel(ListArgs l0, ListArgs l1, int64_t T) {
+  // workgroup b builds list b (two lists in one launch in training)
+  list_rows<1024>(blockIdx.x ? l1 : l0, T);
 }
 
 // Sum over the 8 lanes of each lane octet, result in all 8 (quad swaps,
@@ -184,7 +189,7 @@ __device__ __forceinline__ float octet_sum(float v) {
 // the count are 0 (the partial is not stored). Workgroup b runs on XCD
 // b mod 8, so with 8 slices an XCD gathers from one slice of W_u.
 template <typename E, int NS, int SW>
-__global__ __launch_bounds__(256) void up_partial_kernel(SliceArgs a) {
+__device__ __forceinline__ void up_partial(const SliceArgs& a, int64_t blk) {
   constexpr int EPL = 16 / (int)sizeof(E);
   constexpr int NLD = SW / 8 / EPL;      // 16-byte loads per lane per slot
   constexpr int CH = 64;
@@ -195,8 +200,8 @@ __global__ __launch_bounds__(256) void up_partial_kernel(SliceArgs a) {
   const int wave = threadIdx.x >> 6;
   const int g = lane >> 3;
   const int l = lane & 7;
-  const int s = blockIdx.x % NS;
-  const int64_t t = (int64_t)(blockIdx.x / NS) * 4 + wave;
+  const int s = (int)(blk % NS);
+  const int64_t t = (blk / NS) * 4 + wave;
   if (t >= a.T) return;
   const int n = a.ell_cnt[t];
   if (n == 0) return;
@@ -250,27 +255,29 @@ __global__ __launch_bounds__(256) void up_partial_kernel(SliceArgs a) {
   }
 }
 
-// Between the phases (gated): u_k = sum of the slice partials in slice
-// order and h_k = a_k * u_k, written over slice 0's partial (the lane that
-// reads a slot's partials is the one that writes it); u_k is saved for
-// training. With 16-bit storage a_k is the stored value and u_k is rounded
-// as it would be stored, so that h is what the backward recomputes. One
-// wave per row.
+template <typename E, int NS, int SW>
+__global__ __launch_bounds__(256) void up_partial_kernel(SliceArgs a) {
+  up_partial<E, NS, SW>(a, blockIdx.x);
+}
+
+// The same with the dense path's row lists (one or two) built beside it:
+// workgroups 0 .. 7 are the list builders (those past the lists return at
+// once; eight keep workgroup b of the up projection on XCD b mod 8).
+template <typename E, int NS, int SW>
+__global__ __launch_bounds__(256) void up_partial_list_kernel(SliceArgs a, ListArgs l0,
+                                                               ListArgs l1, int nl, int64_t T) {
+  if (blockIdx.x < 8) {
+    if ((int)blockIdx.x < nl) list_rows<256>(blockIdx.x ? l1 : l0, T);
+    return;
+  }
+  up_partial<E, NS, SW>(a, (int64_t)blockIdx.x - 8);
+}
+
+// Between the phases (gated): the slice sums (hsum_rows, in the header,
+// shared with the dense path's combine launch)
 template <int NS>
 __global__ __launch_bounds__(256) void hsum_kernel(SliceArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.T) return;
-  const int n = a.ell_cnt[t];
-  for (int k = lane; k < n; k += 64) {
-    float u = 0.0f;
-#pragma unroll
-    for (int r = 0; r < NS; ++r) u += a.upart[((int64_t)r * a.T + t) * a.Kp + k];
-    const int64_t q = t * a.K + k;
-    u = sround(u, a.store_bf16);
-    if (a.ell_u) sstore(a.ell_u, q, u, a.store_bf16);
-    a.upart[t * a.Kp + k] = sload(a.ell_a, q, a.store_bf16) * u;
-  }
+  hsum_rows<NS>(a, blockIdx.x);
 }
 
 // Phase 2: y_t = sum_k h_k * W_d[j_k], h_k from the sum above (non-gated:
@@ -522,6 +529,29 @@ void slice_shape(Dtype, int d, int* ns, int* epl) {
 hipError_t launch_rows(const EllArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(rows_kernel, dim3((unsigned)((a.T + 3) / 4)), dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename E, int NS, int SW>
+hipError_t launch_up_lists_t(const SliceArgs& a, const ListArgs& l0, const ListArgs* l1,
+                             int64_t T, hipStream_t st) {
+  const ListArgs none = {};
+  hipLaunchKernelGGL((up_partial_list_kernel<E, NS, SW>),
+                     dim3((unsigned)(8 + NS * ((a.T + 3) / 4))), dim3(256), 0, st, a, l0,
+                     l1 ? *l1 : none, l1 ? 2 : 1, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_up_with_lists(Dtype dt, const SliceArgs& a, const ListArgs& l0,
+                                const ListArgs* l1, int64_t T, hipStream_t s) {
+  int ns, epl;
+  slice_shape(dt, a.d, &ns, &epl);
+  const int sw = a.d / ns;
+  if (dt != kBF16) return hipErrorInvalidValue;
+  if (ns == 2 && sw == 256) return launch_up_lists_t<uint16_t, 2, 256>(a, l0, l1, T, s);
+  if (ns == 4 && sw == 256) return launch_up_lists_t<uint16_t, 4, 256>(a, l0, l1, T, s);
+  if (ns == 8 && sw == 256) return launch_up_lists_t<uint16_t, 8, 256>(a, l0, l1, T, s);
+  if (ns == 8 && sw == 512) return launch_up_lists_t<uint16_t, 8, 512>(a, l0, l1, T, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_backup_list(const ListArgs& l0, const ListArgs* l1, int64_t T, hipStream_t s) {
