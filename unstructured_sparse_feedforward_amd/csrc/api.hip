@@ -718,7 +718,8 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
     f2.split_max = std::min(kSplitMax, f2.K / 32);
     f2.num_cu = h->num_cu;
     f2.grid = gemm_small_grid(h->num_cu);
-    // launched after the sparse down projection
+    // launched after the sparse down projection (joint: before it, its
+    // reduce inside that launch)
     down_late = f2;
   } else if (mcap > 0) {
     GemmArgs f = {};
@@ -805,7 +806,18 @@ static sffn_status sparse_forward(sffn_handle* h, const void* x, const void* w_g
       e = hid_late.out != nullptr ? launch_flag_hidden_hsum(dt, hid_late, sa, stream)
                                   : launch_updown(dt, true, 2, sa, stream);
     }
-    if (e == hipSuccess) {
+    if (e == hipSuccess && joint && down_late.out != nullptr) {
+      // the dense path's down product first, its split-K reduce in the
+      // launch of the sparse down projection (they write other rows of y)
+      {
+        ProfScope ps(h, SFFN_K_FLAG_DOWN, stream);
+        e = launch_gemm_small(true, kEpiStoreF32, down_late, stream);
+      }
+      if (e != hipSuccess) return hip_fail(h, e, "dense-path down GEMM");
+      ProfScope ps(h, SFFN_K_SPARSE_DOWN, stream);
+      e = launch_down_with_reduce(dt, D.gated != 0, sa, down_late, stream);
+      down_late = {};
+    } else if (e == hipSuccess) {
       ProfScope ps(h, SFFN_K_SPARSE_DOWN, stream);
       e = launch_updown(dt, D.gated != 0, 1, sa, stream);
     }

@@ -62,11 +62,8 @@ __device__ __forceinline__ u32x2_t ld8(const char* p) { return *(const u32x2_t*)
 // The host keeps split_max <= the number of K stages, so every split owns
 // at least one stage.
 __device__ __forceinline__ int num_splits(const GemmArgs& g, int mt, int ntl) {
-  if (g.part == nullptr) return 1;
-  int s = g.split_target / (mt * ntl);
-  if (s > g.split_max) s = g.split_max;
-  if (s > kSplitCap) s = kSplitCap;
-  return s < 1 ? 1 : s;
+  static_assert(BM == 128 && BN == 128, "splitk_count's tiles");
+  return splitk_count(g, mt, ntl);
 }
 
 template <typename E>
@@ -453,33 +450,7 @@ __global__ __launch_bounds__(256) void hidden_combine_kernel(GemmArgs g) {
 }
 
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, float* y, int64_t ldy) {
-  const int M = device_rows(g.m_dev, g.m_cap);
-  if (M <= 0) return;
-  const int mt = (M + BM - 1) / BM;
-  const int ntl = g.N / BN;
-  const int S = num_splits(g, mt, ntl);
-  if (S <= 1) return;
-  const int Mpad = mt * BM;
-  const int n4 = g.N / 4;
-  const int64_t total = (int64_t)M * n4;
-  const int64_t pstride = (int64_t)Mpad * g.N;
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int m = (int)(e / n4);
-    const int c = (int)(e - (int64_t)m * n4) * 4;
-    const float* p = g.part + (int64_t)m * g.N + c;
-    float* dst = y + (int64_t)(g.out_rows ? g.out_rows[m] : m) * ldy + c;
-    f32x4_t v[kSplitCap];
-#pragma unroll
-    for (int k = 0; k < kSplitCap; ++k)
-      if (k < S) v[k] = *(const f32x4_t*)(p + k * pstride);
-    f32x4_t acc = v[0];
-#pragma unroll
-    for (int k = 1; k < kSplitCap; ++k)
-      if (k < S) acc += v[k];
-    if (g.accumulate) acc += *(const f32x4_t*)dst;
-    *(f32x4_t*)dst = acc;
-  }
+  splitk_reduce_rows(g, y, ldy, blockIdx.x, gridDim.x);
 }
 
 template <typename E, int NB, bool BT, int EPI>

@@ -316,6 +316,51 @@ __device__ __forceinline__ int device_rows(const int32_t* m_dev, int m_cap) {
   return (m_cap > 0 && m > m_cap) ? m_cap : m;
 }
 
+// Number of K splits of a split-K GEMM over 128 x 128 tiles (mt x ntl of
+// them), as the GEMMs of gemm.hip and gemm_small.hip choose it. The host
+// keeps split_max <= the number of K stages, so every split owns at least
+// one stage.
+__device__ __forceinline__ int splitk_count(const GemmArgs& g, int mt, int ntl) {
+  if (g.part == nullptr) return 1;
+  int s = g.split_target / (mt * ntl);
+  if (s > g.split_max) s = g.split_max;
+  if (s > kSplitCap) s = kSplitCap;
+  return s < 1 ? 1 : s;
+}
+
+// y[out_rows[m], :] (+)= sum of the S split-K partials of row m, in split
+// order (deterministic); workgroup blk of nblk, grid-stride over 4 columns
+// per thread. Nothing to do with a single split (the GEMM stored y).
+__device__ __forceinline__ void splitk_reduce_rows(const GemmArgs& g, float* y, int64_t ldy,
+                                                   int64_t blk, int64_t nblk) {
+  const int M = device_rows(g.m_dev, g.m_cap);
+  if (M <= 0) return;
+  const int mt = (M + 127) / 128;
+  const int ntl = g.N / 128;
+  const int S = splitk_count(g, mt, ntl);
+  if (S <= 1) return;
+  const int Mpad = mt * 128;
+  const int n4 = g.N / 4;
+  const int64_t total = (int64_t)M * n4;
+  const int64_t pstride = (int64_t)Mpad * g.N;
+  for (int64_t e = blk * blockDim.x + threadIdx.x; e < total; e += nblk * blockDim.x) {
+    const int m = (int)(e / n4);
+    const int c = (int)(e - (int64_t)m * n4) * 4;
+    const float* p = g.part + (int64_t)m * g.N + c;
+    float* dst = y + (int64_t)(g.out_rows ? g.out_rows[m] : m) * ldy + c;
+    f32x4_t v[kSplitCap];
+#pragma unroll
+    for (int k = 0; k < kSplitCap; ++k)
+      if (k < S) v[k] = *(const f32x4_t*)(p + k * pstride);
+    f32x4_t acc = v[0];
+#pragma unroll
+    for (int k = 1; k < kSplitCap; ++k)
+      if (k < S) acc += v[k];
+    if (g.accumulate) acc += *(const f32x4_t*)dst;
+    *(f32x4_t*)dst = acc;
+  }
+}
+
 // rows[m] for m < min(*n, cap): out[m, :] = ReLU(z[rows[m], :]) (stored
 // values, F wide)
 hipError_t launch_gather_relu_rows(const float* z, int F, int sb, const int32_t* rows, const int32_t* n,
@@ -371,6 +416,10 @@ hipError_t launch_updown(Dtype dt, bool gated, int phase, const SliceArgs& a, hi
 // beside it in the same launch (l1 nullable)
 hipError_t launch_up_with_lists(Dtype dt, const SliceArgs& a, const ListArgs& l0,
                                 const ListArgs* l1, int64_t T, hipStream_t s);
+// bf16 layers: phase 1 with the split-K reduce of the dense path's down
+// product (launch_splitk_reduce(g, a.y, a.d)) in the same launch
+hipError_t launch_down_with_reduce(Dtype dt, bool gated, const SliceArgs& a, const GemmArgs& g,
+                                   hipStream_t s);
 // bf16 layers, d in {512, 1024, 2048, 4096}: the up and down projections of
 // the ELL rows in one kernel without d slices (rows with bk set skipped)
 hipError_t launch_fused_updown(bool gated, const SliceArgs& a, hipStream_t s);

@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256) void hsum_kernel(SliceArgs a) {
 // time, and reads them back as broadcasts; records past a row's count are
 // zero (neuron 0, no weight).
 template <typename E, int SW, bool GATED, int G>
-__global__ __launch_bounds__(256) void down_kernel(SliceArgs a) {
+__device__ __forceinline__ void down_rows(const SliceArgs& a, int64_t blk) {
   constexpr int EPL = 16 / (int)sizeof(E);
   constexpr int LPR = SW / EPL;
   constexpr int RPW = 64 / LPR;
@@ -307,12 +307,12 @@ __global__ __launch_bounds__(256) void down_kernel(SliceArgs a) {
   int slice;
   int64_t grp;
   if (nsl % 8 == 0) {
-    const int64_t q = blockIdx.x / 8;
-    slice = (int)(q / nbk) * 8 + blockIdx.x % 8;
+    const int64_t q = blk / 8;
+    slice = (int)(q / nbk) * 8 + (int)(blk % 8);
     grp = q % nbk;
   } else {
-    slice = blockIdx.x % nsl;
-    grp = blockIdx.x / nsl;
+    slice = (int)(blk % nsl);
+    grp = blk / nsl;
   }
   const int64_t tw = (grp * 4 + wave) * RPW;
   if (tw >= a.T) return;
@@ -367,6 +367,24 @@ __global__ __launch_bounds__(256) void down_kernel(SliceArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; e += 4) *(f32x4_t*)(yo + e) = f32x4_t{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
   }
+}
+
+template <typename E, int SW, bool GATED, int G>
+__global__ __launch_bounds__(256) void down_kernel(SliceArgs a) {
+  down_rows<E, SW, GATED, G>(a, blockIdx.x);
+}
+
+// The same with the split-K reduce of the dense path's down product into
+// its rows of y (rows the down projection skips) in the first nred
+// workgroups; nred is a multiple of 8, so that workgroup b of the down
+// projection still runs on XCD b mod 8.
+template <typename E, int SW, bool GATED, int G>
+__global__ __launch_bounds__(256) void down_reduce_kernel(SliceArgs a, GemmArgs g, int nred) {
+  if ((int)blockIdx.x < nred) {
+    splitk_reduce_rows(g, a.y, a.d, blockIdx.x, nred);
+    return;
+  }
+  down_rows<E, SW, GATED, G>(a, (int64_t)blockIdx.x - nred);
 }
 
 // The up and down projections in one kernel, without the d slices: one
@@ -552,6 +570,21 @@ hipError_t launch_up_with_lists(Dtype dt, const SliceArgs& a, const ListArgs& l0
   if (ns == 8 && sw == 256) return launch_up_lists_t<uint16_t, 8, 256>(a, l0, l1, T, s);
   if (ns == 8 && sw == 512) return launch_up_lists_t<uint16_t, 8, 512>(a, l0, l1, T, s);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_down_with_reduce(Dtype dt, bool gated, const SliceArgs& a, const GemmArgs& g,
+                                   hipStream_t s) {
+  if (dt != kBF16) return hipErrorInvalidValue;
+  constexpr int DSW = 256;
+  constexpr int DRPW = 64 / (DSW * 2 / 16);
+  if (a.d % DSW != 0) return hipErrorInvalidValue;
+  const int nred = 256;
+  const dim3 grid((unsigned)(nred + (a.d / DSW) * ((a.T + 4 * DRPW - 1) / (4 * DRPW))));
+  if (gated)
+    hipLaunchKernelGGL((down_reduce_kernel<uint16_t, DSW, true, 4>), grid, dim3(256), 0, s, a, g, nred);
+  else
+    hipLaunchKernelGGL((down_reduce_kernel<uint16_t, DSW, false, 4>), grid, dim3(256), 0, s, a, g, nred);
+  return hipGetLastError();
 }
 
 hipError_t launch_backup_list(const ListArgs& l0, const ListArgs* l1, int64_t T, hipStream_t s) {
