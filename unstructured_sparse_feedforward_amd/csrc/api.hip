@@ -1193,23 +1193,6 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
   const int cap = (int)std::min<int64_t>(hy->max_backup, dense_cap(h, T));
   hipError_t e;
 
-  // 1. dh = dy . W_d[j] per ELL slot, as per-slice partial dot products
-  SliceArgs sa = {};
-  sa.x = dy;
-  sa.wu = w_down;
-  sa.ell_idx = hy->ell_idx;
-  sa.ell_cnt = hy->ell_cnt;
-  sa.T = T;
-  sa.d = D.d;
-  sa.K = K;
-  sa.Kp = Kp;
-  sa.upart = at<float>(ws, L.upart);
-  {
-    ProfScope ps(h, SFFN_K_BWD_SDDMM, stream);
-    e = launch_updown(dt, true, 0, sa, stream);
-  }
-  if (e != hipSuccess) return hip_fail(h, e, "backward dh");
-
   BwdArgs ba = {};
   ba.x = x;
   ba.dy = dy;
@@ -1259,6 +1242,30 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
   ba.gh_t = at<char>(ws, L.gh_t);
   ba.ldt = L.ldt;
 
+  // bf16 with backup rows: their x and dy rows are gathered (transposed)
+  // by extra workgroups of the dh launch, and the split-K reduce of their dx
+  // product runs in the launch of the ELL rows' dx sums
+  const bool joint = dt == kBF16 && cap > 0;
+
+  // 1. dh = dy . W_d[j] per ELL slot, as per-slice partial dot products
+  SliceArgs sa = {};
+  sa.x = dy;
+  sa.wu = w_down;
+  sa.ell_idx = hy->ell_idx;
+  sa.ell_cnt = hy->ell_cnt;
+  sa.T = T;
+  sa.d = D.d;
+  sa.K = K;
+  sa.Kp = Kp;
+  sa.upart = at<float>(ws, L.upart);
+  {
+    ProfScope ps(h, SFFN_K_BWD_SDDMM, stream);
+    e = joint ? launch_up_with_gather(dt, sa, gather_args(ba), stream)
+              : launch_updown(dt, true, 0, sa, stream);
+  }
+  if (e != hipSuccess) return hip_fail(h, e, "backward dh");
+
+
   // 2. dZ, dU per slot and dx of the ELL rows
   {
     ProfScope ps(h, SFFN_K_BWD_DX, stream);
@@ -1281,11 +1288,12 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
     return hipStreamSynchronize(h->side);
   };
   bool transposed = false;
+  GemmArgs dx_late = {};   // joint: the backup rows' dx reduce, on the second stream
   if (cap > 0) {
     ProfScope ps(h, SFFN_K_BWD_DENSE, stream);
     const bool split = dt == kBF16;
     float* part = at<float>(ws, L.part);
-    e = launch_backup_prep(dt, gated, ba, stream);
+    if (!joint) e = launch_backup_prep(dt, gated, ba, stream);
     if (e != hipSuccess) return hip_fail(h, e, "backup rows gather");
     GemmArgs g = {};
     g.A = dy;
@@ -1355,8 +1363,9 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
         f.grid = gemm_grid(dt, 1, h->num_cu);
         e = launch_gemm(dt, 1, true, kEpiStoreF32, f, stream);
       }
-      if (e == hipSuccess) e = launch_splitk_reduce(f, dx, D.d, stream);
+      if (e == hipSuccess && !joint) e = launch_splitk_reduce(f, dx, D.d, stream);
       if (e != hipSuccess) return hip_fail(h, e, "backup dx");
+      if (joint) dx_late = f;
     }
     // the neuron-major grouping (needs only the slot records) on the second
     // stream, beside the dW products
@@ -1372,7 +1381,8 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
     forked = true;
     {
       ProfScope ps(h, SFFN_K_BWD_DX, h->side);
-      e = launch_bwd_sparse(dt, gated, 3, ba, h->side);
+      e = dx_late.out != nullptr ? launch_dx_with_reduce(dt, gated, ba, dx_late, h->side)
+                                 : launch_bwd_sparse(dt, gated, 3, ba, h->side);
     }
     if (e == hipSuccess) {
       ProfScope ps(h, SFFN_K_BWD_TRANSPOSE, h->side);

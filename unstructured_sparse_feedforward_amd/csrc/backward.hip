@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void dzu_kernel(BwdArgs a) {
 // {neuron, dZ, dU} in LDS, 64 per row at a time, and reads them back as
 // broadcasts; records past a row's count are zero (neuron 0, no weight).
 template <typename E, int SW, bool GATED, int GRP>
-__global__ __launch_bounds__(256) void dx_sparse_kernel(BwdArgs a) {
+__device__ __forceinline__ void dx_sparse_rows(const BwdArgs& a, int64_t blk) {
   constexpr int EPL = 16 / (int)sizeof(E);
   constexpr int LPR = SW / EPL;
   constexpr int RPW = 64 / LPR;
@@ -79,12 +79,12 @@ __global__ __launch_bounds__(256) void dx_sparse_kernel(BwdArgs a) {
   int slice;
   int64_t grp;
   if (nsl % 8 == 0) {
-    const int64_t q = blockIdx.x / 8;
-    slice = (int)(q / nbk) * 8 + blockIdx.x % 8;
+    const int64_t q = blk / 8;
+    slice = (int)(q / nbk) * 8 + (int)(blk % 8);
     grp = q % nbk;
   } else {
-    slice = blockIdx.x % nsl;
-    grp = blockIdx.x / nsl;
+    slice = (int)(blk % nsl);
+    grp = blk / nsl;
   }
   const int64_t tw = (grp * 4 + wave) * RPW;
   if (tw >= a.T) return;
@@ -143,6 +143,23 @@ __global__ __launch_bounds__(256) void dx_sparse_kernel(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < EPL; e += 4) *(f32x4_t*)(o + e) = f32x4_t{acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
   }
+}
+
+template <typename E, int SW, bool GATED, int GRP>
+__global__ __launch_bounds__(256) void dx_sparse_kernel(BwdArgs a) {
+  dx_sparse_rows<E, SW, GATED, GRP>(a, blockIdx.x);
+}
+
+// The same with the split-K reduce of the backup rows' dx product into their
+// rows of dx (rows the ELL sums skip) in the first nred workgroups; nred is
+// a multiple of 8, so that workgroup b of the sums still runs on XCD b mod 8.
+template <typename E, int SW, bool GATED, int GRP>
+__global__ __launch_bounds__(256) void dx_sparse_reduce_kernel(BwdArgs a, GemmArgs g, int nred) {
+  if ((int)blockIdx.x < nred) {
+    splitk_reduce_rows(g, a.dx, a.d, blockIdx.x, nred);
+    return;
+  }
+  dx_sparse_rows<E, SW, GATED, GRP>(a, (int64_t)blockIdx.x - nred);
 }
 
 constexpr int kDwGrp = 4;   // slots in flight per wave in the dW sums
@@ -486,51 +503,8 @@ __global__ __launch_bounds__(256) void gather_stack_kernel(const E* __restrict__
 // both operands of the dW GEMMs are k-contiguous. A workgroup moves 64 rows
 // x 64 columns through LDS: 16-byte loads along the rows, 16-byte stores
 // along the columns.
-__global__ __launch_bounds__(256) void gather_stack_t_kernel(const uint16_t* __restrict__ src0,
-                                                             const uint16_t* __restrict__ src1,
-                                                             int d, const int32_t* __restrict__ brow,
-                                                             const int32_t* __restrict__ n, int cap,
-                                                             uint16_t* __restrict__ dst0,
-                                                             uint16_t* __restrict__ dst1,
-                                                             int64_t ldt) {
-  __shared__ __align__(16) uint16_t tile[64][72];   // [column][row]
-  // blockIdx.y: x (0) or dy (1)
-  const uint16_t* src = blockIdx.y ? src1 : src0;
-  uint16_t* dst = blockIdx.y ? dst1 : dst0;
-  const int R = device_rows(n, cap);
-  const int Rp = (R + 63) / 64 * 64;
-  const int tid = threadIdx.x;
-  const int nct = d / 64;
-  const int ntiles = (Rp / 64) * nct;
-  for (int t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int r0 = (t / nct) * 64;
-    const int c0 = (t - (t / nct) * nct) * 64;
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int e = p * 256 + tid;     // 64 rows x 8 chunks of 8 columns
-      const int rl = e >> 3;
-      const int ch = e & 7;
-      u32x4_t v = {0, 0, 0, 0};
-      if (r0 + rl < R) v = *(const u32x4_t*)(src + (int64_t)brow[r0 + rl] * d + c0 + ch * 8);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        tile[ch * 8 + 2 * q][rl] = (uint16_t)(v[q] & 0xFFFFu);
-        tile[ch * 8 + 2 * q + 1][rl] = (uint16_t)(v[q] >> 16);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int e = p * 256 + tid;     // 64 columns x 8 chunks of 8 rows
-      const int cl = e >> 3;
-      const int ch = e & 7;
-      const u32x4_t v = *(const u32x4_t*)&tile[cl][ch * 8];
-      uint16_t* o = dst + (int64_t)(c0 + cl) * ldt + r0 + ch * 8;
-      *(u32x4_t*)o = v;
-      *(u32x4_t*)(o + Rp) = v;
-    }
-    __syncthreads();
-  }
+__global__ __launch_bounds__(256) void gather_stack_t_kernel(GatherT a) {
+  gather_stack_t_tiles(a, blockIdx.x, gridDim.x, blockIdx.y);
 }
 
 // From dH of the backup rows: dZ, dU (and H = a u for dW_d) in the layouts
@@ -728,12 +702,30 @@ hipError_t launch_transpose(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+GatherT gather_args(const BwdArgs& a) {
+  return GatherT{(const uint16_t*)a.x, (const uint16_t*)a.dy, a.d, a.brow, a.n_backup, a.cap,
+                 (uint16_t*)a.xb, (uint16_t*)a.dyb, a.ldt};
+}
+
+hipError_t launch_dx_with_reduce(Dtype dt, bool gated, const BwdArgs& a, const GemmArgs& g,
+                                 hipStream_t s) {
+  if (dt != kBF16) return hipErrorInvalidValue;
+  constexpr int XSW = 128;
+  constexpr int XRPW = 64 / (XSW * 2 / 16);
+  if (a.d % XSW != 0) return hipErrorInvalidValue;
+  const int nred = 256;
+  const dim3 grid((unsigned)(nred + (a.d / XSW) * ((a.T + 4 * XRPW - 1) / (4 * XRPW))));
+  if (gated)
+    hipLaunchKernelGGL((dx_sparse_reduce_kernel<uint16_t, XSW, true, 4>), grid, dim3(256), 0, s, a, g, nred);
+  else
+    hipLaunchKernelGGL((dx_sparse_reduce_kernel<uint16_t, XSW, false, 4>), grid, dim3(256), 0, s, a, g, nred);
+  return hipGetLastError();
+}
+
 hipError_t launch_backup_prep(Dtype dt, bool gated, const BwdArgs& a, hipStream_t s) {
   const dim3 g(1024), b(256);
   if (dt == kBF16) {
-    hipLaunchKernelGGL(gather_stack_t_kernel, dim3(512, 2), b, 0, s, (const uint16_t*)a.x,
-                       (const uint16_t*)a.dy, a.d, a.brow, a.n_backup, a.cap, (uint16_t*)a.xb,
-                       (uint16_t*)a.dyb, a.ldt);
+    hipLaunchKernelGGL(gather_stack_t_kernel, dim3(kGatherBlocks, 2), b, 0, s, gather_args(a));
   } else {
     hipLaunchKernelGGL(gather_stack_kernel<float>, g, b, 0, s, (const float*)a.x, a.d, a.brow,
                        a.n_backup, a.cap, (float*)a.xb);

@@ -416,6 +416,74 @@ hipError_t launch_updown(Dtype dt, bool gated, int phase, const SliceArgs& a, hi
 // beside it in the same launch (l1 nullable)
 hipError_t launch_up_with_lists(Dtype dt, const SliceArgs& a, const ListArgs& l0,
                                 const ListArgs* l1, int64_t T, hipStream_t s);
+// The backup rows of x and dy (bf16), transposed for the backward's dW
+// GEMMs: column c of dst0 (dst1) holds src0[brow[r]][c] (src1) at k = r and
+// k = Rp + r for r < R = min(*n, cap), Rp = R rounded up to 64, zeros up
+// to 2 Rp (both operands of those GEMMs k-contiguous, the bf16 hi and lo
+// parts of the other operand meeting the same rows).
+struct GatherT {
+  const uint16_t* src0;
+  const uint16_t* src1;
+  int d;
+  const int32_t* brow;
+  const int32_t* n;
+  int cap;
+  uint16_t* dst0;
+  uint16_t* dst1;
+  int64_t ldt;
+};
+constexpr int kGatherBlocks = 512;   // workgroups per operand
+
+// Workgroup bx of nbx of operand by: 64 rows x 64 columns at a time through
+// LDS, 16-byte loads along the rows, 16-byte stores along the columns.
+__device__ __forceinline__ void gather_stack_t_tiles(const GatherT& a, int bx, int nbx, int by) {
+  const int d = a.d;
+  const int64_t ldt = a.ldt;
+  const int32_t* __restrict__ brow = a.brow;
+  __shared__ __align__(16) uint16_t tile[64][72];   // [column][row]
+  // by: x (0) or dy (1)
+  const uint16_t* src = by ? a.src1 : a.src0;
+  uint16_t* dst = by ? a.dst1 : a.dst0;
+  const int R = device_rows(a.n, a.cap);
+  const int Rp = (R + 63) / 64 * 64;
+  const int tid = threadIdx.x;
+  const int nct = d / 64;
+  const int ntiles = (Rp / 64) * nct;
+  for (int t = bx; t < ntiles; t += nbx) {
+    const int r0 = (t / nct) * 64;
+    const int c0 = (t - (t / nct) * nct) * 64;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int e = p * 256 + tid;     // 64 rows x 8 chunks of 8 columns
+      const int rl = e >> 3;
+      const int ch = e & 7;
+      u32x4_t v = {0, 0, 0, 0};
+      if (r0 + rl < R) v = *(const u32x4_t*)(src + (int64_t)brow[r0 + rl] * d + c0 + ch * 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        tile[ch * 8 + 2 * q][rl] = (uint16_t)(v[q] & 0xFFFFu);
+        tile[ch * 8 + 2 * q + 1][rl] = (uint16_t)(v[q] >> 16);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int e = p * 256 + tid;     // 64 columns x 8 chunks of 8 rows
+      const int cl = e >> 3;
+      const int ch = e & 7;
+      const u32x4_t v = *(const u32x4_t*)&tile[cl][ch * 8];
+      uint16_t* o = dst + (int64_t)(c0 + cl) * ldt + r0 + ch * 8;
+      *(u32x4_t*)o = v;
+      *(u32x4_t*)(o + Rp) = v;
+    }
+    __syncthreads();
+  }
+}
+
+// bf16 layers: phase 0 (the backward's dh, with x := dy and W_u := W_d)
+// with the backup rows' gather of gather_stack_t_tiles in the same launch
+hipError_t launch_up_with_gather(Dtype dt, const SliceArgs& a, const GatherT& gt, hipStream_t s);
+
 // bf16 layers: phase 1 with the split-K reduce of the dense path's down
 // product (launch_splitk_reduce(g, a.y, a.d)) in the same launch
 hipError_t launch_down_with_reduce(Dtype dt, bool gated, const SliceArgs& a, const GemmArgs& g,
@@ -479,5 +547,11 @@ hipError_t launch_transpose(const BwdArgs& a, hipStream_t s);
 int64_t transpose_blocks(int64_t T, int K);
 hipError_t launch_backup_prep(Dtype dt, bool gated, const BwdArgs& a, hipStream_t s);
 hipError_t launch_backup_grad(Dtype dt, bool gated, const BwdArgs& a, hipStream_t s);
+// the gather of launch_backup_prep (bf16) as launch_up_with_gather takes it
+GatherT gather_args(const BwdArgs& a);
+// bf16: which = 3 of launch_bwd_sparse with the split-K reduce of the backup
+// rows' dx product (launch_splitk_reduce(g, a.dx, a.d)) in the same launch
+hipError_t launch_dx_with_reduce(Dtype dt, bool gated, const BwdArgs& a, const GemmArgs& g,
+                                 hipStream_t s);
 
 }  // namespace sffn

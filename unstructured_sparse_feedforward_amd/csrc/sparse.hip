@@ -273,6 +273,18 @@ __global__ __launch_bounds__(256) void up_partial_list_kernel(SliceArgs a, ListA
   up_partial<E, NS, SW>(a, (int64_t)blockIdx.x - 8);
 }
 
+// The backward's dh (phase 0 on dy and W_d) with the backup rows' x and dy
+// gathered beside it: workgroups [0, 2 kGatherBlocks) gather (a multiple of
+// 8, so that workgroup b of the products still runs on XCD b mod 8).
+template <typename E, int NS, int SW>
+__global__ __launch_bounds__(256) void up_partial_gather_kernel(SliceArgs a, GatherT gt) {
+  if (blockIdx.x < 2 * kGatherBlocks) {
+    gather_stack_t_tiles(gt, blockIdx.x % kGatherBlocks, kGatherBlocks, blockIdx.x / kGatherBlocks);
+    return;
+  }
+  up_partial<E, NS, SW>(a, (int64_t)blockIdx.x - 2 * kGatherBlocks);
+}
+
 // Between the phases (gated): the slice sums (hsum_rows, in the header,
 // shared with the dense path's combine launch)
 template <int NS>
@@ -557,6 +569,26 @@ hipError_t launch_up_lists_t(const SliceArgs& a, const ListArgs& l0, const ListA
                      dim3((unsigned)(8 + NS * ((a.T + 3) / 4))), dim3(256), 0, st, a, l0,
                      l1 ? *l1 : none, l1 ? 2 : 1, T);
   return hipGetLastError();
+}
+
+template <typename E, int NS, int SW>
+hipError_t launch_up_gather_t(const SliceArgs& a, const GatherT& gt, hipStream_t st) {
+  hipLaunchKernelGGL((up_partial_gather_kernel<E, NS, SW>),
+                     dim3((unsigned)(2 * kGatherBlocks + NS * ((a.T + 3) / 4))), dim3(256), 0, st,
+                     a, gt);
+  return hipGetLastError();
+}
+
+hipError_t launch_up_with_gather(Dtype dt, const SliceArgs& a, const GatherT& gt, hipStream_t s) {
+  int ns, epl;
+  slice_shape(dt, a.d, &ns, &epl);
+  const int sw = a.d / ns;
+  if (dt != kBF16) return hipErrorInvalidValue;
+  if (ns == 2 && sw == 256) return launch_up_gather_t<uint16_t, 2, 256>(a, gt, s);
+  if (ns == 4 && sw == 256) return launch_up_gather_t<uint16_t, 4, 256>(a, gt, s);
+  if (ns == 8 && sw == 256) return launch_up_gather_t<uint16_t, 8, 256>(a, gt, s);
+  if (ns == 8 && sw == 512) return launch_up_gather_t<uint16_t, 8, 512>(a, gt, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_up_with_lists(Dtype dt, const SliceArgs& a, const ListArgs& l0,
