@@ -324,6 +324,9 @@ def main():
     ap.add_argument("--updown", default="sliced", choices=("sliced", "fused"),
                     help="inference up/down: three XCD-sliced launches (default) or the one "
                          "fused kernel without slices")
+    ap.add_argument("--graph", action=argparse.BooleanOptionalAction, default=True,
+                    help="also time the sparse step captured once as a HIP graph and "
+                         "replayed (forward workloads)")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="cold-cache steps of each mode (a 2 GiB read before each; 0 = skip)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -436,6 +439,33 @@ def bench_forward(args, np, torch, SparseFFN, wl):
                 "dense_value": T_of(layers) / pct(de_cold)["median"],
                 "speedup_sparse_over_dense": pct(de_cold)["median"] / pct(sp_cold)["median"]}
 
+    # the same sparse step captured once as a HIP graph (torch.cuda.CUDAGraph
+    # over the library's launches on the capturing stream) and replayed:
+    # the same kernels without the host's per-launch overhead; every
+    # replayed y is compared bit for bit with the eager step's
+    graph = None
+    if args.graph:
+        ref = [L["y"].clone() for L in layers]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            sparse()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            sparse()
+        g_steps = []
+        ms_g, _, _ = _timed(g.replay, args.steps, args.warmup, torch, per_step=g_steps)
+        torch.cuda.synchronize()
+        same = all(torch.equal(L["y"].view(torch.int32), r.view(torch.int32))
+                   for L, r in zip(layers, ref))
+        del g
+        graph = {"ms_per_step": ms_g, "value": T_of(layers) / ms_g, "step_ms": pct(g_steps),
+                 "same_y_as_eager": bool(same),
+                 "method": "torch.cuda.CUDAGraph capture of one sparse step, replayed; "
+                           "events around the timed replays"}
+
     gbytes, pairs, n_flag = 0.0, 0, 0
     for L in layers:
         b, p, nf = gather_work(L["W"], L["tw"]["cnt"].cpu().numpy(),
@@ -543,6 +573,7 @@ def bench_forward(args, np, torch, SparseFFN, wl):
                            "frac_of_mfma_peak": dense_flops / (ms_d * 1e-3) / 1e12 / peak_mm,
                            "kernels_ms_per_step": per_step(prof_d, args.steps)},
         "cold": cold,
+        "graph": graph,
         "device_rates": rates,
         "torch_dense_layer": torch_ffn,
         "kernels_ms_per_step": per_step(prof, args.steps),
