@@ -1010,8 +1010,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring64_kernel(GemmArgs g) {
 
 // K from which float32-output GEMMs take the 64-k ring (measured on the
 // dense down projection, K = 5632: 155 us with 64-k stages against 180 us
-// for the n-contiguous kernel and 205 us for the 32-k ring)
-constexpr int kRing64MinK = 4096;
+// for the n-contiguous kernel and 205 us for the 32-k ring; on the gate
+// pre-activations, 8192 x 5632 x 2048: 190 against 223 us)
+constexpr int kRing64MinK = 2048;
 
 // 3, 4 and 5 slots time the same on the gate GEMM (the clock, not the
 // load latency, sets the pace once the copies are spread over the MFMAs).
@@ -1065,8 +1066,8 @@ hipError_t launch_gemm_big(int nb, bool bt, Epi epi, const GemmArgs& g, hipStrea
     return hipGetLastError();
   }
   if (epi == kEpiTwell) return launch_ring_twell(g, s);
-  // long K: 64-k stages (half the barriers and copy waits per MFMA) win;
-  // at K = 2048 the 32-k ring is as fast or faster
+  // 64-k stages (half the barriers and copy waits per MFMA, whole 128-byte
+  // rows per copy) win from K = 2048 on
   if (epi == kEpiStoreF32)
     return (!g.k_dev && g.K >= kRing64MinK && g.K % BK == 0)
                ? launch_ring64<1, kEpiStoreF32>(g, s)
