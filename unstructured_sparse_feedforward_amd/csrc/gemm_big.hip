@@ -139,17 +139,34 @@ __device__ __forceinline__ void mfma_substep(f32x16_t (&acc)[NB][4][Cfg<NB>::JB]
 // ---------------------------------------------------------------- epilogues
 
 // ReLU + TwELL of a wave's 128 x 128 accumulator block (one TwELL tile of
-// 128 rows), staged through LDS 32 rows at a time: the wave writes a
-// block's 64 accumulator registers into its 16 KB staging tile, then lane
-// l takes row l % 32 and its half l / 32 of the 128 columns, builds the
-// mask of its 64 positives, exchanges counts with the other half's lane
-// and stores its share of the row's first C entries in ascending column
-// order. The staging tile holds row r's float c at
-// r * 128 + 4 * (((c / 4) ^ r) % 32) + c % 4 (16-byte chunks XOR-swizzled
-// by row: a lane's 16-byte reads of one chunk index across 16 rows hit 16
-// distinct bank groups).
+// 128 rows), 32 rows at a time. Lane l takes row l % 32 and its half l / 32
+// of the 128 columns:
+//  - the positives' masks come from wave ballots of the accumulator
+//    registers: one ballot of register q of column block j holds two rows'
+//    32 columns, and two lane writes move them to the lanes that own those
+//    row halves;
+//  - the block's 64 accumulator registers also go to the wave's 16 KB
+//    staging tile (row-major), from where each lane reads the values of its
+//    row's first C positives, four at a time;
+//  - a popcount and one exchange between the lane halves give the row's
+//    count and the second half's first slot.
+// The staging tile holds row r's float c at r * 128 + 4 * (((c / 4) ^ r) %
+// 32) + c % 4 (16-byte chunks XOR-swizzled by row, so that 16-byte reads of
+// one chunk index across 16 rows hit 16 distinct bank groups).
 __device__ __forceinline__ int stage_off(int r, int c) {
   return r * 128 + ((((c >> 2) ^ r) & 31) << 2) + (c & 3);
+}
+
+// v_writelane_b32: lane `lane` of the result is `val`, the others are `old`
+extern "C" __device__ uint32_t sffn_writelane(uint32_t val, uint32_t lane, uint32_t old)
+    __asm("llvm.amdgcn.writelane.i32");
+
+// x of this lane plus x of the lane 32 away (v_permlane32_swap trades the
+// upper half of one copy with the lower half of the other; the sum of the
+// two results is the pair's sum whichever way the halves go)
+__device__ __forceinline__ int pair_sum(int x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (int)p[0] + (int)p[1];
 }
 
 template <bool SB>
@@ -169,48 +186,50 @@ __device__ __forceinline__ void twell_block_lds(const GemmArgs& g, f32x16_t (&bl
   int lb[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) lb[k] = 512 * h + ((((c32 >> 2) ^ (4 * h) ^ k)) << 2) + (c32 & 3);
+  // w0, w1: this lane's row mask over columns 64 (lane / 32) + 0..31 and
+  // + 32..63. The ballot of register q of block j has row ra's columns
+  // 32 j + 0..31 in its low word and row ra + 4's in its high word; both go
+  // to word j % 2 of the lanes (row) + 32 (j / 2).
+  uint32_t w0 = 0, w1 = 0;
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
+    const int ra = 8 * (q >> 2) + (q & 3);
+    float v[4];
+    uint64_t m[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      stage[lb[q & 3] + ((q >> 2) * 8 + (q & 3)) * 128 + (((j ^ (q >> 2)) & 3) << 5)] =
-          agpr(blk[j][q]);
+    for (int j = 0; j < 4; ++j) {
+      v[j] = agpr(blk[j][q]);
+      stage[lb[q & 3] + ((q >> 2) * 8 + (q & 3)) * 128 + (((j ^ (q >> 2)) & 3) << 5)] = v[j];
+    }
+    // four ballots before their lane writes, so that no write waits on
+    // the compare just before it
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m[j] = __builtin_amdgcn_ballot_w64(v[j] > 0.0f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t ln = ra + 32 * (j >> 1);
+      if (j & 1) {
+        w1 = sffn_writelane((uint32_t)m[j], ln, w1);
+        w1 = sffn_writelane((uint32_t)(m[j] >> 32), ln + 4, w1);
+      } else {
+        w0 = sffn_writelane((uint32_t)m[j], ln, w0);
+        w0 = sffn_writelane((uint32_t)(m[j] >> 32), ln + 4, w0);
+      }
+    }
     // a few register indices at a time (bounded register pressure)
-    if ((q & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    if ((q & 1) == 1) __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-  __builtin_amdgcn_sched_barrier(0);
   const int rr = lane & 31;        // this lane's row of the block
   const int hh = lane >> 5;        // and its half of the 128 columns
   const bool row_ok = rbase + rr < M;
-  // the mask of this half's positives, bit k = column 64 hh + k: its 16
-  // chunks of 4 columns from the last down, 4 reads in flight, each
-  // chunk's bits shifted in at the bottom
-  uint32_t mlo = 0, mhi = 0;
-  {
-    const float* rowp = stage + rr * 128;
-    const int hb = ((16 * hh) ^ rr) & 16;
-    const int x = rr & 15;
-#pragma unroll 1
-    for (int c4 = 3; c4 >= 0; --c4) {
-      f32x4_t v[4];
-#pragma unroll
-      for (int k = 3; k >= 0; --k) v[k] = *(const f32x4_t*)(rowp + ((hb | ((4 * c4 + k) ^ x)) << 2));
-#pragma unroll
-      for (int k = 3; k >= 0; --k) {
-        const uint32_t nib = (uint32_t)(v[k][0] > 0.0f) | ((uint32_t)(v[k][1] > 0.0f) << 1) |
-                             ((uint32_t)(v[k][2] > 0.0f) << 2) | ((uint32_t)(v[k][3] > 0.0f) << 3);
-        mhi = (mhi << 4) | (mlo >> 28);
-        mlo = (mlo << 4) | nib;
-      }
-    }
-  }
-  uint64_t mask = row_ok ? ((uint64_t)mhi << 32) | mlo : 0;
+  const uint64_t mask = row_ok ? ((uint64_t)w1 << 32) | w0 : 0;
   const int n_own = __popcll(mask);
-  const int n_other = __shfl_xor(n_own, 32, 64);
-  const int total = n_own + n_other;
+  const int total = pair_sum(n_own);
+  const int n_other = total - n_own;
   const int C = g.C;
   const int64_t row = (int64_t)rbase + rr;
+  // the staging tile is complete before any lane reads another's values
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
   if (hh == 0 && row_ok) g.tw_cnt[row * g.n_t + tb] = total;
   // a tile row past C keeps all its pre-activations in a record of its
   // own (the tile column's counter hands out the column's next record; its
@@ -219,7 +238,7 @@ __device__ __forceinline__ void twell_block_lds(const GemmArgs& g, f32x16_t (&bl
     const bool ovf = row_ok && total > C;
     int rec = 0;
     if (ovf && hh == 0) rec = atomicAdd(g.ovf_ctr + tb * kCtrStride, 1);
-    rec = __shfl_xor(rec, 32, 64) + rec;   // one of the two lanes holds it
+    rec = pair_sum(rec);   // one of the two lanes holds it
     if (ovf) {
       const int id = rec < g.ovf_cap ? tb * g.ovf_cap + rec : -1;
       if (id >= 0) {
@@ -234,19 +253,32 @@ __device__ __forceinline__ void twell_block_lds(const GemmArgs& g, f32x16_t (&bl
     }
   }
   // this half's positives in ascending column order, ranks from the first
-  // half's count for the second half
+  // half's count for the second half; four values read from the staging
+  // tile per round, then stored
   int rank = hh ? n_other : 0;
+  int todo = min(n_own, C - rank);
   const int64_t e0 = (row * g.n_t + tb) * C;
   uint64_t m = mask;
-  while (m != 0 && rank < C) {
-    const int k = (int)__builtin_ctzll(m);
-    m &= m - 1;
-    const int col = 64 * hh + k;
-    const float v = stage[stage_off(rr, col)];
-    if constexpr (SB) ((uint16_t*)g.tw_val)[e0 + rank] = (uint16_t)f32_to_bf16(v);
-    else ((float*)g.tw_val)[e0 + rank] = v;
-    g.tw_idx[e0 + rank] = (uint16_t)(tb * kTile + col);
-    ++rank;
+  while (todo > 0) {
+    int col[4];
+    float val[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = m != 0 ? (int)__builtin_ctzll(m) : 0;
+      m &= m - 1;
+      col[u] = 64 * hh + k;
+      val[u] = stage[stage_off(rr, col[u])];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (u < todo) {
+        if constexpr (SB) ((uint16_t*)g.tw_val)[e0 + rank + u] = (uint16_t)f32_to_bf16(val[u]);
+        else ((float*)g.tw_val)[e0 + rank + u] = val[u];
+        g.tw_idx[e0 + rank + u] = (uint16_t)(tb * kTile + col[u]);
+      }
+    }
+    rank += 4;
+    todo -= 4;
   }
 }
 
