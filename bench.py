@@ -177,10 +177,33 @@ def oracle_forward_ms(inp, n, np, min_ms=0.0):
     return repeat_ms(lambda: oracle.sparse_ffn(x, wg, wu, wd, w.tile, w.twell_cap), min_ms)
 
 
+def _host():
+    """The host the oracle ran on: CPU model and the BLAS numpy calls."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [{"api": i.get("internal_api"), "threads": i.get("num_threads"),
+                 "arch": i.get("architecture")} for i in threadpool_info()
+                if i.get("user_api") == "blas"]
+    except Exception:
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "blas": blas}
+
+
 def cpu_record(tokens, ms, sample):
     return {"value": tokens / ms, "unit": "input tokens/ms", "cores": _threads(),
             "kind": "oracle",
-            "sample": f"{sample}; {ms / 1e3:.1f} s; host os.cpu_count()={os.cpu_count()}"}
+            "sample": f"{sample}; {ms / 1e3:.1f} s; host os.cpu_count()={os.cpu_count()}",
+            "host": _host()}
 
 
 def gather_work(W, cnt, flag, np, ssz=4):
