@@ -79,7 +79,12 @@ G2048 = wl.GATED_1P5B.replace(F=2048, nnz=12, name="g2048")
                                  # the full gated shape, and a narrower layer with fewer,
                                  # more and ragged 256-row tiles than CUs
                                  (wl.GATED_1P5B, 8192), (G2048, 6144), (G2048, 6100),
-                                 (G2048, 14336)])
+                                 (G2048, 14336),
+                                 # capacities with many stored entries per lane (the
+                                 # epilogue stores them four at a time), and C = 1
+                                 (wl.NONGATED[911], 512),
+                                 (wl.GATED_1P5B.replace(twell_cap=128, name="c128"), 700),
+                                 (wl.GATED_1P5B.replace(twell_cap=1, nnz=400, name="c1"), 260)])
 def test_fused_twell_matches_pack_of_own_z(w, T):
     """The gate GEMM's TwELL epilogue equals the stand-alone pack of the
     same kernel's pre-activations, bit for bit (GPU against GPU)."""
