@@ -50,6 +50,19 @@ constexpr int kWaitAll = wait_imm(0, 0);
 // landed) are issued explicitly before it.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// 16 bytes per lane from base + voff + soff into LDS at lds (+ 16 x lane):
+// a buffer load into LDS over a raw resource on the operand (byte offsets
+// from it; the whole 32-bit range is in bounds, and every offset the
+// kernels form stays inside the operand, since rows are clamped to the last
+// valid one). Word 3 is the gfx9 raw-buffer format (32-bit data). The
+// resource is the same for every copy of an operand, so it is formed once.
+__device__ __forceinline__ void copy16_lds(const void* base, uint32_t voff, uint32_t soff,
+                                           char* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, -1, 0x00020000),
+      (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
 // Read one accumulator element out of its AGPR at the point of use, so the
 // epilogue streams through the 256 accumulators instead of copying them
 // all to VGPRs at once.
@@ -490,11 +503,17 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
   const int lr = lane >> 2;
   const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
 
-  // Per-lane copy sources of tile L: A rows m0 + 64 wave + 16 i + lane/4,
-  // B rows (columns of C) n0 + BN/4 wave + 16 i + lane/4.
+  // Per-lane copy sources of tile L, as 32-bit byte offsets from the
+  // operand bases: A rows m0 + 64 wave + 16 i + lane/4, B rows (columns of
+  // C) n0 + BN/4 wave + 16 i + lane/4. A stage's copies are buffer loads
+  // into LDS with these fixed offsets and the stage's k as the scalar
+  // offset, so no vector instruction rewrites an address register between
+  // two copies (a copy reads its address registers after issue: rewriting
+  // them at once, as global loads with 64-bit addresses needed, held up the
+  // wave, and with it the matrix cores, on every copy).
   struct Src {
-    const char* a[4];
-    const char* b[NB][BPW];
+    uint32_t a[4];
+    uint32_t b[NB][BPW];
   };
   auto tile_src = [&](int L, Src& t) {
     int m0, n0;
@@ -502,30 +521,27 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = min(m0 + wave * 64 + i * 16 + lr, M - 1);
-      t.a[i] = Ab + (int64_t)m * lda_b + lchunk * 16;
+      t.a[i] = (uint32_t)((int64_t)m * lda_b + lchunk * 16);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int i = 0; i < BPW; ++i) {
         const int n = min(n0 + wave * (BN / 4) + i * 16 + lr, g.N - 1);
-        t.b[nb][i] = Bb[nb] + (int64_t)n * ldb_b + lchunk * 16;
+        t.b[nb][i] = (uint32_t)((int64_t)n * ldb_b + lchunk * 16);
       }
   };
   auto issue_stage = [&](const Src& t, int kt, int slot) {
     char* base = smem + slot * SLOT;
-    const int64_t kb = (int64_t)kt * RBK * 2;
+    const uint32_t kb = (uint32_t)kt * RBK * 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(t.a[i] + kb),
-                                       (void*)(base + (wave * 64 + i * 16) * RROWB), 16, 0, 0);
+    for (int i = 0; i < 4; ++i) copy16_lds(Ab, t.a[i], kb, base + (wave * 64 + i * 16) * RROWB);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int i = 0; i < BPW; ++i)
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(t.b[nb][i] + kb),
-            (void*)(base + (BM + nb * BN + wave * (BN / 4) + i * 16) * RROWB), 16, 0, 0);
+        copy16_lds(Bb[nb], t.b[nb][i], kb,
+                   base + (BM + nb * BN + wave * (BN / 4) + i * 16) * RROWB);
   };
 
   f32x16_t acc[NB][4][JB];
@@ -889,9 +905,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring64_kernel(GemmArgs g) {
   // (L%8) ^ swz(row). Copy c of a 64-row (or 32-row) group starts at row
   // 8 c, where swz(row) = (4 c + L/16) & 7.
   const int lr = lane >> 3;
+  // (offsets from the operand bases, as in the 32-k ring)
   struct Src {
-    const char* a[APW];
-    const char* b[NB][BPW];
+    uint32_t a[APW];
+    uint32_t b[NB][BPW];
   };
   auto tile_src = [&](int L, Src& t) {
     int m0, n0;
@@ -900,7 +917,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring64_kernel(GemmArgs g) {
     for (int i = 0; i < APW; ++i) {
       const int m = min(m0 + wave * 64 + i * 8 + lr, M - 1);
       const int ch = (lane & 7) ^ ((4 * i + (lane >> 4)) & 7);
-      t.a[i] = Ab + (int64_t)m * lda_b + ch * 16;
+      t.a[i] = (uint32_t)((int64_t)m * lda_b + ch * 16);
     }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -908,23 +925,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring64_kernel(GemmArgs g) {
       for (int i = 0; i < BPW; ++i) {
         const int n = min(n0 + wave * (BN / 4) + i * 8 + lr, g.N - 1);
         const int ch = (lane & 7) ^ ((4 * i + (lane >> 4)) & 7);
-        t.b[nb][i] = Bb[nb] + (int64_t)n * ldb_b + ch * 16;
+        t.b[nb][i] = (uint32_t)((int64_t)n * ldb_b + ch * 16);
       }
   };
   auto issue_stage = [&](const Src& t, int kt, int slot) {
     char* base = smem + slot * SLOT;
-    const int64_t kb = (int64_t)kt * BK * 2;
+    const uint32_t kb = (uint32_t)kt * BK * 2;
 #pragma unroll
-    for (int i = 0; i < APW; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(t.a[i] + kb),
-                                       (void*)(base + (wave * 64 + i * 8) * ROWB), 16, 0, 0);
+    for (int i = 0; i < APW; ++i) copy16_lds(Ab, t.a[i], kb, base + (wave * 64 + i * 8) * ROWB);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int i = 0; i < BPW; ++i)
-        __builtin_amdgcn_global_load_lds(
-            (const void*)(t.b[nb][i] + kb),
-            (void*)(base + (BM + nb * BN + wave * (BN / 4) + i * 8) * ROWB), 16, 0, 0);
+        copy16_lds(Bb[nb], t.b[nb][i], kb,
+                   base + (BM + nb * BN + wave * (BN / 4) + i * 8) * ROWB);
   };
 
   f32x16_t acc[NB][4][JB];
@@ -1073,6 +1087,12 @@ hipError_t launch_ring64(const GemmArgs& g, hipStream_t s) {
 
 bool gemm_big_supported(Dtype dt, int nb, bool bt, Epi epi, const GemmArgs& g) {
   if (dt != kBF16 || g.m_dev || g.a_rows || g.out_rows || g.part || g.kwrap) return false;
+  // the ring kernel addresses its operands by 32-bit byte offsets
+  const int64_t kmax = g.k_dev ? (int64_t)g.k_mult * ((g.k_cap + 63) / 64 * 64) : g.K;
+  const int64_t lim = (int64_t)UINT32_MAX;
+  if ((int64_t)std::max(g.M, 1) * g.lda * 2 + kmax * 2 > lim ||
+      (int64_t)std::max(g.N, 1) * g.ldb * 2 + kmax * 2 > lim)
+    return false;
   if (g.accumulate && epi != kEpiStoreF32) return false;
   // a device-sized K: one B operand, float32 output
   if (g.k_dev) return nb == 1 && epi == kEpiStoreF32 && g.k_mult >= 1;
