@@ -118,21 +118,30 @@ __device__ __forceinline__ void interleave_reads() {
   __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 }
 
-// The same, then 8 global-to-LDS copies over the last 8 MFMAs (the copies
-// come after the reads in program order: the compiler cannot tell that
-// they write other LDS slots than the reads read).
-__device__ __forceinline__ void interleave_reads_copies() {
+// 8 fragment reads over the first 8 MFMAs, then 4 global-to-LDS copies on
+// every other one of the last 8: half a stage's copies per substep, so the
+// L2-to-LDS path (about a quarter of the MFMA rate in bytes per clock) drains
+// them as they come instead of stalling the wave's in-order issue, and with
+// it the matrix core, behind a burst. (The copies come after the reads in
+// program order: the compiler cannot tell that they write other LDS slots
+// than the reads read.)
+__device__ __forceinline__ void interleave_reads_half_copies() {
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
   }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < 4; ++k) {
     __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one global-to-LDS copy
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
   }
 }
+
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
 
 template <int NB>
 __device__ __forceinline__ void mfma_substep(f32x16_t (&acc)[NB][4][Cfg<NB>::JB],
@@ -531,11 +540,17 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
         t.b[nb][i] = (uint32_t)((int64_t)n * ldb_b + lchunk * 16);
       }
   };
-  auto issue_stage = [&](const Src& t, int kt, int slot) {
+  // A stage's copies go out in two halves of LPS / 2: its A rows, then its
+  // B rows.
+  auto issue_a = [&](const Src& t, int kt, int slot) {
     char* base = smem + slot * SLOT;
     const uint32_t kb = (uint32_t)kt * RBK * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) copy16_lds(Ab, t.a[i], kb, base + (wave * 64 + i * 16) * RROWB);
+  };
+  auto issue_b = [&](const Src& t, int kt, int slot) {
+    char* base = smem + slot * SLOT;
+    const uint32_t kb = (uint32_t)kt * RBK * 2;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -543,6 +558,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
         copy16_lds(Bb[nb], t.b[nb][i], kb,
                    base + (BM + nb * BN + wave * (BN / 4) + i * 16) * RROWB);
   };
+  static_assert(NB * BPW == 4, "halves of 4 copies");
 
   f32x16_t acc[NB][4][JB];
   auto zero_acc = [&]() {
@@ -572,28 +588,34 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
                                             rlds_off(wc * C_::WN + j * 32 + (lane & 31), ch));
   };
 
-  // One ring stage: substep 0 of stage kt (fragments already in registers),
-  // then, after the barrier, substep 1 while the fragments of the stage in
-  // slot `next` are read and stage `issue` of tile t is copied into the slot
-  // stage kt leaves.
+  // One ring stage: substep 0 of stage kt (fragments already in registers)
+  // while the B half of stage `pend` (its A half went out one iteration
+  // earlier) is copied into slot `pslot`; then, after the barrier, substep 1
+  // while the fragments of the stage in slot `next` are read and the A half
+  // of stage `issue` is copied into the slot stage kt leaves. With SW set,
+  // `cur` is switched to tile Lsw between the two (the B half before it is
+  // the old tile's, the A half after it the new tile's).
   //
   // Pipeline. Stage kt lives in slot (slot0 + kt) % NSLOT; NSLOT stages are
   // in flight ahead of the one multiplied. After the barrier of iteration kt
   // (which every wave reaches only once done reading stage kt) the stage
-  // NSLOT further on is copied into the slot stage kt leaves, the copies
-  // spread over the MFMAs. Every iteration issues the same number of
+  // NSLOT further on starts into the slot stage kt leaves; its second half
+  // follows in the next iteration's first substep, so each substep carries
+  // half a stage of copies. Every iteration issues the same number of
   // copies, so "stage kt+1 has landed" is always "at most NSLOT - 2 stages
   // in flight". A substep first waits for its own fragments (read one
   // substep earlier, at most 8 reads in flight, which lgkmcnt can count),
   // then reads the next ones while it multiplies; the second substep of a
   // stage runs after the barrier and reads the first fragments of the
   // next stage.
-  auto ring_step = [&](int slot, int next, const Src& t, int issue) {
+  Src cur;
+  auto ring_step = [&](int slot, int next, int pend, int pslot, int issue, auto sw, int Lsw) {
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // fragments of substep 0
     __builtin_amdgcn_sched_barrier(0);
     read_frags(slot, 1, 1);
+    issue_b(cur, pend, pslot);
     mfma_substep<NB>(acc, af[0], bfr[0]);
-    interleave_reads();
+    interleave_reads_half_copies();
     __builtin_amdgcn_sched_barrier(0);
     // stage kt+1 has landed in this wave's copies, and the fragments of
     // substep 1 are in registers; the barrier makes every wave's copies
@@ -601,11 +623,27 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
     __builtin_amdgcn_s_waitcnt(wait_imm((NSLOT - 2) * LPS, 0));
     wg_barrier();
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(sw)::value) tile_src(Lsw, cur);
     read_frags(next, 0, 0);
-    issue_stage(t, issue, slot);
+    issue_a(cur, issue, slot);
     mfma_substep<NB>(acc, af[1], bfr[1]);
-    interleave_reads_copies();
+    interleave_reads_half_copies();
     __builtin_amdgcn_sched_barrier(0);
+  };
+  // The ring's first NSLOT stages, the last of them without its B half
+  // (the first iteration issues it); then stage 0 has landed once at most
+  // NSLOT - 2 stages and a half are in flight.
+  auto fill_ring = [&](int last) {
+#pragma unroll
+    for (int p = 0; p < NSLOT - 1; ++p) {
+      issue_a(cur, min(p, last), p);
+      issue_b(cur, min(p, last), p);
+    }
+    issue_a(cur, min(NSLOT - 1, last), NSLOT - 1);
+    __builtin_amdgcn_s_waitcnt(wait_imm((NSLOT - 2) * LPS + LPS / 2, 15));
+    wg_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(0, 0, 0);
   };
 
   int L = ts.t_begin + ts.local;
@@ -617,32 +655,29 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
     // next tile's first fragments are in registers before the epilogue
     // and its copies land while the epilogue runs. After the last tile the
     // copies repeat its last stage into slots never read again.
-    Src cur;
     tile_src(L, cur);
     bool has_next = L + ts.G8 < ts.t_end;
-#pragma unroll
-    for (int p = 0; p < NSLOT; ++p) issue_stage(cur, p, p);
-    __builtin_amdgcn_s_waitcnt(wait_imm((NSLOT - 1) * LPS, 15));  // stage 0 landed
-    wg_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(0, 0, 0);
-    int slot = 0;
+    fill_ring(nkt - 1);
+    int slot = 0, pend = NSLOT - 1, pslot = NSLOT - 1;
+    auto step = [&](int issue, auto sw, int Lsw) {
+      const int next = slot + 1 == NSLOT ? 0 : slot + 1;
+      ring_step(slot, next, pend, pslot, issue, sw, Lsw);
+      pend = issue;
+      pslot = slot;
+      slot = next;
+    };
     for (;;) {
       zero_acc();
       const int tail = nkt - NSLOT;
-      for (int kt = 0; kt < tail; ++kt) {
-        const int next = slot + 1 == NSLOT ? 0 : slot + 1;
-        ring_step(slot, next, cur, kt + NSLOT);
-        slot = next;
+      for (int kt = 0; kt < tail; ++kt) step(kt + NSLOT, Flag<false>{}, 0);
+      // the tail copies the next tile's first stages (`cur` switches to the
+      // next tile inside its first step)
+      int kt = tail;
+      if (has_next) {
+        step(0, Flag<true>{}, L + ts.G8);
+        ++kt;
       }
-      // the tail copies the next tile's first stages (from here on `cur`
-      // describes the next tile)
-      if (has_next) tile_src(L + ts.G8, cur);
-      for (int kt = tail; kt < nkt; ++kt) {
-        const int next = slot + 1 == NSLOT ? 0 : slot + 1;
-        ring_step(slot, next, cur, has_next ? kt - tail : nkt - 1);
-        slot = next;
-      }
+      for (; kt < nkt; ++kt) step(has_next ? kt - tail : nkt - 1, Flag<false>{}, 0);
       int m0, n0;
       ts.coords(L, BN, m0, n0);
       epilogue<NB, EPI>(g, acc, m0, n0, wr, wc, lane, stage);
@@ -659,24 +694,21 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
   for (; L < ts.t_end; L += ts.G8) {
     int m0, n0;
     ts.coords(L, BN, m0, n0);
-    Src cur;
     tile_src(L, cur);
     zero_acc();
     if (nkt > 0) {
       __builtin_amdgcn_s_waitcnt(kWaitAll);
       wg_barrier();   // the previous tile's readers are done with LDS
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int p = 0; p < NSLOT; ++p) issue_stage(cur, min(p, nkt - 1), p);
-      __builtin_amdgcn_s_waitcnt(wait_imm((NSLOT - 1) * LPS, 15));  // stage 0 landed
-      wg_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(0, 0, 0);
-      int slot = 0;
+      fill_ring(nkt - 1);
+      int slot = 0, pend = min(NSLOT - 1, nkt - 1), pslot = NSLOT - 1;
       for (int kt = 0; kt < nkt; ++kt) {
         const int next = slot + 1 == NSLOT ? 0 : slot + 1;
         // past the last stage the copies repeat it (stale reads, never used)
-        ring_step(slot, next, cur, min(kt + NSLOT, nkt - 1));
+        const int issue = min(kt + NSLOT, nkt - 1);
+        ring_step(slot, next, pend, pslot, issue, Flag<false>{}, 0);
+        pend = issue;
+        pslot = slot;
         slot = next;
       }
     }
