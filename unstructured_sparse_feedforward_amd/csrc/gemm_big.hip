@@ -12,9 +12,8 @@
 //
 // k-contiguous operands stream through a ring of LDS slots filled by
 // direct-to-LDS copies that are spread over the MFMAs as well: 32 k per
-// slot (gemm_ring_kernel), or 64 k per slot for long K
-// (gemm_ring64_kernel). The ring runs on across a workgroup's tiles, so a
-// tile starts with its first fragments in registers. An n-contiguous B
+// slot (gemm_ring_kernel). The ring runs on across a workgroup's tiles, so
+// a tile starts with its first fragments in registers. An n-contiguous B
 // goes through registers instead, with two 64-wide stages
 // (gemm_bt_kernel).
 //
@@ -882,216 +881,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_bt_kernel(GemmArgs g) {
   }
 }
 
-// ---------------------------------------------------------------- 64-k stages
-
-// The ring kernel with 64-k stages (128-byte LDS rows, swizzled as above)
-// in two 64 KB slots: one barrier and one copy wait per 64 k, half as many
-// as with 32-k stages. A stage is four 16-k substeps; the barrier sits
-// before the last, after which the next stage's first fragments are read
-// and the stage two ahead is copied into the slot just read.
-__device__ __forceinline__ void interleave_reads_copies16() {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one global-to-LDS copy
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one global-to-LDS copy
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-  }
-}
-
-template <int NB, int EPI>
-__global__ __launch_bounds__(NT, 1) void gemm_ring64_kernel(GemmArgs g) {
-  using C_ = Cfg<NB>;
-  constexpr int BN = C_::BN;
-  constexpr int JB = C_::JB;
-  constexpr int SLOT = (BM + NB * BN) * ROWB;   // 64 KB
-  constexpr int APW = 64 / 8;                    // 8-row copies of A per wave
-  constexpr int BPW = BN / 4 / 8;                // 8-row copies of B per wave and operand
-  constexpr int LPS = APW + NB * BPW;            // copies per wave and stage
-  static_assert(LPS == 16, "stage = 16 copies per wave");
-  static_assert(EPI != kEpiTwell, "the TwELL epilogue stages through LDS the ring kernel holds");
-  __shared__ __align__(16) char smem[2 * SLOT];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wave >> 1;
-  const int wc = wave & 1;
-  const int M = g.M;
-  const int Kd = g.k_dev ? g.k_mult * ((device_rows(g.k_dev, g.k_cap) + 63) / 64 * 64) : g.K;
-  const int nkt = Kd / BK;
-  if (nkt == 0 && g.accumulate) return;
-  const TileSched ts(M, g.N, BN);
-
-  const char* Ab = (const char*)g.A;
-  const char* Bb[2] = {(const char*)g.B0, (const char*)g.B1};
-  const int64_t lda_b = g.lda * 2;
-  const int64_t ldb_b = g.ldb * 2;
-
-  // Direct-to-LDS copy: one instruction moves 8 rows x 128 bytes, lane L
-  // landing at row L/8, physical chunk L%8, so it fetches logical chunk
-  // (L%8) ^ swz(row). Copy c of a 64-row (or 32-row) group starts at row
-  // 8 c, where swz(row) = (4 c + L/16) & 7.
-  const int lr = lane >> 3;
-  // (offsets from the operand bases, as in the 32-k ring)
-  struct Src {
-    uint32_t a[APW];
-    uint32_t b[NB][BPW];
-  };
-  auto tile_src = [&](int L, Src& t) {
-    int m0, n0;
-    ts.coords(L, BN, m0, n0);
-#pragma unroll
-    for (int i = 0; i < APW; ++i) {
-      const int m = min(m0 + wave * 64 + i * 8 + lr, M - 1);
-      const int ch = (lane & 7) ^ ((4 * i + (lane >> 4)) & 7);
-      t.a[i] = (uint32_t)((int64_t)m * lda_b + ch * 16);
-    }
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < BPW; ++i) {
-        const int n = min(n0 + wave * (BN / 4) + i * 8 + lr, g.N - 1);
-        const int ch = (lane & 7) ^ ((4 * i + (lane >> 4)) & 7);
-        t.b[nb][i] = (uint32_t)((int64_t)n * ldb_b + ch * 16);
-      }
-  };
-  auto issue_stage = [&](const Src& t, int kt, int slot) {
-    char* base = smem + slot * SLOT;
-    const uint32_t kb = (uint32_t)kt * BK * 2;
-#pragma unroll
-    for (int i = 0; i < APW; ++i) copy16_lds(Ab, t.a[i], kb, base + (wave * 64 + i * 8) * ROWB);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < BPW; ++i)
-        copy16_lds(Bb[nb], t.b[nb][i], kb,
-                   base + (BM + nb * BN + wave * (BN / 4) + i * 8) * ROWB);
-  };
-
-  f32x16_t acc[NB][4][JB];
-  auto zero_acc = [&]() {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < JB; ++j)
-#pragma unroll
-          for (int q = 0; q < 16; ++q) acc[nb][i][j][q] = 0.0f;
-  };
-
-  u32x4_t af[2][4];
-  u32x4_t bfr[2][NB][JB];
-  auto read_frags = [&](int slot, int s, int buf) {
-    const char* sa = smem + slot * SLOT;
-    const int ch = 2 * s + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[buf][i] = *(const u32x4_t*)(sa + lds_off(wr * 128 + i * 32 + (lane & 31), ch));
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int j = 0; j < JB; ++j)
-        bfr[buf][nb][j] = *(const u32x4_t*)(sa + (BM + nb * BN) * ROWB +
-                                            lds_off(wc * C_::WN + j * 32 + (lane & 31), ch));
-  };
-
-  // One stage in slot `slot`: substeps 0-2 each wait for their fragments
-  // (read one substep earlier) and read the next substep's; then the wait
-  // for the next stage's copies (the only ones in flight) and the barrier,
-  // after which substep 3 reads the next stage's first fragments from the
-  // other slot and copies stage `issue` of t into this one.
-  auto ring_step = [&](int slot, const Src& t, int issue) {
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(slot, s + 1, (s + 1) & 1);
-      mfma_substep<NB>(acc, af[s & 1], bfr[s & 1]);
-      interleave_reads();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
-    wg_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(slot ^ 1, 0, 0);
-    issue_stage(t, issue, slot);
-    mfma_substep<NB>(acc, af[1], bfr[1]);
-    interleave_reads_copies16();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  int L = ts.t_begin + ts.local;
-  if (L >= ts.t_end) return;
-
-  if (nkt >= 2) {
-    // the ring runs on across this workgroup's tiles (as in the 32-k ring)
-    Src cur;
-    tile_src(L, cur);
-    bool has_next = L + ts.G8 < ts.t_end;
-    issue_stage(cur, 0, 0);
-    issue_stage(cur, 1, 1);
-    __builtin_amdgcn_s_waitcnt(wait_imm(LPS, 15));  // stage 0 landed
-    wg_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    read_frags(0, 0, 0);
-    int slot = 0;
-    for (;;) {
-      zero_acc();
-      for (int kt = 0; kt < nkt - 2; ++kt) {
-        ring_step(slot, cur, kt + 2);
-        slot ^= 1;
-      }
-      if (has_next) tile_src(L + ts.G8, cur);
-      for (int kt = nkt - 2; kt < nkt; ++kt) {
-        ring_step(slot, cur, has_next ? kt - (nkt - 2) : nkt - 1);
-        slot ^= 1;
-      }
-      int m0, n0;
-      ts.coords(L, BN, m0, n0);
-      epilogue<NB, EPI>(g, acc, m0, n0, wr, wc, lane);
-      if (!has_next) break;
-      L += ts.G8;
-      has_next = L + ts.G8 < ts.t_end;
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitAll);
-    return;
-  }
-
-  // one stage (or none) per tile
-  for (; L < ts.t_end; L += ts.G8) {
-    int m0, n0;
-    ts.coords(L, BN, m0, n0);
-    zero_acc();
-    if (nkt > 0) {
-      Src cur;
-      tile_src(L, cur);
-      __builtin_amdgcn_s_waitcnt(kWaitAll);
-      wg_barrier();   // the previous tile's readers are done with LDS
-      __builtin_amdgcn_sched_barrier(0);
-      issue_stage(cur, 0, 0);
-      __builtin_amdgcn_s_waitcnt(kWaitAll);
-      wg_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(0, 0, 0);
-      ring_step(0, cur, 0);   // copies stage 0 again into slot 0, never read
-    }
-    epilogue<NB, EPI>(g, acc, m0, n0, wr, wc, lane);
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitAll);
-}
-
-// K from which float32-output GEMMs take the 64-k ring (measured on the
-// dense down projection, K = 5632: 155 us with 64-k stages against 180 us
-// for the n-contiguous kernel and 205 us for the 32-k ring; on the gate
-// pre-activations, 8192 x 5632 x 2048: 190 against 223 us)
-constexpr int kRing64MinK = 2048;
-
 // 3, 4 and 5 slots time the same on the gate GEMM (the clock, not the
 // load latency, sets the pace once the copies are spread over the MFMAs).
 constexpr int kSlots = 4;
@@ -1106,12 +895,6 @@ hipError_t launch_ring(const GemmArgs& g, hipStream_t s) {
 // staging tiles fill the 160 KB of LDS
 hipError_t launch_ring_twell(const GemmArgs& g, hipStream_t s) {
   hipLaunchKernelGGL((gemm_ring_kernel<1, kEpiTwell, 3>), dim3(g.grid), dim3(NT), 0, s, g);
-  return hipGetLastError();
-}
-
-template <int NB, int EPI>
-hipError_t launch_ring64(const GemmArgs& g, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_ring64_kernel<NB, EPI>), dim3(g.grid), dim3(NT), 0, s, g);
   return hipGetLastError();
 }
 
@@ -1150,14 +933,9 @@ hipError_t launch_gemm_big(int nb, bool bt, Epi epi, const GemmArgs& g, hipStrea
     return hipGetLastError();
   }
   if (epi == kEpiTwell) return launch_ring_twell(g, s);
-  // 64-k stages (half the barriers and copy waits per MFMA, whole 128-byte
-  // rows per copy) win from K = 2048 on, and on the backup rows' dW products
-  // (device-sized K = 2 x 448 at the training shape: 336 against 344 us for
-  // the backup rows' block of the backward)
-  if (epi == kEpiStoreF32)
-    return (g.k_dev || (g.K >= kRing64MinK && g.K % BK == 0))
-               ? launch_ring64<1, kEpiStoreF32>(g, s)
-               : launch_ring<1, kEpiStoreF32>(g, s);
+  // float32 output, K on the host or on the device (the backup rows' dW
+  // products)
+  if (epi == kEpiStoreF32) return launch_ring<1, kEpiStoreF32>(g, s);
   if (epi == kEpiHiddenBF16) return nb == 2 ? launch_ring<2, kEpiHiddenBF16>(g, s)
                                             : launch_ring<1, kEpiHiddenBF16>(g, s);
   if (epi == kEpiTrainFwd) return nb == 2 ? launch_ring<2, kEpiTrainFwd>(g, s)
