@@ -117,24 +117,37 @@ __device__ __forceinline__ void interleave_reads() {
   __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
 }
 
-// 8 fragment reads over the first 8 MFMAs, then 4 global-to-LDS copies on
-// every other one of the last 8: half a stage's copies per substep, so the
-// L2-to-LDS path (about a quarter of the MFMA rate in bytes per clock) drains
-// them as they come instead of stalling the wave's in-order issue, and with
-// it the matrix core, behind a burst. (The copies come after the reads in
-// program order: the compiler cannot tell that they write other LDS slots
-// than the reads read.)
-__device__ __forceinline__ void interleave_reads_half_copies() {
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one global-to-LDS copy
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
-  }
+// A substep's 16 MFMAs carry its 8 fragment reads (one before each of the
+// first 8) and half a stage of copies, one before MFMAs 2, 6, 10 and 14, so
+// that the L2-to-LDS path (about a quarter of the MFMA rate in bytes per
+// clock) drains the copies as they come instead of stalling the wave's
+// in-order issue, and with it the matrix core, behind a burst. The copies
+// cannot move past reads in program order (the compiler cannot tell that
+// they write other LDS slots than the reads read), so the caller emits
+// them as r0 r1 r2 c0 r3 r4 r5 r6 c1 r7 c2 c3.
+__device__ __forceinline__ void interleave_spread() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+  __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+  __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
 }
 
 template <bool B>
@@ -539,25 +552,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
         t.b[nb][i] = (uint32_t)((int64_t)n * ldb_b + lchunk * 16);
       }
   };
-  // A stage's copies go out in two halves of LPS / 2: its A rows, then its
-  // B rows.
-  auto issue_a = [&](const Src& t, int kt, int slot) {
-    char* base = smem + slot * SLOT;
-    const uint32_t kb = (uint32_t)kt * RBK * 2;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) copy16_lds(Ab, t.a[i], kb, base + (wave * 64 + i * 16) * RROWB);
-  };
-  auto issue_b = [&](const Src& t, int kt, int slot) {
-    char* base = smem + slot * SLOT;
-    const uint32_t kb = (uint32_t)kt * RBK * 2;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < BPW; ++i)
-        copy16_lds(Bb[nb], t.b[nb][i], kb,
-                   base + (BM + nb * BN + wave * (BN / 4) + i * 16) * RROWB);
-  };
-  static_assert(NB * BPW == 4, "halves of 4 copies");
+  // a stage's copies go out in two halves of LPS / 2: its A rows, then its
+  // B rows
+  static_assert(NB * BPW == 4 && 4 + NB * JB == 8, "halves of 4 copies, 8 reads");
 
   f32x16_t acc[NB][4][JB];
   auto zero_acc = [&]() {
@@ -573,18 +570,54 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
 
   u32x4_t af[2][4];
   u32x4_t bfr[2][NB][JB];
-  auto read_frags = [&](int slot, int s, int buf) {
+  // fragment i of substep s of the stage in slot `slot`: A blocks 0..3,
+  // then the B blocks
+  auto read_one = [&](int slot, int s, int buf, int i) {
     const char* sa = smem + slot * SLOT;
     const int ch = 2 * s + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+    if (i < 4) {
       af[buf][i] = *(const u32x4_t*)(sa + rlds_off(wr * 128 + i * 32 + (lane & 31), ch));
+    } else {
+      const int nb = (i - 4) / JB, j = (i - 4) % JB;
+      bfr[buf][nb][j] = *(const u32x4_t*)(sa + (BM + nb * BN) * RROWB +
+                                          rlds_off(wc * C_::WN + j * 32 + (lane & 31), ch));
+    }
+  };
+  // copy i (0..3) of stage kt's A half (its 4 16-row pieces of A) or B half
+  // into slot `slot`
+  auto copy_one = [&](bool is_b, const Src& t, int kt, int slot, int i) {
+    char* base = smem + slot * SLOT;
+    const uint32_t kb = (uint32_t)kt * RBK * 2;
+    if (!is_b) {
+      copy16_lds(Ab, t.a[i], kb, base + (wave * 64 + i * 16) * RROWB);
+    } else {
+      const int nb = i / BPW, ii = i % BPW;
+      copy16_lds(Bb[nb], t.b[nb][ii], kb, base + (BM + nb * BN + wave * (BN / 4) + ii * 16) * RROWB);
+    }
+  };
+  auto read_frags = [&](int slot, int s, int buf) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int i = 0; i < 8; ++i) read_one(slot, s, buf, i);
+  };
+  auto issue_half = [&](bool is_b, const Src& t, int kt, int slot) {
 #pragma unroll
-      for (int j = 0; j < JB; ++j)
-        bfr[buf][nb][j] = *(const u32x4_t*)(sa + (BM + nb * BN) * RROWB +
-                                            rlds_off(wc * C_::WN + j * 32 + (lane & 31), ch));
+    for (int i = 0; i < 4; ++i) copy_one(is_b, t, kt, slot, i);
+  };
+  // the fragment reads of substep s from slot rslot and the A (B) half of
+  // stage kt's copies into slot cslot, in the order interleave_spread places
+  auto frags_copies = [&](int rslot, int s, int buf, bool is_b, const Src& t, int kt, int cslot) {
+    read_one(rslot, s, buf, 0);
+    read_one(rslot, s, buf, 1);
+    read_one(rslot, s, buf, 2);
+    copy_one(is_b, t, kt, cslot, 0);
+    read_one(rslot, s, buf, 3);
+    read_one(rslot, s, buf, 4);
+    read_one(rslot, s, buf, 5);
+    read_one(rslot, s, buf, 6);
+    copy_one(is_b, t, kt, cslot, 1);
+    read_one(rslot, s, buf, 7);
+    copy_one(is_b, t, kt, cslot, 2);
+    copy_one(is_b, t, kt, cslot, 3);
   };
 
   // One ring stage: substep 0 of stage kt (fragments already in registers)
@@ -611,10 +644,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
   auto ring_step = [&](int slot, int next, int pend, int pslot, int issue, auto sw, int Lsw) {
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // fragments of substep 0
     __builtin_amdgcn_sched_barrier(0);
-    read_frags(slot, 1, 1);
-    issue_b(cur, pend, pslot);
+    frags_copies(slot, 1, 1, true, cur, pend, pslot);
     mfma_substep<NB>(acc, af[0], bfr[0]);
-    interleave_reads_half_copies();
+    interleave_spread();
     __builtin_amdgcn_sched_barrier(0);
     // stage kt+1 has landed in this wave's copies, and the fragments of
     // substep 1 are in registers; the barrier makes every wave's copies
@@ -623,10 +655,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
     wg_barrier();
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (decltype(sw)::value) tile_src(Lsw, cur);
-    read_frags(next, 0, 0);
-    issue_a(cur, issue, slot);
+    frags_copies(next, 0, 0, false, cur, issue, slot);
     mfma_substep<NB>(acc, af[1], bfr[1]);
-    interleave_reads_half_copies();
+    interleave_spread();
     __builtin_amdgcn_sched_barrier(0);
   };
   // The ring's first NSLOT stages, the last of them without its B half
@@ -635,10 +666,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_ring_kernel(GemmArgs g) {
   auto fill_ring = [&](int last) {
 #pragma unroll
     for (int p = 0; p < NSLOT - 1; ++p) {
-      issue_a(cur, min(p, last), p);
-      issue_b(cur, min(p, last), p);
+      issue_half(false, cur, min(p, last), p);
+      issue_half(true, cur, min(p, last), p);
     }
-    issue_a(cur, min(NSLOT - 1, last), NSLOT - 1);
+    issue_half(false, cur, min(NSLOT - 1, last), NSLOT - 1);
     __builtin_amdgcn_s_waitcnt(wait_imm((NSLOT - 2) * LPS + LPS / 2, 15));
     wg_barrier();
     __builtin_amdgcn_sched_barrier(0);
