@@ -1447,26 +1447,28 @@ sffn_status sffn_backward(sffn_handle* h, const void* x, const void* w_gate, con
 // which the dense layer is faster than the sparse one, from a cost model
 // of the two paths on MI355X (per token; d model width, F neurons; f the
 // fraction of rows whose TwELL overflowed):
-//   dense   t_d = (3 gated, 2 non-gated) * 2 d F flop at 1.16 PFLOP/s
-//   sparse  2 d F flop (gate GEMM) at 1.09 PFLOP/s + 6 ns (routing, lists,
+//   dense   t_d = (3 gated, 2 non-gated) * 2 d F flop at 1.2 PFLOP/s
+//   sparse  2 d F flop (gate GEMM) at 1.1 PFLOP/s + 6 ns (routing, lists,
 //           slice sums, launches)
 //           + (1 - f) * per active neuron (2 gated, 1 non-gated) * 2 d bytes
-//             of weight rows gathered at 28.6 TB/s
+//             of weight rows gathered at 27.5 TB/s
 //           + f * 2 t_d (overflowing rows on the dense path, whose hidden
 //             rows enter the down GEMM as two bf16 parts)
 // The GEMM rates are the ones measured here for the gate GEMM and the dense
 // layer at d = 2048, F = 5632; the gather rate and the 6 ns are the slope
 // and the intercept (less the gate GEMM) of the sparse layer's time against
 // its mean active count over the 18 layers of the chained stack (T = 16384,
-// 15 to 119 active per token). With f = 0 the model puts the crossover at
-// 113 active per token for the gated layer at F = 5632 and at 147 for the
-// non-gated one at F = 8192; at the stack's f of about 0.02 the gated
-// crossover is 108, where its layers' measured times cross at about 105.
+// 15 to 119 active per token), averaged over two boxes whose measured
+// crossovers were about 90 and 105 active per token (the gather rate varies
+// more from box to box than the GEMM rates). With f = 0 the model puts the
+// crossover at 103 active per token for the gated layer at F = 5632 and at
+// 130 for the non-gated one at F = 8192; at the stack's f of about 0.02 the
+// gated crossover is 98.
 static float model_crossover(const sffn_desc& D, double f) {
   const double dF = (double)D.d * D.d_ff;
-  const double t_dense = (D.gated ? 3.0 : 2.0) * 2.0 * dF / 1.16e15;
-  const double t_fixed = 2.0 * dF / 1.09e15 + 6e-9 + f * 2.0 * t_dense;
-  const double t_pair = (1.0 - f) * (D.gated ? 2.0 : 1.0) * 2.0 * D.d / 28.6e12;
+  const double t_dense = (D.gated ? 3.0 : 2.0) * 2.0 * dF / 1.2e15;
+  const double t_fixed = 2.0 * dF / 1.1e15 + 6e-9 + f * 2.0 * t_dense;
+  const double t_pair = (1.0 - f) * (D.gated ? 2.0 : 1.0) * 2.0 * D.d / 27.5e12;
   const double n = t_pair > 0.0 ? (t_dense - t_fixed) / t_pair : 0.0;
   return (float)(n > 0.0 ? n : 0.0);
 }
